@@ -1,0 +1,385 @@
+// C ABI of libbsattn.so: argument checking, handle management and error reporting.
+// Every compute call is checked completely on the host before anything is
+// enqueued; the kernels assume the shapes checked here.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bsattn {
+
+namespace {
+thread_local std::string g_last_error;
+constexpr int kMaxNb = 4096;
+constexpr int kMaxR = 64;
+constexpr int kMaxLfTokens = 262144;
+}  // namespace
+
+int set_error(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BSATTN_OK;
+  return set_error(BSATTN_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Number of distinct blocks in G U [lo, hi].
+int union_size(const std::vector<int32_t>& G, int lo, int hi) {
+  int in_win = 0;
+  for (int x : G) in_win += (x >= lo && x <= hi);
+  return (hi - lo + 1) + (int)G.size() - in_win;
+}
+
+int check_device(int device) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return check_hip(e, "hipGetDevice");
+  if (cur != device)
+    return set_error(BSATTN_EINVAL, "current device differs from the device the handle was built on");
+  return BSATTN_OK;
+}
+
+int check_tensor_args(int batch, int d, float scale, std::initializer_list<const void*> ptrs,
+                      const char* who) {
+  if (batch < 1) return set_error(BSATTN_EINVAL, std::string(who) + ": batch must be >= 1");
+  if (d != kHead) return set_error(BSATTN_EUNSUPPORTED, std::string(who) + ": head dim must be 64");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return set_error(BSATTN_EINVAL, std::string(who) + ": scale must be finite and > 0");
+  for (const void* p : ptrs) {
+    if (p == nullptr) return set_error(BSATTN_EINVAL, std::string(who) + ": null tensor pointer");
+    if (!aligned16(p)) return set_error(BSATTN_EINVAL, std::string(who) + ": tensor pointer not 16-byte aligned");
+  }
+  return BSATTN_OK;
+}
+
+int check_workspace(void* ws, size_t ws_bytes, size_t need, const char* who) {
+  if (ws_bytes < need)
+    return set_error(BSATTN_EINVAL, std::string(who) + ": workspace too small (need " +
+                                        std::to_string(need) + " bytes)");
+  if (need > 0 && (ws == nullptr || !aligned16(ws)))
+    return set_error(BSATTN_EINVAL, std::string(who) + ": workspace null or not 16-byte aligned");
+  return BSATTN_OK;
+}
+
+void free_layout(bsattn_layout* L) {
+  (void)hipFree(L->d_gblk);
+  (void)hipFree(L->d_ngblk);
+  (void)hipFree(L->d_row_ptr);
+  (void)hipFree(L->d_col_idx);
+  (void)hipFree(L->d_csc_ptr);
+  (void)hipFree(L->d_csc_idx);
+  delete L;
+}
+
+void free_plan(lfattn_plan* P) {
+  (void)hipFree(P->d_gtok);
+  (void)hipFree(P->d_gidx);
+  (void)hipFree(P->d_tile_gmask);
+  delete P;
+}
+
+template <typename T>
+int dev_alloc(T** p, size_t count) {
+  *p = nullptr;
+  if (count == 0) count = 1;
+  hipError_t e = hipMalloc((void**)p, count * sizeof(T));
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return set_error(BSATTN_ENOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+  }
+  return BSATTN_OK;
+}
+
+}  // namespace
+}  // namespace bsattn
+
+using namespace bsattn;
+
+extern "C" {
+
+int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, int g, int w,
+                        int r, uint64_t seed, hipStream_t stream, bsattn_layout** out) {
+  clear_error();
+  if (out == nullptr) return set_error(BSATTN_EINVAL, "layout_build: out is null");
+  *out = nullptr;
+  if (b != kBlock) return set_error(BSATTN_EUNSUPPORTED, "layout_build: block size must be 64");
+  if (n <= 0 || n % b != 0) return set_error(BSATTN_EINVAL, "layout_build: n must be a positive multiple of b");
+  const int nb = n / b;
+  if (nb > kMaxNb) return set_error(BSATTN_EUNSUPPORTED, "layout_build: n/b above 4096");
+  if (heads < 1) return set_error(BSATTN_EINVAL, "layout_build: heads must be >= 1");
+  if (w < 1 || w % 2 == 0) return set_error(BSATTN_EINVAL, "layout_build: w must be odd and >= 1");
+  if (r < 0) return set_error(BSATTN_EINVAL, "layout_build: r must be >= 0");
+  if (r > kMaxR) return set_error(BSATTN_EUNSUPPORTED, "layout_build: r above 64");
+  if (g < 0 || g > nb) return set_error(BSATTN_EINVAL, "layout_build: g out of range");
+  if (g > 0 && global_blocks == nullptr) return set_error(BSATTN_EINVAL, "layout_build: global_blocks is null");
+  std::vector<int32_t> G(global_blocks, global_blocks + g);
+  for (int x = 0; x < g; ++x) {
+    if (G[x] < 0 || G[x] >= nb) return set_error(BSATTN_EINVAL, "layout_build: global block out of range");
+    if (x > 0 && G[x] <= G[x - 1]) return set_error(BSATTN_EINVAL, "layout_build: global blocks not sorted and unique");
+  }
+  const int64_t nnz_limit = (int64_t)1 << 31;
+  auto L = new bsattn_layout();
+  L->n = n; L->b = b; L->nb = nb; L->heads = heads; L->g = g; L->w = w; L->r = r; L->seed = seed;
+  L->gblk = G;
+  std::vector<int32_t> ng;
+  {
+    size_t p = 0;
+    for (int i = 0; i < nb; ++i) {
+      if (p < G.size() && G[p] == i) { ++p; continue; }
+      ng.push_back(i);
+    }
+  }
+  L->row_len.resize(nb);
+  int64_t nnz = 0;
+  const int half = (w - 1) / 2;
+  {
+    size_t p = 0;
+    for (int i = 0; i < nb; ++i) {
+      bool gl = p < G.size() && G[p] == i;
+      if (gl) ++p;
+      int len;
+      if (gl) {
+        len = nb;
+      } else {
+        const int lo = i - half < 0 ? 0 : i - half;
+        const int hi = i + half > nb - 1 ? nb - 1 : i + half;
+        const int e = union_size(G, lo, hi);
+        const int m = nb - e;
+        len = e + (r < m ? r : m);
+      }
+      L->row_len[i] = len;
+      nnz += len;
+    }
+  }
+  L->nnz_per_head = nnz;
+  if (nnz * heads >= nnz_limit) {
+    delete L;
+    return set_error(BSATTN_EUNSUPPORTED, "layout_build: too many block pairs");
+  }
+  L->split = nb > kSeg;
+  L->nseg = L->split ? (nb + kSeg - 1) / kSeg : 1;
+  hipError_t e = hipGetDevice(&L->device);
+  if (e != hipSuccess) { delete L; return check_hip(e, "hipGetDevice"); }
+  int st = BSATTN_OK;
+  if ((st = dev_alloc(&L->d_gblk, (size_t)g)) || (st = dev_alloc(&L->d_ngblk, ng.size())) ||
+      (st = dev_alloc(&L->d_row_ptr, (size_t)heads * nb + 1)) ||
+      (st = dev_alloc(&L->d_col_idx, (size_t)(nnz * heads))) ||
+      (st = dev_alloc(&L->d_csc_ptr, (size_t)heads * nb + 1)) ||
+      (st = dev_alloc(&L->d_csc_idx, (size_t)(nnz * heads)))) {
+    free_layout(L);
+    return st;
+  }
+  // the uploads read host copies owned by the handle, so they stay valid for as
+  // long as the asynchronous copies may run
+  L->ngblk = ng;
+  if (g > 0 && (st = check_hip(hipMemcpyAsync(L->d_gblk, L->gblk.data(), (size_t)g * 4,
+                                              hipMemcpyHostToDevice, stream), "upload global blocks"))) {
+    free_layout(L);
+    return st;
+  }
+  if (!L->ngblk.empty() &&
+      (st = check_hip(hipMemcpyAsync(L->d_ngblk, L->ngblk.data(), L->ngblk.size() * 4,
+                                     hipMemcpyHostToDevice, stream), "upload blocks"))) {
+    free_layout(L);
+    return st;
+  }
+  if ((st = launch_layout_build(L, stream))) { free_layout(L); return st; }
+  *out = L;
+  return BSATTN_OK;
+}
+
+int bsattn_layout_rebuild(bsattn_layout* L, uint64_t seed, hipStream_t stream) {
+  clear_error();
+  if (L == nullptr) return set_error(BSATTN_EINVAL, "layout_rebuild: null layout");
+  int st = check_device(L->device);
+  if (st) return st;
+  L->seed = seed;
+  return launch_layout_build(L, stream);
+}
+
+int bsattn_layout_info(const bsattn_layout* L, int* nb, int* heads, int64_t* nnzb_total) {
+  clear_error();
+  if (L == nullptr) return set_error(BSATTN_EINVAL, "layout_info: null layout");
+  if (nb) *nb = L->nb;
+  if (heads) *heads = L->heads;
+  if (nnzb_total) *nnzb_total = L->nnz_per_head * L->heads;
+  return BSATTN_OK;
+}
+
+int bsattn_layout_to_host(const bsattn_layout* L, int32_t* row_ptr, int32_t* col_idx,
+                          int32_t* csc_ptr, int32_t* csc_idx) {
+  clear_error();
+  if (L == nullptr) return set_error(BSATTN_EINVAL, "layout_to_host: null layout");
+  int st = check_device(L->device);
+  if (st) return st;
+  if ((st = check_hip(hipDeviceSynchronize(), "layout_to_host sync"))) return st;
+  const size_t np = ((size_t)L->heads * L->nb + 1) * 4;
+  const size_t nz = (size_t)(L->nnz_per_head * L->heads) * 4;
+  if (row_ptr && (st = check_hip(hipMemcpy(row_ptr, L->d_row_ptr, np, hipMemcpyDeviceToHost), "copy row_ptr"))) return st;
+  if (col_idx && (st = check_hip(hipMemcpy(col_idx, L->d_col_idx, nz, hipMemcpyDeviceToHost), "copy col_idx"))) return st;
+  if (csc_ptr && (st = check_hip(hipMemcpy(csc_ptr, L->d_csc_ptr, np, hipMemcpyDeviceToHost), "copy csc_ptr"))) return st;
+  if (csc_idx && (st = check_hip(hipMemcpy(csc_idx, L->d_csc_idx, nz, hipMemcpyDeviceToHost), "copy csc_idx"))) return st;
+  return BSATTN_OK;
+}
+
+int bsattn_layout_destroy(bsattn_layout* L) {
+  clear_error();
+  if (L == nullptr) return BSATTN_OK;
+  int st = check_hip(hipDeviceSynchronize(), "layout_destroy sync");
+  free_layout(L);
+  return st;
+}
+
+size_t bsattn_fwd_workspace(const bsattn_layout* L, int batch, int d) {
+  if (L == nullptr || batch < 1 || d != kHead) return 0;
+  return fwd_workspace_bytes(L, batch);
+}
+
+size_t bsattn_bwd_workspace(const bsattn_layout* L, int batch, int d) {
+  if (L == nullptr || batch < 1 || d != kHead) return 0;
+  return bwd_workspace_bytes(L, batch);
+}
+
+int bsattn_fwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
+               const void* q, const void* k, const void* v, void* o, float* lse,
+               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (L == nullptr) return set_error(BSATTN_EINVAL, "fwd: null layout");
+  if (dt != BSATTN_F32 && dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "fwd: unknown dtype");
+  int st = check_tensor_args(batch, d, scale, {q, k, v, o}, "fwd");
+  if (st) return st;
+  if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, "fwd: lse not 16-byte aligned");
+  if ((int64_t)batch * L->heads * L->n * kHead >= ((int64_t)1 << 40))
+    return set_error(BSATTN_EUNSUPPORTED, "fwd: tensor too large");
+  const size_t need = dt == BSATTN_F32 ? 0 : fwd_workspace_bytes(L, batch);
+  if ((st = check_workspace(workspace, ws_bytes, need, "fwd"))) return st;
+  if ((st = check_device(L->device))) return st;
+  return launch_fwd(L, batch, dt, scale, q, k, v, o, lse, workspace, stream);
+}
+
+int bsattn_bwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
+               const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+               hipStream_t stream) {
+  clear_error();
+  if (L == nullptr) return set_error(BSATTN_EINVAL, "bwd: null layout");
+  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "bwd: only bf16 is built");
+  int st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "bwd");
+  if (st) return st;
+  if ((int64_t)batch * L->heads * L->n * kHead >= ((int64_t)1 << 40))
+    return set_error(BSATTN_EUNSUPPORTED, "bwd: tensor too large");
+  if ((st = check_workspace(workspace, ws_bytes, bwd_workspace_bytes(L, batch), "bwd"))) return st;
+  if ((st = check_device(L->device))) return st;
+  return launch_bwd(L, batch, scale, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream);
+}
+
+int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, int n_global,
+                      hipStream_t stream, lfattn_plan** out) {
+  clear_error();
+  if (out == nullptr) return set_error(BSATTN_EINVAL, "lf_plan_build: out is null");
+  *out = nullptr;
+  if (n <= 0 || n % kBlock != 0) return set_error(BSATTN_EINVAL, "lf_plan_build: n must be a positive multiple of 64");
+  if (n > kMaxLfTokens) return set_error(BSATTN_EUNSUPPORTED, "lf_plan_build: n above 262144");
+  if (window_one_side < 0) return set_error(BSATTN_EINVAL, "lf_plan_build: window must be >= 0");
+  if (n_global < 0 || n_global > n) return set_error(BSATTN_EINVAL, "lf_plan_build: n_global out of range");
+  if (n_global > 0 && global_tokens == nullptr) return set_error(BSATTN_EINVAL, "lf_plan_build: global_tokens is null");
+  for (int x = 0; x < n_global; ++x) {
+    if (global_tokens[x] < 0 || global_tokens[x] >= n) return set_error(BSATTN_EINVAL, "lf_plan_build: global token out of range");
+    if (x > 0 && global_tokens[x] <= global_tokens[x - 1]) return set_error(BSATTN_EINVAL, "lf_plan_build: global tokens not sorted and unique");
+  }
+  auto P = new lfattn_plan();
+  P->n = n;
+  P->w1 = window_one_side;
+  P->ng = n_global;
+  P->nt = n / kBlock;
+  P->ngt = (n_global + kBlock - 1) / kBlock;
+  P->nseg = (P->nt + kSeg - 1) / kSeg;
+  P->gtok.assign(global_tokens, global_tokens + n_global);
+  P->gidx.assign(n, -1);
+  P->tile_gmask.assign(P->nt, 0ull);
+  for (int x = 0; x < n_global; ++x) {
+    const int t = P->gtok[x];
+    P->gidx[t] = x;
+    P->tile_gmask[t / kBlock] |= 1ull << (t % kBlock);
+  }
+  hipError_t e = hipGetDevice(&P->device);
+  if (e != hipSuccess) { delete P; return check_hip(e, "hipGetDevice"); }
+  int st;
+  if ((st = dev_alloc(&P->d_gtok, (size_t)n_global)) || (st = dev_alloc(&P->d_gidx, (size_t)n)) ||
+      (st = dev_alloc(&P->d_tile_gmask, (size_t)P->nt))) {
+    free_plan(P);
+    return st;
+  }
+  if ((n_global > 0 && (st = check_hip(hipMemcpyAsync(P->d_gtok, P->gtok.data(), (size_t)n_global * 4,
+                                                      hipMemcpyHostToDevice, stream), "upload global tokens"))) ||
+      (st = check_hip(hipMemcpyAsync(P->d_gidx, P->gidx.data(), (size_t)n * 4, hipMemcpyHostToDevice, stream),
+                      "upload token index")) ||
+      (st = check_hip(hipMemcpyAsync(P->d_tile_gmask, P->tile_gmask.data(), (size_t)P->nt * 8,
+                                     hipMemcpyHostToDevice, stream), "upload tile masks"))) {
+    free_plan(P);
+    return st;
+  }
+  *out = P;
+  return BSATTN_OK;
+}
+
+int lfattn_plan_destroy(lfattn_plan* P) {
+  clear_error();
+  if (P == nullptr) return BSATTN_OK;
+  int st = check_hip(hipDeviceSynchronize(), "lf_plan_destroy sync");
+  free_plan(P);
+  return st;
+}
+
+size_t lfattn_fwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
+  if (P == nullptr || batch < 1 || heads < 1 || d != kHead) return 0;
+  return lf_workspace_bytes(P, batch, heads);
+}
+
+int lfattn_fwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt, float scale,
+               const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+               size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (P == nullptr) return set_error(BSATTN_EINVAL, "lf_fwd: null plan");
+  if (heads < 1) return set_error(BSATTN_EINVAL, "lf_fwd: heads must be >= 1");
+  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "lf_fwd: only bf16 is built");
+  int st = check_tensor_args(batch, d, scale, {q, k, v, o}, "lf_fwd");
+  if (st) return st;
+  if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, "lf_fwd: lse not 16-byte aligned");
+  if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
+    return set_error(BSATTN_EUNSUPPORTED, "lf_fwd: tensor too large");
+  if ((st = check_workspace(workspace, ws_bytes, lf_workspace_bytes(P, batch, heads), "lf_fwd"))) return st;
+  if ((st = check_device(P->device))) return st;
+  return launch_lf_fwd(P, batch, heads, scale, q, k, v, o, lse, workspace, stream);
+}
+
+const char* bsattn_status_str(int status) {
+  switch (status) {
+    case BSATTN_OK: return "BSATTN_OK";
+    case BSATTN_EINVAL: return "BSATTN_EINVAL";
+    case BSATTN_EUNSUPPORTED: return "BSATTN_EUNSUPPORTED";
+    case BSATTN_EHIP: return "BSATTN_EHIP";
+    case BSATTN_ENOMEM: return "BSATTN_ENOMEM";
+    default: return "BSATTN_UNKNOWN";
+  }
+}
+
+const char* bsattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* bsattn_version(void) { return "bsattn 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+// One step of the streaming attention forward for a 64-row query tile held by two
+// waves (wave w owns query rows 32w..32w+31, one query per lane column):
+//   S^T = K Q^T over a 64-key tile, online softmax in fp32, O^T += V^T P^T.
+// Shared by the block-sparse and the banded forward kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace bsattn {
+
+struct FwdState {
+  f32x16 o0, o1;   // O^T accumulators: d rows 0..31 and 32..63, column = query
+  float m, l;      // running max (log2 units, scaled) and this half-lane's sum
+};
+
+__device__ __forceinline__ void fwd_state_init(FwdState& st) {
+  st.o0 = zero16();
+  st.o1 = zero16();
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// S^T for the 64 keys of the LDS tile sK (natural layout) against this lane's query.
+// s0 holds keys 0..31, s1 keys 32..63; register r <-> key 8*(r/4) + 4*hl + r%4.
+__device__ __forceinline__ void qk_tile(const uint16_t* sK, const bf16x8 (&qB)[4], int col,
+                                        int hl, f32x16& s0, f32x16& s1) {
+  s0 = zero16();
+  s1 = zero16();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bf16x8 a0 = ld16(sK + col * kLdsStride + 16 * c + 8 * hl);
+    const bf16x8 a1 = ld16(sK + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+    s0 = mfma32(a0, qB[c], s0);
+    s1 = mfma32(a1, qB[c], s1);
+  }
+}
+
+// Online softmax over one key tile.  Scores equal to -inf are excluded keys.
+// On return s0/s1 hold the unnormalised probabilities 2^(s*sl2 - m).
+__device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& st, float sl2) {
+  float mx = s0[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx * sl2);
+  // a row with no allowed key so far keeps m = -inf; use 0 as its reference so
+  // that exp2 of excluded scores is 0 rather than NaN
+  const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_ref);
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = fast_exp2(__builtin_fmaf(s0[r], sl2, -m_ref));
+    s1[r] = fast_exp2(__builtin_fmaf(s1[r], sl2, -m_ref));
+    rs += s0[r] + s1[r];
+  }
+  st.l = st.l * alpha + rs;
+  st.m = m_new;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    st.o0[r] *= alpha;
+    st.o1[r] *= alpha;
+  }
+}
+
+// O^T += V^T P^T with V^T staged in sVt (row d, key x at position perm16(x)).
+__device__ __forceinline__ void pv_tile(const uint16_t* sVt, const f32x16& p0, const f32x16& p1,
+                                        int col, int hl, FwdState& st) {
+  const bf16x8 pc[4] = {pack8(p0, 0), pack8(p0, 8), pack8(p1, 0), pack8(p1, 8)};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bf16x8 v0 = ld16(sVt + col * kLdsStride + 16 * c + 8 * hl);
+    const bf16x8 v1 = ld16(sVt + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+    st.o0 = mfma32(v0, pc[c], st.o0);
+    st.o1 = mfma32(v1, pc[c], st.o1);
+  }
+}
+
+// Final write of a finished row: O (bf16, normalised) and lse (natural log).
+// orow points at this lane's query row of O; lse_out may be null.
+__device__ __forceinline__ void write_o_bf16(const FwdState& st, float l_tot, int hl,
+                                             uint16_t* orow, float* lse_out) {
+  const float inv = 1.f / l_tot;
+  uint16_t* op = orow + 4 * hl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x2 w0, w1;
+    w0[0] = pack_bf16x2(st.o0[4 * j] * inv, st.o0[4 * j + 1] * inv);
+    w0[1] = pack_bf16x2(st.o0[4 * j + 2] * inv, st.o0[4 * j + 3] * inv);
+    w1[0] = pack_bf16x2(st.o1[4 * j] * inv, st.o1[4 * j + 1] * inv);
+    w1[1] = pack_bf16x2(st.o1[4 * j + 2] * inv, st.o1[4 * j + 3] * inv);
+    *reinterpret_cast<u32x2*>(op + 8 * j) = w0;
+    *reinterpret_cast<u32x2*>(op + 32 + 8 * j) = w1;
+  }
+  if (lse_out != nullptr && hl == 0) *lse_out = (st.m + __log2f(l_tot)) * kLn2;
+}
+
+// Partial record of a split full row: O unnormalised [64][64] fp32, then m[64],
+// then l[64] (both log2 units / plain sums), row qr of the query tile.
+constexpr int kPartFloats = kBlock * kHead + 2 * kBlock;
+
+__device__ __forceinline__ void write_partial(const FwdState& st, float l_tot, int hl, int qr,
+                                              float* rec) {
+  float* orow = rec + qr * kHead + 4 * hl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x4 w0, w1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w0[e] = st.o0[4 * j + e];
+      w1[e] = st.o1[4 * j + e];
+    }
+    *reinterpret_cast<f32x4*>(orow + 8 * j) = w0;
+    *reinterpret_cast<f32x4*>(orow + 32 + 8 * j) = w1;
+  }
+  if (hl == 0) {
+    rec[kBlock * kHead + qr] = st.m;
+    rec[kBlock * kHead + kBlock + qr] = l_tot;
+  }
+}
+
+// Merge nseg partial records (stride kPartFloats) for row `row`, columns dq..dq+15,
+// in segment order: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
+__device__ __forceinline__ void merge_partials(const float* base, int nseg, int row, int dq,
+                                               float (&acc)[16], float& M, float& L) {
+  M = -INFINITY;
+  for (int s = 0; s < nseg; ++s) M = fmaxf(M, base[(size_t)s * kPartFloats + kBlock * kHead + row]);
+  const float Mref = M == -INFINITY ? 0.f : M;
+  L = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int s = 0; s < nseg; ++s) {
+    const float* ps = base + (size_t)s * kPartFloats;
+    const float f = fast_exp2(ps[kBlock * kHead + row] - Mref);
+    L += ps[kBlock * kHead + kBlock + row] * f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(ps + row * kHead + dq + e);
+      acc[e] += x[0] * f;
+      acc[e + 1] += x[1] * f;
+      acc[e + 2] += x[2] * f;
+      acc[e + 3] += x[3] * f;
+    }
+  }
+}
+
+__device__ __forceinline__ void store16_bf16(uint16_t* dst, const float (&acc)[16], float mul) {
+#pragma unroll
+  for (int e = 0; e < 16; e += 8) {
+    u32x4 w;
+    w[0] = pack_bf16x2(acc[e] * mul, acc[e + 1] * mul);
+    w[1] = pack_bf16x2(acc[e + 2] * mul, acc[e + 3] * mul);
+    w[2] = pack_bf16x2(acc[e + 4] * mul, acc[e + 5] * mul);
+    w[3] = pack_bf16x2(acc[e + 6] * mul, acc[e + 7] * mul);
+    *reinterpret_cast<u32x4*>(dst + e) = w;
+  }
+}
+
+}  // namespace bsattn

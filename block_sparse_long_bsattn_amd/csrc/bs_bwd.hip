@@ -1,0 +1,449 @@
+// BigBird-ITC block-sparse attention backward on gfx950.
+//
+// The pages give no backward pass; this is the exact gradient of the forward in
+// bs_fwd.hip ("Big Bird: Transformers for Longer Sequences", §2 eq. (AT); App. D
+// Fig. 6), recomputing P = exp(scale * Q K^T - lse) from the saved log-sum-exp:
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// No atomics: every output tile has one owner.
+//   bs_bwd_dq    one work-group per query block (row of the layout): computes
+//                D for its rows (written for the next kernel) and dQ.
+//   bs_bwd_dkdv  one work-group per key block (column of the transposed layout):
+//                dK and dV, walking the query blocks that see that key block.
+//   bs_bwd_reduce  global rows / columns are full-length; they are split into
+//                kSeg-block items writing fp32 partials, summed here in segment
+//                order, so results are bitwise reproducible.
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bsattn {
+namespace {
+
+constexpr int kThreads = 128;
+constexpr int kTile = kBlock * kHead;   // floats in one 64x64 partial tile
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dbuf;      // D [B*H*n]
+  float* part_q;    // [B*H*g*nseg][64][64]
+  float* part_kv;   // [B*H*g*nseg][2][64][64]
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* csc_ptr;
+  const int32_t* csc_idx;
+  const int32_t* gblk;
+  const int32_t* ngblk;
+  int heads, n, nb, g, nseg, split;
+  int items_per_bh, total_items;
+  float scale, sl2;
+};
+
+struct Item {
+  int bh, h, blk, start, len, slot, seg;
+};
+
+// Item v of a per-(batch, head) list: non-global blocks first (whole list), then
+// each global block's kSeg-long segments.  ptr is the row or column pointer.
+__device__ __forceinline__ Item decode(const BwdArgs& a, int v, const int32_t* ptr) {
+  Item it;
+  it.bh = v / a.items_per_bh;
+  const int r = v - it.bh * a.items_per_bh;
+  it.h = it.bh % a.heads;
+  const int ng = a.nb - a.g;
+  it.seg = 0;
+  it.slot = -1;
+  it.start = 0;
+  it.len = -1;
+  if (r < ng) {
+    it.blk = a.ngblk[r];
+  } else {
+    const int gi = (r - ng) / a.nseg;
+    const int s = (r - ng) - gi * a.nseg;
+    it.blk = a.gblk[gi];
+    it.seg = s;
+    if (a.split) {
+      it.start = s * kSeg;
+      it.len = min(kSeg, a.nb - s * kSeg);
+      it.slot = (it.bh * a.g + gi) * a.nseg + s;
+    }
+  }
+  const int p0 = ptr[(int64_t)it.h * a.nb + it.blk];
+  if (it.len < 0) it.len = ptr[(int64_t)it.h * a.nb + it.blk + 1] - p0;
+  it.start += p0;
+  return it;
+}
+
+__global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sKt[kHead * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kBlock * kLdsStride];
+
+  const int v = xcd_remap(blockIdx.x, a.total_items);
+  if (v >= a.total_items) return;
+  const Item it = decode(a, v, a.row_ptr);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const size_t bh_off = (size_t)it.bh * a.n * kHead;
+  const int qrow = it.blk * kBlock + 32 * wave + col;
+
+  bf16x8 qB[4], doB[4];
+  float dsum = 0.f;
+  {
+    const size_t off = bh_off + (size_t)qrow * kHead + 8 * hl;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 qv = ldg16(a.q + off + 16 * c);
+      const u32x4 dv = ldg16(a.dout + off + 16 * c);
+      const u32x4 ov = ldg16(a.o + off + 16 * c);
+      qB[c] = __builtin_bit_cast(bf16x8, qv);
+      doB[c] = __builtin_bit_cast(bf16x8, dv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsum = __builtin_fmaf(bf16_lo(dv[e]), bf16_lo(ov[e]), dsum);
+        dsum = __builtin_fmaf(bf16_hi(dv[e]), bf16_hi(ov[e]), dsum);
+      }
+    }
+  }
+  const float Dq = dsum + __shfl_xor(dsum, 32);
+  if (it.seg == 0 && hl == 0) a.dbuf[(size_t)it.bh * a.n + qrow] = Dq;
+  const float lse2 = a.lse[(size_t)it.bh * a.n + qrow] * kLog2e;
+  const float sl2 = a.sl2;
+
+  f32x16 g0 = zero16(), g1 = zero16();   // dQ^T, d rows 0..31 and 32..63
+  const int32_t* keys = a.col_idx + it.start;
+  const uint16_t* kbase = a.k + bh_off;
+  const uint16_t* vbase = a.v + bh_off;
+  TileRegs kr, vr;
+  if (it.len > 0) {
+    const int kb = keys[0];
+    gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
+    gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+  }
+  for (int t = 0; t < it.len; ++t) {
+    lds_store_nat(sK, kr, tid);
+    lds_store_nat(sV, vr, tid);
+    __syncthreads();
+    {
+      // K^T built from the natural LDS copy: thread t reads key rows 4*(t/8)..+3,
+      // columns 8*(t%8)..+7, and writes LDS rows (d) 8*(t%8)..+7 at positions
+      // perm16(4*(t/8)) .. +3
+      const int c = tid & 7, x0 = 4 * (tid >> 3);
+      const int pos = perm16(x0);
+      u32x4 rows[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rows[u] = *reinterpret_cast<const u32x4*>(sK + (x0 + u) * kLdsStride + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wd = e >> 1, hi = e & 1;
+        uint32_t v0 = hi ? (rows[0][wd] >> 16) : (rows[0][wd] & 0xffffu);
+        uint32_t v1 = hi ? (rows[1][wd] >> 16) : (rows[1][wd] & 0xffffu);
+        uint32_t v2 = hi ? (rows[2][wd] >> 16) : (rows[2][wd] & 0xffffu);
+        uint32_t v3 = hi ? (rows[3][wd] >> 16) : (rows[3][wd] & 0xffffu);
+        u32x2 pk;
+        pk[0] = v0 | (v1 << 16);
+        pk[1] = v2 | (v3 << 16);
+        *reinterpret_cast<u32x2*>(sKt + (8 * c + e) * kLdsStride + pos) = pk;
+      }
+    }
+    __syncthreads();
+    if (t + 1 < it.len) {
+      const int kb = keys[t + 1];
+      gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
+      gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+    }
+    // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
+    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 k0 = ld16(sK + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 k1 = ld16(sK + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 v0 = ld16(sV + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 v1 = ld16(sV + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      s0 = mfma32(k0, qB[c], s0);
+      s1 = mfma32(k1, qB[c], s1);
+      p0 = mfma32(v0, doB[c], p0);
+      p1 = mfma32(v1, doB[c], p1);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e0 = fast_exp2(__builtin_fmaf(s0[r], sl2, -lse2));
+      const float e1 = fast_exp2(__builtin_fmaf(s1[r], sl2, -lse2));
+      s0[r] = e0 * (p0[r] - Dq);
+      s1[r] = e1 * (p1[r] - Dq);
+    }
+    // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
+    const bf16x8 d0 = pack8(s0, 0), d1 = pack8(s0, 8), d2 = pack8(s1, 0), d3 = pack8(s1, 8);
+    const bf16x8 dc[4] = {d0, d1, d2, d3};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 a0 = ld16(sKt + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 a1 = ld16(sKt + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      g0 = mfma32(a0, dc[c], g0);
+      g1 = mfma32(a1, dc[c], g1);
+    }
+    __syncthreads();
+  }
+
+  const float sc = a.scale;
+  if (it.slot < 0) {
+    uint16_t* op = a.dq + bh_off + (size_t)qrow * kHead + 4 * hl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 w0, w1;
+      w0[0] = pack_bf16x2(g0[4 * j] * sc, g0[4 * j + 1] * sc);
+      w0[1] = pack_bf16x2(g0[4 * j + 2] * sc, g0[4 * j + 3] * sc);
+      w1[0] = pack_bf16x2(g1[4 * j] * sc, g1[4 * j + 1] * sc);
+      w1[1] = pack_bf16x2(g1[4 * j + 2] * sc, g1[4 * j + 3] * sc);
+      *reinterpret_cast<u32x2*>(op + 8 * j) = w0;
+      *reinterpret_cast<u32x2*>(op + 32 + 8 * j) = w1;
+    }
+  } else {
+    float* pp = a.part_q + (size_t)it.slot * kTile + (32 * wave + col) * kHead + 4 * hl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 w0, w1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { w0[e] = g0[4 * j + e] * sc; w1[e] = g1[4 * j + e] * sc; }
+      *reinterpret_cast<f32x4*>(pp + 8 * j) = w0;
+      *reinterpret_cast<f32x4*>(pp + 32 + 8 * j) = w1;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sQt[kHead * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[kBlock * kLdsStride];   // dO
+  __shared__ __attribute__((aligned(16))) uint16_t sOt[kHead * kLdsStride];  // dO^T
+  __shared__ __attribute__((aligned(16))) float sL[kBlock];   // lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[kBlock];
+
+  const int v = xcd_remap(blockIdx.x, a.total_items);
+  if (v >= a.total_items) return;
+  const Item it = decode(a, v, a.csc_ptr);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const size_t bh_off = (size_t)it.bh * a.n * kHead;
+  const int krow = it.blk * kBlock + 32 * wave + col;   // this lane's key token
+
+  bf16x8 kB[4], vB[4];
+  {
+    const size_t off = bh_off + (size_t)krow * kHead + 8 * hl;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      kB[c] = ld16(a.k + off + 16 * c);
+      vB[c] = ld16(a.v + off + 16 * c);
+    }
+  }
+  f32x16 dv0 = zero16(), dv1 = zero16(), dk0 = zero16(), dk1 = zero16();
+  const float sl2 = a.sl2;
+  const int32_t* qblks = a.csc_idx + it.start;
+  const uint16_t* qbase = a.q + bh_off;
+  const uint16_t* dobase = a.dout + bh_off;
+  const float* lbase = a.lse + (size_t)it.bh * a.n;
+  const float* dbase = a.dbuf + (size_t)it.bh * a.n;
+
+  TileRegs qr, qtr, dr, dtr;
+  float lv = 0.f, dval = 0.f;
+  if (it.len > 0) {
+    const int qb = qblks[0];
+    gload_nat(qr, qbase + (size_t)qb * kBlock * kHead, tid);
+    gload_tr(qtr, qbase + (size_t)qb * kBlock * kHead, tid);
+    gload_nat(dr, dobase + (size_t)qb * kBlock * kHead, tid);
+    gload_tr(dtr, dobase + (size_t)qb * kBlock * kHead, tid);
+    if (tid < kBlock) { lv = lbase[qb * kBlock + tid]; dval = dbase[qb * kBlock + tid]; }
+  }
+  for (int t = 0; t < it.len; ++t) {
+    lds_store_nat(sQ, qr, tid);
+    lds_store_tr(sQt, qtr, tid);
+    lds_store_nat(sO, dr, tid);
+    lds_store_tr(sOt, dtr, tid);
+    if (tid < kBlock) { sL[tid] = lv * kLog2e; sD[tid] = dval; }
+    __syncthreads();
+    if (t + 1 < it.len) {
+      const int qb = qblks[t + 1];
+      gload_nat(qr, qbase + (size_t)qb * kBlock * kHead, tid);
+      gload_tr(qtr, qbase + (size_t)qb * kBlock * kHead, tid);
+      gload_nat(dr, dobase + (size_t)qb * kBlock * kHead, tid);
+      gload_tr(dtr, dobase + (size_t)qb * kBlock * kHead, tid);
+      if (tid < kBlock) { lv = lbase[qb * kBlock + tid]; dval = dbase[qb * kBlock + tid]; }
+    }
+    // S[q][key] = Q K^T, dP[q][key] = dO V^T; rows = queries (2 tiles), column = key
+    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 q0 = ld16(sQ + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 q1 = ld16(sQ + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 o0 = ld16(sO + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 o1 = ld16(sO + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      s0 = mfma32(q0, kB[c], s0);
+      s1 = mfma32(q1, kB[c], s1);
+      p0 = mfma32(o0, vB[c], p0);
+      p1 = mfma32(o1, vB[c], p1);
+    }
+    // rows held by this lane: q = 32*qt + 8*j + 4*hl + e
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(sL + 8 * j + 4 * hl);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(sL + 32 + 8 * j + 4 * hl);
+      const f32x4 D0 = *reinterpret_cast<const f32x4*>(sD + 8 * j + 4 * hl);
+      const f32x4 D1 = *reinterpret_cast<const f32x4*>(sD + 32 + 8 * j + 4 * hl);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * j + e;
+        const float e0 = fast_exp2(__builtin_fmaf(s0[r], sl2, -l0[e]));
+        const float e1 = fast_exp2(__builtin_fmaf(s1[r], sl2, -l1[e]));
+        s0[r] = e0;                       // P
+        s1[r] = e1;
+        p0[r] = e0 * (p0[r] - D0[e]);     // dS
+        p1[r] = e1 * (p1[r] - D1[e]);
+      }
+    }
+    // dV^T[d][key] += sum_q dO^T[d][q] P[q][key];  dK^T[d][key] += sum_q Q^T[d][q] dS[q][key]
+    const bf16x8 pc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
+    const bf16x8 dc[4] = {pack8(p0, 0), pack8(p0, 8), pack8(p1, 0), pack8(p1, 8)};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 ot0 = ld16(sOt + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 ot1 = ld16(sOt + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 qt0 = ld16(sQt + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 qt1 = ld16(sQt + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      dv0 = mfma32(ot0, pc[c], dv0);
+      dv1 = mfma32(ot1, pc[c], dv1);
+      dk0 = mfma32(qt0, dc[c], dk0);
+      dk1 = mfma32(qt1, dc[c], dk1);
+    }
+    __syncthreads();
+  }
+
+  const float sc = a.scale;
+  if (it.slot < 0) {
+    const size_t off = bh_off + (size_t)krow * kHead + 4 * hl;
+    uint16_t* kp = a.dk + off;
+    uint16_t* vp = a.dv + off;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 k0w, k1w, v0w, v1w;
+      k0w[0] = pack_bf16x2(dk0[4 * j] * sc, dk0[4 * j + 1] * sc);
+      k0w[1] = pack_bf16x2(dk0[4 * j + 2] * sc, dk0[4 * j + 3] * sc);
+      k1w[0] = pack_bf16x2(dk1[4 * j] * sc, dk1[4 * j + 1] * sc);
+      k1w[1] = pack_bf16x2(dk1[4 * j + 2] * sc, dk1[4 * j + 3] * sc);
+      v0w[0] = pack_bf16x2(dv0[4 * j], dv0[4 * j + 1]);
+      v0w[1] = pack_bf16x2(dv0[4 * j + 2], dv0[4 * j + 3]);
+      v1w[0] = pack_bf16x2(dv1[4 * j], dv1[4 * j + 1]);
+      v1w[1] = pack_bf16x2(dv1[4 * j + 2], dv1[4 * j + 3]);
+      *reinterpret_cast<u32x2*>(kp + 8 * j) = k0w;
+      *reinterpret_cast<u32x2*>(kp + 32 + 8 * j) = k1w;
+      *reinterpret_cast<u32x2*>(vp + 8 * j) = v0w;
+      *reinterpret_cast<u32x2*>(vp + 32 + 8 * j) = v1w;
+    }
+  } else {
+    float* pk = a.part_kv + (size_t)it.slot * 2 * kTile + (32 * wave + col) * kHead + 4 * hl;
+    float* pv = pk + kTile;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 k0w, k1w, v0w, v1w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k0w[e] = dk0[4 * j + e] * sc; k1w[e] = dk1[4 * j + e] * sc;
+        v0w[e] = dv0[4 * j + e]; v1w[e] = dv1[4 * j + e];
+      }
+      *reinterpret_cast<f32x4*>(pk + 8 * j) = k0w;
+      *reinterpret_cast<f32x4*>(pk + 32 + 8 * j) = k1w;
+      *reinterpret_cast<f32x4*>(pv + 8 * j) = v0w;
+      *reinterpret_cast<f32x4*>(pv + 32 + 8 * j) = v1w;
+    }
+  }
+}
+
+// Sum the fp32 partial tiles of split global rows (dQ) and columns (dK, dV) in
+// segment order.  Work-group (bh*g + gi)*3 + kind, kind 0 = dQ, 1 = dK, 2 = dV.
+__global__ __launch_bounds__(256) void bs_bwd_reduce_kernel(
+    const float* __restrict__ part_q, const float* __restrict__ part_kv,
+    const int32_t* __restrict__ gblk, int n, int g, int nseg, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  const int kind = blockIdx.x % 3;
+  const int idx = blockIdx.x / 3;   // bh*g + gi
+  const int bh = idx / g, gi = idx - bh * g;
+  const int e0 = threadIdx.x * 16;  // 16 consecutive floats of the 64x64 tile
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int s = 0; s < nseg; ++s) {
+    const size_t slot = (size_t)idx * nseg + s;
+    const float* src = kind == 0 ? part_q + slot * kTile
+                                 : part_kv + slot * 2 * kTile + (kind - 1) * kTile;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + e0 + e);
+      acc[e] += x[0]; acc[e + 1] += x[1]; acc[e + 2] += x[2]; acc[e + 3] += x[3];
+    }
+  }
+  uint16_t* dst = kind == 0 ? dq : (kind == 1 ? dk : dv);
+  dst += ((size_t)bh * n + (size_t)gblk[gi] * kBlock) * kHead + e0;
+#pragma unroll
+  for (int e = 0; e < 16; e += 8) {
+    u32x4 w;
+    w[0] = pack_bf16x2(acc[e], acc[e + 1]);
+    w[1] = pack_bf16x2(acc[e + 2], acc[e + 3]);
+    w[2] = pack_bf16x2(acc[e + 4], acc[e + 5]);
+    w[3] = pack_bf16x2(acc[e + 6], acc[e + 7]);
+    *reinterpret_cast<u32x4*>(dst + e) = w;
+  }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const bsattn_layout* L, int batch) {
+  size_t bytes = (size_t)batch * L->heads * L->n * sizeof(float);   // D
+  bytes = (bytes + 255) & ~(size_t)255;
+  if (L->split) bytes += (size_t)batch * L->heads * L->g * L->nseg * 3 * kTile * sizeof(float);
+  return bytes;
+}
+
+int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, const void* k,
+               const void* v, const void* o, const float* lse, const void* dout, void* dq,
+               void* dk, void* dv, void* ws, hipStream_t stream) {
+  BwdArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o; a.lse = lse; a.dout = (const uint16_t*)dout;
+  a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
+  char* w = (char*)ws;
+  a.dbuf = (float*)w;
+  size_t off = ((size_t)batch * L->heads * L->n * sizeof(float) + 255) & ~(size_t)255;
+  const size_t nslots = (size_t)batch * L->heads * L->g * L->nseg;
+  a.part_q = L->split ? (float*)(w + off) : nullptr;
+  a.part_kv = L->split ? (float*)(w + off + nslots * kTile * sizeof(float)) : nullptr;
+  a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
+  a.csc_ptr = L->d_csc_ptr; a.csc_idx = L->d_csc_idx;
+  a.gblk = L->d_gblk; a.ngblk = L->d_ngblk;
+  a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
+  a.nseg = L->nseg; a.split = L->split ? 1 : 0;
+  a.items_per_bh = (L->nb - L->g) + L->g * L->nseg;
+  a.total_items = batch * L->heads * a.items_per_bh;
+  a.scale = scale;
+  a.sl2 = scale * kLog2e;
+  const int grid = 8 * ((a.total_items + 7) / 8);
+  hipLaunchKernelGGL(bs_bwd_dq_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  int st = check_hip(hipGetLastError(), "bs_bwd_dq launch");
+  if (st) return st;
+  hipLaunchKernelGGL(bs_bwd_dkdv_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  st = check_hip(hipGetLastError(), "bs_bwd_dkdv launch");
+  if (st || !L->split || L->g == 0) return st;
+  hipLaunchKernelGGL(bs_bwd_reduce_kernel, dim3(batch * L->heads * L->g * 3), dim3(256), 0,
+                     stream, (const float*)a.part_q, (const float*)a.part_kv, L->d_gblk, L->n,
+                     L->g, L->nseg, a.dq, a.dk, a.dv);
+  return check_hip(hipGetLastError(), "bs_bwd_reduce launch");
+}
+
+}  // namespace bsattn

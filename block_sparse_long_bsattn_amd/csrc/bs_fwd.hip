@@ -1,0 +1,281 @@
+// BigBird-ITC block-sparse attention forward on gfx950.
+//
+// Computes, per (batch, head) and query block i, softmax over the keys of the
+// blocks in N(i) of scale * Q K^T, times V ("Big Bird: Transformers for Longer
+// Sequences", §2 eq. (AT) and App. D eq. (13), Fig. 6; scaled scores as in
+// "Longformer: The Long-Document Transformer", §3.1 eq. (1)).
+//
+// Work decomposition (one 128-thread work-group = 2 waves = one 64-row query
+// block; wave w owns query rows 32w .. 32w+31):
+//   * a non-global query block is one item walking its whole key-block list;
+//   * a global query block (a full row, App. D Fig. 6 "direct multiplication")
+//     is split into items of kSeg key blocks that write partial (unnormalised O,
+//     running max, running sum); bs_fwd_combine merges them in a fixed order.
+// Per key block: K (natural) and V (transposed) are staged through LDS; S^T =
+// K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA; the online softmax runs in
+// fp32 registers, one query per lane (column of the accumulator), 32 keys per
+// lane and the other 32 in the partner lane l ^ 32.
+
+#include "attn_tile.hpp"
+#include "internal.hpp"
+
+namespace bsattn {
+namespace {
+
+constexpr int kFwdThreads = 128;
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  float* part;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* gblk;
+  const int32_t* ngblk;
+  int heads, n, nb, g, nseg, split;
+  int items_per_bh, total_items;
+  float sl2;  // scale * log2(e)
+};
+
+struct Item {
+  int bh, h, i, start, len, slot;
+};
+
+__device__ __forceinline__ Item decode_row_item(int v, int heads, int nb, int g, int nseg,
+                                                int split, int ipb, const int32_t* gblk,
+                                                const int32_t* ngblk, const int32_t* row_ptr) {
+  Item it;
+  it.bh = v / ipb;
+  const int r = v - it.bh * ipb;
+  it.h = it.bh % heads;
+  const int ng = nb - g;
+  if (r < ng) {
+    it.i = ngblk[r];
+    it.start = 0;
+    it.len = -1;
+    it.slot = -1;
+  } else {
+    const int gi = (r - ng) / nseg;
+    const int s = (r - ng) - gi * nseg;
+    it.i = gblk[gi];
+    if (split) {
+      it.start = s * kSeg;
+      it.len = min(kSeg, nb - s * kSeg);
+      it.slot = (it.bh * g + gi) * nseg + s;
+    } else {
+      it.start = 0;
+      it.len = -1;
+      it.slot = -1;
+    }
+  }
+  const int64_t rp0 = row_ptr[(int64_t)it.h * nb + it.i];
+  if (it.len < 0) it.len = row_ptr[(int64_t)it.h * nb + it.i + 1] - (int)rp0;
+  it.start += (int)rp0;
+  return it;
+}
+
+__global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[kHead * kLdsStride];
+
+  const int v = xcd_remap(blockIdx.x, a.total_items);
+  if (v >= a.total_items) return;
+  const Item it = decode_row_item(v, a.heads, a.nb, a.g, a.nseg, a.split, a.items_per_bh,
+                                  a.gblk, a.ngblk, a.row_ptr);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const size_t bh_off = (size_t)it.bh * a.n * kHead;
+  const int qrow = it.i * kBlock + 32 * wave + col;   // token index of this lane's query
+
+  bf16x8 qB[4];
+  {
+    const uint16_t* qp = a.q + bh_off + (size_t)qrow * kHead + 8 * hl;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
+  }
+
+  FwdState st;
+  fwd_state_init(st);
+  const float sl2 = a.sl2;
+  const int32_t* keys = a.col_idx + it.start;
+  const uint16_t* kbase = a.k + bh_off;
+  const uint16_t* vbase = a.v + bh_off;
+
+  TileRegs kr, vr;
+  if (it.len > 0) {
+    const int kb = keys[0];
+    gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
+    gload_tr(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+  }
+  for (int t = 0; t < it.len; ++t) {
+    lds_store_nat(sK, kr, tid);
+    lds_store_tr(sVt, vr, tid);
+    __syncthreads();
+    if (t + 1 < it.len) {
+      const int kb = keys[t + 1];
+      gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
+      gload_tr(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+    }
+    f32x16 s0, s1;
+    qk_tile(sK, qB, col, hl, s0, s1);
+    softmax_step(s0, s1, st, sl2);
+    pv_tile(sVt, s0, s1, col, hl, st);
+    __syncthreads();
+  }
+
+  const float l_tot = st.l + __shfl_xor(st.l, 32);
+  if (it.slot < 0) {
+    write_o_bf16(st, l_tot, hl, a.o + bh_off + (size_t)qrow * kHead,
+                 a.lse != nullptr ? a.lse + (size_t)it.bh * a.n + qrow : nullptr);
+  } else {
+    write_partial(st, l_tot, hl, 32 * wave + col, a.part + (size_t)it.slot * kPartFloats);
+  }
+}
+
+// Merge the kSeg-block partials of every split global query block, in segment
+// order: M = max_s m_s, L = sum_s l_s 2^(m_s - M), O = sum_s O_s 2^(m_s - M) / L.
+__global__ __launch_bounds__(256) void bs_fwd_combine_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ gblk, int heads, int n,
+    int g, int nseg, uint16_t* __restrict__ o, float* __restrict__ lse) {
+  const int idx = blockIdx.x;           // (bh, gi)
+  const int bh = idx / g, gi = idx - bh * g;
+  const int row = threadIdx.x >> 2, dq = (threadIdx.x & 3) * 16;
+  float acc[16], M, L;
+  merge_partials(part + (size_t)idx * nseg * kPartFloats, nseg, row, dq, acc, M, L);
+  const int tok = gblk[gi] * kBlock + row;
+  store16_bf16(o + ((size_t)bh * n + tok) * kHead + dq, acc, 1.f / L);
+  if (lse != nullptr && (threadIdx.x & 3) == 0)
+    lse[(size_t)bh * n + tok] = (M + __log2f(L)) * kLn2;
+  (void)heads;
+}
+
+// fp32 path: plain FMA tiles, one 256-thread work-group per query block walking
+// the whole row.  Thread t owns query row t/4 and a quarter (16 keys for the
+// scores, 16 columns for the output).
+struct FwdF32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int heads, n, nb, total_items;
+  float scale;
+};
+
+__global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
+  __shared__ float sK[kBlock][kHead + 1];
+  __shared__ float sV[kBlock][kHead];
+  __shared__ float sP[kBlock][kBlock + 1];
+  const int v = xcd_remap(blockIdx.x, a.total_items);
+  if (v >= a.total_items) return;
+  const int bh = v / a.nb, i = v - bh * a.nb, h = bh % a.heads;
+  const int tid = threadIdx.x, row = tid >> 2, qq = tid & 3;
+  const size_t bh_off = (size_t)bh * a.n * kHead;
+  const int tok = i * kBlock + row;
+  float qv[kHead];
+#pragma unroll
+  for (int c = 0; c < kHead; ++c) qv[c] = a.q[bh_off + (size_t)tok * kHead + c];
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int rp0 = a.row_ptr[(int64_t)h * a.nb + i], rp1 = a.row_ptr[(int64_t)h * a.nb + i + 1];
+  for (int e = rp0; e < rp1; ++e) {
+    const int kb = a.col_idx[e];
+    const float* kp = a.k + bh_off + (size_t)kb * kBlock * kHead;
+    const float* vp = a.v + bh_off + (size_t)kb * kBlock * kHead;
+    __syncthreads();
+    for (int x = tid; x < kBlock * kHead; x += 256) {
+      sK[x / kHead][x % kHead] = kp[x];
+      sV[x / kHead][x % kHead] = vp[x];
+    }
+    __syncthreads();
+    float s[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < kHead; ++c) dot = __builtin_fmaf(qv[c], sK[qq * 16 + kk][c], dot);
+      s[kk] = dot * a.scale;
+      mx = fmaxf(mx, s[kk]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = expf(m - m_new);
+    float rs = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const float p = expf(s[kk] - m_new);
+      sP[row][qq * 16 + kk] = p;
+      rs += p;
+    }
+    l = l * alpha + rs;
+    m = m_new;
+    __syncthreads();
+#pragma unroll
+    for (int e2 = 0; e2 < 16; ++e2) acc[e2] *= alpha;
+    for (int kk = 0; kk < kBlock; ++kk) {
+      const float p = sP[row][kk];
+#pragma unroll
+      for (int e2 = 0; e2 < 16; ++e2) acc[e2] = __builtin_fmaf(p, sV[kk][qq * 16 + e2], acc[e2]);
+    }
+  }
+  l += __shfl_xor(l, 1);
+  l += __shfl_xor(l, 2);
+  const float inv = 1.f / l;
+  float* op = a.o + bh_off + (size_t)tok * kHead + qq * 16;
+#pragma unroll
+  for (int e2 = 0; e2 < 16; ++e2) op[e2] = acc[e2] * inv;
+  if (a.lse != nullptr && qq == 0) a.lse[(size_t)bh * a.n + tok] = m + logf(l);
+}
+
+}  // namespace
+
+size_t fwd_workspace_bytes(const bsattn_layout* L, int batch) {
+  if (!L->split) return 0;
+  return (size_t)batch * L->heads * L->g * L->nseg * kPartFloats * sizeof(float);
+}
+
+int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, const void* q,
+               const void* k, const void* v, void* o, float* lse, void* ws, hipStream_t stream) {
+  const int bhn = batch * L->heads;
+  if (dt == BSATTN_F32) {
+    FwdF32Args a;
+    a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;
+    a.o = (float*)o; a.lse = lse;
+    a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
+    a.heads = L->heads; a.n = L->n; a.nb = L->nb;
+    a.total_items = bhn * L->nb;
+    a.scale = scale;
+    const int grid = 8 * ((a.total_items + 7) / 8);
+    hipLaunchKernelGGL(bs_fwd_f32_kernel, dim3(grid), dim3(256), 0, stream, a);
+    return check_hip(hipGetLastError(), "bs_fwd_f32 launch");
+  }
+  FwdArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o; a.lse = lse; a.part = (float*)ws;
+  a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
+  a.gblk = L->d_gblk; a.ngblk = L->d_ngblk;
+  a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
+  a.nseg = L->nseg; a.split = L->split ? 1 : 0;
+  a.items_per_bh = (L->nb - L->g) + L->g * L->nseg;
+  a.total_items = bhn * a.items_per_bh;
+  a.sl2 = scale * kLog2e;
+  const int grid = 8 * ((a.total_items + 7) / 8);
+  hipLaunchKernelGGL(bs_fwd_bf16_kernel, dim3(grid), dim3(kFwdThreads), 0, stream, a);
+  int st = check_hip(hipGetLastError(), "bs_fwd_bf16 launch");
+  if (st || !L->split || L->g == 0) return st;
+  hipLaunchKernelGGL(bs_fwd_combine_kernel, dim3(bhn * L->g), dim3(256), 0, stream,
+                     (const float*)ws, L->d_gblk, L->heads, L->n, L->g, L->nseg,
+                     (uint16_t*)o, lse);
+  return check_hip(hipGetLastError(), "bs_fwd_combine launch");
+}
+
+}  // namespace bsattn

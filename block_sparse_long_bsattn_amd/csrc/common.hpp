@@ -1,0 +1,142 @@
+// Shared device and host helpers for the gfx950 attention kernels.
+//
+// Tile conventions used by every kernel in this library (CDNA4, wave64):
+//
+// * One 32x32x16 bf16 MFMA computes C[m][n] += sum_k A[m][k] B[k][n].  Lane l
+//   supplies A row (l % 32) and B column (l % 32), eight k-values each, taken
+//   from k-slots (l / 32, e), e = 0..7.  Which k index a slot stands for does not
+//   matter as long as A and B agree, because the product sums over all slots.
+// * The 16 accumulator registers of lane l hold column (l % 32) and rows
+//   8*(r/4) + 4*(l/32) + (r%4), r = 0..15.
+// * A contraction over a 64-long block dimension (keys or queries) whose
+//   operand comes out of a previous MFMA accumulator therefore pairs register
+//   r = 8c' + e of tile t with k-slot e of chunk 2t + c'.  The index it stands
+//   for is 16c + 8jj + 4h + i with c = 2t + c', e = 4jj + i, h = l / 32.  The
+//   matching operand read from LDS stores index x at position perm16(x), which
+//   swaps bits 2 and 3 of x, so that each lane reads eight contiguous values.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsattn {
+
+constexpr int kBlock = 64;   // tokens per block (b) and per Longformer tile
+constexpr int kHead = 64;    // head dimension (d)
+constexpr int kSeg = 8;      // key blocks per work item of a split full row
+constexpr int kLdsStride = 72;  // bf16 elements per LDS tile row (64 + 8 pad)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int perm16(int x) {
+  // swap bits 2 and 3
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;   // round to nearest even
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Eight consecutive accumulator registers, rounded to bf16, as one MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+  u32x4 u;
+  u[0] = pack_bf16x2(s[base + 0], s[base + 1]);
+  u[1] = pack_bf16x2(s[base + 2], s[base + 3]);
+  u[2] = pack_bf16x2(s[base + 4], s[base + 5]);
+  u[3] = pack_bf16x2(s[base + 6], s[base + 7]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bf16x8 ld16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Cooperative 64x64 bf16 tile staging through LDS (128 threads).
+//
+// Natural copy: LDS row x holds global row x (64 values + pad).  Thread t moves
+// 16-byte chunk (t % 8) of rows (t / 8) + 16u, u = 0..3.
+// Transposed copy: LDS row c (a column of the global tile) holds, at position
+// perm16(x), the value of global row x.  Thread t moves rows 4*(t / 8) .. +3,
+// columns 8*(t % 8) .. +7.
+// ---------------------------------------------------------------------------
+
+struct TileRegs { u32x4 v[4]; };
+
+__device__ __forceinline__ void gload_nat(TileRegs& r, const uint16_t* g, int tid) {
+  const int c = tid & 7, row = tid >> 3;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) r.v[u] = ldg16(g + (row + 16 * u) * kHead + 8 * c);
+}
+
+__device__ __forceinline__ void lds_store_nat(uint16_t* s, const TileRegs& r, int tid) {
+  const int c = tid & 7, row = tid >> 3;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    *reinterpret_cast<u32x4*>(s + (row + 16 * u) * kLdsStride + 8 * c) = r.v[u];
+}
+
+__device__ __forceinline__ void gload_tr(TileRegs& r, const uint16_t* g, int tid) {
+  const int c = tid & 7, x0 = 4 * (tid >> 3);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) r.v[u] = ldg16(g + (x0 + u) * kHead + 8 * c);
+}
+
+__device__ __forceinline__ void lds_store_tr(uint16_t* s, const TileRegs& r, int tid) {
+  const int c = tid & 7, x0 = 4 * (tid >> 3);
+  const int pos = perm16(x0);   // x0..x0+3 map to pos..pos+3 (bits 0,1 untouched)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    // column 8c+e: four rows x0..x0+3
+    const int w = e >> 1, hi = e & 1;
+    uint32_t a0 = hi ? (r.v[0][w] >> 16) : (r.v[0][w] & 0xffffu);
+    uint32_t a1 = hi ? (r.v[1][w] >> 16) : (r.v[1][w] & 0xffffu);
+    uint32_t a2 = hi ? (r.v[2][w] >> 16) : (r.v[2][w] & 0xffffu);
+    uint32_t a3 = hi ? (r.v[3][w] >> 16) : (r.v[3][w] & 0xffffu);
+    u32x2 pk;
+    pk[0] = a0 | (a1 << 16);
+    pk[1] = a2 | (a3 << 16);
+    *reinterpret_cast<u32x2*>(s + (8 * c + e) * kLdsStride + pos) = pk;
+  }
+}
+
+// XCD-aware work mapping: the dispatcher hands consecutive work-groups to the 8
+// XCDs in turn; remap so that each XCD walks one contiguous range of items (and
+// so reuses the K/V blocks of the same heads from its own L2).
+__device__ __forceinline__ int xcd_remap(int g, int total) {
+  const int per = (total + 7) / 8;
+  return (g & 7) * per + (g >> 3);
+}
+
+}  // namespace bsattn

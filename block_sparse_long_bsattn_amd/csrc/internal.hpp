@@ -1,0 +1,66 @@
+// Host-side internals shared by the translation units of libbsattn.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/bsattn.h"
+
+struct bsattn_layout {
+  int n = 0, b = 0, nb = 0, heads = 0, g = 0, w = 0, r = 0;
+  uint64_t seed = 0;
+  int device = 0;
+  int64_t nnz_per_head = 0;      // same for every head (row lengths do not depend on h)
+  std::vector<int32_t> gblk;     // global blocks (host copy)
+  std::vector<int32_t> ngblk;    // non-global blocks ascending (host copy)
+  std::vector<int32_t> row_len;  // length of each query-block row (host copy)
+  int nseg = 1;                  // work items per split (global) row / column
+  bool split = false;            // global rows and columns are split into kSeg items
+  // device arrays (owned)
+  int32_t* d_gblk = nullptr;     // [g]
+  int32_t* d_ngblk = nullptr;    // [nb - g] non-global block ids, ascending
+  int32_t* d_row_ptr = nullptr;  // [heads*nb + 1]
+  int32_t* d_col_idx = nullptr;  // [heads*nnz_per_head]
+  int32_t* d_csc_ptr = nullptr;  // [heads*nb + 1]
+  int32_t* d_csc_idx = nullptr;  // [heads*nnz_per_head]
+};
+
+struct lfattn_plan {
+  int n = 0, w1 = 0, ng = 0, nt = 0, ngt = 0;  // tokens, window per side, globals, tiles
+  int device = 0;
+  int nseg = 1;                  // items per packed global query tile
+  int32_t* d_gtok = nullptr;     // [ng] global positions ascending
+  int32_t* d_gidx = nullptr;     // [n] index into d_gtok, or -1 for non-global tokens
+  uint64_t* d_tile_gmask = nullptr;  // [nt] bit x set iff token 64*t + x is global
+  std::vector<int32_t> gtok;     // host copies backing the build-time uploads
+  std::vector<int32_t> gidx;
+  std::vector<uint64_t> tile_gmask;
+};
+
+namespace bsattn {
+
+int set_error(int status, const std::string& msg);
+void clear_error();
+int check_hip(hipError_t e, const char* what);
+
+// Launch helpers implemented in the kernel translation units.
+int launch_layout_build(bsattn_layout* L, hipStream_t stream);
+int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale,
+               const void* q, const void* k, const void* v, void* o, float* lse,
+               void* ws, hipStream_t stream);
+int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q,
+               const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* ws,
+               hipStream_t stream);
+int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
+                  const void* k, const void* v, void* o, float* lse, void* ws,
+                  hipStream_t stream);
+
+size_t fwd_workspace_bytes(const bsattn_layout* L, int batch);
+size_t bwd_workspace_bytes(const bsattn_layout* L, int batch);
+size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads);
+
+}  // namespace bsattn

@@ -1,0 +1,222 @@
+/*
+ * bsattn.h -- C ABI of libbsattn.so: block-sparse (BigBird-ITC) and banded
+ * (Longformer) self-attention on AMD Instinct MI355X (gfx950).
+ *
+ * The library takes per-head, post-projection Q, K, V and computes the attention
+ * of each head over a sparse pattern.  Projections, the sum over heads and the
+ * residual connection stay with the caller.
+ *
+ * Sources for what is computed:
+ *   [BB]  "Big Bird: Transformers for Longer Sequences": §2 eq. (AT) (attention of
+ *         query i over a key set N(i)); §2 "global tokens" (global tokens attend to
+ *         all tokens and all tokens attend to them); App. D "Implementation details"
+ *         with eq. (13), Fig. 4 and Fig. 6 (sparsity on b x b blocks; each query
+ *         block sees the global blocks, w window blocks and r random blocks; the
+ *         global row-block is a full row); hyper-parameter table of App. E
+ *         (b = 64, g = 2b, w = 3b, r = 3b).
+ *   [BW]  Chinese walkthrough of Big Bird (gitcode.csdn.net), §2.1-2.3 (r random
+ *         keys per query, w/2 neighbours per side, g global tokens) and §4.2.
+ *   [LF]  "Longformer: The Long-Document Transformer": §3.1 "Sliding Window" (w/2
+ *         tokens per side), "Global Attention" (symmetric attention on preselected
+ *         positions), eq. (1) (softmax(Q K^T / sqrt(d_k)) V); §3.2 and App. A
+ *         (banded matrix product).
+ *
+ * Conventions for every call
+ *   - Tensors are dense row-major [batch, heads, n, d] with d fastest; element
+ *     type given by bsattn_dtype (bf16 = raw 16-bit bfloat16 bits).
+ *   - lse is float32 [batch, heads, n], natural-log log-sum-exp of the scaled
+ *     scores of each query row over its allowed keys.
+ *   - Accumulation and softmax run in fp32; outputs are rounded (nearest-even) to
+ *     the input type.
+ *   - Device pointers must be 16-byte aligned.  All device work is enqueued on
+ *     `stream` and is asynchronous unless a function says otherwise.
+ *   - The caller owns every tensor and every workspace.  Compute calls never
+ *     allocate.  Handles (bsattn_layout, lfattn_plan) own their own small device
+ *     arrays, allocated at build time and freed by the matching destroy call; a
+ *     built handle is read-only for compute calls and may be shared by streams.
+ *   - Errors are returned as negative bsattn_status codes; nothing is thrown
+ *     across the ABI.  Arguments are checked on the host before any launch;
+ *     bsattn_last_error() returns a message for the calling thread's last error.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSATTN_OK = 0,
+  BSATTN_EINVAL = -1,       /* bad argument: shape, pattern, pointer, workspace size */
+  BSATTN_EUNSUPPORTED = -2, /* valid but not built: block size, head dim, dtype     */
+  BSATTN_EHIP = -3,         /* a HIP runtime call or kernel launch failed           */
+  BSATTN_ENOMEM = -4        /* device allocation failed while building a handle     */
+} bsattn_status;
+
+typedef enum { BSATTN_F32 = 0, BSATTN_BF16 = 1 } bsattn_dtype;
+
+/* ------------------------------------------------------------------------- */
+/* BigBird-ITC block layout                                                   */
+/* ------------------------------------------------------------------------- */
+
+typedef struct bsattn_layout bsattn_layout;
+
+/*
+ * Build the block layout of [BB] App. D on the device: for every head h and query
+ * block i (nb = n / b blocks), the ascending key-block list
+ *     N(i) = G  U  W_i  U  R_i      for i not in G,      N(i) = {0..nb-1} for i in G,
+ * where G = global_blocks, W_i = { j : |i - j| <= (w-1)/2, 0 <= j < nb } and R_i
+ * holds min(r, m) blocks drawn uniformly without replacement from the m blocks not
+ * in G U W_i.  The draw is a partial Fisher-Yates over the ascending candidate
+ * list, step t (t = 0..) swapping entries t and t + (u mod (m - t)), where u is
+ * SplitMix64 output number (h*nb + i)*r + t + 1 of the stream seeded with `seed`.
+ * The transpose (for each key block, the ascending list of query blocks that see
+ * it) is built too.  One layout serves every batch element.
+ *
+ *   n, b            sequence length and block size; b must be 64 (else
+ *                   EUNSUPPORTED), n a positive multiple of b with n/b <= 4096.
+ *   heads           number of heads, >= 1; each head draws its own random blocks.
+ *   global_blocks   HOST array of g block ids, sorted, unique, in [0, n/b);
+ *                   may be NULL when g == 0.
+ *   w               window width in blocks, odd, >= 1.
+ *   r               random blocks per query block, 0 <= r <= 64.
+ *   seed            64-bit generator seed.
+ *   stream          stream for the build kernels.
+ *   out             receives the handle.  The build is asynchronous; the handle
+ *                   may be used by later work on `stream` at once.
+ * Returns OK, EINVAL, EUNSUPPORTED, ENOMEM or EHIP.
+ */
+int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, int g,
+                        int w, int r, uint64_t seed, hipStream_t stream,
+                        bsattn_layout** out);
+
+/* Redraw the random blocks of an existing layout with a new seed, in place, on
+ * `stream`.  No allocation.  Work already enqueued with the old layout on other
+ * streams must have finished.  Returns OK, EINVAL or EHIP. */
+int bsattn_layout_rebuild(bsattn_layout* layout, uint64_t seed, hipStream_t stream);
+
+/* Sizes of a layout: blocks per head, heads, and total stored block pairs over all
+ * heads (the length of col_idx and of csc_idx).  Any output pointer may be NULL. */
+int bsattn_layout_info(const bsattn_layout* layout, int* nb, int* heads,
+                       int64_t* nnzb_total);
+
+/*
+ * Copy a layout to host memory (synchronous; waits for the build).
+ *   row_ptr [heads*nb + 1]  head h, query block i: keys at col_idx[row_ptr[h*nb+i] ..
+ *                           row_ptr[h*nb+i+1]), ascending.
+ *   col_idx [nnzb_total]
+ *   csc_ptr [heads*nb + 1]  head h, key block j: queries at csc_idx[csc_ptr[h*nb+j] ..
+ *                           csc_ptr[h*nb+j+1]), ascending.
+ *   csc_idx [nnzb_total]
+ * Any pointer may be NULL to skip that array.  Returns OK, EINVAL or EHIP.
+ */
+int bsattn_layout_to_host(const bsattn_layout* layout, int32_t* row_ptr, int32_t* col_idx,
+                          int32_t* csc_ptr, int32_t* csc_idx);
+
+/* Free a layout (synchronises the device first).  NULL is accepted. */
+int bsattn_layout_destroy(bsattn_layout* layout);
+
+/* ------------------------------------------------------------------------- */
+/* BigBird-ITC forward and backward                                           */
+/* ------------------------------------------------------------------------- */
+
+/* Workspace bytes bsattn_fwd / bsattn_bwd need for this layout and batch (may be
+ * 0).  d must be 64.  Returns 0 for invalid arguments as well. */
+size_t bsattn_fwd_workspace(const bsattn_layout* layout, int batch, int d);
+size_t bsattn_bwd_workspace(const bsattn_layout* layout, int batch, int d);
+
+/*
+ * Forward ([BB] eq. (AT) inner part, per head; scores scaled as in [LF] eq. (1)):
+ *   O[p] = sum_{q : block(q) in N(block(p))} softmax_q(scale * Q[p].K[q]) V[q]
+ *   lse[p] = log sum_q exp(scale * Q[p].K[q]) over the same keys.
+ * Rows of global query blocks are full rows ([BB] Fig. 6 "direct multiplication").
+ *
+ *   layout      built layout (heads and n taken from it).
+ *   batch       >= 1.
+ *   d           head dimension; must be 64.
+ *   dt          BSATTN_BF16 (bf16 MFMA products, fp32 softmax) or BSATTN_F32.
+ *   scale       score scale, e.g. 1/sqrt(d).
+ *   q, k, v     DEVICE [batch, heads, n, d] of type dt.
+ *   o           DEVICE [batch, heads, n, d] of type dt, written.
+ *   lse         DEVICE float32 [batch, heads, n], written; may be NULL.
+ *   workspace   DEVICE scratch of at least bsattn_fwd_workspace() bytes (NULL if 0).
+ * Returns OK, EINVAL, EUNSUPPORTED or EHIP.
+ */
+int bsattn_fwd(const bsattn_layout* layout, int batch, int d, bsattn_dtype dt, float scale,
+               const void* q, const void* k, const void* v, void* o, float* lse,
+               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward: the exact gradient of bsattn_fwd for the loss <dout, O>.
+ *   q, k, v, o  DEVICE [batch, heads, n, d] (o from bsattn_fwd).
+ *   lse         DEVICE float32 [batch, heads, n] from bsattn_fwd (required).
+ *   dout        DEVICE [batch, heads, n, d].
+ *   dq, dk, dv  DEVICE [batch, heads, n, d], written.
+ *   workspace   DEVICE scratch of at least bsattn_bwd_workspace() bytes.
+ * dK and dV of each key block are accumulated by the one work-group that owns it,
+ * walking the transposed layout; dQ by the owner of the query block.  No atomics,
+ * so results are bitwise reproducible.  dt must be BSATTN_BF16 (else
+ * EUNSUPPORTED).  Returns OK, EINVAL, EUNSUPPORTED or EHIP.
+ */
+int bsattn_bwd(const bsattn_layout* layout, int batch, int d, bsattn_dtype dt, float scale,
+               const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Longformer sliding window + symmetric global attention                     */
+/* ------------------------------------------------------------------------- */
+
+typedef struct lfattn_plan lfattn_plan;
+
+/*
+ * Plan for [LF] §3.1: token p attends to token q iff |p - q| <= window_one_side,
+ * or p is global, or q is global (window clipped at the sequence ends).
+ *   n                sequence length, positive multiple of 64, <= 262144.
+ *   window_one_side  keys per side, >= 0 (the token itself is always included).
+ *   global_tokens    HOST array of n_global positions, sorted, unique, in [0, n);
+ *                    may be NULL when n_global == 0.
+ * The plan copies the global set to the device on `stream`.  Returns OK, EINVAL,
+ * ENOMEM or EHIP.
+ */
+int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens,
+                      int n_global, hipStream_t stream, lfattn_plan** out);
+
+/* Free a plan (synchronises the device first).  NULL is accepted. */
+int lfattn_plan_destroy(lfattn_plan* plan);
+
+/* Workspace bytes lfattn_fwd needs.  d must be 64.  0 for invalid arguments. */
+size_t lfattn_fwd_workspace(const lfattn_plan* plan, int batch, int heads, int d);
+
+/*
+ * Longformer forward: O and lse as in bsattn_fwd, with the plan's token pattern.
+ * Query rows of global tokens are full rows.  q, k, v, o are DEVICE [batch, heads,
+ * n, d]; lse DEVICE float32 [batch, heads, n] or NULL.  dt must be BSATTN_BF16.
+ * Returns OK, EINVAL, EUNSUPPORTED or EHIP.
+ */
+int lfattn_fwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,
+               float scale, const void* q, const void* k, const void* v, void* o,
+               float* lse, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Diagnostics                                                                */
+/* ------------------------------------------------------------------------- */
+
+/* Static name of a status code. */
+const char* bsattn_status_str(int status);
+
+/* Message for the calling thread's most recent error ("" if none). */
+const char* bsattn_last_error(void);
+
+/* Library version string. */
+const char* bsattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

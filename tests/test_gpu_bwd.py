@@ -1,0 +1,90 @@
+"""GPU block-sparse backward vs the fp64 oracle's exact gradient."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_bsattn_amd import _lib as B
+from block_sparse_long_bsattn_amd import inputs as I
+from oracle import attention as OA
+from gpu_util import BF16_TOL, max_abs, qkv, say, to_f64
+from test_gpu_fwd import oracle_mask
+
+pytestmark = pytest.mark.gpu
+
+
+def run_bwd(n, heads, bsz, G, w, r, seed):
+    shape = (bsz, heads, n, 64)
+    (q, k, v, do), (qr, kr, vr, dor) = qkv(shape, "bf16",
+                                          (I.SEED_Q, I.SEED_K, I.SEED_V, I.SEED_DO))
+    h = B.bsattn_layout_build(n, 64, heads, G, w, r, seed)
+    try:
+        o = torch.empty_like(q)
+        lse = torch.empty((bsz, heads, n), dtype=torch.float32, device="cuda")
+        wsf = torch.empty(max(1, B.bsattn_fwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(1, B.bsattn_bwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        B.bsattn_fwd(h, q, k, v, o, lse, wsf)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        B.bsattn_bwd(h, q, k, v, o, lse, do, dq, dk, dv, wsb)
+        torch.cuda.synchronize()
+    finally:
+        B.bsattn_layout_destroy(h)
+    return (qr, kr, vr, dor), (to_f64(dq), to_f64(dk), to_f64(dv))
+
+
+@pytest.mark.parametrize("case", [
+    (1024, 2, 2, [0, 15], 3, 3),      # split global rows and columns
+    (768, 2, 1, [0, 11], 3, 3),       # ragged last segment
+    (512, 1, 2, [0, 7], 3, 3),        # unsplit
+    (640, 2, 1, [], 3, 4),            # no global blocks
+    (64, 1, 2, [0], 1, 3),            # single block
+    (576, 2, 1, [4], 5, 2),           # interior global block, wider window
+    (1536, 1, 1, [0, 5, 23], 3, 20),  # many random blocks
+])
+def test_bwd_full_compare(case):
+    n, heads, bsz, G, w, r = case
+    say(f"bwd full-compare n={n} H={heads} B={bsz} G={G} w={w} r={r}")
+    (qr, kr, vr, dor), got = run_bwd(n, heads, bsz, G, w, r, 21)
+    mask, _ = oracle_mask(n, heads, G, w, r, 21)
+    ref = OA.attention_bwd(qr, kr, vr, dor, mask, 1 / 8.0)
+    errs = [max_abs(a, b) for a, b in zip(got, ref)]
+    say(f"   max-abs dQ {errs[0]:.3e} dK {errs[1]:.3e} dV {errs[2]:.3e}")
+    assert max(errs) <= BF16_TOL
+
+
+def test_bwd_full_size_sampled():
+    """batch 4, 12 heads, n = 4096, G = {0, 63}, w = 3, r = 3: the whole job runs on
+    the GPU; three (batch, head) slices are compared in full with the oracle."""
+    n, heads, bsz, G = 4096, 12, 4, [0, 63]
+    say("bwd full-size n=4096 H=12 B=4")
+    (qr, kr, vr, dor), got = run_bwd(n, heads, bsz, G, 3, 3, I.SEED_LAYOUT)
+    mask, _ = oracle_mask(n, heads, G, 3, 3, I.SEED_LAYOUT)
+    worst = 0.0
+    for bi, h in ((0, 0), (1, 5), (3, 11)):
+        sl = (slice(bi, bi + 1), slice(h, h + 1))
+        ref = OA.attention_bwd(qr[sl], kr[sl], vr[sl], dor[sl],
+                               lambda hh, p0, p1: mask(h, p0, p1), 1 / 8.0, row_chunk=1024)
+        for a, b in zip(got, ref):
+            worst = max(worst, max_abs(a[bi, h], b[0, 0]))
+    say(f"   worst max-abs {worst:.3e}")
+    assert worst <= BF16_TOL
+
+
+def test_bwd_gradient_sum_identities():
+    """Rows of P sum to 1 and rows of dS to 0, so per (batch, head) the dV rows sum
+    to the dO rows and the dK rows sum to zero."""
+    n, heads, bsz = 2048, 2, 2
+    (qr, kr, vr, dor), (dq, dk, dv) = run_bwd(n, heads, bsz, [0, 31], 3, 3, 8)
+    e_v = max_abs(dv.sum(2), dor.sum(2))
+    e_k = float(np.max(np.abs(dk.sum(2))))
+    say(f"   sum identities: dV {e_v:.3e} dK {e_k:.3e}")
+    assert e_v <= 0.5 and e_k <= 0.5      # sums over 2048 rows of bf16-rounded values
+
+
+def test_bwd_deterministic():
+    _, a = run_bwd(1024, 2, 2, [0, 15], 3, 3, 4)
+    _, b = run_bwd(1024, 2, 2, [0, 15], 3, 3, 4)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

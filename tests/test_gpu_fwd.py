@@ -1,0 +1,177 @@
+"""GPU block-sparse forward vs the fp64 oracle.
+
+Small and medium patterns are compared element by element over every output;
+the full-size workloads are compared on whole (batch, head) slices and on sampled
+query rows of every slice.  Tolerances: max-abs 1e-5 for fp32 inputs, 2e-2 for
+bf16 inputs with fp32 accumulation.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_bsattn_amd import _lib as B
+from block_sparse_long_bsattn_amd import inputs as I
+from oracle import attention as OA
+from oracle import layout as OL
+from gpu_util import BF16_TOL, F32_TOL, max_abs, qkv, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(n, heads, bsz, G, w, r, seed, dtype, zero_q=False, ones_v=False):
+    shape = (bsz, heads, n, 64)
+    (q, k, v), (qr, kr, vr) = qkv(shape, dtype)
+    if zero_q:
+        q.zero_()
+        qr = np.zeros(shape)
+    if ones_v:
+        v.fill_(1.0)
+        vr = np.ones(shape)
+    h = B.bsattn_layout_build(n, 64, heads, G, w, r, seed)
+    try:
+        o = torch.empty_like(q)
+        lse = torch.empty((bsz, heads, n), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, B.bsattn_fwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        B.bsattn_fwd(h, q, k, v, o, lse, ws, scale=1 / math.sqrt(64))
+        torch.cuda.synchronize()
+    finally:
+        B.bsattn_layout_destroy(h)
+    return (qr, kr, vr), to_f64(o), to_f64(lse)
+
+
+def oracle_mask(n, heads, G, w, r, seed):
+    lay = OL.build_layout(n, 64, heads, G, w, r, seed)
+    nb = n // 64
+    rows = lay["rows"]
+
+    def mask(h, p0, p1):
+        blocks = np.zeros((p1 - p0, nb), dtype=bool)
+        for p in range(p0, p1):
+            blocks[p - p0, rows[h][p // 64]] = True
+        return np.repeat(blocks, 64, axis=1)
+    return mask, lay
+
+
+def check_full(n, heads, bsz, G, w, r, seed, dtype="bf16"):
+    say(f"fwd full-compare n={n} H={heads} B={bsz} G={G} w={w} r={r} {dtype}")
+    (qr, kr, vr), o, lse = run_fwd(n, heads, bsz, G, w, r, seed, dtype)
+    mask, _ = oracle_mask(n, heads, G, w, r, seed)
+    ro, rl = OA.attention_fwd(qr, kr, vr, mask, 1 / math.sqrt(64))
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    err_o, err_l = max_abs(o, ro), max_abs(lse, rl)
+    say(f"   max|dO|={err_o:.3e} max|dlse|={err_l:.3e}")
+    assert err_o <= tol
+    assert err_l <= tol
+
+
+def test_fwd_fp32_512_full_size():
+    """fp32, batch 1, 1 head, n = 512, G = {0, 7}, w = 3, r = 3."""
+    check_full(512, 1, 1, [0, 7], 3, 3, I.SEED_LAYOUT, dtype="f32")
+
+
+@pytest.mark.parametrize("case", [
+    (1024, 3, 2, [0, 15], 3, 3),      # 16 blocks: global rows split into 2 items
+    (768, 2, 2, [0, 11], 3, 3),       # 12 blocks: ragged last segment (8 + 4)
+    (576, 2, 1, [4], 3, 2),           # 9 blocks, interior global block
+    (512, 2, 2, [0, 7], 3, 3),        # 8 blocks: global rows not split
+    (640, 2, 1, [], 1, 0),            # block diagonal only
+    (640, 2, 1, [], 3, 4),            # no global blocks
+    (64, 2, 3, [0], 1, 3),            # a single block
+    (64, 1, 1, [], 1, 0),             # a single block, nothing global
+    (1024, 1, 1, [0], 31, 3),         # window covers every block
+    (640, 2, 1, list(range(10)), 1, 0),   # every block global
+    (1536, 2, 1, [0, 5, 23], 5, 20),  # r beyond the candidates of most rows
+])
+def test_fwd_bf16_full_compare(case):
+    n, heads, bsz, G, w, r = case
+    check_full(n, heads, bsz, G, w, r, 77)
+
+
+def test_fwd_fp32_other_shapes():
+    check_full(1024, 2, 1, [0, 15], 3, 3, 5, dtype="f32")
+    check_full(64, 1, 1, [0], 1, 3, 5, dtype="f32")
+
+
+@pytest.mark.parametrize("cfg", [
+    # n, heads, batch, G   (4096: 2 x 12 heads; 16384: 16 heads)
+    (4096, 12, 2, [0, 63]),
+    (16384, 16, 1, [0, 255]),
+])
+def test_fwd_bf16_full_size_sampled(cfg):
+    n, heads, bsz, G = cfg
+    say(f"fwd full-size n={n} H={heads} B={bsz}")
+    (qr, kr, vr), o, lse = run_fwd(n, heads, bsz, G, 3, 3, I.SEED_LAYOUT, "bf16")
+    mask, _ = oracle_mask(n, heads, G, 3, 3, I.SEED_LAYOUT)
+    rng = np.random.default_rng(n)
+    worst = 0.0
+    # two whole slices
+    for bi, h in ((0, 0), (bsz - 1, heads - 1)):
+        ro, rl = OA.attention_fwd(qr[bi:bi + 1, h:h + 1], kr[bi:bi + 1, h:h + 1],
+                                  vr[bi:bi + 1, h:h + 1], lambda hh, p0, p1: mask(h, p0, p1),
+                                  1 / 8.0, row_chunk=1024)
+        worst = max(worst, max_abs(o[bi, h], ro[0, 0]), max_abs(lse[bi, h], rl[0, 0]))
+    # sampled rows of every slice: a global row, the ends and random interior rows
+    for bi in range(bsz):
+        for h in range(heads):
+            rows = np.unique(np.r_[0, 63, 64, n - 65, n - 1, rng.integers(0, n, 8)])
+            ro, rl = OA.attention_fwd_rows(qr, kr, vr, mask, 1 / 8.0, bi, h, rows)
+            worst = max(worst, max_abs(o[bi, h, rows], ro), max_abs(lse[bi, h, rows], rl))
+    say(f"   worst max-abs {worst:.3e}")
+    assert worst <= BF16_TOL
+
+
+def test_fwd_zero_queries_closed_form():
+    """Q = 0: every score is exactly 0 and every probability exactly 1/|keys|, so O is
+    the plain mean of the allowed value rows (fp32 sums) and lse = ln(64 |N(i)|);
+    this pins the mask independently of the exponential."""
+    n, heads, G = 2048, 3, [0, 31]
+    (qr, kr, vr), o, lse = run_fwd(n, heads, 1, G, 3, 3, 9, "bf16", zero_q=True)
+    lay = OL.build_layout(n, 64, heads, G, 3, 3, 9)
+    worst_o = worst_l = 0.0
+    for h in range(heads):
+        for i in range(n // 64):
+            keys = lay["rows"][h][i]
+            idx = np.concatenate([np.arange(64 * j, 64 * j + 64) for j in keys])
+            mean = vr[0, h, idx].mean(0)
+            worst_o = max(worst_o, max_abs(o[0, h, 64 * i:64 * i + 64], np.broadcast_to(mean, (64, 64))))
+            worst_l = max(worst_l, float(np.max(np.abs(lse[0, h, 64 * i:64 * i + 64] - math.log(64 * len(keys))))))
+    say(f"   Q=0: max|dO|={worst_o:.3e} max|dlse|={worst_l:.3e}")
+    assert worst_o <= 2e-3       # output rounded to bf16: half an ulp of |mean| << 1
+    assert worst_l <= 1e-5
+
+
+def test_fwd_unit_values():
+    """V = 1 gives O = 1 (within the bf16 rounding of the probabilities)."""
+    n, heads = 1024, 2
+    _, o, _ = run_fwd(n, heads, 1, [0, 15], 3, 3, 3, "bf16", ones_v=True)
+    assert np.max(np.abs(o - 1.0)) <= 4e-3
+
+
+def test_fwd_deterministic():
+    n, heads, G = 2048, 2, [0, 31]
+    _, o1, l1 = run_fwd(n, heads, 2, G, 3, 3, 4, "bf16")
+    _, o2, l2 = run_fwd(n, heads, 2, G, 3, 3, 4, "bf16")
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_fwd_rejects_wrong_shapes():
+    h = B.bsattn_layout_build(512, 64, 2, [0], 3, 3, 1)
+    try:
+        q = torch.zeros((1, 2, 512, 64), dtype=torch.bfloat16, device="cuda")
+        bad = torch.zeros((1, 2, 448, 64), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(ValueError):
+            B.bsattn_fwd(h, q, bad, q, torch.empty_like(q))
+        with pytest.raises(ValueError):
+            B.bsattn_fwd(h, q, q, q, torch.empty_like(q), workspace=None,
+                         lse=torch.empty((1, 2, 500), device="cuda"))
+        # the C ABI itself rejects a short workspace and a bad scale
+        lib = B.load()
+        assert lib.bsattn_fwd(h, 1, 64, 1, -1.0, q.data_ptr(), q.data_ptr(), q.data_ptr(),
+                              q.data_ptr(), None, None, 0, None) == B.BSATTN_EINVAL
+        assert lib.bsattn_fwd(h, 1, 32, 1, 0.1, q.data_ptr(), q.data_ptr(), q.data_ptr(),
+                              q.data_ptr(), None, None, 0, None) == B.BSATTN_EUNSUPPORTED
+    finally:
+        B.bsattn_layout_destroy(h)
