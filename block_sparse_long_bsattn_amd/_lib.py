@@ -29,7 +29,7 @@ EXPORTS = (
     "bsattn_layout_to_host", "bsattn_layout_destroy", "bsattn_fwd_workspace",
     "bsattn_bwd_workspace", "bsattn_fwd", "bsattn_bwd", "lfattn_plan_build",
     "lfattn_plan_destroy", "lfattn_fwd_workspace", "lfattn_fwd", "bsattn_status_str",
-    "bsattn_last_error", "bsattn_version",
+    "bsattn_last_error", "bsattn_version", "bsattn_profile_enable", "bsattn_profile_read",
 )
 
 
@@ -75,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bsattn_status_str": (c_char_p, [c_int]),
         "bsattn_last_error": (c_char_p, []),
         "bsattn_version": (c_char_p, []),
+        "bsattn_profile_enable": (c_int, [c_int]),
+        "bsattn_profile_read": (c_int, [c_int, c_void_p, c_void_p, c_void_p, POINTER(c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -277,3 +279,23 @@ def bsattn_last_error() -> str:
 
 def bsattn_version() -> str:
     return load().bsattn_version().decode()
+
+
+def bsattn_profile_enable(on: bool) -> None:
+    _check(load().bsattn_profile_enable(1 if on else 0), "bsattn_profile_enable")
+
+
+def bsattn_profile_read(max_kernels: int = 64) -> dict:
+    """{kernel name: (launches, total milliseconds)} since the last read (synchronous)."""
+    import numpy as np
+    names = ctypes.create_string_buffer(48 * max_kernels)
+    counts = np.zeros(max_kernels, dtype=np.int64)
+    ms = np.zeros(max_kernels, dtype=np.float64)
+    n = c_int()
+    _check(load().bsattn_profile_read(max_kernels, names, counts.ctypes.data, ms.ctypes.data,
+                                      ctypes.byref(n)), "bsattn_profile_read")
+    out = {}
+    for i in range(n.value):
+        nm = names.raw[48 * i:48 * i + 48].split(b"\0", 1)[0].decode()
+        out[nm] = (int(counts[i]), float(ms[i]))
+    return out

@@ -25,6 +25,9 @@ ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the softmax reads them with VALU
+    # instructions, and the AGPR form costs a copy per accumulator register
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -6,6 +6,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -20,6 +22,38 @@ constexpr int kMaxNb = 4096;
 constexpr int kMaxR = 64;
 constexpr int kMaxLfTokens = 262144;
 }  // namespace
+
+namespace {
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
+}  // namespace
+
+ProfScope::ProfScope(const char* name, hipStream_t stream) : name_(name), stream_(stream) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  if (hipEventCreate(&start_) != hipSuccess) { start_ = nullptr; return; }
+  if (hipEventRecord(start_, stream_) != hipSuccess) {
+    (void)hipEventDestroy(start_);
+    start_ = nullptr;
+  }
+}
+
+ProfScope::~ProfScope() {
+  if (start_ == nullptr) return;
+  hipEvent_t stop = nullptr;
+  if (hipEventCreate(&stop) != hipSuccess || hipEventRecord(stop, stream_) != hipSuccess) {
+    if (stop) (void)hipEventDestroy(stop);
+    (void)hipEventDestroy(start_);
+    return;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back({name_, start_, stop});
+}
 
 int set_error(int status, const std::string& msg) {
   g_last_error = msg;
@@ -82,6 +116,7 @@ void free_layout(bsattn_layout* L) {
   (void)hipFree(L->d_col_idx);
   (void)hipFree(L->d_csc_ptr);
   (void)hipFree(L->d_csc_idx);
+  (void)hipFree(L->d_rbits);
   delete L;
 }
 
@@ -179,7 +214,13 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
       (st = dev_alloc(&L->d_row_ptr, (size_t)heads * nb + 1)) ||
       (st = dev_alloc(&L->d_col_idx, (size_t)(nnz * heads))) ||
       (st = dev_alloc(&L->d_csc_ptr, (size_t)heads * nb + 1)) ||
-      (st = dev_alloc(&L->d_csc_idx, (size_t)(nnz * heads)))) {
+      (st = dev_alloc(&L->d_csc_idx, (size_t)(nnz * heads))) ||
+      (st = dev_alloc(&L->d_rbits, (size_t)heads * nb * ((nb + 31) / 32)))) {
+    free_layout(L);
+    return st;
+  }
+  if ((st = check_hip(hipMemsetAsync(L->d_rbits, 0, (size_t)heads * nb * ((nb + 31) / 32) * 4, stream),
+                      "clear random-pick bitmap"))) {
     free_layout(L);
     return st;
   }
@@ -197,7 +238,10 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
     free_layout(L);
     return st;
   }
-  if ((st = launch_layout_build(L, stream))) { free_layout(L); return st; }
+  if ((st = launch_layout_rowptr(L, stream)) || (st = launch_layout_build(L, stream))) {
+    free_layout(L);
+    return st;
+  }
   *out = L;
   return BSATTN_OK;
 }
@@ -381,5 +425,51 @@ const char* bsattn_status_str(int status) {
 const char* bsattn_last_error(void) { return g_last_error.c_str(); }
 
 const char* bsattn_version(void) { return "bsattn 0.1.0 (gfx950)"; }
+
+int bsattn_profile_enable(int on) {
+  clear_error();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return BSATTN_OK;
+}
+
+int bsattn_profile_read(int max_kernels, char* names, int64_t* counts, double* total_ms,
+                        int* n_kernels) {
+  clear_error();
+  if (max_kernels < 0 || (max_kernels > 0 && (!names || !counts || !total_ms)) || !n_kernels)
+    return set_error(BSATTN_EINVAL, "profile_read: bad arguments");
+  std::vector<ProfRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof);
+  }
+  std::vector<std::string> keys;
+  std::vector<int64_t> cnt;
+  std::vector<double> ms;
+  int st = BSATTN_OK;
+  for (const ProfRecord& r : recs) {
+    float t = 0.f;
+    if (st == BSATTN_OK) st = check_hip(hipEventSynchronize(r.stop), "profile sync");
+    if (st == BSATTN_OK) st = check_hip(hipEventElapsedTime(&t, r.start, r.stop), "profile elapsed");
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+    if (st) continue;
+    size_t k = 0;
+    while (k < keys.size() && keys[k] != r.name) ++k;
+    if (k == keys.size()) { keys.push_back(r.name); cnt.push_back(0); ms.push_back(0.0); }
+    cnt[k] += 1;
+    ms[k] += t;
+  }
+  if (st) return st;
+  const int n = (int)keys.size() < max_kernels ? (int)keys.size() : max_kernels;
+  for (int i = 0; i < n; ++i) {
+    std::memset(names + 48 * i, 0, 48);
+    std::strncpy(names + 48 * i, keys[i].c_str(), 47);
+    counts[i] = cnt[i];
+    total_ms[i] = ms[i];
+  }
+  *n_kernels = n;
+  return BSATTN_OK;
+}
 
 }  // extern "C"

@@ -36,50 +36,65 @@ __device__ __forceinline__ void qk_tile(const uint16_t* sK, const bf16x8 (&qB)[4
 }
 
 // Online softmax over one key tile.  Scores equal to -inf are excluded keys.
-// On return s0/s1 hold the unnormalised probabilities 2^(s*sl2 - m).
-__device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& st, float sl2) {
-  float mx = s0[0];
+// The reference max st.m only moves when a block's max exceeds it by more than
+// kRescaleSlack (log2 units); the unnormalised probabilities 2^(s*sl2 - m) then
+// stay below 2^kRescaleSlack and O, l need no rescaling for most blocks.  The
+// result is exact either way: numerator and denominator share the reference.
+// On return pc[c] holds the bf16 probabilities of key chunk c as MFMA operands,
+// and st.l has grown by the fp32 sum of the probabilities.
+constexpr float kRescaleSlack = 8.f;
+
+__device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& st, float sl2,
+                                             bf16x8 (&pc)[4]) {
+  float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = partner_max(mx) * sl2;
+  if (__any(mx > st.m + kRescaleSlack)) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = m_new == st.m ? 1.f : fast_exp2(st.m - m_new);
+    st.l *= alpha;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx * sl2);
+    for (int r = 0; r < 16; ++r) {
+      st.o0[r] *= alpha;
+      st.o1[r] *= alpha;
+    }
+    st.m = m_new;
+  }
   // a row with no allowed key so far keeps m = -inf; use 0 as its reference so
   // that exp2 of excluded scores is 0 rather than NaN
-  const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - m_ref);
-  float rs = 0.f;
+  const float m_ref = st.m == -INFINITY ? 0.f : st.m;
+  float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     s0[r] = fast_exp2(__builtin_fmaf(s0[r], sl2, -m_ref));
     s1[r] = fast_exp2(__builtin_fmaf(s1[r], sl2, -m_ref));
-    rs += s0[r] + s1[r];
+    rs0 += s0[r];
+    rs1 += s1[r];
   }
-  st.l = st.l * alpha + rs;
-  st.m = m_new;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    st.o0[r] *= alpha;
-    st.o1[r] *= alpha;
-  }
+  st.l += rs0 + rs1;
+  pc[0] = pack8(s0, 0);
+  pc[1] = pack8(s0, 8);
+  pc[2] = pack8(s1, 0);
+  pc[3] = pack8(s1, 8);
 }
 
-// O^T += V^T P^T with V^T staged in sVt (row d, key x at position perm16(x)).
-__device__ __forceinline__ void pv_tile(const uint16_t* sVt, const f32x16& p0, const f32x16& p1,
-                                        int col, int hl, FwdState& st) {
-  const bf16x8 pc[4] = {pack8(p0, 0), pack8(p0, 8), pack8(p1, 0), pack8(p1, 8)};
+// O^T += V^T P^T; V is the natural LDS tile sV (row = key), its transposed
+// operand comes from ds_read_b64_tr_b16 reads.
+__device__ __forceinline__ void pv_tile(const uint16_t* sV, const bf16x8 (&pc)[4], int lane,
+                                        FwdState& st) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const bf16x8 v0 = ld16(sVt + col * kLdsStride + 16 * c + 8 * hl);
-    const bf16x8 v1 = ld16(sVt + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+    const bf16x8 v0 = ld_tr8(sV, 0, c, lane);
+    const bf16x8 v1 = ld_tr8(sV, 1, c, lane);
     st.o0 = mfma32(v0, pc[c], st.o0);
     st.o1 = mfma32(v1, pc[c], st.o1);
   }
 }
 
 // Final write of a finished row: O (bf16, normalised) and lse (natural log).
-// orow points at this lane's query row of O; lse_out may be null.
+// orow points at this lane's query row of O; lse_out may be null.  l_tot is the
+// row's full sum (both half-lanes, partner_sum).
 __device__ __forceinline__ void write_o_bf16(const FwdState& st, float l_tot, int hl,
                                              uint16_t* orow, float* lse_out) {
   const float inv = 1.f / l_tot;

@@ -84,9 +84,8 @@ __device__ __forceinline__ Item decode(const BwdArgs& a, int v, const int32_t* p
 }
 
 __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[kHead * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
 
   const int v = xcd_remap(blockIdx.x, a.total_items);
   if (v >= a.total_items) return;
@@ -96,6 +95,15 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   const size_t bh_off = (size_t)it.bh * a.n * kHead;
   const int qrow = it.blk * kBlock + 32 * wave + col;
 
+  const int32_t* keys = a.col_idx + it.start;
+  const uint16_t* kbase = a.k + bh_off;
+  const uint16_t* vbase = a.v + bh_off;
+  TileRegs kr, vr;
+  if (it.len > 0) {
+    const int kb = keys[0];
+    gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
+    gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+  }
   bf16x8 qB[4], doB[4];
   float dsum = 0.f;
   {
@@ -114,49 +122,19 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
       }
     }
   }
-  const float Dq = dsum + __shfl_xor(dsum, 32);
+  const float Dq = partner_sum(dsum);   // D = rowsum(dO * O)
   if (it.seg == 0 && hl == 0) a.dbuf[(size_t)it.bh * a.n + qrow] = Dq;
   const float lse2 = a.lse[(size_t)it.bh * a.n + qrow] * kLog2e;
   const float sl2 = a.sl2;
+  lds_store_nat(sK[0], kr, tid);
+  lds_store_nat(sV[0], vr, tid);
 
   f32x16 g0 = zero16(), g1 = zero16();   // dQ^T, d rows 0..31 and 32..63
-  const int32_t* keys = a.col_idx + it.start;
-  const uint16_t* kbase = a.k + bh_off;
-  const uint16_t* vbase = a.v + bh_off;
-  TileRegs kr, vr;
-  if (it.len > 0) {
-    const int kb = keys[0];
-    gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
-    gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
-  }
   for (int t = 0; t < it.len; ++t) {
-    lds_store_nat(sK, kr, tid);
-    lds_store_nat(sV, vr, tid);
+    const int cur = t & 1;
     __syncthreads();
-    {
-      // K^T built from the natural LDS copy: thread t reads key rows 4*(t/8)..+3,
-      // columns 8*(t%8)..+7, and writes LDS rows (d) 8*(t%8)..+7 at positions
-      // perm16(4*(t/8)) .. +3
-      const int c = tid & 7, x0 = 4 * (tid >> 3);
-      const int pos = perm16(x0);
-      u32x4 rows[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) rows[u] = *reinterpret_cast<const u32x4*>(sK + (x0 + u) * kLdsStride + 8 * c);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1, hi = e & 1;
-        uint32_t v0 = hi ? (rows[0][wd] >> 16) : (rows[0][wd] & 0xffffu);
-        uint32_t v1 = hi ? (rows[1][wd] >> 16) : (rows[1][wd] & 0xffffu);
-        uint32_t v2 = hi ? (rows[2][wd] >> 16) : (rows[2][wd] & 0xffffu);
-        uint32_t v3 = hi ? (rows[3][wd] >> 16) : (rows[3][wd] & 0xffffu);
-        u32x2 pk;
-        pk[0] = v0 | (v1 << 16);
-        pk[1] = v2 | (v3 << 16);
-        *reinterpret_cast<u32x2*>(sKt + (8 * c + e) * kLdsStride + pos) = pk;
-      }
-    }
-    __syncthreads();
-    if (t + 1 < it.len) {
+    const bool more = t + 1 < it.len;
+    if (more) {
       const int kb = keys[t + 1];
       gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
       gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
@@ -165,10 +143,10 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bf16x8 k0 = ld16(sK + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 k1 = ld16(sK + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 v0 = ld16(sV + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 v1 = ld16(sV + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 k0 = ld16(sK[cur] + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 k1 = ld16(sK[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 v0 = ld16(sV[cur] + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 v1 = ld16(sV[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
       s0 = mfma32(k0, qB[c], s0);
       s1 = mfma32(k1, qB[c], s1);
       p0 = mfma32(v0, doB[c], p0);
@@ -181,17 +159,17 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
       s0[r] = e0 * (p0[r] - Dq);
       s1[r] = e1 * (p1[r] - Dq);
     }
-    // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
-    const bf16x8 d0 = pack8(s0, 0), d1 = pack8(s0, 8), d2 = pack8(s1, 0), d3 = pack8(s1, 8);
-    const bf16x8 dc[4] = {d0, d1, d2, d3};
+    // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]; K^T from transpose reads
+    const bf16x8 dc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bf16x8 a0 = ld16(sKt + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 a1 = ld16(sKt + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-      g0 = mfma32(a0, dc[c], g0);
-      g1 = mfma32(a1, dc[c], g1);
+      g0 = mfma32(ld_tr8(sK[cur], 0, c, lane), dc[c], g0);
+      g1 = mfma32(ld_tr8(sK[cur], 1, c, lane), dc[c], g1);
     }
-    __syncthreads();
+    if (more) {
+      lds_store_nat(sK[cur ^ 1], kr, tid);
+      lds_store_nat(sV[cur ^ 1], vr, tid);
+    }
   }
 
   const float sc = a.scale;
@@ -221,12 +199,10 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
 }
 
 __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[kHead * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[kBlock * kLdsStride];   // dO
-  __shared__ __attribute__((aligned(16))) uint16_t sOt[kHead * kLdsStride];  // dO^T
-  __shared__ __attribute__((aligned(16))) float sL[kBlock];   // lse * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[kBlock];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[2][kBlock * kLdsStride];   // dO
+  __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kBlock];
 
   const int v = xcd_remap(blockIdx.x, a.total_items);
   if (v >= a.total_items) return;
@@ -236,6 +212,19 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   const size_t bh_off = (size_t)it.bh * a.n * kHead;
   const int krow = it.blk * kBlock + 32 * wave + col;   // this lane's key token
 
+  const int32_t* qblks = a.csc_idx + it.start;
+  const uint16_t* qbase = a.q + bh_off;
+  const uint16_t* dobase = a.dout + bh_off;
+  const float* lbase = a.lse + (size_t)it.bh * a.n;
+  const float* dbase = a.dbuf + (size_t)it.bh * a.n;
+  TileRegs qr, dr;
+  float lv = 0.f, dval = 0.f;
+  if (it.len > 0) {
+    const int qb = qblks[0];
+    gload_nat(qr, qbase + (size_t)qb * kBlock * kHead, tid);
+    gload_nat(dr, dobase + (size_t)qb * kBlock * kHead, tid);
+    if (tid < kBlock) { lv = lbase[qb * kBlock + tid]; dval = dbase[qb * kBlock + tid]; }
+  }
   bf16x8 kB[4], vB[4];
   {
     const size_t off = bh_off + (size_t)krow * kHead + 8 * hl;
@@ -245,47 +234,30 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
       vB[c] = ld16(a.v + off + 16 * c);
     }
   }
+  lds_store_nat(sQ[0], qr, tid);
+  lds_store_nat(sO[0], dr, tid);
+  if (tid < kBlock) { sL[0][tid] = lv * kLog2e; sD[0][tid] = dval; }
+
   f32x16 dv0 = zero16(), dv1 = zero16(), dk0 = zero16(), dk1 = zero16();
   const float sl2 = a.sl2;
-  const int32_t* qblks = a.csc_idx + it.start;
-  const uint16_t* qbase = a.q + bh_off;
-  const uint16_t* dobase = a.dout + bh_off;
-  const float* lbase = a.lse + (size_t)it.bh * a.n;
-  const float* dbase = a.dbuf + (size_t)it.bh * a.n;
-
-  TileRegs qr, qtr, dr, dtr;
-  float lv = 0.f, dval = 0.f;
-  if (it.len > 0) {
-    const int qb = qblks[0];
-    gload_nat(qr, qbase + (size_t)qb * kBlock * kHead, tid);
-    gload_tr(qtr, qbase + (size_t)qb * kBlock * kHead, tid);
-    gload_nat(dr, dobase + (size_t)qb * kBlock * kHead, tid);
-    gload_tr(dtr, dobase + (size_t)qb * kBlock * kHead, tid);
-    if (tid < kBlock) { lv = lbase[qb * kBlock + tid]; dval = dbase[qb * kBlock + tid]; }
-  }
   for (int t = 0; t < it.len; ++t) {
-    lds_store_nat(sQ, qr, tid);
-    lds_store_tr(sQt, qtr, tid);
-    lds_store_nat(sO, dr, tid);
-    lds_store_tr(sOt, dtr, tid);
-    if (tid < kBlock) { sL[tid] = lv * kLog2e; sD[tid] = dval; }
+    const int cur = t & 1;
     __syncthreads();
-    if (t + 1 < it.len) {
+    const bool more = t + 1 < it.len;
+    if (more) {
       const int qb = qblks[t + 1];
       gload_nat(qr, qbase + (size_t)qb * kBlock * kHead, tid);
-      gload_tr(qtr, qbase + (size_t)qb * kBlock * kHead, tid);
       gload_nat(dr, dobase + (size_t)qb * kBlock * kHead, tid);
-      gload_tr(dtr, dobase + (size_t)qb * kBlock * kHead, tid);
       if (tid < kBlock) { lv = lbase[qb * kBlock + tid]; dval = dbase[qb * kBlock + tid]; }
     }
     // S[q][key] = Q K^T, dP[q][key] = dO V^T; rows = queries (2 tiles), column = key
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bf16x8 q0 = ld16(sQ + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 q1 = ld16(sQ + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 o0 = ld16(sO + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 o1 = ld16(sO + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 q0 = ld16(sQ[cur] + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 q1 = ld16(sQ[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 o0 = ld16(sO[cur] + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 o1 = ld16(sO[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
       s0 = mfma32(q0, kB[c], s0);
       s1 = mfma32(q1, kB[c], s1);
       p0 = mfma32(o0, vB[c], p0);
@@ -294,10 +266,10 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     // rows held by this lane: q = 32*qt + 8*j + 4*hl + e
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(sL + 8 * j + 4 * hl);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(sL + 32 + 8 * j + 4 * hl);
-      const f32x4 D0 = *reinterpret_cast<const f32x4*>(sD + 8 * j + 4 * hl);
-      const f32x4 D1 = *reinterpret_cast<const f32x4*>(sD + 32 + 8 * j + 4 * hl);
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sL[cur][8 * j + 4 * hl]);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sL[cur][32 + 8 * j + 4 * hl]);
+      const f32x4 D0 = *reinterpret_cast<const f32x4*>(&sD[cur][8 * j + 4 * hl]);
+      const f32x4 D1 = *reinterpret_cast<const f32x4*>(&sD[cur][32 + 8 * j + 4 * hl]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * j + e;
@@ -314,16 +286,16 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     const bf16x8 dc[4] = {pack8(p0, 0), pack8(p0, 8), pack8(p1, 0), pack8(p1, 8)};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bf16x8 ot0 = ld16(sOt + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 ot1 = ld16(sOt + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 qt0 = ld16(sQt + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 qt1 = ld16(sQt + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-      dv0 = mfma32(ot0, pc[c], dv0);
-      dv1 = mfma32(ot1, pc[c], dv1);
-      dk0 = mfma32(qt0, dc[c], dk0);
-      dk1 = mfma32(qt1, dc[c], dk1);
+      dv0 = mfma32(ld_tr8(sO[cur], 0, c, lane), pc[c], dv0);
+      dv1 = mfma32(ld_tr8(sO[cur], 1, c, lane), pc[c], dv1);
+      dk0 = mfma32(ld_tr8(sQ[cur], 0, c, lane), dc[c], dk0);
+      dk1 = mfma32(ld_tr8(sQ[cur], 1, c, lane), dc[c], dk1);
     }
-    __syncthreads();
+    if (more) {
+      lds_store_nat(sQ[cur ^ 1], qr, tid);
+      lds_store_nat(sO[cur ^ 1], dr, tid);
+      if (tid < kBlock) { sL[cur ^ 1][tid] = lv * kLog2e; sD[cur ^ 1][tid] = dval; }
+    }
   }
 
   const float sc = a.scale;
@@ -434,15 +406,24 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, co
   a.scale = scale;
   a.sl2 = scale * kLog2e;
   const int grid = 8 * ((a.total_items + 7) / 8);
-  hipLaunchKernelGGL(bs_bwd_dq_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  {
+    ProfScope prof_("bs_bwd_dq", stream);
+    hipLaunchKernelGGL(bs_bwd_dq_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  }
   int st = check_hip(hipGetLastError(), "bs_bwd_dq launch");
   if (st) return st;
-  hipLaunchKernelGGL(bs_bwd_dkdv_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  {
+    ProfScope prof_("bs_bwd_dkdv", stream);
+    hipLaunchKernelGGL(bs_bwd_dkdv_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  }
   st = check_hip(hipGetLastError(), "bs_bwd_dkdv launch");
   if (st || !L->split || L->g == 0) return st;
-  hipLaunchKernelGGL(bs_bwd_reduce_kernel, dim3(batch * L->heads * L->g * 3), dim3(256), 0,
-                     stream, (const float*)a.part_q, (const float*)a.part_kv, L->d_gblk, L->n,
-                     L->g, L->nseg, a.dq, a.dk, a.dv);
+  {
+    ProfScope prof_("bs_bwd_reduce", stream);
+    hipLaunchKernelGGL(bs_bwd_reduce_kernel, dim3(batch * L->heads * L->g * 3), dim3(256), 0,
+                       stream, (const float*)a.part_q, (const float*)a.part_kv, L->d_gblk, L->n,
+                       L->g, L->nseg, a.dq, a.dk, a.dv);
+  }
   return check_hip(hipGetLastError(), "bs_bwd_reduce launch");
 }
 

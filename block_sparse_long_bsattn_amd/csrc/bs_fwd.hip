@@ -11,10 +11,11 @@
 //   * a global query block (a full row, App. D Fig. 6 "direct multiplication")
 //     is split into items of kSeg key blocks that write partial (unnormalised O,
 //     running max, running sum); bs_fwd_combine merges them in a fixed order.
-// Per key block: K (natural) and V (transposed) are staged through LDS; S^T =
-// K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA; the online softmax runs in
-// fp32 registers, one query per lane (column of the accumulator), 32 keys per
-// lane and the other 32 in the partner lane l ^ 32.
+// Per key block: K and V are staged through double-buffered LDS in natural
+// layout; S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA (V^T read with
+// LDS transpose reads); the online softmax runs in fp32 registers, one query per
+// lane (column of the accumulator), 32 keys per lane and the other 32 in the
+// partner lane l ^ 32.
 
 #include "attn_tile.hpp"
 #include "internal.hpp"
@@ -78,8 +79,8 @@ __device__ __forceinline__ Item decode_row_item(int v, int heads, int nb, int g,
 }
 
 __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[kHead * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
 
   const int v = xcd_remap(blockIdx.x, a.total_items);
   if (v >= a.total_items) return;
@@ -90,43 +91,50 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   const size_t bh_off = (size_t)it.bh * a.n * kHead;
   const int qrow = it.i * kBlock + 32 * wave + col;   // token index of this lane's query
 
+  const int32_t* keys = a.col_idx + it.start;
+  const uint16_t* kbase = a.k + bh_off;
+  const uint16_t* vbase = a.v + bh_off;
+  TileRegs kr, vr;
+  if (it.len > 0) {
+    const int kb = keys[0];
+    gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
+    gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+  }
   bf16x8 qB[4];
   {
     const uint16_t* qp = a.q + bh_off + (size_t)qrow * kHead + 8 * hl;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
   }
+  lds_store_nat(sK[0], kr, tid);
+  lds_store_nat(sV[0], vr, tid);
 
   FwdState st;
   fwd_state_init(st);
   const float sl2 = a.sl2;
-  const int32_t* keys = a.col_idx + it.start;
-  const uint16_t* kbase = a.k + bh_off;
-  const uint16_t* vbase = a.v + bh_off;
-
-  TileRegs kr, vr;
-  if (it.len > 0) {
-    const int kb = keys[0];
-    gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
-    gload_tr(vr, vbase + (size_t)kb * kBlock * kHead, tid);
-  }
+  // double buffer: block t+1 is fetched into registers during block t and stored
+  // into the other LDS buffer after it; one barrier per block
   for (int t = 0; t < it.len; ++t) {
-    lds_store_nat(sK, kr, tid);
-    lds_store_tr(sVt, vr, tid);
+    const int cur = t & 1;
     __syncthreads();
-    if (t + 1 < it.len) {
+    const bool more = t + 1 < it.len;
+    if (more) {
       const int kb = keys[t + 1];
       gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
-      gload_tr(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+      gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
     }
     f32x16 s0, s1;
-    qk_tile(sK, qB, col, hl, s0, s1);
-    softmax_step(s0, s1, st, sl2);
-    pv_tile(sVt, s0, s1, col, hl, st);
-    __syncthreads();
+    qk_tile(sK[cur], qB, col, hl, s0, s1);
+    bf16x8 pc[4];
+    softmax_step(s0, s1, st, sl2, pc);
+    pv_tile(sV[cur], pc, lane, st);
+    if (more) {
+      lds_store_nat(sK[cur ^ 1], kr, tid);
+      lds_store_nat(sV[cur ^ 1], vr, tid);
+    }
   }
 
-  const float l_tot = st.l + __shfl_xor(st.l, 32);
+  const float l_tot = partner_sum(st.l);
   if (it.slot < 0) {
     write_o_bf16(st, l_tot, hl, a.o + bh_off + (size_t)qrow * kHead,
                  a.lse != nullptr ? a.lse + (size_t)it.bh * a.n + qrow : nullptr);
@@ -255,7 +263,10 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
     a.total_items = bhn * L->nb;
     a.scale = scale;
     const int grid = 8 * ((a.total_items + 7) / 8);
+    {
+    ProfScope prof_("bs_fwd_f32", stream);
     hipLaunchKernelGGL(bs_fwd_f32_kernel, dim3(grid), dim3(256), 0, stream, a);
+  }
     return check_hip(hipGetLastError(), "bs_fwd_f32 launch");
   }
   FwdArgs a;
@@ -269,12 +280,18 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
   a.total_items = bhn * a.items_per_bh;
   a.sl2 = scale * kLog2e;
   const int grid = 8 * ((a.total_items + 7) / 8);
-  hipLaunchKernelGGL(bs_fwd_bf16_kernel, dim3(grid), dim3(kFwdThreads), 0, stream, a);
+  {
+    ProfScope prof_("bs_fwd_bf16", stream);
+    hipLaunchKernelGGL(bs_fwd_bf16_kernel, dim3(grid), dim3(kFwdThreads), 0, stream, a);
+  }
   int st = check_hip(hipGetLastError(), "bs_fwd_bf16 launch");
   if (st || !L->split || L->g == 0) return st;
-  hipLaunchKernelGGL(bs_fwd_combine_kernel, dim3(bhn * L->g), dim3(256), 0, stream,
-                     (const float*)ws, L->d_gblk, L->heads, L->n, L->g, L->nseg,
-                     (uint16_t*)o, lse);
+  {
+    ProfScope prof_("bs_fwd_combine", stream);
+    hipLaunchKernelGGL(bs_fwd_combine_kernel, dim3(bhn * L->g), dim3(256), 0, stream,
+                       (const float*)ws, L->d_gblk, L->heads, L->n, L->g, L->nseg,
+                       (uint16_t*)o, lse);
+  }
   return check_hip(hipGetLastError(), "bs_fwd_combine launch");
 }
 

@@ -10,10 +10,17 @@
 //   8*(r/4) + 4*(l/32) + (r%4), r = 0..15.
 // * A contraction over a 64-long block dimension (keys or queries) whose
 //   operand comes out of a previous MFMA accumulator therefore pairs register
-//   r = 8c' + e of tile t with k-slot e of chunk 2t + c'.  The index it stands
-//   for is 16c + 8jj + 4h + i with c = 2t + c', e = 4jj + i, h = l / 32.  The
-//   matching operand read from LDS stores index x at position perm16(x), which
-//   swaps bits 2 and 3 of x, so that each lane reads eight contiguous values.
+//   r = 8c' + e of tile t with k-slot e of chunk c = 2t + c'.  The index it stands
+//   for is 16c + 8(e/4) + 4h + (e%4), h = l / 32.  The matching other operand is
+//   read from a natural LDS tile (row = contraction index, 64 columns) with two
+//   ds_read_b64_tr_b16: within each 16-lane group, lane 16g + 4a + b receives
+//   element b of the 8-byte chunks addressed by lanes 16g + a + 4j, j = 0..3.
+//   Lane s therefore addresses row 16c + 8t + 4(s/32) + (s%16)/4 (t = 0, 1),
+//   columns 16((s/16)%2) + 4(s%4) .. +3, and receives column (s % 32) of rows
+//   16c + 8t + 4(s/32) + j: exactly k-slots e = 4t + j of the pairing above.
+// * Every LDS tile is stored in natural layout with 16-byte stores; rows are
+//   padded to 72 elements so that the row-strided 16-byte and 8-byte reads above
+//   spread over the banks.
 
 #pragma once
 
@@ -36,10 +43,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ int perm16(int x) {
-  // swap bits 2 and 3
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -55,14 +60,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// Eight consecutive accumulator registers, rounded to bf16, as one MFMA operand.
-__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+// Eight consecutive accumulator registers rounded to bf16 and packed in pairs.
+__device__ __forceinline__ u32x4 pack8u(const f32x16& s, int base) {
   u32x4 u;
   u[0] = pack_bf16x2(s[base + 0], s[base + 1]);
   u[1] = pack_bf16x2(s[base + 2], s[base + 3]);
   u[2] = pack_bf16x2(s[base + 4], s[base + 5]);
   u[3] = pack_bf16x2(s[base + 6], s[base + 7]);
-  return __builtin_bit_cast(bf16x8, u);
+  return u;
+}
+
+// The same, as one MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+  return __builtin_bit_cast(bf16x8, pack8u(s, base));
 }
 
 __device__ __forceinline__ bf16x8 ld16(const uint16_t* p) {
@@ -83,13 +93,9 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
-// Cooperative 64x64 bf16 tile staging through LDS (128 threads).
-//
-// Natural copy: LDS row x holds global row x (64 values + pad).  Thread t moves
-// 16-byte chunk (t % 8) of rows (t / 8) + 16u, u = 0..3.
-// Transposed copy: LDS row c (a column of the global tile) holds, at position
-// perm16(x), the value of global row x.  Thread t moves rows 4*(t / 8) .. +3,
-// columns 8*(t % 8) .. +7.
+// Cooperative 64x64 bf16 tile staging through LDS (128 threads): LDS row x holds
+// global row x (64 values + pad).  Thread t moves 16-byte chunk (t % 8) of rows
+// (t / 8) + 16u, u = 0..3, so eight lanes cover one 128-byte row.
 // ---------------------------------------------------------------------------
 
 struct TileRegs { u32x4 v[4]; };
@@ -107,28 +113,31 @@ __device__ __forceinline__ void lds_store_nat(uint16_t* s, const TileRegs& r, in
     *reinterpret_cast<u32x4*>(s + (row + 16 * u) * kLdsStride + 8 * c) = r.v[u];
 }
 
-__device__ __forceinline__ void gload_tr(TileRegs& r, const uint16_t* g, int tid) {
-  const int c = tid & 7, x0 = 4 * (tid >> 3);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) r.v[u] = ldg16(g + (x0 + u) * kHead + 8 * c);
+// MFMA operand of 8 k-slots for chunk c of a contraction over the rows of the
+// natural LDS tile s, for output rows/columns 32*tile .. 32*tile + 31 (the tile's
+// columns).  See the lane mapping described at the top of this file.
+__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* s, int tile, int c, int lane) {
+  const int row = 16 * c + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = 32 * tile + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const lds_v4i16* p0 = (const lds_v4i16*)(s + row * kLdsStride + col);
+  const lds_v4i16* p1 = (const lds_v4i16*)(s + (row + 8) * kLdsStride + col);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4i16*>(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4i16*>(p1));
+  const v4i16 both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, both);
 }
 
-__device__ __forceinline__ void lds_store_tr(uint16_t* s, const TileRegs& r, int tid) {
-  const int c = tid & 7, x0 = 4 * (tid >> 3);
-  const int pos = perm16(x0);   // x0..x0+3 map to pos..pos+3 (bits 0,1 untouched)
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    // column 8c+e: four rows x0..x0+3
-    const int w = e >> 1, hi = e & 1;
-    uint32_t a0 = hi ? (r.v[0][w] >> 16) : (r.v[0][w] & 0xffffu);
-    uint32_t a1 = hi ? (r.v[1][w] >> 16) : (r.v[1][w] & 0xffffu);
-    uint32_t a2 = hi ? (r.v[2][w] >> 16) : (r.v[2][w] & 0xffffu);
-    uint32_t a3 = hi ? (r.v[3][w] >> 16) : (r.v[3][w] & 0xffffu);
-    u32x2 pk;
-    pk[0] = a0 | (a1 << 16);
-    pk[1] = a2 | (a3 << 16);
-    *reinterpret_cast<u32x2*>(s + (8 * c + e) * kLdsStride + pos) = pk;
-  }
+// max over lanes l and l ^ 32 (the two halves of one accumulator column)
+__device__ __forceinline__ float partner_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float partner_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 // XCD-aware work mapping: the dispatcher hands consecutive work-groups to the 8

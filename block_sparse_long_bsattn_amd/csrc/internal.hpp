@@ -26,6 +26,7 @@ struct bsattn_layout {
   int32_t* d_col_idx = nullptr;  // [heads*nnz_per_head]
   int32_t* d_csc_ptr = nullptr;  // [heads*nb + 1]
   int32_t* d_csc_idx = nullptr;  // [heads*nnz_per_head]
+  uint32_t* d_rbits = nullptr;   // [heads][nb][ceil(nb/32)] random picks, zero between builds
 };
 
 struct lfattn_plan {
@@ -42,11 +43,26 @@ struct lfattn_plan {
 
 namespace bsattn {
 
+// Brackets one kernel launch with hipEvents while profiling is enabled.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t stream);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr;
+};
+
 int set_error(int status, const std::string& msg);
 void clear_error();
 int check_hip(hipError_t e, const char* what);
 
 // Launch helpers implemented in the kernel translation units.
+int launch_layout_rowptr(bsattn_layout* L, hipStream_t stream);
 int launch_layout_build(bsattn_layout* L, hipStream_t stream);
 int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale,
                const void* q, const void* k, const void* v, void* o, float* lse,

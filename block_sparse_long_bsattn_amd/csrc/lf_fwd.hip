@@ -77,8 +77,8 @@ __global__ __launch_bounds__(256) void lf_gather_kernel(LfArgs a) {
 }
 
 __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[kHead * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
 
   const int v = xcd_remap(blockIdx.x, a.total_items);
   if (v >= a.total_items) return;
@@ -140,21 +140,22 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
     const uint16_t *ks, *vs;
     tile_src(x, ks, vs);
     gload_nat(kr, ks, tid);
-    gload_tr(vr, vs, tid);
+    gload_nat(vr, vs, tid);
+    lds_store_nat(sK[0], kr, tid);
+    lds_store_nat(sV[0], vr, tid);
   }
+  int cur = 0;
   while (x < ntile) {
-    lds_store_nat(sK, kr, tid);
-    lds_store_tr(sVt, vr, tid);
     __syncthreads();
     const int xn = next_tile(x + 1);
     if (xn < ntile) {
       const uint16_t *ks, *vs;
       tile_src(xn, ks, vs);
       gload_nat(kr, ks, tid);
-      gload_tr(vr, vs, tid);
+      gload_nat(vr, vs, tid);
     }
     f32x16 s0, s1;
-    qk_tile(sK, qB, col, hl, s0, s1);
+    qk_tile(sK[cur], qB, col, hl, s0, s1);
     if (x < nband) {
       const int u0 = (lo_u + x) * kBlock;
       // the whole tile lies in the band iff its farthest pair does
@@ -180,21 +181,26 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
         }
       }
     }
-    softmax_step(s0, s1, st, sl2);
-    pv_tile(sVt, s0, s1, col, hl, st);
-    __syncthreads();
+    bf16x8 pc[4];
+    softmax_step(s0, s1, st, sl2, pc);
+    pv_tile(sV[cur], pc, lane, st);
+    if (xn < ntile) {
+      lds_store_nat(sK[cur ^ 1], kr, tid);
+      lds_store_nat(sV[cur ^ 1], vr, tid);
+    }
+    cur ^= 1;
     x = xn;
   }
 
-  const float l_tot = st.l + __shfl_xor(st.l, 32);
+  const float l_tot = partner_sum(st.l);
   if (a.gidx[p] < 0)
     write_o_bf16(st, l_tot, hl, a.o + bh_off + (size_t)p * kHead,
                  a.lse != nullptr ? a.lse + (size_t)bh * a.n + p : nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void lf_global_kernel(LfArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[kHead * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
 
   const int per_bh = a.ngt * a.nseg;
   const int v = xcd_remap(blockIdx.x, a.total_items);
@@ -219,22 +225,28 @@ __global__ __launch_bounds__(kThreads) void lf_global_kernel(LfArgs a) {
   fwd_state_init(st);
   TileRegs kr, vr;
   gload_nat(kr, a.k + bh_off + (size_t)u_begin * kBlock * kHead, tid);
-  gload_tr(vr, a.v + bh_off + (size_t)u_begin * kBlock * kHead, tid);
+  gload_nat(vr, a.v + bh_off + (size_t)u_begin * kBlock * kHead, tid);
+  lds_store_nat(sK[0], kr, tid);
+  lds_store_nat(sV[0], vr, tid);
   for (int u = u_begin; u < u_end; ++u) {
-    lds_store_nat(sK, kr, tid);
-    lds_store_tr(sVt, vr, tid);
+    const int cur = (u - u_begin) & 1;
     __syncthreads();
-    if (u + 1 < u_end) {
+    const bool more = u + 1 < u_end;
+    if (more) {
       gload_nat(kr, a.k + bh_off + (size_t)(u + 1) * kBlock * kHead, tid);
-      gload_tr(vr, a.v + bh_off + (size_t)(u + 1) * kBlock * kHead, tid);
+      gload_nat(vr, a.v + bh_off + (size_t)(u + 1) * kBlock * kHead, tid);
     }
     f32x16 s0, s1;
-    qk_tile(sK, qB, col, hl, s0, s1);
-    softmax_step(s0, s1, st, a.sl2);
-    pv_tile(sVt, s0, s1, col, hl, st);
-    __syncthreads();
+    qk_tile(sK[cur], qB, col, hl, s0, s1);
+    bf16x8 pc[4];
+    softmax_step(s0, s1, st, a.sl2, pc);
+    pv_tile(sV[cur], pc, lane, st);
+    if (more) {
+      lds_store_nat(sK[cur ^ 1], kr, tid);
+      lds_store_nat(sV[cur ^ 1], vr, tid);
+    }
   }
-  const float l_tot = st.l + __shfl_xor(st.l, 32);
+  const float l_tot = partner_sum(st.l);
   write_partial(st, l_tot, hl, qr, a.part + (size_t)v * kPartFloats);
 }
 
@@ -296,19 +308,31 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const
   const int bhn = batch * heads;
   int st;
   if (has_g) {
+    {
+    ProfScope prof_("lf_gather", stream);
     hipLaunchKernelGGL(lf_gather_kernel, dim3(bhn * P->ngt), dim3(256), 0, stream, a);
+  }
     if ((st = check_hip(hipGetLastError(), "lf_gather launch"))) return st;
   }
   a.total_items = bhn * P->nt;
-  hipLaunchKernelGGL(lf_band_kernel, dim3(8 * ((a.total_items + 7) / 8)), dim3(kThreads), 0,
-                     stream, a);
+  {
+    ProfScope prof_("lf_band", stream);
+    hipLaunchKernelGGL(lf_band_kernel, dim3(8 * ((a.total_items + 7) / 8)), dim3(kThreads), 0,
+                       stream, a);
+  }
   if ((st = check_hip(hipGetLastError(), "lf_band launch"))) return st;
   if (!has_g) return 0;
   a.total_items = bhn * P->ngt * P->nseg;
-  hipLaunchKernelGGL(lf_global_kernel, dim3(8 * ((a.total_items + 7) / 8)), dim3(kThreads), 0,
-                     stream, a);
+  {
+    ProfScope prof_("lf_global", stream);
+    hipLaunchKernelGGL(lf_global_kernel, dim3(8 * ((a.total_items + 7) / 8)), dim3(kThreads), 0,
+                       stream, a);
+  }
   if ((st = check_hip(hipGetLastError(), "lf_global launch"))) return st;
-  hipLaunchKernelGGL(lf_combine_kernel, dim3(bhn * P->ngt), dim3(256), 0, stream, a);
+  {
+    ProfScope prof_("lf_combine", stream);
+    hipLaunchKernelGGL(lf_combine_kernel, dim3(bhn * P->ngt), dim3(256), 0, stream, a);
+  }
   return check_hip(hipGetLastError(), "lf_combine launch");
 }
 

@@ -215,6 +215,20 @@ const char* bsattn_last_error(void);
 /* Library version string. */
 const char* bsattn_version(void);
 
+/*
+ * Per-kernel timing for measurement tools.  While enabled (on != 0), every kernel
+ * the library launches is bracketed by two hipEvents recorded on the stream it is
+ * launched on.  bsattn_profile_read waits for those events and reports, for up to
+ * max_kernels distinct kernel names, the name (NUL-terminated, at most 47 chars,
+ * stored at names + 48*i), the number of launches and their summed elapsed time
+ * in milliseconds; it then forgets the recorded launches.  *n_kernels receives
+ * the number of names written.  Timing adds event records between launches, so
+ * measure end-to-end throughput with profiling off.  Returns OK, EINVAL or EHIP.
+ */
+int bsattn_profile_enable(int on);
+int bsattn_profile_read(int max_kernels, char* names, int64_t* counts, double* total_ms,
+                        int* n_kernels);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_binding_exports():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     assert sorted(_lib.EXPORTS) == names
 
 
@@ -84,6 +84,7 @@ def test_null_handles_are_rejected():
     assert lib.lfattn_fwd_workspace(None, 1, 1, 64) == 0
     assert lib.bsattn_layout_destroy(None) == 0
     assert lib.lfattn_plan_destroy(None) == 0
+    assert lib.bsattn_profile_read(-1, None, None, None, None) == -1
 
 
 @pytest.mark.parametrize("args,code", [

@@ -57,6 +57,9 @@ def test_layout_edge_cases_bit_exact():
     compare(640, 2, [], 1, 0, 5)                 # window only
     compare(1024, 2, [0], 1, 64, 5)              # r beyond the candidates
     compare(64 * 300, 1, [0, 299], 3, 3, 2**64 - 1)   # largest seed
+    compare(64 * 600, 2, [0, 7, 599], 3, 3, 99)      # more than 512 blocks: two-kernel path
+    compare(64 * 600, 1, [1, 300], 5, 12, 98)        # ... with more than 8 random blocks
+    compare(64 * 40, 3, [2], 3, 9, 97)               # more than 8 random blocks
 
 
 def test_layout_rebuild_matches_new_seed():
