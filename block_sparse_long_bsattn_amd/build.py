@@ -28,6 +28,9 @@ FLAGS = [
     # keep MFMA accumulators in ordinary VGPRs: the softmax reads them with VALU
     # instructions, and the AGPR form costs a copy per accumulator register
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # NaN inputs give NaN outputs either way; without this every fmaxf operand is
+    # canonicalised first (infinities are still honoured: masking relies on -inf)
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -10,65 +10,115 @@ namespace bsattn {
 
 struct FwdState {
   f32x16 o0, o1;   // O^T accumulators: d rows 0..31 and 32..63, column = query
-  float m, l;      // running max (log2 units, scaled) and this half-lane's sum
+  f32x16 cinit;    // every register = -(reference max), the QK^T accumulator seed
+  float m;         // reference max (log2 units), -inf until the row saw a finite score
+  float l;         // this half-lane's share of the row sum
 };
 
 __device__ __forceinline__ void fwd_state_init(FwdState& st) {
   st.o0 = zero16();
   st.o1 = zero16();
+  st.cinit = zero16();
   st.m = -INFINITY;
   st.l = 0.f;
 }
 
-// S^T for the 64 keys of the LDS tile sK (natural layout) against this lane's query.
-// s0 holds keys 0..31, s1 keys 32..63; register r <-> key 8*(r/4) + 4*hl + r%4.
-__device__ __forceinline__ void qk_tile(const uint16_t* sK, const bf16x8 (&qB)[4], int col,
-                                        int hl, f32x16& s0, f32x16& s1) {
-  s0 = zero16();
-  s1 = zero16();
+// reference currently baked into st.cinit
+__device__ __forceinline__ float seed_ref(const FwdState& st) {
+  return st.m != -INFINITY ? st.m : 0.f;
+}
+
+// Q operand pre-scaled by sl2 = scale*log2(e) (rounded to bf16), so that the QK^T
+// products come out in log2 units.
+__device__ __forceinline__ void scale_operands(bf16x8 (&qB)[4], float sl2) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const bf16x8 a0 = ld16(sK + col * kLdsStride + 16 * c + 8 * hl);
-    const bf16x8 a1 = ld16(sK + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-    s0 = mfma32(a0, qB[c], s0);
-    s1 = mfma32(a1, qB[c], s1);
+    const u32x4 u = __builtin_bit_cast(u32x4, qB[c]);
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(bf16_lo(u[e]) * sl2, bf16_hi(u[e]) * sl2);
+    qB[c] = __builtin_bit_cast(bf16x8, w);
   }
 }
 
-// Online softmax over one key tile.  Scores equal to -inf are excluded keys.
-// The reference max st.m only moves when a block's max exceeds it by more than
-// kRescaleSlack (log2 units); the unnormalised probabilities 2^(s*sl2 - m) then
-// stay below 2^kRescaleSlack and O, l need no rescaling for most blocks.  The
-// result is exact either way: numerator and denominator share the reference.
-// On return pc[c] holds the bf16 probabilities of key chunk c as MFMA operands,
-// and st.l has grown by the fp32 sum of the probabilities.
+// S^T for the 64 keys of the LDS tile sK (natural layout) against this lane's query,
+// accumulated on top of `seed`.  s0 holds keys 0..31, s1 keys 32..63; register r <->
+// key 8*(r/4) + 4*hl + r%4.
+__device__ __forceinline__ void qk_tile(const uint16_t* sK, const bf16x8 (&qB)[4], int col,
+                                        int hl, const f32x16& seed, f32x16& s0, f32x16& s1) {
+  bf16x8 a[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    a[2 * c] = ld16(sK + col * kLdsStride + 16 * c + 8 * hl);
+    a[2 * c + 1] = ld16(sK + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+  }
+  s0 = mfma32(a[0], qB[0], seed);
+  s1 = mfma32(a[1], qB[0], seed);
+#pragma unroll
+  for (int c = 1; c < 4; ++c) {
+    s0 = mfma32(a[2 * c], qB[c], s0);
+    s1 = mfma32(a[2 * c + 1], qB[c], s1);
+  }
+}
+
+// Online softmax over one key tile whose scores s = S' - m_c arrive relative to the
+// seeded reference m_c (log2 units; -inf marks an excluded key).  The reference
+// only moves when a block's maximum exceeds it by more than kRescaleSlack, so the
+// unnormalised probabilities 2^s stay below 2^kRescaleSlack and most blocks need
+// no rescale of O and l; the result is exact either way since numerator and
+// denominator share the reference.  On return pc[c] holds the bf16 probabilities
+// of key chunk c as MFMA operands and st.l has grown by their fp32 sum.
 constexpr float kRescaleSlack = 8.f;
 
-__device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& st, float sl2,
-                                             bf16x8 (&pc)[4]) {
-  float mx = fmaxf(s0[0], s1[0]);
+// ref_used is the reference the scores were seeded with (the reference can have
+// moved since, when the next block's scores are computed ahead of this softmax).
+__device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& st,
+                                             bf16x8 (&pc)[4], float ref_used) {
+  float mx = __builtin_fmaxf(s0[0], s1[0]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  mx = partner_max(mx) * sl2;
-  if (__any(mx > st.m + kRescaleSlack)) {
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = m_new == st.m ? 1.f : fast_exp2(st.m - m_new);
-    st.l *= alpha;
+  for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[r]), s1[r]);
+  mx = partner_max(mx);
+  {
+    const float now = st.m != -INFINITY ? st.m : 0.f;
+    const float shift = now - ref_used;
+    if (__any(shift != 0.f)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      st.o0[r] *= alpha;
-      st.o1[r] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        s0[r] -= shift;
+        s1[r] -= shift;
+      }
+      mx -= shift;
     }
-    st.m = m_new;
   }
-  // a row with no allowed key so far keeps m = -inf; use 0 as its reference so
-  // that exp2 of excluded scores is 0 rather than NaN
-  const float m_ref = st.m == -INFINITY ? 0.f : st.m;
-  float rs0 = 0.f, rs1 = 0.f;
+  // a row starts at its first finite score; afterwards it rescales only when the
+  // block exceeds the reference by more than the slack
+  const bool started = st.m != -INFINITY;
+  const bool need = started ? mx > kRescaleSlack : mx != -INFINITY;
+  if (__any(need)) {
+    if (need) {
+      const float mc = started ? st.m : 0.f;    // reference baked into the seed
+      const float m_new = mc + mx;
+      const float alpha = started ? fast_exp2(st.m - m_new) : 0.f;
+      st.l *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st.o0[r] *= alpha;
+        st.o1[r] *= alpha;
+        s0[r] -= mx;
+        s1[r] -= mx;
+        st.cinit[r] = -m_new;
+      }
+      st.m = m_new;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s0[r] = fast_exp2(__builtin_fmaf(s0[r], sl2, -m_ref));
-    s1[r] = fast_exp2(__builtin_fmaf(s1[r], sl2, -m_ref));
+    s0[r] = fast_exp2(s0[r]);
+    s1[r] = fast_exp2(s1[r]);
+  }
+  float rs0 = s0[0], rs1 = s1[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) {
     rs0 += s0[r];
     rs1 += s1[r];
   }
@@ -83,12 +133,16 @@ __device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& s
 // operand comes from ds_read_b64_tr_b16 reads.
 __device__ __forceinline__ void pv_tile(const uint16_t* sV, const bf16x8 (&pc)[4], int lane,
                                         FwdState& st) {
+  bf16x8 v[8];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const bf16x8 v0 = ld_tr8(sV, 0, c, lane);
-    const bf16x8 v1 = ld_tr8(sV, 1, c, lane);
-    st.o0 = mfma32(v0, pc[c], st.o0);
-    st.o1 = mfma32(v1, pc[c], st.o1);
+    v[2 * c] = ld_tr8(sV, 0, c, lane);
+    v[2 * c + 1] = ld_tr8(sV, 1, c, lane);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    st.o0 = mfma32(v[2 * c], pc[c], st.o0);
+    st.o1 = mfma32(v[2 * c + 1], pc[c], st.o1);
   }
 }
 

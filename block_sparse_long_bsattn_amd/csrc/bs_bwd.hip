@@ -104,6 +104,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
     gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
   }
+  // block index of the next tile, read one iteration ahead of its use
+  int kb_next = it.len > 1 ? keys[1] : 0;
   bf16x8 qB[4], doB[4];
   float dsum = 0.f;
   {
@@ -135,9 +137,9 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
     const bool more = t + 1 < it.len;
     if (more) {
-      const int kb = keys[t + 1];
-      gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
-      gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+      gload_nat(kr, kbase + (size_t)kb_next * kBlock * kHead, tid);
+      gload_nat(vr, vbase + (size_t)kb_next * kBlock * kHead, tid);
+      kb_next = t + 2 < it.len ? keys[t + 2] : 0;
     }
     // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
@@ -225,6 +227,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     gload_nat(dr, dobase + (size_t)qb * kBlock * kHead, tid);
     if (tid < kBlock) { lv = lbase[qb * kBlock + tid]; dval = dbase[qb * kBlock + tid]; }
   }
+  // block index of the next tile, read one iteration ahead of its use
+  int qb_next = it.len > 1 ? qblks[1] : 0;
   bf16x8 kB[4], vB[4];
   {
     const size_t off = bh_off + (size_t)krow * kHead + 8 * hl;
@@ -245,10 +249,10 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
     const bool more = t + 1 < it.len;
     if (more) {
-      const int qb = qblks[t + 1];
-      gload_nat(qr, qbase + (size_t)qb * kBlock * kHead, tid);
-      gload_nat(dr, dobase + (size_t)qb * kBlock * kHead, tid);
-      if (tid < kBlock) { lv = lbase[qb * kBlock + tid]; dval = dbase[qb * kBlock + tid]; }
+      gload_nat(qr, qbase + (size_t)qb_next * kBlock * kHead, tid);
+      gload_nat(dr, dobase + (size_t)qb_next * kBlock * kHead, tid);
+      if (tid < kBlock) { lv = lbase[qb_next * kBlock + tid]; dval = dbase[qb_next * kBlock + tid]; }
+      qb_next = t + 2 < it.len ? qblks[t + 2] : 0;
     }
     // S[q][key] = Q K^T, dP[q][key] = dO V^T; rows = queries (2 tiles), column = key
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();

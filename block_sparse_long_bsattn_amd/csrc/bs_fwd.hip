@@ -90,43 +90,44 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)it.bh * a.n * kHead;
   const int qrow = it.i * kBlock + 32 * wave + col;   // token index of this lane's query
-
   const int32_t* keys = a.col_idx + it.start;
   const uint16_t* kbase = a.k + bh_off;
   const uint16_t* vbase = a.v + bh_off;
+  const int len = it.len;
+  auto kaddr = [&](int kb) { return kbase + (size_t)kb * kBlock * kHead; };
+  auto vaddr = [&](int kb) { return vbase + (size_t)kb * kBlock * kHead; };
+
   TileRegs kr, vr;
-  if (it.len > 0) {
+  if (len > 0) {
     const int kb = keys[0];
-    gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
-    gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+    gload_nat(kr, kaddr(kb), tid);
+    gload_nat(vr, vaddr(kb), tid);
   }
+  int kb_next = len > 1 ? keys[1] : 0;
   bf16x8 qB[4];
   {
     const uint16_t* qp = a.q + bh_off + (size_t)qrow * kHead + 8 * hl;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
   }
+  scale_operands(qB, a.sl2);
   lds_store_nat(sK[0], kr, tid);
   lds_store_nat(sV[0], vr, tid);
-
   FwdState st;
   fwd_state_init(st);
-  const float sl2 = a.sl2;
-  // double buffer: block t+1 is fetched into registers during block t and stored
-  // into the other LDS buffer after it; one barrier per block
-  for (int t = 0; t < it.len; ++t) {
+  for (int t = 0; t < len; ++t) {
     const int cur = t & 1;
     __syncthreads();
-    const bool more = t + 1 < it.len;
-    if (more) {
-      const int kb = keys[t + 1];
-      gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
-      gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
-    }
+    const bool more = t + 1 < len;
     f32x16 s0, s1;
-    qk_tile(sK[cur], qB, col, hl, s0, s1);
+    qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
+    if (more) {
+      gload_nat(kr, kaddr(kb_next), tid);
+      gload_nat(vr, vaddr(kb_next), tid);
+      kb_next = t + 2 < len ? keys[t + 2] : 0;
+    }
     bf16x8 pc[4];
-    softmax_step(s0, s1, st, sl2, pc);
+    softmax_step(s0, s1, st, pc, seed_ref(st));
     pv_tile(sV[cur], pc, lane, st);
     if (more) {
       lds_store_nat(sK[cur ^ 1], kr, tid);

@@ -38,32 +38,65 @@ __device__ __forceinline__ uint64_t splitmix64_draw(uint64_t seed, uint64_t k) {
   return z ^ (z >> 31);
 }
 
-// number of entries of the sorted array a[0..n) that are <= x
-__device__ int count_le(const int32_t* a, int n, int x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if (a[mid] <= x) lo = mid + 1; else hi = mid;
+// The global block set, searched many times per row and column.  GReg keeps up to
+// kRegG entries in registers (uniform, padded with INT_MAX), so every query is a
+// few independent compares; GLds searches a sorted copy in LDS.
+constexpr int kRegG = 8;
+
+struct GReg {
+  int v[kRegG];
+  int g;
+  __device__ int count_le(int x) const {
+    int c = 0;
+#pragma unroll
+    for (int a = 0; a < kRegG; ++a) c += v[a] <= x;
+    return c;
   }
-  return lo;
-}
+  __device__ bool contains(int x) const {
+    bool f = false;
+#pragma unroll
+    for (int a = 0; a < kRegG; ++a) f |= v[a] == x;
+    return f;
+  }
+  template <typename F> __device__ void for_each(F f) const {
+#pragma unroll
+    for (int a = 0; a < kRegG; ++a)
+      if (a < g) f(a, v[a]);
+  }
+};
 
-__device__ bool contains(const int32_t* a, int n, int x) {
-  int c = count_le(a, n, x);
-  return c > 0 && a[c - 1] == x;
-}
+struct GLds {
+  const int32_t* p;
+  int g;
+  __device__ int count_le(int x) const {
+    int lo = 0, hi = g;
+    while (lo < hi) {
+      int mid = (lo + hi) >> 1;
+      if (p[mid] <= x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  }
+  __device__ bool contains(int x) const {
+    const int c = count_le(x);
+    return c > 0 && p[c - 1] == x;
+  }
+  template <typename F> __device__ void for_each(F f) const {
+    for (int a = 0; a < g; ++a) f(a, p[a]);
+  }
+};
 
+template <typename GS>
 struct RowCtx {
-  const int32_t* G;
-  int g, nb, lo, hi;   // window [lo, hi]
+  GS G;
+  int nb, lo, hi;   // window [lo, hi]
   // |E intersect [0, y]| with E = G U [lo, hi]
   __device__ int excl_le(int y) const {
-    int cg = count_le(G, g, y);
+    int cg = G.count_le(y);
     int cw = 0, cgw = 0;
     if (y >= lo) {
       int top = y < hi ? y : hi;
       cw = top - lo + 1;
-      cgw = count_le(G, g, top) - count_le(G, g, lo - 1);
+      cgw = G.count_le(top) - G.count_le(lo - 1);
     }
     return cg + cw - cgw;
   }
@@ -77,17 +110,24 @@ struct RowCtx {
     }
   }
   __device__ int excl_size() const { return excl_le(nb - 1); }
+  // window members that are not global, below x
+  __device__ int win_below(int x) const {
+    if (x <= lo) return 0;
+    const int top = x - 1 < hi ? x - 1 : hi;
+    return (top - lo + 1) - (G.count_le(top) - G.count_le(lo - 1));
+  }
 };
 
-__device__ RowCtx row_ctx(const int32_t* G, int g, int nb, int w, int i) {
+template <typename GS>
+__device__ RowCtx<GS> row_ctx(const GS& G, int nb, int w, int i) {
   const int half = (w - 1) / 2;
-  return RowCtx{G, g, nb, i - half < 0 ? 0 : i - half, i + half > nb - 1 ? nb - 1 : i + half};
+  return RowCtx<GS>{G, nb, i - half < 0 ? 0 : i - half, i + half > nb - 1 ? nb - 1 : i + half};
 }
 
-__device__ int row_length(const int32_t* G, int g, int nb, int w, int r, int i, bool& is_global) {
-  is_global = contains(G, g, i);
-  if (is_global) return nb;
-  const RowCtx c = row_ctx(G, g, nb, w, i);
+template <typename GS>
+__device__ int row_length(const GS& G, int nb, int w, int r, int i) {
+  if (G.contains(i)) return nb;
+  const RowCtx<GS> c = row_ctx(G, nb, w, i);
   const int e = c.excl_size();
   const int m = nb - e;
   return e + (r < m ? r : m);
@@ -95,27 +135,17 @@ __device__ int row_length(const int32_t* G, int g, int nb, int w, int r, int i, 
 
 // Writes row i's sorted key blocks G U [lo, hi] U R (R sorted, disjoint from the
 // rest) by rank.  cnt_r_below(x) = #{y in R : y < x}; rnd_at(t) = t-th of R.
-template <typename CountR, typename AtR>
-__device__ void write_row(const RowCtx& c, int take, CountR cnt_r_below, AtR rnd_at, int32_t* out) {
-  const int32_t* G = c.G;
-  const int g = c.g;
-  // window members that are not global, below x
-  auto win_below = [&](int x) -> int {
-    if (x <= c.lo) return 0;
-    const int top = x - 1 < c.hi ? x - 1 : c.hi;
-    return (top - c.lo + 1) - (count_le(G, g, top) - count_le(G, g, c.lo - 1));
-  };
-  for (int a = 0; a < g; ++a) {
-    const int x = G[a];
-    out[a + win_below(x) + cnt_r_below(x)] = x;
-  }
+template <typename GS, typename CountR, typename AtR>
+__device__ void write_row(const RowCtx<GS>& c, int take, CountR cnt_r_below, AtR rnd_at,
+                          int32_t* out) {
+  c.G.for_each([&](int a, int x) { out[a + c.win_below(x) + cnt_r_below(x)] = x; });
   for (int x = c.lo; x <= c.hi; ++x) {
-    if (contains(G, g, x)) continue;
-    out[count_le(G, g, x - 1) + win_below(x) + cnt_r_below(x)] = x;
+    if (c.G.contains(x)) continue;
+    out[c.G.count_le(x - 1) + c.win_below(x) + cnt_r_below(x)] = x;
   }
   for (int t = 0; t < take; ++t) {
     const int x = rnd_at(t);
-    out[count_le(G, g, x - 1) + win_below(x) + t] = x;
+    out[c.G.count_le(x - 1) + c.win_below(x) + t] = x;
   }
 }
 
@@ -123,7 +153,8 @@ __device__ void write_row(const RowCtx& c, int take, CountR cnt_r_below, AtR rnd
 // Fisher-Yates whose swaps are logged per step (position written, value); the
 // value at a position is the latest logged write to it, else the untouched
 // candidate.  Positions below the current step are never read again.
-__device__ void draw_fast(const RowCtx& c, int m, int take, uint64_t seed, uint64_t k0,
+template <typename GS>
+__device__ void draw_fast(const RowCtx<GS>& c, int m, int take, uint64_t seed, uint64_t k0,
                           int (&rnd)[kFastR]) {
   int key[kFastR], val[kFastR];
 #pragma unroll
@@ -163,7 +194,8 @@ __device__ void draw_fast(const RowCtx& c, int m, int take, uint64_t seed, uint6
 }
 
 // General r (up to kMaxR): the same algorithm with per-thread arrays.
-__device__ void draw_any(const RowCtx& c, int m, int take, uint64_t seed, uint64_t k0,
+template <typename GS>
+__device__ void draw_any(const RowCtx<GS>& c, int m, int take, uint64_t seed, uint64_t k0,
                          int* rnd) {
   int key[kMaxR], val[kMaxR];
   for (int t = 0; t < take; ++t) {
@@ -190,13 +222,14 @@ __device__ void draw_any(const RowCtx& c, int m, int take, uint64_t seed, uint64
 // Build row i of head h: its sorted list at out and its random picks marked in
 // the column-major bitmap (word (j, i/32) of head h's bitmap `hb`, wpc words per
 // column; atomics on LDS or global memory).
-__device__ void build_row(const int32_t* G, int g, int nb, int w, int r, uint64_t seed, int h,
-                          int i, int32_t* out, uint32_t* hb, int wpc) {
-  if (contains(G, g, i)) {
+template <typename GS>
+__device__ void build_row(const GS& G, int nb, int w, int r, uint64_t seed, int h, int i,
+                          int32_t* out, uint32_t* hb, int wpc) {
+  if (G.contains(i)) {
     for (int j = 0; j < nb; ++j) out[j] = j;
     return;
   }
-  const RowCtx c = row_ctx(G, g, nb, w, i);
+  const RowCtx<GS> c = row_ctx(G, nb, w, i);
   const int m = nb - c.excl_size();
   const int take = r < m ? r : m;
   const uint64_t k0 = (uint64_t)((int64_t)h * nb + i) * (uint64_t)r + 1;
@@ -233,112 +266,135 @@ __device__ void build_row(const int32_t* G, int g, int nb, int w, int r, uint64_
   }
 }
 
-// Column j: length, and the ascending list.  The query blocks seeing key block j
-// are all blocks when j is global, otherwise the global blocks, the non-global
-// blocks within the window of j, and the blocks whose random draw picked j; the
-// three sets are disjoint.
-__device__ int col_length(const int32_t* G, int g, int nb, int w, int j, const uint32_t* bits,
-                          int wpc) {
-  if (contains(G, g, j)) return nb;
-  const int half = (w - 1) / 2;
-  const int lo = j - half < 0 ? 0 : j - half, hi = j + half > nb - 1 ? nb - 1 : j + half;
-  int n = g + (hi - lo + 1) - (count_le(G, g, hi) - count_le(G, g, lo - 1));
+// Column j.  The query blocks seeing key block j are all blocks when j is global,
+// otherwise the global blocks, the non-global blocks within the window of j, and
+// the blocks whose random draw picked j (bitmap bits); the three sets are
+// disjoint, so the list is written by rank like the rows.
+template <typename GS>
+__device__ int col_length(const GS& G, int nb, int w, int j, const uint32_t* bits, int wpc) {
+  if (G.contains(j)) return nb;
+  const RowCtx<GS> c = row_ctx(G, nb, w, j);
+  int n = G.g + c.win_below(c.hi + 1);
   for (int x = 0; x < wpc; ++x) n += __popc(bits[x]);
   return n;
 }
 
-__device__ void write_col(const int32_t* G, int g, int nb, int w, int j, uint32_t* bits, int wpc,
+template <typename GS>
+__device__ void write_col(const GS& G, int nb, int w, int j, uint32_t* bits, int wpc,
                           int32_t* out) {
-  int k = 0;
-  if (contains(G, g, j)) {
-    for (int i = 0; i < nb; ++i) out[k++] = i;
+  if (G.contains(j)) {
+    for (int i = 0; i < nb; ++i) out[i] = i;
   } else {
-    const int half = (w - 1) / 2;
-    const int lo = j - half < 0 ? 0 : j - half, hi = j + half > nb - 1 ? nb - 1 : j + half;
-    int pg = 0, pw = lo, x = 0;
-    uint32_t word = wpc > 0 ? bits[0] : 0u;
-    const int big = 1 << 30;
-    for (;;) {
-      while (pw <= hi && contains(G, g, pw)) ++pw;       // window rows exclude G
-      while (word == 0u && x + 1 < wpc) word = bits[++x];
-      const int vg = pg < g ? G[pg] : big;
-      const int vw = pw <= hi ? pw : big;
-      const int vr = word ? 32 * x + __builtin_ctz(word) : big;
-      int v = vg < vw ? vg : vw;
-      v = v < vr ? v : vr;
-      if (v == big) break;
-      out[k++] = v;
-      if (v == vg) ++pg;
-      else if (v == vw) ++pw;
-      else word &= word - 1u;
+    const RowCtx<GS> c = row_ctx(G, nb, w, j);
+    // random rows below x, from the bitmap
+    auto rnd_below = [&](int x) -> int {
+      int n = 0;
+      const int wx = x >> 5;
+      for (int y = 0; y < wx && y < wpc; ++y) n += __popc(bits[y]);
+      if (wx < wpc && (x & 31)) n += __popc(bits[wx] & ((1u << (x & 31)) - 1u));
+      return n;
+    };
+    G.for_each([&](int a, int x) { out[a + c.win_below(x) + rnd_below(x)] = x; });
+    for (int x = c.lo; x <= c.hi; ++x) {
+      if (G.contains(x)) continue;
+      out[G.count_le(x - 1) + c.win_below(x) + rnd_below(x)] = x;
+    }
+    int t = 0;
+    for (int y = 0; y < wpc; ++y) {
+      uint32_t word = bits[y];
+      while (word) {
+        const int x = 32 * y + __builtin_ctz(word);
+        word &= word - 1u;
+        out[G.count_le(x - 1) + c.win_below(x) + t] = x;
+        ++t;
+      }
     }
   }
   for (int y = 0; y < wpc; ++y) bits[y] = 0u;          // ready for the next draw
 }
 
-// inclusive Hillis-Steele scan of part[0..kBuildThreads) in LDS
-__device__ void block_scan(int* part, int tid) {
-  for (int off = 1; off < kBuildThreads; off <<= 1) {
-    int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+// exclusive scan of v over the work-group (kBuildThreads threads); `part` holds
+// one int per wave.  Returns the exclusive prefix.
+__device__ int block_exclusive_scan(int v, int* part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
+  if (lane == 63) part[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int q = 0; q < wave; ++q) base += part[q];
+  __syncthreads();
+  return base + x - v;
+}
+
+template <typename GS>
+__device__ GS load_gset(const int32_t* Gglob, int g, int32_t* lds);
+
+template <>
+__device__ GReg load_gset<GReg>(const int32_t* Gglob, int g, int32_t*) {
+  GReg G;
+  G.g = g;
+#pragma unroll
+  for (int a = 0; a < kRegG; ++a) G.v[a] = a < g ? Gglob[a] : 0x7fffffff;
+  return G;
+}
+
+template <>
+__device__ GLds load_gset<GLds>(const int32_t* Gglob, int g, int32_t* lds) {
+  for (int x = threadIdx.x; x < g; x += blockDim.x) lds[x] = Gglob[x];
+  __syncthreads();
+  return GLds{lds, g};
 }
 
 __global__ __launch_bounds__(kBuildThreads) void layout_rowptr_kernel(
-    const int32_t* __restrict__ G, int g, int nb, int w, int r, int heads,
+    const int32_t* __restrict__ Gglob, int g, int nb, int w, int r, int heads,
     int64_t nnz_per_head, int32_t* __restrict__ row_ptr) {
-  __shared__ int part[kBuildThreads];
+  extern __shared__ int32_t sG[];
+  __shared__ int part[kBuildThreads / 64];
+  const GLds G = load_gset<GLds>(Gglob, g, sG);
   const int tid = threadIdx.x;
   const int per = (nb + kBuildThreads - 1) / kBuildThreads;
   const int i0 = min(nb, tid * per), i1 = min(nb, i0 + per);
   int local = 0;
-  for (int i = i0; i < i1; ++i) {
-    bool gl;
-    local += row_length(G, g, nb, w, r, i, gl);
-  }
-  part[tid] = local;
-  __syncthreads();
-  block_scan(part, tid);
-  int pos = part[tid] - local;
+  for (int i = i0; i < i1; ++i) local += row_length(G, nb, w, r, i);
+  int pos = block_exclusive_scan(local, part);
   for (int i = i0; i < i1; ++i) {
     for (int h = 0; h < heads; ++h) row_ptr[(int64_t)h * nb + i] = (int32_t)(h * nnz_per_head + pos);
-    bool gl;
-    pos += row_length(G, g, nb, w, r, i, gl);
+    pos += row_length(G, nb, w, r, i);
   }
   if (tid == 0) row_ptr[(int64_t)heads * nb] = (int32_t)(heads * nnz_per_head);
 }
 
 // One work-group per head, nb <= kLdsBitmapNb: bitmap (nb x wpc words) in LDS.
+template <typename GS>
 __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     const int32_t* __restrict__ Gglob, int g, int nb, int w, int r, uint64_t seed,
     int64_t nnz_per_head, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
     int32_t* __restrict__ csc_ptr, int32_t* __restrict__ csc_idx) {
-  extern __shared__ int32_t dyn[];          // G[g] then bitmap[nb * wpc]
-  __shared__ int part[kBuildThreads];
+  extern __shared__ int32_t dyn[];          // bitmap[nb * wpc], then G[g] for GLds
+  __shared__ int part[kBuildThreads / 64];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int wpc = (nb + 31) / 32;
-  int32_t* sG = dyn;
-  uint32_t* bm = reinterpret_cast<uint32_t*>(dyn + g);
-  for (int x = tid; x < g; x += kBuildThreads) sG[x] = Gglob[x];
+  uint32_t* bm = reinterpret_cast<uint32_t*>(dyn);
   for (int x = tid; x < nb * wpc; x += kBuildThreads) bm[x] = 0u;
+  const GS G = load_gset<GS>(Gglob, g, dyn + nb * wpc);
   __syncthreads();
   for (int i = tid; i < nb; i += kBuildThreads)
-    build_row(sG, g, nb, w, r, seed, h, i, col_idx + row_ptr[(int64_t)h * nb + i], bm, wpc);
+    build_row(G, nb, w, r, seed, h, i, col_idx + row_ptr[(int64_t)h * nb + i], bm, wpc);
   __syncthreads();
   const int per = (nb + kBuildThreads - 1) / kBuildThreads;
   const int j0 = min(nb, tid * per), j1 = min(nb, j0 + per);
   int local = 0;
-  for (int j = j0; j < j1; ++j) local += col_length(sG, g, nb, w, j, bm + j * wpc, wpc);
-  part[tid] = local;
-  __syncthreads();
-  block_scan(part, tid);
-  int64_t pos = (int64_t)h * nnz_per_head + (part[tid] - local);
+  for (int j = j0; j < j1; ++j) local += col_length(G, nb, w, j, bm + j * wpc, wpc);
+  int64_t pos = (int64_t)h * nnz_per_head + block_exclusive_scan(local, part);
   for (int j = j0; j < j1; ++j) {
     csc_ptr[(int64_t)h * nb + j] = (int32_t)pos;
-    const int len = col_length(sG, g, nb, w, j, bm + j * wpc, wpc);
-    write_col(sG, g, nb, w, j, bm + j * wpc, wpc, csc_idx + pos);
+    const int len = col_length(G, nb, w, j, bm + j * wpc, wpc);
+    write_col(G, nb, w, j, bm + j * wpc, wpc, csc_idx + pos);
     pos += len;
   }
   if (h == gridDim.x - 1 && tid == kBuildThreads - 1)
@@ -347,43 +403,39 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
 
 // Larger layouts, phase 1: one thread per (head, query block); bitmap in global
 // memory, zero on entry (cleared by phase 2 of the previous build).
+template <typename GS>
 __global__ __launch_bounds__(64) void layout_rows_kernel(
     const int32_t* __restrict__ Gglob, int g, int nb, int w, int r, int heads, uint64_t seed,
     const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
     uint32_t* __restrict__ rbits, int wpc) {
   extern __shared__ int32_t sG[];
-  for (int x = threadIdx.x; x < g; x += 64) sG[x] = Gglob[x];
-  __syncthreads();
+  const GS G = load_gset<GS>(Gglob, g, sG);
   const int idx = blockIdx.x * 64 + threadIdx.x;
   if (idx >= heads * nb) return;
   const int h = idx / nb, i = idx - h * nb;
-  build_row(sG, g, nb, w, r, seed, h, i, col_idx + row_ptr[idx], rbits + (int64_t)h * nb * wpc,
-            wpc);
+  build_row(G, nb, w, r, seed, h, i, col_idx + row_ptr[idx], rbits + (int64_t)h * nb * wpc, wpc);
 }
 
 // Larger layouts, phase 2: one work-group per head; clears the bitmap.
+template <typename GS>
 __global__ __launch_bounds__(kBuildThreads) void layout_cols_kernel(
     const int32_t* __restrict__ Gglob, int g, int nb, int w, int64_t nnz_per_head,
     uint32_t* __restrict__ rbits, int wpc, int32_t* __restrict__ csc_ptr,
     int32_t* __restrict__ csc_idx) {
-  __shared__ int part[kBuildThreads];
   extern __shared__ int32_t sG[];
+  __shared__ int part[kBuildThreads / 64];
   const int h = blockIdx.x, tid = threadIdx.x;
-  for (int x = tid; x < g; x += kBuildThreads) sG[x] = Gglob[x];
-  __syncthreads();
+  const GS G = load_gset<GS>(Gglob, g, sG);
   uint32_t* hb = rbits + (int64_t)h * nb * wpc;
   const int per = (nb + kBuildThreads - 1) / kBuildThreads;
   const int j0 = min(nb, tid * per), j1 = min(nb, j0 + per);
   int local = 0;
-  for (int j = j0; j < j1; ++j) local += col_length(sG, g, nb, w, j, hb + (int64_t)j * wpc, wpc);
-  part[tid] = local;
-  __syncthreads();
-  block_scan(part, tid);
-  int64_t pos = (int64_t)h * nnz_per_head + (part[tid] - local);
+  for (int j = j0; j < j1; ++j) local += col_length(G, nb, w, j, hb + (int64_t)j * wpc, wpc);
+  int64_t pos = (int64_t)h * nnz_per_head + block_exclusive_scan(local, part);
   for (int j = j0; j < j1; ++j) {
     csc_ptr[(int64_t)h * nb + j] = (int32_t)pos;
-    const int len = col_length(sG, g, nb, w, j, hb + (int64_t)j * wpc, wpc);
-    write_col(sG, g, nb, w, j, hb + (int64_t)j * wpc, wpc, csc_idx + pos);
+    const int len = col_length(G, nb, w, j, hb + (int64_t)j * wpc, wpc);
+    write_col(G, nb, w, j, hb + (int64_t)j * wpc, wpc, csc_idx + pos);
     pos += len;
   }
   if (h == gridDim.x - 1 && tid == kBuildThreads - 1)
@@ -395,39 +447,48 @@ __global__ __launch_bounds__(kBuildThreads) void layout_cols_kernel(
 int launch_layout_rowptr(bsattn_layout* L, hipStream_t stream) {
   {
     ProfScope prof_("layout_rowptr", stream);
-    hipLaunchKernelGGL(layout_rowptr_kernel, dim3(1), dim3(kBuildThreads), 0, stream, L->d_gblk,
-                       L->g, L->nb, L->w, L->r, L->heads, L->nnz_per_head, L->d_row_ptr);
+    hipLaunchKernelGGL(layout_rowptr_kernel, dim3(1), dim3(kBuildThreads),
+                       (size_t)L->g * sizeof(int32_t), stream, L->d_gblk, L->g, L->nb, L->w,
+                       L->r, L->heads, L->nnz_per_head, L->d_row_ptr);
   }
   return check_hip(hipGetLastError(), "layout_rowptr launch");
 }
 
-int launch_layout_build(bsattn_layout* L, hipStream_t stream) {
+namespace {
+template <typename GS>
+int launch_build(bsattn_layout* L, hipStream_t stream) {
   const int wpc = (L->nb + 31) / 32;
+  const size_t g_lds = (size_t)L->g * sizeof(int32_t);
   if (L->nb <= kLdsBitmapNb) {
-    const size_t lds = ((size_t)L->g + (size_t)L->nb * wpc) * sizeof(int32_t);
+    const size_t lds = (size_t)L->nb * wpc * sizeof(uint32_t) + g_lds;
     {
       ProfScope prof_("layout_head", stream);
-      hipLaunchKernelGGL(layout_head_kernel, dim3(L->heads), dim3(kBuildThreads), lds, stream,
-                         L->d_gblk, L->g, L->nb, L->w, L->r, L->seed, L->nnz_per_head,
+      hipLaunchKernelGGL(layout_head_kernel<GS>, dim3(L->heads), dim3(kBuildThreads), lds,
+                         stream, L->d_gblk, L->g, L->nb, L->w, L->r, L->seed, L->nnz_per_head,
                          L->d_row_ptr, L->d_col_idx, L->d_csc_ptr, L->d_csc_idx);
     }
     return check_hip(hipGetLastError(), "layout_head launch");
   }
   {
     ProfScope prof_("layout_rows", stream);
-    hipLaunchKernelGGL(layout_rows_kernel, dim3((L->heads * L->nb + 63) / 64), dim3(64),
-                       (size_t)L->g * sizeof(int32_t), stream, L->d_gblk, L->g, L->nb, L->w,
-                       L->r, L->heads, L->seed, L->d_row_ptr, L->d_col_idx, L->d_rbits, wpc);
+    hipLaunchKernelGGL(layout_rows_kernel<GS>, dim3((L->heads * L->nb + 63) / 64), dim3(64),
+                       g_lds, stream, L->d_gblk, L->g, L->nb, L->w, L->r, L->heads, L->seed,
+                       L->d_row_ptr, L->d_col_idx, L->d_rbits, wpc);
   }
   int st = check_hip(hipGetLastError(), "layout_rows launch");
   if (st) return st;
   {
     ProfScope prof_("layout_cols", stream);
-    hipLaunchKernelGGL(layout_cols_kernel, dim3(L->heads), dim3(kBuildThreads),
-                       (size_t)L->g * sizeof(int32_t), stream, L->d_gblk, L->g, L->nb, L->w,
-                       L->nnz_per_head, L->d_rbits, wpc, L->d_csc_ptr, L->d_csc_idx);
+    hipLaunchKernelGGL(layout_cols_kernel<GS>, dim3(L->heads), dim3(kBuildThreads), g_lds,
+                       stream, L->d_gblk, L->g, L->nb, L->w, L->nnz_per_head, L->d_rbits, wpc,
+                       L->d_csc_ptr, L->d_csc_idx);
   }
   return check_hip(hipGetLastError(), "layout_cols launch");
+}
+}  // namespace
+
+int launch_layout_build(bsattn_layout* L, hipStream_t stream) {
+  return L->g <= kRegG ? launch_build<GReg>(L, stream) : launch_build<GLds>(L, stream);
 }
 
 }  // namespace bsattn

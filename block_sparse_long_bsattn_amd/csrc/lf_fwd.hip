@@ -113,9 +113,9 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
     return ballot64(ok);
   };
 
+  scale_operands(qB, a.sl2);
   FwdState st;
   fwd_state_init(st);
-  const float sl2 = a.sl2;
   const uint16_t* kg_bh = a.kg + (size_t)bh * a.ngt * kBlock * kHead;
   const uint16_t* vg_bh = a.vg + (size_t)bh * a.ngt * kBlock * kHead;
   auto tile_src = [&](int x, const uint16_t*& ks, const uint16_t*& vs) {
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
       gload_nat(vr, vs, tid);
     }
     f32x16 s0, s1;
-    qk_tile(sK[cur], qB, col, hl, s0, s1);
+    qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
     if (x < nband) {
       const int u0 = (lo_u + x) * kBlock;
       // the whole tile lies in the band iff its farthest pair does
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
       }
     }
     bf16x8 pc[4];
-    softmax_step(s0, s1, st, sl2, pc);
+    softmax_step(s0, s1, st, pc, seed_ref(st));
     pv_tile(sV[cur], pc, lane, st);
     if (xn < ntile) {
       lds_store_nat(sK[cur ^ 1], kr, tid);
@@ -221,6 +221,7 @@ __global__ __launch_bounds__(kThreads) void lf_global_kernel(LfArgs a) {
   }
   const int u_begin = s * kSeg;
   const int u_end = min(a.nt, u_begin + kSeg);
+  scale_operands(qB, a.sl2);
   FwdState st;
   fwd_state_init(st);
   TileRegs kr, vr;
@@ -237,9 +238,9 @@ __global__ __launch_bounds__(kThreads) void lf_global_kernel(LfArgs a) {
       gload_nat(vr, a.v + bh_off + (size_t)(u + 1) * kBlock * kHead, tid);
     }
     f32x16 s0, s1;
-    qk_tile(sK[cur], qB, col, hl, s0, s1);
+    qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
     bf16x8 pc[4];
-    softmax_step(s0, s1, st, a.sl2, pc);
+    softmax_step(s0, s1, st, pc, seed_ref(st));
     pv_tile(sV[cur], pc, lane, st);
     if (more) {
       lds_store_nat(sK[cur ^ 1], kr, tid);

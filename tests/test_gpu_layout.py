@@ -60,6 +60,8 @@ def test_layout_edge_cases_bit_exact():
     compare(64 * 600, 2, [0, 7, 599], 3, 3, 99)      # more than 512 blocks: two-kernel path
     compare(64 * 600, 1, [1, 300], 5, 12, 98)        # ... with more than 8 random blocks
     compare(64 * 40, 3, [2], 3, 9, 97)               # more than 8 random blocks
+    compare(64 * 600, 1, list(range(0, 600, 50)), 3, 3, 96)   # > 512 blocks, > 8 global
+    compare(64 * 100, 2, list(range(3, 100, 9)), 5, 4, 95)    # > 8 global blocks
 
 
 def test_layout_rebuild_matches_new_seed():
