@@ -15,7 +15,7 @@
 //                kSeg-block items writing fp32 partials, summed here in segment
 //                order, so results are bitwise reproducible.
 
-#include "common.hpp"
+#include "attn_tile.hpp"
 #include "internal.hpp"
 
 namespace bsattn {
@@ -126,8 +126,16 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   }
   const float Dq = partner_sum(dsum);   // D = rowsum(dO * O)
   if (it.seg == 0 && hl == 0) a.dbuf[(size_t)it.bh * a.n + qrow] = Dq;
+  // Q pre-scaled by scale*log2(e) exactly as in the forward, and the accumulators
+  // seeded so that the MFMAs return S*scale*log2(e) - lse*log2(e) and dP - D
+  scale_operands(qB, a.sl2);
   const float lse2 = a.lse[(size_t)it.bh * a.n + qrow] * kLog2e;
-  const float sl2 = a.sl2;
+  f32x16 seed_s, seed_d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    seed_s[r] = -lse2;
+    seed_d[r] = -Dq;
+  }
   lds_store_nat(sK[0], kr, tid);
   lds_store_nat(sV[0], vr, tid);
 
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
       kb_next = t + 2 < it.len ? keys[t + 2] : 0;
     }
     // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
-    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
+    f32x16 s0 = seed_s, s1 = seed_s, p0 = seed_d, p1 = seed_d;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const bf16x8 k0 = ld16(sK[cur] + col * kLdsStride + 16 * c + 8 * hl);
@@ -156,10 +164,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e0 = fast_exp2(__builtin_fmaf(s0[r], sl2, -lse2));
-      const float e1 = fast_exp2(__builtin_fmaf(s1[r], sl2, -lse2));
-      s0[r] = e0 * (p0[r] - Dq);
-      s1[r] = e1 * (p1[r] - Dq);
+      s0[r] = fast_exp2(s0[r]) * p0[r];      // dS = P * (dP - D)
+      s1[r] = fast_exp2(s1[r]) * p1[r];
     }
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]; K^T from transpose reads
     const bf16x8 dc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
@@ -203,8 +209,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
 __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kBlock * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t sO[2][kBlock * kLdsStride];   // dO
-  __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // lse * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[2][kBlock];
+  __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
 
   const int v = xcd_remap(blockIdx.x, a.total_items);
   if (v >= a.total_items) return;
@@ -238,12 +244,14 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
       vB[c] = ld16(a.v + off + 16 * c);
     }
   }
+  // K pre-scaled by scale*log2(e) (the products match the forward's scaled-Q ones
+  // up to bf16 rounding); sL and sD hold -lse*log2(e) and -D to seed S and dP
+  scale_operands(kB, a.sl2);
   lds_store_nat(sQ[0], qr, tid);
   lds_store_nat(sO[0], dr, tid);
-  if (tid < kBlock) { sL[0][tid] = lv * kLog2e; sD[0][tid] = dval; }
+  if (tid < kBlock) { sL[0][tid] = -lv * kLog2e; sD[0][tid] = -dval; }
 
   f32x16 dv0 = zero16(), dv1 = zero16(), dk0 = zero16(), dk1 = zero16();
-  const float sl2 = a.sl2;
   for (int t = 0; t < it.len; ++t) {
     const int cur = t & 1;
     __syncthreads();
@@ -254,8 +262,24 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
       if (tid < kBlock) { lv = lbase[qb_next * kBlock + tid]; dval = dbase[qb_next * kBlock + tid]; }
       qb_next = t + 2 < it.len ? qblks[t + 2] : 0;
     }
-    // S[q][key] = Q K^T, dP[q][key] = dO V^T; rows = queries (2 tiles), column = key
-    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
+    // S[q][key] = Q K^T, dP[q][key] = dO V^T; rows = queries (2 tiles), column = key.
+    // Row q of register r is 32*qt + 8*(r/4) + 4*hl + r%4: the seeds are the
+    // matching -lse*log2(e) and -D values.
+    f32x16 s0, s1, p0, p1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sL[cur][8 * j + 4 * hl]);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sL[cur][32 + 8 * j + 4 * hl]);
+      const f32x4 D0 = *reinterpret_cast<const f32x4*>(&sD[cur][8 * j + 4 * hl]);
+      const f32x4 D1 = *reinterpret_cast<const f32x4*>(&sD[cur][32 + 8 * j + 4 * hl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s0[4 * j + e] = l0[e];
+        s1[4 * j + e] = l1[e];
+        p0[4 * j + e] = D0[e];
+        p1[4 * j + e] = D1[e];
+      }
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const bf16x8 q0 = ld16(sQ[cur] + col * kLdsStride + 16 * c + 8 * hl);
@@ -267,23 +291,12 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
       p0 = mfma32(o0, vB[c], p0);
       p1 = mfma32(o1, vB[c], p1);
     }
-    // rows held by this lane: q = 32*qt + 8*j + 4*hl + e
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sL[cur][8 * j + 4 * hl]);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sL[cur][32 + 8 * j + 4 * hl]);
-      const f32x4 D0 = *reinterpret_cast<const f32x4*>(&sD[cur][8 * j + 4 * hl]);
-      const f32x4 D1 = *reinterpret_cast<const f32x4*>(&sD[cur][32 + 8 * j + 4 * hl]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * j + e;
-        const float e0 = fast_exp2(__builtin_fmaf(s0[r], sl2, -l0[e]));
-        const float e1 = fast_exp2(__builtin_fmaf(s1[r], sl2, -l1[e]));
-        s0[r] = e0;                       // P
-        s1[r] = e1;
-        p0[r] = e0 * (p0[r] - D0[e]);     // dS
-        p1[r] = e1 * (p1[r] - D1[e]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = fast_exp2(s0[r]);             // P
+      s1[r] = fast_exp2(s1[r]);
+      p0[r] *= s0[r];                       // dS = P * (dP - D)
+      p1[r] *= s1[r];
     }
     // dV^T[d][key] += sum_q dO^T[d][q] P[q][key];  dK^T[d][key] += sum_q Q^T[d][q] dS[q][key]
     const bf16x8 pc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
@@ -298,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     if (more) {
       lds_store_nat(sQ[cur ^ 1], qr, tid);
       lds_store_nat(sO[cur ^ 1], dr, tid);
-      if (tid < kBlock) { sL[cur ^ 1][tid] = lv * kLog2e; sD[cur ^ 1][tid] = dval; }
+      if (tid < kBlock) { sL[cur ^ 1][tid] = -lv * kLog2e; sD[cur ^ 1][tid] = -dval; }
     }
   }
 
