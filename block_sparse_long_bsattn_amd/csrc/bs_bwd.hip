@@ -250,6 +250,9 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   lds_store_nat(sQ[0], qr, tid);
   lds_store_nat(sO[0], dr, tid);
   if (tid < kBlock) { sL[0][tid] = -lv * kLog2e; sD[0][tid] = -dval; }
+  // vB is first read inside the loop: drain the prologue's loads here, or the
+  // loop's first use of vB waits on every iteration's tile prefetch as well
+  wait_all_loads();
 
   f32x16 dv0 = zero16(), dv1 = zero16(), dk0 = zero16(), dk1 = zero16();
   for (int t = 0; t < it.len; ++t) {

@@ -93,6 +93,12 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0).  Placed before a loop whose body first
+// reads registers loaded ahead of it: the compiler's wait for them would otherwise
+// stay inside the loop and, since the counter is shared, also wait for the loads
+// each iteration issues for the next one.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
 // ---------------------------------------------------------------------------
 // Cooperative 64x64 bf16 tile staging through LDS (128 threads): LDS row x holds
 // global row x (64 values + pad).  Thread t moves 16-byte chunk (t % 8) of rows

@@ -11,14 +11,15 @@
 // Kernels:
 //   layout_rowptr (at build only): row lengths -> row offsets (block scan); they do
 //                 not depend on the draws, so a redraw keeps them.
-//   layout_head   (n/b <= 512): one work-group per head does everything: rows,
-//                 random picks marked in an LDS bitmap, column lengths, column
-//                 offsets (block scan) and column lists.
-//   layout_rows + layout_cols (larger n/b): the same two phases as separate
-//                 kernels with the bitmap in global memory (cleared after use).
-// Row lists are written by rank: the position of a key block in the sorted union
-// G U W_i U R_i is the number of union members below it, so no merge buffers are
-// needed.  Random draws for r <= 8 stay in registers.
+//   layout_head   (n/b <= 512): one work-group per head.  Rows and columns are
+//                 bitmaps in registers (row i = G | window | R_i; column j = G |
+//                 window | rows that drew j), the lists are their set bits in
+//                 ascending order, the column offsets a block scan.
+//   layout_rows + layout_cols (larger n/b): one thread per row, then one
+//                 work-group per head for the columns, with the random picks in a
+//                 global bitmap (cleared after use).  Row and column lists are
+//                 written by rank: the position of a block in the sorted union is
+//                 the number of union members below it.
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -369,36 +370,199 @@ __global__ __launch_bounds__(kBuildThreads) void layout_rowptr_kernel(
   if (tid == 0) row_ptr[(int64_t)heads * nb] = (int32_t)(heads * nnz_per_head);
 }
 
-// One work-group per head, nb <= kLdsBitmapNb: bitmap (nb x wpc words) in LDS.
-template <typename GS>
+// ---------------------------------------------------------------------------
+// One work-group per head for n/b <= 512.  Every row and column of the head is a
+// bitmap of W 64-bit words in registers: row i is G | window(i) | R_i, column j is
+// G | window(j) | {i : j in R_i} (all rows when j is global), and the sorted
+// lists come out of a lowest-set-bit walk.  The i-th entry of the ascending
+// candidate list is the i-th set bit of the row's free-block bitmap.
+// ---------------------------------------------------------------------------
+
+// bits lo..hi of the whole bitmap (inclusive; may be empty or reach past either
+// end) that fall in word k
+__device__ __forceinline__ uint64_t span_bits(int k, int lo, int hi) {
+  const int a = max(lo - 64 * k, 0), b = min(hi - 64 * k, 63);
+  if (a > b) return 0ull;
+  const uint64_t upto = b == 63 ? ~0ull : (2ull << b) - 1ull;
+  return upto & ~((1ull << a) - 1ull);
+}
+
+template <int W>
+__device__ __forceinline__ bool bit_of(const uint64_t (&b)[W], int x) {
+  uint64_t v = 0;
+#pragma unroll
+  for (int k = 0; k < W; ++k) v = (x >> 6) == k ? b[k] : v;
+  return (v >> (x & 63)) & 1ull;
+}
+
+template <int W>
+__device__ __forceinline__ void set_bit(uint64_t (&b)[W], int x) {
+#pragma unroll
+  for (int k = 0; k < W; ++k)
+    if ((x >> 6) == k) b[k] |= 1ull << (x & 63);
+}
+
+// position of the x-th (0-based) set bit; x < popcount(f)
+template <int W>
+__device__ __forceinline__ int select_bit(const uint64_t (&f)[W], int x) {
+  uint64_t word = 0;
+  int base = 0;
+  bool found = false;
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    const int c = __popcll(f[k]);
+    const bool here = !found && x < c;
+    word = here ? f[k] : word;
+    base = here ? 64 * k : base;
+    x = (found || here) ? x : x - c;
+    found = found || here;
+  }
+  int pos = 0;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    const int c = __popcll(word & ((1ull << s) - 1ull));
+    if (x >= c) {
+      x -= c;
+      word >>= s;
+      pos += s;
+    }
+  }
+  return base + pos;
+}
+
+// u mod d for 1 <= d < 2^15 with 32-bit remainders only:
+// u = hi 2^32 + lo, so u mod d = ((hi mod d)(2^32 mod d) + lo mod d) mod d
+__device__ __forceinline__ uint32_t mod_small(uint64_t u, uint32_t d) {
+  const uint32_t hi = (uint32_t)(u >> 32), lo = (uint32_t)u;
+  const uint32_t p32 = (0xffffffffu % d + 1u) % d;
+  return ((hi % d) * p32 + lo % d) % d;
+}
+
+template <int W>
+__device__ __forceinline__ int write_bits(const uint64_t (&b)[W], int32_t* out) {
+  int q = 0;
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    uint64_t x = b[k];
+    while (x) {
+      out[q++] = 64 * k + __builtin_ctzll(x);
+      x &= x - 1ull;
+    }
+  }
+  return q;
+}
+
+// RMAX bounds r: the swap log of the partial Fisher-Yates lives in registers for
+// RMAX <= 8 (fully unrolled), in per-thread memory otherwise.
+template <int W, int RMAX>
 __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     const int32_t* __restrict__ Gglob, int g, int nb, int w, int r, uint64_t seed,
     int64_t nnz_per_head, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
     int32_t* __restrict__ csc_ptr, int32_t* __restrict__ csc_idx) {
-  extern __shared__ int32_t dyn[];          // bitmap[nb * wpc], then G[g] for GLds
+  // dynamic LDS: random picks per key block (nb x wpc words, bit i = query block
+  // i), the global list G[g], then every column's offset within the head
+  extern __shared__ int32_t dyn[];
+  __shared__ uint32_t sGb[2 * W];
   __shared__ int part[kBuildThreads / 64];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int wpc = (nb + 31) / 32;
-  uint32_t* bm = reinterpret_cast<uint32_t*>(dyn);
-  for (int x = tid; x < nb * wpc; x += kBuildThreads) bm[x] = 0u;
-  const GS G = load_gset<GS>(Gglob, g, dyn + nb * wpc);
+  uint32_t* colmap = reinterpret_cast<uint32_t*>(dyn);
+  int32_t* sG = dyn + nb * wpc;
+  int32_t* sColPos = sG + g;
+  for (int x = tid; x < nb * wpc; x += kBuildThreads) colmap[x] = 0u;
+  for (int x = tid; x < g; x += kBuildThreads) sG[x] = Gglob[x];
+  if (tid < 2 * W) sGb[tid] = 0u;
   __syncthreads();
-  for (int i = tid; i < nb; i += kBuildThreads)
-    build_row(G, nb, w, r, seed, h, i, col_idx + row_ptr[(int64_t)h * nb + i], bm, wpc);
+  for (int x = tid; x < g; x += kBuildThreads) atomicOr(&sGb[sG[x] >> 5], 1u << (sG[x] & 31));
   __syncthreads();
+  uint64_t gb[W], valid[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    gb[k] = sGb[2 * k] | ((uint64_t)sGb[2 * k + 1] << 32);
+    valid[k] = span_bits(k, 0, nb - 1);
+  }
+  const int half = (w - 1) / 2;
+
+  // rows (global rows are written by the whole group at the end)
+  for (int i = tid; i < nb; i += kBuildThreads) {
+    if (bit_of(gb, i)) continue;
+    uint64_t row[W], freeb[W];
+    int m = 0;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      row[k] = (gb[k] | span_bits(k, i - half, i + half)) & valid[k];
+      freeb[k] = valid[k] & ~row[k];
+      m += __popcll(freeb[k]);
+    }
+    const int take = r < m ? r : m;
+    const uint64_t k0 = (uint64_t)((int64_t)h * nb + i) * (uint64_t)r + 1;
+    int key[RMAX], val[RMAX];
+    constexpr int kUnroll = RMAX <= kFastR ? RMAX : 1;
+#pragma unroll kUnroll
+    for (int t = 0; t < RMAX; ++t) {
+      if (t < take) {
+        const uint64_t u = splitmix64_draw(seed, k0 + t);
+        const int s = t + (int)mod_small(u, (uint32_t)(m - t));
+        int vt = -1, vs = -1;
+#pragma unroll kUnroll
+        for (int q = 0; q < t; ++q) {
+          if (key[q] == t) vt = val[q];
+          if (key[q] == s) vs = val[q];
+        }
+        if (vt < 0) vt = select_bit(freeb, t);
+        if (vs < 0) vs = select_bit(freeb, s);
+        key[t] = s != t ? s : -1;
+        val[t] = vt;
+        set_bit(row, vs);
+        atomicOr(&colmap[vs * wpc + (i >> 5)], 1u << (i & 31));
+      }
+    }
+    write_bits(row, col_idx + row_ptr[(int64_t)h * nb + i]);
+  }
+  __syncthreads();
+
+  // columns: lengths, offsets (block scan), lists
+  auto col_bits = [&](int j, uint64_t (&c)[W]) {
+    const bool global = bit_of(gb, j);
+    int len = 0;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      const uint32_t lo = 2 * k < wpc ? colmap[j * wpc + 2 * k] : 0u;
+      const uint32_t hi = 2 * k + 1 < wpc ? colmap[j * wpc + 2 * k + 1] : 0u;
+      const uint64_t picked = lo | ((uint64_t)hi << 32);
+      c[k] = global ? valid[k] : (gb[k] | span_bits(k, j - half, j + half) | picked) & valid[k];
+      len += __popcll(c[k]);
+    }
+    return len;
+  };
   const int per = (nb + kBuildThreads - 1) / kBuildThreads;
   const int j0 = min(nb, tid * per), j1 = min(nb, j0 + per);
   int local = 0;
-  for (int j = j0; j < j1; ++j) local += col_length(G, nb, w, j, bm + j * wpc, wpc);
-  int64_t pos = (int64_t)h * nnz_per_head + block_exclusive_scan(local, part);
   for (int j = j0; j < j1; ++j) {
-    csc_ptr[(int64_t)h * nb + j] = (int32_t)pos;
-    const int len = col_length(G, nb, w, j, bm + j * wpc, wpc);
-    write_col(G, nb, w, j, bm + j * wpc, wpc, csc_idx + pos);
+    uint64_t c[W];
+    local += col_bits(j, c);
+  }
+  int pos = block_exclusive_scan(local, part);
+  for (int j = j0; j < j1; ++j) {
+    uint64_t c[W];
+    const int len = col_bits(j, c);
+    const int64_t p = (int64_t)h * nnz_per_head + pos;
+    csc_ptr[(int64_t)h * nb + j] = (int32_t)p;
+    sColPos[j] = pos;
+    if (!bit_of(gb, j)) write_bits(c, csc_idx + p);
     pos += len;
   }
   if (h == gridDim.x - 1 && tid == kBuildThreads - 1)
     csc_ptr[(int64_t)gridDim.x * nb] = (int32_t)((int64_t)gridDim.x * nnz_per_head);
+  __syncthreads();
+
+  // global rows and columns hold every block
+  for (int e = tid; e < g * nb; e += kBuildThreads) {
+    const int a = e / nb, j = e - a * nb;
+    const int x = sG[a];
+    col_idx[row_ptr[(int64_t)h * nb + x] + j] = j;
+    csc_idx[(int64_t)h * nnz_per_head + sColPos[x] + j] = j;
+  }
 }
 
 // Larger layouts, phase 1: one thread per (head, query block); bitmap in global
@@ -455,20 +619,31 @@ int launch_layout_rowptr(bsattn_layout* L, hipStream_t stream) {
 }
 
 namespace {
+template <int W, int RMAX>
+int launch_head(bsattn_layout* L, hipStream_t stream) {
+  const int wpc = (L->nb + 31) / 32;
+  const size_t lds = ((size_t)L->nb * wpc + L->g + L->nb) * sizeof(int32_t);
+  {
+    ProfScope prof_("layout_head", stream);
+    hipLaunchKernelGGL((layout_head_kernel<W, RMAX>), dim3(L->heads), dim3(kBuildThreads), lds,
+                       stream, L->d_gblk, L->g, L->nb, L->w, L->r, L->seed, L->nnz_per_head,
+                       L->d_row_ptr, L->d_col_idx, L->d_csc_ptr, L->d_csc_idx);
+  }
+  return check_hip(hipGetLastError(), "layout_head launch");
+}
+
+template <int RMAX>
+int launch_head_r(bsattn_layout* L, hipStream_t stream) {
+  if (L->nb <= 64) return launch_head<1, RMAX>(L, stream);
+  if (L->nb <= 128) return launch_head<2, RMAX>(L, stream);
+  if (L->nb <= 256) return launch_head<4, RMAX>(L, stream);
+  return launch_head<8, RMAX>(L, stream);
+}
+
 template <typename GS>
-int launch_build(bsattn_layout* L, hipStream_t stream) {
+int launch_rows_cols(bsattn_layout* L, hipStream_t stream) {
   const int wpc = (L->nb + 31) / 32;
   const size_t g_lds = (size_t)L->g * sizeof(int32_t);
-  if (L->nb <= kLdsBitmapNb) {
-    const size_t lds = (size_t)L->nb * wpc * sizeof(uint32_t) + g_lds;
-    {
-      ProfScope prof_("layout_head", stream);
-      hipLaunchKernelGGL(layout_head_kernel<GS>, dim3(L->heads), dim3(kBuildThreads), lds,
-                         stream, L->d_gblk, L->g, L->nb, L->w, L->r, L->seed, L->nnz_per_head,
-                         L->d_row_ptr, L->d_col_idx, L->d_csc_ptr, L->d_csc_idx);
-    }
-    return check_hip(hipGetLastError(), "layout_head launch");
-  }
   {
     ProfScope prof_("layout_rows", stream);
     hipLaunchKernelGGL(layout_rows_kernel<GS>, dim3((L->heads * L->nb + 63) / 64), dim3(64),
@@ -488,7 +663,9 @@ int launch_build(bsattn_layout* L, hipStream_t stream) {
 }  // namespace
 
 int launch_layout_build(bsattn_layout* L, hipStream_t stream) {
-  return L->g <= kRegG ? launch_build<GReg>(L, stream) : launch_build<GLds>(L, stream);
+  if (L->nb <= kLdsBitmapNb)
+    return L->r <= kFastR ? launch_head_r<kFastR>(L, stream) : launch_head_r<kMaxR>(L, stream);
+  return L->g <= kRegG ? launch_rows_cols<GReg>(L, stream) : launch_rows_cols<GLds>(L, stream);
 }
 
 }  // namespace bsattn
