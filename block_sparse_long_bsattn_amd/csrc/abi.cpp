@@ -142,6 +142,22 @@ int dev_alloc(T** p, size_t count) {
 }  // namespace
 }  // namespace bsattn
 
+SegPlan seg_plan(const bsattn_layout* L, int batch) {
+  // A segment is one work item, so it should be no longer than the average work
+  // of one work-group slot (4 per compute unit): the segments are scheduled first
+  // and then end within the run, while longer segments mean fewer fp32 partial
+  // tiles to write and merge.  Largest power of two within that average, 8..64.
+  const int64_t pairs = (int64_t)batch * L->heads * L->nnz_per_head;
+  const int64_t avg = pairs / (4 * (int64_t)(L->cus > 0 ? L->cus : 1));
+  int seg = 8;
+  while (seg < 64 && 2 * seg <= avg) seg *= 2;
+  SegPlan p;
+  p.split = L->nb > seg ? 1 : 0;
+  p.seg = p.split ? seg : L->nb;
+  p.nseg = p.split ? (L->nb + seg - 1) / seg : 1;
+  return p;
+}
+
 using namespace bsattn;
 
 extern "C" {
@@ -205,10 +221,10 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
     delete L;
     return set_error(BSATTN_EUNSUPPORTED, "layout_build: too many block pairs");
   }
-  L->split = nb > kSeg;
-  L->nseg = L->split ? (nb + kSeg - 1) / kSeg : 1;
   hipError_t e = hipGetDevice(&L->device);
   if (e != hipSuccess) { delete L; return check_hip(e, "hipGetDevice"); }
+  e = hipDeviceGetAttribute(&L->cus, hipDeviceAttributeMultiprocessorCount, L->device);
+  if (e != hipSuccess) { delete L; return check_hip(e, "hipDeviceGetAttribute"); }
   int st = BSATTN_OK;
   if ((st = dev_alloc(&L->d_gblk, (size_t)g)) || (st = dev_alloc(&L->d_ngblk, ng.size())) ||
       (st = dev_alloc(&L->d_row_ptr, (size_t)heads * nb + 1)) ||
@@ -351,7 +367,7 @@ int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, 
   P->ng = n_global;
   P->nt = n / kBlock;
   P->ngt = (n_global + kBlock - 1) / kBlock;
-  P->nseg = (P->nt + kSeg - 1) / kSeg;
+  P->nseg = (P->nt + kLfSeg - 1) / kLfSeg;
   P->gtok.assign(global_tokens, global_tokens + n_global);
   P->gidx.assign(n, -1);
   P->tile_gmask.assign(P->nt, 0ull);

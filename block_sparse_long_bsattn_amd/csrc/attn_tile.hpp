@@ -195,11 +195,13 @@ __device__ __forceinline__ void write_partial(const FwdState& st, float l_tot, i
 __device__ __forceinline__ void merge_partials(const float* base, int nseg, int row, int dq,
                                                float (&acc)[16], float& M, float& L) {
   M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < nseg; ++s) M = fmaxf(M, base[(size_t)s * kPartFloats + kBlock * kHead + row]);
   const float Mref = M == -INFINITY ? 0.f : M;
   L = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll 4
   for (int s = 0; s < nseg; ++s) {
     const float* ps = base + (size_t)s * kPartFloats;
     const float f = fast_exp2(ps[kBlock * kHead + row] - Mref);

@@ -12,8 +12,9 @@
 //   bs_bwd_dkdv  one work-group per key block (column of the transposed layout):
 //                dK and dV, walking the query blocks that see that key block.
 //   bs_bwd_reduce  global rows / columns are full-length; they are split into
-//                kSeg-block items writing fp32 partials, summed here in segment
-//                order, so results are bitwise reproducible.
+//                segments (length set per call from the total work) writing fp32
+//                partials, summed here in segment order, so results are bitwise
+//                reproducible.  Each XCD starts its segments before other items.
 
 #include "attn_tile.hpp"
 #include "internal.hpp"
@@ -43,7 +44,7 @@ struct BwdArgs {
   const int32_t* csc_idx;
   const int32_t* gblk;
   const int32_t* ngblk;
-  int heads, n, nb, g, nseg, split;
+  int heads, n, nb, g, seg, nseg, split;
   int items_per_bh, total_items;
   float scale, sl2;
 };
@@ -53,7 +54,7 @@ struct Item {
 };
 
 // Item v of a per-(batch, head) list: non-global blocks first (whole list), then
-// each global block's kSeg-long segments.  ptr is the row or column pointer.
+// each global block's segments of a.seg blocks.  ptr is the row or column pointer.
 __device__ __forceinline__ Item decode(const BwdArgs& a, int v, const int32_t* ptr) {
   Item it;
   it.bh = v / a.items_per_bh;
@@ -72,8 +73,8 @@ __device__ __forceinline__ Item decode(const BwdArgs& a, int v, const int32_t* p
     it.blk = a.gblk[gi];
     it.seg = s;
     if (a.split) {
-      it.start = s * kSeg;
-      it.len = min(kSeg, a.nb - s * kSeg);
+      it.start = s * a.seg;
+      it.len = min(a.seg, a.nb - s * a.seg);
       it.slot = (it.bh * a.g + gi) * a.nseg + s;
     }
   }
@@ -87,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
 
-  const int v = xcd_remap(blockIdx.x, a.total_items);
-  if (v >= a.total_items) return;
+  const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
+  if (v < 0) return;
   const Item it = decode(a, v, a.row_ptr);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
@@ -212,8 +213,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
 
-  const int v = xcd_remap(blockIdx.x, a.total_items);
-  if (v >= a.total_items) return;
+  const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
+  if (v < 0) return;
   const Item it = decode(a, v, a.csc_ptr);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
@@ -371,6 +372,7 @@ __global__ __launch_bounds__(256) void bs_bwd_reduce_kernel(
   float acc[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll 4
   for (int s = 0; s < nseg; ++s) {
     const size_t slot = (size_t)idx * nseg + s;
     const float* src = kind == 0 ? part_q + slot * kTile
@@ -399,7 +401,8 @@ __global__ __launch_bounds__(256) void bs_bwd_reduce_kernel(
 size_t bwd_workspace_bytes(const bsattn_layout* L, int batch) {
   size_t bytes = (size_t)batch * L->heads * L->n * sizeof(float);   // D
   bytes = (bytes + 255) & ~(size_t)255;
-  if (L->split) bytes += (size_t)batch * L->heads * L->g * L->nseg * 3 * kTile * sizeof(float);
+  const SegPlan sp = seg_plan(L, batch);
+  if (sp.split) bytes += (size_t)batch * L->heads * L->g * sp.nseg * 3 * kTile * sizeof(float);
   return bytes;
 }
 
@@ -413,15 +416,16 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, co
   char* w = (char*)ws;
   a.dbuf = (float*)w;
   size_t off = ((size_t)batch * L->heads * L->n * sizeof(float) + 255) & ~(size_t)255;
-  const size_t nslots = (size_t)batch * L->heads * L->g * L->nseg;
-  a.part_q = L->split ? (float*)(w + off) : nullptr;
-  a.part_kv = L->split ? (float*)(w + off + nslots * kTile * sizeof(float)) : nullptr;
+  const SegPlan sp = seg_plan(L, batch);
+  const size_t nslots = (size_t)batch * L->heads * L->g * sp.nseg;
+  a.part_q = sp.split ? (float*)(w + off) : nullptr;
+  a.part_kv = sp.split ? (float*)(w + off + nslots * kTile * sizeof(float)) : nullptr;
   a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
   a.csc_ptr = L->d_csc_ptr; a.csc_idx = L->d_csc_idx;
   a.gblk = L->d_gblk; a.ngblk = L->d_ngblk;
   a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
-  a.nseg = L->nseg; a.split = L->split ? 1 : 0;
-  a.items_per_bh = (L->nb - L->g) + L->g * L->nseg;
+  a.seg = sp.seg; a.nseg = sp.nseg; a.split = sp.split;
+  a.items_per_bh = (L->nb - L->g) + L->g * sp.nseg;
   a.total_items = batch * L->heads * a.items_per_bh;
   a.scale = scale;
   a.sl2 = scale * kLog2e;
@@ -437,12 +441,12 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, co
     hipLaunchKernelGGL(bs_bwd_dkdv_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
   }
   st = check_hip(hipGetLastError(), "bs_bwd_dkdv launch");
-  if (st || !L->split || L->g == 0) return st;
+  if (st || !sp.split || L->g == 0) return st;
   {
     ProfScope prof_("bs_bwd_reduce", stream);
     hipLaunchKernelGGL(bs_bwd_reduce_kernel, dim3(batch * L->heads * L->g * 3), dim3(256), 0,
                        stream, (const float*)a.part_q, (const float*)a.part_kv, L->d_gblk, L->n,
-                       L->g, L->nseg, a.dq, a.dk, a.dv);
+                       L->g, sp.nseg, a.dq, a.dk, a.dv);
   }
   return check_hip(hipGetLastError(), "bs_bwd_reduce launch");
 }

@@ -9,8 +9,10 @@
 // block; wave w owns query rows 32w .. 32w+31):
 //   * a non-global query block is one item walking its whole key-block list;
 //   * a global query block (a full row, App. D Fig. 6 "direct multiplication")
-//     is split into items of kSeg key blocks that write partial (unnormalised O,
-//     running max, running sum); bs_fwd_combine merges them in a fixed order.
+//     is split into segments of key blocks (their length set per call from the
+//     total work) that write partial (unnormalised O, running max, running sum);
+//     bs_fwd_combine merges them in a fixed order.  Each XCD starts the segments
+//     of its share of the items before the other items.
 // Per key block: K and V are staged through double-buffered LDS in natural
 // layout; S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA (V^T read with
 // LDS transpose reads); the online softmax runs in fp32 registers, one query per
@@ -36,7 +38,7 @@ struct FwdArgs {
   const int32_t* col_idx;
   const int32_t* gblk;
   const int32_t* ngblk;
-  int heads, n, nb, g, nseg, split;
+  int heads, n, nb, g, seg, nseg, split;
   int items_per_bh, total_items;
   float sl2;  // scale * log2(e)
 };
@@ -45,7 +47,7 @@ struct Item {
   int bh, h, i, start, len, slot;
 };
 
-__device__ __forceinline__ Item decode_row_item(int v, int heads, int nb, int g, int nseg,
+__device__ __forceinline__ Item decode_row_item(int v, int heads, int nb, int g, int seg, int nseg,
                                                 int split, int ipb, const int32_t* gblk,
                                                 const int32_t* ngblk, const int32_t* row_ptr) {
   Item it;
@@ -63,8 +65,8 @@ __device__ __forceinline__ Item decode_row_item(int v, int heads, int nb, int g,
     const int s = (r - ng) - gi * nseg;
     it.i = gblk[gi];
     if (split) {
-      it.start = s * kSeg;
-      it.len = min(kSeg, nb - s * kSeg);
+      it.start = s * seg;
+      it.len = min(seg, nb - s * seg);
       it.slot = (it.bh * g + gi) * nseg + s;
     } else {
       it.start = 0;
@@ -82,9 +84,9 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
 
-  const int v = xcd_remap(blockIdx.x, a.total_items);
-  if (v >= a.total_items) return;
-  const Item it = decode_row_item(v, a.heads, a.nb, a.g, a.nseg, a.split, a.items_per_bh,
+  const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
+  if (v < 0) return;
+  const Item it = decode_row_item(v, a.heads, a.nb, a.g, a.seg, a.nseg, a.split, a.items_per_bh,
                                   a.gblk, a.ngblk, a.row_ptr);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-// Merge the kSeg-block partials of every split global query block, in segment
+// Merge the segment partials of every split global query block, in segment
 // order: M = max_s m_s, L = sum_s l_s 2^(m_s - M), O = sum_s O_s 2^(m_s - M) / L.
 __global__ __launch_bounds__(256) void bs_fwd_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ gblk, int heads, int n,
@@ -248,8 +250,9 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
 }  // namespace
 
 size_t fwd_workspace_bytes(const bsattn_layout* L, int batch) {
-  if (!L->split) return 0;
-  return (size_t)batch * L->heads * L->g * L->nseg * kPartFloats * sizeof(float);
+  const SegPlan sp = seg_plan(L, batch);
+  if (!sp.split) return 0;
+  return (size_t)batch * L->heads * L->g * sp.nseg * kPartFloats * sizeof(float);
 }
 
 int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, const void* q,
@@ -276,8 +279,9 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
   a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
   a.gblk = L->d_gblk; a.ngblk = L->d_ngblk;
   a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
-  a.nseg = L->nseg; a.split = L->split ? 1 : 0;
-  a.items_per_bh = (L->nb - L->g) + L->g * L->nseg;
+  const SegPlan sp = seg_plan(L, batch);
+  a.seg = sp.seg; a.nseg = sp.nseg; a.split = sp.split;
+  a.items_per_bh = (L->nb - L->g) + L->g * sp.nseg;
   a.total_items = bhn * a.items_per_bh;
   a.sl2 = scale * kLog2e;
   const int grid = 8 * ((a.total_items + 7) / 8);
@@ -286,11 +290,11 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
     hipLaunchKernelGGL(bs_fwd_bf16_kernel, dim3(grid), dim3(kFwdThreads), 0, stream, a);
   }
   int st = check_hip(hipGetLastError(), "bs_fwd_bf16 launch");
-  if (st || !L->split || L->g == 0) return st;
+  if (st || !sp.split || L->g == 0) return st;
   {
     ProfScope prof_("bs_fwd_combine", stream);
     hipLaunchKernelGGL(bs_fwd_combine_kernel, dim3(bhn * L->g), dim3(256), 0, stream,
-                       (const float*)ws, L->d_gblk, L->heads, L->n, L->g, L->nseg,
+                       (const float*)ws, L->d_gblk, L->heads, L->n, L->g, sp.nseg,
                        (uint16_t*)o, lse);
   }
   return check_hip(hipGetLastError(), "bs_fwd_combine launch");

@@ -31,7 +31,7 @@ namespace bsattn {
 
 constexpr int kBlock = 64;   // tokens per block (b) and per Longformer tile
 constexpr int kHead = 64;    // head dimension (d)
-constexpr int kSeg = 8;      // key blocks per work item of a split full row
+constexpr int kLfSeg = 8;    // key tiles per work item of a split Longformer global row
 constexpr int kLdsStride = 72;  // bf16 elements per LDS tile row (64 + 8 pad)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -153,6 +153,30 @@ __device__ __forceinline__ float partner_sum(float x) {
 __device__ __forceinline__ int xcd_remap(int g, int total) {
   const int per = (total + 7) / 8;
   return (g & 7) * per + (g >> 3);
+}
+
+// The same eighths, for a list made of consecutive groups of ipb items whose
+// first ng are short and the rest long: each XCD runs the long items of its eighth
+// before the short ones, so the longest work starts first.  Returns the item of
+// work-group g, or -1 past the end of its eighth.
+__device__ __forceinline__ int xcd_item_long_first(int g, int total, int ipb, int ng) {
+  const int per = (total + 7) / 8;
+  const int lo = (g & 7) * per, k = g >> 3;
+  const int hi = min(total, lo + per);
+  if (k >= hi - lo) return -1;
+  const int nl = ipb - ng;
+  auto longs_before = [&](int v) {
+    const int b = v / ipb, r = v - b * ipb;
+    return b * nl + max(0, r - ng);
+  };
+  const int l0 = longs_before(lo), nlong = longs_before(hi) - l0;
+  if (k < nlong) {
+    const int t = l0 + k;
+    return (t / nl) * ipb + ng + t % nl;
+  }
+  const int b0 = lo / ipb, r0 = lo - b0 * ipb;
+  const int t = b0 * ng + min(r0, ng) + (k - nlong);
+  return (t / ng) * ipb + t % ng;
 }
 
 }  // namespace bsattn

@@ -17,8 +17,7 @@ struct bsattn_layout {
   std::vector<int32_t> gblk;     // global blocks (host copy)
   std::vector<int32_t> ngblk;    // non-global blocks ascending (host copy)
   std::vector<int32_t> row_len;  // length of each query-block row (host copy)
-  int nseg = 1;                  // work items per split (global) row / column
-  bool split = false;            // global rows and columns are split into kSeg items
+  int cus = 256;                 // compute units of the device (sizes the segment plan)
   // device arrays (owned)
   int32_t* d_gblk = nullptr;     // [g]
   int32_t* d_ngblk = nullptr;    // [nb - g] non-global block ids, ascending
@@ -28,6 +27,13 @@ struct bsattn_layout {
   int32_t* d_csc_idx = nullptr;  // [heads*nnz_per_head]
   uint32_t* d_rbits = nullptr;   // [heads][nb][ceil(nb/32)] random picks, zero between builds
 };
+
+// How one call cuts the full-length (global) rows and columns into work items:
+// segments of `seg` blocks, `nseg` per global block (split = 0: one whole item).
+struct SegPlan {
+  int seg, nseg, split;
+};
+SegPlan seg_plan(const bsattn_layout* L, int batch);
 
 struct lfattn_plan {
   int n = 0, w1 = 0, ng = 0, nt = 0, ngt = 0;  // tokens, window per side, globals, tiles

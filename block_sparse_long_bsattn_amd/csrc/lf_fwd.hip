@@ -15,7 +15,7 @@
 //               Rows of global tokens are skipped at write time.
 //   lf_global   the global query rows are full rows ("a token with global
 //               attention attends to all tokens"): packed query tiles times all key
-//               tiles, split into kSeg-tile items writing partial records.
+//               tiles, split into kLfSeg-tile items writing partial records.
 //   lf_combine  merges those partials in a fixed order and scatters O and lse back
 //               to the global tokens' positions.
 
@@ -219,8 +219,8 @@ __global__ __launch_bounds__(kThreads) void lf_global_kernel(LfArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
   }
-  const int u_begin = s * kSeg;
-  const int u_end = min(a.nt, u_begin + kSeg);
+  const int u_begin = s * kLfSeg;
+  const int u_end = min(a.nt, u_begin + kLfSeg);
   scale_operands(qB, a.sl2);
   FwdState st;
   fwd_state_init(st);
