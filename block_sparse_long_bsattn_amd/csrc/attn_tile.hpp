@@ -129,21 +129,30 @@ __device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& s
   pc[3] = pack8(s1, 8);
 }
 
-// O^T += V^T P^T; V is the natural LDS tile sV (row = key), its transposed
-// operand comes from ds_read_b64_tr_b16 reads.
-__device__ __forceinline__ void pv_tile(const uint16_t* sV, const bf16x8 (&pc)[4], int lane,
-                                        FwdState& st) {
-  bf16x8 v[8];
+// O^T += V^T P^T; V is the natural LDS tile sV, its transposed operand comes from
+// ds_read_b64_tr_b16 reads.  pv_load issues the reads (early, so that their latency
+// hides behind the softmax), pv_mma the MFMAs.
+__device__ __forceinline__ void pv_load(const uint16_t* sV, int lane, bf16x8 (&v)[8]) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     v[2 * c] = ld_tr8(sV, 0, c, lane);
     v[2 * c + 1] = ld_tr8(sV, 1, c, lane);
   }
+}
+
+__device__ __forceinline__ void pv_mma(const bf16x8 (&v)[8], const bf16x8 (&pc)[4], FwdState& st) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     st.o0 = mfma32(v[2 * c], pc[c], st.o0);
     st.o1 = mfma32(v[2 * c + 1], pc[c], st.o1);
   }
+}
+
+__device__ __forceinline__ void pv_tile(const uint16_t* sV, const bf16x8 (&pc)[4], int lane,
+                                        FwdState& st) {
+  bf16x8 v[8];
+  pv_load(sV, lane, v);
+  pv_mma(v, pc, st);
 }
 
 // Final write of a finished row: O (bf16, normalised) and lse (natural log).

@@ -128,9 +128,13 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
       gload_nat(vr, vaddr(kb_next), tid);
       kb_next = t + 2 < len ? keys[t + 2] : 0;
     }
+    // V^T operands read now; the softmax covers their LDS latency
+    bf16x8 vA[8];
+    pv_load(sV[cur], lane, vA);
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 pc[4];
     softmax_step(s0, s1, st, pc, seed_ref(st));
-    pv_tile(sV[cur], pc, lane, st);
+    pv_mma(vA, pc, st);
     if (more) {
       lds_store_nat(sK[cur ^ 1], kr, tid);
       lds_store_nat(sV[cur ^ 1], vr, tid);
