@@ -57,7 +57,7 @@ PRIMARY = "bigbird_fwd_bwd_b4_h12_n4096"
 
 # useful FLOPs per attended (query, key) pair credited to each kernel
 FLOPS_PER_PAIR = {"bs_fwd_bf16": 4 * D, "bs_fwd_f32": 4 * D, "bs_bwd_dq": 2 * D,
-                  "bs_bwd_dkdv": 6 * D, "lf_band": 4 * D, "lf_global": 4 * D}
+                  "bs_bwd_dkdv": 6 * D, "lf_attn": 4 * D}
 # every source of the library: a traffic figure is only reported while none of them
 # has changed since the counters were taken
 CSRC = os.path.join(ROOT, "block_sparse_long_bsattn_amd", "csrc")

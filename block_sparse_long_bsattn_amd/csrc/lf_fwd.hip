@@ -7,15 +7,15 @@
 // of diagonals; here the band is walked in 64x64 tiles.
 //
 // Kernels (per call):
-//   lf_gather   packs the Q, K, V rows of the global tokens into 64-row tiles.
-//   lf_band     one 128-thread work-group per 64-row query tile: the key tiles that
-//               overlap the band, then the packed global-key tiles whose keys lie
-//               outside those band tiles.  Only tiles the band cuts need an
-//               element mask; keys that are global are allowed in every tile.
-//               Rows of global tokens are skipped at write time.
-//   lf_global   the global query rows are full rows ("a token with global
-//               attention attends to all tokens"): packed query tiles times all key
-//               tiles, split into kLfSeg-tile items writing partial records.
+//   lf_attn     one 128-thread work-group per item, two kinds of item:
+//               * a 64-row query tile: the key tiles that overlap the band, then
+//                 the tiles of global keys (rows gathered by index from K and V)
+//                 whose keys lie outside those band tiles.  Only tiles the band
+//                 cuts need an element mask; keys that are global are allowed in
+//                 every tile.  Rows of global tokens are skipped at write time.
+//               * a segment of kLfSeg key tiles for a tile of global query rows
+//                 ("a token with global attention attends to all tokens"), query
+//                 rows gathered by index, writing a partial record.
 //   lf_combine  merges those partials in a fixed order and scatters O and lse back
 //               to the global tokens' positions.
 
@@ -33,57 +33,37 @@ struct LfArgs {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  const uint16_t* qg;   // packed global rows [B*H][ngt*64][64]
-  const uint16_t* kg;
-  const uint16_t* vg;
-  float* part;          // [B*H*ngt*nseg] partial records
+  float* part;          // [B*H*ngt*nseg] partial records of the global query rows
   const int32_t* gtok;  // [ng]
   const int32_t* gidx;  // [n]
   const uint64_t* tile_gmask;  // [nt] bit x set iff token 64u+x is global
   int heads, n, nt, ng, ngt, nseg, w1;
-  int total_items;
+  int band_items, total_items;
   float sl2;
 };
 
+typedef uint16_t LdsTile[kBlock * kLdsStride];
+
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
-__global__ __launch_bounds__(256) void lf_gather_kernel(LfArgs a) {
-  const int idx = blockIdx.x;   // bh * ngt + gt
-  const int bh = idx / a.ngt, gt = idx - bh * a.ngt;
-  const int x = threadIdx.x >> 2, dq = (threadIdx.x & 3) * 16;
-  const int j = gt * kBlock + x;
-  const size_t src_bh = (size_t)bh * a.n * kHead;
-  const size_t dst = ((size_t)bh * a.ngt * kBlock + j) * kHead + dq;
-  uint16_t* qd = const_cast<uint16_t*>(a.qg) + dst;
-  uint16_t* kd = const_cast<uint16_t*>(a.kg) + dst;
-  uint16_t* vd = const_cast<uint16_t*>(a.vg) + dst;
-  if (j < a.ng) {
-    const size_t src = src_bh + (size_t)a.gtok[j] * kHead + dq;
-#pragma unroll
-    for (int e = 0; e < 16; e += 8) {
-      *reinterpret_cast<u32x4*>(qd + e) = ldg16(a.q + src + e);
-      *reinterpret_cast<u32x4*>(kd + e) = ldg16(a.k + src + e);
-      *reinterpret_cast<u32x4*>(vd + e) = ldg16(a.v + src + e);
-    }
-  } else {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 16; e += 8) {
-      *reinterpret_cast<u32x4*>(qd + e) = z;
-      *reinterpret_cast<u32x4*>(kd + e) = z;
-      *reinterpret_cast<u32x4*>(vd + e) = z;
-    }
-  }
+// Token behind row x of global tile gt: the (gt*64 + x)-th global token; rows past
+// the last one repeat it (their keys are masked out, their query rows not written).
+__device__ __forceinline__ int global_token(const LfArgs& a, int gt, int x) {
+  return a.gtok[min(gt * kBlock + x, a.ng - 1)];
 }
 
-__global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
+// gload_nat for a tile of global tokens, rows gathered from the [n][64] tensor.
+__device__ __forceinline__ void gload_gather(TileRegs& r, const LfArgs& a, const uint16_t* base,
+                                             int gt, int tid) {
+  const int c = tid & 7, row = tid >> 3;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    r.v[u] = ldg16(base + (size_t)global_token(a, gt, row + 16 * u) * kHead + 8 * c);
+}
 
-  const int v = xcd_remap(blockIdx.x, a.total_items);
-  if (v >= a.total_items) return;
+__device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK, LdsTile* sV) {
   const int bh = v / a.nt, t = v - bh * a.nt;
-  if (a.tile_gmask[t] == ~0ull) return;   // every row global: lf_global owns them
+  if (a.tile_gmask[t] == ~0ull) return;   // every row global: the global items own them
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)bh * a.n * kHead;
@@ -101,8 +81,8 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
   const int nband = hi_u - lo_u + 1;
   const int ntile = nband + a.ngt;
 
-  // A packed global tile gt contributes key j iff j < ng and the key's own tile
-  // lies outside [lo_u, hi_u] (inside, the band tile already counts it).
+  // Global tile gt contributes key j iff j < ng and the key's own tile lies
+  // outside [lo_u, hi_u] (inside, the band tile already counts it).
   auto global_elig = [&](int gt) -> uint64_t {
     const int j = gt * kBlock + lane;
     bool ok = false;
@@ -116,19 +96,17 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
   scale_operands(qB, a.sl2);
   FwdState st;
   fwd_state_init(st);
-  const uint16_t* kg_bh = a.kg + (size_t)bh * a.ngt * kBlock * kHead;
-  const uint16_t* vg_bh = a.vg + (size_t)bh * a.ngt * kBlock * kHead;
-  auto tile_src = [&](int x, const uint16_t*& ks, const uint16_t*& vs) {
+  auto tile_load = [&](int x, TileRegs& kr, TileRegs& vr) {
     if (x < nband) {
-      ks = a.k + bh_off + (size_t)(lo_u + x) * kBlock * kHead;
-      vs = a.v + bh_off + (size_t)(lo_u + x) * kBlock * kHead;
+      gload_nat(kr, a.k + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
+      gload_nat(vr, a.v + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
     } else {
-      ks = kg_bh + (size_t)(x - nband) * kBlock * kHead;
-      vs = vg_bh + (size_t)(x - nband) * kBlock * kHead;
+      gload_gather(kr, a, a.k + bh_off, x - nband, tid);
+      gload_gather(vr, a, a.v + bh_off, x - nband, tid);
     }
   };
 
-  // skip packed tiles with no eligible key
+  // skip global tiles with no eligible key
   auto next_tile = [&](int x) -> int {
     while (x < ntile && x >= nband && global_elig(x - nband) == 0ull) ++x;
     return x;
@@ -137,10 +115,7 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
   int x = next_tile(0);
   TileRegs kr, vr;
   if (x < ntile) {
-    const uint16_t *ks, *vs;
-    tile_src(x, ks, vs);
-    gload_nat(kr, ks, tid);
-    gload_nat(vr, vs, tid);
+    tile_load(x, kr, vr);
     lds_store_nat(sK[0], kr, tid);
     lds_store_nat(sV[0], vr, tid);
   }
@@ -148,12 +123,7 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
   while (x < ntile) {
     __syncthreads();
     const int xn = next_tile(x + 1);
-    if (xn < ntile) {
-      const uint16_t *ks, *vs;
-      tile_src(xn, ks, vs);
-      gload_nat(kr, ks, tid);
-      gload_nat(vr, vs, tid);
-    }
+    if (xn < ntile) tile_load(xn, kr, vr);
     f32x16 s0, s1;
     qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
     if (x < nband) {
@@ -198,13 +168,9 @@ __global__ __launch_bounds__(kThreads) void lf_band_kernel(LfArgs a) {
                  a.lse != nullptr ? a.lse + (size_t)bh * a.n + p : nullptr);
 }
 
-__global__ __launch_bounds__(kThreads) void lf_global_kernel(LfArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
-
+// Item v of the global rows: (bh, global tile gt, segment s of kLfSeg key tiles).
+__device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* sK, LdsTile* sV) {
   const int per_bh = a.ngt * a.nseg;
-  const int v = xcd_remap(blockIdx.x, a.total_items);
-  if (v >= a.total_items) return;
   const int bh = v / per_bh;
   const int rem = v - bh * per_bh;
   const int gt = rem / a.nseg, s = rem - gt * a.nseg;
@@ -215,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void lf_global_kernel(LfArgs a) {
 
   bf16x8 qB[4];
   {
-    const uint16_t* qp = a.qg + ((size_t)bh * a.ngt * kBlock + gt * kBlock + qr) * kHead + 8 * hl;
+    const uint16_t* qp = a.q + bh_off + (size_t)global_token(a, gt, qr) * kHead + 8 * hl;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
   }
@@ -251,6 +217,18 @@ __global__ __launch_bounds__(kThreads) void lf_global_kernel(LfArgs a) {
   write_partial(st, l_tot, hl, qr, a.part + (size_t)v * kPartFloats);
 }
 
+// Band items first, then the global-row segments (about as long as a band item).
+__global__ __launch_bounds__(kThreads, 2) void lf_attn_kernel(LfArgs a) {
+  __shared__ __attribute__((aligned(16))) LdsTile sK[2];
+  __shared__ __attribute__((aligned(16))) LdsTile sV[2];
+  const int v = xcd_remap(blockIdx.x, a.total_items);
+  if (v >= a.total_items) return;
+  if (v < a.band_items)
+    lf_band_item(a, v, sK, sV);
+  else
+    lf_global_item(a, v - a.band_items, sK, sV);
+}
+
 __global__ __launch_bounds__(256) void lf_combine_kernel(LfArgs a) {
   const int idx = blockIdx.x;   // bh * ngt + gt
   const int bh = idx / a.ngt, gt = idx - bh * a.ngt;
@@ -265,28 +243,11 @@ __global__ __launch_bounds__(256) void lf_combine_kernel(LfArgs a) {
     a.lse[(size_t)bh * a.n + tok] = (M + __log2f(L)) * kLn2;
 }
 
-struct LfWs {
-  size_t qg, kg, vg, part, total;
-};
-
-LfWs lf_ws_layout(const lfattn_plan* P, int batch, int heads) {
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  LfWs w;
-  const size_t bh = (size_t)batch * heads;
-  const size_t tile_bytes = (size_t)P->ngt * kBlock * kHead * sizeof(uint16_t);
-  w.qg = 0;
-  w.kg = up(w.qg + bh * tile_bytes);
-  w.vg = up(w.kg + bh * tile_bytes);
-  w.part = up(w.vg + bh * tile_bytes);
-  w.total = up(w.part + bh * P->ngt * P->nseg * kPartFloats * sizeof(float));
-  return w;
-}
-
 }  // namespace
 
 size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads) {
   if (P->ng == 0) return 0;
-  return lf_ws_layout(P, batch, heads).total;
+  return (size_t)batch * heads * P->ngt * P->nseg * kPartFloats * sizeof(float);
 }
 
 int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
@@ -296,40 +257,22 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.o = (uint16_t*)o; a.lse = lse;
   const bool has_g = P->ng > 0;
-  LfWs w = lf_ws_layout(P, batch, heads);
-  char* base = (char*)ws;
-  a.qg = has_g ? (const uint16_t*)(base + w.qg) : nullptr;
-  a.kg = has_g ? (const uint16_t*)(base + w.kg) : nullptr;
-  a.vg = has_g ? (const uint16_t*)(base + w.vg) : nullptr;
-  a.part = has_g ? (float*)(base + w.part) : nullptr;
+  a.part = has_g ? (float*)ws : nullptr;
   a.gtok = P->d_gtok; a.gidx = P->d_gidx; a.tile_gmask = P->d_tile_gmask;
   a.heads = heads; a.n = P->n; a.nt = P->nt; a.ng = P->ng; a.ngt = P->ngt;
   a.nseg = P->nseg; a.w1 = P->w1;
   a.sl2 = scale * kLog2e;
   const int bhn = batch * heads;
+  a.band_items = bhn * P->nt;
+  a.total_items = a.band_items + (has_g ? bhn * P->ngt * P->nseg : 0);
   int st;
-  if (has_g) {
-    {
-    ProfScope prof_("lf_gather", stream);
-    hipLaunchKernelGGL(lf_gather_kernel, dim3(bhn * P->ngt), dim3(256), 0, stream, a);
-  }
-    if ((st = check_hip(hipGetLastError(), "lf_gather launch"))) return st;
-  }
-  a.total_items = bhn * P->nt;
   {
-    ProfScope prof_("lf_band", stream);
-    hipLaunchKernelGGL(lf_band_kernel, dim3(8 * ((a.total_items + 7) / 8)), dim3(kThreads), 0,
+    ProfScope prof_("lf_attn", stream);
+    hipLaunchKernelGGL(lf_attn_kernel, dim3(8 * ((a.total_items + 7) / 8)), dim3(kThreads), 0,
                        stream, a);
   }
-  if ((st = check_hip(hipGetLastError(), "lf_band launch"))) return st;
+  if ((st = check_hip(hipGetLastError(), "lf_attn launch"))) return st;
   if (!has_g) return 0;
-  a.total_items = bhn * P->ngt * P->nseg;
-  {
-    ProfScope prof_("lf_global", stream);
-    hipLaunchKernelGGL(lf_global_kernel, dim3(8 * ((a.total_items + 7) / 8)), dim3(kThreads), 0,
-                       stream, a);
-  }
-  if ((st = check_hip(hipGetLastError(), "lf_global launch"))) return st;
   {
     ProfScope prof_("lf_combine", stream);
     hipLaunchKernelGGL(lf_combine_kernel, dim3(bhn * P->ngt), dim3(256), 0, stream, a);
