@@ -167,9 +167,13 @@ __global__ __launch_bounds__(256) void bs_fwd_combine_kernel(
   (void)heads;
 }
 
-// fp32 path: plain FMA tiles, one 256-thread work-group per query block walking
-// the whole row.  Thread t owns query row t/4 and a quarter (16 keys for the
-// scores, 16 columns for the output).
+// fp32 path: register-tiled FMA, one 256-thread work-group per query block walking
+// its whole row.  Thread t owns queries 4*(t/16)..+3 and, for the scores, keys
+// 4*(t%16)..+3 of the current key block; for the output, head-dim columns
+// 4*(t%16)..+3.  Each step reads float4 operands from LDS (64 FMAs per 8 reads);
+// tile rows are padded to 68 floats, which keeps the float4 reads of 16 different
+// rows on distinct banks.  The 16 threads of a query group are 16 consecutive
+// lanes, so row reductions are xor-shuffles over 1, 2, 4, 8.
 struct FwdF32Args {
   const float* q;
   const float* k;
@@ -182,73 +186,149 @@ struct FwdF32Args {
   float scale;
 };
 
+constexpr int kF32Stride = kHead + 4;
+
+// one 64x64 fp32 tile: 4 float4 per thread, row-major global -> padded LDS rows
+struct TileF32 { f32x4 v[4]; };
+
+__device__ __forceinline__ void load_f32_tile(TileF32& t, const float* g, int tid) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) t.v[u] = *reinterpret_cast<const f32x4*>(g + 4 * tid + 1024 * u);
+}
+
+__device__ __forceinline__ void store_f32_tile(float* s, const TileF32& t, int tid) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int x = 4 * tid + 1024 * u, row = x / kHead, col = x % kHead;
+    *reinterpret_cast<f32x4*>(s + row * kF32Stride + col) = t.v[u];
+  }
+}
+
+__device__ __forceinline__ float group16_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float group16_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
-  __shared__ float sK[kBlock][kHead + 1];
-  __shared__ float sV[kBlock][kHead];
-  __shared__ float sP[kBlock][kBlock + 1];
+  __shared__ __attribute__((aligned(16))) float sQ[kBlock * kF32Stride];
+  __shared__ __attribute__((aligned(16))) float sK[kBlock * kF32Stride];   // K, then P
+  __shared__ __attribute__((aligned(16))) float sV[kBlock * kF32Stride];
   const int v = xcd_remap(blockIdx.x, a.total_items);
   if (v >= a.total_items) return;
   const int bh = v / a.nb, i = v - bh * a.nb, h = bh % a.heads;
-  const int tid = threadIdx.x, row = tid >> 2, qq = tid & 3;
+  const int tid = threadIdx.x, tq = tid >> 4, tk = tid & 15;
   const size_t bh_off = (size_t)bh * a.n * kHead;
-  const int tok = i * kBlock + row;
-  float qv[kHead];
+  {
+    TileF32 qt;
+    load_f32_tile(qt, a.q + bh_off + (size_t)i * kBlock * kHead, tid);
+    store_f32_tile(sQ, qt, tid);
+  }
+
+  float m[4], l[4], acc[4][4];
 #pragma unroll
-  for (int c = 0; c < kHead; ++c) qv[c] = a.q[bh_off + (size_t)tok * kHead + c];
-  float acc[16];
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-  float m = -INFINITY, l = 0.f;
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+  }
   const int rp0 = a.row_ptr[(int64_t)h * a.nb + i], rp1 = a.row_ptr[(int64_t)h * a.nb + i + 1];
+  // K and V of the next key block are loaded into registers one block ahead
+  TileF32 kt, vt;
+  if (rp0 < rp1) {
+    const int kb = a.col_idx[rp0];
+    load_f32_tile(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid);
+    load_f32_tile(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid);
+  }
   for (int e = rp0; e < rp1; ++e) {
-    const int kb = a.col_idx[e];
-    const float* kp = a.k + bh_off + (size_t)kb * kBlock * kHead;
-    const float* vp = a.v + bh_off + (size_t)kb * kBlock * kHead;
-    __syncthreads();
-    for (int x = tid; x < kBlock * kHead; x += 256) {
-      sK[x / kHead][x % kHead] = kp[x];
-      sV[x / kHead][x % kHead] = vp[x];
+    __syncthreads();   // the previous block's P (in sK) and V are no longer read
+    store_f32_tile(sK, kt, tid);
+    store_f32_tile(sV, vt, tid);
+    if (e + 1 < rp1) {
+      const int kb = a.col_idx[e + 1];
+      load_f32_tile(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid);
+      load_f32_tile(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid);
     }
     __syncthreads();
-    float s[16];
-    float mx = -INFINITY;
+    // S = Q K^T for queries 4tq+r, keys 4tk+j
+    float s[4][4];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float dot = 0.f;
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int c = 0; c < kHead; ++c) dot = __builtin_fmaf(qv[c], sK[qq * 16 + kk][c], dot);
-      s[kk] = dot * a.scale;
-      mx = fmaxf(mx, s[kk]);
+      for (int j = 0; j < 4; ++j) s[r][j] = 0.f;
+    for (int c = 0; c < kHead; c += 4) {
+      f32x4 qv[4], kv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qv[r] = *reinterpret_cast<const f32x4*>(sQ + (4 * tq + r) * kF32Stride + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kv[j] = *reinterpret_cast<const f32x4*>(sK + (4 * tk + j) * kF32Stride + c);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) s[r][j] = __builtin_fmaf(qv[r][x], kv[j][x], s[r][j]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = expf(m - m_new);
-    float rs = 0.f;
+    // online softmax per query row (its 64 keys live in the 16 threads of the group)
+    float p[4][4];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float p = expf(s[kk] - m_new);
-      sP[row][qq * 16 + kk] = p;
-      rs += p;
+    for (int r = 0; r < 4; ++r) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[r][j] *= a.scale;
+        mx = fmaxf(mx, s[r][j]);
+      }
+      const float m_new = fmaxf(m[r], group16_max(mx));
+      const float alpha = expf(m[r] - m_new);
+      float rs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[r][j] = expf(s[r][j] - m_new);
+        rs += p[r][j];
+      }
+      l[r] = l[r] * alpha + group16_sum(rs);
+      m[r] = m_new;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] *= alpha;
     }
-    l = l * alpha + rs;
-    m = m_new;
+    __syncthreads();   // every thread is done reading K
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 w = {p[r][0], p[r][1], p[r][2], p[r][3]};
+      *reinterpret_cast<f32x4*>(sK + (4 * tq + r) * kF32Stride + 4 * tk) = w;
+    }
     __syncthreads();
+    // O += P V for queries 4tq+r, head-dim columns 4tk..4tk+3
+    for (int k0 = 0; k0 < kBlock; k0 += 4) {
+      f32x4 pv[4], vv[4];
 #pragma unroll
-    for (int e2 = 0; e2 < 16; ++e2) acc[e2] *= alpha;
-    for (int kk = 0; kk < kBlock; ++kk) {
-      const float p = sP[row][kk];
+      for (int r = 0; r < 4; ++r) pv[r] = *reinterpret_cast<const f32x4*>(sK + (4 * tq + r) * kF32Stride + k0);
 #pragma unroll
-      for (int e2 = 0; e2 < 16; ++e2) acc[e2] = __builtin_fmaf(p, sV[kk][qq * 16 + e2], acc[e2]);
+      for (int x = 0; x < 4; ++x) vv[x] = *reinterpret_cast<const f32x4*>(sV + (k0 + x) * kF32Stride + 4 * tk);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(pv[r][x], vv[x][c], acc[r][c]);
     }
   }
-  l += __shfl_xor(l, 1);
-  l += __shfl_xor(l, 2);
-  const float inv = 1.f / l;
-  float* op = a.o + bh_off + (size_t)tok * kHead + qq * 16;
 #pragma unroll
-  for (int e2 = 0; e2 < 16; ++e2) op[e2] = acc[e2] * inv;
-  if (a.lse != nullptr && qq == 0) a.lse[(size_t)bh * a.n + tok] = m + logf(l);
+  for (int r = 0; r < 4; ++r) {
+    const int tok = i * kBlock + 4 * tq + r;
+    const float inv = 1.f / l[r];
+    const f32x4 w = {acc[r][0] * inv, acc[r][1] * inv, acc[r][2] * inv, acc[r][3] * inv};
+    *reinterpret_cast<f32x4*>(a.o + bh_off + (size_t)tok * kHead + 4 * tk) = w;
+    if (a.lse != nullptr && tk == 0) a.lse[(size_t)bh * a.n + tok] = m[r] + logf(l[r]);
+  }
 }
 
 }  // namespace
