@@ -58,20 +58,28 @@ PRIMARY = "bigbird_fwd_bwd_b4_h12_n4096"
 # useful FLOPs per attended (query, key) pair credited to each kernel
 FLOPS_PER_PAIR = {"bs_fwd_bf16": 4 * D, "bs_fwd_f32": 4 * D, "bs_bwd_dq": 2 * D,
                   "bs_bwd_dkdv": 6 * D, "lf_attn": 4 * D}
-# every source of the library: a traffic figure is only reported while none of them
-# has changed since the counters were taken
 CSRC = os.path.join(ROOT, "block_sparse_long_bsattn_amd", "csrc")
+# the sources a kernel's code and launch depend on: a stored traffic figure is only
+# reported while none of them has changed since the counters were taken
+KERNEL_SOURCES = {
+    "bs_bwd_dkdv": ["bs_bwd.hip", "attn_tile.hpp", "common.hpp", "internal.hpp", "abi.cpp"],
+    "bs_bwd_dq": ["bs_bwd.hip", "attn_tile.hpp", "common.hpp", "internal.hpp", "abi.cpp"],
+    "bs_fwd_bf16": ["bs_fwd.hip", "attn_tile.hpp", "common.hpp", "internal.hpp", "abi.cpp"],
+    "lf_attn": ["lf_fwd.hip", "attn_tile.hpp", "common.hpp", "internal.hpp", "abi.cpp"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(kernel: str | None = None) -> str:
-    """sha256 over all library sources (sorted by name); `kernel` is not used to
-    narrow the set, so any change to the library invalidates stored counters."""
+def kernel_source_hash(kernel: str) -> str | None:
+    """sha256 over the kernel's source files (in the listed order), None if unknown."""
+    files = KERNEL_SOURCES.get(kernel)
+    if not files:
+        return None
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
