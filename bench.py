@@ -13,7 +13,8 @@ bf16 inputs with fp32 accumulation.  Prints ONE JSON line on stdout:
   cpu_baseline  the fp64 oracle (dense mask) timed on a bounded sample on the
              host cores, in the same unit
   secondary  the other workloads (forward only at n = 4096 and 16384, fp32 at
-             n = 512, Longformer window 256 + 64 global tokens), each timed alone
+             n = 512, Longformer window 256 + 64 global tokens forward, and its
+             forward + backward), each timed alone
 
 Progress goes to stderr.  Inputs are resident in device memory before timing.
 """
@@ -52,12 +53,16 @@ WORKLOADS = {
     "longformer_fwd_b1_h12_n4096_w256_g64": dict(kind="longformer", n=4096, heads=12, batch=1,
                                                   w1=256, G=list(range(64)), dtype="bf16",
                                                   bwd=False),
+    "longformer_fwd_bwd_b1_h12_n4096_w256_g64": dict(kind="longformer", n=4096, heads=12,
+                                                      batch=1, w1=256, G=list(range(64)),
+                                                      dtype="bf16", bwd=True),
 }
 PRIMARY = "bigbird_fwd_bwd_b4_h12_n4096"
 
 # useful FLOPs per attended (query, key) pair credited to each kernel
 FLOPS_PER_PAIR = {"bs_fwd_bf16": 4 * D, "bs_fwd_f32": 4 * D, "bs_bwd_dq": 2 * D,
-                  "bs_bwd_dkdv": 6 * D, "lf_attn": 4 * D}
+                  "bs_bwd_dkdv": 6 * D, "lf_attn": 4 * D, "lf_bwd_dq": 2 * D,
+                  "lf_bwd_dkdv": 6 * D}
 CSRC = os.path.join(ROOT, "block_sparse_long_bsattn_amd", "csrc")
 # the sources a kernel's code and launch depend on: a stored traffic figure is only
 # reported while none of them has changed since the counters were taken
@@ -65,7 +70,10 @@ KERNEL_SOURCES = {
     "bs_bwd_dkdv": ["bs_bwd.hip", "attn_tile.hpp", "common.hpp", "internal.hpp", "abi.cpp"],
     "bs_bwd_dq": ["bs_bwd.hip", "attn_tile.hpp", "common.hpp", "internal.hpp", "abi.cpp"],
     "bs_fwd_bf16": ["bs_fwd.hip", "attn_tile.hpp", "common.hpp", "internal.hpp", "abi.cpp"],
-    "lf_attn": ["lf_fwd.hip", "attn_tile.hpp", "common.hpp", "internal.hpp", "abi.cpp"],
+    "lf_attn": ["lf_fwd.hip", "lf_tile.hpp", "attn_tile.hpp", "common.hpp", "internal.hpp",
+                "abi.cpp"],
+    "lf_bwd_dkdv": ["lf_bwd.hip", "lf_tile.hpp", "attn_tile.hpp", "common.hpp", "internal.hpp",
+                    "abi.cpp"],
 }
 
 
@@ -157,6 +165,19 @@ class Job:
                                                 P(self.v), P(self.o), P(self.lse), P(self.wsf),
                                                 self.wsf.numel(), stream)))
             self.flops = 4 * D * self.pairs
+            if cfg["bwd"]:
+                self.do = dev(I.SEED_DO)
+                self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+                wsb = B.lfattn_bwd_workspace(self.handle, bsz, heads)
+                self.wsb = torch.empty(max(16, wsb), dtype=torch.uint8, device="cuda")
+                B.lfattn_bwd(self.handle, self.q, self.k, self.v, self.o, self.lse, self.do,
+                             self.dq, self.dk, self.dv, self.wsb)
+                self.calls.append((lib.lfattn_bwd, (h, bsz, heads, D, dt, scale, P(self.q),
+                                                    P(self.k), P(self.v), P(self.o),
+                                                    P(self.lse), P(self.do), P(self.dq),
+                                                    P(self.dk), P(self.dv), P(self.wsb),
+                                                    self.wsb.numel(), stream)))
+                self.flops += 8 * D * self.pairs
         torch.cuda.synchronize()
 
     def step(self):

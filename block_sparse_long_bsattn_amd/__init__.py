@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     bsattn_layout_to_host,
     bsattn_status_str,
     bsattn_version,
+    lfattn_bwd,
+    lfattn_bwd_workspace,
     lfattn_fwd,
     lfattn_fwd_workspace,
     lfattn_plan_build,

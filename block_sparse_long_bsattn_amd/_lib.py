@@ -28,7 +28,8 @@ EXPORTS = (
     "bsattn_layout_build", "bsattn_layout_rebuild", "bsattn_layout_info",
     "bsattn_layout_to_host", "bsattn_layout_destroy", "bsattn_fwd_workspace",
     "bsattn_bwd_workspace", "bsattn_fwd", "bsattn_bwd", "lfattn_plan_build",
-    "lfattn_plan_destroy", "lfattn_fwd_workspace", "lfattn_fwd", "bsattn_status_str",
+    "lfattn_plan_destroy", "lfattn_fwd_workspace", "lfattn_fwd", "lfattn_bwd_workspace",
+    "lfattn_bwd", "bsattn_status_str",
     "bsattn_last_error", "bsattn_version", "bsattn_profile_enable", "bsattn_profile_read",
 )
 
@@ -72,6 +73,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lfattn_fwd_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int]),
         "lfattn_fwd": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "lfattn_bwd_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int]),
+        "lfattn_bwd": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_size_t, c_void_p]),
         "bsattn_status_str": (c_char_p, [c_int]),
         "bsattn_last_error": (c_char_p, []),
         "bsattn_version": (c_char_p, []),
@@ -265,6 +270,30 @@ def lfattn_fwd(plan, q, k, v, o, lse=None, workspace=None, scale=None, stream=No
     _check(load().lfattn_fwd(plan, bsz, heads, d, _dtype_code(q), c_float(scale), _ptr(q),
                              _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
                              _stream(stream)), "lfattn_fwd")
+
+
+def lfattn_bwd_workspace(plan, batch, heads, d=64) -> int:
+    return int(load().lfattn_bwd_workspace(plan, batch, heads, d))
+
+
+def lfattn_bwd(plan, q, k, v, o, lse, dout, dq, dk, dv, workspace=None, scale=None,
+               stream=None) -> None:
+    bsz, heads, _, d = q.shape
+    if plan not in _plan_n:
+        raise ValueError("lfattn_bwd: unknown plan handle")
+    if lse is None:
+        raise ValueError("lfattn_bwd: lse is required")
+    shape = (bsz, heads, _plan_n[plan], d)
+    _check_tensors("lfattn_bwd", shape, q.dtype,
+                   (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)), lse, workspace,
+                   lfattn_bwd_workspace(plan, bsz, heads, d))
+    scale = d ** -0.5 if scale is None else scale
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().lfattn_bwd(plan, bsz, heads, d, _dtype_code(q), c_float(scale), _ptr(q),
+                             _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)),
+           "lfattn_bwd")
 
 
 # --- diagnostics ----------------------------------------------------------------

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbsattn.so")
-SOURCES = ["abi.cpp", "layout.hip", "bs_fwd.hip", "bs_bwd.hip", "lf_fwd.hip"]
+SOURCES = ["abi.cpp", "layout.hip", "bs_fwd.hip", "bs_bwd.hip", "lf_fwd.hip", "lf_bwd.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -124,6 +125,7 @@ void free_plan(lfattn_plan* P) {
   (void)hipFree(P->d_gtok);
   (void)hipFree(P->d_gidx);
   (void)hipFree(P->d_tile_gmask);
+  (void)hipFree(P->d_ktiles);
   delete P;
 }
 
@@ -376,11 +378,17 @@ int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, 
     P->gidx[t] = x;
     P->tile_gmask[t / kBlock] |= 1ull << (t % kBlock);
   }
+  for (int t = 0; t < P->nt; ++t)
+    if (P->tile_gmask[t] == 0ull) P->ktiles.push_back(t);
+  for (int t = 0; t < P->nt; ++t)
+    if (P->tile_gmask[t] != 0ull) P->ktiles.push_back(t);
+  P->ngkt = P->nt - (int)std::count(P->tile_gmask.begin(), P->tile_gmask.end(), 0ull);
   hipError_t e = hipGetDevice(&P->device);
   if (e != hipSuccess) { delete P; return check_hip(e, "hipGetDevice"); }
   int st;
   if ((st = dev_alloc(&P->d_gtok, (size_t)n_global)) || (st = dev_alloc(&P->d_gidx, (size_t)n)) ||
-      (st = dev_alloc(&P->d_tile_gmask, (size_t)P->nt))) {
+      (st = dev_alloc(&P->d_tile_gmask, (size_t)P->nt)) ||
+      (st = dev_alloc(&P->d_ktiles, (size_t)P->nt))) {
     free_plan(P);
     return st;
   }
@@ -389,7 +397,9 @@ int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, 
       (st = check_hip(hipMemcpyAsync(P->d_gidx, P->gidx.data(), (size_t)n * 4, hipMemcpyHostToDevice, stream),
                       "upload token index")) ||
       (st = check_hip(hipMemcpyAsync(P->d_tile_gmask, P->tile_gmask.data(), (size_t)P->nt * 8,
-                                     hipMemcpyHostToDevice, stream), "upload tile masks"))) {
+                                     hipMemcpyHostToDevice, stream), "upload tile masks")) ||
+      (st = check_hip(hipMemcpyAsync(P->d_ktiles, P->ktiles.data(), (size_t)P->nt * 4,
+                                     hipMemcpyHostToDevice, stream), "upload key tiles"))) {
     free_plan(P);
     return st;
   }
@@ -425,6 +435,29 @@ int lfattn_fwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype d
   if ((st = check_workspace(workspace, ws_bytes, lf_workspace_bytes(P, batch, heads), "lf_fwd"))) return st;
   if ((st = check_device(P->device))) return st;
   return launch_lf_fwd(P, batch, heads, scale, q, k, v, o, lse, workspace, stream);
+}
+
+size_t lfattn_bwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
+  if (P == nullptr || batch < 1 || heads < 1 || d != kHead) return 0;
+  return lf_bwd_workspace_bytes(P, batch, heads);
+}
+
+int lfattn_bwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt, float scale,
+               const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+               hipStream_t stream) {
+  clear_error();
+  if (P == nullptr) return set_error(BSATTN_EINVAL, "lf_bwd: null plan");
+  if (heads < 1) return set_error(BSATTN_EINVAL, "lf_bwd: heads must be >= 1");
+  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "lf_bwd: only bf16 is built");
+  int st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "lf_bwd");
+  if (st) return st;
+  if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
+    return set_error(BSATTN_EUNSUPPORTED, "lf_bwd: tensor too large");
+  if ((st = check_workspace(workspace, ws_bytes, lf_bwd_workspace_bytes(P, batch, heads), "lf_bwd")))
+    return st;
+  if ((st = check_device(P->device))) return st;
+  return launch_lf_bwd(P, batch, heads, scale, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream);
 }
 
 const char* bsattn_status_str(int status) {

@@ -41,6 +41,18 @@ __device__ __forceinline__ void scale_operands(bf16x8 (&qB)[4], float sl2) {
   }
 }
 
+// The same rounding applied to a staged tile (32 values per thread), so that a
+// kernel holding Q in LDS tiles scores with exactly the forward's operands.
+__device__ __forceinline__ void scale_tile(TileRegs& t, float sl2) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(bf16_lo(t.v[u][e]) * sl2, bf16_hi(t.v[u][e]) * sl2);
+    t.v[u] = w;
+  }
+}
+
 // S^T for the 64 keys of the LDS tile sK (natural layout) against this lane's query,
 // accumulated on top of `seed`.  s0 holds keys 0..31, s1 keys 32..63; register r <->
 // key 8*(r/4) + 4*hl + r%4.

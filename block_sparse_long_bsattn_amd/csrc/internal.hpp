@@ -38,13 +38,16 @@ SegPlan seg_plan(const bsattn_layout* L, int batch);
 struct lfattn_plan {
   int n = 0, w1 = 0, ng = 0, nt = 0, ngt = 0;  // tokens, window per side, globals, tiles
   int device = 0;
-  int nseg = 1;                  // items per packed global query tile
+  int nseg = 1;                  // kLfSeg-tile segments of a full row or column
+  int ngkt = 0;                  // key tiles holding at least one global token
   int32_t* d_gtok = nullptr;     // [ng] global positions ascending
   int32_t* d_gidx = nullptr;     // [n] index into d_gtok, or -1 for non-global tokens
   uint64_t* d_tile_gmask = nullptr;  // [nt] bit x set iff token 64*t + x is global
+  int32_t* d_ktiles = nullptr;   // [nt] tiles without global tokens, then those with
   std::vector<int32_t> gtok;     // host copies backing the build-time uploads
   std::vector<int32_t> gidx;
   std::vector<uint64_t> tile_gmask;
+  std::vector<int32_t> ktiles;
 };
 
 namespace bsattn {
@@ -84,5 +87,9 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const
 size_t fwd_workspace_bytes(const bsattn_layout* L, int batch);
 size_t bwd_workspace_bytes(const bsattn_layout* L, int batch);
 size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads);
+int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
+                  const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t stream);
+size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads);
 
 }  // namespace bsattn

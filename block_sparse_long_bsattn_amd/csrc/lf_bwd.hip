@@ -1,0 +1,601 @@
+// Longformer sliding-window + symmetric global attention backward on gfx950.
+//
+// The page gives the forward only ("Longformer: The Long-Document Transformer",
+// §3.1 "Sliding Window" and "Global Attention", eq. (1)); this is its exact
+// gradient, recomputing P = exp(scale * Q K^T - lse) from the saved log-sum-exp:
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = scale * dS K,  dK = scale * dS^T Q,
+// where token p attends to token q iff |p - q| <= w1, or p is global, or q is
+// global.  No atomics: every output tile has one owner.
+//
+// Kernels (per call):
+//   lf_bwd_dq    row-owned, two kinds of item:
+//                * a 64-row query tile (not made only of global tokens): its band
+//                  key tiles, then the tiles of global keys outside them (rows
+//                  gathered by index), as in the forward; writes D for its rows and
+//                  dQ for its non-global rows;
+//                * a segment of kLfSeg key tiles for a tile of global query rows
+//                  (full rows): writes D (first segment) and an fp32 partial dQ.
+//   lf_bwd_dkdv  column-owned, two kinds of item:
+//                * a 64-key tile holding no global key: the query tiles within the
+//                  band, then the global query rows outside them (gathered);
+//                * a segment of kLfSeg query tiles for a key tile holding global
+//                  keys (their columns are full): fp32 partial dK, dV.
+//   lf_bwd_reduce  sums the partials in segment order and writes dQ of the
+//                global rows and dK, dV of the key tiles holding global keys.
+
+#include "attn_tile.hpp"
+#include "internal.hpp"
+#include "lf_tile.hpp"
+
+namespace bsattn {
+namespace {
+
+constexpr int kThreads = 128;
+constexpr int kTile = kBlock * kHead;
+
+struct LfBwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dbuf;       // D [B*H*n]
+  float* part_q;     // [B*H*ngt*nseg][64][64] dQ of the global query rows
+  float* part_kv;    // [B*H*ngkt*nseg][2][64][64] dK, dV of key tiles holding global keys
+  const int32_t* gtok;         // [ng]
+  const int32_t* gidx;         // [n]
+  const uint64_t* tile_gmask;  // [nt]
+  const int32_t* ktiles;       // [nt]: key tiles without global keys, then those with
+  int heads, n, nt, ng, ngt, ngkt, nseg, w1;
+  int dq_band_items, dq_items, kv_plain_items, kv_items;
+  float scale, sl2;
+};
+
+// Sets the score registers of (row = key kx, column = this lane's query p) to -inf
+// unless allowed(p, q); the S^T layout of the dQ kernel.
+template <typename Allowed>
+__device__ __forceinline__ void mask_keys(f32x16& s0, f32x16& s1, int hl, Allowed allowed) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kx = 8 * (r >> 2) + 4 * hl + (r & 3);
+    if (!allowed(kx)) s0[r] = -INFINITY;
+    if (!allowed(32 + kx)) s1[r] = -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and D)
+// ---------------------------------------------------------------------------
+
+typedef uint16_t LdsTile[kBlock * kLdsStride];
+
+// One dQ item; kBand: a 64-row query tile (v indexes B*H*nt), else a segment of a
+// global query tile (v indexes B*H*ngt*nseg).
+template <bool kBand>
+__device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTile* sK,
+                                               LdsTile* sV) {
+  constexpr bool band = kBand;
+  int bh, t = 0, gt = 0, seg = 0;
+  if constexpr (kBand) {
+    bh = v / a.nt;
+    t = v - bh * a.nt;
+    if (a.tile_gmask[t] == ~0ull) return;   // all rows global: the global items own them
+  } else {
+    const int per_bh = a.ngt * a.nseg;
+    bh = v / per_bh;
+    const int rem = v - bh * per_bh;
+    gt = rem / a.nseg;
+    seg = rem - gt * a.nseg;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const size_t bh_off = (size_t)bh * a.n * kHead;
+  // this lane's query token
+  const int p = band ? t * kBlock + 32 * wave + col : global_token(a.gtok, a.ng, gt, 32 * wave + col);
+
+  // key tiles: band items walk [lo_u, hi_u] then the global tiles with an eligible
+  // key; global items walk the kLfSeg natural tiles of their segment
+  int lo_u = 0, hi_u = -1, ntile;
+  if constexpr (kBand) {
+    band_range(t, a.w1, a.nt, lo_u, hi_u);
+    ntile = hi_u - lo_u + 1 + a.ngt;
+  } else {
+    lo_u = seg * kLfSeg;
+    hi_u = min(a.nt, lo_u + kLfSeg) - 1;
+    ntile = hi_u - lo_u + 1;
+  }
+  const int nband = hi_u - lo_u + 1;
+  auto next_tile = [&](int x) -> int {
+    while (x < ntile && x >= nband &&
+           global_rows_outside(a.gtok, a.ng, x - nband, lo_u, hi_u, lane) == 0ull)
+      ++x;
+    return x;
+  };
+  auto tile_load = [&](int x, TileRegs& kr, TileRegs& vr) {
+    if (x < nband) {
+      gload_nat(kr, a.k + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
+      gload_nat(vr, a.v + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
+    } else {
+      gload_gather(kr, a.k + bh_off, a.gtok, a.ng, x - nband, tid);
+      gload_gather(vr, a.v + bh_off, a.gtok, a.ng, x - nband, tid);
+    }
+  };
+
+  int x = next_tile(0);
+  TileRegs kr, vr;
+  if (x < ntile) tile_load(x, kr, vr);
+  bf16x8 qB[4], doB[4];
+  float dsum = 0.f;
+  {
+    const size_t off = bh_off + (size_t)p * kHead + 8 * hl;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 qv = ldg16(a.q + off + 16 * c);
+      const u32x4 dv = ldg16(a.dout + off + 16 * c);
+      const u32x4 ov = ldg16(a.o + off + 16 * c);
+      qB[c] = __builtin_bit_cast(bf16x8, qv);
+      doB[c] = __builtin_bit_cast(bf16x8, dv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsum = __builtin_fmaf(bf16_lo(dv[e]), bf16_lo(ov[e]), dsum);
+        dsum = __builtin_fmaf(bf16_hi(dv[e]), bf16_hi(ov[e]), dsum);
+      }
+    }
+  }
+  const float Dq = partner_sum(dsum);   // D = rowsum(dO * O)
+  if (seg == 0 && hl == 0) a.dbuf[(size_t)bh * a.n + p] = Dq;
+  scale_operands(qB, a.sl2);
+  const float lse2 = a.lse[(size_t)bh * a.n + p] * kLog2e;
+  if (x < ntile) {
+    lds_store_nat(sK[0], kr, tid);
+    lds_store_nat(sV[0], vr, tid);
+  }
+  wait_all_loads();
+
+  const uint64_t gm_q = band ? a.tile_gmask[t] : 0ull;
+  f32x16 g0 = zero16(), g1 = zero16();   // dQ^T, d rows 0..31 and 32..63
+  int cur = 0;
+  while (x < ntile) {
+    __syncthreads();
+    const int xn = next_tile(x + 1);
+    if (xn < ntile) tile_load(xn, kr, vr);
+    // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
+    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 k0 = ld16(sK[cur] + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 k1 = ld16(sK[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 v0 = ld16(sV[cur] + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 v1 = ld16(sV[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      s0 = mfma32(k0, qB[c], s0);
+      s1 = mfma32(k1, qB[c], s1);
+      p0 = mfma32(v0, doB[c], p0);
+      p1 = mfma32(v1, doB[c], p1);
+    }
+    if constexpr (kBand) {
+      if (x < nband) {
+        const int u0 = (lo_u + x) * kBlock;
+        const int i0 = t * kBlock;
+        const int far = max(abs(i0 - (u0 + kBlock - 1)), abs(i0 + kBlock - 1 - u0));
+        if (far > a.w1) {
+          const uint64_t gm = a.tile_gmask[lo_u + x];
+          mask_keys(s0, s1, hl, [&](int kx) {
+            return abs(p - (u0 + kx)) <= a.w1 || ((gm >> kx) & 1ull);
+          });
+        }
+      } else {
+        const uint64_t el = global_rows_outside(a.gtok, a.ng, x - nband, lo_u, hi_u, lane);
+        if (el != ~0ull) mask_keys(s0, s1, hl, [&](int kx) { return ((el >> kx) & 1ull) != 0; });
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = fast_exp2(s0[r] - lse2) * (p0[r] - Dq);      // dS = P * (dP - D)
+      s1[r] = fast_exp2(s1[r] - lse2) * (p1[r] - Dq);
+    }
+    // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]; K^T from transpose reads
+    const bf16x8 dc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      g0 = mfma32(ld_tr8(sK[cur], 0, c, lane), dc[c], g0);
+      g1 = mfma32(ld_tr8(sK[cur], 1, c, lane), dc[c], g1);
+    }
+    if (xn < ntile) {
+      lds_store_nat(sK[cur ^ 1], kr, tid);
+      lds_store_nat(sV[cur ^ 1], vr, tid);
+    }
+    cur ^= 1;
+    x = xn;
+  }
+
+  const float sc = a.scale;
+  if constexpr (kBand) {
+    if (!((gm_q >> (32 * wave + col)) & 1ull)) {   // rows of global tokens: global items
+      uint16_t* op = a.dq + bh_off + (size_t)p * kHead + 4 * hl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w0, w1;
+        w0[0] = pack_bf16x2(g0[4 * j] * sc, g0[4 * j + 1] * sc);
+        w0[1] = pack_bf16x2(g0[4 * j + 2] * sc, g0[4 * j + 3] * sc);
+        w1[0] = pack_bf16x2(g1[4 * j] * sc, g1[4 * j + 1] * sc);
+        w1[1] = pack_bf16x2(g1[4 * j + 2] * sc, g1[4 * j + 3] * sc);
+        *reinterpret_cast<u32x2*>(op + 8 * j) = w0;
+        *reinterpret_cast<u32x2*>(op + 32 + 8 * j) = w1;
+      }
+    }
+  } else {
+    const size_t slot = ((size_t)bh * a.ngt + gt) * a.nseg + seg;
+    float* pp = a.part_q + slot * kTile + (32 * wave + col) * kHead + 4 * hl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 w0, w1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { w0[e] = g0[4 * j + e] * sc; w1[e] = g1[4 * j + e] * sc; }
+      *reinterpret_cast<f32x4*>(pp + 8 * j) = w0;
+      *reinterpret_cast<f32x4*>(pp + 32 + 8 * j) = w1;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void lf_bwd_dq_kernel(LfBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) LdsTile sK[2];
+  __shared__ __attribute__((aligned(16))) LdsTile sV[2];
+  const int v = xcd_remap(blockIdx.x, a.dq_items);
+  if (v >= a.dq_items) return;
+  if (v < a.dq_band_items)
+    lf_bwd_dq_item<true>(a, v, sK, sV);
+  else
+    lf_bwd_dq_item<false>(a, v - a.dq_band_items, sK, sV);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+
+// One dK/dV item; kPlain: a key tile without global keys (v indexes
+// B*H*(nt - ngkt)), else a segment of a key tile holding global keys.
+template <bool kPlain>
+__device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsTile* sQ,
+                                                 LdsTile* sO, float (*sL)[kBlock],
+                                                 float (*sD)[kBlock]) {
+  const int nplain = a.nt - a.ngkt;   // key tiles without global keys
+  int bh, u, gki = 0, seg = 0;
+  if constexpr (kPlain) {
+    bh = v / nplain;
+    u = a.ktiles[v - bh * nplain];
+  } else {
+    const int per_bh = a.ngkt * a.nseg;
+    bh = v / per_bh;
+    const int rem = v - bh * per_bh;
+    gki = rem / a.nseg;
+    seg = rem - gki * a.nseg;
+    u = a.ktiles[nplain + gki];
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const size_t bh_off = (size_t)bh * a.n * kHead;
+  const int kx = 32 * wave + col;       // this lane's key within the tile
+  const int q_tok = u * kBlock + kx;    // ... and its token
+  const uint64_t gm_k = a.tile_gmask[u];
+  const bool key_global = (gm_k >> kx) & 1ull;
+
+  // query tiles: plain items walk the band tiles [lo, hi], then the global tiles
+  // with an eligible row; segment items walk kLfSeg natural tiles
+  int lo, hi, ntile;
+  if constexpr (kPlain) {
+    band_range(u, a.w1, a.nt, lo, hi);
+    ntile = hi - lo + 1 + a.ngt;
+  } else {
+    lo = seg * kLfSeg;
+    hi = min(a.nt, lo + kLfSeg) - 1;
+    ntile = hi - lo + 1;
+  }
+  const int nband = hi - lo + 1;
+  auto next_tile = [&](int x) -> int {
+    while (x < ntile && x >= nband &&
+           global_rows_outside(a.gtok, a.ng, x - nband, lo, hi, lane) == 0ull)
+      ++x;
+    return x;
+  };
+  const uint16_t* qbase = a.q + bh_off;
+  const uint16_t* dobase = a.dout + bh_off;
+  const float* lbase = a.lse + (size_t)bh * a.n;
+  const float* dbase = a.dbuf + (size_t)bh * a.n;
+  // tile loads plus the lse and D of row tid (tid < 64)
+  auto tile_load = [&](int x, TileRegs& qr, TileRegs& dr, float& lv, float& dval) {
+    int tok_row;
+    if (x < nband) {
+      gload_nat(qr, qbase + (size_t)(lo + x) * kBlock * kHead, tid);
+      gload_nat(dr, dobase + (size_t)(lo + x) * kBlock * kHead, tid);
+      tok_row = (lo + x) * kBlock + (tid & 63);
+    } else {
+      gload_gather(qr, qbase, a.gtok, a.ng, x - nband, tid);
+      gload_gather(dr, dobase, a.gtok, a.ng, x - nband, tid);
+      tok_row = global_token(a.gtok, a.ng, x - nband, tid & 63);
+    }
+    if (tid < kBlock) {
+      lv = lbase[tok_row];
+      dval = dbase[tok_row];
+    }
+  };
+
+  int x = next_tile(0);
+  TileRegs qr, dr;
+  float lv = 0.f, dval = 0.f;
+  if (x < ntile) tile_load(x, qr, dr, lv, dval);
+  bf16x8 kB[4], vB[4];
+  {
+    const size_t off = bh_off + (size_t)q_tok * kHead + 8 * hl;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      kB[c] = ld16(a.k + off + 16 * c);
+      vB[c] = ld16(a.v + off + 16 * c);
+    }
+  }
+  // Q tiles are staged pre-scaled by scale*log2(e), rounded to bf16 exactly as the
+  // forward rounds its Q operand, so P here is the forward's P bit for bit in the
+  // exponent; dK is rescaled by scale / (scale*log2(e)) at the end
+  if (x < ntile) {
+    scale_tile(qr, a.sl2);
+    lds_store_nat(sQ[0], qr, tid);
+    lds_store_nat(sO[0], dr, tid);
+    if (tid < kBlock) { sL[0][tid] = -lv * kLog2e; sD[0][tid] = -dval; }
+  }
+  wait_all_loads();
+
+  f32x16 dv0 = zero16(), dv1 = zero16(), dk0 = zero16(), dk1 = zero16();
+  int cur = 0;
+  while (x < ntile) {
+    __syncthreads();
+    const int xn = next_tile(x + 1);
+    if (xn < ntile) tile_load(xn, qr, dr, lv, dval);
+    // S[q][key] = Q K^T, dP[q][key] = dO V^T; rows = queries (2 tiles), column = key.
+    // Row q of register r is 32*qt + 8*(r/4) + 4*hl + r%4.
+    f32x16 s0, s1, p0, p1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sL[cur][8 * j + 4 * hl]);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sL[cur][32 + 8 * j + 4 * hl]);
+      const f32x4 D0 = *reinterpret_cast<const f32x4*>(&sD[cur][8 * j + 4 * hl]);
+      const f32x4 D1 = *reinterpret_cast<const f32x4*>(&sD[cur][32 + 8 * j + 4 * hl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s0[4 * j + e] = l0[e];
+        s1[4 * j + e] = l1[e];
+        p0[4 * j + e] = D0[e];
+        p1[4 * j + e] = D1[e];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 q0 = ld16(sQ[cur] + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 q1 = ld16(sQ[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 o0 = ld16(sO[cur] + col * kLdsStride + 16 * c + 8 * hl);
+      const bf16x8 o1 = ld16(sO[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+      s0 = mfma32(q0, kB[c], s0);
+      s1 = mfma32(q1, kB[c], s1);
+      p0 = mfma32(o0, vB[c], p0);
+      p1 = mfma32(o1, vB[c], p1);
+    }
+    // allowed (query row qx of this tile, this lane's key): in the band, or the
+    // query is global, or the key is global
+    if (x < nband) {
+      const int tq = lo + x, p0tok = tq * kBlock;
+      const uint64_t gm_q = a.tile_gmask[tq];
+      const int far = max(abs(p0tok - (u * kBlock + kBlock - 1)), abs(p0tok + kBlock - 1 - u * kBlock));
+      if (far > a.w1 && !key_global) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qx = 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (abs(p0tok + qx - q_tok) > a.w1 && !((gm_q >> qx) & 1ull)) s0[r] = -INFINITY;
+          if (abs(p0tok + 32 + qx - q_tok) > a.w1 && !((gm_q >> (32 + qx)) & 1ull)) s1[r] = -INFINITY;
+        }
+      }
+    } else {
+      const uint64_t el = global_rows_outside(a.gtok, a.ng, x - nband, lo, hi, lane);
+      if (el != ~0ull) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qx = 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (!((el >> qx) & 1ull)) s0[r] = -INFINITY;
+          if (!((el >> (32 + qx)) & 1ull)) s1[r] = -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = fast_exp2(s0[r]);             // P
+      s1[r] = fast_exp2(s1[r]);
+      p0[r] *= s0[r];                       // dS = P * (dP - D)
+      p1[r] *= s1[r];
+    }
+    // dV^T[d][key] += sum_q dO^T[d][q] P[q][key];  dK^T[d][key] += sum_q Q^T[d][q] dS[q][key]
+    const bf16x8 pc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
+    const bf16x8 dc[4] = {pack8(p0, 0), pack8(p0, 8), pack8(p1, 0), pack8(p1, 8)};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      dv0 = mfma32(ld_tr8(sO[cur], 0, c, lane), pc[c], dv0);
+      dv1 = mfma32(ld_tr8(sO[cur], 1, c, lane), pc[c], dv1);
+      dk0 = mfma32(ld_tr8(sQ[cur], 0, c, lane), dc[c], dk0);
+      dk1 = mfma32(ld_tr8(sQ[cur], 1, c, lane), dc[c], dk1);
+    }
+    if (xn < ntile) {
+      scale_tile(qr, a.sl2);
+      lds_store_nat(sQ[cur ^ 1], qr, tid);
+      lds_store_nat(sO[cur ^ 1], dr, tid);
+      if (tid < kBlock) { sL[cur ^ 1][tid] = -lv * kLog2e; sD[cur ^ 1][tid] = -dval; }
+    }
+    cur ^= 1;
+    x = xn;
+  }
+
+  const float sc = a.scale / a.sl2;   // dK was accumulated against the scaled Q
+  if constexpr (kPlain) {
+    const size_t off = bh_off + (size_t)q_tok * kHead + 4 * hl;
+    uint16_t* kp = a.dk + off;
+    uint16_t* vp = a.dv + off;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 k0w, k1w, v0w, v1w;
+      k0w[0] = pack_bf16x2(dk0[4 * j] * sc, dk0[4 * j + 1] * sc);
+      k0w[1] = pack_bf16x2(dk0[4 * j + 2] * sc, dk0[4 * j + 3] * sc);
+      k1w[0] = pack_bf16x2(dk1[4 * j] * sc, dk1[4 * j + 1] * sc);
+      k1w[1] = pack_bf16x2(dk1[4 * j + 2] * sc, dk1[4 * j + 3] * sc);
+      v0w[0] = pack_bf16x2(dv0[4 * j], dv0[4 * j + 1]);
+      v0w[1] = pack_bf16x2(dv0[4 * j + 2], dv0[4 * j + 3]);
+      v1w[0] = pack_bf16x2(dv1[4 * j], dv1[4 * j + 1]);
+      v1w[1] = pack_bf16x2(dv1[4 * j + 2], dv1[4 * j + 3]);
+      *reinterpret_cast<u32x2*>(kp + 8 * j) = k0w;
+      *reinterpret_cast<u32x2*>(kp + 32 + 8 * j) = k1w;
+      *reinterpret_cast<u32x2*>(vp + 8 * j) = v0w;
+      *reinterpret_cast<u32x2*>(vp + 32 + 8 * j) = v1w;
+    }
+  } else {
+    const size_t slot = ((size_t)bh * a.ngkt + gki) * a.nseg + seg;
+    float* pk = a.part_kv + slot * 2 * kTile + kx * kHead + 4 * hl;
+    float* pv = pk + kTile;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 k0w, k1w, v0w, v1w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k0w[e] = dk0[4 * j + e] * sc; k1w[e] = dk1[4 * j + e] * sc;
+        v0w[e] = dv0[4 * j + e]; v1w[e] = dv1[4 * j + e];
+      }
+      *reinterpret_cast<f32x4*>(pk + 8 * j) = k0w;
+      *reinterpret_cast<f32x4*>(pk + 32 + 8 * j) = k1w;
+      *reinterpret_cast<f32x4*>(pv + 8 * j) = v0w;
+      *reinterpret_cast<f32x4*>(pv + 32 + 8 * j) = v1w;
+    }
+  }
+}
+
+// Occupancy 1 (AGPRs hold the overflow): at two waves per SIMD this kernel spilled
+// inside its loop and ran ~20 % slower.
+__global__ __launch_bounds__(kThreads) void lf_bwd_dkdv_kernel(LfBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) LdsTile sQ[2];
+  __shared__ __attribute__((aligned(16))) LdsTile sO[2];   // dO
+  __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
+  const int v = xcd_remap(blockIdx.x, a.kv_items);
+  if (v >= a.kv_items) return;
+  if (v < a.kv_plain_items)
+    lf_bwd_dkdv_item<true>(a, v, sQ, sO, sL, sD);
+  else
+    lf_bwd_dkdv_item<false>(a, v - a.kv_plain_items, sQ, sO, sL, sD);
+}
+
+// Segment sums in segment order.  Work-groups [0, B*H*ngt): dQ of global tile gt,
+// rows scattered to their tokens; then B*H*ngkt*2: dK (kind 0) or dV (kind 1) of
+// the key tiles holding global keys.
+__global__ __launch_bounds__(256) void lf_bwd_reduce_kernel(LfBwdArgs a, int nq_groups) {
+  const int e0 = threadIdx.x * 16;   // 16 consecutive floats of the 64x64 tile
+  const int row = e0 / kHead;
+  const float* src;
+  size_t stride;
+  uint16_t* dst;
+  if ((int)blockIdx.x < nq_groups) {
+    const int idx = blockIdx.x;   // bh * ngt + gt
+    const int bh = idx / a.ngt, gt = idx - bh * a.ngt;
+    const int j = gt * kBlock + row;
+    if (j >= a.ng) return;
+    src = a.part_q + (size_t)idx * a.nseg * kTile + e0;
+    stride = kTile;
+    dst = a.dq + ((size_t)bh * a.n + a.gtok[j]) * kHead + (e0 % kHead);
+  } else {
+    const int w = blockIdx.x - nq_groups;
+    const int kind = w & 1, idx = w >> 1;   // idx = bh * ngkt + gki
+    const int bh = idx / a.ngkt, gki = idx - bh * a.ngkt;
+    const int u = a.ktiles[a.nt - a.ngkt + gki];
+    src = a.part_kv + (size_t)idx * a.nseg * 2 * kTile + kind * kTile + e0;
+    stride = 2 * kTile;
+    dst = (kind == 0 ? a.dk : a.dv) + ((size_t)bh * a.n + (size_t)u * kBlock) * kHead + e0;
+  }
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < a.nseg; ++s) {
+    const float* ps = src + (size_t)s * stride;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(ps + e);
+      acc[e] += x[0]; acc[e + 1] += x[1]; acc[e + 2] += x[2]; acc[e + 3] += x[3];
+    }
+  }
+  store16_bf16(dst, acc, 1.f);
+}
+
+struct LfBwdWs {
+  size_t dbuf, part_q, part_kv, total;
+};
+
+LfBwdWs lf_bwd_ws_layout(const lfattn_plan* P, int batch, int heads) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t bh = (size_t)batch * heads;
+  LfBwdWs w;
+  w.dbuf = 0;
+  w.part_q = up(bh * P->n * sizeof(float));
+  w.part_kv = up(w.part_q + bh * P->ngt * P->nseg * kTile * sizeof(float));
+  w.total = up(w.part_kv + bh * P->ngkt * P->nseg * 2 * kTile * sizeof(float));
+  return w;
+}
+
+}  // namespace
+
+size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads) {
+  return lf_bwd_ws_layout(P, batch, heads).total;
+}
+
+int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
+                  const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t stream) {
+  const LfBwdWs w = lf_bwd_ws_layout(P, batch, heads);
+  char* base = (char*)ws;
+  LfBwdArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o; a.lse = lse; a.dout = (const uint16_t*)dout;
+  a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
+  a.dbuf = (float*)(base + w.dbuf);
+  a.part_q = (float*)(base + w.part_q);
+  a.part_kv = (float*)(base + w.part_kv);
+  a.gtok = P->d_gtok; a.gidx = P->d_gidx; a.tile_gmask = P->d_tile_gmask;
+  a.ktiles = P->d_ktiles;
+  a.heads = heads; a.n = P->n; a.nt = P->nt; a.ng = P->ng; a.ngt = P->ngt;
+  a.ngkt = P->ngkt; a.nseg = P->nseg; a.w1 = P->w1;
+  a.scale = scale;
+  a.sl2 = scale * kLog2e;
+  const int bhn = batch * heads;
+  a.dq_band_items = bhn * P->nt;
+  a.dq_items = a.dq_band_items + bhn * P->ngt * P->nseg;
+  a.kv_plain_items = bhn * (P->nt - P->ngkt);
+  a.kv_items = a.kv_plain_items + bhn * P->ngkt * P->nseg;
+  int st;
+  {
+    ProfScope prof_("lf_bwd_dq", stream);
+    hipLaunchKernelGGL(lf_bwd_dq_kernel, dim3(8 * ((a.dq_items + 7) / 8)), dim3(kThreads), 0,
+                       stream, a);
+  }
+  if ((st = check_hip(hipGetLastError(), "lf_bwd_dq launch"))) return st;
+  {
+    ProfScope prof_("lf_bwd_dkdv", stream);
+    hipLaunchKernelGGL(lf_bwd_dkdv_kernel, dim3(8 * ((a.kv_items + 7) / 8)), dim3(kThreads), 0,
+                       stream, a);
+  }
+  if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv launch"))) return st;
+  const int nq_groups = bhn * P->ngt;
+  const int groups = nq_groups + bhn * P->ngkt * 2;
+  if (groups == 0) return 0;
+  {
+    ProfScope prof_("lf_bwd_reduce", stream);
+    hipLaunchKernelGGL(lf_bwd_reduce_kernel, dim3(groups), dim3(256), 0, stream, a, nq_groups);
+  }
+  return check_hip(hipGetLastError(), "lf_bwd_reduce launch");
+}
+
+}  // namespace bsattn

@@ -21,6 +21,7 @@
 
 #include "attn_tile.hpp"
 #include "internal.hpp"
+#include "lf_tile.hpp"
 
 namespace bsattn {
 namespace {
@@ -44,23 +45,6 @@ struct LfArgs {
 
 typedef uint16_t LdsTile[kBlock * kLdsStride];
 
-__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
-
-// Token behind row x of global tile gt: the (gt*64 + x)-th global token; rows past
-// the last one repeat it (their keys are masked out, their query rows not written).
-__device__ __forceinline__ int global_token(const LfArgs& a, int gt, int x) {
-  return a.gtok[min(gt * kBlock + x, a.ng - 1)];
-}
-
-// gload_nat for a tile of global tokens, rows gathered from the [n][64] tensor.
-__device__ __forceinline__ void gload_gather(TileRegs& r, const LfArgs& a, const uint16_t* base,
-                                             int gt, int tid) {
-  const int c = tid & 7, row = tid >> 3;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    r.v[u] = ldg16(base + (size_t)global_token(a, gt, row + 16 * u) * kHead + 8 * c);
-}
-
 __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK, LdsTile* sV) {
   const int bh = v / a.nt, t = v - bh * a.nt;
   if (a.tile_gmask[t] == ~0ull) return;   // every row global: the global items own them
@@ -76,21 +60,15 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
 #pragma unroll
     for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
   }
-  const int lo_u = max(0, i0 - a.w1) / kBlock;
-  const int hi_u = min(a.nt - 1, (i0 + kBlock - 1 + a.w1) / kBlock);
+  int lo_u, hi_u;
+  band_range(t, a.w1, a.nt, lo_u, hi_u);
   const int nband = hi_u - lo_u + 1;
   const int ntile = nband + a.ngt;
 
   // Global tile gt contributes key j iff j < ng and the key's own tile lies
   // outside [lo_u, hi_u] (inside, the band tile already counts it).
   auto global_elig = [&](int gt) -> uint64_t {
-    const int j = gt * kBlock + lane;
-    bool ok = false;
-    if (j < a.ng) {
-      const int u = a.gtok[j] / kBlock;
-      ok = u < lo_u || u > hi_u;
-    }
-    return ballot64(ok);
+    return global_rows_outside(a.gtok, a.ng, gt, lo_u, hi_u, lane);
   };
 
   scale_operands(qB, a.sl2);
@@ -101,8 +79,8 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
       gload_nat(kr, a.k + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
       gload_nat(vr, a.v + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
     } else {
-      gload_gather(kr, a, a.k + bh_off, x - nband, tid);
-      gload_gather(vr, a, a.v + bh_off, x - nband, tid);
+      gload_gather(kr, a.k + bh_off, a.gtok, a.ng, x - nband, tid);
+      gload_gather(vr, a.v + bh_off, a.gtok, a.ng, x - nband, tid);
     }
   };
 
@@ -181,7 +159,7 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
 
   bf16x8 qB[4];
   {
-    const uint16_t* qp = a.q + bh_off + (size_t)global_token(a, gt, qr) * kHead + 8 * hl;
+    const uint16_t* qp = a.q + bh_off + (size_t)global_token(a.gtok, a.ng, gt, qr) * kHead + 8 * hl;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
   }

@@ -202,6 +202,29 @@ int lfattn_fwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtyp
                float scale, const void* q, const void* k, const void* v, void* o,
                float* lse, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes lfattn_bwd needs.  d must be 64.  0 for invalid arguments. */
+size_t lfattn_bwd_workspace(const lfattn_plan* plan, int batch, int heads, int d);
+
+/*
+ * Longformer backward: the exact gradient of lfattn_fwd for the loss <dout, O>
+ * (the page describes the forward only; the gradient is the plain one of
+ * softmax attention restricted to the plan's token pattern).
+ *   q, k, v, o  DEVICE [batch, heads, n, d] (o from lfattn_fwd).
+ *   lse         DEVICE float32 [batch, heads, n] from lfattn_fwd (required).
+ *   dout        DEVICE [batch, heads, n, d].
+ *   dq, dk, dv  DEVICE [batch, heads, n, d], written.
+ *   workspace   DEVICE scratch of at least lfattn_bwd_workspace() bytes.
+ * Every output tile has a single owning work-group; the full rows of global
+ * queries and the full columns of key tiles holding global keys are split into
+ * segments whose fp32 partials are summed in a fixed order.  No atomics, so
+ * results are bitwise reproducible.  dt must be BSATTN_BF16 (else EUNSUPPORTED).
+ * Returns OK, EINVAL, EUNSUPPORTED or EHIP.
+ */
+int lfattn_bwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,
+               float scale, const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Diagnostics                                                                */
 /* ------------------------------------------------------------------------- */

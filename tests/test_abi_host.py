@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_binding_exports():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     assert sorted(_lib.EXPORTS) == names
 
 
@@ -77,11 +77,13 @@ def test_null_handles_are_rejected():
     assert lib.bsattn_fwd(None, 1, 64, 1, 0.125, None, None, None, None, None, None, 0, None) == -1
     assert lib.bsattn_bwd(None, 1, 64, 1, 0.125, *([None] * 9), None, 0, None) == -1
     assert lib.lfattn_fwd(None, 1, 1, 64, 1, 0.125, *([None] * 5), None, 0, None) == -1
+    assert lib.lfattn_bwd(None, 1, 1, 64, 1, 0.125, *([None] * 9), None, 0, None) == -1
     assert lib.bsattn_layout_info(None, None, None, None) == -1
     assert lib.bsattn_layout_rebuild(None, 1, None) == -1
     assert lib.bsattn_fwd_workspace(None, 1, 64) == 0
     assert lib.bsattn_bwd_workspace(None, 1, 64) == 0
     assert lib.lfattn_fwd_workspace(None, 1, 1, 64) == 0
+    assert lib.lfattn_bwd_workspace(None, 1, 1, 64) == 0
     assert lib.bsattn_layout_destroy(None) == 0
     assert lib.lfattn_plan_destroy(None) == 0
     assert lib.bsattn_profile_read(-1, None, None, None, None) == -1

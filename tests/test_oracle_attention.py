@@ -321,3 +321,40 @@ def test_longformer_zero_queries_closed_form():
             if p not in G else list(range(n))
         np.testing.assert_allclose(o[0, 0, p], v[0, 0, keys].mean(0), rtol=0, atol=1e-13)
         assert abs(lse[0, 0, p] - math.log(len(keys))) < 1e-13
+
+
+def test_longformer_backward_finite_differences():
+    """The backward the Longformer GPU gradient is checked against, pinned by central
+    differences of the forward on a tiny band + scattered-global pattern."""
+    n, H, d, w1 = 48, 1, 6, 3
+    G = [0, 29]
+    mask = LF.longformer_mask(n, w1, G)
+    q, k, v, do = (rnd(s, 1, H, n, d) for s in (61, 62, 63, 64))
+    scale = 0.5
+    dq, dk, dv = A.attention_bwd(q, k, v, do, mask, scale)
+
+    def loss(q_, k_, v_):
+        o, _ = A.attention_fwd(q_, k_, v_, mask, scale)
+        return float((o * do).sum())
+
+    eps = 1e-5
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for t in range(3):
+            e = rnd(200 + 10 * which + t, 1, H, n, d)
+            plus, minus = [q, k, v], [q, k, v]
+            plus[which] = plus[which] + eps * e
+            minus[which] = minus[which] - eps * e
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            an = float((grad * e).sum())
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+def test_longformer_backward_full_window_matches_autograd():
+    n, H, d = 96, 2, 16
+    q, k, v, do = (rnd(s, 1, H, n, d) for s in (65, 66, 67, 68))
+    dq, dk, dv = A.attention_bwd(q, k, v, do, LF.longformer_mask(n, n, [5]), 0.25)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.softmax(0.25 * tq @ tk.transpose(-1, -2), dim=-1) @ tv
+    o.backward(torch.tensor(do))
+    for a, b in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(a, b.grad.numpy(), rtol=0, atol=1e-12)
