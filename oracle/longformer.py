@@ -7,10 +7,23 @@ size w every token attends to w/2 tokens on each side.  Here the per-side count
 is the argument ``w1`` and the token itself is included, so token p sees keys q
 with |p - q| <= w1, clipped at the sequence ends.
 
+Same page, §3.1 "Dilated Sliding Window" and Fig. 2(c): the window may have gaps
+of d tokens between the tokens it attends to.  Reading: with dilation d the
+window still holds w1 tokens on each side, spaced d + 1 apart, so q is in p's
+window iff p - q is a multiple of d + 1 and |p - q| <= w1 * (d + 1).  d = 0 is
+the plain window (Table 12 lists dilation 0 for layers without dilation).  §3.1
+allows a different dilation per head, so ``dilation`` may be one value per head.
+
 Same page, §3.1 "Global Attention": attention on pre-selected locations is made
 symmetric: a global token attends to all tokens and all tokens attend to it.
 
-So token p may attend to token q iff |p - q| <= w1, or p is global, or q is
+Same page, §4.1 and App. B "Character LM Hyperparameters": the kernel has an
+autoregressive mode in which a token attends to a window of earlier tokens only.
+Reading: with ``causal`` the window keeps its left half and the token itself,
+0 <= p - q <= w1 * (d + 1); global tokens are not defined in that mode (a global
+token would see later tokens), so a causal pattern with global tokens is rejected.
+
+So token p may attend to token q iff q is in p's window, or p is global, or q is
 global.  Forward and backward then follow ``oracle.attention`` on this mask.
 """
 
@@ -19,20 +32,47 @@ from __future__ import annotations
 import numpy as np
 
 
-def longformer_allowed(p: int, q: int, w1: int, global_tokens) -> bool:
+def _check(global_tokens, causal: bool):
+    g = [int(x) for x in global_tokens]
+    if causal and g:
+        raise ValueError("the causal window has no global tokens")
+    return g
+
+
+def in_window(p: int, q: int, w1: int, dilation: int = 0, causal: bool = False) -> bool:
+    """Window membership of the pair (query p, key q) for one head."""
+    s = dilation + 1
+    delta = p - q
+    if delta % s != 0:
+        return False
+    if causal:
+        return 0 <= delta <= w1 * s
+    return abs(delta) <= w1 * s
+
+
+def longformer_allowed(p: int, q: int, w1: int, global_tokens, dilation: int = 0,
+                       causal: bool = False) -> bool:
     """Pairwise predicate, used by brute-force pins."""
-    g = set(int(x) for x in global_tokens)
-    return abs(p - q) <= w1 or p in g or q in g
+    g = set(_check(global_tokens, causal))
+    return in_window(p, q, w1, dilation, causal) or p in g or q in g
 
 
-def longformer_mask(n: int, w1: int, global_tokens):
-    """Callable row-band mask(h, p0, p1) -> bool [p1-p0, n]; identical for every head."""
+def longformer_mask(n: int, w1: int, global_tokens, dilation=0, causal: bool = False):
+    """Callable row-band mask(h, p0, p1) -> bool [p1-p0, n].
+
+    ``dilation`` is one int for every head or a sequence indexed by head."""
+    g = _check(global_tokens, causal)
     gt = np.zeros(n, dtype=bool)
-    gt[np.asarray(list(global_tokens), dtype=np.int64)] = True
+    gt[np.asarray(g, dtype=np.int64)] = True
+    per_head = not np.isscalar(dilation)
 
     def rows(h: int, p0: int, p1: int) -> np.ndarray:
+        s = int(dilation[h] if per_head else dilation) + 1
         p = np.arange(p0, p1)[:, None]
         q = np.arange(n)[None, :]
-        return (np.abs(p - q) <= w1) | gt[p0:p1, None] | gt[None, :]
+        delta = p - q
+        lo = 0 if causal else -w1 * s
+        win = (delta % s == 0) & (delta >= lo) & (delta <= w1 * s)
+        return win | gt[p0:p1, None] | gt[None, :]
 
     return rows
