@@ -28,7 +28,7 @@ EXPORTS = (
     "bsattn_layout_build", "bsattn_layout_rebuild", "bsattn_layout_info",
     "bsattn_layout_to_host", "bsattn_layout_destroy", "bsattn_fwd_workspace",
     "bsattn_bwd_workspace", "bsattn_fwd", "bsattn_bwd", "lfattn_plan_build",
-    "lfattn_plan_destroy", "lfattn_fwd_workspace", "lfattn_fwd", "lfattn_bwd_workspace",
+    "lfattn_plan_build_dilated", "lfattn_plan_destroy", "lfattn_fwd_workspace", "lfattn_fwd", "lfattn_bwd_workspace",
     "lfattn_bwd", "bsattn_status_str",
     "bsattn_last_error", "bsattn_version", "bsattn_profile_enable", "bsattn_profile_read",
 )
@@ -69,6 +69,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                c_void_p, c_size_t, c_void_p]),
         "lfattn_plan_build": (c_int, [c_int, c_int, POINTER(c_int32), c_int, c_void_p,
                                       POINTER(c_void_p)]),
+        "lfattn_plan_build_dilated": (c_int, [c_int, c_int, POINTER(c_int32), c_int, c_int,
+                                              POINTER(c_int32), c_int, c_void_p,
+                                              POINTER(c_void_p)]),
         "lfattn_plan_destroy": (c_int, [c_void_p]),
         "lfattn_fwd_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int]),
         "lfattn_fwd": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
@@ -245,6 +248,24 @@ def lfattn_plan_build(n, window_one_side, global_tokens, stream=None) -> int:
     out = c_void_p()
     _check(load().lfattn_plan_build(n, window_one_side, arr if ng else None, ng,
                                     _stream(stream), ctypes.byref(out)), "lfattn_plan_build")
+    _plan_n[out.value] = n
+    return out.value
+
+
+def lfattn_plan_build_dilated(n, window_one_side, global_tokens, heads, dilation=None,
+                              causal=False, stream=None) -> int:
+    """Plan with one dilation per head (None: 0 for every head) and the optional
+    causal window; calls must pass the same head count."""
+    arr, ng = _int32_array(global_tokens)
+    dil = None
+    if dilation is not None:
+        dil, nd = _int32_array(dilation)
+        if nd != heads:
+            raise ValueError("lfattn_plan_build_dilated: need one dilation per head")
+    out = c_void_p()
+    _check(load().lfattn_plan_build_dilated(n, window_one_side, arr if ng else None, ng, heads,
+                                            dil, 1 if causal else 0, _stream(stream),
+                                            ctypes.byref(out)), "lfattn_plan_build_dilated")
     _plan_n[out.value] = n
     return out.value
 

@@ -22,6 +22,8 @@ thread_local std::string g_last_error;
 constexpr int kMaxNb = 4096;
 constexpr int kMaxR = 64;
 constexpr int kMaxLfTokens = 262144;
+constexpr int kMaxLfDilation = 1023;   // stride and class fit the int16 fields of LfTileRef
+constexpr int kMaxLfHeads = 4096;
 }  // namespace
 
 namespace {
@@ -125,7 +127,7 @@ void free_plan(lfattn_plan* P) {
   (void)hipFree(P->d_gtok);
   (void)hipFree(P->d_gidx);
   (void)hipFree(P->d_tile_gmask);
-  (void)hipFree(P->d_ktiles);
+  (void)hipFree(P->d_ct);
   delete P;
 }
 
@@ -349,8 +351,43 @@ int bsattn_bwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float 
   return launch_bwd(L, batch, scale, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream);
 }
 
-int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, int n_global,
-                      hipStream_t stream, lfattn_plan** out) {
+}  // extern "C"
+
+namespace {
+
+// Class tiles of one head period: for each head, each residue class modulo its
+// stride and each 64-index tile of the class; tiles holding no global token
+// first, then the others, each group in (head, class, tile) order.
+void build_class_tiles(lfattn_plan* P) {
+  const int ph = P->heads > 0 ? P->heads : 1;
+  std::vector<LfTileRef> with_g;
+  P->ct.clear();
+  for (int h = 0; h < ph; ++h) {
+    const int s = P->dil[h] + 1;
+    for (int c = 0; c < s; ++c) {
+      const int nc = (P->n - c + s - 1) / s;
+      for (int t = 0; t * kBlock < nc; ++t) {
+        LfTileRef r;
+        r.h = h;
+        r.c = (int16_t)c;
+        r.s = (int16_t)s;
+        r.t = t;
+        r.nc = nc;
+        bool g = false;
+        for (int x = t * kBlock; x < std::min(nc, (t + 1) * kBlock) && !g; ++x)
+          g = P->gidx[c + s * x] >= 0;
+        (g ? with_g : P->ct).push_back(r);
+      }
+    }
+  }
+  P->nct_plain = (int)P->ct.size();
+  P->ct.insert(P->ct.end(), with_g.begin(), with_g.end());
+  P->nct = (int)P->ct.size();
+}
+
+int lf_plan_build(int n, int window_one_side, const int32_t* global_tokens, int n_global,
+                  int heads, const int32_t* dilation, int causal, hipStream_t stream,
+                  lfattn_plan** out) {
   clear_error();
   if (out == nullptr) return set_error(BSATTN_EINVAL, "lf_plan_build: out is null");
   *out = nullptr;
@@ -363,6 +400,19 @@ int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, 
     if (global_tokens[x] < 0 || global_tokens[x] >= n) return set_error(BSATTN_EINVAL, "lf_plan_build: global token out of range");
     if (x > 0 && global_tokens[x] <= global_tokens[x - 1]) return set_error(BSATTN_EINVAL, "lf_plan_build: global tokens not sorted and unique");
   }
+  if (heads < 0 || heads > kMaxLfHeads) return set_error(BSATTN_EINVAL, "lf_plan_build: heads out of range");
+  if (causal != 0 && causal != 1) return set_error(BSATTN_EINVAL, "lf_plan_build: causal must be 0 or 1");
+  if (causal && n_global > 0)
+    return set_error(BSATTN_EINVAL, "lf_plan_build: the causal window takes no global tokens");
+  for (int h = 0; dilation != nullptr && h < heads; ++h)
+    if (dilation[h] < 0 || dilation[h] > kMaxLfDilation)
+      return set_error(BSATTN_EINVAL, "lf_plan_build: dilation out of [0, 1023]");
+  // the window span w1 * (d + 1) must stay an int
+  int64_t span = window_one_side;
+  for (int h = 0; dilation != nullptr && h < heads; ++h)
+    span = std::max(span, (int64_t)window_one_side * (dilation[h] + 1));
+  if (span > ((int64_t)1 << 30)) return set_error(BSATTN_EUNSUPPORTED, "lf_plan_build: window too long");
+
   auto P = new lfattn_plan();
   P->n = n;
   P->w1 = window_one_side;
@@ -370,6 +420,14 @@ int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, 
   P->nt = n / kBlock;
   P->ngt = (n_global + kBlock - 1) / kBlock;
   P->nseg = (P->nt + kLfSeg - 1) / kLfSeg;
+  P->heads = heads;
+  P->causal = causal;
+  if (heads == 0)
+    P->dil.assign(1, 0);
+  else if (dilation == nullptr)
+    P->dil.assign(heads, 0);
+  else
+    P->dil.assign(dilation, dilation + heads);
   P->gtok.assign(global_tokens, global_tokens + n_global);
   P->gidx.assign(n, -1);
   P->tile_gmask.assign(P->nt, 0ull);
@@ -378,17 +436,13 @@ int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, 
     P->gidx[t] = x;
     P->tile_gmask[t / kBlock] |= 1ull << (t % kBlock);
   }
-  for (int t = 0; t < P->nt; ++t)
-    if (P->tile_gmask[t] == 0ull) P->ktiles.push_back(t);
-  for (int t = 0; t < P->nt; ++t)
-    if (P->tile_gmask[t] != 0ull) P->ktiles.push_back(t);
-  P->ngkt = P->nt - (int)std::count(P->tile_gmask.begin(), P->tile_gmask.end(), 0ull);
+  build_class_tiles(P);
   hipError_t e = hipGetDevice(&P->device);
   if (e != hipSuccess) { delete P; return check_hip(e, "hipGetDevice"); }
   int st;
   if ((st = dev_alloc(&P->d_gtok, (size_t)n_global)) || (st = dev_alloc(&P->d_gidx, (size_t)n)) ||
       (st = dev_alloc(&P->d_tile_gmask, (size_t)P->nt)) ||
-      (st = dev_alloc(&P->d_ktiles, (size_t)P->nt))) {
+      (st = dev_alloc(&P->d_ct, (size_t)P->nct))) {
     free_plan(P);
     return st;
   }
@@ -398,13 +452,41 @@ int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, 
                       "upload token index")) ||
       (st = check_hip(hipMemcpyAsync(P->d_tile_gmask, P->tile_gmask.data(), (size_t)P->nt * 8,
                                      hipMemcpyHostToDevice, stream), "upload tile masks")) ||
-      (st = check_hip(hipMemcpyAsync(P->d_ktiles, P->ktiles.data(), (size_t)P->nt * 4,
-                                     hipMemcpyHostToDevice, stream), "upload key tiles"))) {
+      (st = check_hip(hipMemcpyAsync(P->d_ct, P->ct.data(), (size_t)P->nct * sizeof(LfTileRef),
+                                     hipMemcpyHostToDevice, stream), "upload class tiles"))) {
     free_plan(P);
     return st;
   }
   *out = P;
   return BSATTN_OK;
+}
+
+// A plan fixed to a head count takes calls with that count only.
+int check_plan_heads(const lfattn_plan* P, int heads, const char* who) {
+  if (P->heads > 0 && heads != P->heads)
+    return set_error(BSATTN_EINVAL, std::string(who) + ": heads differ from the plan's");
+  return BSATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, int n_global,
+                      hipStream_t stream, lfattn_plan** out) {
+  return lf_plan_build(n, window_one_side, global_tokens, n_global, 0, nullptr, 0, stream, out);
+}
+
+int lfattn_plan_build_dilated(int n, int window_one_side, const int32_t* global_tokens,
+                              int n_global, int heads, const int32_t* dilation, int causal,
+                              hipStream_t stream, lfattn_plan** out) {
+  if (heads < 1) {
+    clear_error();
+    if (out != nullptr) *out = nullptr;
+    return set_error(BSATTN_EINVAL, "lf_plan_build: heads must be >= 1");
+  }
+  return lf_plan_build(n, window_one_side, global_tokens, n_global, heads, dilation, causal,
+                       stream, out);
 }
 
 int lfattn_plan_destroy(lfattn_plan* P) {
@@ -417,6 +499,7 @@ int lfattn_plan_destroy(lfattn_plan* P) {
 
 size_t lfattn_fwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
   if (P == nullptr || batch < 1 || heads < 1 || d != kHead) return 0;
+  if (P->heads > 0 && heads != P->heads) return 0;
   return lf_workspace_bytes(P, batch, heads);
 }
 
@@ -426,9 +509,10 @@ int lfattn_fwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype d
   clear_error();
   if (P == nullptr) return set_error(BSATTN_EINVAL, "lf_fwd: null plan");
   if (heads < 1) return set_error(BSATTN_EINVAL, "lf_fwd: heads must be >= 1");
-  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "lf_fwd: only bf16 is built");
-  int st = check_tensor_args(batch, d, scale, {q, k, v, o}, "lf_fwd");
+  int st = check_plan_heads(P, heads, "lf_fwd");
   if (st) return st;
+  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "lf_fwd: only bf16 is built");
+  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o}, "lf_fwd"))) return st;
   if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, "lf_fwd: lse not 16-byte aligned");
   if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, "lf_fwd: tensor too large");
@@ -439,6 +523,7 @@ int lfattn_fwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype d
 
 size_t lfattn_bwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
   if (P == nullptr || batch < 1 || heads < 1 || d != kHead) return 0;
+  if (P->heads > 0 && heads != P->heads) return 0;
   return lf_bwd_workspace_bytes(P, batch, heads);
 }
 
@@ -449,9 +534,11 @@ int lfattn_bwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype d
   clear_error();
   if (P == nullptr) return set_error(BSATTN_EINVAL, "lf_bwd: null plan");
   if (heads < 1) return set_error(BSATTN_EINVAL, "lf_bwd: heads must be >= 1");
-  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "lf_bwd: only bf16 is built");
-  int st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "lf_bwd");
+  int st = check_plan_heads(P, heads, "lf_bwd");
   if (st) return st;
+  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "lf_bwd: only bf16 is built");
+  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "lf_bwd")))
+    return st;
   if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, "lf_bwd: tensor too large");
   if ((st = check_workspace(workspace, ws_bytes, lf_bwd_workspace_bytes(P, batch, heads), "lf_bwd")))

@@ -35,19 +35,33 @@ struct SegPlan {
 };
 SegPlan seg_plan(const bsattn_layout* L, int batch);
 
+// A 64-token tile of one residue class of one head's window pattern: with stride
+// s (dilation + 1), class c holds tokens c, c + s, c + 2s, ... (nc of them); row x
+// of tile t is class index 64*t + x, i.e. token c + s*(64*t + x), valid iff that
+// index is below nc.  Stride 1 gives the natural tiles (c = 0, nc = n).
+struct LfTileRef {
+  int32_t h;        // head within the plan's head period
+  int16_t c, s;     // residue class, stride
+  int32_t t, nc;    // tile within the class, class length
+};
+
 struct lfattn_plan {
   int n = 0, w1 = 0, ng = 0, nt = 0, ngt = 0;  // tokens, window per side, globals, tiles
+  int heads = 0;                 // 0: any head count, one pattern; else the plan's heads
+  int causal = 0;                // window of earlier tokens only
   int device = 0;
   int nseg = 1;                  // kLfSeg-tile segments of a full row or column
-  int ngkt = 0;                  // key tiles holding at least one global token
+  int nct = 0;                   // class tiles per head period (all heads, or one)
+  int nct_plain = 0;             // ... of them holding no global key (listed first)
   int32_t* d_gtok = nullptr;     // [ng] global positions ascending
   int32_t* d_gidx = nullptr;     // [n] index into d_gtok, or -1 for non-global tokens
   uint64_t* d_tile_gmask = nullptr;  // [nt] bit x set iff token 64*t + x is global
-  int32_t* d_ktiles = nullptr;   // [nt] tiles without global tokens, then those with
+  LfTileRef* d_ct = nullptr;     // [nct] class tiles, those without global keys first
   std::vector<int32_t> gtok;     // host copies backing the build-time uploads
   std::vector<int32_t> gidx;
   std::vector<uint64_t> tile_gmask;
-  std::vector<int32_t> ktiles;
+  std::vector<int32_t> dil;      // dilation per head ([heads], or one value)
+  std::vector<LfTileRef> ct;
 };
 
 namespace bsattn {

@@ -1,28 +1,33 @@
 // Longformer sliding-window + symmetric global attention backward on gfx950.
 //
 // The page gives the forward only ("Longformer: The Long-Document Transformer",
-// §3.1 "Sliding Window" and "Global Attention", eq. (1)); this is its exact
-// gradient, recomputing P = exp(scale * Q K^T - lse) from the saved log-sum-exp:
+// §3.1 "Sliding Window", "Dilated Sliding Window" and "Global Attention", eq. (1);
+// the autoregressive mode of §4.1); this is its exact gradient, recomputing
+// P = exp(scale * Q K^T - lse) from the saved log-sum-exp:
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q,
-// where token p attends to token q iff |p - q| <= w1, or p is global, or q is
-// global.  No atomics: every output tile has one owner.
+// where token p attends to token q iff q is in p's (dilated, possibly causal)
+// window, or p is global, or q is global.  Each residue class of a dilated window
+// is walked in its own 64-row class tiles.  No atomics: every output tile has one
+// owner.
 //
 // Kernels (per call):
 //   lf_bwd_dq    row-owned, two kinds of item:
-//                * a 64-row query tile (not made only of global tokens): its band
-//                  key tiles, then the tiles of global keys outside them (rows
-//                  gathered by index), as in the forward; writes D for its rows and
-//                  dQ for its non-global rows;
+//                * a 64-row query class tile (not made only of global tokens): its
+//                  window's key tiles, then the tiles of global keys outside them
+//                  (rows gathered by index), as in the forward; writes D for its
+//                  rows and dQ for its non-global rows;
 //                * a segment of kLfSeg key tiles for a tile of global query rows
 //                  (full rows): writes D (first segment) and an fp32 partial dQ.
 //   lf_bwd_dkdv  column-owned, two kinds of item:
-//                * a 64-key tile holding no global key: the query tiles within the
-//                  band, then the global query rows outside them (gathered);
-//                * a segment of kLfSeg query tiles for a key tile holding global
-//                  keys (their columns are full): fp32 partial dK, dV.
+//                * a 64-key class tile holding no global key: the query tiles of
+//                  its class within the window, then the global query rows
+//                  outside them (gathered);
+//                * a segment of kLfSeg natural query tiles for a key class tile
+//                  holding global keys (their columns are full): fp32 partial
+//                  dK, dV.
 //   lf_bwd_reduce  sums the partials in segment order and writes dQ of the
-//                global rows and dK, dV of the key tiles holding global keys.
+//                global rows and dK, dV of the key class tiles holding global keys.
 
 #include "attn_tile.hpp"
 #include "internal.hpp"
@@ -46,27 +51,19 @@ struct LfBwdArgs {
   uint16_t* dv;
   float* dbuf;       // D [B*H*n]
   float* part_q;     // [B*H*ngt*nseg][64][64] dQ of the global query rows
-  float* part_kv;    // [B*H*ngkt*nseg][2][64][64] dK, dV of key tiles holding global keys
+  float* part_kv;    // [periods*nct_g*nseg][2][64][64] dK, dV of key class tiles
+                     // holding global keys
   const int32_t* gtok;         // [ng]
   const int32_t* gidx;         // [n]
   const uint64_t* tile_gmask;  // [nt]
-  const int32_t* ktiles;       // [nt]: key tiles without global keys, then those with
-  int heads, n, nt, ng, ngt, ngkt, nseg, w1;
+  const LfTileRef* ct;         // [nct]: class tiles without global keys, then those with
+  int heads, n, nt, ng, ngt, nseg;
+  int nct, nct_plain, nct_g, ph;   // class tiles (all / without / with global keys), heads
+                                   // per head period
+  int dlo, dhi;                    // window: class index differences i - j in [dlo, dhi]
   int dq_band_items, dq_items, kv_plain_items, kv_items;
   float scale, sl2;
 };
-
-// Sets the score registers of (row = key kx, column = this lane's query p) to -inf
-// unless allowed(p, q); the S^T layout of the dQ kernel.
-template <typename Allowed>
-__device__ __forceinline__ void mask_keys(f32x16& s0, f32x16& s1, int hl, Allowed allowed) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kx = 8 * (r >> 2) + 4 * hl + (r & 3);
-    if (!allowed(kx)) s0[r] = -INFINITY;
-    if (!allowed(32 + kx)) s1[r] = -INFINITY;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dQ (and D)
@@ -74,17 +71,24 @@ __device__ __forceinline__ void mask_keys(f32x16& s0, f32x16& s1, int hl, Allowe
 
 typedef uint16_t LdsTile[kBlock * kLdsStride];
 
-// One dQ item; kBand: a 64-row query tile (v indexes B*H*nt), else a segment of a
-// global query tile (v indexes B*H*ngt*nseg).
+// One dQ item; kBand: a 64-row query class tile (v indexes periods*nct), else a
+// segment of a global query tile (v indexes B*H*ngt*nseg).
 template <bool kBand>
 __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTile* sK,
                                                LdsTile* sV) {
   constexpr bool band = kBand;
-  int bh, t = 0, gt = 0, seg = 0;
+  int bh, gt = 0, seg = 0;
+  int cls = 0, stride = 1, t = 0, nc = a.n;   // class tile of a band item
+  uint64_t vm_q = ~0ull, gm_q = 0ull;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if constexpr (kBand) {
-    bh = v / a.nt;
-    t = v - bh * a.nt;
-    if (a.tile_gmask[t] == ~0ull) return;   // all rows global: the global items own them
+    const int per = v / a.nct;
+    const LfTileRef e = a.ct[v - per * a.nct];
+    bh = per * a.ph + e.h;
+    cls = e.c; stride = e.s; t = e.t; nc = e.nc;
+    vm_q = valid_rows(t, nc);
+    gm_q = class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, t, nc, lane);
+    if (gm_q == vm_q) return;   // all rows global: the global items own them
   } else {
     const int per_bh = a.ngt * a.nseg;
     bh = v / per_bh;
@@ -92,17 +96,19 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     gt = rem / a.nseg;
     seg = rem - gt * a.nseg;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)bh * a.n * kHead;
-  // this lane's query token
-  const int p = band ? t * kBlock + 32 * wave + col : global_token(a.gtok, a.ng, gt, 32 * wave + col);
+  const int xq = 32 * wave + col;
+  // this lane's class index (band items) and query token
+  const int i = band ? min(t * kBlock + xq, nc - 1) : 0;
+  const int p = band ? cls + stride * i : global_token(a.gtok, a.ng, gt, xq);
 
-  // key tiles: band items walk [lo_u, hi_u] then the global tiles with an eligible
-  // key; global items walk the kLfSeg natural tiles of their segment
+  // key tiles: band items walk the window's class tiles [lo_u, hi_u], then the
+  // global tiles with an eligible key; global items walk the kLfSeg natural tiles
+  // of their segment
   int lo_u = 0, hi_u = -1, ntile;
   if constexpr (kBand) {
-    band_range(t, a.w1, a.nt, lo_u, hi_u);
+    band_keys(t, a.dlo, a.dhi, (nc + kBlock - 1) / kBlock, lo_u, hi_u);
     ntile = hi_u - lo_u + 1 + a.ngt;
   } else {
     lo_u = seg * kLfSeg;
@@ -112,14 +118,14 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
   const int nband = hi_u - lo_u + 1;
   auto next_tile = [&](int x) -> int {
     while (x < ntile && x >= nband &&
-           global_rows_outside(a.gtok, a.ng, x - nband, lo_u, hi_u, lane) == 0ull)
+           global_outside(a.gtok, a.ng, x - nband, cls, stride, lo_u, hi_u, lane) == 0ull)
       ++x;
     return x;
   };
   auto tile_load = [&](int x, TileRegs& kr, TileRegs& vr) {
     if (x < nband) {
-      gload_nat(kr, a.k + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
-      gload_nat(vr, a.v + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
+      gload_class(kr, a.k + bh_off, cls, stride, lo_u + x, nc, tid);
+      gload_class(vr, a.v + bh_off, cls, stride, lo_u + x, nc, tid);
     } else {
       gload_gather(kr, a.k + bh_off, a.gtok, a.ng, x - nband, tid);
       gload_gather(vr, a.v + bh_off, a.gtok, a.ng, x - nband, tid);
@@ -148,7 +154,7 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     }
   }
   const float Dq = partner_sum(dsum);   // D = rowsum(dO * O)
-  if (seg == 0 && hl == 0) a.dbuf[(size_t)bh * a.n + p] = Dq;
+  if (seg == 0 && hl == 0 && ((vm_q >> xq) & 1ull)) a.dbuf[(size_t)bh * a.n + p] = Dq;
   scale_operands(qB, a.sl2);
   const float lse2 = a.lse[(size_t)bh * a.n + p] * kLog2e;
   if (x < ntile) {
@@ -157,7 +163,6 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
   }
   wait_all_loads();
 
-  const uint64_t gm_q = band ? a.tile_gmask[t] : 0ull;
   f32x16 g0 = zero16(), g1 = zero16();   // dQ^T, d rows 0..31 and 32..63
   int cur = 0;
   while (x < ntile) {
@@ -179,18 +184,17 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     }
     if constexpr (kBand) {
       if (x < nband) {
-        const int u0 = (lo_u + x) * kBlock;
-        const int i0 = t * kBlock;
-        const int far = max(abs(i0 - (u0 + kBlock - 1)), abs(i0 + kBlock - 1 - u0));
-        if (far > a.w1) {
-          const uint64_t gm = a.tile_gmask[lo_u + x];
-          mask_keys(s0, s1, hl, [&](int kx) {
-            return abs(p - (u0 + kx)) <= a.w1 || ((gm >> kx) & 1ull);
-          });
+        const int u = lo_u + x;
+        const uint64_t vm = valid_rows(u, nc);
+        if (!tiles_in_window(t, u, a.dlo, a.dhi) || vm != ~0ull) {
+          const int j0 = u * kBlock;
+          const uint64_t ok = (bit_range(i - a.dhi - j0, i - a.dlo - j0) & vm) |
+                              class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane);
+          mask_rows(s0, s1, hl, ok);
         }
       } else {
-        const uint64_t el = global_rows_outside(a.gtok, a.ng, x - nband, lo_u, hi_u, lane);
-        if (el != ~0ull) mask_keys(s0, s1, hl, [&](int kx) { return ((el >> kx) & 1ull) != 0; });
+        const uint64_t el = global_outside(a.gtok, a.ng, x - nband, cls, stride, lo_u, hi_u, lane);
+        if (el != ~0ull) mask_rows(s0, s1, hl, el);
       }
     }
 #pragma unroll
@@ -215,7 +219,7 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
 
   const float sc = a.scale;
   if constexpr (kBand) {
-    if (!((gm_q >> (32 * wave + col)) & 1ull)) {   // rows of global tokens: global items
+    if (((vm_q & ~gm_q) >> xq) & 1ull) {   // rows of global tokens: global items
       uint16_t* op = a.dq + bh_off + (size_t)p * kHead + 4 * hl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -230,7 +234,7 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     }
   } else {
     const size_t slot = ((size_t)bh * a.ngt + gt) * a.nseg + seg;
-    float* pp = a.part_q + slot * kTile + (32 * wave + col) * kHead + 4 * hl;
+    float* pp = a.part_q + slot * kTile + xq * kHead + 4 * hl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f32x4 w0, w1;
@@ -257,40 +261,48 @@ __global__ __launch_bounds__(kThreads, 2) void lf_bwd_dq_kernel(LfBwdArgs a) {
 // dK, dV
 // ---------------------------------------------------------------------------
 
-// One dK/dV item; kPlain: a key tile without global keys (v indexes
-// B*H*(nt - ngkt)), else a segment of a key tile holding global keys.
+// One dK/dV item; kPlain: a key class tile without global keys (v indexes
+// periods*nct_plain), else a segment of a key class tile holding global keys.
 template <bool kPlain>
 __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsTile* sQ,
                                                  LdsTile* sO, float (*sL)[kBlock],
                                                  float (*sD)[kBlock]) {
-  const int nplain = a.nt - a.ngkt;   // key tiles without global keys
-  int bh, u, gki = 0, seg = 0;
+  int per, gki = 0, seg = 0;
+  LfTileRef ref;
   if constexpr (kPlain) {
-    bh = v / nplain;
-    u = a.ktiles[v - bh * nplain];
+    per = v / a.nct_plain;
+    ref = a.ct[v - per * a.nct_plain];
   } else {
-    const int per_bh = a.ngkt * a.nseg;
-    bh = v / per_bh;
-    const int rem = v - bh * per_bh;
+    const int per_p = a.nct_g * a.nseg;
+    per = v / per_p;
+    const int rem = v - per * per_p;
     gki = rem / a.nseg;
     seg = rem - gki * a.nseg;
-    u = a.ktiles[nplain + gki];
+    ref = a.ct[a.nct_plain + gki];
   }
+  const int bh = per * a.ph + ref.h;
+  const int cls = ref.c, stride = ref.s, u = ref.t, nc = ref.nc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)bh * a.n * kHead;
-  const int kx = 32 * wave + col;       // this lane's key within the tile
-  const int q_tok = u * kBlock + kx;    // ... and its token
-  const uint64_t gm_k = a.tile_gmask[u];
-  const bool key_global = (gm_k >> kx) & 1ull;
+  const int kx = 32 * wave + col;                 // this lane's key within the tile
+  const int jc = min(u * kBlock + kx, nc - 1);    // ... its class index
+  const int q_tok = cls + stride * jc;            // ... and its token
+  const bool key_valid = u * kBlock + kx < nc;
+  bool key_global = false;
+  if constexpr (!kPlain)
+    key_global = (class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane) >> kx) & 1ull;
 
-  // query tiles: plain items walk the band tiles [lo, hi], then the global tiles
-  // with an eligible row; segment items walk kLfSeg natural tiles
+  // query tiles: plain items walk the window's class tiles [lo, hi] of the key's
+  // class, then the global tiles with an eligible row; segment items walk kLfSeg
+  // natural tiles (the column of a global key is full)
   int lo, hi, ntile;
+  int qc = cls, qs = stride, qnc = nc;   // class of the query tiles walked
   if constexpr (kPlain) {
-    band_range(u, a.w1, a.nt, lo, hi);
+    band_queries(u, a.dlo, a.dhi, (nc + kBlock - 1) / kBlock, lo, hi);
     ntile = hi - lo + 1 + a.ngt;
   } else {
+    qc = 0; qs = 1; qnc = a.n;
     lo = seg * kLfSeg;
     hi = min(a.nt, lo + kLfSeg) - 1;
     ntile = hi - lo + 1;
@@ -298,10 +310,15 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   const int nband = hi - lo + 1;
   auto next_tile = [&](int x) -> int {
     while (x < ntile && x >= nband &&
-           global_rows_outside(a.gtok, a.ng, x - nband, lo, hi, lane) == 0ull)
+           global_outside(a.gtok, a.ng, x - nband, cls, stride, lo, hi, lane) == 0ull)
       ++x;
     return x;
   };
+  // Segment items test the dilated window in token coordinates: query rows whose
+  // distance to the key is a multiple of the stride (bits 0, s, 2s, ... shifted).
+  uint64_t stride_bits = 0ull;
+  if constexpr (!kPlain)
+    for (int b = 0; b < kBlock; b += stride) stride_bits |= 1ull << b;
   const uint16_t* qbase = a.q + bh_off;
   const uint16_t* dobase = a.dout + bh_off;
   const float* lbase = a.lse + (size_t)bh * a.n;
@@ -310,9 +327,9 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   auto tile_load = [&](int x, TileRegs& qr, TileRegs& dr, float& lv, float& dval) {
     int tok_row;
     if (x < nband) {
-      gload_nat(qr, qbase + (size_t)(lo + x) * kBlock * kHead, tid);
-      gload_nat(dr, dobase + (size_t)(lo + x) * kBlock * kHead, tid);
-      tok_row = (lo + x) * kBlock + (tid & 63);
+      gload_class(qr, qbase, qc, qs, lo + x, qnc, tid);
+      gload_class(dr, dobase, qc, qs, lo + x, qnc, tid);
+      tok_row = class_token(qc, qs, lo + x, qnc, tid & 63);
     } else {
       gload_gather(qr, qbase, a.gtok, a.ng, x - nband, tid);
       gload_gather(dr, dobase, a.gtok, a.ng, x - nband, tid);
@@ -382,30 +399,31 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
       p0 = mfma32(o0, vB[c], p0);
       p1 = mfma32(o1, vB[c], p1);
     }
-    // allowed (query row qx of this tile, this lane's key): in the band, or the
+    // allowed (query row of this tile, this lane's key): in the window, or the
     // query is global, or the key is global
     if (x < nband) {
-      const int tq = lo + x, p0tok = tq * kBlock;
-      const uint64_t gm_q = a.tile_gmask[tq];
-      const int far = max(abs(p0tok - (u * kBlock + kBlock - 1)), abs(p0tok + kBlock - 1 - u * kBlock));
-      if (far > a.w1 && !key_global) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qx = 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (abs(p0tok + qx - q_tok) > a.w1 && !((gm_q >> qx) & 1ull)) s0[r] = -INFINITY;
-          if (abs(p0tok + 32 + qx - q_tok) > a.w1 && !((gm_q >> (32 + qx)) & 1ull)) s1[r] = -INFINITY;
+      const int tq = lo + x, i0 = tq * kBlock;
+      if constexpr (kPlain) {
+        const uint64_t vq = valid_rows(tq, nc);
+        if (!tiles_in_window(tq, u, a.dlo, a.dhi) || vq != ~0ull) {
+          const uint64_t ok = (bit_range(jc + a.dlo - i0, jc + a.dhi - i0) & vq) |
+                              class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, tq, nc, lane);
+          mask_rows(s0, s1, hl, ok);
+        }
+      } else if (stride > 1 || !tiles_in_window(tq, u, a.dlo, a.dhi)) {
+        // natural query tile: rows p = i0 + x with p - q_tok in [dlo*s, dhi*s] and a
+        // multiple of s
+        if (!key_global) {
+          int r = (q_tok - i0) % stride;
+          if (r < 0) r += stride;
+          const uint64_t ok = (bit_range(q_tok + a.dlo * stride - i0, q_tok + a.dhi * stride - i0) &
+                               (stride_bits << r)) | a.tile_gmask[tq];
+          mask_rows(s0, s1, hl, ok);
         }
       }
     } else {
-      const uint64_t el = global_rows_outside(a.gtok, a.ng, x - nband, lo, hi, lane);
-      if (el != ~0ull) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qx = 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (!((el >> qx) & 1ull)) s0[r] = -INFINITY;
-          if (!((el >> (32 + qx)) & 1ull)) s1[r] = -INFINITY;
-        }
-      }
+      const uint64_t el = global_outside(a.gtok, a.ng, x - nband, cls, stride, lo, hi, lane);
+      if (el != ~0ull) mask_rows(s0, s1, hl, el);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -436,6 +454,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
 
   const float sc = a.scale / a.sl2;   // dK was accumulated against the scaled Q
   if constexpr (kPlain) {
+    if (!key_valid) return;
     const size_t off = bh_off + (size_t)q_tok * kHead + 4 * hl;
     uint16_t* kp = a.dk + off;
     uint16_t* vp = a.dv + off;
@@ -456,7 +475,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
       *reinterpret_cast<u32x2*>(vp + 32 + 8 * j) = v1w;
     }
   } else {
-    const size_t slot = ((size_t)bh * a.ngkt + gki) * a.nseg + seg;
+    const size_t slot = ((size_t)per * a.nct_g + gki) * a.nseg + seg;
     float* pk = a.part_kv + slot * 2 * kTile + kx * kHead + 4 * hl;
     float* pv = pk + kTile;
 #pragma unroll
@@ -491,8 +510,8 @@ __global__ __launch_bounds__(kThreads) void lf_bwd_dkdv_kernel(LfBwdArgs a) {
 }
 
 // Segment sums in segment order.  Work-groups [0, B*H*ngt): dQ of global tile gt,
-// rows scattered to their tokens; then B*H*ngkt*2: dK (kind 0) or dV (kind 1) of
-// the key tiles holding global keys.
+// rows scattered to their tokens; then periods*nct_g*2: dK (kind 0) or dV (kind 1)
+// of the key class tiles holding global keys, rows scattered to their tokens.
 __global__ __launch_bounds__(256) void lf_bwd_reduce_kernel(LfBwdArgs a, int nq_groups) {
   const int e0 = threadIdx.x * 16;   // 16 consecutive floats of the 64x64 tile
   const int row = e0 / kHead;
@@ -509,12 +528,16 @@ __global__ __launch_bounds__(256) void lf_bwd_reduce_kernel(LfBwdArgs a, int nq_
     dst = a.dq + ((size_t)bh * a.n + a.gtok[j]) * kHead + (e0 % kHead);
   } else {
     const int w = blockIdx.x - nq_groups;
-    const int kind = w & 1, idx = w >> 1;   // idx = bh * ngkt + gki
-    const int bh = idx / a.ngkt, gki = idx - bh * a.ngkt;
-    const int u = a.ktiles[a.nt - a.ngkt + gki];
+    const int kind = w & 1, idx = w >> 1;   // idx = period * nct_g + gki
+    const int per = idx / a.nct_g, gki = idx - per * a.nct_g;
+    const LfTileRef e = a.ct[a.nct_plain + gki];
+    const int ci = e.t * kBlock + row;      // class index of this row
+    if (ci >= e.nc) return;
+    const int bh = per * a.ph + e.h;
     src = a.part_kv + (size_t)idx * a.nseg * 2 * kTile + kind * kTile + e0;
     stride = 2 * kTile;
-    dst = (kind == 0 ? a.dk : a.dv) + ((size_t)bh * a.n + (size_t)u * kBlock) * kHead + e0;
+    dst = (kind == 0 ? a.dk : a.dv) + ((size_t)bh * a.n + e.c + (size_t)e.s * ci) * kHead +
+          (e0 % kHead);
   }
   float acc[16];
 #pragma unroll
@@ -538,11 +561,13 @@ struct LfBwdWs {
 LfBwdWs lf_bwd_ws_layout(const lfattn_plan* P, int batch, int heads) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t bh = (size_t)batch * heads;
+  const size_t periods = bh / (P->heads > 0 ? P->heads : 1);
   LfBwdWs w;
   w.dbuf = 0;
   w.part_q = up(bh * P->n * sizeof(float));
   w.part_kv = up(w.part_q + bh * P->ngt * P->nseg * kTile * sizeof(float));
-  w.total = up(w.part_kv + bh * P->ngkt * P->nseg * 2 * kTile * sizeof(float));
+  w.total = up(w.part_kv + periods * (P->nct - P->nct_plain) * P->nseg * 2 * kTile *
+                               sizeof(float));
   return w;
 }
 
@@ -565,16 +590,21 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const
   a.part_q = (float*)(base + w.part_q);
   a.part_kv = (float*)(base + w.part_kv);
   a.gtok = P->d_gtok; a.gidx = P->d_gidx; a.tile_gmask = P->d_tile_gmask;
-  a.ktiles = P->d_ktiles;
+  a.ct = P->d_ct;
   a.heads = heads; a.n = P->n; a.nt = P->nt; a.ng = P->ng; a.ngt = P->ngt;
-  a.ngkt = P->ngkt; a.nseg = P->nseg; a.w1 = P->w1;
+  a.nseg = P->nseg;
+  a.nct = P->nct; a.nct_plain = P->nct_plain; a.nct_g = P->nct - P->nct_plain;
+  a.ph = P->heads > 0 ? P->heads : 1;
+  a.dlo = P->causal ? 0 : -P->w1;
+  a.dhi = P->w1;
   a.scale = scale;
   a.sl2 = scale * kLog2e;
   const int bhn = batch * heads;
-  a.dq_band_items = bhn * P->nt;
+  const int periods = bhn / a.ph;
+  a.dq_band_items = periods * a.nct;
   a.dq_items = a.dq_band_items + bhn * P->ngt * P->nseg;
-  a.kv_plain_items = bhn * (P->nt - P->ngkt);
-  a.kv_items = a.kv_plain_items + bhn * P->ngkt * P->nseg;
+  a.kv_plain_items = periods * a.nct_plain;
+  a.kv_items = a.kv_plain_items + periods * a.nct_g * P->nseg;
   int st;
   {
     ProfScope prof_("lf_bwd_dq", stream);
@@ -589,7 +619,7 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const
   }
   if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv launch"))) return st;
   const int nq_groups = bhn * P->ngt;
-  const int groups = nq_groups + bhn * P->ngkt * 2;
+  const int groups = nq_groups + periods * a.nct_g * 2;
   if (groups == 0) return 0;
   {
     ProfScope prof_("lf_bwd_reduce", stream);

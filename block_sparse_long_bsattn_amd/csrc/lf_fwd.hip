@@ -1,18 +1,21 @@
 // Longformer sliding-window + symmetric global attention forward on gfx950.
 //
-// Pattern ("Longformer: The Long-Document Transformer", §3.1 "Sliding Window" and
-// "Global Attention"): token p attends to token q iff |p - q| <= w1, or p is
+// Pattern ("Longformer: The Long-Document Transformer", §3.1 "Sliding Window",
+// "Dilated Sliding Window" and "Global Attention"; the autoregressive mode of
+// §4.1): token p attends to token q iff q is in p's window (q = p + k*(d+1) with
+// k in [-w1, w1], or in [-w1, 0] when causal; d is the head's dilation), or p is
 // global, or q is global.  Scores are scaled as in §3.1 eq. (1).  §3.2 and App. A
 // describe the band as a banded matrix product that only computes a fixed number
-// of diagonals; here the band is walked in 64x64 tiles.
+// of diagonals; here each residue class of the window is walked in 64x64 tiles.
 //
 // Kernels (per call):
 //   lf_attn     one 128-thread work-group per item, two kinds of item:
-//               * a 64-row query tile: the key tiles that overlap the band, then
-//                 the tiles of global keys (rows gathered by index from K and V)
-//                 whose keys lie outside those band tiles.  Only tiles the band
-//                 cuts need an element mask; keys that are global are allowed in
-//                 every tile.  Rows of global tokens are skipped at write time.
+//               * a 64-row query tile of one residue class: the class's key tiles
+//                 that overlap the window, then the tiles of global keys (rows
+//                 gathered by index from K and V) that those tiles do not hold.
+//                 Only tiles the window cuts need an element mask; keys that are
+//                 global are allowed in every tile.  Rows of global tokens and
+//                 rows past the class's end are not written.
 //               * a segment of kLfSeg key tiles for a tile of global query rows
 //                 ("a token with global attention attends to all tokens"), query
 //                 rows gathered by index, writing a partial record.
@@ -38,7 +41,10 @@ struct LfArgs {
   const int32_t* gtok;  // [ng]
   const int32_t* gidx;  // [n]
   const uint64_t* tile_gmask;  // [nt] bit x set iff token 64u+x is global
-  int heads, n, nt, ng, ngt, nseg, w1;
+  const LfTileRef* ct;  // [nct] class tiles of one head period
+  int heads, n, nt, ng, ngt, nseg;
+  int nct, ph;          // class tiles and heads per head period
+  int dlo, dhi;         // window: class index differences i - j in [dlo, dhi]
   int band_items, total_items;
   float sl2;
 };
@@ -46,29 +52,35 @@ struct LfArgs {
 typedef uint16_t LdsTile[kBlock * kLdsStride];
 
 __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK, LdsTile* sV) {
-  const int bh = v / a.nt, t = v - bh * a.nt;
-  if (a.tile_gmask[t] == ~0ull) return;   // every row global: the global items own them
+  const int per = v / a.nct;
+  const LfTileRef e = a.ct[v - per * a.nct];
+  const int bh = per * a.ph + e.h;
+  const int cls = e.c, stride = e.s, t = e.t, nc = e.nc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
+  const uint64_t vm_q = valid_rows(t, nc);
+  const uint64_t gm_q = class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, t, nc, lane);
+  if (gm_q == vm_q) return;   // every row global: the global items own them
   const size_t bh_off = (size_t)bh * a.n * kHead;
-  const int i0 = t * kBlock;
-  const int p = i0 + 32 * wave + col;   // this lane's query token
+  const int xq = 32 * wave + col;
+  const int i = min(t * kBlock + xq, nc - 1);   // this lane's class index
+  const int p = cls + stride * i;               // ... and its token
 
   bf16x8 qB[4];
   {
     const uint16_t* qp = a.q + bh_off + (size_t)p * kHead + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
+    for (int k = 0; k < 4; ++k) qB[k] = ld16(qp + 16 * k);
   }
+  const int ntc = (nc + kBlock - 1) / kBlock;
   int lo_u, hi_u;
-  band_range(t, a.w1, a.nt, lo_u, hi_u);
+  band_keys(t, a.dlo, a.dhi, ntc, lo_u, hi_u);
   const int nband = hi_u - lo_u + 1;
   const int ntile = nband + a.ngt;
 
-  // Global tile gt contributes key j iff j < ng and the key's own tile lies
-  // outside [lo_u, hi_u] (inside, the band tile already counts it).
+  // Global tile gt contributes key j iff j < ng and no band tile holds that key.
   auto global_elig = [&](int gt) -> uint64_t {
-    return global_rows_outside(a.gtok, a.ng, gt, lo_u, hi_u, lane);
+    return global_outside(a.gtok, a.ng, gt, cls, stride, lo_u, hi_u, lane);
   };
 
   scale_operands(qB, a.sl2);
@@ -76,8 +88,8 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
   fwd_state_init(st);
   auto tile_load = [&](int x, TileRegs& kr, TileRegs& vr) {
     if (x < nband) {
-      gload_nat(kr, a.k + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
-      gload_nat(vr, a.v + bh_off + (size_t)(lo_u + x) * kBlock * kHead, tid);
+      gload_class(kr, a.k + bh_off, cls, stride, lo_u + x, nc, tid);
+      gload_class(vr, a.v + bh_off, cls, stride, lo_u + x, nc, tid);
     } else {
       gload_gather(kr, a.k + bh_off, a.gtok, a.ng, x - nband, tid);
       gload_gather(vr, a.v + bh_off, a.gtok, a.ng, x - nband, tid);
@@ -105,29 +117,17 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
     f32x16 s0, s1;
     qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
     if (x < nband) {
-      const int u0 = (lo_u + x) * kBlock;
-      // the whole tile lies in the band iff its farthest pair does
-      const int far = max(abs(i0 - (u0 + kBlock - 1)), abs(i0 + kBlock - 1 - u0));
-      if (far > a.w1) {
-        const uint64_t gm = a.tile_gmask[lo_u + x];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kx = 8 * (r >> 2) + 4 * hl + (r & 3);
-          const int q0 = u0 + kx, q1 = u0 + 32 + kx;
-          if (abs(p - q0) > a.w1 && !((gm >> kx) & 1ull)) s0[r] = -INFINITY;
-          if (abs(p - q1) > a.w1 && !((gm >> (32 + kx)) & 1ull)) s1[r] = -INFINITY;
-        }
+      const int u = lo_u + x;
+      const uint64_t vm = valid_rows(u, nc);
+      if (!tiles_in_window(t, u, a.dlo, a.dhi) || vm != ~0ull) {
+        const int j0 = u * kBlock;
+        const uint64_t ok = (bit_range(i - a.dhi - j0, i - a.dlo - j0) & vm) |
+                            class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane);
+        mask_rows(s0, s1, hl, ok);
       }
     } else {
       const uint64_t el = global_elig(x - nband);
-      if (el != ~0ull) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kx = 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (!((el >> kx) & 1ull)) s0[r] = -INFINITY;
-          if (!((el >> (32 + kx)) & 1ull)) s1[r] = -INFINITY;
-        }
-      }
+      if (el != ~0ull) mask_rows(s0, s1, hl, el);
     }
     bf16x8 pc[4];
     softmax_step(s0, s1, st, pc, seed_ref(st));
@@ -141,7 +141,7 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
   }
 
   const float l_tot = partner_sum(st.l);
-  if (a.gidx[p] < 0)
+  if (((vm_q & ~gm_q) >> xq) & 1ull)
     write_o_bf16(st, l_tot, hl, a.o + bh_off + (size_t)p * kHead,
                  a.lse != nullptr ? a.lse + (size_t)bh * a.n + p : nullptr);
 }
@@ -237,11 +237,16 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const
   const bool has_g = P->ng > 0;
   a.part = has_g ? (float*)ws : nullptr;
   a.gtok = P->d_gtok; a.gidx = P->d_gidx; a.tile_gmask = P->d_tile_gmask;
+  a.ct = P->d_ct;
   a.heads = heads; a.n = P->n; a.nt = P->nt; a.ng = P->ng; a.ngt = P->ngt;
-  a.nseg = P->nseg; a.w1 = P->w1;
+  a.nseg = P->nseg;
+  a.nct = P->nct;
+  a.ph = P->heads > 0 ? P->heads : 1;
+  a.dlo = P->causal ? 0 : -P->w1;
+  a.dhi = P->w1;
   a.sl2 = scale * kLog2e;
   const int bhn = batch * heads;
-  a.band_items = bhn * P->nt;
+  a.band_items = bhn / a.ph * P->nct;
   a.total_items = a.band_items + (has_g ? bhn * P->ngt * P->nseg : 0);
   int st;
   {

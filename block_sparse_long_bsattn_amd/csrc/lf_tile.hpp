@@ -1,8 +1,19 @@
-// Helpers shared by the Longformer forward and backward kernels: tiles whose rows
-// are global tokens are gathered by index from the [n][64] tensors.
+// Helpers shared by the Longformer forward and backward kernels.
+//
+// Windows ("Longformer: The Long-Document Transformer", §3.1 "Sliding Window" and
+// "Dilated Sliding Window", Fig. 2(c)): with dilation d the window of token p holds
+// the tokens p + k*(d+1) for k in [-w1, w1] (k in [-w1, 0] in the autoregressive
+// mode of §4.1).  Tokens of one residue class modulo s = d + 1 only see their own
+// class, so each class is a plain sliding window over its class indices
+// (token = c + s * index), walked in 64-row class tiles (LfTileRef); the window is
+// then the index difference range dlo <= i - j <= dhi.
+//
+// Tiles whose rows are global tokens are gathered by index from the [n][64]
+// tensors.
 #pragma once
 
 #include "common.hpp"
+#include "internal.hpp"
 
 namespace bsattn {
 
@@ -21,25 +32,93 @@ __device__ __forceinline__ void gload_gather(TileRegs& r, const uint16_t* base,
     r.v[u] = ldg16(base + (size_t)global_token(gtok, ng, gt, row + 16 * u) * kHead + 8 * c);
 }
 
-// Which rows of global tile gt are global tokens whose own 64-token tile lies
-// outside [lo, hi] (inside, a natural tile of that range already holds them):
-// bit x <-> row x.  Every lane of the wave must call it.
-__device__ __forceinline__ uint64_t global_rows_outside(const int32_t* gtok, int ng, int gt,
-                                                        int lo, int hi, int lane) {
+// Token of row x of class tile t; rows past the class repeat its last token.
+__device__ __forceinline__ int class_token(int c, int s, int t, int nc, int x) {
+  return c + s * min(t * kBlock + x, nc - 1);
+}
+
+// gload_nat for class tile t: row x from token c + s*(64t + x) of `base` ([n][64]).
+__device__ __forceinline__ void gload_class(TileRegs& r, const uint16_t* base, int c, int s,
+                                            int t, int nc, int tid) {
+  const int k = tid & 7, row = tid >> 3;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    r.v[u] = ldg16(base + (size_t)class_token(c, s, t, nc, row + 16 * u) * kHead + 8 * k);
+}
+
+// Bits [lo, hi] of a 64-bit word, clipped to [0, 63]; empty when hi < lo.
+__device__ __forceinline__ uint64_t bit_range(int lo, int hi) {
+  lo = max(lo, 0);
+  hi = min(hi, kBlock - 1);
+  if (hi < lo) return 0ull;
+  return (~0ull >> (kBlock - 1 - hi)) & (~0ull << lo);
+}
+
+// Rows of class tile t that hold a token (class index below nc; nc > 64t).
+__device__ __forceinline__ uint64_t valid_rows(int t, int nc) {
+  const int m = nc - t * kBlock;
+  return m >= kBlock ? ~0ull : (1ull << m) - 1;
+}
+
+// Rows of class tile t that are global tokens.  Every lane of the wave must call
+// it (a ballot, except for stride 1 where the natural tile mask is read).
+__device__ __forceinline__ uint64_t class_gbits(const int32_t* gidx, const uint64_t* tile_gmask,
+                                                int ng, int c, int s, int t, int nc, int lane) {
+  if (ng == 0) return 0ull;
+  if (s == 1) return tile_gmask[t];
+  const int i = t * kBlock + lane;
+  return __ballot(i < nc && gidx[c + s * i] >= 0);
+}
+
+// Which rows of global tile gt are global tokens that no tile of [lo, hi] in class
+// (c, s) holds (inside, such a tile already counts them): bit x <-> row x.  Every
+// lane of the wave must call it.
+__device__ __forceinline__ uint64_t global_outside(const int32_t* gtok, int ng, int gt, int c,
+                                                   int s, int lo, int hi, int lane) {
   const int j = gt * kBlock + lane;
   bool ok = false;
   if (j < ng) {
-    const int u = gtok[j] / kBlock;
+    const int rel = gtok[j] - c;
+    int u = -1;   // tile within class c, -1 for another class
+    if (s == 1)
+      u = rel / kBlock;
+    else if (rel >= 0 && rel % s == 0)
+      u = rel / s / kBlock;
     ok = u < lo || u > hi;
   }
   return __ballot(ok);
 }
 
-// Band tiles of tile t: the tiles holding a token within w1 of one of t's tokens.
-__device__ __forceinline__ void band_range(int t, int w1, int nt, int& lo, int& hi) {
-  const int i0 = t * kBlock;
-  lo = max(0, i0 - w1) / kBlock;
-  hi = min(nt - 1, (i0 + kBlock - 1 + w1) / kBlock);
+// Key tiles holding a key in the window of some row of query tile t
+// (dlo <= i - j <= dhi), among the ntc tiles of the class.
+__device__ __forceinline__ void band_keys(int t, int dlo, int dhi, int ntc, int& lo, int& hi) {
+  lo = max(0, t * kBlock - dhi) / kBlock;
+  hi = min(ntc - 1, (t * kBlock + kBlock - 1 - dlo) / kBlock);
+}
+
+// Query tiles holding a row whose window has a key of key tile u.
+__device__ __forceinline__ void band_queries(int u, int dlo, int dhi, int ntc, int& lo, int& hi) {
+  lo = max(0, u * kBlock + dlo) / kBlock;
+  hi = min(ntc - 1, (u * kBlock + kBlock - 1 + dhi) / kBlock);
+}
+
+// Whether every (row of query tile tq, row of key tile tk) pair is in the window.
+__device__ __forceinline__ bool tiles_in_window(int tq, int tk, int dlo, int dhi) {
+  const int d0 = (tq - tk) * kBlock;
+  return d0 - (kBlock - 1) >= dlo && d0 + (kBlock - 1) <= dhi;
+}
+
+// Sets score registers to -inf where `allowed` has no bit.  Register r of s0 holds
+// tile row 8*(r/4) + 4*hl + r%4, of s1 that row + 32 (keys in the S^T layout of
+// the forward and dQ kernels, queries in the S layout of the dK/dV kernel).
+__device__ __forceinline__ void mask_rows(f32x16& s0, f32x16& s1, int hl, uint64_t allowed) {
+  const uint64_t a = allowed >> (4 * hl);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int x = 8 * (r >> 2) + (r & 3);
+    if (!((a >> x) & 1ull)) s0[r] = -INFINITY;
+    if (!((a >> (32 + x)) & 1ull)) s1[r] = -INFINITY;
+  }
 }
 
 }  // namespace bsattn

@@ -181,10 +181,30 @@ typedef struct lfattn_plan lfattn_plan;
  *   global_tokens    HOST array of n_global positions, sorted, unique, in [0, n);
  *                    may be NULL when n_global == 0.
  * The plan copies the global set to the device on `stream`.  Returns OK, EINVAL,
- * ENOMEM or EHIP.
+ * ENOMEM or EHIP.  Such a plan serves any head count.
  */
 int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens,
                       int n_global, hipStream_t stream, lfattn_plan** out);
+
+/*
+ * Plan with a dilation per head and an optional autoregressive mode: [LF] §3.1
+ * "Dilated Sliding Window" (Fig. 2(c): gaps of d tokens between the attended
+ * tokens; a different dilation per head) and §4.1 with App. B (a window of
+ * earlier tokens only).  Head h's window of token p holds the tokens
+ * p + k*(dilation[h] + 1) inside [0, n), for k in [-window_one_side,
+ * window_one_side], or k in [-window_one_side, 0] when causal = 1; global tokens
+ * act as in lfattn_plan_build.
+ *   heads      >= 1 and <= 4096; calls with this plan must pass this head count
+ *              (EINVAL otherwise; the workspace queries then return 0).
+ *   dilation   HOST int32[heads], each in [0, 1023]; NULL means 0 for every head.
+ *   causal     0 or 1.  With 1, n_global must be 0 (EINVAL otherwise): a global
+ *              token would attend to later tokens.
+ * Other arguments, limits and return codes as lfattn_plan_build; EUNSUPPORTED
+ * also when window_one_side * (dilation + 1) exceeds 2^30.
+ */
+int lfattn_plan_build_dilated(int n, int window_one_side, const int32_t* global_tokens,
+                              int n_global, int heads, const int32_t* dilation, int causal,
+                              hipStream_t stream, lfattn_plan** out);
 
 /* Free a plan (synchronises the device first).  NULL is accepted. */
 int lfattn_plan_destroy(lfattn_plan* plan);

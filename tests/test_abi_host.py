@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_binding_exports():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     assert sorted(_lib.EXPORTS) == names
 
 
@@ -84,6 +84,7 @@ def test_null_handles_are_rejected():
     assert lib.bsattn_bwd_workspace(None, 1, 64) == 0
     assert lib.lfattn_fwd_workspace(None, 1, 1, 64) == 0
     assert lib.lfattn_bwd_workspace(None, 1, 1, 64) == 0
+    assert lib.lfattn_plan_build_dilated(100, 1, None, 0, 1, None, 0, None, None) == -1
     assert lib.bsattn_layout_destroy(None) == 0
     assert lib.lfattn_plan_destroy(None) == 0
     assert lib.bsattn_profile_read(-1, None, None, None, None) == -1
@@ -113,3 +114,26 @@ def test_missing_library_fails_loudly(tmp_path):
             _lib.load(str(tmp_path / "nope.so"))
     finally:
         _lib._lib = saved
+
+
+@pytest.mark.parametrize("args,code", [
+    ((512, 8, [0], 2, [0, 1], 1), -1),      # causal window with a global token
+    ((512, 8, [], 2, [0, -1], 0), -1),      # negative dilation
+    ((512, 8, [], 2, [0, 1024], 0), -1),    # dilation above the limit
+    ((512, 8, [], 0, [], 0), -1),           # no heads
+    ((512, 8, [], 4097, None, 0), -1),      # too many heads
+    ((512, 8, [], 1, [0], 2), -1),          # causal flag not 0/1
+    ((500, 8, [], 1, [0], 0), -1),          # n not a multiple of 64
+    ((512, 1 << 21, [], 1, [1023], 0), -2), # window span above 2^30
+])
+def test_dilated_plan_rejects_bad_arguments(args, code):
+    lib = _lib.load()
+    n, w1, G, heads, dil, causal = args
+    garr = (ctypes.c_int32 * max(1, len(G)))(*G)
+    darr = None if dil is None else (ctypes.c_int32 * len(dil))(*dil)
+    out = ctypes.c_void_p(7)
+    st = lib.lfattn_plan_build_dilated(n, w1, garr if G else None, len(G), heads, darr, causal,
+                                       None, ctypes.byref(out))
+    assert st == code
+    assert out.value is None
+    assert _lib.bsattn_last_error() != ""
