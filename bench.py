@@ -14,7 +14,8 @@ bf16 inputs with fp32 accumulation.  Prints ONE JSON line on stdout:
              host cores, in the same unit
   secondary  the other workloads (forward only at n = 4096 and 16384, fp32 at
              n = 512, Longformer window 256 + 64 global tokens forward, and its
-             forward + backward), each timed alone
+             forward + backward, and the causal character-LM shape with dilation
+             on two heads, forward + backward), each timed alone
 
 Progress goes to stderr.  Inputs are resident in device memory before timing.
 """
@@ -56,6 +57,10 @@ WORKLOADS = {
     "longformer_fwd_bwd_b1_h12_n4096_w256_g64": dict(kind="longformer", n=4096, heads=12,
                                                       batch=1, w1=256, G=list(range(64)),
                                                       dtype="bf16", bwd=True),
+    # character-LM shape: 8 heads, 256 earlier tokens, dilation 3 on two heads
+    "longformer_causal_fwd_bwd_b1_h8_n23040_w256_dil3x2": dict(
+        kind="longformer", n=23040, heads=8, batch=1, w1=256, G=[], dtype="bf16", bwd=True,
+        dil=[3, 3, 0, 0, 0, 0, 0, 0], causal=True),
 }
 PRIMARY = "bigbird_fwd_bwd_b4_h12_n4096"
 
@@ -155,8 +160,16 @@ class Job:
                                                     stream)))
                 self.flops += 8 * D * self.pairs
         else:
-            self.handle = B.lfattn_plan_build(n, cfg["w1"], cfg["G"])
-            self.pairs = bsz * heads * longformer_pairs(n, cfg["w1"], cfg["G"])
+            dil = cfg.get("dil")
+            causal = cfg.get("causal", False)
+            if dil is None and not causal:
+                self.handle = B.lfattn_plan_build(n, cfg["w1"], cfg["G"])
+            else:
+                self.handle = B.lfattn_plan_build_dilated(n, cfg["w1"], cfg["G"], heads, dil,
+                                                          causal)
+            self.pairs = bsz * sum(longformer_pairs(n, cfg["w1"], cfg["G"],
+                                                    dil[h] if dil else 0, causal)
+                                   for h in range(heads))
             ws = B.lfattn_fwd_workspace(self.handle, bsz, heads)
             self.wsf = torch.empty(max(16, ws), dtype=torch.uint8, device="cuda")
             B.lfattn_fwd(self.handle, self.q, self.k, self.v, self.o, self.lse, self.wsf)
@@ -193,19 +206,30 @@ class Job:
             self.B.lfattn_plan_destroy(self.handle)
 
 
-def longformer_pairs(n: int, w1: int, G) -> int:
-    """Attended (query, key) pairs of one head: |p - q| <= w1 or p or q global."""
+def longformer_pairs(n: int, w1: int, G, dil: int = 0, causal: bool = False) -> int:
+    """Attended (query, key) pairs of one head: q in p's window (q = p + k*(dil+1),
+    k in [-w1, w1], or [-w1, 0] when causal), or p or q global."""
+    s = dil + 1
+    p = np.arange(n)
+    idx = p // s                          # index of p within its residue class
+    nc = (n - p % s + s - 1) // s         # length of that class
+    win = np.minimum(w1, idx) + 1
+    if not causal:
+        win = win + np.minimum(w1, nc - 1 - idx)
+    if len(G) == 0:
+        return int(win.sum())
+    gpos = np.asarray(sorted(G), dtype=np.int64)
     g = np.zeros(n, dtype=bool)
-    g[list(G)] = True
-    gpos = np.nonzero(g)[0]
+    g[gpos] = True
+    lo = 0 if causal else -w1 * s
     total = 0
-    for p in range(n):
-        if g[p]:
+    for x in range(n):
+        if g[x]:
             total += n
             continue
-        lo, hi = max(0, p - w1), min(n - 1, p + w1)
-        outside = np.count_nonzero((gpos < lo) | (gpos > hi))
-        total += (hi - lo + 1) + outside
+        delta = x - gpos
+        inside = (delta % s == 0) & (delta >= lo) & (delta <= w1 * s)
+        total += int(win[x]) + int(np.count_nonzero(~inside))
     return total
 
 
@@ -401,7 +425,9 @@ def main() -> int:
                    **({"block": 64, "global_blocks": cfg["G"], "window_blocks": cfg["w"],
                        "random_blocks": cfg["r"], "passes": "layout+fwd+bwd" if cfg["bwd"] else "layout+fwd"}
                       if cfg["kind"] == "bigbird" else
-                      {"window_one_side": cfg["w1"], "global_tokens": len(cfg["G"]), "passes": "fwd"})},
+                      {"window_one_side": cfg["w1"], "global_tokens": len(cfg["G"]),
+                       "dilation": cfg.get("dil", 0), "causal": cfg.get("causal", False),
+                       "passes": "fwd+bwd" if cfg["bwd"] else "fwd"})},
         "pct_peak": round(100 * value / peak, 3),
         "useful_pairs": job.pairs,
         "kernels_us": {k: round(v["avg_ms"] * 1e3, 2) for k, v in kb.items()},
