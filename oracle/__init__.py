@@ -9,7 +9,8 @@ Modules
 -------
 layout      block layout: window / global / seeded random key blocks per query block
 attention   masked softmax attention forward and backward on a materialised mask
-longformer  token-level sliding window + symmetric global mask
+longformer  token-level sliding window (dilated, causal) + symmetric global mask
+etc         BigBird-ETC: added global tokens + blocked window, any sequence length
 
 Parity status: every public function is pinned by tests under ``tests/``
 (``test_oracle_*.py``) against closed forms, library routines, published
@@ -31,4 +32,5 @@ from .attention import (  # noqa: F401
     attention_bwd,
     attention_fwd_rows,
 )
-from .longformer import longformer_mask, longformer_allowed  # noqa: F401
+from .longformer import longformer_mask, longformer_allowed, in_window  # noqa: F401
+from .etc import etc_mask, etc_allowed  # noqa: F401
