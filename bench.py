@@ -14,8 +14,9 @@ bf16 inputs with fp32 accumulation.  Prints ONE JSON line on stdout:
              host cores, in the same unit
   secondary  the other workloads (forward only at n = 4096 and 16384, fp32 at
              n = 512, Longformer window 256 + 64 global tokens forward, and its
-             forward + backward, and the causal character-LM shape with dilation
-             on two heads, forward + backward), each timed alone
+             forward + backward, BigBird-etc base (256 added global tokens,
+             blocks of 84) forward + backward, and the causal character-LM shape
+             with dilation on two heads, forward + backward), each timed alone
 
 Progress goes to stderr.  Inputs are resident in device memory before timing.
 """
@@ -57,6 +58,9 @@ WORKLOADS = {
     "longformer_fwd_bwd_b1_h12_n4096_w256_g64": dict(kind="longformer", n=4096, heads=12,
                                                       batch=1, w1=256, G=list(range(64)),
                                                       dtype="bf16", bwd=True),
+    # BigBird-etc base: 256 added global tokens, blocks of 84, window of 3 blocks
+    "etc_fwd_bwd_b4_h12_g256_n4096_b84": dict(kind="etc", g=256, n=4096, b=84, w=3, heads=12,
+                                              batch=4, dtype="bf16", bwd=True),
     # character-LM shape: 8 heads, 256 earlier tokens, dilation 3 on two heads
     "longformer_causal_fwd_bwd_b1_h8_n23040_w256_dil3x2": dict(
         kind="longformer", n=23040, heads=8, batch=1, w1=256, G=[], dtype="bf16", bwd=True,
@@ -111,7 +115,8 @@ class Job:
         from block_sparse_long_bsattn_amd import inputs as I
         self.name, self.cfg, self.B = name, cfg, B
         lib = B.load()
-        bsz, heads, n = cfg["batch"], cfg["heads"], cfg["n"]
+        bsz, heads = cfg["batch"], cfg["heads"]
+        n = cfg["n"] + cfg.get("g", 0) if cfg["kind"] == "etc" else cfg["n"]
         shape = (bsz, heads, n, D)
         tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
 
@@ -162,14 +167,18 @@ class Job:
         else:
             dil = cfg.get("dil")
             causal = cfg.get("causal", False)
-            if dil is None and not causal:
+            if cfg["kind"] == "etc":
+                self.handle = B.lfattn_plan_build_etc(cfg["g"], cfg["n"], cfg["b"], cfg["w"])
+                self.pairs = bsz * heads * etc_pairs(cfg["g"], cfg["n"], cfg["b"], cfg["w"])
+            elif dil is None and not causal:
                 self.handle = B.lfattn_plan_build(n, cfg["w1"], cfg["G"])
             else:
                 self.handle = B.lfattn_plan_build_dilated(n, cfg["w1"], cfg["G"], heads, dil,
                                                           causal)
-            self.pairs = bsz * sum(longformer_pairs(n, cfg["w1"], cfg["G"],
-                                                    dil[h] if dil else 0, causal)
-                                   for h in range(heads))
+            if cfg["kind"] != "etc":
+                self.pairs = bsz * sum(longformer_pairs(n, cfg["w1"], cfg["G"],
+                                                        dil[h] if dil else 0, causal)
+                                       for h in range(heads))
             ws = B.lfattn_fwd_workspace(self.handle, bsz, heads)
             self.wsf = torch.empty(max(16, ws), dtype=torch.uint8, device="cuda")
             B.lfattn_fwd(self.handle, self.q, self.k, self.v, self.o, self.lse, self.wsf)
@@ -230,6 +239,19 @@ def longformer_pairs(n: int, w1: int, G, dil: int = 0, causal: bool = False) -> 
         delta = x - gpos
         inside = (delta % s == 0) & (delta >= lo) & (delta <= w1 * s)
         total += int(win[x]) + int(np.count_nonzero(~inside))
+    return total
+
+
+def etc_pairs(g: int, n: int, b: int, w: int) -> int:
+    """Attended pairs of one head of the ETC pattern: g full rows of g + n keys; an
+    ordinary token of block k sees the g global tokens and the blocks within
+    (w-1)/2 of k (the last block holds n - b*(nb-1) tokens)."""
+    nb = -(-n // b)
+    size = [min(b, n - b * j) for j in range(nb)]
+    half = (w - 1) // 2
+    total = g * (g + n)
+    for k in range(nb):
+        total += size[k] * (g + sum(size[max(0, k - half):min(nb, k + half + 1)]))
     return total
 
 
@@ -425,6 +447,8 @@ def main() -> int:
                    **({"block": 64, "global_blocks": cfg["G"], "window_blocks": cfg["w"],
                        "random_blocks": cfg["r"], "passes": "layout+fwd+bwd" if cfg["bwd"] else "layout+fwd"}
                       if cfg["kind"] == "bigbird" else
+                      {"added_global_tokens": cfg["g"], "block": cfg["b"], "window_blocks": cfg["w"],
+                       "passes": "fwd+bwd" if cfg["bwd"] else "fwd"} if cfg["kind"] == "etc" else
                       {"window_one_side": cfg["w1"], "global_tokens": len(cfg["G"]),
                        "dilation": cfg.get("dil", 0), "causal": cfg.get("causal", False),
                        "passes": "fwd+bwd" if cfg["bwd"] else "fwd"})},

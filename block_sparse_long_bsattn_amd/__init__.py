@@ -28,5 +28,6 @@ from ._lib import (  # noqa: F401
     lfattn_fwd_workspace,
     lfattn_plan_build,
     lfattn_plan_build_dilated,
+    lfattn_plan_build_etc,
     lfattn_plan_destroy,
 )

@@ -28,7 +28,7 @@ EXPORTS = (
     "bsattn_layout_build", "bsattn_layout_rebuild", "bsattn_layout_info",
     "bsattn_layout_to_host", "bsattn_layout_destroy", "bsattn_fwd_workspace",
     "bsattn_bwd_workspace", "bsattn_fwd", "bsattn_bwd", "lfattn_plan_build",
-    "lfattn_plan_build_dilated", "lfattn_plan_destroy", "lfattn_fwd_workspace", "lfattn_fwd", "lfattn_bwd_workspace",
+    "lfattn_plan_build_dilated", "lfattn_plan_build_etc", "lfattn_plan_destroy", "lfattn_fwd_workspace", "lfattn_fwd", "lfattn_bwd_workspace",
     "lfattn_bwd", "bsattn_status_str",
     "bsattn_last_error", "bsattn_version", "bsattn_profile_enable", "bsattn_profile_read",
 )
@@ -72,6 +72,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lfattn_plan_build_dilated": (c_int, [c_int, c_int, POINTER(c_int32), c_int, c_int,
                                               POINTER(c_int32), c_int, c_void_p,
                                               POINTER(c_void_p)]),
+        "lfattn_plan_build_etc": (c_int, [c_int, c_int, c_int, c_int, c_void_p,
+                                          POINTER(c_void_p)]),
         "lfattn_plan_destroy": (c_int, [c_void_p]),
         "lfattn_fwd_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int]),
         "lfattn_fwd": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
@@ -267,6 +269,16 @@ def lfattn_plan_build_dilated(n, window_one_side, global_tokens, heads, dilation
                                             dil, 1 if causal else 0, _stream(stream),
                                             ctypes.byref(out)), "lfattn_plan_build_dilated")
     _plan_n[out.value] = n
+    return out.value
+
+
+def lfattn_plan_build_etc(g, n, b, w, stream=None) -> int:
+    """BigBird-ETC plan: g added global tokens, then n ordinary tokens in blocks of b
+    with a window of w blocks; tensors hold g + n tokens."""
+    out = c_void_p()
+    _check(load().lfattn_plan_build_etc(g, n, b, w, _stream(stream), ctypes.byref(out)),
+           "lfattn_plan_build_etc")
+    _plan_n[out.value] = g + n
     return out.value
 
 

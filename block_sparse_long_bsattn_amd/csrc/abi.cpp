@@ -385,13 +385,18 @@ void build_class_tiles(lfattn_plan* P) {
   P->nct = (int)P->ct.size();
 }
 
+// Blocked window of the ETC construction (block size wb > 0; 0: sliding window).
+struct BlockedWindow {
+  int wb = 0, woff = 0, whalf = 0;
+};
+
 int lf_plan_build(int n, int window_one_side, const int32_t* global_tokens, int n_global,
                   int heads, const int32_t* dilation, int causal, hipStream_t stream,
-                  lfattn_plan** out) {
+                  lfattn_plan** out, BlockedWindow bw = BlockedWindow()) {
   clear_error();
   if (out == nullptr) return set_error(BSATTN_EINVAL, "lf_plan_build: out is null");
   *out = nullptr;
-  if (n <= 0 || n % kBlock != 0) return set_error(BSATTN_EINVAL, "lf_plan_build: n must be a positive multiple of 64");
+  if (n <= 0) return set_error(BSATTN_EINVAL, "lf_plan_build: n must be positive");
   if (n > kMaxLfTokens) return set_error(BSATTN_EUNSUPPORTED, "lf_plan_build: n above 262144");
   if (window_one_side < 0) return set_error(BSATTN_EINVAL, "lf_plan_build: window must be >= 0");
   if (n_global < 0 || n_global > n) return set_error(BSATTN_EINVAL, "lf_plan_build: n_global out of range");
@@ -417,11 +422,14 @@ int lf_plan_build(int n, int window_one_side, const int32_t* global_tokens, int 
   P->n = n;
   P->w1 = window_one_side;
   P->ng = n_global;
-  P->nt = n / kBlock;
+  P->nt = (n + kBlock - 1) / kBlock;
   P->ngt = (n_global + kBlock - 1) / kBlock;
   P->nseg = (P->nt + kLfSeg - 1) / kLfSeg;
   P->heads = heads;
   P->causal = causal;
+  P->wb = bw.wb;
+  P->woff = bw.woff;
+  P->whalf = bw.whalf;
   if (heads == 0)
     P->dil.assign(1, 0);
   else if (dilation == nullptr)
@@ -475,6 +483,23 @@ extern "C" {
 int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens, int n_global,
                       hipStream_t stream, lfattn_plan** out) {
   return lf_plan_build(n, window_one_side, global_tokens, n_global, 0, nullptr, 0, stream, out);
+}
+
+int lfattn_plan_build_etc(int g, int n, int b, int w, hipStream_t stream, lfattn_plan** out) {
+  clear_error();
+  if (out == nullptr) return set_error(BSATTN_EINVAL, "lf_plan_build_etc: out is null");
+  *out = nullptr;
+  if (g < 0 || n < 1 || b < 1) return set_error(BSATTN_EINVAL, "lf_plan_build_etc: need g >= 0, n >= 1, b >= 1");
+  if (w < 1 || w % 2 == 0) return set_error(BSATTN_EINVAL, "lf_plan_build_etc: w must be odd and >= 1");
+  if ((int64_t)g + n > kMaxLfTokens) return set_error(BSATTN_EUNSUPPORTED, "lf_plan_build_etc: g + n above 262144");
+  const int nb = (n + b - 1) / b;
+  BlockedWindow bw;
+  bw.wb = b;
+  bw.woff = g;
+  bw.whalf = std::min((w - 1) / 2, nb);   // a wider window holds the same blocks
+  std::vector<int32_t> gt(g);
+  for (int x = 0; x < g; ++x) gt[x] = x;
+  return lf_plan_build(g + n, 0, gt.data(), g, 0, nullptr, 0, stream, out, bw);
 }
 
 int lfattn_plan_build_dilated(int n, int window_one_side, const int32_t* global_tokens,

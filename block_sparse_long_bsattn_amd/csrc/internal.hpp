@@ -46,9 +46,12 @@ struct LfTileRef {
 };
 
 struct lfattn_plan {
-  int n = 0, w1 = 0, ng = 0, nt = 0, ngt = 0;  // tokens, window per side, globals, tiles
+  int n = 0, w1 = 0, ng = 0, nt = 0, ngt = 0;  // tokens, window per side, globals,
+                                               // 64-token tiles (the last may be partial)
   int heads = 0;                 // 0: any head count, one pattern; else the plan's heads
   int causal = 0;                // window of earlier tokens only
+  int wb = 0, woff = 0, whalf = 0;   // blocked window: block size (0: sliding window),
+                                     // first ordinary token, (w - 1) / 2
   int device = 0;
   int nseg = 1;                  // kLfSeg-tile segments of a full row or column
   int nct = 0;                   // class tiles per head period (all heads, or one)

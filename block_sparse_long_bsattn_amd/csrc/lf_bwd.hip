@@ -60,7 +60,7 @@ struct LfBwdArgs {
   int heads, n, nt, ng, ngt, nseg;
   int nct, nct_plain, nct_g, ph;   // class tiles (all / without / with global keys), heads
                                    // per head period
-  int dlo, dhi;                    // window: class index differences i - j in [dlo, dhi]
+  LfWindow win;                    // key range of each row, in class indices
   int dq_band_items, dq_items, kv_plain_items, kv_items;
   float scale, sl2;
 };
@@ -107,8 +107,10 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
   // global tiles with an eligible key; global items walk the kLfSeg natural tiles
   // of their segment
   int lo_u = 0, hi_u = -1, ntile;
+  int klo = 0, khi = -1;   // this row's window, in class indices (band items)
   if constexpr (kBand) {
-    band_keys(t, a.dlo, a.dhi, (nc + kBlock - 1) / kBlock, lo_u, hi_u);
+    band_keys(a.win, t, nc, (nc + kBlock - 1) / kBlock, lo_u, hi_u);
+    a.win.keys(i, klo, khi);
     ntile = hi_u - lo_u + 1 + a.ngt;
   } else {
     lo_u = seg * kLfSeg;
@@ -186,9 +188,9 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
       if (x < nband) {
         const int u = lo_u + x;
         const uint64_t vm = valid_rows(u, nc);
-        if (!tiles_in_window(t, u, a.dlo, a.dhi) || vm != ~0ull) {
+        if (!tiles_in_window(a.win, t, u) || vm != ~0ull) {
           const int j0 = u * kBlock;
-          const uint64_t ok = (bit_range(i - a.dhi - j0, i - a.dlo - j0) & vm) |
+          const uint64_t ok = (bit_range(klo - j0, khi - j0) & vm) |
                               class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane);
           mask_rows(s0, s1, hl, ok);
         }
@@ -196,6 +198,9 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
         const uint64_t el = global_outside(a.gtok, a.ng, x - nband, cls, stride, lo_u, hi_u, lane);
         if (el != ~0ull) mask_rows(s0, s1, hl, el);
       }
+    } else if (lo_u + x == a.nt - 1) {   // keys past the end of the sequence
+      const uint64_t vm = valid_rows(a.nt - 1, a.n);
+      if (vm != ~0ull) mask_rows(s0, s1, hl, vm);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -289,6 +294,8 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   const int jc = min(u * kBlock + kx, nc - 1);    // ... its class index
   const int q_tok = cls + stride * jc;            // ... and its token
   const bool key_valid = u * kBlock + kx < nc;
+  int rlo, rhi;   // rows whose window holds this lane's key, in class indices
+  a.win.rows(jc, rlo, rhi);
   bool key_global = false;
   if constexpr (!kPlain)
     key_global = (class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane) >> kx) & 1ull;
@@ -299,7 +306,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   int lo, hi, ntile;
   int qc = cls, qs = stride, qnc = nc;   // class of the query tiles walked
   if constexpr (kPlain) {
-    band_queries(u, a.dlo, a.dhi, (nc + kBlock - 1) / kBlock, lo, hi);
+    band_queries(a.win, u, nc, (nc + kBlock - 1) / kBlock, lo, hi);
     ntile = hi - lo + 1 + a.ngt;
   } else {
     qc = 0; qs = 1; qnc = a.n;
@@ -405,19 +412,23 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
       const int tq = lo + x, i0 = tq * kBlock;
       if constexpr (kPlain) {
         const uint64_t vq = valid_rows(tq, nc);
-        if (!tiles_in_window(tq, u, a.dlo, a.dhi) || vq != ~0ull) {
-          const uint64_t ok = (bit_range(jc + a.dlo - i0, jc + a.dhi - i0) & vq) |
+        if (!tiles_in_window(a.win, tq, u) || vq != ~0ull) {
+          const uint64_t ok = (bit_range(rlo - i0, rhi - i0) & vq) |
                               class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, tq, nc, lane);
           mask_rows(s0, s1, hl, ok);
         }
-      } else if (stride > 1 || !tiles_in_window(tq, u, a.dlo, a.dhi)) {
-        // natural query tile: rows p = i0 + x with p - q_tok in [dlo*s, dhi*s] and a
-        // multiple of s
-        if (!key_global) {
+      } else {
+        // natural query tile: the rows p = i0 + x whose window holds the key (tokens
+        // cls + s*rlo .. cls + s*rhi at a multiple of s from it) or that are global;
+        // every row for a global key; only rows before the end of the sequence
+        const uint64_t vq = valid_rows(tq, a.n);
+        if (key_global) {
+          if (vq != ~0ull) mask_rows(s0, s1, hl, vq);
+        } else if (stride > 1 || vq != ~0ull || !tiles_in_window(a.win, tq, u)) {
           int r = (q_tok - i0) % stride;
           if (r < 0) r += stride;
-          const uint64_t ok = (bit_range(q_tok + a.dlo * stride - i0, q_tok + a.dhi * stride - i0) &
-                               (stride_bits << r)) | a.tile_gmask[tq];
+          const uint64_t ok = ((bit_range(cls + stride * rlo - i0, cls + stride * rhi - i0) &
+                                (stride_bits << r)) | a.tile_gmask[tq]) & vq;
           mask_rows(s0, s1, hl, ok);
         }
       }
@@ -595,8 +606,7 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const
   a.nseg = P->nseg;
   a.nct = P->nct; a.nct_plain = P->nct_plain; a.nct_g = P->nct - P->nct_plain;
   a.ph = P->heads > 0 ? P->heads : 1;
-  a.dlo = P->causal ? 0 : -P->w1;
-  a.dhi = P->w1;
+  a.win = lf_window(P);
   a.scale = scale;
   a.sl2 = scale * kLog2e;
   const int bhn = batch * heads;

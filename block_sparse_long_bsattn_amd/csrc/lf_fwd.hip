@@ -44,7 +44,7 @@ struct LfArgs {
   const LfTileRef* ct;  // [nct] class tiles of one head period
   int heads, n, nt, ng, ngt, nseg;
   int nct, ph;          // class tiles and heads per head period
-  int dlo, dhi;         // window: class index differences i - j in [dlo, dhi]
+  LfWindow win;         // key range of each row, in class indices
   int band_items, total_items;
   float sl2;
 };
@@ -74,7 +74,9 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
   }
   const int ntc = (nc + kBlock - 1) / kBlock;
   int lo_u, hi_u;
-  band_keys(t, a.dlo, a.dhi, ntc, lo_u, hi_u);
+  band_keys(a.win, t, nc, ntc, lo_u, hi_u);
+  int klo, khi;   // this row's window, in class indices
+  a.win.keys(i, klo, khi);
   const int nband = hi_u - lo_u + 1;
   const int ntile = nband + a.ngt;
 
@@ -119,9 +121,9 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
     if (x < nband) {
       const int u = lo_u + x;
       const uint64_t vm = valid_rows(u, nc);
-      if (!tiles_in_window(t, u, a.dlo, a.dhi) || vm != ~0ull) {
+      if (!tiles_in_window(a.win, t, u) || vm != ~0ull) {
         const int j0 = u * kBlock;
-        const uint64_t ok = (bit_range(i - a.dhi - j0, i - a.dlo - j0) & vm) |
+        const uint64_t ok = (bit_range(klo - j0, khi - j0) & vm) |
                             class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane);
         mask_rows(s0, s1, hl, ok);
       }
@@ -169,8 +171,8 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
   FwdState st;
   fwd_state_init(st);
   TileRegs kr, vr;
-  gload_nat(kr, a.k + bh_off + (size_t)u_begin * kBlock * kHead, tid);
-  gload_nat(vr, a.v + bh_off + (size_t)u_begin * kBlock * kHead, tid);
+  gload_class(kr, a.k + bh_off, 0, 1, u_begin, a.n, tid);
+  gload_class(vr, a.v + bh_off, 0, 1, u_begin, a.n, tid);
   lds_store_nat(sK[0], kr, tid);
   lds_store_nat(sV[0], vr, tid);
   for (int u = u_begin; u < u_end; ++u) {
@@ -178,11 +180,15 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
     __syncthreads();
     const bool more = u + 1 < u_end;
     if (more) {
-      gload_nat(kr, a.k + bh_off + (size_t)(u + 1) * kBlock * kHead, tid);
-      gload_nat(vr, a.v + bh_off + (size_t)(u + 1) * kBlock * kHead, tid);
+      gload_class(kr, a.k + bh_off, 0, 1, u + 1, a.n, tid);
+      gload_class(vr, a.v + bh_off, 0, 1, u + 1, a.n, tid);
     }
     f32x16 s0, s1;
     qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
+    if (u == a.nt - 1) {   // keys past the end of a sequence that ends inside a tile
+      const uint64_t vm = valid_rows(u, a.n);
+      if (vm != ~0ull) mask_rows(s0, s1, hl, vm);
+    }
     bf16x8 pc[4];
     softmax_step(s0, s1, st, pc, seed_ref(st));
     pv_tile(sV[cur], pc, lane, st);
@@ -242,8 +248,7 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const
   a.nseg = P->nseg;
   a.nct = P->nct;
   a.ph = P->heads > 0 ? P->heads : 1;
-  a.dlo = P->causal ? 0 : -P->w1;
-  a.dhi = P->w1;
+  a.win = lf_window(P);
   a.sl2 = scale * kLog2e;
   const int bhn = batch * heads;
   a.band_items = bhn / a.ph * P->nct;

@@ -6,7 +6,10 @@
 // mode of §4.1).  Tokens of one residue class modulo s = d + 1 only see their own
 // class, so each class is a plain sliding window over its class indices
 // (token = c + s * index), walked in 64-row class tiles (LfTileRef); the window is
-// then the index difference range dlo <= i - j <= dhi.
+// then the index difference range dlo <= i - j <= dhi.  The blocked window of the
+// BigBird-ETC construction ("Big Bird", §2, App. E) is the other kind of LfWindow.
+// Sequences need not fill their last 64-token tile: rows past the end are clamped
+// on load and masked or skipped.
 //
 // Tiles whose rows are global tokens are gathered by index from the [n][64]
 // tensors.
@@ -89,23 +92,76 @@ __device__ __forceinline__ uint64_t global_outside(const int32_t* gtok, int ng, 
   return __ballot(ok);
 }
 
-// Key tiles holding a key in the window of some row of query tile t
-// (dlo <= i - j <= dhi), among the ntc tiles of the class.
-__device__ __forceinline__ void band_keys(int t, int dlo, int dhi, int ntc, int& lo, int& hi) {
-  lo = max(0, t * kBlock - dhi) / kBlock;
-  hi = min(ntc - 1, (t * kBlock + kBlock - 1 - dlo) / kBlock);
+// The window as a contiguous range per row, in class indices: the keys of row i and
+// the rows whose window holds key j.  Both ends are non-decreasing in i (in j), so
+// a tile's range runs from its first row's start to its last row's end.
+//   relative (b == 0): i - j in [dlo, dhi] (sliding, dilated within a class, causal)
+//   blocked  (b > 0): tokens from off on form blocks of b; a token of block k sees
+//                     the tokens of blocks k - half .. k + half (the blocked window of
+//                     "Big Bird", §2 and App. D, over the ordinary tokens of the ETC
+//                     construction; tokens below off are global)
+struct LfWindow {
+  int dlo, dhi;
+  int b, off, half;
+  __device__ __forceinline__ void keys(int i, int& lo, int& hi) const {
+    if (b == 0) {
+      lo = i - dhi;
+      hi = i - dlo;
+    } else {
+      const int k = (max(i, off) - off) / b;
+      lo = off + b * (k - half);
+      hi = off + b * (k + half + 1) - 1;
+    }
+  }
+  __device__ __forceinline__ void rows(int j, int& lo, int& hi) const {
+    if (b == 0) {
+      lo = j + dlo;
+      hi = j + dhi;
+    } else {
+      keys(j, lo, hi);   // the blocked window is symmetric
+    }
+  }
+};
+
+// The plan's window: relative (sliding, dilated, causal) or blocked (ETC).
+inline LfWindow lf_window(const lfattn_plan* P) {
+  LfWindow w;
+  w.dlo = P->causal ? 0 : -P->w1;
+  w.dhi = P->w1;
+  w.b = P->wb;
+  w.off = P->woff;
+  w.half = P->whalf;
+  return w;
+}
+
+// Key tiles holding a key in the window of some row of query tile t, among the
+// ntc tiles of a class of nc indices.
+__device__ __forceinline__ void band_keys(const LfWindow& w, int t, int nc, int ntc, int& lo,
+                                          int& hi) {
+  int a0, a1, b0, b1;
+  w.keys(t * kBlock, a0, a1);
+  w.keys(min(t * kBlock + kBlock - 1, nc - 1), b0, b1);
+  lo = max(0, a0) / kBlock;
+  hi = min(ntc - 1, b1 / kBlock);
 }
 
 // Query tiles holding a row whose window has a key of key tile u.
-__device__ __forceinline__ void band_queries(int u, int dlo, int dhi, int ntc, int& lo, int& hi) {
-  lo = max(0, u * kBlock + dlo) / kBlock;
-  hi = min(ntc - 1, (u * kBlock + kBlock - 1 + dhi) / kBlock);
+__device__ __forceinline__ void band_queries(const LfWindow& w, int u, int nc, int ntc, int& lo,
+                                             int& hi) {
+  int a0, a1, b0, b1;
+  w.rows(u * kBlock, a0, a1);
+  w.rows(min(u * kBlock + kBlock - 1, nc - 1), b0, b1);
+  lo = max(0, a0) / kBlock;
+  hi = min(ntc - 1, b1 / kBlock);
 }
 
 // Whether every (row of query tile tq, row of key tile tk) pair is in the window.
-__device__ __forceinline__ bool tiles_in_window(int tq, int tk, int dlo, int dhi) {
-  const int d0 = (tq - tk) * kBlock;
-  return d0 - (kBlock - 1) >= dlo && d0 + (kBlock - 1) <= dhi;
+__device__ __forceinline__ bool tiles_in_window(const LfWindow& w, int tq, int tk) {
+  // the first row's keys end earliest, the last row's keys start latest
+  int a0, a1, b0, b1;
+  w.keys(tq * kBlock, a0, a1);
+  w.keys(tq * kBlock + kBlock - 1, b0, b1);
+  return b0 <= tk * kBlock && a1 >= tk * kBlock + kBlock - 1;
 }
 
 // Sets score registers to -inf where `allowed` has no bit.  Register r of s0 holds

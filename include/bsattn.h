@@ -176,7 +176,8 @@ typedef struct lfattn_plan lfattn_plan;
 /*
  * Plan for [LF] §3.1: token p attends to token q iff |p - q| <= window_one_side,
  * or p is global, or q is global (window clipped at the sequence ends).
- *   n                sequence length, positive multiple of 64, <= 262144.
+ *   n                sequence length, 1 .. 262144 (any length: a last partial
+ *                    64-token tile is masked inside the kernels).
  *   window_one_side  keys per side, >= 0 (the token itself is always included).
  *   global_tokens    HOST array of n_global positions, sorted, unique, in [0, n);
  *                    may be NULL when n_global == 0.
@@ -185,6 +186,24 @@ typedef struct lfattn_plan lfattn_plan;
  */
 int lfattn_plan_build(int n, int window_one_side, const int32_t* global_tokens,
                       int n_global, hipStream_t stream, lfattn_plan** out);
+
+/*
+ * Plan for the BigBird-ETC construction ([BB] §2 "global tokens", App. E: the
+ * BigBird-etc configurations, block length 84 or 169, g = 230 ... 430 added
+ * global tokens, a window of 3 blocks, no random blocks): a sequence of g + n
+ * tokens whose first g are added global tokens (they attend to every token and
+ * every token attends to them), followed by n ordinary tokens in ceil(n / b)
+ * blocks of b tokens (the last block shorter when b does not divide n; nothing is
+ * padded).  An ordinary token of block k attends to the ordinary tokens of blocks
+ * k - (w-1)/2 ... k + (w-1)/2, clipped at the ends, and to the global tokens.
+ *   g   >= 0;  n >= 1;  g + n <= 262144.
+ *   b   block length, >= 1.
+ *   w   window in blocks, odd, >= 1.
+ * Tensors for lfattn_fwd / lfattn_bwd are then [batch, heads, g + n, d]; the plan
+ * serves any head count.  Returns OK, EINVAL (bad argument), EUNSUPPORTED
+ * (too long), ENOMEM or EHIP.
+ */
+int lfattn_plan_build_etc(int g, int n, int b, int w, hipStream_t stream, lfattn_plan** out);
 
 /*
  * Plan with a dilation per head and an optional autoregressive mode: [LF] §3.1

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_binding_exports():
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     assert sorted(_lib.EXPORTS) == names
 
 
@@ -91,7 +91,7 @@ def test_null_handles_are_rejected():
 
 
 @pytest.mark.parametrize("args,code", [
-    ((100, 16, [0], 1), -1),       # n not a multiple of 64
+    ((0, 16, [], 0), -1),          # empty sequence
     ((512, -1, [0], 1), -1),       # negative window
     ((512, 16, [5, 1], 2), -1),    # unsorted
     ((512, 16, [512], 1), -1),     # out of range
@@ -123,7 +123,7 @@ def test_missing_library_fails_loudly(tmp_path):
     ((512, 8, [], 0, [], 0), -1),           # no heads
     ((512, 8, [], 4097, None, 0), -1),      # too many heads
     ((512, 8, [], 1, [0], 2), -1),          # causal flag not 0/1
-    ((500, 8, [], 1, [0], 0), -1),          # n not a multiple of 64
+    ((0, 8, [], 1, [0], 0), -1),            # empty sequence
     ((512, 1 << 21, [], 1, [1023], 0), -2), # window span above 2^30
 ])
 def test_dilated_plan_rejects_bad_arguments(args, code):
@@ -135,5 +135,21 @@ def test_dilated_plan_rejects_bad_arguments(args, code):
     st = lib.lfattn_plan_build_dilated(n, w1, garr if G else None, len(G), heads, darr, causal,
                                        None, ctypes.byref(out))
     assert st == code
+    assert out.value is None
+    assert _lib.bsattn_last_error() != ""
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 100, 8, 3), -1),       # negative g
+    ((4, 0, 8, 3), -1),          # no ordinary tokens
+    ((4, 100, 0, 3), -1),        # empty blocks
+    ((4, 100, 8, 2), -1),        # even window
+    ((4, 100, 8, -1), -1),       # negative window
+    ((200000, 62145, 84, 3), -2),  # g + n above the limit
+])
+def test_etc_plan_rejects_bad_arguments(args, code):
+    lib = _lib.load()
+    out = ctypes.c_void_p(7)
+    assert lib.lfattn_plan_build_etc(*args, None, ctypes.byref(out)) == code
     assert out.value is None
     assert _lib.bsattn_last_error() != ""

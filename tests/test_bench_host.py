@@ -26,3 +26,13 @@ def test_workloads_have_the_documented_shapes():
     assert (w["n"], w["heads"], w["w1"], w["causal"]) == (23040, 8, 256, True)
     assert sorted(w["dil"]) == [0] * 6 + [3, 3]
     assert bench.WORKLOADS[bench.PRIMARY]["n"] == 4096
+
+
+@pytest.mark.parametrize("g,n,b,w", [(256, 4096, 84, 3), (430, 4096, 169, 3), (5, 100, 13, 5),
+                                     (0, 64, 64, 1)])
+def test_etc_pair_count_matches_oracle_mask(g, n, b, w):
+    from oracle import etc as E
+    m = E.etc_mask(g, n, b, w)
+    N = g + n
+    count = sum(int(m(0, p0, min(N, p0 + 1024)).sum()) for p0 in range(0, N, 1024))
+    assert bench.etc_pairs(g, n, b, w) == count
