@@ -32,5 +32,6 @@ from .attention import (  # noqa: F401
     attention_bwd,
     attention_fwd_rows,
 )
-from .longformer import longformer_mask, longformer_allowed, in_window  # noqa: F401
+from .longformer import (  # noqa: F401
+    longformer_mask, longformer_allowed, in_window, longformer_gproj_fwd, longformer_gproj_bwd)
 from .etc import etc_mask, etc_allowed  # noqa: F401

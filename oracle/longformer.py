@@ -76,3 +76,47 @@ def longformer_mask(n: int, w1: int, global_tokens, dilation=0, causal: bool = F
         return win | gt[p0:p1, None] | gt[None, :]
 
     return rows
+
+
+# --- separate global projections ---------------------------------------------------
+#
+# Same page, §3.1 "Linear Projections for Global Attention": one set of projections
+# (Q_s, K_s, V_s) scores the sliding-window attention and another (Q_g, K_g, V_g) the
+# global attention, the second set starting equal to the first.  Reading: the
+# "global attention" is the attention of a global token, whose row covers every
+# token; it uses Q_g for that token and K_g, V_g for all keys.  Every other row (its
+# window and the global keys) uses Q_s, K_s, V_s.  Each row therefore belongs to one
+# of two independent masked attentions, and O, lse and the gradients are those of
+# the two problems with each row taken from its own.
+
+def _rows_split(n: int, global_tokens):
+    g = np.zeros(n, dtype=bool)
+    g[np.asarray(list(global_tokens), dtype=np.int64)] = True
+    return g
+
+
+def longformer_gproj_fwd(q, k, v, qg, kg, vg, n: int, w1: int, global_tokens, scale: float):
+    """O and lse [B,H,n] with separate global projections (fp64)."""
+    from . import attention as A
+    g = _rows_split(n, global_tokens)
+    o_s, l_s = A.attention_fwd(q, k, v, longformer_mask(n, w1, global_tokens), scale)
+    full = np.ones((n, n), dtype=bool)
+    o_g, l_g = A.attention_fwd(qg, kg, vg, full, scale)
+    o = np.where(g[None, None, :, None], o_g, o_s)
+    lse = np.where(g[None, None, :], l_g, l_s)
+    return o, lse
+
+
+def longformer_gproj_bwd(q, k, v, qg, kg, vg, dout, n: int, w1: int, global_tokens,
+                         scale: float):
+    """(dQ, dK, dV, dQ_g, dK_g, dV_g) for the loss <dout, O> of longformer_gproj_fwd:
+    each problem sees the output gradient of its own rows only."""
+    from . import attention as A
+    g = _rows_split(n, global_tokens)
+    dout = np.asarray(dout, dtype=np.float64)
+    d_s = np.where(g[None, None, :, None], 0.0, dout)
+    d_g = np.where(g[None, None, :, None], dout, 0.0)
+    dq, dk, dv = A.attention_bwd(q, k, v, d_s, longformer_mask(n, w1, global_tokens), scale)
+    full = np.ones((n, n), dtype=bool)
+    dqg, dkg, dvg = A.attention_bwd(qg, kg, vg, d_g, full, scale)
+    return dq, dk, dv, dqg, dkg, dvg

@@ -206,3 +206,66 @@ def test_plain_reading_unchanged_at_zero_dilation():
     for p in range(n):
         for t in range(n):
             assert m[p, t] == (abs(p - t) <= w1 or p in G or t in G)
+
+
+# --- separate global projections (§3.1) --------------------------------------------
+
+def gproj_torch(q, k, v, qg, kg, vg, n, w1, G, scale):
+    """Independent torch formulation: two score matrices, rows chosen by a mask."""
+    t = lambda x: torch.tensor(np.ascontiguousarray(x), requires_grad=True)
+    tq, tk, tv, tqg, tkg, tvg = (t(x) for x in (q, k, v, qg, kg, vg))
+    idx = torch.arange(n)
+    win = (idx[:, None] - idx[None, :]).abs() <= w1
+    gl = torch.zeros(n, dtype=torch.bool)
+    gl[list(G)] = True
+    allowed = win | gl[:, None] | gl[None, :]
+    s_s = (tq @ tk.transpose(-1, -2)) * scale
+    s_s = s_s.masked_fill(~allowed, float("-inf"))
+    o_s = torch.softmax(s_s, dim=-1) @ tv
+    o_g = torch.softmax((tqg @ tkg.transpose(-1, -2)) * scale, dim=-1) @ tvg
+    o = torch.where(gl[None, None, :, None], o_g, o_s)
+    return o, (tq, tk, tv, tqg, tkg, tvg)
+
+
+def test_gproj_equal_projections_reduce_to_one_set():
+    """The global projections start equal to the window ones (§3.1): then the output
+    is the single-projection Longformer attention."""
+    n, H, dh, w1, G = 96, 2, 8, 5, [0, 40, 95]
+    q, k, v = rnd(92, 1, H, n, dh), rnd(93, 1, H, n, dh), rnd(94, 1, H, n, dh)
+    o, lse = LF.longformer_gproj_fwd(q, k, v, q, k, v, n, w1, G, 0.3)
+    o1, l1 = A.attention_fwd(q, k, v, LF.longformer_mask(n, w1, G), 0.3)
+    np.testing.assert_allclose(o, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, l1, rtol=0, atol=1e-13)
+
+
+def test_gproj_forward_and_backward_match_torch_autograd():
+    n, H, dh, w1, G = 80, 2, 8, 4, [3, 17, 79]
+    xs = [rnd(95 + i, 1, H, n, dh) for i in range(7)]
+    q, k, v, qg, kg, vg, do = xs
+    o, _ = LF.longformer_gproj_fwd(q, k, v, qg, kg, vg, n, w1, G, 0.4)
+    grads = LF.longformer_gproj_bwd(q, k, v, qg, kg, vg, do, n, w1, G, 0.4)
+    to, leaves = gproj_torch(q, k, v, qg, kg, vg, n, w1, G, 0.4)
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=0, atol=1e-12)
+    to.backward(torch.tensor(do))
+    for a, b in zip(grads, leaves):
+        np.testing.assert_allclose(a, b.grad.numpy(), rtol=0, atol=1e-12)
+    # the window projections get nothing from global rows and vice versa
+    gl = np.zeros(n, dtype=bool)
+    gl[G] = True
+    assert np.all(grads[0][:, :, gl] == 0) and np.all(grads[3][:, :, ~gl] == 0)
+
+
+def test_gproj_global_rows_ignore_window_projections():
+    """Changing Q_s, K_s, V_s leaves the rows of global tokens unchanged, and changing
+    Q_g, K_g, V_g leaves the other rows unchanged."""
+    n, H, dh, w1, G = 64, 1, 4, 3, [0, 30]
+    xs = [rnd(110 + i, 1, H, n, dh) for i in range(6)]
+    o, _ = LF.longformer_gproj_fwd(*xs, n, w1, G, 0.5)
+    o2, _ = LF.longformer_gproj_fwd(*[x + 1.0 for x in xs[:3]], *xs[3:], n, w1, G, 0.5)
+    o3, _ = LF.longformer_gproj_fwd(*xs[:3], *[x - 0.5 for x in xs[3:]], n, w1, G, 0.5)
+    gl = np.zeros(n, dtype=bool)
+    gl[G] = True
+    np.testing.assert_array_equal(o[:, :, gl], o2[:, :, gl])
+    np.testing.assert_array_equal(o[:, :, ~gl], o3[:, :, ~gl])
+    assert np.abs(o[:, :, ~gl] - o2[:, :, ~gl]).max() > 1e-3
+    assert np.abs(o[:, :, gl] - o3[:, :, gl]).max() > 1e-3
