@@ -23,8 +23,10 @@ from ._lib import (  # noqa: F401
     bsattn_status_str,
     bsattn_version,
     lfattn_bwd,
+    lfattn_bwd_gproj,
     lfattn_bwd_workspace,
     lfattn_fwd,
+    lfattn_fwd_gproj,
     lfattn_fwd_workspace,
     lfattn_plan_build,
     lfattn_plan_build_dilated,

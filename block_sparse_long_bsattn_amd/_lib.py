@@ -28,8 +28,9 @@ EXPORTS = (
     "bsattn_layout_build", "bsattn_layout_rebuild", "bsattn_layout_info",
     "bsattn_layout_to_host", "bsattn_layout_destroy", "bsattn_fwd_workspace",
     "bsattn_bwd_workspace", "bsattn_fwd", "bsattn_bwd", "lfattn_plan_build",
-    "lfattn_plan_build_dilated", "lfattn_plan_build_etc", "lfattn_plan_destroy", "lfattn_fwd_workspace", "lfattn_fwd", "lfattn_bwd_workspace",
-    "lfattn_bwd", "bsattn_status_str",
+    "lfattn_plan_build_dilated", "lfattn_plan_build_etc", "lfattn_plan_destroy",
+    "lfattn_fwd_workspace", "lfattn_fwd", "lfattn_bwd_workspace", "lfattn_bwd",
+    "lfattn_fwd_gproj", "lfattn_bwd_gproj", "bsattn_status_str",
     "bsattn_last_error", "bsattn_version", "bsattn_profile_enable", "bsattn_profile_read",
 )
 
@@ -82,6 +83,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lfattn_bwd": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, c_size_t, c_void_p]),
+        "lfattn_fwd_gproj": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float]
+                             + [c_void_p] * 9 + [c_size_t, c_void_p]),
+        "lfattn_bwd_gproj": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float]
+                             + [c_void_p] * 16 + [c_size_t, c_void_p]),
         "bsattn_status_str": (c_char_p, [c_int]),
         "bsattn_last_error": (c_char_p, []),
         "bsattn_version": (c_char_p, []),
@@ -327,6 +332,47 @@ def lfattn_bwd(plan, q, k, v, o, lse, dout, dq, dk, dv, workspace=None, scale=No
                              _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                              _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)),
            "lfattn_bwd")
+
+
+def lfattn_fwd_gproj(plan, q, k, v, qg, kg, vg, o, lse=None, workspace=None, scale=None,
+                     stream=None) -> None:
+    """Forward with separate projections (qg, kg, vg) for the rows of global tokens."""
+    bsz, heads, _, d = q.shape
+    if plan not in _plan_n:
+        raise ValueError("lfattn_fwd_gproj: unknown plan handle")
+    shape = (bsz, heads, _plan_n[plan], d)
+    _check_tensors("lfattn_fwd_gproj", shape, q.dtype,
+                   (("q", q), ("k", k), ("v", v), ("qg", qg), ("kg", kg), ("vg", vg), ("o", o)),
+                   lse, workspace, lfattn_fwd_workspace(plan, bsz, heads, d))
+    scale = d ** -0.5 if scale is None else scale
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().lfattn_fwd_gproj(plan, bsz, heads, d, _dtype_code(q), c_float(scale), _ptr(q),
+                                   _ptr(k), _ptr(v), _ptr(qg), _ptr(kg), _ptr(vg), _ptr(o),
+                                   _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)),
+           "lfattn_fwd_gproj")
+
+
+def lfattn_bwd_gproj(plan, q, k, v, qg, kg, vg, o, lse, dout, dq, dk, dv, dqg, dkg, dvg,
+                     workspace=None, scale=None, stream=None) -> None:
+    """Backward of lfattn_fwd_gproj: gradients for both projection sets."""
+    bsz, heads, _, d = q.shape
+    if plan not in _plan_n:
+        raise ValueError("lfattn_bwd_gproj: unknown plan handle")
+    if lse is None:
+        raise ValueError("lfattn_bwd_gproj: lse is required")
+    shape = (bsz, heads, _plan_n[plan], d)
+    _check_tensors("lfattn_bwd_gproj", shape, q.dtype,
+                   (("q", q), ("k", k), ("v", v), ("qg", qg), ("kg", kg), ("vg", vg), ("o", o),
+                    ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv), ("dqg", dqg),
+                    ("dkg", dkg), ("dvg", dvg)),
+                   lse, workspace, lfattn_bwd_workspace(plan, bsz, heads, d))
+    scale = d ** -0.5 if scale is None else scale
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().lfattn_bwd_gproj(plan, bsz, heads, d, _dtype_code(q), c_float(scale), _ptr(q),
+                                   _ptr(k), _ptr(v), _ptr(qg), _ptr(kg), _ptr(vg), _ptr(o),
+                                   _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _ptr(dqg), _ptr(dkg), _ptr(dvg), _ptr(workspace), ws_bytes,
+                                   _stream(stream)), "lfattn_bwd_gproj")
 
 
 # --- diagnostics ----------------------------------------------------------------

@@ -528,22 +528,52 @@ size_t lfattn_fwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
   return lf_workspace_bytes(P, batch, heads);
 }
 
+}  // extern "C"
+
+namespace {
+
+int lf_fwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int d,
+                bsattn_dtype dt, float scale, const void* q, const void* k, const void* v,
+                const void* qg, const void* kg, const void* vg, void* o, float* lse,
+                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  const std::string w(who);
+  if (P == nullptr) return set_error(BSATTN_EINVAL, w + ": null plan");
+  if (heads < 1) return set_error(BSATTN_EINVAL, w + ": heads must be >= 1");
+  int st = check_plan_heads(P, heads, who);
+  if (st) return st;
+  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, w + ": only bf16 is built");
+  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o}, who))) return st;
+  if (qg != nullptr && (st = check_tensor_args(batch, d, scale, {qg, kg, vg}, who))) return st;
+  if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, w + ": lse not 16-byte aligned");
+  if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
+    return set_error(BSATTN_EUNSUPPORTED, w + ": tensor too large");
+  if ((st = check_workspace(workspace, ws_bytes, lf_workspace_bytes(P, batch, heads), who))) return st;
+  if ((st = check_device(P->device))) return st;
+  return launch_lf_fwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, lse, workspace, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
 int lfattn_fwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt, float scale,
                const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
                size_t ws_bytes, hipStream_t stream) {
-  clear_error();
-  if (P == nullptr) return set_error(BSATTN_EINVAL, "lf_fwd: null plan");
-  if (heads < 1) return set_error(BSATTN_EINVAL, "lf_fwd: heads must be >= 1");
-  int st = check_plan_heads(P, heads, "lf_fwd");
-  if (st) return st;
-  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "lf_fwd: only bf16 is built");
-  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o}, "lf_fwd"))) return st;
-  if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, "lf_fwd: lse not 16-byte aligned");
-  if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
-    return set_error(BSATTN_EUNSUPPORTED, "lf_fwd: tensor too large");
-  if ((st = check_workspace(workspace, ws_bytes, lf_workspace_bytes(P, batch, heads), "lf_fwd"))) return st;
-  if ((st = check_device(P->device))) return st;
-  return launch_lf_fwd(P, batch, heads, scale, q, k, v, o, lse, workspace, stream);
+  return lf_fwd_impl("lf_fwd", P, batch, heads, d, dt, scale, q, k, v, nullptr, nullptr,
+                     nullptr, o, lse, workspace, ws_bytes, stream);
+}
+
+int lfattn_fwd_gproj(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt,
+                     float scale, const void* q, const void* k, const void* v, const void* qg,
+                     const void* kg, const void* vg, void* o, float* lse, void* workspace,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (qg == nullptr || kg == nullptr || vg == nullptr) {
+    clear_error();
+    return set_error(BSATTN_EINVAL, "lf_fwd_gproj: null global projection");
+  }
+  return lf_fwd_impl("lf_fwd_gproj", P, batch, heads, d, dt, scale, q, k, v, qg, kg, vg, o, lse,
+                     workspace, ws_bytes, stream);
 }
 
 size_t lfattn_bwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
@@ -552,24 +582,65 @@ size_t lfattn_bwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
   return lf_bwd_workspace_bytes(P, batch, heads);
 }
 
+}  // extern "C"
+
+namespace {
+
+int lf_bwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int d,
+                bsattn_dtype dt, float scale, const void* q, const void* k, const void* v,
+                const void* qg, const void* kg, const void* vg, const void* o, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg, void* dvg,
+                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  const std::string w(who);
+  if (P == nullptr) return set_error(BSATTN_EINVAL, w + ": null plan");
+  if (heads < 1) return set_error(BSATTN_EINVAL, w + ": heads must be >= 1");
+  int st = check_plan_heads(P, heads, who);
+  if (st) return st;
+  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, w + ": only bf16 is built");
+  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, who)))
+    return st;
+  if (qg != nullptr) {
+    if ((st = check_tensor_args(batch, d, scale, {qg, kg, vg, dqg, dkg, dvg}, who))) return st;
+    const void* outs[6] = {dq, dk, dv, dqg, dkg, dvg};
+    for (int x = 0; x < 6; ++x)
+      for (int y = x + 1; y < 6; ++y)
+        if (outs[x] == outs[y]) return set_error(BSATTN_EINVAL, w + ": output gradients alias");
+  }
+  if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
+    return set_error(BSATTN_EUNSUPPORTED, w + ": tensor too large");
+  if ((st = check_workspace(workspace, ws_bytes, lf_bwd_workspace_bytes(P, batch, heads), who)))
+    return st;
+  if ((st = check_device(P->device))) return st;
+  return launch_lf_bwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, lse, dout, dq, dk, dv,
+                       dqg, dkg, dvg, workspace, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
 int lfattn_bwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt, float scale,
                const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                hipStream_t stream) {
-  clear_error();
-  if (P == nullptr) return set_error(BSATTN_EINVAL, "lf_bwd: null plan");
-  if (heads < 1) return set_error(BSATTN_EINVAL, "lf_bwd: heads must be >= 1");
-  int st = check_plan_heads(P, heads, "lf_bwd");
-  if (st) return st;
-  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "lf_bwd: only bf16 is built");
-  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "lf_bwd")))
-    return st;
-  if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
-    return set_error(BSATTN_EUNSUPPORTED, "lf_bwd: tensor too large");
-  if ((st = check_workspace(workspace, ws_bytes, lf_bwd_workspace_bytes(P, batch, heads), "lf_bwd")))
-    return st;
-  if ((st = check_device(P->device))) return st;
-  return launch_lf_bwd(P, batch, heads, scale, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream);
+  return lf_bwd_impl("lf_bwd", P, batch, heads, d, dt, scale, q, k, v, nullptr, nullptr, nullptr,
+                     o, lse, dout, dq, dk, dv, nullptr, nullptr, nullptr, workspace, ws_bytes,
+                     stream);
+}
+
+int lfattn_bwd_gproj(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt,
+                     float scale, const void* q, const void* k, const void* v, const void* qg,
+                     const void* kg, const void* vg, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg,
+                     void* dvg, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (qg == nullptr || kg == nullptr || vg == nullptr || dqg == nullptr || dkg == nullptr ||
+      dvg == nullptr) {
+    clear_error();
+    return set_error(BSATTN_EINVAL, "lf_bwd_gproj: null global projection or gradient");
+  }
+  return lf_bwd_impl("lf_bwd_gproj", P, batch, heads, d, dt, scale, q, k, v, qg, kg, vg, o, lse,
+                     dout, dq, dk, dv, dqg, dkg, dvg, workspace, ws_bytes, stream);
 }
 
 const char* bsattn_status_str(int status) {

@@ -97,16 +97,19 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q,
                const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* ws,
                hipStream_t stream);
+// qg, kg, vg (and dqg, dkg, dvg) may be null: one projection set for every row.
 int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
-                  const void* k, const void* v, void* o, float* lse, void* ws,
-                  hipStream_t stream);
+                  const void* k, const void* v, const void* qg, const void* kg,
+                  const void* vg, void* o, float* lse, void* ws, hipStream_t stream);
 
 size_t fwd_workspace_bytes(const bsattn_layout* L, int batch);
 size_t bwd_workspace_bytes(const bsattn_layout* L, int batch);
 size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads);
 int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
-                  const void* k, const void* v, const void* o, const float* lse,
-                  const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t stream);
+                  const void* k, const void* v, const void* qg, const void* kg,
+                  const void* vg, const void* o, const float* lse, const void* dout, void* dq,
+                  void* dk, void* dv, void* dqg, void* dkg, void* dvg, void* ws,
+                  hipStream_t stream);
 size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads);
 
 }  // namespace bsattn

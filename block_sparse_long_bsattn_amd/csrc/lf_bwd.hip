@@ -49,6 +49,15 @@ struct LfBwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
+  // projections of the global rows' attention and their gradients: the same as
+  // q, k, v, dq, dk, dv unless separate global projections are given (gproj)
+  const uint16_t* qg;
+  const uint16_t* kg;
+  const uint16_t* vg;
+  uint16_t* dqg;
+  uint16_t* dkg;
+  uint16_t* dvg;
+  int gproj;
   float* dbuf;       // D [B*H*n]
   float* part_q;     // [B*H*ngt*nseg][64][64] dQ of the global query rows
   float* part_kv;    // [periods*nct_g*nseg][2][64][64] dK, dV of key class tiles
@@ -61,7 +70,7 @@ struct LfBwdArgs {
   int nct, nct_plain, nct_g, ph;   // class tiles (all / without / with global keys), heads
                                    // per head period
   LfWindow win;                    // key range of each row, in class indices
-  int dq_band_items, dq_items, kv_plain_items, kv_items;
+  int dq_band_items, dq_items, kv_plain_items, kv_seg_items, kv_items;
   float scale, sl2;
 };
 
@@ -124,10 +133,12 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
       ++x;
     return x;
   };
+  const uint16_t* kbase = (band ? a.k : a.kg) + bh_off;
+  const uint16_t* vbase = (band ? a.v : a.vg) + bh_off;
   auto tile_load = [&](int x, TileRegs& kr, TileRegs& vr) {
     if (x < nband) {
-      gload_class(kr, a.k + bh_off, cls, stride, lo_u + x, nc, tid);
-      gload_class(vr, a.v + bh_off, cls, stride, lo_u + x, nc, tid);
+      gload_class(kr, kbase, cls, stride, lo_u + x, nc, tid);
+      gload_class(vr, vbase, cls, stride, lo_u + x, nc, tid);
     } else {
       gload_gather(kr, a.k + bh_off, a.gtok, a.ng, x - nband, tid);
       gload_gather(vr, a.v + bh_off, a.gtok, a.ng, x - nband, tid);
@@ -143,7 +154,7 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     const size_t off = bh_off + (size_t)p * kHead + 8 * hl;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4 qv = ldg16(a.q + off + 16 * c);
+      const u32x4 qv = ldg16((band ? a.q : a.qg) + off + 16 * c);
       const u32x4 dv = ldg16(a.dout + off + 16 * c);
       const u32x4 ov = ldg16(a.o + off + 16 * c);
       qB[c] = __builtin_bit_cast(bf16x8, qv);
@@ -236,6 +247,15 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
         *reinterpret_cast<u32x2*>(op + 8 * j) = w0;
         *reinterpret_cast<u32x2*>(op + 32 + 8 * j) = w1;
       }
+      if (a.gproj) {   // the global projections get nothing from this row
+        uint16_t* zp = a.dqg + bh_off + (size_t)p * kHead + 4 * hl;
+        const u32x2 z = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          *reinterpret_cast<u32x2*>(zp + 8 * j) = z;
+          *reinterpret_cast<u32x2*>(zp + 32 + 8 * j) = z;
+        }
+      }
     }
   } else {
     const size_t slot = ((size_t)bh * a.ngt + gt) * a.nseg + seg;
@@ -266,27 +286,40 @@ __global__ __launch_bounds__(kThreads, 2) void lf_bwd_dq_kernel(LfBwdArgs a) {
 // dK, dV
 // ---------------------------------------------------------------------------
 
-// One dK/dV item; kPlain: a key class tile without global keys (v indexes
-// periods*nct_plain), else a segment of a key class tile holding global keys.
-template <bool kPlain>
+// Kinds of dK/dV item.
+enum LfKvKind {
+  kKvPlain = 0,   // a key class tile without global keys (v indexes periods*nct_plain)
+  kKvSeg = 1,     // a segment of a key class tile holding global keys
+  kKvGRows = 2,   // with separate global projections: a natural key tile against the
+                  // global query rows only, giving dK_g, dV_g (v indexes B*H*nt)
+};
+
+template <int kKind>
 __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsTile* sQ,
                                                  LdsTile* sO, float (*sL)[kBlock],
                                                  float (*sD)[kBlock]) {
-  int per, gki = 0, seg = 0;
-  LfTileRef ref;
-  if constexpr (kPlain) {
-    per = v / a.nct_plain;
-    ref = a.ct[v - per * a.nct_plain];
+  constexpr bool kPlain = kKind == kKvPlain;
+  constexpr bool kGRows = kKind == kKvGRows;
+  int per = 0, gki = 0, seg = 0, bh, cls = 0, stride = 1, u, nc = a.n;
+  if constexpr (kGRows) {
+    bh = v / a.nt;
+    u = v - bh * a.nt;
   } else {
-    const int per_p = a.nct_g * a.nseg;
-    per = v / per_p;
-    const int rem = v - per * per_p;
-    gki = rem / a.nseg;
-    seg = rem - gki * a.nseg;
-    ref = a.ct[a.nct_plain + gki];
+    LfTileRef ref;
+    if constexpr (kPlain) {
+      per = v / a.nct_plain;
+      ref = a.ct[v - per * a.nct_plain];
+    } else {
+      const int per_p = a.nct_g * a.nseg;
+      per = v / per_p;
+      const int rem = v - per * per_p;
+      gki = rem / a.nseg;
+      seg = rem - gki * a.nseg;
+      ref = a.ct[a.nct_plain + gki];
+    }
+    bh = per * a.ph + ref.h;
+    cls = ref.c; stride = ref.s; u = ref.t; nc = ref.nc;
   }
-  const int bh = per * a.ph + ref.h;
-  const int cls = ref.c, stride = ref.s, u = ref.t, nc = ref.nc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)bh * a.n * kHead;
@@ -297,17 +330,23 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   int rlo, rhi;   // rows whose window holds this lane's key, in class indices
   a.win.rows(jc, rlo, rhi);
   bool key_global = false;
-  if constexpr (!kPlain)
+  if constexpr (kKind == kKvSeg)
     key_global = (class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane) >> kx) & 1ull;
 
   // query tiles: plain items walk the window's class tiles [lo, hi] of the key's
-  // class, then the global tiles with an eligible row; segment items walk kLfSeg
-  // natural tiles (the column of a global key is full)
+  // class, then the global tiles with an eligible row (none with separate global
+  // projections: those rows are the global-row items'); segment items walk kLfSeg
+  // natural tiles (the column of a global key is full); global-row items walk the
+  // global tiles only
   int lo, hi, ntile;
   int qc = cls, qs = stride, qnc = nc;   // class of the query tiles walked
   if constexpr (kPlain) {
     band_queries(a.win, u, nc, (nc + kBlock - 1) / kBlock, lo, hi);
-    ntile = hi - lo + 1 + a.ngt;
+    ntile = hi - lo + 1 + (a.gproj ? 0 : a.ngt);
+  } else if constexpr (kGRows) {
+    lo = 0;
+    hi = -1;
+    ntile = a.ngt;
   } else {
     qc = 0; qs = 1; qnc = a.n;
     lo = seg * kLfSeg;
@@ -324,9 +363,9 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   // Segment items test the dilated window in token coordinates: query rows whose
   // distance to the key is a multiple of the stride (bits 0, s, 2s, ... shifted).
   uint64_t stride_bits = 0ull;
-  if constexpr (!kPlain)
+  if constexpr (kKind == kKvSeg)
     for (int b = 0; b < kBlock; b += stride) stride_bits |= 1ull << b;
-  const uint16_t* qbase = a.q + bh_off;
+  const uint16_t* qbase = (kGRows ? a.qg : a.q) + bh_off;
   const uint16_t* dobase = a.dout + bh_off;
   const float* lbase = a.lse + (size_t)bh * a.n;
   const float* dbase = a.dbuf + (size_t)bh * a.n;
@@ -357,8 +396,8 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
     const size_t off = bh_off + (size_t)q_tok * kHead + 8 * hl;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      kB[c] = ld16(a.k + off + 16 * c);
-      vB[c] = ld16(a.v + off + 16 * c);
+      kB[c] = ld16((kGRows ? a.kg : a.k) + off + 16 * c);
+      vB[c] = ld16((kGRows ? a.vg : a.v) + off + 16 * c);
     }
   }
   // Q tiles are staged pre-scaled by scale*log2(e), rounded to bf16 exactly as the
@@ -411,24 +450,29 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
     if (x < nband) {
       const int tq = lo + x, i0 = tq * kBlock;
       if constexpr (kPlain) {
+        // with separate global projections the rows of global tokens are excluded
         const uint64_t vq = valid_rows(tq, nc);
-        if (!tiles_in_window(a.win, tq, u) || vq != ~0ull) {
-          const uint64_t ok = (bit_range(rlo - i0, rhi - i0) & vq) |
-                              class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, tq, nc, lane);
-          mask_rows(s0, s1, hl, ok);
+        if (!tiles_in_window(a.win, tq, u) || vq != ~0ull || a.gproj) {
+          const uint64_t win = bit_range(rlo - i0, rhi - i0) & vq;
+          const uint64_t gq = class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, tq, nc, lane);
+          const uint64_t ok = a.gproj ? win & ~gq : win | gq;
+          if (ok != ~0ull) mask_rows(s0, s1, hl, ok);
         }
-      } else {
+      } else if constexpr (kKind == kKvSeg) {
         // natural query tile: the rows p = i0 + x whose window holds the key (tokens
         // cls + s*rlo .. cls + s*rhi at a multiple of s from it) or that are global;
         // every row for a global key; only rows before the end of the sequence
         const uint64_t vq = valid_rows(tq, a.n);
+        const uint64_t gq = a.tile_gmask[tq];
         if (key_global) {
-          if (vq != ~0ull) mask_rows(s0, s1, hl, vq);
-        } else if (stride > 1 || vq != ~0ull || !tiles_in_window(a.win, tq, u)) {
+          const uint64_t ok = a.gproj ? vq & ~gq : vq;
+          if (ok != ~0ull) mask_rows(s0, s1, hl, ok);
+        } else if (stride > 1 || vq != ~0ull || a.gproj || !tiles_in_window(a.win, tq, u)) {
           int r = (q_tok - i0) % stride;
           if (r < 0) r += stride;
-          const uint64_t ok = ((bit_range(cls + stride * rlo - i0, cls + stride * rhi - i0) &
-                                (stride_bits << r)) | a.tile_gmask[tq]) & vq;
+          const uint64_t win = bit_range(cls + stride * rlo - i0, cls + stride * rhi - i0) &
+                               (stride_bits << r);
+          const uint64_t ok = (a.gproj ? win & ~gq : win | gq) & vq;
           mask_rows(s0, s1, hl, ok);
         }
       }
@@ -464,11 +508,11 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   }
 
   const float sc = a.scale / a.sl2;   // dK was accumulated against the scaled Q
-  if constexpr (kPlain) {
+  if constexpr (kKind != kKvSeg) {
     if (!key_valid) return;
     const size_t off = bh_off + (size_t)q_tok * kHead + 4 * hl;
-    uint16_t* kp = a.dk + off;
-    uint16_t* vp = a.dv + off;
+    uint16_t* kp = (kGRows ? a.dkg : a.dk) + off;
+    uint16_t* vp = (kGRows ? a.dvg : a.dv) + off;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x2 k0w, k1w, v0w, v1w;
@@ -505,8 +549,9 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   }
 }
 
-// Occupancy 1 (AGPRs hold the overflow): at two waves per SIMD this kernel spilled
-// inside its loop and ran ~20 % slower.
+// Built at 256 VGPRs with no spills, so it runs two waves per SIMD, about 25 %
+// faster than one.  Asking for two waves explicitly makes the compiler spill two
+// registers instead; the resource report of the build shows which one it got.
 __global__ __launch_bounds__(kThreads) void lf_bwd_dkdv_kernel(LfBwdArgs a) {
   __shared__ __attribute__((aligned(16))) LdsTile sQ[2];
   __shared__ __attribute__((aligned(16))) LdsTile sO[2];   // dO
@@ -515,9 +560,11 @@ __global__ __launch_bounds__(kThreads) void lf_bwd_dkdv_kernel(LfBwdArgs a) {
   const int v = xcd_remap(blockIdx.x, a.kv_items);
   if (v >= a.kv_items) return;
   if (v < a.kv_plain_items)
-    lf_bwd_dkdv_item<true>(a, v, sQ, sO, sL, sD);
+    lf_bwd_dkdv_item<kKvPlain>(a, v, sQ, sO, sL, sD);
+  else if (v < a.kv_seg_items)
+    lf_bwd_dkdv_item<kKvSeg>(a, v - a.kv_plain_items, sQ, sO, sL, sD);
   else
-    lf_bwd_dkdv_item<false>(a, v - a.kv_plain_items, sQ, sO, sL, sD);
+    lf_bwd_dkdv_item<kKvGRows>(a, v - a.kv_seg_items, sQ, sO, sL, sD);
 }
 
 // Segment sums in segment order.  Work-groups [0, B*H*ngt): dQ of global tile gt,
@@ -536,7 +583,14 @@ __global__ __launch_bounds__(256) void lf_bwd_reduce_kernel(LfBwdArgs a, int nq_
     if (j >= a.ng) return;
     src = a.part_q + (size_t)idx * a.nseg * kTile + e0;
     stride = kTile;
-    dst = a.dq + ((size_t)bh * a.n + a.gtok[j]) * kHead + (e0 % kHead);
+    const size_t row_off = ((size_t)bh * a.n + a.gtok[j]) * kHead + (e0 % kHead);
+    dst = a.dqg + row_off;
+    if (a.gproj) {   // the window projections get nothing from a global row
+      float z[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) z[e] = 0.f;
+      store16_bf16(a.dq + row_off, z, 1.f);
+    }
   } else {
     const int w = blockIdx.x - nq_groups;
     const int kind = w & 1, idx = w >> 1;   // idx = period * nct_g + gki
@@ -589,14 +643,23 @@ size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads) {
 }
 
 int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
-                  const void* k, const void* v, const void* o, const float* lse,
-                  const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t stream) {
+                  const void* k, const void* v, const void* qg, const void* kg,
+                  const void* vg, const void* o, const float* lse, const void* dout, void* dq,
+                  void* dk, void* dv, void* dqg, void* dkg, void* dvg, void* ws,
+                  hipStream_t stream) {
   const LfBwdWs w = lf_bwd_ws_layout(P, batch, heads);
   char* base = (char*)ws;
   LfBwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.o = (const uint16_t*)o; a.lse = lse; a.dout = (const uint16_t*)dout;
   a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
+  a.gproj = qg != nullptr ? 1 : 0;
+  a.qg = (const uint16_t*)(a.gproj ? qg : q);
+  a.kg = (const uint16_t*)(a.gproj ? kg : k);
+  a.vg = (const uint16_t*)(a.gproj ? vg : v);
+  a.dqg = (uint16_t*)(a.gproj ? dqg : dq);
+  a.dkg = (uint16_t*)(a.gproj ? dkg : dk);
+  a.dvg = (uint16_t*)(a.gproj ? dvg : dv);
   a.dbuf = (float*)(base + w.dbuf);
   a.part_q = (float*)(base + w.part_q);
   a.part_kv = (float*)(base + w.part_kv);
@@ -614,7 +677,8 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const
   a.dq_band_items = periods * a.nct;
   a.dq_items = a.dq_band_items + bhn * P->ngt * P->nseg;
   a.kv_plain_items = periods * a.nct_plain;
-  a.kv_items = a.kv_plain_items + periods * a.nct_g * P->nseg;
+  a.kv_seg_items = a.kv_plain_items + periods * a.nct_g * P->nseg;
+  a.kv_items = a.kv_seg_items + (a.gproj ? bhn * P->nt : 0);
   int st;
   {
     ProfScope prof_("lf_bwd_dq", stream);

@@ -17,8 +17,10 @@
 //                 global are allowed in every tile.  Rows of global tokens and
 //                 rows past the class's end are not written.
 //               * a segment of kLfSeg key tiles for a tile of global query rows
-//                 ("a token with global attention attends to all tokens"), query
-//                 rows gathered by index, writing a partial record.
+//                 (a global token attends to every token), query rows gathered by
+//                 index, writing a partial record.  With separate global
+//                 projections (§3.1 "Linear Projections for Global Attention") these
+//                 rows read Q_g, K_g, V_g instead of Q, K, V.
 //   lf_combine  merges those partials in a fixed order and scatters O and lse back
 //               to the global tokens' positions.
 
@@ -35,6 +37,9 @@ struct LfArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
+  const uint16_t* qg;   // projections of the global rows' attention (q, k, v unless
+  const uint16_t* kg;   // separate global projections are given)
+  const uint16_t* vg;
   uint16_t* o;
   float* lse;
   float* part;          // [B*H*ngt*nseg] partial records of the global query rows
@@ -161,7 +166,7 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
 
   bf16x8 qB[4];
   {
-    const uint16_t* qp = a.q + bh_off + (size_t)global_token(a.gtok, a.ng, gt, qr) * kHead + 8 * hl;
+    const uint16_t* qp = a.qg + bh_off + (size_t)global_token(a.gtok, a.ng, gt, qr) * kHead + 8 * hl;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
   }
@@ -171,8 +176,8 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
   FwdState st;
   fwd_state_init(st);
   TileRegs kr, vr;
-  gload_class(kr, a.k + bh_off, 0, 1, u_begin, a.n, tid);
-  gload_class(vr, a.v + bh_off, 0, 1, u_begin, a.n, tid);
+  gload_class(kr, a.kg + bh_off, 0, 1, u_begin, a.n, tid);
+  gload_class(vr, a.vg + bh_off, 0, 1, u_begin, a.n, tid);
   lds_store_nat(sK[0], kr, tid);
   lds_store_nat(sV[0], vr, tid);
   for (int u = u_begin; u < u_end; ++u) {
@@ -180,8 +185,8 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
     __syncthreads();
     const bool more = u + 1 < u_end;
     if (more) {
-      gload_class(kr, a.k + bh_off, 0, 1, u + 1, a.n, tid);
-      gload_class(vr, a.v + bh_off, 0, 1, u + 1, a.n, tid);
+      gload_class(kr, a.kg + bh_off, 0, 1, u + 1, a.n, tid);
+      gload_class(vr, a.vg + bh_off, 0, 1, u + 1, a.n, tid);
     }
     f32x16 s0, s1;
     qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
@@ -235,10 +240,13 @@ size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads) {
 }
 
 int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
-                  const void* k, const void* v, void* o, float* lse, void* ws,
-                  hipStream_t stream) {
+                  const void* k, const void* v, const void* qg, const void* kg,
+                  const void* vg, void* o, float* lse, void* ws, hipStream_t stream) {
   LfArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.qg = (const uint16_t*)(qg != nullptr ? qg : q);
+  a.kg = (const uint16_t*)(kg != nullptr ? kg : k);
+  a.vg = (const uint16_t*)(vg != nullptr ? vg : v);
   a.o = (uint16_t*)o; a.lse = lse;
   const bool has_g = P->ng > 0;
   a.part = has_g ? (float*)ws : nullptr;

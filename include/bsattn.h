@@ -264,6 +264,37 @@ int lfattn_bwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtyp
                const float* lse, const void* dout, void* dq, void* dk, void* dv,
                void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Separate projections for the global attention ([LF] §3.1 "Linear Projections for
+ * Global Attention": one set Q_s, K_s, V_s for the sliding-window attention and
+ * another Q_g, K_g, V_g for the global attention, the second starting equal to
+ * the first).  Reading: the row of a global token (which covers every token) is
+ * computed from Qg at that token and Kg, Vg at every token; every other row (its
+ * window and the global keys) from Q, K, V.  So O and lse are those of lfattn_fwd
+ * with the global rows recomputed on the second set; passing qg = q, kg = k,
+ * vg = v gives lfattn_fwd's result.
+ *   qg, kg, vg   DEVICE [batch, heads, n, d], the second projection set.
+ * Other arguments, workspace size (lfattn_fwd_workspace) and return codes as
+ * lfattn_fwd; EINVAL when qg, kg or vg is NULL.
+ */
+int lfattn_fwd_gproj(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,
+                     float scale, const void* q, const void* k, const void* v, const void* qg,
+                     const void* kg, const void* vg, void* o, float* lse, void* workspace,
+                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradient of lfattn_fwd_gproj for the loss <dout, O>: dq, dk, dv for the first
+ * set (dq is 0 on the rows of global tokens) and dqg, dkg, dvg for the second
+ * (dqg is 0 on the other rows; dkg, dvg collect the global rows' attention over
+ * every token).  The six outputs must be distinct buffers (EINVAL otherwise).
+ * Workspace size lfattn_bwd_workspace; other arguments and codes as lfattn_bwd.
+ */
+int lfattn_bwd_gproj(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,
+                     float scale, const void* q, const void* k, const void* v, const void* qg,
+                     const void* kg, const void* vg, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg,
+                     void* dvg, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Diagnostics                                                                */
 /* ------------------------------------------------------------------------- */

@@ -95,11 +95,12 @@ def _rows_split(n: int, global_tokens):
     return g
 
 
-def longformer_gproj_fwd(q, k, v, qg, kg, vg, n: int, w1: int, global_tokens, scale: float):
+def longformer_gproj_fwd(q, k, v, qg, kg, vg, n: int, w1: int, global_tokens, scale: float,
+                         dilation=0):
     """O and lse [B,H,n] with separate global projections (fp64)."""
     from . import attention as A
     g = _rows_split(n, global_tokens)
-    o_s, l_s = A.attention_fwd(q, k, v, longformer_mask(n, w1, global_tokens), scale)
+    o_s, l_s = A.attention_fwd(q, k, v, longformer_mask(n, w1, global_tokens, dilation), scale)
     full = np.ones((n, n), dtype=bool)
     o_g, l_g = A.attention_fwd(qg, kg, vg, full, scale)
     o = np.where(g[None, None, :, None], o_g, o_s)
@@ -108,7 +109,7 @@ def longformer_gproj_fwd(q, k, v, qg, kg, vg, n: int, w1: int, global_tokens, sc
 
 
 def longformer_gproj_bwd(q, k, v, qg, kg, vg, dout, n: int, w1: int, global_tokens,
-                         scale: float):
+                         scale: float, dilation=0):
     """(dQ, dK, dV, dQ_g, dK_g, dV_g) for the loss <dout, O> of longformer_gproj_fwd:
     each problem sees the output gradient of its own rows only."""
     from . import attention as A
@@ -116,7 +117,8 @@ def longformer_gproj_bwd(q, k, v, qg, kg, vg, dout, n: int, w1: int, global_toke
     dout = np.asarray(dout, dtype=np.float64)
     d_s = np.where(g[None, None, :, None], 0.0, dout)
     d_g = np.where(g[None, None, :, None], dout, 0.0)
-    dq, dk, dv = A.attention_bwd(q, k, v, d_s, longformer_mask(n, w1, global_tokens), scale)
+    dq, dk, dv = A.attention_bwd(q, k, v, d_s, longformer_mask(n, w1, global_tokens, dilation),
+                                 scale)
     full = np.ones((n, n), dtype=bool)
     dqg, dkg, dvg = A.attention_bwd(qg, kg, vg, d_g, full, scale)
     return dq, dk, dv, dqg, dkg, dvg

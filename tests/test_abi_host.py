@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_binding_exports():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     assert sorted(_lib.EXPORTS) == names
 
 
@@ -78,6 +78,8 @@ def test_null_handles_are_rejected():
     assert lib.bsattn_bwd(None, 1, 64, 1, 0.125, *([None] * 9), None, 0, None) == -1
     assert lib.lfattn_fwd(None, 1, 1, 64, 1, 0.125, *([None] * 5), None, 0, None) == -1
     assert lib.lfattn_bwd(None, 1, 1, 64, 1, 0.125, *([None] * 9), None, 0, None) == -1
+    assert lib.lfattn_fwd_gproj(None, 1, 1, 64, 1, 0.125, *([None] * 8), None, 0, None) == -1
+    assert lib.lfattn_bwd_gproj(None, 1, 1, 64, 1, 0.125, *([None] * 15), None, 0, None) == -1
     assert lib.bsattn_layout_info(None, None, None, None) == -1
     assert lib.bsattn_layout_rebuild(None, 1, None) == -1
     assert lib.bsattn_fwd_workspace(None, 1, 64) == 0
