@@ -120,6 +120,7 @@ void free_layout(bsattn_layout* L) {
   (void)hipFree(L->d_csc_ptr);
   (void)hipFree(L->d_csc_idx);
   (void)hipFree(L->d_rbits);
+  (void)hipFree(L->d_kv_order);
   delete L;
 }
 
@@ -229,13 +230,16 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
   if (e != hipSuccess) { delete L; return check_hip(e, "hipGetDevice"); }
   e = hipDeviceGetAttribute(&L->cus, hipDeviceAttributeMultiprocessorCount, L->device);
   if (e != hipSuccess) { delete L; return check_hip(e, "hipDeviceGetAttribute"); }
+  e = hipDeviceGetAttribute(&L->max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, L->device);
+  if (e != hipSuccess) { delete L; return check_hip(e, "hipDeviceGetAttribute"); }
   int st = BSATTN_OK;
   if ((st = dev_alloc(&L->d_gblk, (size_t)g)) || (st = dev_alloc(&L->d_ngblk, ng.size())) ||
       (st = dev_alloc(&L->d_row_ptr, (size_t)heads * nb + 1)) ||
       (st = dev_alloc(&L->d_col_idx, (size_t)(nnz * heads))) ||
       (st = dev_alloc(&L->d_csc_ptr, (size_t)heads * nb + 1)) ||
       (st = dev_alloc(&L->d_csc_idx, (size_t)(nnz * heads))) ||
-      (st = dev_alloc(&L->d_rbits, (size_t)heads * nb * ((nb + 31) / 32)))) {
+      (st = dev_alloc(&L->d_rbits, (size_t)heads * nb * ((nb + 31) / 32))) ||
+      (st = dev_alloc(&L->d_kv_order, (size_t)heads * ng.size()))) {
     free_layout(L);
     return st;
   }
@@ -255,6 +259,14 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
   if (!L->ngblk.empty() &&
       (st = check_hip(hipMemcpyAsync(L->d_ngblk, L->ngblk.data(), L->ngblk.size() * 4,
                                      hipMemcpyHostToDevice, stream), "upload blocks"))) {
+    free_layout(L);
+    return st;
+  }
+  for (int h = 0; h < heads; ++h) L->kv_order_init.insert(L->kv_order_init.end(), ng.begin(), ng.end());
+  if (!L->kv_order_init.empty() &&
+      (st = check_hip(hipMemcpyAsync(L->d_kv_order, L->kv_order_init.data(),
+                                     L->kv_order_init.size() * 4, hipMemcpyHostToDevice, stream),
+                      "upload work order"))) {
     free_layout(L);
     return st;
   }

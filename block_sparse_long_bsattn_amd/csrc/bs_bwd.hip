@@ -44,6 +44,7 @@ struct BwdArgs {
   const int32_t* csc_idx;
   const int32_t* gblk;
   const int32_t* ngblk;
+  const int32_t* kv_order;   // [heads][nb - g] dK/dV order of the non-global key blocks
   int heads, n, nb, g, seg, nseg, split;
   int items_per_bh, total_items;
   float scale, sl2;
@@ -55,7 +56,8 @@ struct Item {
 
 // Item v of a per-(batch, head) list: non-global blocks first (whole list), then
 // each global block's segments of a.seg blocks.  ptr is the row or column pointer.
-__device__ __forceinline__ Item decode(const BwdArgs& a, int v, const int32_t* ptr) {
+// kv: the dK/dV items, whose non-global key blocks run longest column first
+__device__ __forceinline__ Item decode(const BwdArgs& a, int v, const int32_t* ptr, bool kv) {
   Item it;
   it.bh = v / a.items_per_bh;
   const int r = v - it.bh * a.items_per_bh;
@@ -66,7 +68,7 @@ __device__ __forceinline__ Item decode(const BwdArgs& a, int v, const int32_t* p
   it.start = 0;
   it.len = -1;
   if (r < ng) {
-    it.blk = a.ngblk[r];
+    it.blk = kv ? a.kv_order[(int64_t)it.h * ng + r] : a.ngblk[r];
   } else {
     const int gi = (r - ng) / a.nseg;
     const int s = (r - ng) - gi * a.nseg;
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
 
   const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
   if (v < 0) return;
-  const Item it = decode(a, v, a.row_ptr);
+  const Item it = decode(a, v, a.row_ptr, false);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)it.bh * a.n * kHead;
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
 
   const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
   if (v < 0) return;
-  const Item it = decode(a, v, a.csc_ptr);
+  const Item it = decode(a, v, a.csc_ptr, true);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)it.bh * a.n * kHead;
@@ -422,7 +424,7 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, co
   a.part_kv = sp.split ? (float*)(w + off + nslots * kTile * sizeof(float)) : nullptr;
   a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
   a.csc_ptr = L->d_csc_ptr; a.csc_idx = L->d_csc_idx;
-  a.gblk = L->d_gblk; a.ngblk = L->d_ngblk;
+  a.gblk = L->d_gblk; a.ngblk = L->d_ngblk; a.kv_order = L->d_kv_order;
   a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
   a.seg = sp.seg; a.nseg = sp.nseg; a.split = sp.split;
   a.items_per_bh = (L->nb - L->g) + L->g * sp.nseg;

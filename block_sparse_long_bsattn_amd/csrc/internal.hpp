@@ -18,6 +18,7 @@ struct bsattn_layout {
   std::vector<int32_t> ngblk;    // non-global blocks ascending (host copy)
   std::vector<int32_t> row_len;  // length of each query-block row (host copy)
   int cus = 256;                 // compute units of the device (sizes the segment plan)
+  int max_lds = 65536;           // LDS bytes one work-group may use on the device
   // device arrays (owned)
   int32_t* d_gblk = nullptr;     // [g]
   int32_t* d_ngblk = nullptr;    // [nb - g] non-global block ids, ascending
@@ -26,6 +27,10 @@ struct bsattn_layout {
   int32_t* d_csc_ptr = nullptr;  // [heads*nb + 1]
   int32_t* d_csc_idx = nullptr;  // [heads*nnz_per_head]
   uint32_t* d_rbits = nullptr;   // [heads][nb][ceil(nb/32)] random picks, zero between builds
+  int32_t* d_kv_order = nullptr; // [heads][nb - g] non-global key blocks, longest column
+                                 // first (the dK/dV work order; ascending until a build
+                                 // kernel that sorts has run)
+  std::vector<int32_t> kv_order_init;
 };
 
 // How one call cuts the full-length (global) rows and columns into work items:

@@ -458,10 +458,11 @@ template <int W, int RMAX>
 __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     const int32_t* __restrict__ Gglob, int g, int nb, int w, int r, uint64_t seed,
     int64_t nnz_per_head, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
-    int32_t* __restrict__ csc_ptr, int32_t* __restrict__ csc_idx) {
+    int32_t* __restrict__ csc_ptr, int32_t* __restrict__ csc_idx, int32_t* __restrict__ kv_order) {
   // dynamic LDS: random picks per key block (nb x wpc words, bit i = query block
-  // i), the global list G[g], then every column's offset within the head
-  extern __shared__ int32_t dyn[];
+  // i), the global list G[g], every column's offset within the head, then every
+  // column's length
+  extern __shared__ __attribute__((aligned(16))) int32_t dyn[];
   __shared__ uint32_t sGb[2 * W];
   __shared__ int part[kBuildThreads / 64];
   const int h = blockIdx.x, tid = threadIdx.x;
@@ -469,7 +470,11 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
   uint32_t* colmap = reinterpret_cast<uint32_t*>(dyn);
   int32_t* sG = dyn + nb * wpc;
   int32_t* sColPos = sG + g;
+  int32_t* sColLen = sColPos + nb;                 // column lengths
+  uint32_t* sBk = reinterpret_cast<uint32_t*>(sColLen + nb);   // [nb + 1][wpc] columns by length
+  int32_t* sBase = reinterpret_cast<int32_t*>(sBk + (nb + 1) * wpc);   // [nb + 1] first rank
   for (int x = tid; x < nb * wpc; x += kBuildThreads) colmap[x] = 0u;
+  for (int x = tid; x < (nb + 1) * wpc; x += kBuildThreads) sBk[x] = 0u;
   for (int x = tid; x < g; x += kBuildThreads) sG[x] = Gglob[x];
   if (tid < 2 * W) sGb[tid] = 0u;
   __syncthreads();
@@ -549,12 +554,40 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     const int64_t p = (int64_t)h * nnz_per_head + pos;
     csc_ptr[(int64_t)h * nb + j] = (int32_t)p;
     sColPos[j] = pos;
+    sColLen[j] = len;
+    if (!bit_of(gb, j)) atomicOr(&sBk[len * wpc + (j >> 5)], 1u << (j & 31));
     if (!bit_of(gb, j)) write_bits(c, csc_idx + p);
     pos += len;
   }
   if (h == gridDim.x - 1 && tid == kBuildThreads - 1)
     csc_ptr[(int64_t)gridDim.x * nb] = (int32_t)((int64_t)gridDim.x * nnz_per_head);
   __syncthreads();
+
+  // work order of the non-global key blocks for dK/dV: longest column first, ties
+  // by block index.  sBk[L] holds the columns of length L as a bitmap; the rank of
+  // column j is the count of longer columns plus the columns of its length before
+  // it.
+  {
+    const int bper = (nb + 1 + kBuildThreads - 1) / kBuildThreads;
+    const int d0 = min(nb + 1, tid * bper), d1 = min(nb + 1, d0 + bper);   // L = nb - d
+    int cnt = 0;
+    for (int d = d0; d < d1; ++d)
+      for (int x = 0; x < wpc; ++x) cnt += __popc(sBk[(nb - d) * wpc + x]);
+    int base = block_exclusive_scan(cnt, part);
+    for (int d = d0; d < d1; ++d) {
+      sBase[nb - d] = base;
+      for (int x = 0; x < wpc; ++x) base += __popc(sBk[(nb - d) * wpc + x]);
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < nb; j += kBuildThreads) {
+    if (bit_of(gb, j)) continue;
+    const uint32_t* bk = sBk + sColLen[j] * wpc;
+    int rank = sBase[sColLen[j]];
+    for (int x = 0; x < (j >> 5); ++x) rank += __popc(bk[x]);
+    rank += __popc(bk[j >> 5] & ((1u << (j & 31)) - 1u));
+    kv_order[(int64_t)h * (nb - g) + rank] = j;
+  }
 
   // global rows and columns hold every block
   for (int e = tid; e < g * nb; e += kBuildThreads) {
@@ -619,15 +652,22 @@ int launch_layout_rowptr(bsattn_layout* L, hipStream_t stream) {
 }
 
 namespace {
+// Dynamic LDS of layout_head_kernel: random picks, global list, column offsets and
+// lengths, columns by length, first rank per length.
+size_t head_lds_bytes(const bsattn_layout* L) {
+  const int wpc = (L->nb + 31) / 32;
+  return ((size_t)L->nb * wpc + L->g + 2 * L->nb + (size_t)(L->nb + 1) * (wpc + 1)) *
+         sizeof(int32_t);
+}
+
 template <int W, int RMAX>
 int launch_head(bsattn_layout* L, hipStream_t stream) {
-  const int wpc = (L->nb + 31) / 32;
-  const size_t lds = ((size_t)L->nb * wpc + L->g + L->nb) * sizeof(int32_t);
+  const size_t lds = head_lds_bytes(L);
   {
     ProfScope prof_("layout_head", stream);
     hipLaunchKernelGGL((layout_head_kernel<W, RMAX>), dim3(L->heads), dim3(kBuildThreads), lds,
                        stream, L->d_gblk, L->g, L->nb, L->w, L->r, L->seed, L->nnz_per_head,
-                       L->d_row_ptr, L->d_col_idx, L->d_csc_ptr, L->d_csc_idx);
+                       L->d_row_ptr, L->d_col_idx, L->d_csc_ptr, L->d_csc_idx, L->d_kv_order);
   }
   return check_hip(hipGetLastError(), "layout_head launch");
 }
@@ -663,7 +703,7 @@ int launch_rows_cols(bsattn_layout* L, hipStream_t stream) {
 }  // namespace
 
 int launch_layout_build(bsattn_layout* L, hipStream_t stream) {
-  if (L->nb <= kLdsBitmapNb)
+  if (L->nb <= kLdsBitmapNb && head_lds_bytes(L) <= (size_t)L->max_lds)
     return L->r <= kFastR ? launch_head_r<kFastR>(L, stream) : launch_head_r<kMaxR>(L, stream);
   return L->g <= kRegG ? launch_rows_cols<GReg>(L, stream) : launch_rows_cols<GLds>(L, stream);
 }

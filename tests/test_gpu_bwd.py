@@ -42,6 +42,8 @@ def run_bwd(n, heads, bsz, G, w, r, seed):
     (64, 1, 2, [0], 1, 3),            # single block
     (576, 2, 1, [4], 5, 2),           # interior global block, wider window
     (1536, 1, 1, [0, 5, 23], 3, 20),  # many random blocks
+    (6400, 1, 1, [0, 99], 3, 3),      # 100 blocks: dK/dV order from 2-word bitmaps
+    (9600, 1, 1, [0, 149], 3, 5),     # 150 blocks: 4-word bitmaps
 ])
 def test_bwd_full_compare(case):
     n, heads, bsz, G, w, r = case

@@ -62,6 +62,7 @@ def test_layout_edge_cases_bit_exact():
     compare(64 * 40, 3, [2], 3, 9, 97)               # more than 8 random blocks
     compare(64 * 600, 1, list(range(0, 600, 50)), 3, 3, 96)   # > 512 blocks, > 8 global
     compare(64 * 100, 2, list(range(3, 100, 9)), 5, 4, 95)    # > 8 global blocks
+    compare(64 * 512, 1, [0, 511], 3, 3, 94)         # 512 blocks: largest one-kernel layout
 
 
 def test_layout_rebuild_matches_new_seed():
