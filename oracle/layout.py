@@ -30,6 +30,10 @@ What the pages leave open, and the reading taken here
   for t < min(r, m), swap C[t] with C[t + (u_t mod (m - t))]; the first
   min(r, m) entries are the random blocks.
 * One layout per head, shared by every batch element.
+* Sequence length not a multiple of b: App. D eq. (13) counts ceil(n/b) blocks.
+  The last block then holds n - b*(ceil(n/b) - 1) tokens; the layout is the same
+  block pattern over ceil(n/b) blocks, and the missing positions of the last
+  block are simply not tokens (no query, no key; nothing is padded).
 """
 
 from __future__ import annotations
@@ -83,18 +87,18 @@ def row_blocks(h: int, i: int, nb: int, global_blocks, w: int, r: int,
 
 def check_args(n: int, b: int, heads: int, global_blocks, w: int, r: int) -> int:
     """Validate the pattern arguments; return nb.  Raises ValueError."""
-    if b <= 0 or n <= 0 or n % b != 0:
-        raise ValueError("n must be a positive multiple of b")
+    if b <= 0 or n <= 0:
+        raise ValueError("n and b must be positive")
     if heads <= 0:
         raise ValueError("heads must be positive")
     if w < 1 or w % 2 == 0:
         raise ValueError("w must be odd and >= 1")
     if r < 0:
         raise ValueError("r must be >= 0")
-    nb = n // b
+    nb = -(-n // b)                  # ceil(n / b): the last block may be shorter
     g = list(global_blocks)
     if any(not (0 <= x < nb) for x in g) or g != sorted(set(g)):
-        raise ValueError("global blocks must be sorted, unique and inside [0, n/b)")
+        raise ValueError("global blocks must be sorted, unique and inside [0, ceil(n/b))")
     return nb
 
 
@@ -147,6 +151,9 @@ def block_mask(rows_h, nb: int) -> np.ndarray:
     return m
 
 
-def token_mask(rows_h, nb: int, b: int) -> np.ndarray:
-    """n x n boolean: token p may attend to token q iff block(q) is in N(block(p))."""
-    return np.kron(block_mask(rows_h, nb), np.ones((b, b), dtype=bool)).astype(bool)
+def token_mask(rows_h, nb: int, b: int, n: int | None = None) -> np.ndarray:
+    """n x n boolean: token p may attend to token q iff block(q) is in N(block(p)).
+    n defaults to nb * b; a shorter n drops the positions past the end."""
+    m = np.kron(block_mask(rows_h, nb), np.ones((b, b), dtype=bool)).astype(bool)
+    n = nb * b if n is None else n
+    return m[:n, :n]

@@ -128,7 +128,9 @@ def test_block_and_token_mask():
 
 def test_bad_arguments_rejected():
     with pytest.raises(ValueError):
-        L.build_layout(500, 64, 1, [0], 3, 3, 0)      # n not a multiple of b
+        L.build_layout(0, 64, 1, [], 3, 3, 0)         # empty sequence
+    with pytest.raises(ValueError):
+        L.build_layout(500, 64, 1, [8], 3, 3, 0)      # block 8 past ceil(500/64) = 8
     with pytest.raises(ValueError):
         L.build_layout(512, 64, 1, [0], 2, 3, 0)      # even window
     with pytest.raises(ValueError):
@@ -192,3 +194,31 @@ def test_expected_random_indegree():
             expect[j] += min(r, len(cand)) / len(cand)
     assert np.max(np.abs(hits / trials - expect)) < 0.25
     assert math.isclose(hits.sum() / trials, expect.sum(), rel_tol=1e-12)
+
+
+# --- sequences that end inside a block ----------------------------------------
+
+@pytest.mark.parametrize("n,G,w,r", [(1000, [0, 15], 3, 3), (4000, [0, 62], 3, 3),
+                                     (130, [2], 1, 2), (700, [], 5, 4)])
+def test_ragged_length_pairs_closed_form(n, G, w, r):
+    """ceil(n/b) blocks, the last one short: each query block i contributes
+    rows(i) * sum of the sizes of the blocks in N(i), sizes b except the last."""
+    b = 64
+    lay = L.build_layout(n, b, 2, G, w, r, 3)
+    nb = lay["nb"]
+    assert nb == (n + b - 1) // b
+    size = [b] * (nb - 1) + [n - b * (nb - 1)]
+    for h in range(2):
+        want = sum(size[i] * sum(size[j] for j in lay["rows"][h][i]) for i in range(nb))
+        assert int(L.token_mask(lay["rows"][h], nb, b, n).sum()) == want
+
+
+def test_ragged_length_is_the_padded_pattern_cut_to_n():
+    """The layout depends on ceil(n/b) only: the mask of n tokens is the mask of
+    the padded length with the positions past n removed."""
+    n, b = 1000, 64
+    lay = L.build_layout(n, b, 1, [0, 15], 3, 3, 9)
+    pad = L.build_layout(16 * b, b, 1, [0, 15], 3, 3, 9)
+    assert lay["rows"] == pad["rows"]
+    full = L.token_mask(pad["rows"][0], 16, b)
+    assert np.array_equal(L.token_mask(lay["rows"][0], 16, b, n), full[:n, :n])
