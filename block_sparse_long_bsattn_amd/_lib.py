@@ -166,6 +166,9 @@ def _int32_array(values):
 
 # --- layout -------------------------------------------------------------------
 
+_layout_n = {}   # layout handle -> sequence length it was built for
+
+
 def bsattn_layout_build(n, b, heads, global_blocks, w, r, seed, stream=None) -> int:
     """Returns an opaque layout handle (an int); free it with bsattn_layout_destroy."""
     arr, g = _int32_array(global_blocks)
@@ -173,7 +176,13 @@ def bsattn_layout_build(n, b, heads, global_blocks, w, r, seed, stream=None) -> 
     _check(load().bsattn_layout_build(n, b, heads, arr if g else None, g, w, r,
                                       c_uint64(seed & (2**64 - 1)), _stream(stream),
                                       ctypes.byref(out)), "bsattn_layout_build")
+    _layout_n[out.value] = n
     return out.value
+
+
+def _layout_len(layout, nb):
+    """Sequence length of a layout (tensors are [B, H, n, d]); nb * 64 if unknown."""
+    return _layout_n.get(layout, nb * 64)
 
 
 def bsattn_layout_rebuild(layout, seed, stream=None) -> None:
@@ -204,6 +213,7 @@ def bsattn_layout_to_host(layout):
 
 def bsattn_layout_destroy(layout) -> None:
     _check(load().bsattn_layout_destroy(layout), "bsattn_layout_destroy")
+    _layout_n.pop(layout, None)
 
 
 # --- BigBird forward / backward -------------------------------------------------
@@ -220,7 +230,7 @@ def bsattn_fwd(layout, q, k, v, o, lse=None, workspace=None, scale=None, stream=
     """Tensors [B, H, n, d] on the GPU (bf16 or fp32); lse float32 [B, H, n] or None."""
     bsz, _, _, d = q.shape
     nb, heads, _ = bsattn_layout_info(layout)
-    shape = (bsz, heads, nb * 64, d)
+    shape = (bsz, heads, _layout_len(layout, nb), d)
     need = bsattn_fwd_workspace(layout, bsz, d) if _dtype_code(q) == BSATTN_BF16 else 0
     _check_tensors("bsattn_fwd", shape, q.dtype, (("q", q), ("k", k), ("v", v), ("o", o)),
                    lse, workspace, need)
@@ -235,7 +245,7 @@ def bsattn_bwd(layout, q, k, v, o, lse, dout, dq, dk, dv, workspace=None, scale=
                stream=None) -> None:
     bsz, _, _, d = q.shape
     nb, heads, _ = bsattn_layout_info(layout)
-    shape = (bsz, heads, nb * 64, d)
+    shape = (bsz, heads, _layout_len(layout, nb), d)
     if lse is None:
         raise ValueError("bsattn_bwd: lse is required")
     _check_tensors("bsattn_bwd", shape, q.dtype,

@@ -173,8 +173,11 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
   if (out == nullptr) return set_error(BSATTN_EINVAL, "layout_build: out is null");
   *out = nullptr;
   if (b != kBlock) return set_error(BSATTN_EUNSUPPORTED, "layout_build: block size must be 64");
-  if (n <= 0 || n % b != 0) return set_error(BSATTN_EINVAL, "layout_build: n must be a positive multiple of b");
-  const int nb = n / b;
+  if (n <= 0) return set_error(BSATTN_EINVAL, "layout_build: n must be positive");
+  if (n > kMaxNb * kBlock) return set_error(BSATTN_EUNSUPPORTED, "layout_build: n/b above 4096");
+  // ceil(n / b) blocks ([BB] App. D eq. (13)); the last one is short when b does
+  // not divide n, and its missing positions are not tokens (nothing is padded)
+  const int nb = (n + b - 1) / b;
   if (nb > kMaxNb) return set_error(BSATTN_EUNSUPPORTED, "layout_build: n/b above 4096");
   if (heads < 1) return set_error(BSATTN_EINVAL, "layout_build: heads must be >= 1");
   if (w < 1 || w % 2 == 0) return set_error(BSATTN_EINVAL, "layout_build: w must be odd and >= 1");

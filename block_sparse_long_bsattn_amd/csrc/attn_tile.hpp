@@ -73,6 +73,18 @@ __device__ __forceinline__ void qk_tile(const uint16_t* sK, const bf16x8 (&qB)[4
   }
 }
 
+// Keys kmin.. of an S^T tile (s0: keys 0..31, s1: keys 32..63, register r <-> key
+// 8*(r/4) + 4*hl + r%4) set to -inf: the positions past the end of a sequence
+// that ends inside the tile's block.
+__device__ __forceinline__ void mask_keys_from(f32x16& s0, f32x16& s1, int hl, int kmin) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int x = 8 * (r >> 2) + 4 * hl + (r & 3);
+    if (x >= kmin) s0[r] = -INFINITY;
+    if (32 + x >= kmin) s1[r] = -INFINITY;
+  }
+}
+
 // Online softmax over one key tile whose scores s = S' - m_c arrive relative to the
 // seeded reference m_c (log2 units; -inf marks an excluded key).  The reference
 // only moves when a block's maximum exceeds it by more than kRescaleSlack, so the

@@ -46,9 +46,19 @@ struct BwdArgs {
   const int32_t* ngblk;
   const int32_t* kv_order;   // [heads][nb - g] dK/dV order of the non-global key blocks
   int heads, n, nb, g, seg, nseg, split;
+  int last_rows;   // tokens in the last block: n - 64 (nb - 1), 1..64
   int items_per_bh, total_items;
   float scale, sl2;
 };
+
+// Tile loads for a sequence that may end inside its last block: that block's
+// missing rows are not read and stage as zeros.
+__device__ __forceinline__ void load_block(TileRegs& r, const uint16_t* base, int blk,
+                                           const BwdArgs& a, int tid) {
+  const uint16_t* g = base + (size_t)blk * kBlock * kHead;
+  if (a.last_rows < kBlock && blk == a.nb - 1) gload_nat_rows(r, g, tid, a.last_rows);
+  else gload_nat(r, g, tid);
+}
 
 struct Item {
   int bh, h, blk, start, len, slot, seg;
@@ -101,23 +111,28 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   const int32_t* keys = a.col_idx + it.start;
   const uint16_t* kbase = a.k + bh_off;
   const uint16_t* vbase = a.v + bh_off;
+  // Keys past the end of a sequence that ends inside its last block stage as zero
+  // rows of K and V, which give them dP = 0 and no dQ contribution; query rows past
+  // the end read nothing and write nothing.
   TileRegs kr, vr;
   if (it.len > 0) {
     const int kb = keys[0];
-    gload_nat(kr, kbase + (size_t)kb * kBlock * kHead, tid);
-    gload_nat(vr, vbase + (size_t)kb * kBlock * kHead, tid);
+    load_block(kr, kbase, kb, a, tid);
+    load_block(vr, vbase, kb, a, tid);
   }
   // block index of the next tile, read one iteration ahead of its use
   int kb_next = it.len > 1 ? keys[1] : 0;
+  const bool qvalid = qrow < a.n;
   bf16x8 qB[4], doB[4];
   float dsum = 0.f;
   {
     const size_t off = bh_off + (size_t)qrow * kHead + 8 * hl;
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4 qv = ldg16(a.q + off + 16 * c);
-      const u32x4 dv = ldg16(a.dout + off + 16 * c);
-      const u32x4 ov = ldg16(a.o + off + 16 * c);
+      const u32x4 qv = qvalid ? ldg16(a.q + off + 16 * c) : z;
+      const u32x4 dv = qvalid ? ldg16(a.dout + off + 16 * c) : z;
+      const u32x4 ov = qvalid ? ldg16(a.o + off + 16 * c) : z;
       qB[c] = __builtin_bit_cast(bf16x8, qv);
       doB[c] = __builtin_bit_cast(bf16x8, dv);
 #pragma unroll
@@ -128,11 +143,11 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     }
   }
   const float Dq = partner_sum(dsum);   // D = rowsum(dO * O)
-  if (it.seg == 0 && hl == 0) a.dbuf[(size_t)it.bh * a.n + qrow] = Dq;
+  if (it.seg == 0 && hl == 0 && qvalid) a.dbuf[(size_t)it.bh * a.n + qrow] = Dq;
   // Q pre-scaled by scale*log2(e) exactly as in the forward, and the accumulators
   // seeded so that the MFMAs return S*scale*log2(e) - lse*log2(e) and dP - D
   scale_operands(qB, a.sl2);
-  const float lse2 = a.lse[(size_t)it.bh * a.n + qrow] * kLog2e;
+  const float lse2 = qvalid ? a.lse[(size_t)it.bh * a.n + qrow] * kLog2e : 0.f;
   f32x16 seed_s, seed_d;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -148,8 +163,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
     const bool more = t + 1 < it.len;
     if (more) {
-      gload_nat(kr, kbase + (size_t)kb_next * kBlock * kHead, tid);
-      gload_nat(vr, vbase + (size_t)kb_next * kBlock * kHead, tid);
+      load_block(kr, kbase, kb_next, a, tid);
+      load_block(vr, vbase, kb_next, a, tid);
       kb_next = t + 2 < it.len ? keys[t + 2] : 0;
     }
     // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
@@ -185,6 +200,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
 
   const float sc = a.scale;
   if (it.slot < 0) {
+    if (!qvalid) return;
     uint16_t* op = a.dq + bh_off + (size_t)qrow * kHead + 4 * hl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -228,23 +244,34 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   const uint16_t* dobase = a.dout + bh_off;
   const float* lbase = a.lse + (size_t)it.bh * a.n;
   const float* dbase = a.dbuf + (size_t)it.bh * a.n;
+  // Query rows past the end of a sequence that ends inside its last block stage as
+  // zero rows of Q and dO with lse = +inf and D = 0, so that P = 0 and dS = 0 there;
+  // key rows past the end read nothing and write nothing.
   TileRegs qr, dr;
   float lv = 0.f, dval = 0.f;
+  auto load_rowvals = [&](int qb) {
+    if (tid < kBlock) {
+      const bool ok = qb * kBlock + tid < a.n;
+      lv = ok ? lbase[qb * kBlock + tid] : INFINITY;
+      dval = ok ? dbase[qb * kBlock + tid] : 0.f;
+    }
+  };
   if (it.len > 0) {
     const int qb = qblks[0];
-    gload_nat(qr, qbase + (size_t)qb * kBlock * kHead, tid);
-    gload_nat(dr, dobase + (size_t)qb * kBlock * kHead, tid);
-    if (tid < kBlock) { lv = lbase[qb * kBlock + tid]; dval = dbase[qb * kBlock + tid]; }
+    load_block(qr, qbase, qb, a, tid);
+    load_block(dr, dobase, qb, a, tid);
+    load_rowvals(qb);
   }
   // block index of the next tile, read one iteration ahead of its use
   int qb_next = it.len > 1 ? qblks[1] : 0;
+  const bool kvalid = krow < a.n;
   bf16x8 kB[4], vB[4];
   {
     const size_t off = bh_off + (size_t)krow * kHead + 8 * hl;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      kB[c] = ld16(a.k + off + 16 * c);
-      vB[c] = ld16(a.v + off + 16 * c);
+      kB[c] = kvalid ? ld16(a.k + off + 16 * c) : bf16x8{};
+      vB[c] = kvalid ? ld16(a.v + off + 16 * c) : bf16x8{};
     }
   }
   // K pre-scaled by scale*log2(e) (the products match the forward's scaled-Q ones
@@ -263,9 +290,9 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
     const bool more = t + 1 < it.len;
     if (more) {
-      gload_nat(qr, qbase + (size_t)qb_next * kBlock * kHead, tid);
-      gload_nat(dr, dobase + (size_t)qb_next * kBlock * kHead, tid);
-      if (tid < kBlock) { lv = lbase[qb_next * kBlock + tid]; dval = dbase[qb_next * kBlock + tid]; }
+      load_block(qr, qbase, qb_next, a, tid);
+      load_block(dr, dobase, qb_next, a, tid);
+      load_rowvals(qb_next);
       qb_next = t + 2 < it.len ? qblks[t + 2] : 0;
     }
     // S[q][key] = Q K^T, dP[q][key] = dO V^T; rows = queries (2 tiles), column = key.
@@ -323,6 +350,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
 
   const float sc = a.scale;
   if (it.slot < 0) {
+    if (!kvalid) return;
     const size_t off = bh_off + (size_t)krow * kHead + 4 * hl;
     uint16_t* kp = a.dk + off;
     uint16_t* vp = a.dv + off;
@@ -385,6 +413,8 @@ __global__ __launch_bounds__(256) void bs_bwd_reduce_kernel(
       acc[e] += x[0]; acc[e + 1] += x[1]; acc[e + 2] += x[2]; acc[e + 3] += x[3];
     }
   }
+  // rows past the end of a sequence that ends inside this block are not written
+  if (gblk[gi] * kBlock + e0 / kHead >= n) return;
   uint16_t* dst = kind == 0 ? dq : (kind == 1 ? dk : dv);
   dst += ((size_t)bh * n + (size_t)gblk[gi] * kBlock) * kHead + e0;
 #pragma unroll
@@ -426,6 +456,7 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, co
   a.csc_ptr = L->d_csc_ptr; a.csc_idx = L->d_csc_idx;
   a.gblk = L->d_gblk; a.ngblk = L->d_ngblk; a.kv_order = L->d_kv_order;
   a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
+  a.last_rows = L->n - kBlock * (L->nb - 1);
   a.seg = sp.seg; a.nseg = sp.nseg; a.split = sp.split;
   a.items_per_bh = (L->nb - L->g) + L->g * sp.nseg;
   a.total_items = batch * L->heads * a.items_per_bh;

@@ -39,6 +39,7 @@ struct FwdArgs {
   const int32_t* gblk;
   const int32_t* ngblk;
   int heads, n, nb, g, seg, nseg, split;
+  int last_rows;   // tokens in the last block: n - 64 (nb - 1), 1..64
   int items_per_bh, total_items;
   float sl2;  // scale * log2(e)
 };
@@ -98,19 +99,31 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   const int len = it.len;
   auto kaddr = [&](int kb) { return kbase + (size_t)kb * kBlock * kHead; };
   auto vaddr = [&](int kb) { return vbase + (size_t)kb * kBlock * kHead; };
+  // a sequence that ends inside its last block: that block's missing rows are
+  // neither read nor attended to, and no output is written for them
+  const bool ragged = a.last_rows < kBlock;
+  auto tile_load = [&](int kb, TileRegs& kr, TileRegs& vr) {
+    if (ragged && kb == a.nb - 1) {
+      gload_nat_rows(kr, kaddr(kb), tid, a.last_rows);
+      gload_nat_rows(vr, vaddr(kb), tid, a.last_rows);
+    } else {
+      gload_nat(kr, kaddr(kb), tid);
+      gload_nat(vr, vaddr(kb), tid);
+    }
+  };
 
   TileRegs kr, vr;
+  int kb_cur = 0;
   if (len > 0) {
-    const int kb = keys[0];
-    gload_nat(kr, kaddr(kb), tid);
-    gload_nat(vr, vaddr(kb), tid);
+    kb_cur = keys[0];
+    tile_load(kb_cur, kr, vr);
   }
   int kb_next = len > 1 ? keys[1] : 0;
   bf16x8 qB[4];
   {
     const uint16_t* qp = a.q + bh_off + (size_t)qrow * kHead + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
+    for (int c = 0; c < 4; ++c) qB[c] = qrow < a.n ? ld16(qp + 16 * c) : bf16x8{};
   }
   scale_operands(qB, a.sl2);
   lds_store_nat(sK[0], kr, tid);
@@ -123,9 +136,10 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
     const bool more = t + 1 < len;
     f32x16 s0, s1;
     qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
+    if (ragged && kb_cur == a.nb - 1) mask_keys_from(s0, s1, hl, a.last_rows);
+    const int kb_after = kb_next;   // block of tile t + 1
     if (more) {
-      gload_nat(kr, kaddr(kb_next), tid);
-      gload_nat(vr, vaddr(kb_next), tid);
+      tile_load(kb_next, kr, vr);
       kb_next = t + 2 < len ? keys[t + 2] : 0;
     }
     // V^T operands read now; the softmax covers their LDS latency
@@ -139,11 +153,13 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
       lds_store_nat(sK[cur ^ 1], kr, tid);
       lds_store_nat(sV[cur ^ 1], vr, tid);
     }
+    kb_cur = kb_after;
   }
 
   const float l_tot = partner_sum(st.l);
   if (it.slot < 0) {
-    write_o_bf16(st, l_tot, hl, a.o + bh_off + (size_t)qrow * kHead,
+    if (qrow < a.n)
+      write_o_bf16(st, l_tot, hl, a.o + bh_off + (size_t)qrow * kHead,
                  a.lse != nullptr ? a.lse + (size_t)it.bh * a.n + qrow : nullptr);
   } else {
     write_partial(st, l_tot, hl, 32 * wave + col, a.part + (size_t)it.slot * kPartFloats);
@@ -161,6 +177,7 @@ __global__ __launch_bounds__(256) void bs_fwd_combine_kernel(
   float acc[16], M, L;
   merge_partials(part + (size_t)idx * nseg * kPartFloats, nseg, row, dq, acc, M, L);
   const int tok = gblk[gi] * kBlock + row;
+  if (tok >= n) return;   // past the end of a sequence that ends inside this block
   store16_bf16(o + ((size_t)bh * n + tok) * kHead + dq, acc, 1.f / L);
   if (lse != nullptr && (threadIdx.x & 3) == 0)
     lse[(size_t)bh * n + tok] = (M + __log2f(L)) * kLn2;
@@ -183,6 +200,7 @@ struct FwdF32Args {
   const int32_t* row_ptr;
   const int32_t* col_idx;
   int heads, n, nb, total_items;
+  int last_rows;   // tokens in the last block: n - 64 (nb - 1), 1..64
   float scale;
 };
 
@@ -191,9 +209,15 @@ constexpr int kF32Stride = kHead + 4;
 // one 64x64 fp32 tile: 4 float4 per thread, row-major global -> padded LDS rows
 struct TileF32 { f32x4 v[4]; };
 
-__device__ __forceinline__ void load_f32_tile(TileF32& t, const float* g, int tid) {
+// rows at or past `rows` (the end of a sequence inside the last block) are not
+// read and stage as zeros
+__device__ __forceinline__ void load_f32_tile(TileF32& t, const float* g, int tid, int rows) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) t.v[u] = *reinterpret_cast<const f32x4*>(g + 4 * tid + 1024 * u);
+  for (int u = 0; u < 4; ++u) {
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if ((4 * tid + 1024 * u) / kHead < rows) x = *reinterpret_cast<const f32x4*>(g + 4 * tid + 1024 * u);
+    t.v[u] = x;
+  }
 }
 
 __device__ __forceinline__ void store_f32_tile(float* s, const TileF32& t, int tid) {
@@ -225,9 +249,10 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
   const int bh = v / a.nb, i = v - bh * a.nb, h = bh % a.heads;
   const int tid = threadIdx.x, tq = tid >> 4, tk = tid & 15;
   const size_t bh_off = (size_t)bh * a.n * kHead;
+  auto rows_of = [&](int blk) { return blk == a.nb - 1 ? a.last_rows : kBlock; };
   {
     TileF32 qt;
-    load_f32_tile(qt, a.q + bh_off + (size_t)i * kBlock * kHead, tid);
+    load_f32_tile(qt, a.q + bh_off + (size_t)i * kBlock * kHead, tid, rows_of(i));
     store_f32_tile(sQ, qt, tid);
   }
 
@@ -244,17 +269,18 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
   TileF32 kt, vt;
   if (rp0 < rp1) {
     const int kb = a.col_idx[rp0];
-    load_f32_tile(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid);
-    load_f32_tile(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid);
+    load_f32_tile(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
+    load_f32_tile(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
   }
   for (int e = rp0; e < rp1; ++e) {
+    const int krows = rows_of(a.col_idx[e]);   // keys of this block that are tokens
     __syncthreads();   // the previous block's P (in sK) and V are no longer read
     store_f32_tile(sK, kt, tid);
     store_f32_tile(sV, vt, tid);
     if (e + 1 < rp1) {
       const int kb = a.col_idx[e + 1];
-      load_f32_tile(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid);
-      load_f32_tile(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid);
+      load_f32_tile(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
+      load_f32_tile(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
     }
     __syncthreads();
     // S = Q K^T for queries 4tq+r, keys 4tk+j
@@ -283,7 +309,7 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        s[r][j] *= a.scale;
+        s[r][j] = 4 * tk + j < krows ? s[r][j] * a.scale : -INFINITY;
         mx = fmaxf(mx, s[r][j]);
       }
       const float m_new = fmaxf(m[r], group16_max(mx));
@@ -324,6 +350,7 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int tok = i * kBlock + 4 * tq + r;
+    if (tok >= a.n) break;
     const float inv = 1.f / l[r];
     const f32x4 w = {acc[r][0] * inv, acc[r][1] * inv, acc[r][2] * inv, acc[r][3] * inv};
     *reinterpret_cast<f32x4*>(a.o + bh_off + (size_t)tok * kHead + 4 * tk) = w;
@@ -349,6 +376,7 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
     a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
     a.heads = L->heads; a.n = L->n; a.nb = L->nb;
     a.total_items = bhn * L->nb;
+    a.last_rows = L->n - kBlock * (L->nb - 1);
     a.scale = scale;
     const int grid = 8 * ((a.total_items + 7) / 8);
     {
@@ -363,6 +391,7 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
   a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
   a.gblk = L->d_gblk; a.ngblk = L->d_ngblk;
   a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
+  a.last_rows = L->n - kBlock * (L->nb - 1);
   const SegPlan sp = seg_plan(L, batch);
   a.seg = sp.seg; a.nseg = sp.nseg; a.split = sp.split;
   a.items_per_bh = (L->nb - L->g) + L->g * sp.nseg;

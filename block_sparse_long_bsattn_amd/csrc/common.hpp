@@ -113,6 +113,18 @@ __device__ __forceinline__ void gload_nat(TileRegs& r, const uint16_t* g, int ti
   for (int u = 0; u < 4; ++u) r.v[u] = ldg16(g + (row + 16 * u) * kHead + 8 * c);
 }
 
+// The same for the last block of a sequence that ends inside it: only its first
+// `rows` rows are tokens; the others are not read and are staged as zeros.
+__device__ __forceinline__ void gload_nat_rows(TileRegs& r, const uint16_t* g, int tid, int rows) {
+  const int c = tid & 7, row = tid >> 3;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row + 16 * u < rows) x = ldg16(g + (row + 16 * u) * kHead + 8 * c);
+    r.v[u] = x;
+  }
+}
+
 __device__ __forceinline__ void lds_store_nat(uint16_t* s, const TileRegs& r, int tid) {
   const int c = tid & 7, row = tid >> 3;
 #pragma unroll

@@ -67,7 +67,7 @@ typedef struct bsattn_layout bsattn_layout;
 
 /*
  * Build the block layout of [BB] App. D on the device: for every head h and query
- * block i (nb = n / b blocks), the ascending key-block list
+ * block i (nb = ceil(n / b) blocks, [BB] App. D eq. (13)), the ascending key-block list
  *     N(i) = G  U  W_i  U  R_i      for i not in G,      N(i) = {0..nb-1} for i in G,
  * where G = global_blocks, W_i = { j : |i - j| <= (w-1)/2, 0 <= j < nb } and R_i
  * holds min(r, m) blocks drawn uniformly without replacement from the m blocks not
@@ -78,9 +78,12 @@ typedef struct bsattn_layout bsattn_layout;
  * it) is built too.  One layout serves every batch element.
  *
  *   n, b            sequence length and block size; b must be 64 (else
- *                   EUNSUPPORTED), n a positive multiple of b with n/b <= 4096.
+ *                   EUNSUPPORTED), n >= 1 with ceil(n/b) <= 4096.  When b does not
+ *                   divide n the last block holds n - b*(nb - 1) tokens: the layout
+ *                   is that of nb full blocks and the missing positions are simply
+ *                   not tokens (no query, no key; nothing is padded or written).
  *   heads           number of heads, >= 1; each head draws its own random blocks.
- *   global_blocks   HOST array of g block ids, sorted, unique, in [0, n/b);
+ *   global_blocks   HOST array of g block ids, sorted, unique, in [0, nb);
  *                   may be NULL when g == 0.
  *   w               window width in blocks, odd, >= 1.
  *   r               random blocks per query block, 0 <= r <= 64.

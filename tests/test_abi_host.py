@@ -53,7 +53,8 @@ def _build_status(n, b, heads, G, w, r):
 
 
 @pytest.mark.parametrize("args,code", [
-    ((500, 64, 1, [0], 3, 3), -1),          # n not a multiple of b
+    ((0, 64, 1, [], 3, 3), -1),             # empty sequence
+    ((500, 64, 1, [8], 3, 3), -1),          # block 8 past ceil(500/64) = 8 blocks
     ((512, 32, 1, [0], 3, 3), -2),          # block size other than 64
     ((512, 64, 0, [0], 3, 3), -1),          # no heads
     ((512, 64, 1, [0], 2, 3), -1),          # even window
