@@ -51,12 +51,14 @@ struct BwdArgs {
   float scale, sl2;
 };
 
-// Tile loads for a sequence that may end inside its last block: that block's
-// missing rows are not read and stage as zeros.
+// Tile loads for a sequence that may end inside its last block (kRagged): that
+// block's missing rows are not read and stage as zeros.  The kernels below are
+// instantiated with and without those guards; the whole-block instance has none.
+template <bool kRagged>
 __device__ __forceinline__ void load_block(TileRegs& r, const uint16_t* base, int blk,
                                            const BwdArgs& a, int tid) {
   const uint16_t* g = base + (size_t)blk * kBlock * kHead;
-  if (a.last_rows < kBlock && blk == a.nb - 1) gload_nat_rows(r, g, tid, a.last_rows);
+  if (kRagged && blk == a.nb - 1) gload_nat_rows(r, g, tid, a.last_rows);
   else gload_nat(r, g, tid);
 }
 
@@ -96,6 +98,7 @@ __device__ __forceinline__ Item decode(const BwdArgs& a, int v, const int32_t* p
   return it;
 }
 
+template <bool kRagged>
 __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
@@ -117,12 +120,12 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   TileRegs kr, vr;
   if (it.len > 0) {
     const int kb = keys[0];
-    load_block(kr, kbase, kb, a, tid);
-    load_block(vr, vbase, kb, a, tid);
+    load_block<kRagged>(kr, kbase, kb, a, tid);
+    load_block<kRagged>(vr, vbase, kb, a, tid);
   }
   // block index of the next tile, read one iteration ahead of its use
   int kb_next = it.len > 1 ? keys[1] : 0;
-  const bool qvalid = qrow < a.n;
+  const bool qvalid = !kRagged || qrow < a.n;
   bf16x8 qB[4], doB[4];
   float dsum = 0.f;
   {
@@ -163,8 +166,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
     const bool more = t + 1 < it.len;
     if (more) {
-      load_block(kr, kbase, kb_next, a, tid);
-      load_block(vr, vbase, kb_next, a, tid);
+      load_block<kRagged>(kr, kbase, kb_next, a, tid);
+      load_block<kRagged>(vr, vbase, kb_next, a, tid);
       kb_next = t + 2 < it.len ? keys[t + 2] : 0;
     }
     // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
@@ -225,6 +228,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+template <bool kRagged>
 __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kBlock * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t sO[2][kBlock * kLdsStride];   // dO
@@ -251,20 +255,20 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   float lv = 0.f, dval = 0.f;
   auto load_rowvals = [&](int qb) {
     if (tid < kBlock) {
-      const bool ok = qb * kBlock + tid < a.n;
+      const bool ok = !kRagged || qb * kBlock + tid < a.n;
       lv = ok ? lbase[qb * kBlock + tid] : INFINITY;
       dval = ok ? dbase[qb * kBlock + tid] : 0.f;
     }
   };
   if (it.len > 0) {
     const int qb = qblks[0];
-    load_block(qr, qbase, qb, a, tid);
-    load_block(dr, dobase, qb, a, tid);
+    load_block<kRagged>(qr, qbase, qb, a, tid);
+    load_block<kRagged>(dr, dobase, qb, a, tid);
     load_rowvals(qb);
   }
   // block index of the next tile, read one iteration ahead of its use
   int qb_next = it.len > 1 ? qblks[1] : 0;
-  const bool kvalid = krow < a.n;
+  const bool kvalid = !kRagged || krow < a.n;
   bf16x8 kB[4], vB[4];
   {
     const size_t off = bh_off + (size_t)krow * kHead + 8 * hl;
@@ -290,8 +294,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
     const bool more = t + 1 < it.len;
     if (more) {
-      load_block(qr, qbase, qb_next, a, tid);
-      load_block(dr, dobase, qb_next, a, tid);
+      load_block<kRagged>(qr, qbase, qb_next, a, tid);
+      load_block<kRagged>(dr, dobase, qb_next, a, tid);
       load_rowvals(qb_next);
       qb_next = t + 2 < it.len ? qblks[t + 2] : 0;
     }
@@ -465,13 +469,19 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, co
   const int grid = 8 * ((a.total_items + 7) / 8);
   {
     ProfScope prof_("bs_bwd_dq", stream);
-    hipLaunchKernelGGL(bs_bwd_dq_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+    if (a.last_rows < kBlock)
+      hipLaunchKernelGGL(bs_bwd_dq_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(bs_bwd_dq_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
   }
   int st = check_hip(hipGetLastError(), "bs_bwd_dq launch");
   if (st) return st;
   {
     ProfScope prof_("bs_bwd_dkdv", stream);
-    hipLaunchKernelGGL(bs_bwd_dkdv_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+    if (a.last_rows < kBlock)
+      hipLaunchKernelGGL(bs_bwd_dkdv_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(bs_bwd_dkdv_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
   }
   st = check_hip(hipGetLastError(), "bs_bwd_dkdv launch");
   if (st || !sp.split || L->g == 0) return st;

@@ -81,6 +81,9 @@ __device__ __forceinline__ Item decode_row_item(int v, int heads, int nb, int g,
   return it;
 }
 
+// kRagged: the sequence ends inside its last block (n % 64 != 0); the instance for
+// whole blocks carries none of that block's masking and guards.
+template <bool kRagged>
 __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
@@ -101,9 +104,8 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   auto vaddr = [&](int kb) { return vbase + (size_t)kb * kBlock * kHead; };
   // a sequence that ends inside its last block: that block's missing rows are
   // neither read nor attended to, and no output is written for them
-  const bool ragged = a.last_rows < kBlock;
   auto tile_load = [&](int kb, TileRegs& kr, TileRegs& vr) {
-    if (ragged && kb == a.nb - 1) {
+    if (kRagged && kb == a.nb - 1) {
       gload_nat_rows(kr, kaddr(kb), tid, a.last_rows);
       gload_nat_rows(vr, vaddr(kb), tid, a.last_rows);
     } else {
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   {
     const uint16_t* qp = a.q + bh_off + (size_t)qrow * kHead + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qB[c] = qrow < a.n ? ld16(qp + 16 * c) : bf16x8{};
+    for (int c = 0; c < 4; ++c) qB[c] = !kRagged || qrow < a.n ? ld16(qp + 16 * c) : bf16x8{};
   }
   scale_operands(qB, a.sl2);
   lds_store_nat(sK[0], kr, tid);
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
     const bool more = t + 1 < len;
     f32x16 s0, s1;
     qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
-    if (ragged && kb_cur == a.nb - 1) mask_keys_from(s0, s1, hl, a.last_rows);
+    if (kRagged && kb_cur == a.nb - 1) mask_keys_from(s0, s1, hl, a.last_rows);
     const int kb_after = kb_next;   // block of tile t + 1
     if (more) {
       tile_load(kb_next, kr, vr);
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
 
   const float l_tot = partner_sum(st.l);
   if (it.slot < 0) {
-    if (qrow < a.n)
+    if (!kRagged || qrow < a.n)
       write_o_bf16(st, l_tot, hl, a.o + bh_off + (size_t)qrow * kHead,
                  a.lse != nullptr ? a.lse + (size_t)it.bh * a.n + qrow : nullptr);
   } else {
@@ -400,7 +402,10 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
   const int grid = 8 * ((a.total_items + 7) / 8);
   {
     ProfScope prof_("bs_fwd_bf16", stream);
-    hipLaunchKernelGGL(bs_fwd_bf16_kernel, dim3(grid), dim3(kFwdThreads), 0, stream, a);
+    if (a.last_rows < kBlock)
+      hipLaunchKernelGGL(bs_fwd_bf16_kernel<true>, dim3(grid), dim3(kFwdThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(bs_fwd_bf16_kernel<false>, dim3(grid), dim3(kFwdThreads), 0, stream, a);
   }
   int st = check_hip(hipGetLastError(), "bs_fwd_bf16 launch");
   if (st || !sp.split || L->g == 0) return st;
