@@ -213,11 +213,13 @@ struct TileF32 { f32x4 v[4]; };
 
 // rows at or past `rows` (the end of a sequence inside the last block) are not
 // read and stage as zeros
+template <bool kRagged>
 __device__ __forceinline__ void load_f32_tile(TileF32& t, const float* g, int tid, int rows) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if ((4 * tid + 1024 * u) / kHead < rows) x = *reinterpret_cast<const f32x4*>(g + 4 * tid + 1024 * u);
+    if (!kRagged || (4 * tid + 1024 * u) / kHead < rows)
+      x = *reinterpret_cast<const f32x4*>(g + 4 * tid + 1024 * u);
     t.v[u] = x;
   }
 }
@@ -242,6 +244,8 @@ __device__ __forceinline__ float group16_sum(float x) {
   return x;
 }
 
+// kRagged as for the bf16 kernel: the sequence ends inside its last block.
+template <bool kRagged>
 __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
   __shared__ __attribute__((aligned(16))) float sQ[kBlock * kF32Stride];
   __shared__ __attribute__((aligned(16))) float sK[kBlock * kF32Stride];   // K, then P
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
   auto rows_of = [&](int blk) { return blk == a.nb - 1 ? a.last_rows : kBlock; };
   {
     TileF32 qt;
-    load_f32_tile(qt, a.q + bh_off + (size_t)i * kBlock * kHead, tid, rows_of(i));
+    load_f32_tile<kRagged>(qt, a.q + bh_off + (size_t)i * kBlock * kHead, tid, rows_of(i));
     store_f32_tile(sQ, qt, tid);
   }
 
@@ -271,18 +275,20 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
   TileF32 kt, vt;
   if (rp0 < rp1) {
     const int kb = a.col_idx[rp0];
-    load_f32_tile(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
-    load_f32_tile(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
+    load_f32_tile<kRagged>(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
+    load_f32_tile<kRagged>(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
   }
+  int krows_next = rp0 < rp1 && kRagged ? rows_of(a.col_idx[rp0]) : kBlock;
   for (int e = rp0; e < rp1; ++e) {
-    const int krows = rows_of(a.col_idx[e]);   // keys of this block that are tokens
+    const int krows = krows_next;   // keys of this block that are tokens
     __syncthreads();   // the previous block's P (in sK) and V are no longer read
     store_f32_tile(sK, kt, tid);
     store_f32_tile(sV, vt, tid);
     if (e + 1 < rp1) {
       const int kb = a.col_idx[e + 1];
-      load_f32_tile(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
-      load_f32_tile(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
+      load_f32_tile<kRagged>(kt, a.k + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
+      load_f32_tile<kRagged>(vt, a.v + bh_off + (size_t)kb * kBlock * kHead, tid, rows_of(kb));
+      if (kRagged) krows_next = rows_of(kb);
     }
     __syncthreads();
     // S = Q K^T for queries 4tq+r, keys 4tk+j
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        s[r][j] = 4 * tk + j < krows ? s[r][j] * a.scale : -INFINITY;
+        s[r][j] = !kRagged || 4 * tk + j < krows ? s[r][j] * a.scale : -INFINITY;
         mx = fmaxf(mx, s[r][j]);
       }
       const float m_new = fmaxf(m[r], group16_max(mx));
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int tok = i * kBlock + 4 * tq + r;
-    if (tok >= a.n) break;
+    if (kRagged && tok >= a.n) break;
     const float inv = 1.f / l[r];
     const f32x4 w = {acc[r][0] * inv, acc[r][1] * inv, acc[r][2] * inv, acc[r][3] * inv};
     *reinterpret_cast<f32x4*>(a.o + bh_off + (size_t)tok * kHead + 4 * tk) = w;
@@ -383,7 +389,10 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
     const int grid = 8 * ((a.total_items + 7) / 8);
     {
     ProfScope prof_("bs_fwd_f32", stream);
-    hipLaunchKernelGGL(bs_fwd_f32_kernel, dim3(grid), dim3(256), 0, stream, a);
+    if (a.last_rows < kBlock)
+      hipLaunchKernelGGL(bs_fwd_f32_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(bs_fwd_f32_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
   }
     return check_hip(hipGetLastError(), "bs_fwd_f32 launch");
   }
