@@ -231,7 +231,7 @@ def bsattn_fwd(layout, q, k, v, o, lse=None, workspace=None, scale=None, stream=
     bsz, _, _, d = q.shape
     nb, heads, _ = bsattn_layout_info(layout)
     shape = (bsz, heads, _layout_len(layout, nb), d)
-    need = bsattn_fwd_workspace(layout, bsz, d) if _dtype_code(q) == BSATTN_BF16 else 0
+    need = bsattn_fwd_workspace(layout, bsz, d)   # covers both dtypes
     _check_tensors("bsattn_fwd", shape, q.dtype, (("q", q), ("k", k), ("v", v), ("o", o)),
                    lse, workspace, need)
     scale = d ** -0.5 if scale is None else scale

@@ -344,7 +344,7 @@ int bsattn_fwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float 
   if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, "fwd: lse not 16-byte aligned");
   if ((int64_t)batch * L->heads * L->n * kHead >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, "fwd: tensor too large");
-  const size_t need = dt == BSATTN_F32 ? 0 : fwd_workspace_bytes(L, batch);
+  const size_t need = fwd_workspace_bytes_dt(L, batch, dt);
   if ((st = check_workspace(workspace, ws_bytes, need, "fwd"))) return st;
   if ((st = check_device(L->device))) return st;
   return launch_fwd(L, batch, dt, scale, q, k, v, o, lse, workspace, stream);

@@ -19,6 +19,8 @@
 // lane (column of the accumulator), 32 keys per lane and the other 32 in the
 // partner lane l ^ 32.
 
+#include <algorithm>
+
 #include "attn_tile.hpp"
 #include "internal.hpp"
 
@@ -187,7 +189,10 @@ __global__ __launch_bounds__(256) void bs_fwd_combine_kernel(
 }
 
 // fp32 path: register-tiled FMA, one 256-thread work-group per query block walking
-// its whole row.  Thread t owns queries 4*(t/16)..+3 and, for the scores, keys
+// its whole row or, when the whole problem has fewer rows than the device has
+// work-group slots, per segment of `fseg` key blocks of a row, writing a partial
+// record (unnormalised O, running max, running sum) that bs_fwd_f32_combine merges
+// in segment order.  Thread t owns queries 4*(t/16)..+3 and, for the scores, keys
 // 4*(t%16)..+3 of the current key block; for the output, head-dim columns
 // 4*(t%16)..+3.  Each step reads float4 operands from LDS (64 FMAs per 8 reads);
 // tile rows are padded to 68 floats, which keeps the float4 reads of 16 different
@@ -201,8 +206,10 @@ struct FwdF32Args {
   float* lse;
   const int32_t* row_ptr;
   const int32_t* col_idx;
+  float* part;       // partial records [rows][nseg][kPartFloats] when split
   int heads, n, nb, total_items;
   int last_rows;   // tokens in the last block: n - 64 (nb - 1), 1..64
+  int fseg, nseg;  // split rows: segments of fseg key blocks, at most nseg per row
   float scale;
 };
 
@@ -252,7 +259,8 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
   __shared__ __attribute__((aligned(16))) float sV[kBlock * kF32Stride];
   const int v = xcd_remap(blockIdx.x, a.total_items);
   if (v >= a.total_items) return;
-  const int bh = v / a.nb, i = v - bh * a.nb, h = bh % a.heads;
+  const int row = v / a.nseg, seg = v - row * a.nseg;
+  const int bh = row / a.nb, i = row - bh * a.nb, h = bh % a.heads;
   const int tid = threadIdx.x, tq = tid >> 4, tk = tid & 15;
   const size_t bh_off = (size_t)bh * a.n * kHead;
   auto rows_of = [&](int blk) { return blk == a.nb - 1 ? a.last_rows : kBlock; };
@@ -270,7 +278,12 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
   }
-  const int rp0 = a.row_ptr[(int64_t)h * a.nb + i], rp1 = a.row_ptr[(int64_t)h * a.nb + i + 1];
+  int rp0 = a.row_ptr[(int64_t)h * a.nb + i], rp1 = a.row_ptr[(int64_t)h * a.nb + i + 1];
+  if (a.nseg > 1) {   // this item's segment of the row
+    rp0 += seg * a.fseg;
+    if (rp0 >= rp1) return;
+    rp1 = min(rp1, rp0 + a.fseg);
+  }
   // K and V of the next key block are loaded into registers one block ahead
   TileF32 kt, vt;
   if (rp0 < rp1) {
@@ -355,6 +368,19 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
           for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(pv[r][x], vv[x][c], acc[r][c]);
     }
   }
+  if (a.nseg > 1) {   // partial record: O unnormalised, then m, then l (natural log units)
+    float* rec = a.part + (size_t)v * kPartFloats;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 w = {acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+      *reinterpret_cast<f32x4*>(rec + (4 * tq + r) * kHead + 4 * tk) = w;
+      if (tk == 0) {
+        rec[kBlock * kHead + 4 * tq + r] = m[r];
+        rec[kBlock * kHead + kBlock + 4 * tq + r] = l[r];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int tok = i * kBlock + 4 * tq + r;
@@ -366,12 +392,85 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
   }
 }
 
+// Merge the segment records of every split fp32 row, in segment order:
+// M = max_s m_s, L = sum_s l_s e^(m_s - M), O = sum_s O_s e^(m_s - M) / L, lse = M + ln L.
+// One work-group per row (query block); thread t: query row t / 4, 16 columns.
+__global__ __launch_bounds__(256) void bs_fwd_f32_combine_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ row_ptr, int heads, int n,
+    int nb, int fseg, int nseg, float* __restrict__ o, float* __restrict__ lse) {
+  const int row = blockIdx.x;   // (bh, i)
+  const int bh = row / nb, i = row - bh * nb, h = bh % heads;
+  const int qr = threadIdx.x >> 2, dq = (threadIdx.x & 3) * 16;
+  const int tok = i * kBlock + qr;
+  if (tok >= n) return;   // past the end of a sequence that ends inside this block
+  const int len = row_ptr[(int64_t)h * nb + i + 1] - row_ptr[(int64_t)h * nb + i];
+  const int ns = (len + fseg - 1) / fseg;
+  const float* base = part + (size_t)row * nseg * kPartFloats;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, base[(size_t)s * kPartFloats + kBlock * kHead + qr]);
+  float L = 0.f, acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float* ps = base + (size_t)s * kPartFloats;
+    const float f = expf(ps[kBlock * kHead + qr] - M);
+    L += ps[kBlock * kHead + kBlock + qr] * f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(ps + qr * kHead + dq + e);
+      acc[e] += x[0] * f;
+      acc[e + 1] += x[1] * f;
+      acc[e + 2] += x[2] * f;
+      acc[e + 3] += x[3] * f;
+    }
+  }
+  const float inv = 1.f / L;
+  float* op = o + ((size_t)bh * n + tok) * kHead + dq;
+#pragma unroll
+  for (int e = 0; e < 16; e += 4) {
+    const f32x4 w = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+    *reinterpret_cast<f32x4*>(op + e) = w;
+  }
+  if (lse != nullptr && (threadIdx.x & 3) == 0) lse[(size_t)bh * n + tok] = M + logf(L);
+}
+
+// fp32 row split: rows of fseg key blocks when the rows alone would leave most
+// work-group slots (four per compute unit) idle; at most kF32MaxItems items.
+struct F32Plan { int fseg, nseg; };
+constexpr int kF32MaxItems = 2048;
+
+F32Plan f32_plan(const bsattn_layout* L, int batch) {
+  const int64_t rows = (int64_t)batch * L->heads * L->nb;
+  const int64_t slots = 4 * (int64_t)(L->cus > 0 ? L->cus : 1);
+  F32Plan p{L->nb, 1};
+  if (2 * rows >= slots) return p;
+  const int64_t pairs = (int64_t)batch * L->heads * L->nnz_per_head;
+  int fseg = (int)std::max<int64_t>(1, (pairs + slots - 1) / slots);
+  int nseg = (L->nb + fseg - 1) / fseg;
+  while (rows * nseg > kF32MaxItems) {
+    fseg *= 2;
+    nseg = (L->nb + fseg - 1) / fseg;
+  }
+  if (nseg > 1) p = F32Plan{fseg, nseg};
+  return p;
+}
+
 }  // namespace
 
-size_t fwd_workspace_bytes(const bsattn_layout* L, int batch) {
+// Workspace of one dtype's forward: bf16 global-row segments or fp32 row segments.
+size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt) {
+  if (dt == BSATTN_F32) {
+    const F32Plan fp = f32_plan(L, batch);
+    return fp.nseg > 1 ? (size_t)batch * L->heads * L->nb * fp.nseg * kPartFloats * sizeof(float) : 0;
+  }
   const SegPlan sp = seg_plan(L, batch);
-  if (!sp.split) return 0;
-  return (size_t)batch * L->heads * L->g * sp.nseg * kPartFloats * sizeof(float);
+  return sp.split ? (size_t)batch * L->heads * L->g * sp.nseg * kPartFloats * sizeof(float) : 0;
+}
+
+// The size the public query reports: enough for either dtype.
+size_t fwd_workspace_bytes(const bsattn_layout* L, int batch) {
+  return std::max(fwd_workspace_bytes_dt(L, batch, BSATTN_BF16),
+                  fwd_workspace_bytes_dt(L, batch, BSATTN_F32));
 }
 
 int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, const void* q,
@@ -383,18 +482,29 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
     a.o = (float*)o; a.lse = lse;
     a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
     a.heads = L->heads; a.n = L->n; a.nb = L->nb;
-    a.total_items = bhn * L->nb;
+    const F32Plan fp = f32_plan(L, batch);
+    a.fseg = fp.fseg; a.nseg = fp.nseg;
+    a.part = (float*)ws;
+    a.total_items = bhn * L->nb * fp.nseg;
     a.last_rows = L->n - kBlock * (L->nb - 1);
     a.scale = scale;
     const int grid = 8 * ((a.total_items + 7) / 8);
     {
-    ProfScope prof_("bs_fwd_f32", stream);
-    if (a.last_rows < kBlock)
-      hipLaunchKernelGGL(bs_fwd_f32_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL(bs_fwd_f32_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
-  }
-    return check_hip(hipGetLastError(), "bs_fwd_f32 launch");
+      ProfScope prof_("bs_fwd_f32", stream);
+      if (a.last_rows < kBlock)
+        hipLaunchKernelGGL(bs_fwd_f32_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL(bs_fwd_f32_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+    }
+    int st = check_hip(hipGetLastError(), "bs_fwd_f32 launch");
+    if (st || fp.nseg == 1) return st;
+    {
+      ProfScope prof_("bs_fwd_f32_combine", stream);
+      hipLaunchKernelGGL(bs_fwd_f32_combine_kernel, dim3(bhn * L->nb), dim3(256), 0, stream,
+                         (const float*)ws, L->d_row_ptr, L->heads, L->n, L->nb, fp.fseg, fp.nseg,
+                         (float*)o, lse);
+    }
+    return check_hip(hipGetLastError(), "bs_fwd_f32_combine launch");
   }
   FwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;

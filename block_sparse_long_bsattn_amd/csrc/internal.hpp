@@ -107,7 +107,8 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const
                   const void* k, const void* v, const void* qg, const void* kg,
                   const void* vg, void* o, float* lse, void* ws, hipStream_t stream);
 
-size_t fwd_workspace_bytes(const bsattn_layout* L, int batch);
+size_t fwd_workspace_bytes(const bsattn_layout* L, int batch);   // enough for either dtype
+size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt);
 size_t bwd_workspace_bytes(const bsattn_layout* L, int batch);
 size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads);
 int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,

@@ -128,7 +128,10 @@ int bsattn_layout_destroy(bsattn_layout* layout);
 /* ------------------------------------------------------------------------- */
 
 /* Workspace bytes bsattn_fwd / bsattn_bwd need for this layout and batch (may be
- * 0).  d must be 64.  Returns 0 for invalid arguments as well. */
+ * 0).  d must be 64.  Returns 0 for invalid arguments as well.  The forward's size
+ * serves both dtypes: bf16 uses it for the segments of split global rows, fp32 for
+ * the segments of rows split when the problem has fewer query blocks than half
+ * the device's work-group slots (small, latency-bound problems). */
 size_t bsattn_fwd_workspace(const bsattn_layout* layout, int batch, int d);
 size_t bsattn_bwd_workspace(const bsattn_layout* layout, int batch, int d);
 

@@ -91,8 +91,16 @@ def test_fwd_bf16_full_compare(case):
 
 
 def test_fwd_fp32_other_shapes():
+    """Small fp32 problems split every row into segments merged in order (n = 1024:
+    32 rows of up to 16 blocks); a single block is one unsplit item."""
     check_full(1024, 2, 1, [0, 15], 3, 3, 5, dtype="f32")
     check_full(64, 1, 1, [0], 1, 3, 5, dtype="f32")
+
+
+def test_fwd_fp32_unsplit_rows():
+    """Enough query blocks (batch 1, 8 heads, n = 4096: 512 rows) that fp32 rows run
+    whole, one work-group per row."""
+    check_full(4096, 8, 1, [0, 63], 3, 3, 6, dtype="f32")
 
 
 @pytest.mark.parametrize("cfg", [
