@@ -225,15 +225,54 @@ __device__ __forceinline__ void write_partial(const FwdState& st, float l_tot, i
 
 // Merge nseg partial records (stride kPartFloats) for row `row`, columns dq..dq+15,
 // in segment order: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
+// Up to kMergeBatch records are read with all their loads in flight together (one
+// memory round trip: these merges run on few work-groups and are latency-bound);
+// the arithmetic is the same, in the same order, either way.
+constexpr int kMergeBatch = 8;
+
 __device__ __forceinline__ void merge_partials(const float* base, int nseg, int row, int dq,
                                                float (&acc)[16], float& M, float& L) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  L = 0.f;
+  if (nseg <= kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch];
+    f32x4 x[kMergeBatch][4];
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s) {
+      if (s < nseg) {
+        const float* ps = base + (size_t)s * kPartFloats;
+        mv[s] = ps[kBlock * kHead + row];
+        lv[s] = ps[kBlock * kHead + kBlock + row];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[s][q] = *reinterpret_cast<const f32x4*>(ps + row * kHead + dq + 4 * q);
+      }
+    }
+    M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s)
+      if (s < nseg) M = fmaxf(M, mv[s]);
+    const float Mref = M == -INFINITY ? 0.f : M;
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s) {
+      if (s < nseg) {
+        const float f = fast_exp2(mv[s] - Mref);
+        L += lv[s] * f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[4 * q] += x[s][q][0] * f;
+          acc[4 * q + 1] += x[s][q][1] * f;
+          acc[4 * q + 2] += x[s][q][2] * f;
+          acc[4 * q + 3] += x[s][q][3] * f;
+        }
+      }
+    }
+    return;
+  }
   M = -INFINITY;
 #pragma unroll 8
   for (int s = 0; s < nseg; ++s) M = fmaxf(M, base[(size_t)s * kPartFloats + kBlock * kHead + row]);
   const float Mref = M == -INFINITY ? 0.f : M;
-  L = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll 4
   for (int s = 0; s < nseg; ++s) {
     const float* ps = base + (size_t)s * kPartFloats;
@@ -246,6 +285,42 @@ __device__ __forceinline__ void merge_partials(const float* base, int nseg, int 
       acc[e + 1] += x[1] * f;
       acc[e + 2] += x[2] * f;
       acc[e + 3] += x[3] * f;
+    }
+  }
+}
+
+// Sum of nseg fp32 partial tiles (16 consecutive floats at src + s*stride), in
+// segment order; up to kMergeBatch tiles with all loads in flight together.
+__device__ __forceinline__ void sum_partials(const float* src, size_t stride, int nseg,
+                                             float (&acc)[16]) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  if (nseg <= kMergeBatch) {
+    f32x4 x[kMergeBatch][4];
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s)
+      if (s < nseg)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[s][q] = *reinterpret_cast<const f32x4*>(src + s * stride + 4 * q);
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s)
+      if (s < nseg)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[4 * q] += x[s][q][0];
+          acc[4 * q + 1] += x[s][q][1];
+          acc[4 * q + 2] += x[s][q][2];
+          acc[4 * q + 3] += x[s][q][3];
+        }
+    return;
+  }
+#pragma unroll 4
+  for (int s = 0; s < nseg; ++s) {
+    const float* ps = src + (size_t)s * stride;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(ps + e);
+      acc[e] += x[0]; acc[e + 1] += x[1]; acc[e + 2] += x[2]; acc[e + 3] += x[3];
     }
   }
 }

@@ -403,20 +403,10 @@ __global__ __launch_bounds__(256) void bs_bwd_reduce_kernel(
   const int idx = blockIdx.x / 3;   // bh*g + gi
   const int bh = idx / g, gi = idx - bh * g;
   const int e0 = threadIdx.x * 16;  // 16 consecutive floats of the 64x64 tile
+  const size_t slot0 = (size_t)idx * nseg;
   float acc[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < nseg; ++s) {
-    const size_t slot = (size_t)idx * nseg + s;
-    const float* src = kind == 0 ? part_q + slot * kTile
-                                 : part_kv + slot * 2 * kTile + (kind - 1) * kTile;
-#pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(src + e0 + e);
-      acc[e] += x[0]; acc[e + 1] += x[1]; acc[e + 2] += x[2]; acc[e + 3] += x[3];
-    }
-  }
+  if (kind == 0) sum_partials(part_q + slot0 * kTile + e0, kTile, nseg, acc);
+  else sum_partials(part_kv + slot0 * 2 * kTile + (kind - 1) * kTile + e0, 2 * kTile, nseg, acc);
   // rows past the end of a sequence that ends inside this block are not written
   if (gblk[gi] * kBlock + e0 / kHead >= n) return;
   uint16_t* dst = kind == 0 ? dq : (kind == 1 ? dk : dv);

@@ -605,17 +605,7 @@ __global__ __launch_bounds__(256) void lf_bwd_reduce_kernel(LfBwdArgs a, int nq_
           (e0 % kHead);
   }
   float acc[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < a.nseg; ++s) {
-    const float* ps = src + (size_t)s * stride;
-#pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(ps + e);
-      acc[e] += x[0]; acc[e + 1] += x[1]; acc[e + 2] += x[2]; acc[e + 3] += x[3];
-    }
-  }
+  sum_partials(src, stride, a.nseg, acc);
   store16_bf16(dst, acc, 1.f);
 }
 

@@ -224,9 +224,9 @@ __global__ __launch_bounds__(256) void lf_combine_kernel(LfArgs a) {
   const int row = threadIdx.x >> 2, dq = (threadIdx.x & 3) * 16;
   const int j = gt * kBlock + row;
   if (j >= a.ng) return;
+  const int tok = a.gtok[j];   // read alongside the partial records
   float acc[16], M, L;
   merge_partials(a.part + (size_t)idx * a.nseg * kPartFloats, a.nseg, row, dq, acc, M, L);
-  const int tok = a.gtok[j];
   store16_bf16(a.o + ((size_t)bh * a.n + tok) * kHead + dq, acc, 1.f / L);
   if (a.lse != nullptr && (threadIdx.x & 3) == 0)
     a.lse[(size_t)bh * a.n + tok] = (M + __log2f(L)) * kLn2;
