@@ -121,6 +121,8 @@ void free_layout(bsattn_layout* L) {
   (void)hipFree(L->d_csc_idx);
   (void)hipFree(L->d_rbits);
   (void)hipFree(L->d_kv_order);
+  (void)hipFree(L->d_row_info);
+  (void)hipFree(L->d_col_info);
   delete L;
 }
 
@@ -242,7 +244,9 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
       (st = dev_alloc(&L->d_csc_ptr, (size_t)heads * nb + 1)) ||
       (st = dev_alloc(&L->d_csc_idx, (size_t)(nnz * heads))) ||
       (st = dev_alloc(&L->d_rbits, (size_t)heads * nb * ((nb + 31) / 32))) ||
-      (st = dev_alloc(&L->d_kv_order, (size_t)heads * ng.size()))) {
+      (st = dev_alloc(&L->d_kv_order, (size_t)heads * ng.size())) ||
+      (st = dev_alloc(&L->d_row_info, (size_t)heads * ng.size() * 4)) ||
+      (st = dev_alloc(&L->d_col_info, (size_t)heads * ng.size() * 4))) {
     free_layout(L);
     return st;
   }

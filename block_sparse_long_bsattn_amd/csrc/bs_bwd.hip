@@ -16,87 +16,14 @@
 //                partials, summed here in segment order, so results are bitwise
 //                reproducible.  Each XCD starts its segments before other items.
 
-#include "attn_tile.hpp"
-#include "internal.hpp"
+#include "bs_bwd.hpp"
 
 namespace bsattn {
 namespace {
 
+using namespace bwd;
+
 constexpr int kThreads = 128;
-constexpr int kTile = kBlock * kHead;   // floats in one 64x64 partial tile
-
-struct BwdArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const uint16_t* o;
-  const float* lse;
-  const uint16_t* dout;
-  uint16_t* dq;
-  uint16_t* dk;
-  uint16_t* dv;
-  float* dbuf;      // D [B*H*n]
-  float* part_q;    // [B*H*g*nseg][64][64]
-  float* part_kv;   // [B*H*g*nseg][2][64][64]
-  const int32_t* row_ptr;
-  const int32_t* col_idx;
-  const int32_t* csc_ptr;
-  const int32_t* csc_idx;
-  const int32_t* gblk;
-  const int32_t* ngblk;
-  const int32_t* kv_order;   // [heads][nb - g] dK/dV order of the non-global key blocks
-  int heads, n, nb, g, seg, nseg, split;
-  int last_rows;   // tokens in the last block: n - 64 (nb - 1), 1..64
-  int items_per_bh, total_items;
-  float scale, sl2;
-};
-
-// Tile loads for a sequence that may end inside its last block (kRagged): that
-// block's missing rows are not read and stage as zeros.  The kernels below are
-// instantiated with and without those guards; the whole-block instance has none.
-template <bool kRagged>
-__device__ __forceinline__ void load_block(TileRegs& r, const uint16_t* base, int blk,
-                                           const BwdArgs& a, int tid) {
-  const uint16_t* g = base + (size_t)blk * kBlock * kHead;
-  if (kRagged && blk == a.nb - 1) gload_nat_rows(r, g, tid, a.last_rows);
-  else gload_nat(r, g, tid);
-}
-
-struct Item {
-  int bh, h, blk, start, len, slot, seg;
-};
-
-// Item v of a per-(batch, head) list: non-global blocks first (whole list), then
-// each global block's segments of a.seg blocks.  ptr is the row or column pointer.
-// kv: the dK/dV items, whose non-global key blocks run longest column first
-__device__ __forceinline__ Item decode(const BwdArgs& a, int v, const int32_t* ptr, bool kv) {
-  Item it;
-  it.bh = v / a.items_per_bh;
-  const int r = v - it.bh * a.items_per_bh;
-  it.h = it.bh % a.heads;
-  const int ng = a.nb - a.g;
-  it.seg = 0;
-  it.slot = -1;
-  it.start = 0;
-  it.len = -1;
-  if (r < ng) {
-    it.blk = kv ? a.kv_order[(int64_t)it.h * ng + r] : a.ngblk[r];
-  } else {
-    const int gi = (r - ng) / a.nseg;
-    const int s = (r - ng) - gi * a.nseg;
-    it.blk = a.gblk[gi];
-    it.seg = s;
-    if (a.split) {
-      it.start = s * a.seg;
-      it.len = min(a.seg, a.nb - s * a.seg);
-      it.slot = (it.bh * a.g + gi) * a.nseg + s;
-    }
-  }
-  const int p0 = ptr[(int64_t)it.h * a.nb + it.blk];
-  if (it.len < 0) it.len = ptr[(int64_t)it.h * a.nb + it.blk + 1] - p0;
-  it.start += p0;
-  return it;
-}
 
 template <bool kRagged>
 __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
@@ -105,7 +32,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
 
   const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
   if (v < 0) return;
-  const Item it = decode(a, v, a.row_ptr, false);
+  const Item it = decode(a, v, false);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)it.bh * a.n * kHead;
@@ -119,12 +46,11 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   // the end read nothing and write nothing.
   TileRegs kr, vr;
   if (it.len > 0) {
-    const int kb = keys[0];
-    load_block<kRagged>(kr, kbase, kb, a, tid);
-    load_block<kRagged>(vr, vbase, kb, a, tid);
+    load_block<kRagged>(kr, kbase, it.first, a, tid);
+    load_block<kRagged>(vr, vbase, it.first, a, tid);
   }
   // block index of the next tile, read one iteration ahead of its use
-  int kb_next = it.len > 1 ? keys[1] : 0;
+  int kb_next = it.len > 1 ? it.at(keys, 1) : 0;
   const bool qvalid = !kRagged || qrow < a.n;
   bf16x8 qB[4], doB[4];
   float dsum = 0.f;
@@ -168,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     if (more) {
       load_block<kRagged>(kr, kbase, kb_next, a, tid);
       load_block<kRagged>(vr, vbase, kb_next, a, tid);
-      kb_next = t + 2 < it.len ? keys[t + 2] : 0;
+      kb_next = t + 2 < it.len ? it.at(keys, t + 2) : 0;
     }
     // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
     f32x16 s0 = seed_s, s1 = seed_s, p0 = seed_d, p1 = seed_d;
@@ -237,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
 
   const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
   if (v < 0) return;
-  const Item it = decode(a, v, a.csc_ptr, true);
+  const Item it = decode(a, v, true);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)it.bh * a.n * kHead;
@@ -261,13 +187,12 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   if (it.len > 0) {
-    const int qb = qblks[0];
-    load_block<kRagged>(qr, qbase, qb, a, tid);
-    load_block<kRagged>(dr, dobase, qb, a, tid);
-    load_rowvals(qb);
+    load_block<kRagged>(qr, qbase, it.first, a, tid);
+    load_block<kRagged>(dr, dobase, it.first, a, tid);
+    load_rowvals(it.first);
   }
   // block index of the next tile, read one iteration ahead of its use
-  int qb_next = it.len > 1 ? qblks[1] : 0;
+  int qb_next = it.len > 1 ? it.at(qblks, 1) : 0;
   const bool kvalid = !kRagged || krow < a.n;
   bf16x8 kB[4], vB[4];
   {
@@ -297,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
       load_block<kRagged>(qr, qbase, qb_next, a, tid);
       load_block<kRagged>(dr, dobase, qb_next, a, tid);
       load_rowvals(qb_next);
-      qb_next = t + 2 < it.len ? qblks[t + 2] : 0;
+      qb_next = t + 2 < it.len ? it.at(qblks, t + 2) : 0;
     }
     // S[q][key] = Q K^T, dP[q][key] = dO V^T; rows = queries (2 tiles), column = key.
     // Row q of register r is 32*qt + 8*(r/4) + 4*hl + r%4: the seeds are the
@@ -446,9 +371,9 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, co
   const size_t nslots = (size_t)batch * L->heads * L->g * sp.nseg;
   a.part_q = sp.split ? (float*)(w + off) : nullptr;
   a.part_kv = sp.split ? (float*)(w + off + nslots * kTile * sizeof(float)) : nullptr;
-  a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
-  a.csc_ptr = L->d_csc_ptr; a.csc_idx = L->d_csc_idx;
-  a.gblk = L->d_gblk; a.ngblk = L->d_ngblk; a.kv_order = L->d_kv_order;
+  a.col_idx = L->d_col_idx; a.csc_idx = L->d_csc_idx;
+  a.gblk = L->d_gblk;
+  a.row_info = L->d_row_info; a.col_info = L->d_col_info;
   a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
   a.last_rows = L->n - kBlock * (L->nb - 1);
   a.seg = sp.seg; a.nseg = sp.nseg; a.split = sp.split;

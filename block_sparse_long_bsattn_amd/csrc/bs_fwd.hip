@@ -36,10 +36,9 @@ struct FwdArgs {
   uint16_t* o;
   float* lse;
   float* part;
-  const int32_t* row_ptr;
   const int32_t* col_idx;
+  const int32_t* row_info;   // [heads][nb - g][4] non-global row records
   const int32_t* gblk;
-  const int32_t* ngblk;
   int heads, n, nb, g, seg, nseg, split;
   int last_rows;   // tokens in the last block: n - 64 (nb - 1), 1..64
   int items_per_bh, total_items;
@@ -48,38 +47,47 @@ struct FwdArgs {
 
 struct Item {
   int bh, h, i, start, len, slot;
+  int first;   // first key block of the item
+  bool full;   // the row lists every key block in order (a global row)
+  // key block of list entry t (the list is read only for a row that is not full)
+  __device__ __forceinline__ int at(const int32_t* list, int t) const {
+    return full ? first + t : list[t];
+  }
 };
 
-__device__ __forceinline__ Item decode_row_item(int v, int heads, int nb, int g, int seg, int nseg,
-                                                int split, int ipb, const int32_t* gblk,
-                                                const int32_t* ngblk, const int32_t* row_ptr) {
+// Item v of a per-(batch, head) list: non-global rows first (whole row, from the
+// row's record: block, list start, length, first key block), then each global
+// row's segments of a.seg key blocks; a global row lists every key block in
+// order, so its segments need no lookup.
+__device__ __forceinline__ Item decode_row_item(const FwdArgs& a, int v) {
   Item it;
-  it.bh = v / ipb;
-  const int r = v - it.bh * ipb;
-  it.h = it.bh % heads;
-  const int ng = nb - g;
+  it.bh = v / a.items_per_bh;
+  const int r = v - it.bh * a.items_per_bh;
+  it.h = it.bh % a.heads;
+  const int ng = a.nb - a.g;
+  it.slot = -1;
   if (r < ng) {
-    it.i = ngblk[r];
-    it.start = 0;
-    it.len = -1;
-    it.slot = -1;
+    const int4 rec = *reinterpret_cast<const int4*>(a.row_info + 4 * ((int64_t)it.h * ng + r));
+    it.i = rec.x;
+    it.start = rec.y;
+    it.len = rec.z;
+    it.first = rec.w;
+    it.full = false;
   } else {
-    const int gi = (r - ng) / nseg;
-    const int s = (r - ng) - gi * nseg;
-    it.i = gblk[gi];
-    if (split) {
-      it.start = s * seg;
-      it.len = min(seg, nb - s * seg);
-      it.slot = (it.bh * g + gi) * nseg + s;
+    const int gi = (r - ng) / a.nseg;
+    const int s = (r - ng) - gi * a.nseg;
+    it.i = a.gblk[gi];
+    it.full = true;
+    it.start = 0;
+    if (a.split) {
+      it.first = s * a.seg;
+      it.len = min(a.seg, a.nb - s * a.seg);
+      it.slot = (it.bh * a.g + gi) * a.nseg + s;
     } else {
-      it.start = 0;
-      it.len = -1;
-      it.slot = -1;
+      it.first = 0;
+      it.len = a.nb;
     }
   }
-  const int64_t rp0 = row_ptr[(int64_t)it.h * nb + it.i];
-  if (it.len < 0) it.len = row_ptr[(int64_t)it.h * nb + it.i + 1] - (int)rp0;
-  it.start += (int)rp0;
   return it;
 }
 
@@ -92,8 +100,7 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
 
   const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
   if (v < 0) return;
-  const Item it = decode_row_item(v, a.heads, a.nb, a.g, a.seg, a.nseg, a.split, a.items_per_bh,
-                                  a.gblk, a.ngblk, a.row_ptr);
+  const Item it = decode_row_item(a, v);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t bh_off = (size_t)it.bh * a.n * kHead;
@@ -119,10 +126,10 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   TileRegs kr, vr;
   int kb_cur = 0;
   if (len > 0) {
-    kb_cur = keys[0];
+    kb_cur = it.first;
     tile_load(kb_cur, kr, vr);
   }
-  int kb_next = len > 1 ? keys[1] : 0;
+  int kb_next = len > 1 ? it.at(keys, 1) : 0;
   bf16x8 qB[4];
   {
     const uint16_t* qp = a.q + bh_off + (size_t)qrow * kHead + 8 * hl;
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
     const int kb_after = kb_next;   // block of tile t + 1
     if (more) {
       tile_load(kb_next, kr, vr);
-      kb_next = t + 2 < len ? keys[t + 2] : 0;
+      kb_next = t + 2 < len ? it.at(keys, t + 2) : 0;
     }
     // V^T operands read now; the softmax covers their LDS latency
     bf16x8 vA[8];
@@ -509,8 +516,8 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
   FwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.o = (uint16_t*)o; a.lse = lse; a.part = (float*)ws;
-  a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
-  a.gblk = L->d_gblk; a.ngblk = L->d_ngblk;
+  a.col_idx = L->d_col_idx; a.row_info = L->d_row_info;
+  a.gblk = L->d_gblk;
   a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
   a.last_rows = L->n - kBlock * (L->nb - 1);
   const SegPlan sp = seg_plan(L, batch);

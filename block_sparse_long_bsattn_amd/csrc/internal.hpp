@@ -30,6 +30,11 @@ struct bsattn_layout {
   int32_t* d_kv_order = nullptr; // [heads][nb - g] non-global key blocks, longest column
                                  // first (the dK/dV work order; ascending until a build
                                  // kernel that sorts has run)
+  // Work-item records {block, list start, list length, first listed block}, four
+  // int32 each: [heads][nb - g] non-global rows in block order, and non-global
+  // columns in d_kv_order's order.
+  int32_t* d_row_info = nullptr;
+  int32_t* d_col_info = nullptr;
   std::vector<int32_t> kv_order_init;
 };
 

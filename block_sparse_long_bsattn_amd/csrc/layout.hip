@@ -438,6 +438,25 @@ __device__ __forceinline__ uint32_t mod_small(uint64_t u, uint32_t d) {
   return ((hi % d) * p32 + lo % d) % d;
 }
 
+// lowest set bit (the bitmap is not empty)
+template <int W>
+__device__ __forceinline__ int first_bit(const uint64_t (&b)[W]) {
+  int pos = -1;
+#pragma unroll
+  for (int k = W - 1; k >= 0; --k)
+    if (b[k]) pos = 64 * k + __builtin_ctzll(b[k]);
+  return pos;
+}
+
+// number of set bits below position x
+template <int W>
+__device__ __forceinline__ int bits_below(const uint64_t (&b)[W], int x) {
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k < W; ++k) c += __popcll(b[k] & span_bits(k, 0, x - 1));
+  return c;
+}
+
 template <int W>
 __device__ __forceinline__ int write_bits(const uint64_t (&b)[W], int32_t* out) {
   int q = 0;
@@ -458,10 +477,12 @@ template <int W, int RMAX>
 __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     const int32_t* __restrict__ Gglob, int g, int nb, int w, int r, uint64_t seed,
     int64_t nnz_per_head, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
-    int32_t* __restrict__ csc_ptr, int32_t* __restrict__ csc_idx, int32_t* __restrict__ kv_order) {
+    int32_t* __restrict__ csc_ptr, int32_t* __restrict__ csc_idx, int32_t* __restrict__ kv_order,
+    int32_t* __restrict__ row_info, int32_t* __restrict__ col_info) {
   // dynamic LDS: random picks per key block (nb x wpc words, bit i = query block
-  // i), the global list G[g], every column's offset within the head, then every
-  // column's length
+  // i), the global list G[g], every column's offset within the head, every
+  // column's length, columns by length, first rank per length, every column's
+  // first query block
   extern __shared__ __attribute__((aligned(16))) int32_t dyn[];
   __shared__ uint32_t sGb[2 * W];
   __shared__ int part[kBuildThreads / 64];
@@ -473,6 +494,7 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
   int32_t* sColLen = sColPos + nb;                 // column lengths
   uint32_t* sBk = reinterpret_cast<uint32_t*>(sColLen + nb);   // [nb + 1][wpc] columns by length
   int32_t* sBase = reinterpret_cast<int32_t*>(sBk + (nb + 1) * wpc);   // [nb + 1] first rank
+  int32_t* sColFirst = sBase + nb + 1;                 // [nb] first query block
   for (int x = tid; x < nb * wpc; x += kBuildThreads) colmap[x] = 0u;
   for (int x = tid; x < (nb + 1) * wpc; x += kBuildThreads) sBk[x] = 0u;
   for (int x = tid; x < g; x += kBuildThreads) sG[x] = Gglob[x];
@@ -522,7 +544,11 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
         atomicOr(&colmap[vs * wpc + (i >> 5)], 1u << (i & 31));
       }
     }
-    write_bits(row, col_idx + row_ptr[(int64_t)h * nb + i]);
+    const int rp = row_ptr[(int64_t)h * nb + i];
+    const int len = write_bits(row, col_idx + rp);
+    // the row's work-item record, at its rank among the non-global rows
+    int32_t* rec = row_info + 4 * ((int64_t)h * (nb - g) + i - bits_below(gb, i));
+    rec[0] = i; rec[1] = rp; rec[2] = len; rec[3] = first_bit(row);
   }
   __syncthreads();
 
@@ -555,6 +581,7 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     csc_ptr[(int64_t)h * nb + j] = (int32_t)p;
     sColPos[j] = pos;
     sColLen[j] = len;
+    sColFirst[j] = first_bit(c);
     if (!bit_of(gb, j)) atomicOr(&sBk[len * wpc + (j >> 5)], 1u << (j & 31));
     if (!bit_of(gb, j)) write_bits(c, csc_idx + p);
     pos += len;
@@ -587,6 +614,9 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     for (int x = 0; x < (j >> 5); ++x) rank += __popc(bk[x]);
     rank += __popc(bk[j >> 5] & ((1u << (j & 31)) - 1u));
     kv_order[(int64_t)h * (nb - g) + rank] = j;
+    int32_t* rec = col_info + 4 * ((int64_t)h * (nb - g) + rank);
+    rec[0] = j; rec[1] = (int32_t)((int64_t)h * nnz_per_head + sColPos[j]);
+    rec[2] = sColLen[j]; rec[3] = sColFirst[j];
   }
 
   // global rows and columns hold every block
@@ -651,12 +681,33 @@ int launch_layout_rowptr(bsattn_layout* L, hipStream_t stream) {
   return check_hip(hipGetLastError(), "layout_rowptr launch");
 }
 
+// Larger layouts, phase 3: the work-item records of the non-global rows (in block
+// order) and columns (in dK/dV order), one thread per (head, rank).
+__global__ __launch_bounds__(64) void layout_info_kernel(
+    const int32_t* __restrict__ ngblk, const int32_t* __restrict__ kv_order, int nb, int g,
+    int heads, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const int32_t* __restrict__ csc_ptr, const int32_t* __restrict__ csc_idx,
+    int32_t* __restrict__ row_info, int32_t* __restrict__ col_info) {
+  const int ng = nb - g;
+  const int idx = blockIdx.x * 64 + threadIdx.x;
+  if (idx >= heads * ng) return;
+  const int h = idx / ng, r = idx - h * ng;
+  const int i = ngblk[r];
+  const int rp = row_ptr[(int64_t)h * nb + i];
+  int32_t* rec = row_info + 4 * (int64_t)idx;
+  rec[0] = i; rec[1] = rp; rec[2] = row_ptr[(int64_t)h * nb + i + 1] - rp; rec[3] = col_idx[rp];
+  const int j = kv_order[idx];
+  const int cp = csc_ptr[(int64_t)h * nb + j];
+  rec = col_info + 4 * (int64_t)idx;
+  rec[0] = j; rec[1] = cp; rec[2] = csc_ptr[(int64_t)h * nb + j + 1] - cp; rec[3] = csc_idx[cp];
+}
+
 namespace {
 // Dynamic LDS of layout_head_kernel: random picks, global list, column offsets and
 // lengths, columns by length, first rank per length.
 size_t head_lds_bytes(const bsattn_layout* L) {
   const int wpc = (L->nb + 31) / 32;
-  return ((size_t)L->nb * wpc + L->g + 2 * L->nb + (size_t)(L->nb + 1) * (wpc + 1)) *
+  return ((size_t)L->nb * wpc + L->g + 3 * L->nb + (size_t)(L->nb + 1) * (wpc + 1)) *
          sizeof(int32_t);
 }
 
@@ -667,7 +718,8 @@ int launch_head(bsattn_layout* L, hipStream_t stream) {
     ProfScope prof_("layout_head", stream);
     hipLaunchKernelGGL((layout_head_kernel<W, RMAX>), dim3(L->heads), dim3(kBuildThreads), lds,
                        stream, L->d_gblk, L->g, L->nb, L->w, L->r, L->seed, L->nnz_per_head,
-                       L->d_row_ptr, L->d_col_idx, L->d_csc_ptr, L->d_csc_idx, L->d_kv_order);
+                       L->d_row_ptr, L->d_col_idx, L->d_csc_ptr, L->d_csc_idx, L->d_kv_order,
+                       L->d_row_info, L->d_col_info);
   }
   return check_hip(hipGetLastError(), "layout_head launch");
 }
@@ -698,7 +750,16 @@ int launch_rows_cols(bsattn_layout* L, hipStream_t stream) {
                        stream, L->d_gblk, L->g, L->nb, L->w, L->nnz_per_head, L->d_rbits, wpc,
                        L->d_csc_ptr, L->d_csc_idx);
   }
-  return check_hip(hipGetLastError(), "layout_cols launch");
+  st = check_hip(hipGetLastError(), "layout_cols launch");
+  const int ng = L->nb - L->g;
+  if (st || ng == 0) return st;
+  {
+    ProfScope prof_("layout_info", stream);
+    hipLaunchKernelGGL(layout_info_kernel, dim3((L->heads * ng + 63) / 64), dim3(64), 0, stream,
+                       L->d_ngblk, L->d_kv_order, L->nb, L->g, L->heads, L->d_row_ptr,
+                       L->d_col_idx, L->d_csc_ptr, L->d_csc_idx, L->d_row_info, L->d_col_info);
+  }
+  return check_hip(hipGetLastError(), "layout_info launch");
 }
 }  // namespace
 
