@@ -90,3 +90,58 @@ def test_bwd_deterministic():
     _, b = run_bwd(1024, 2, 2, [0, 15], 3, 3, 4)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_fwd_bwd_layout_over_512_blocks_sampled():
+    """n = 64 * 600 (a layout built by the two-kernel path, whose work-item records
+    come from a kernel of their own), 2 heads, G = {0, 7, 599}.  Forward on sampled
+    rows; dQ, dK and dV of three non-global key blocks per head, with the oracle
+    run on exactly the query rows that attend to them (the only rows with a
+    non-zero probability there), so those gradients are exact; the sum identities
+    over all rows cover the global columns."""
+    n, heads, bsz, G = 64 * 600, 2, 1, [0, 7, 599]
+    say("fwd+bwd n=38400 H=2 (more than 512 blocks)")
+    shape = (bsz, heads, n, 64)
+    (q, k, v, do), (qr, kr, vr, dor) = qkv(shape, "bf16",
+                                          (I.SEED_Q, I.SEED_K, I.SEED_V, I.SEED_DO))
+    h = B.bsattn_layout_build(n, 64, heads, G, 3, 3, 31)
+    try:
+        o = torch.empty_like(q)
+        lse = torch.empty((bsz, heads, n), dtype=torch.float32, device="cuda")
+        wsf = torch.empty(max(1, B.bsattn_fwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(1, B.bsattn_bwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        B.bsattn_fwd(h, q, k, v, o, lse, wsf)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        B.bsattn_bwd(h, q, k, v, o, lse, do, dq, dk, dv, wsb)
+        torch.cuda.synchronize()
+    finally:
+        B.bsattn_layout_destroy(h)
+    o, lse, dq, dk, dv = (to_f64(t) for t in (o, lse, dq, dk, dv))
+    mask, lay = oracle_mask(n, heads, G, 3, 3, 31)
+    rng = np.random.default_rng(600)
+    worst = 0.0
+    for hh in range(heads):
+        rows = np.unique(np.r_[0, 7 * 64 + 5, 599 * 64 + 63, 64, n - 65, rng.integers(0, n, 6)])
+        ro, rl = OA.attention_fwd_rows(qr, kr, vr, mask, 1 / 8.0, 0, hh, rows)
+        worst = max(worst, max_abs(o[0, hh, rows], ro), max_abs(lse[0, hh, rows], rl))
+        cp, cs = lay["csc_ptr"], lay["csc_idx"]
+        base = hh * lay["nb"]
+        cols = [j for j in rng.choice(lay["nb"], 8, replace=False) if j not in G][:3]
+        qblks = np.unique(np.concatenate([cs[cp[base + j]:cp[base + j + 1]] for j in cols]))
+        sel = (qblks[:, None] * 64 + np.arange(64)).ravel()
+        sub = (slice(0, 1), slice(hh, hh + 1))
+
+        def sub_mask(_h, p0, p1, hh=hh, sel=sel):
+            return np.concatenate([mask(hh, int(p), int(p) + 1) for p in sel[p0:p1]])
+        rdq, rdk, rdv = OA.attention_bwd(qr[sub][:, :, sel], kr[sub], vr[sub], dor[sub][:, :, sel],
+                                         sub_mask, 1 / 8.0, row_chunk=1024)
+        worst = max(worst, max_abs(dq[0, hh, sel], rdq[0, 0]))
+        for j in cols:
+            kr_ = slice(64 * j, 64 * j + 64)
+            worst = max(worst, max_abs(dk[0, hh, kr_], rdk[0, 0, kr_]),
+                        max_abs(dv[0, hh, kr_], rdv[0, 0, kr_]))
+    e_v = max_abs(dv.sum(2), dor.sum(2))
+    e_k = float(np.max(np.abs(dk.sum(2))))
+    say(f"   worst max-abs {worst:.3e}; sum identities dV {e_v:.3e} dK {e_k:.3e}")
+    assert worst <= BF16_TOL
+    assert e_v <= 2.0 and e_k <= 2.0      # sums over 38400 rows of bf16-rounded values
