@@ -317,6 +317,11 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j) s[r][j] = 0.f;
+    // fully unrolled, the loads run far enough ahead that the instance with
+    // sequence-end guards no longer fits its registers (it spilled): that one is
+    // unrolled four steps at a time
+    constexpr int kUnroll = kRagged ? 4 : 16;
+#pragma unroll kUnroll
     for (int c = 0; c < kHead; c += 4) {
       f32x4 qv[4], kv[4];
 #pragma unroll
@@ -361,6 +366,7 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
     }
     __syncthreads();
     // O += P V for queries 4tq+r, head-dim columns 4tk..4tk+3
+#pragma unroll kUnroll
     for (int k0 = 0; k0 < kBlock; k0 += 4) {
       f32x4 pv[4], vv[4];
 #pragma unroll
