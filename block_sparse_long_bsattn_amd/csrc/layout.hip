@@ -314,6 +314,19 @@ __device__ void write_col(const GS& G, int nb, int w, int j, uint32_t* bits, int
   for (int y = 0; y < wpc; ++y) bits[y] = 0u;          // ready for the next draw
 }
 
+// exclusive scan of v within each wave (no work-group barrier): for values that
+// only the first wave holds
+__device__ __forceinline__ int wave_exclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x - v;
+}
+
 // exclusive scan of v over the work-group (kBuildThreads threads); `part` holds
 // one int per wave.  Returns the exclusive prefix.
 __device__ int block_exclusive_scan(int v, int* part) {
@@ -434,7 +447,7 @@ __device__ __forceinline__ int select_bit(const uint64_t (&f)[W], int x) {
 // u = hi 2^32 + lo, so u mod d = ((hi mod d)(2^32 mod d) + lo mod d) mod d
 __device__ __forceinline__ uint32_t mod_small(uint64_t u, uint32_t d) {
   const uint32_t hi = (uint32_t)(u >> 32), lo = (uint32_t)u;
-  const uint32_t p32 = (0xffffffffu % d + 1u) % d;
+  const uint32_t p32 = (0u - d) % d;   // (2^32 - d) mod d = 2^32 mod d
   return ((hi % d) * p32 + lo % d) % d;
 }
 
@@ -573,7 +586,8 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     uint64_t c[W];
     local += col_bits(j, c);
   }
-  int pos = block_exclusive_scan(local, part);
+  // up to 64 blocks every column sits in the first wave: no work-group scan
+  int pos = nb <= 64 ? wave_exclusive_scan(local) : block_exclusive_scan(local, part);
   for (int j = j0; j < j1; ++j) {
     uint64_t c[W];
     const int len = col_bits(j, c);
@@ -595,12 +609,14 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
   // column j is the count of longer columns plus the columns of its length before
   // it.
   {
-    const int bper = (nb + 1 + kBuildThreads - 1) / kBuildThreads;
+    // the nb + 1 lengths are counted by the first wave alone (a wave scan, no
+    // work-group barrier)
+    const int bper = (nb + 1 + 63) / 64;
     const int d0 = min(nb + 1, tid * bper), d1 = min(nb + 1, d0 + bper);   // L = nb - d
     int cnt = 0;
     for (int d = d0; d < d1; ++d)
       for (int x = 0; x < wpc; ++x) cnt += __popc(sBk[(nb - d) * wpc + x]);
-    int base = block_exclusive_scan(cnt, part);
+    int base = wave_exclusive_scan(cnt);
     for (int d = d0; d < d1; ++d) {
       sBase[nb - d] = base;
       for (int x = 0; x < wpc; ++x) base += __popc(sBk[(nb - d) * wpc + x]);
