@@ -145,3 +145,34 @@ def test_fwd_bwd_layout_over_512_blocks_sampled():
     say(f"   worst max-abs {worst:.3e}; sum identities dV {e_v:.3e} dK {e_k:.3e}")
     assert worst <= BF16_TOL
     assert e_v <= 2.0 and e_k <= 2.0      # sums over 38400 rows of bf16-rounded values
+
+
+def test_fwd_bwd_after_rebuild():
+    """A layout redrawn with a new seed (bsattn_layout_rebuild rewrites the lists, the
+    dK/dV order and the per-row and per-column work-item records): forward and
+    backward match the oracle on the new seed's pattern."""
+    n, heads, bsz, G = 1024, 2, 2, [0, 15]
+    say("fwd+bwd after layout_rebuild n=1024 H=2 B=2")
+    shape = (bsz, heads, n, 64)
+    (q, k, v, do), (qr, kr, vr, dor) = qkv(shape, "bf16",
+                                          (I.SEED_Q, I.SEED_K, I.SEED_V, I.SEED_DO))
+    h = B.bsattn_layout_build(n, 64, heads, G, 3, 3, 3)
+    try:
+        B.bsattn_layout_rebuild(h, 0xABCDEF)
+        o = torch.empty_like(q)
+        lse = torch.empty((bsz, heads, n), dtype=torch.float32, device="cuda")
+        wsf = torch.empty(max(1, B.bsattn_fwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(1, B.bsattn_bwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        B.bsattn_fwd(h, q, k, v, o, lse, wsf)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        B.bsattn_bwd(h, q, k, v, o, lse, do, dq, dk, dv, wsb)
+        torch.cuda.synchronize()
+    finally:
+        B.bsattn_layout_destroy(h)
+    mask, _ = oracle_mask(n, heads, G, 3, 3, 0xABCDEF)
+    ro, rl = OA.attention_fwd(qr, kr, vr, mask, 1 / 8.0)
+    ref = OA.attention_bwd(qr, kr, vr, dor, mask, 1 / 8.0)
+    errs = [max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)] + \
+        [max_abs(to_f64(a), b) for a, b in zip((dq, dk, dv), ref)]
+    say("   max-abs O {:.3e} lse {:.3e} dQ {:.3e} dK {:.3e} dV {:.3e}".format(*errs))
+    assert max(errs) <= BF16_TOL
