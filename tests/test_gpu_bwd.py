@@ -92,20 +92,24 @@ def test_bwd_deterministic():
         assert np.array_equal(x, y)
 
 
-def test_fwd_bwd_layout_over_512_blocks_sampled():
+@pytest.mark.parametrize("redraw", [False, True])
+def test_fwd_bwd_layout_over_512_blocks_sampled(redraw):
     """n = 64 * 600 (a layout built by the two-kernel path, whose work-item records
-    come from a kernel of their own), 2 heads, G = {0, 7, 599}.  Forward on sampled
-    rows; dQ, dK and dV of three non-global key blocks per head, with the oracle
-    run on exactly the query rows that attend to them (the only rows with a
-    non-zero probability there), so those gradients are exact; the sum identities
-    over all rows cover the global columns."""
+    come from a kernel of their own), 2 heads, G = {0, 7, 599}, as built or redrawn
+    with another seed.  Forward on sampled rows; dQ, dK and dV of three non-global
+    key blocks per head, with the oracle run on exactly the query rows that attend
+    to them (the only rows with a non-zero probability there), so those gradients
+    are exact; the sum identities over all rows cover the global columns."""
     n, heads, bsz, G = 64 * 600, 2, 1, [0, 7, 599]
-    say("fwd+bwd n=38400 H=2 (more than 512 blocks)")
+    seed = 32 if redraw else 31
+    say(f"fwd+bwd n=38400 H=2 (more than 512 blocks), redraw={redraw}")
     shape = (bsz, heads, n, 64)
     (q, k, v, do), (qr, kr, vr, dor) = qkv(shape, "bf16",
                                           (I.SEED_Q, I.SEED_K, I.SEED_V, I.SEED_DO))
     h = B.bsattn_layout_build(n, 64, heads, G, 3, 3, 31)
     try:
+        if redraw:
+            B.bsattn_layout_rebuild(h, seed)
         o = torch.empty_like(q)
         lse = torch.empty((bsz, heads, n), dtype=torch.float32, device="cuda")
         wsf = torch.empty(max(1, B.bsattn_fwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
@@ -117,7 +121,7 @@ def test_fwd_bwd_layout_over_512_blocks_sampled():
     finally:
         B.bsattn_layout_destroy(h)
     o, lse, dq, dk, dv = (to_f64(t) for t in (o, lse, dq, dk, dv))
-    mask, lay = oracle_mask(n, heads, G, 3, 3, 31)
+    mask, lay = oracle_mask(n, heads, G, 3, 3, seed)
     rng = np.random.default_rng(600)
     worst = 0.0
     for hh in range(heads):
