@@ -63,11 +63,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bsattn_layout_destroy": (c_int, [c_void_p]),
         "bsattn_fwd_workspace": (c_size_t, [c_void_p, c_int, c_int]),
         "bsattn_bwd_workspace": (c_size_t, [c_void_p, c_int, c_int]),
-        "bsattn_fwd": (c_int, [c_void_p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p,
-                               c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
-        "bsattn_bwd": (c_int, [c_void_p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p,
-                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                               c_void_p, c_size_t, c_void_p]),
+        "bsattn_fwd": (c_int, [c_void_p, c_int, c_int, c_int, c_float] + [c_void_p] * 7
+                       + [c_size_t, c_void_p]),
+        "bsattn_bwd": (c_int, [c_void_p, c_int, c_int, c_int, c_float] + [c_void_p] * 11
+                       + [c_size_t, c_void_p]),
         "lfattn_plan_build": (c_int, [c_int, c_int, POINTER(c_int32), c_int, c_void_p,
                                       POINTER(c_void_p)]),
         "lfattn_plan_build_dilated": (c_int, [c_int, c_int, POINTER(c_int32), c_int, c_int,
@@ -77,16 +76,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                           POINTER(c_void_p)]),
         "lfattn_plan_destroy": (c_int, [c_void_p]),
         "lfattn_fwd_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int]),
-        "lfattn_fwd": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
-                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "lfattn_fwd": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float] + [c_void_p] * 7
+                       + [c_size_t, c_void_p]),
         "lfattn_bwd_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int]),
-        "lfattn_bwd": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
-                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                               c_void_p, c_void_p, c_size_t, c_void_p]),
+        "lfattn_bwd": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float] + [c_void_p] * 11
+                       + [c_size_t, c_void_p]),
         "lfattn_fwd_gproj": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float]
-                             + [c_void_p] * 9 + [c_size_t, c_void_p]),
+                             + [c_void_p] * 10 + [c_size_t, c_void_p]),
         "lfattn_bwd_gproj": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_float]
-                             + [c_void_p] * 16 + [c_size_t, c_void_p]),
+                             + [c_void_p] * 17 + [c_size_t, c_void_p]),
         "bsattn_status_str": (c_char_p, [c_int]),
         "bsattn_last_error": (c_char_p, []),
         "bsattn_version": (c_char_p, []),
@@ -131,10 +129,15 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
 
 
-def _check_tensors(where, shape, dtype, named, lse=None, workspace=None, ws_need=0):
+def _check_tensors(where, shape, dtype, named, lse=None, workspace=None, ws_need=0,
+                   o_lo=None):
     """Host-side guard: every tensor is a contiguous GPU tensor of the exact shape
     the kernels index, so no launch can read or write past a buffer."""
     import torch
+    if o_lo is not None:
+        if dtype != torch.bfloat16:
+            raise ValueError(f"{where}: o_lo is for bf16 tensors only")
+        named = tuple(named) + (("o_lo", o_lo),)
     for name, t in named:
         if t is None:
             raise ValueError(f"{where}: {name} is None")
@@ -226,23 +229,26 @@ def bsattn_bwd_workspace(layout, batch, d=64) -> int:
     return int(load().bsattn_bwd_workspace(layout, batch, d))
 
 
-def bsattn_fwd(layout, q, k, v, o, lse=None, workspace=None, scale=None, stream=None) -> None:
-    """Tensors [B, H, n, d] on the GPU (bf16 or fp32); lse float32 [B, H, n] or None."""
+def bsattn_fwd(layout, q, k, v, o, lse=None, workspace=None, scale=None, stream=None,
+               o_lo=None) -> None:
+    """Tensors [B, H, n, d] on the GPU (bf16 or fp32); lse float32 [B, H, n] or None;
+    o_lo (bf16 only) receives the rounding residual of O, or None."""
     bsz, _, _, d = q.shape
     nb, heads, _ = bsattn_layout_info(layout)
     shape = (bsz, heads, _layout_len(layout, nb), d)
     need = bsattn_fwd_workspace(layout, bsz, d)   # covers both dtypes
     _check_tensors("bsattn_fwd", shape, q.dtype, (("q", q), ("k", k), ("v", v), ("o", o)),
-                   lse, workspace, need)
+                   lse, workspace, need, o_lo)
     scale = d ** -0.5 if scale is None else scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().bsattn_fwd(layout, bsz, d, _dtype_code(q), c_float(scale), _ptr(q), _ptr(k),
-                             _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
+                             _ptr(v), _ptr(o), _ptr(lse), _ptr(o_lo), _ptr(workspace), ws_bytes,
                              _stream(stream)), "bsattn_fwd")
 
 
 def bsattn_bwd(layout, q, k, v, o, lse, dout, dq, dk, dv, workspace=None, scale=None,
-               stream=None) -> None:
+               stream=None, o_lo=None) -> None:
+    """o_lo: the forward's rounding residual of O, or None."""
     bsz, _, _, d = q.shape
     nb, heads, _ = bsattn_layout_info(layout)
     shape = (bsz, heads, _layout_len(layout, nb), d)
@@ -250,12 +256,14 @@ def bsattn_bwd(layout, q, k, v, o, lse, dout, dq, dk, dv, workspace=None, scale=
         raise ValueError("bsattn_bwd: lse is required")
     _check_tensors("bsattn_bwd", shape, q.dtype,
                    (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
-                    ("dk", dk), ("dv", dv)), lse, workspace, bsattn_bwd_workspace(layout, bsz, d))
+                    ("dk", dk), ("dv", dv)), lse, workspace, bsattn_bwd_workspace(layout, bsz, d),
+                   o_lo)
     scale = d ** -0.5 if scale is None else scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().bsattn_bwd(layout, bsz, d, _dtype_code(q), c_float(scale), _ptr(q), _ptr(k),
-                             _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
-                             _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)), "bsattn_bwd")
+                             _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(dout), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)),
+           "bsattn_bwd")
 
 
 # --- Longformer -----------------------------------------------------------------
@@ -306,18 +314,19 @@ def lfattn_fwd_workspace(plan, batch, heads, d=64) -> int:
     return int(load().lfattn_fwd_workspace(plan, batch, heads, d))
 
 
-def lfattn_fwd(plan, q, k, v, o, lse=None, workspace=None, scale=None, stream=None) -> None:
+def lfattn_fwd(plan, q, k, v, o, lse=None, workspace=None, scale=None, stream=None,
+               o_lo=None) -> None:
     bsz, heads, _, d = q.shape
     if plan not in _plan_n:
         raise ValueError("lfattn_fwd: unknown plan handle")
     shape = (bsz, heads, _plan_n[plan], d)
     _check_tensors("lfattn_fwd", shape, q.dtype, (("q", q), ("k", k), ("v", v), ("o", o)),
-                   lse, workspace, lfattn_fwd_workspace(plan, bsz, heads, d))
+                   lse, workspace, lfattn_fwd_workspace(plan, bsz, heads, d), o_lo)
     scale = d ** -0.5 if scale is None else scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().lfattn_fwd(plan, bsz, heads, d, _dtype_code(q), c_float(scale), _ptr(q),
-                             _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
-                             _stream(stream)), "lfattn_fwd")
+                             _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o_lo), _ptr(workspace),
+                             ws_bytes, _stream(stream)), "lfattn_fwd")
 
 
 def lfattn_bwd_workspace(plan, batch, heads, d=64) -> int:
@@ -325,7 +334,7 @@ def lfattn_bwd_workspace(plan, batch, heads, d=64) -> int:
 
 
 def lfattn_bwd(plan, q, k, v, o, lse, dout, dq, dk, dv, workspace=None, scale=None,
-               stream=None) -> None:
+               stream=None, o_lo=None) -> None:
     bsz, heads, _, d = q.shape
     if plan not in _plan_n:
         raise ValueError("lfattn_bwd: unknown plan handle")
@@ -335,17 +344,17 @@ def lfattn_bwd(plan, q, k, v, o, lse, dout, dq, dk, dv, workspace=None, scale=No
     _check_tensors("lfattn_bwd", shape, q.dtype,
                    (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
                     ("dk", dk), ("dv", dv)), lse, workspace,
-                   lfattn_bwd_workspace(plan, bsz, heads, d))
+                   lfattn_bwd_workspace(plan, bsz, heads, d), o_lo)
     scale = d ** -0.5 if scale is None else scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().lfattn_bwd(plan, bsz, heads, d, _dtype_code(q), c_float(scale), _ptr(q),
-                             _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                             _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)),
-           "lfattn_bwd")
+                             _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(dout),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                             _stream(stream)), "lfattn_bwd")
 
 
 def lfattn_fwd_gproj(plan, q, k, v, qg, kg, vg, o, lse=None, workspace=None, scale=None,
-                     stream=None) -> None:
+                     stream=None, o_lo=None) -> None:
     """Forward with separate projections (qg, kg, vg) for the rows of global tokens."""
     bsz, heads, _, d = q.shape
     if plan not in _plan_n:
@@ -353,17 +362,17 @@ def lfattn_fwd_gproj(plan, q, k, v, qg, kg, vg, o, lse=None, workspace=None, sca
     shape = (bsz, heads, _plan_n[plan], d)
     _check_tensors("lfattn_fwd_gproj", shape, q.dtype,
                    (("q", q), ("k", k), ("v", v), ("qg", qg), ("kg", kg), ("vg", vg), ("o", o)),
-                   lse, workspace, lfattn_fwd_workspace(plan, bsz, heads, d))
+                   lse, workspace, lfattn_fwd_workspace(plan, bsz, heads, d), o_lo)
     scale = d ** -0.5 if scale is None else scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().lfattn_fwd_gproj(plan, bsz, heads, d, _dtype_code(q), c_float(scale), _ptr(q),
                                    _ptr(k), _ptr(v), _ptr(qg), _ptr(kg), _ptr(vg), _ptr(o),
-                                   _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)),
-           "lfattn_fwd_gproj")
+                                   _ptr(lse), _ptr(o_lo), _ptr(workspace), ws_bytes,
+                                   _stream(stream)), "lfattn_fwd_gproj")
 
 
 def lfattn_bwd_gproj(plan, q, k, v, qg, kg, vg, o, lse, dout, dq, dk, dv, dqg, dkg, dvg,
-                     workspace=None, scale=None, stream=None) -> None:
+                     workspace=None, scale=None, stream=None, o_lo=None) -> None:
     """Backward of lfattn_fwd_gproj: gradients for both projection sets."""
     bsz, heads, _, d = q.shape
     if plan not in _plan_n:
@@ -375,12 +384,12 @@ def lfattn_bwd_gproj(plan, q, k, v, qg, kg, vg, o, lse, dout, dq, dk, dv, dqg, d
                    (("q", q), ("k", k), ("v", v), ("qg", qg), ("kg", kg), ("vg", vg), ("o", o),
                     ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv), ("dqg", dqg),
                     ("dkg", dkg), ("dvg", dvg)),
-                   lse, workspace, lfattn_bwd_workspace(plan, bsz, heads, d))
+                   lse, workspace, lfattn_bwd_workspace(plan, bsz, heads, d), o_lo)
     scale = d ** -0.5 if scale is None else scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().lfattn_bwd_gproj(plan, bsz, heads, d, _dtype_code(q), c_float(scale), _ptr(q),
                                    _ptr(k), _ptr(v), _ptr(qg), _ptr(kg), _ptr(vg), _ptr(o),
-                                   _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _ptr(o_lo), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                    _ptr(dqg), _ptr(dkg), _ptr(dvg), _ptr(workspace), ws_bytes,
                                    _stream(stream)), "lfattn_bwd_gproj")
 

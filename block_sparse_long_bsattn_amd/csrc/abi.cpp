@@ -103,6 +103,15 @@ int check_tensor_args(int batch, int d, float scale, std::initializer_list<const
   return BSATTN_OK;
 }
 
+// The rounding residual of O is a bf16 tensor like O; it has no meaning for fp32.
+int check_o_lo(const void* o_lo, bsattn_dtype dt, const char* who) {
+  if (o_lo == nullptr) return BSATTN_OK;
+  if (dt != BSATTN_BF16)
+    return set_error(BSATTN_EINVAL, std::string(who) + ": o_lo is for bf16 outputs only");
+  if (!aligned16(o_lo)) return set_error(BSATTN_EINVAL, std::string(who) + ": o_lo not 16-byte aligned");
+  return BSATTN_OK;
+}
+
 int check_workspace(void* ws, size_t ws_bytes, size_t need, const char* who) {
   if (ws_bytes < need)
     return set_error(BSATTN_EINVAL, std::string(who) + ": workspace too small (need " +
@@ -338,7 +347,7 @@ size_t bsattn_bwd_workspace(const bsattn_layout* L, int batch, int d) {
 }
 
 int bsattn_fwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
-               const void* q, const void* k, const void* v, void* o, float* lse,
+               const void* q, const void* k, const void* v, void* o, float* lse, void* o_lo,
                void* workspace, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   if (L == nullptr) return set_error(BSATTN_EINVAL, "fwd: null layout");
@@ -346,28 +355,30 @@ int bsattn_fwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float 
   int st = check_tensor_args(batch, d, scale, {q, k, v, o}, "fwd");
   if (st) return st;
   if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, "fwd: lse not 16-byte aligned");
+  if ((st = check_o_lo(o_lo, dt, "fwd"))) return st;
   if ((int64_t)batch * L->heads * L->n * kHead >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, "fwd: tensor too large");
   const size_t need = fwd_workspace_bytes_dt(L, batch, dt);
   if ((st = check_workspace(workspace, ws_bytes, need, "fwd"))) return st;
   if ((st = check_device(L->device))) return st;
-  return launch_fwd(L, batch, dt, scale, q, k, v, o, lse, workspace, stream);
+  return launch_fwd(L, batch, dt, scale, q, k, v, o, lse, o_lo, workspace, stream);
 }
 
 int bsattn_bwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
-               const void* q, const void* k, const void* v, const void* o, const float* lse,
-               const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
-               hipStream_t stream) {
+               const void* q, const void* k, const void* v, const void* o, const void* o_lo,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               void* workspace, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   if (L == nullptr) return set_error(BSATTN_EINVAL, "bwd: null layout");
   if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "bwd: only bf16 is built");
   int st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "bwd");
   if (st) return st;
+  if ((st = check_o_lo(o_lo, dt, "bwd"))) return st;
   if ((int64_t)batch * L->heads * L->n * kHead >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, "bwd: tensor too large");
   if ((st = check_workspace(workspace, ws_bytes, bwd_workspace_bytes(L, batch), "bwd"))) return st;
   if ((st = check_device(L->device))) return st;
-  return launch_bwd(L, batch, scale, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream);
+  return launch_bwd(L, batch, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, workspace, stream);
 }
 
 }  // extern "C"
@@ -554,7 +565,7 @@ namespace {
 int lf_fwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int d,
                 bsattn_dtype dt, float scale, const void* q, const void* k, const void* v,
                 const void* qg, const void* kg, const void* vg, void* o, float* lse,
-                void* workspace, size_t ws_bytes, hipStream_t stream) {
+                void* o_lo, void* workspace, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   const std::string w(who);
   if (P == nullptr) return set_error(BSATTN_EINVAL, w + ": null plan");
@@ -565,11 +576,13 @@ int lf_fwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int
   if ((st = check_tensor_args(batch, d, scale, {q, k, v, o}, who))) return st;
   if (qg != nullptr && (st = check_tensor_args(batch, d, scale, {qg, kg, vg}, who))) return st;
   if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, w + ": lse not 16-byte aligned");
+  if ((st = check_o_lo(o_lo, dt, who))) return st;
   if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, w + ": tensor too large");
   if ((st = check_workspace(workspace, ws_bytes, lf_workspace_bytes(P, batch, heads), who))) return st;
   if ((st = check_device(P->device))) return st;
-  return launch_lf_fwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, lse, workspace, stream);
+  return launch_lf_fwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, lse, o_lo, workspace,
+                       stream);
 }
 
 }  // namespace
@@ -577,22 +590,22 @@ int lf_fwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int
 extern "C" {
 
 int lfattn_fwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt, float scale,
-               const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
-               size_t ws_bytes, hipStream_t stream) {
+               const void* q, const void* k, const void* v, void* o, float* lse, void* o_lo,
+               void* workspace, size_t ws_bytes, hipStream_t stream) {
   return lf_fwd_impl("lf_fwd", P, batch, heads, d, dt, scale, q, k, v, nullptr, nullptr,
-                     nullptr, o, lse, workspace, ws_bytes, stream);
+                     nullptr, o, lse, o_lo, workspace, ws_bytes, stream);
 }
 
 int lfattn_fwd_gproj(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt,
                      float scale, const void* q, const void* k, const void* v, const void* qg,
-                     const void* kg, const void* vg, void* o, float* lse, void* workspace,
-                     size_t ws_bytes, hipStream_t stream) {
+                     const void* kg, const void* vg, void* o, float* lse, void* o_lo,
+                     void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (qg == nullptr || kg == nullptr || vg == nullptr) {
     clear_error();
     return set_error(BSATTN_EINVAL, "lf_fwd_gproj: null global projection");
   }
   return lf_fwd_impl("lf_fwd_gproj", P, batch, heads, d, dt, scale, q, k, v, qg, kg, vg, o, lse,
-                     workspace, ws_bytes, stream);
+                     o_lo, workspace, ws_bytes, stream);
 }
 
 size_t lfattn_bwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
@@ -607,9 +620,9 @@ namespace {
 
 int lf_bwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int d,
                 bsattn_dtype dt, float scale, const void* q, const void* k, const void* v,
-                const void* qg, const void* kg, const void* vg, const void* o, const float* lse,
-                const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg, void* dvg,
-                void* workspace, size_t ws_bytes, hipStream_t stream) {
+                const void* qg, const void* kg, const void* vg, const void* o, const void* o_lo,
+                const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dqg,
+                void* dkg, void* dvg, void* workspace, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   const std::string w(who);
   if (P == nullptr) return set_error(BSATTN_EINVAL, w + ": null plan");
@@ -619,6 +632,7 @@ int lf_bwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int
   if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, w + ": only bf16 is built");
   if ((st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, who)))
     return st;
+  if ((st = check_o_lo(o_lo, dt, who))) return st;
   if (qg != nullptr) {
     if ((st = check_tensor_args(batch, d, scale, {qg, kg, vg, dqg, dkg, dvg}, who))) return st;
     const void* outs[6] = {dq, dk, dv, dqg, dkg, dvg};
@@ -631,8 +645,8 @@ int lf_bwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int
   if ((st = check_workspace(workspace, ws_bytes, lf_bwd_workspace_bytes(P, batch, heads), who)))
     return st;
   if ((st = check_device(P->device))) return st;
-  return launch_lf_bwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, lse, dout, dq, dk, dv,
-                       dqg, dkg, dvg, workspace, stream);
+  return launch_lf_bwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, o_lo, lse, dout, dq, dk,
+                       dv, dqg, dkg, dvg, workspace, stream);
 }
 
 }  // namespace
@@ -640,26 +654,27 @@ int lf_bwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int
 extern "C" {
 
 int lfattn_bwd(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt, float scale,
-               const void* q, const void* k, const void* v, const void* o, const float* lse,
-               const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
-               hipStream_t stream) {
+               const void* q, const void* k, const void* v, const void* o, const void* o_lo,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               void* workspace, size_t ws_bytes, hipStream_t stream) {
   return lf_bwd_impl("lf_bwd", P, batch, heads, d, dt, scale, q, k, v, nullptr, nullptr, nullptr,
-                     o, lse, dout, dq, dk, dv, nullptr, nullptr, nullptr, workspace, ws_bytes,
-                     stream);
+                     o, o_lo, lse, dout, dq, dk, dv, nullptr, nullptr, nullptr, workspace,
+                     ws_bytes, stream);
 }
 
 int lfattn_bwd_gproj(const lfattn_plan* P, int batch, int heads, int d, bsattn_dtype dt,
                      float scale, const void* q, const void* k, const void* v, const void* qg,
-                     const void* kg, const void* vg, const void* o, const float* lse,
-                     const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg,
-                     void* dvg, void* workspace, size_t ws_bytes, hipStream_t stream) {
+                     const void* kg, const void* vg, const void* o, const void* o_lo,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     void* dqg, void* dkg, void* dvg, void* workspace, size_t ws_bytes,
+                     hipStream_t stream) {
   if (qg == nullptr || kg == nullptr || vg == nullptr || dqg == nullptr || dkg == nullptr ||
       dvg == nullptr) {
     clear_error();
     return set_error(BSATTN_EINVAL, "lf_bwd_gproj: null global projection or gradient");
   }
-  return lf_bwd_impl("lf_bwd_gproj", P, batch, heads, d, dt, scale, q, k, v, qg, kg, vg, o, lse,
-                     dout, dq, dk, dv, dqg, dkg, dvg, workspace, ws_bytes, stream);
+  return lf_bwd_impl("lf_bwd_gproj", P, batch, heads, d, dt, scale, q, k, v, qg, kg, vg, o, o_lo,
+                     lse, dout, dq, dk, dv, dqg, dkg, dvg, workspace, ws_bytes, stream);
 }
 
 const char* bsattn_status_str(int status) {

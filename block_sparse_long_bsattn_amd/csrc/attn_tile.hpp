@@ -10,62 +10,34 @@ namespace bsattn {
 
 struct FwdState {
   f32x16 o0, o1;   // O^T accumulators: d rows 0..31 and 32..63, column = query
-  f32x16 cinit;    // every register = -(reference max), the QK^T accumulator seed
   float m;         // reference max (log2 units), -inf until the row saw a finite score
-  float l;         // this half-lane's share of the row sum
+  float l;         // this half-lane's share of the row sum (fp32 probabilities)
+  float lb;        // ... of the bf16-rounded probabilities that the PV product uses
 };
 
 __device__ __forceinline__ void fwd_state_init(FwdState& st) {
   st.o0 = zero16();
   st.o1 = zero16();
-  st.cinit = zero16();
   st.m = -INFINITY;
   st.l = 0.f;
+  st.lb = 0.f;
 }
 
-// reference currently baked into st.cinit
-__device__ __forceinline__ float seed_ref(const FwdState& st) {
-  return st.m != -INFINITY ? st.m : 0.f;
-}
-
-// Q operand pre-scaled by sl2 = scale*log2(e) (rounded to bf16), so that the QK^T
-// products come out in log2 units.
-__device__ __forceinline__ void scale_operands(bf16x8 (&qB)[4], float sl2) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const u32x4 u = __builtin_bit_cast(u32x4, qB[c]);
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(bf16_lo(u[e]) * sl2, bf16_hi(u[e]) * sl2);
-    qB[c] = __builtin_bit_cast(bf16x8, w);
-  }
-}
-
-// The same rounding applied to a staged tile (32 values per thread), so that a
-// kernel holding Q in LDS tiles scores with exactly the forward's operands.
-__device__ __forceinline__ void scale_tile(TileRegs& t, float sl2) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(bf16_lo(t.v[u][e]) * sl2, bf16_hi(t.v[u][e]) * sl2);
-    t.v[u] = w;
-  }
-}
-
-// S^T for the 64 keys of the LDS tile sK (natural layout) against this lane's query,
-// accumulated on top of `seed`.  s0 holds keys 0..31, s1 keys 32..63; register r <->
-// key 8*(r/4) + 4*hl + r%4.
+// S^T for the 64 keys of the LDS tile sK (natural layout) against this lane's query:
+// the plain products of the bf16 operands, accumulated in fp32 (the scale is applied
+// afterwards, in fp32).  s0 holds keys 0..31, s1 keys 32..63; register r <-> key
+// 8*(r/4) + 4*hl + r%4.
 __device__ __forceinline__ void qk_tile(const uint16_t* sK, const bf16x8 (&qB)[4], int col,
-                                        int hl, const f32x16& seed, f32x16& s0, f32x16& s1) {
+                                        int hl, f32x16& s0, f32x16& s1) {
   bf16x8 a[8];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     a[2 * c] = ld16(sK + col * kLdsStride + 16 * c + 8 * hl);
     a[2 * c + 1] = ld16(sK + (32 + col) * kLdsStride + 16 * c + 8 * hl);
   }
-  s0 = mfma32(a[0], qB[0], seed);
-  s1 = mfma32(a[1], qB[0], seed);
+  const f32x16 z = zero16();
+  s0 = mfma32(a[0], qB[0], z);
+  s1 = mfma32(a[1], qB[0], z);
 #pragma unroll
   for (int c = 1; c < 4; ++c) {
     s0 = mfma32(a[2 * c], qB[c], s0);
@@ -85,60 +57,51 @@ __device__ __forceinline__ void mask_keys_from(f32x16& s0, f32x16& s1, int hl, i
   }
 }
 
-// Online softmax over one key tile whose scores s = S' - m_c arrive relative to the
-// seeded reference m_c (log2 units; -inf marks an excluded key).  The reference
-// only moves when a block's maximum exceeds it by more than kRescaleSlack, so the
-// unnormalised probabilities 2^s stay below 2^kRescaleSlack and most blocks need
-// no rescale of O and l; the result is exact either way since numerator and
-// denominator share the reference.  On return pc[c] holds the bf16 probabilities
-// of key chunk c as MFMA operands and st.l has grown by their fp32 sum.
+// Online softmax over one key tile of raw scores S = Q.K (fp32; -inf marks an
+// excluded key).  Probabilities are 2^(S*sl2 - m) with sl2 = scale*log2(e) applied
+// in fp32 and m a reference maximum in log2 units.  The reference only moves when
+// a block's maximum exceeds it by more than kRescaleSlack, so the unnormalised
+// probabilities stay below 2^kRescaleSlack and most blocks need no rescale of O
+// and l; the result is exact either way since numerator and denominator share the
+// reference.  On return pc[c] holds the bf16 probabilities of key chunk c as MFMA
+// operands; st.l has grown by their fp32 sum and st.lb by the sum of the bf16
+// values themselves.  O is normalised by lb, which makes it an exact weighted
+// average of V (weights summing to 1) whatever the rounding of each P -- this
+// matters when one key dominates a row, since that key's P (up to
+// 2^kRescaleSlack, not 1) is rounded by up to 2^-8 relative, and the backward's
+// D = rowsum(dO * O) inherits any inconsistency of O.  lse comes from l: the
+// backward recomputes every P from it, and a sum over many rows of P (the
+// gradient of a key that every row sees) would accumulate its rounding.
 constexpr float kRescaleSlack = 8.f;
 
-// ref_used is the reference the scores were seeded with (the reference can have
-// moved since, when the next block's scores are computed ahead of this softmax).
 __device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& st,
-                                             bf16x8 (&pc)[4], float ref_used) {
+                                             bf16x8 (&pc)[4], float sl2) {
   float mx = __builtin_fmaxf(s0[0], s1[0]);
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[r]), s1[r]);
-  mx = partner_max(mx);
-  {
-    const float now = st.m != -INFINITY ? st.m : 0.f;
-    const float shift = now - ref_used;
-    if (__any(shift != 0.f)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] -= shift;
-        s1[r] -= shift;
-      }
-      mx -= shift;
-    }
-  }
+  mx = partner_max(mx) * sl2;   // block maximum, log2 units (-inf stays -inf)
   // a row starts at its first finite score; afterwards it rescales only when the
   // block exceeds the reference by more than the slack
   const bool started = st.m != -INFINITY;
-  const bool need = started ? mx > kRescaleSlack : mx != -INFINITY;
+  const bool need = started ? mx - st.m > kRescaleSlack : mx != -INFINITY;
   if (__any(need)) {
     if (need) {
-      const float mc = started ? st.m : 0.f;    // reference baked into the seed
-      const float m_new = mc + mx;
-      const float alpha = started ? fast_exp2(st.m - m_new) : 0.f;
+      const float alpha = started ? fast_exp2(st.m - mx) : 0.f;
       st.l *= alpha;
+      st.lb *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         st.o0[r] *= alpha;
         st.o1[r] *= alpha;
-        s0[r] -= mx;
-        s1[r] -= mx;
-        st.cinit[r] = -m_new;
       }
-      st.m = m_new;
+      st.m = mx;
     }
   }
+  const float nref = st.m != -INFINITY ? -st.m : 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s0[r] = fast_exp2(s0[r]);
-    s1[r] = fast_exp2(s1[r]);
+    s0[r] = fast_exp2(__builtin_fmaf(s0[r], sl2, nref));
+    s1[r] = fast_exp2(__builtin_fmaf(s1[r], sl2, nref));
   }
   float rs0 = s0[0], rs1 = s1[0];
 #pragma unroll
@@ -151,6 +114,19 @@ __device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& s
   pc[1] = pack8(s0, 8);
   pc[2] = pack8(s1, 0);
   pc[3] = pack8(s1, 8);
+  // row sum of the rounded probabilities: one dot product with (1, 1) per pair
+  float rb0 = 0.f, rb1 = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const u32x4 u0 = __builtin_bit_cast(u32x4, pc[c]);
+    const u32x4 u1 = __builtin_bit_cast(u32x4, pc[c + 2]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      rb0 = sum_bf16x2(u0[e], rb0);
+      rb1 = sum_bf16x2(u1[e], rb1);
+    }
+  }
+  st.lb += rb0 + rb1;
 }
 
 // O^T += V^T P^T; V is the natural LDS tile sV, its transposed operand comes from
@@ -179,32 +155,51 @@ __device__ __forceinline__ void pv_tile(const uint16_t* sV, const bf16x8 (&pc)[4
   pv_mma(v, pc, st);
 }
 
-// Final write of a finished row: O (bf16, normalised) and lse (natural log).
-// orow points at this lane's query row of O; lse_out may be null.  l_tot is the
-// row's full sum (both half-lanes, partner_sum).
-__device__ __forceinline__ void write_o_bf16(const FwdState& st, float l_tot, int hl,
-                                             uint16_t* orow, float* lse_out) {
-  const float inv = 1.f / l_tot;
+// Final write of a finished row: O (bf16, normalised by lb_tot), optionally its
+// rounding residual O - bf16(O) rounded to bf16 (olo_row, may be null), and lse
+// (natural log, from l_tot).  orow / olo_row point at this lane's query row;
+// lse_out may be null.  l_tot and lb_tot are the row's full sums (both
+// half-lanes, partner_sum) of st.l and st.lb.
+__device__ __forceinline__ void write_o_bf16(const FwdState& st, float l_tot, float lb_tot,
+                                             int hl, uint16_t* orow, uint16_t* olo_row,
+                                             float* lse_out) {
+  const float inv = 1.f / lb_tot;
   uint16_t* op = orow + 4 * hl;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    float x0[4], x1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x0[e] = st.o0[4 * j + e] * inv;
+      x1[e] = st.o1[4 * j + e] * inv;
+    }
     u32x2 w0, w1;
-    w0[0] = pack_bf16x2(st.o0[4 * j] * inv, st.o0[4 * j + 1] * inv);
-    w0[1] = pack_bf16x2(st.o0[4 * j + 2] * inv, st.o0[4 * j + 3] * inv);
-    w1[0] = pack_bf16x2(st.o1[4 * j] * inv, st.o1[4 * j + 1] * inv);
-    w1[1] = pack_bf16x2(st.o1[4 * j + 2] * inv, st.o1[4 * j + 3] * inv);
+    w0[0] = pack_bf16x2(x0[0], x0[1]);
+    w0[1] = pack_bf16x2(x0[2], x0[3]);
+    w1[0] = pack_bf16x2(x1[0], x1[1]);
+    w1[1] = pack_bf16x2(x1[2], x1[3]);
     *reinterpret_cast<u32x2*>(op + 8 * j) = w0;
     *reinterpret_cast<u32x2*>(op + 32 + 8 * j) = w1;
+    if (olo_row != nullptr) {
+      uint16_t* lp = olo_row + 4 * hl;
+      u32x2 r0, r1;
+      r0[0] = pack_bf16x2(x0[0] - bf16_lo(w0[0]), x0[1] - bf16_hi(w0[0]));
+      r0[1] = pack_bf16x2(x0[2] - bf16_lo(w0[1]), x0[3] - bf16_hi(w0[1]));
+      r1[0] = pack_bf16x2(x1[0] - bf16_lo(w1[0]), x1[1] - bf16_hi(w1[0]));
+      r1[1] = pack_bf16x2(x1[2] - bf16_lo(w1[1]), x1[3] - bf16_hi(w1[1]));
+      *reinterpret_cast<u32x2*>(lp + 8 * j) = r0;
+      *reinterpret_cast<u32x2*>(lp + 32 + 8 * j) = r1;
+    }
   }
   if (lse_out != nullptr && hl == 0) *lse_out = (st.m + __log2f(l_tot)) * kLn2;
 }
 
-// Partial record of a split full row: O unnormalised [64][64] fp32, then m[64],
-// then l[64] (both log2 units / plain sums), row qr of the query tile.
-constexpr int kPartFloats = kBlock * kHead + 2 * kBlock;
+// Partial record of a split full row: O unnormalised [64][64] fp32, then m[64]
+// (log2 units), l[64] and lb[64] (the two row sums), row qr of the query tile.
+constexpr int kPartFloats = kBlock * kHead + 3 * kBlock;
 
-__device__ __forceinline__ void write_partial(const FwdState& st, float l_tot, int hl, int qr,
-                                              float* rec) {
+__device__ __forceinline__ void write_partial(const FwdState& st, float l_tot, float lb_tot,
+                                              int hl, int qr, float* rec) {
   float* orow = rec + qr * kHead + 4 * hl;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -220,30 +215,36 @@ __device__ __forceinline__ void write_partial(const FwdState& st, float l_tot, i
   if (hl == 0) {
     rec[kBlock * kHead + qr] = st.m;
     rec[kBlock * kHead + kBlock + qr] = l_tot;
+    rec[kBlock * kHead + 2 * kBlock + qr] = lb_tot;
   }
 }
 
 // Merge nseg partial records (stride kPartFloats) for row `row`, columns dq..dq+15,
-// in segment order: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
+// in segment order: M = max m_s, f_s = 2^(m_s - M), L = sum l_s f_s,
+// Lb = sum lb_s f_s, acc = sum O_s f_s (O is then acc / Lb, lse M + log2 L).
 // Up to kMergeBatch records are read with all their loads in flight together (one
 // memory round trip: these merges run on few work-groups and are latency-bound);
 // the arithmetic is the same, in the same order, either way.
 constexpr int kMergeBatch = 8;
 
 __device__ __forceinline__ void merge_partials(const float* base, int nseg, int row, int dq,
-                                               float (&acc)[16], float& M, float& L) {
+                                               float (&acc)[16], float& M, float& L,
+                                               float& Lb) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   L = 0.f;
+  Lb = 0.f;
+  constexpr int kM = kBlock * kHead, kL = kM + kBlock, kLb = kM + 2 * kBlock;
   if (nseg <= kMergeBatch) {
-    float mv[kMergeBatch], lv[kMergeBatch];
+    float mv[kMergeBatch], lv[kMergeBatch], lbv[kMergeBatch];
     f32x4 x[kMergeBatch][4];
 #pragma unroll
     for (int s = 0; s < kMergeBatch; ++s) {
       if (s < nseg) {
         const float* ps = base + (size_t)s * kPartFloats;
-        mv[s] = ps[kBlock * kHead + row];
-        lv[s] = ps[kBlock * kHead + kBlock + row];
+        mv[s] = ps[kM + row];
+        lv[s] = ps[kL + row];
+        lbv[s] = ps[kLb + row];
 #pragma unroll
         for (int q = 0; q < 4; ++q) x[s][q] = *reinterpret_cast<const f32x4*>(ps + row * kHead + dq + 4 * q);
       }
@@ -258,6 +259,7 @@ __device__ __forceinline__ void merge_partials(const float* base, int nseg, int 
       if (s < nseg) {
         const float f = fast_exp2(mv[s] - Mref);
         L += lv[s] * f;
+        Lb += lbv[s] * f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           acc[4 * q] += x[s][q][0] * f;
@@ -271,13 +273,14 @@ __device__ __forceinline__ void merge_partials(const float* base, int nseg, int 
   }
   M = -INFINITY;
 #pragma unroll 8
-  for (int s = 0; s < nseg; ++s) M = fmaxf(M, base[(size_t)s * kPartFloats + kBlock * kHead + row]);
+  for (int s = 0; s < nseg; ++s) M = fmaxf(M, base[(size_t)s * kPartFloats + kM + row]);
   const float Mref = M == -INFINITY ? 0.f : M;
 #pragma unroll 4
   for (int s = 0; s < nseg; ++s) {
     const float* ps = base + (size_t)s * kPartFloats;
-    const float f = fast_exp2(ps[kBlock * kHead + row] - Mref);
-    L += ps[kBlock * kHead + kBlock + row] * f;
+    const float f = fast_exp2(ps[kM + row] - Mref);
+    L += ps[kL + row] * f;
+    Lb += ps[kLb + row] * f;
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(ps + row * kHead + dq + e);
@@ -321,6 +324,28 @@ __device__ __forceinline__ void sum_partials(const float* src, size_t stride, in
     for (int e = 0; e < 16; e += 4) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(ps + e);
       acc[e] += x[0]; acc[e + 1] += x[1]; acc[e + 2] += x[2]; acc[e + 3] += x[3];
+    }
+  }
+}
+
+// The same, plus the bf16 rounding residual of each value at dst_lo (may be null).
+__device__ __forceinline__ void store16_bf16_lo(uint16_t* dst, uint16_t* dst_lo,
+                                                const float (&acc)[16], float mul) {
+#pragma unroll
+  for (int e = 0; e < 16; e += 8) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = acc[e + i] * mul;
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(dst + e) = w;
+    if (dst_lo != nullptr) {
+      u32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r[i] = pack_bf16x2(x[2 * i] - bf16_lo(w[i]), x[2 * i + 1] - bf16_hi(w[i]));
+      *reinterpret_cast<u32x4*>(dst_lo + e) = r;
     }
   }
 }

@@ -69,18 +69,26 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
         dsum = __builtin_fmaf(bf16_lo(dv[e]), bf16_lo(ov[e]), dsum);
         dsum = __builtin_fmaf(bf16_hi(dv[e]), bf16_hi(ov[e]), dsum);
       }
+      if (a.o_lo != nullptr) {   // O + its rounding residual: D to ~2^-17 relative
+        const u32x4 rv = qvalid ? ldg16(a.o_lo + off + 16 * c) : z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dsum = __builtin_fmaf(bf16_lo(dv[e]), bf16_lo(rv[e]), dsum);
+          dsum = __builtin_fmaf(bf16_hi(dv[e]), bf16_hi(rv[e]), dsum);
+        }
+      }
     }
   }
   const float Dq = partner_sum(dsum);   // D = rowsum(dO * O)
   if (it.seg == 0 && hl == 0 && qvalid) a.dbuf[(size_t)it.bh * a.n + qrow] = Dq;
-  // Q pre-scaled by scale*log2(e) exactly as in the forward, and the accumulators
-  // seeded so that the MFMAs return S*scale*log2(e) - lse*log2(e) and dP - D
-  scale_operands(qB, a.sl2);
-  const float lse2 = qvalid ? a.lse[(size_t)it.bh * a.n + qrow] * kLog2e : 0.f;
+  // accumulators seeded so that the MFMAs return S - lse/scale (raw score units,
+  // the scale applied in fp32 below: P = 2^((S - lse/scale) * scale*log2(e))) and
+  // dP - D
+  const float lraw = qvalid ? a.lse[(size_t)it.bh * a.n + qrow] * a.inv_scale : 0.f;
   f32x16 seed_s, seed_d;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    seed_s[r] = -lse2;
+    seed_s[r] = -lraw;
     seed_d[r] = -Dq;
   }
   lds_store_nat(sK[0], kr, tid);
@@ -111,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = fast_exp2(s0[r]) * p0[r];      // dS = P * (dP - D)
-      s1[r] = fast_exp2(s1[r]) * p1[r];
+      s0[r] = fast_exp2(s0[r] * a.sl2) * p0[r];      // dS = P * (dP - D)
+      s1[r] = fast_exp2(s1[r] * a.sl2) * p1[r];
     }
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]; K^T from transpose reads
     const bf16x8 dc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
@@ -158,7 +166,7 @@ template <bool kRagged>
 __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kBlock * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t sO[2][kBlock * kLdsStride];   // dO
-  __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse / scale
   __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
 
   const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
@@ -203,12 +211,11 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
       vB[c] = kvalid ? ld16(a.v + off + 16 * c) : bf16x8{};
     }
   }
-  // K pre-scaled by scale*log2(e) (the products match the forward's scaled-Q ones
-  // up to bf16 rounding); sL and sD hold -lse*log2(e) and -D to seed S and dP
-  scale_operands(kB, a.sl2);
+  // sL and sD hold -lse/scale and -D to seed S (raw score units; the scale is
+  // applied in fp32 before the exponential) and dP
   lds_store_nat(sQ[0], qr, tid);
   lds_store_nat(sO[0], dr, tid);
-  if (tid < kBlock) { sL[0][tid] = -lv * kLog2e; sD[0][tid] = -dval; }
+  if (tid < kBlock) { sL[0][tid] = -lv * a.inv_scale; sD[0][tid] = -dval; }
   // vB is first read inside the loop: drain the prologue's loads here, or the
   // loop's first use of vB waits on every iteration's tile prefetch as well
   wait_all_loads();
@@ -255,8 +262,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = fast_exp2(s0[r]);             // P
-      s1[r] = fast_exp2(s1[r]);
+      s0[r] = fast_exp2(s0[r] * a.sl2);     // P
+      s1[r] = fast_exp2(s1[r] * a.sl2);
       p0[r] *= s0[r];                       // dS = P * (dP - D)
       p1[r] *= s1[r];
     }
@@ -273,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     if (more) {
       lds_store_nat(sQ[cur ^ 1], qr, tid);
       lds_store_nat(sO[cur ^ 1], dr, tid);
-      if (tid < kBlock) { sL[cur ^ 1][tid] = -lv * kLog2e; sD[cur ^ 1][tid] = -dval; }
+      if (tid < kBlock) { sL[cur ^ 1][tid] = -lv * a.inv_scale; sD[cur ^ 1][tid] = -dval; }
     }
   }
 
@@ -358,11 +365,12 @@ size_t bwd_workspace_bytes(const bsattn_layout* L, int batch) {
 }
 
 int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, const void* k,
-               const void* v, const void* o, const float* lse, const void* dout, void* dq,
-               void* dk, void* dv, void* ws, hipStream_t stream) {
+               const void* v, const void* o, const void* o_lo, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t stream) {
   BwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.o = (const uint16_t*)o; a.lse = lse; a.dout = (const uint16_t*)dout;
+  a.o = (const uint16_t*)o; a.o_lo = (const uint16_t*)o_lo; a.lse = lse;
+  a.dout = (const uint16_t*)dout;
   a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
   char* w = (char*)ws;
   a.dbuf = (float*)w;
@@ -381,6 +389,7 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, co
   a.total_items = batch * L->heads * a.items_per_bh;
   a.scale = scale;
   a.sl2 = scale * kLog2e;
+  a.inv_scale = 1.f / scale;
   const int grid = 8 * ((a.total_items + 7) / 8);
   {
     ProfScope prof_("bs_bwd_dq", stream);

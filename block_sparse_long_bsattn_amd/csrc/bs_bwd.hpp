@@ -14,6 +14,7 @@ struct BwdArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* o;
+  const uint16_t* o_lo;   // bf16 rounding residual of O, or null
   const float* lse;
   const uint16_t* dout;
   uint16_t* dq;
@@ -30,7 +31,7 @@ struct BwdArgs {
   int heads, n, nb, g, seg, nseg, split;
   int last_rows;   // tokens in the last block: n - 64 (nb - 1), 1..64
   int items_per_bh, total_items;
-  float scale, sl2;
+  float scale, sl2, inv_scale;   // scale, scale*log2(e), 1/scale
 };
 
 // Tile loads for a sequence that may end inside its last block (kRagged): that

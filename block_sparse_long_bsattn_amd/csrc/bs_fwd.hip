@@ -34,6 +34,7 @@ struct FwdArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
+  uint16_t* o_lo;   // bf16 rounding residual of O, or null
   float* lse;
   float* part;
   const int32_t* col_idx;
@@ -136,7 +137,6 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) qB[c] = !kRagged || qrow < a.n ? ld16(qp + 16 * c) : bf16x8{};
   }
-  scale_operands(qB, a.sl2);
   lds_store_nat(sK[0], kr, tid);
   lds_store_nat(sV[0], vr, tid);
   FwdState st;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
     __syncthreads();
     const bool more = t + 1 < len;
     f32x16 s0, s1;
-    qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
+    qk_tile(sK[cur], qB, col, hl, s0, s1);
     if (kRagged && kb_cur == a.nb - 1) mask_keys_from(s0, s1, hl, a.last_rows);
     const int kb_after = kb_next;   // block of tile t + 1
     if (more) {
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
     pv_load(sV[cur], lane, vA);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 pc[4];
-    softmax_step(s0, s1, st, pc, seed_ref(st));
+    softmax_step(s0, s1, st, pc, a.sl2);
     pv_mma(vA, pc, st);
     if (more) {
       lds_store_nat(sK[cur ^ 1], kr, tid);
@@ -167,29 +167,34 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
     kb_cur = kb_after;
   }
 
-  const float l_tot = partner_sum(st.l);
+  const float l_tot = partner_sum(st.l), lb_tot = partner_sum(st.lb);
   if (it.slot < 0) {
     if (!kRagged || qrow < a.n)
-      write_o_bf16(st, l_tot, hl, a.o + bh_off + (size_t)qrow * kHead,
-                 a.lse != nullptr ? a.lse + (size_t)it.bh * a.n + qrow : nullptr);
+      write_o_bf16(st, l_tot, lb_tot, hl, a.o + bh_off + (size_t)qrow * kHead,
+                   a.o_lo != nullptr ? a.o_lo + bh_off + (size_t)qrow * kHead : nullptr,
+                   a.lse != nullptr ? a.lse + (size_t)it.bh * a.n + qrow : nullptr);
   } else {
-    write_partial(st, l_tot, hl, 32 * wave + col, a.part + (size_t)it.slot * kPartFloats);
+    write_partial(st, l_tot, lb_tot, hl, 32 * wave + col,
+                  a.part + (size_t)it.slot * kPartFloats);
   }
 }
 
 // Merge the segment partials of every split global query block, in segment
-// order: M = max_s m_s, L = sum_s l_s 2^(m_s - M), O = sum_s O_s 2^(m_s - M) / L.
+// order: M = max_s m_s, L = sum_s l_s 2^(m_s - M) (and Lb from the lb_s),
+// O = sum_s O_s 2^(m_s - M) / Lb, lse = M + log2 L.
 __global__ __launch_bounds__(256) void bs_fwd_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ gblk, int heads, int n,
-    int g, int nseg, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    int g, int nseg, uint16_t* __restrict__ o, uint16_t* __restrict__ o_lo,
+    float* __restrict__ lse) {
   const int idx = blockIdx.x;           // (bh, gi)
   const int bh = idx / g, gi = idx - bh * g;
   const int row = threadIdx.x >> 2, dq = (threadIdx.x & 3) * 16;
-  float acc[16], M, L;
-  merge_partials(part + (size_t)idx * nseg * kPartFloats, nseg, row, dq, acc, M, L);
+  float acc[16], M, L, Lb;
+  merge_partials(part + (size_t)idx * nseg * kPartFloats, nseg, row, dq, acc, M, L, Lb);
   const int tok = gblk[gi] * kBlock + row;
   if (tok >= n) return;   // past the end of a sequence that ends inside this block
-  store16_bf16(o + ((size_t)bh * n + tok) * kHead + dq, acc, 1.f / L);
+  const size_t off = ((size_t)bh * n + tok) * kHead + dq;
+  store16_bf16_lo(o + off, o_lo != nullptr ? o_lo + off : nullptr, acc, 1.f / Lb);
   if (lse != nullptr && (threadIdx.x & 3) == 0)
     lse[(size_t)bh * n + tok] = (M + __log2f(L)) * kLn2;
   (void)heads;
@@ -487,7 +492,8 @@ size_t fwd_workspace_bytes(const bsattn_layout* L, int batch) {
 }
 
 int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, const void* q,
-               const void* k, const void* v, void* o, float* lse, void* ws, hipStream_t stream) {
+               const void* k, const void* v, void* o, float* lse, void* o_lo, void* ws,
+               hipStream_t stream) {
   const int bhn = batch * L->heads;
   if (dt == BSATTN_F32) {
     FwdF32Args a;
@@ -521,7 +527,7 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
   }
   FwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.o = (uint16_t*)o; a.lse = lse; a.part = (float*)ws;
+  a.o = (uint16_t*)o; a.o_lo = (uint16_t*)o_lo; a.lse = lse; a.part = (float*)ws;
   a.col_idx = L->d_col_idx; a.row_info = L->d_row_info;
   a.gblk = L->d_gblk;
   a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
@@ -545,7 +551,7 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
     ProfScope prof_("bs_fwd_combine", stream);
     hipLaunchKernelGGL(bs_fwd_combine_kernel, dim3(bhn * L->g), dim3(256), 0, stream,
                        (const float*)ws, L->d_gblk, L->heads, L->n, L->g, sp.nseg,
-                       (uint16_t*)o, lse);
+                       (uint16_t*)o, (uint16_t*)o_lo, lse);
   }
   return check_hip(hipGetLastError(), "bs_fwd_combine launch");
 }

@@ -61,6 +61,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// acc + (both bf16 values of the packed pair w), one v_dot2 with (1, 1): the
+// products by one are exact and the sum is accumulated in fp32.
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
 // Eight consecutive accumulator registers rounded to bf16 and packed in pairs.
 __device__ __forceinline__ u32x4 pack8u(const f32x16& s, int base) {
   u32x4 u;
@@ -74,6 +82,17 @@ __device__ __forceinline__ u32x4 pack8u(const f32x16& s, int base) {
 // The same, as one MFMA operand.
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   return __builtin_bit_cast(bf16x8, pack8u(s, base));
+}
+
+// Registers base .. base+7 of s replaced by what their bf16 rounding h (the
+// operand pack8(s, base) made of them) left out: s - h, exact in fp32.
+__device__ __forceinline__ void residue8(f32x16& s, const bf16x8& h, int base) {
+  const u32x4 u = __builtin_bit_cast(u32x4, h);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s[base + 2 * e] -= bf16_lo(u[e]);
+    s[base + 2 * e + 1] -= bf16_hi(u[e]);
+  }
 }
 
 __device__ __forceinline__ bf16x8 ld16(const uint16_t* p) {

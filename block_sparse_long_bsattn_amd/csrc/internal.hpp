@@ -100,17 +100,20 @@ int check_hip(hipError_t e, const char* what);
 // Launch helpers implemented in the kernel translation units.
 int launch_layout_rowptr(bsattn_layout* L, hipStream_t stream);
 int launch_layout_build(bsattn_layout* L, hipStream_t stream);
+// o_lo (forward: written, backward: read) is the bf16 rounding residual of O, or
+// null.
 int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale,
                const void* q, const void* k, const void* v, void* o, float* lse,
-               void* ws, hipStream_t stream);
+               void* o_lo, void* ws, hipStream_t stream);
 int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q,
-               const void* k, const void* v, const void* o, const float* lse,
-               const void* dout, void* dq, void* dk, void* dv, void* ws,
+               const void* k, const void* v, const void* o, const void* o_lo,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
                hipStream_t stream);
 // qg, kg, vg (and dqg, dkg, dvg) may be null: one projection set for every row.
 int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,
-                  const void* vg, void* o, float* lse, void* ws, hipStream_t stream);
+                  const void* vg, void* o, float* lse, void* o_lo, void* ws,
+                  hipStream_t stream);
 
 size_t fwd_workspace_bytes(const bsattn_layout* L, int batch);   // enough for either dtype
 size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt);
@@ -118,9 +121,9 @@ size_t bwd_workspace_bytes(const bsattn_layout* L, int batch);
 size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads);
 int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,
-                  const void* vg, const void* o, const float* lse, const void* dout, void* dq,
-                  void* dk, void* dv, void* dqg, void* dkg, void* dvg, void* ws,
-                  hipStream_t stream);
+                  const void* vg, const void* o, const void* o_lo, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg,
+                  void* dvg, void* ws, hipStream_t stream);
 size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads);
 
 }  // namespace bsattn

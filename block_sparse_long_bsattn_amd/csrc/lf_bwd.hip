@@ -44,6 +44,7 @@ struct LfBwdArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* o;
+  const uint16_t* o_lo;   // bf16 rounding residual of O, or null
   const float* lse;
   const uint16_t* dout;
   uint16_t* dq;
@@ -70,8 +71,10 @@ struct LfBwdArgs {
   int nct, nct_plain, nct_g, ph;   // class tiles (all / without / with global keys), heads
                                    // per head period
   LfWindow win;                    // key range of each row, in class indices
-  int dq_band_items, dq_items, kv_plain_items, kv_seg_items, kv_items;
-  float scale, sl2;
+  int dq_band_items, dq_items;
+  int kv_plain_items, kv_items;   // lf_bwd_dkdv_kernel: window items, then global-row items
+  int kv_seg_items;               // lf_bwd_dkdv_seg_kernel: global-column segments
+  float scale, sl2, inv_scale;   // scale, scale*log2(e), 1/scale
 };
 
 // ---------------------------------------------------------------------------
@@ -164,11 +167,18 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
         dsum = __builtin_fmaf(bf16_lo(dv[e]), bf16_lo(ov[e]), dsum);
         dsum = __builtin_fmaf(bf16_hi(dv[e]), bf16_hi(ov[e]), dsum);
       }
+      if (a.o_lo != nullptr) {   // O + its rounding residual: D to ~2^-17 relative
+        const u32x4 rv = ldg16(a.o_lo + off + 16 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dsum = __builtin_fmaf(bf16_lo(dv[e]), bf16_lo(rv[e]), dsum);
+          dsum = __builtin_fmaf(bf16_hi(dv[e]), bf16_hi(rv[e]), dsum);
+        }
+      }
     }
   }
   const float Dq = partner_sum(dsum);   // D = rowsum(dO * O)
   if (seg == 0 && hl == 0 && ((vm_q >> xq) & 1ull)) a.dbuf[(size_t)bh * a.n + p] = Dq;
-  scale_operands(qB, a.sl2);
   const float lse2 = a.lse[(size_t)bh * a.n + p] * kLog2e;
   if (x < ntile) {
     lds_store_nat(sK[0], kr, tid);
@@ -215,8 +225,10 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = fast_exp2(s0[r] - lse2) * (p0[r] - Dq);      // dS = P * (dP - D)
-      s1[r] = fast_exp2(s1[r] - lse2) * (p1[r] - Dq);
+      // P = 2^(S*scale*log2(e) - lse*log2(e)), the scale applied in fp32;
+      // dS = P * (dP - D)
+      s0[r] = fast_exp2(__builtin_fmaf(s0[r], a.sl2, -lse2)) * (p0[r] - Dq);
+      s1[r] = fast_exp2(__builtin_fmaf(s1[r], a.sl2, -lse2)) * (p1[r] - Dq);
     }
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]; K^T from transpose reads
     const bf16x8 dc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
@@ -400,14 +412,12 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
       vB[c] = ld16((kGRows ? a.vg : a.v) + off + 16 * c);
     }
   }
-  // Q tiles are staged pre-scaled by scale*log2(e), rounded to bf16 exactly as the
-  // forward rounds its Q operand, so P here is the forward's P bit for bit in the
-  // exponent; dK is rescaled by scale / (scale*log2(e)) at the end
+  // sL and sD hold -lse/scale and -D to seed S (raw score units; the scale is
+  // applied in fp32 before the exponential) and dP
   if (x < ntile) {
-    scale_tile(qr, a.sl2);
     lds_store_nat(sQ[0], qr, tid);
     lds_store_nat(sO[0], dr, tid);
-    if (tid < kBlock) { sL[0][tid] = -lv * kLog2e; sD[0][tid] = -dval; }
+    if (tid < kBlock) { sL[0][tid] = -lv * a.inv_scale; sD[0][tid] = -dval; }
   }
   wait_all_loads();
 
@@ -482,8 +492,8 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = fast_exp2(s0[r]);             // P
-      s1[r] = fast_exp2(s1[r]);
+      s0[r] = fast_exp2(s0[r] * a.sl2);     // P
+      s1[r] = fast_exp2(s1[r] * a.sl2);
       p0[r] *= s0[r];                       // dS = P * (dP - D)
       p1[r] *= s1[r];
     }
@@ -497,17 +507,37 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
       dk0 = mfma32(ld_tr8(sQ[cur], 0, c, lane), dc[c], dk0);
       dk1 = mfma32(ld_tr8(sQ[cur], 1, c, lane), dc[c], dk1);
     }
+    if constexpr (kKind == kKvSeg) {
+      // A column holding global keys sums over every row of the sequence, and with a
+      // short window each row can put a large share of its mass on a global key:
+      // then the bf16 rounding of P and dS (2^-9 relative per term) would add up
+      // over n terms of dV and dK.  These items also feed the rounding residues,
+      // P - bf16(P) and dS - bf16(dS) rounded to bf16, through the same products,
+      // which leaves about 2^-17 relative per term.
+      residue8(s0, pc[0], 0); residue8(s0, pc[1], 8);
+      residue8(s1, pc[2], 0); residue8(s1, pc[3], 8);
+      residue8(p0, dc[0], 0); residue8(p0, dc[1], 8);
+      residue8(p1, dc[2], 0); residue8(p1, dc[3], 8);
+      const bf16x8 pl[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
+      const bf16x8 dl[4] = {pack8(p0, 0), pack8(p0, 8), pack8(p1, 0), pack8(p1, 8)};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        dv0 = mfma32(ld_tr8(sO[cur], 0, c, lane), pl[c], dv0);
+        dv1 = mfma32(ld_tr8(sO[cur], 1, c, lane), pl[c], dv1);
+        dk0 = mfma32(ld_tr8(sQ[cur], 0, c, lane), dl[c], dk0);
+        dk1 = mfma32(ld_tr8(sQ[cur], 1, c, lane), dl[c], dk1);
+      }
+    }
     if (xn < ntile) {
-      scale_tile(qr, a.sl2);
       lds_store_nat(sQ[cur ^ 1], qr, tid);
       lds_store_nat(sO[cur ^ 1], dr, tid);
-      if (tid < kBlock) { sL[cur ^ 1][tid] = -lv * kLog2e; sD[cur ^ 1][tid] = -dval; }
+      if (tid < kBlock) { sL[cur ^ 1][tid] = -lv * a.inv_scale; sD[cur ^ 1][tid] = -dval; }
     }
     cur ^= 1;
     x = xn;
   }
 
-  const float sc = a.scale / a.sl2;   // dK was accumulated against the scaled Q
+  const float sc = a.scale;
   if constexpr (kKind != kKvSeg) {
     if (!key_valid) return;
     const size_t off = bh_off + (size_t)q_tok * kHead + 4 * hl;
@@ -549,22 +579,35 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   }
 }
 
-// Built at 256 VGPRs with no spills, so it runs two waves per SIMD, about 25 %
-// faster than one.  Asking for two waves explicitly makes the compiler spill two
-// registers instead; the resource report of the build shows which one it got.
+// The window and global-row items: built at 256 VGPRs with no spills, so they run
+// two waves per SIMD, about 25 % faster than one.  (Asking for two waves
+// explicitly makes the compiler spill two registers instead; the resource report
+// of the build shows which one it got.)
 __global__ __launch_bounds__(kThreads) void lf_bwd_dkdv_kernel(LfBwdArgs a) {
   __shared__ __attribute__((aligned(16))) LdsTile sQ[2];
   __shared__ __attribute__((aligned(16))) LdsTile sO[2];   // dO
-  __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse / scale
   __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
   const int v = xcd_remap(blockIdx.x, a.kv_items);
   if (v >= a.kv_items) return;
   if (v < a.kv_plain_items)
     lf_bwd_dkdv_item<kKvPlain>(a, v, sQ, sO, sL, sD);
-  else if (v < a.kv_seg_items)
-    lf_bwd_dkdv_item<kKvSeg>(a, v - a.kv_plain_items, sQ, sO, sL, sD);
   else
-    lf_bwd_dkdv_item<kKvGRows>(a, v - a.kv_seg_items, sQ, sO, sL, sD);
+    lf_bwd_dkdv_item<kKvGRows>(a, v - a.kv_plain_items, sQ, sO, sL, sD);
+}
+
+// The segments of key class tiles holding global keys, a launch of their own: their
+// residue products need more registers than the window items may use at two
+// waves per SIMD.  Launched before lf_bwd_dkdv_kernel: they are few and as long as
+// its items.
+__global__ __launch_bounds__(kThreads) void lf_bwd_dkdv_seg_kernel(LfBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) LdsTile sQ[2];
+  __shared__ __attribute__((aligned(16))) LdsTile sO[2];   // dO
+  __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse / scale
+  __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
+  const int v = xcd_remap(blockIdx.x, a.kv_seg_items);
+  if (v >= a.kv_seg_items) return;
+  lf_bwd_dkdv_item<kKvSeg>(a, v, sQ, sO, sL, sD);
 }
 
 // Segment sums in segment order.  Work-groups [0, B*H*ngt): dQ of global tile gt,
@@ -634,14 +677,15 @@ size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads) {
 
 int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,
-                  const void* vg, const void* o, const float* lse, const void* dout, void* dq,
-                  void* dk, void* dv, void* dqg, void* dkg, void* dvg, void* ws,
-                  hipStream_t stream) {
+                  const void* vg, const void* o, const void* o_lo, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg,
+                  void* dvg, void* ws, hipStream_t stream) {
   const LfBwdWs w = lf_bwd_ws_layout(P, batch, heads);
   char* base = (char*)ws;
   LfBwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.o = (const uint16_t*)o; a.lse = lse; a.dout = (const uint16_t*)dout;
+  a.o = (const uint16_t*)o; a.o_lo = (const uint16_t*)o_lo; a.lse = lse;
+  a.dout = (const uint16_t*)dout;
   a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
   a.gproj = qg != nullptr ? 1 : 0;
   a.qg = (const uint16_t*)(a.gproj ? qg : q);
@@ -662,13 +706,14 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const
   a.win = lf_window(P);
   a.scale = scale;
   a.sl2 = scale * kLog2e;
+  a.inv_scale = 1.f / scale;
   const int bhn = batch * heads;
   const int periods = bhn / a.ph;
   a.dq_band_items = periods * a.nct;
   a.dq_items = a.dq_band_items + bhn * P->ngt * P->nseg;
   a.kv_plain_items = periods * a.nct_plain;
-  a.kv_seg_items = a.kv_plain_items + periods * a.nct_g * P->nseg;
-  a.kv_items = a.kv_seg_items + (a.gproj ? bhn * P->nt : 0);
+  a.kv_items = a.kv_plain_items + (a.gproj ? bhn * P->nt : 0);
+  a.kv_seg_items = periods * a.nct_g * P->nseg;
   int st;
   {
     ProfScope prof_("lf_bwd_dq", stream);
@@ -676,12 +721,22 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const
                        stream, a);
   }
   if ((st = check_hip(hipGetLastError(), "lf_bwd_dq launch"))) return st;
-  {
-    ProfScope prof_("lf_bwd_dkdv", stream);
-    hipLaunchKernelGGL(lf_bwd_dkdv_kernel, dim3(8 * ((a.kv_items + 7) / 8)), dim3(kThreads), 0,
-                       stream, a);
+  if (a.kv_seg_items > 0) {
+    {
+      ProfScope prof_("lf_bwd_dkdv_seg", stream);
+      hipLaunchKernelGGL(lf_bwd_dkdv_seg_kernel, dim3(8 * ((a.kv_seg_items + 7) / 8)),
+                         dim3(kThreads), 0, stream, a);
+    }
+    if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv_seg launch"))) return st;
   }
-  if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv launch"))) return st;
+  if (a.kv_items > 0) {
+    {
+      ProfScope prof_("lf_bwd_dkdv", stream);
+      hipLaunchKernelGGL(lf_bwd_dkdv_kernel, dim3(8 * ((a.kv_items + 7) / 8)), dim3(kThreads),
+                         0, stream, a);
+    }
+    if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv launch"))) return st;
+  }
   const int nq_groups = bhn * P->ngt;
   const int groups = nq_groups + periods * a.nct_g * 2;
   if (groups == 0) return 0;

@@ -41,6 +41,7 @@ struct LfArgs {
   const uint16_t* kg;   // separate global projections are given)
   const uint16_t* vg;
   uint16_t* o;
+  uint16_t* o_lo;       // bf16 rounding residual of O, or null
   float* lse;
   float* part;          // [B*H*ngt*nseg] partial records of the global query rows
   const int32_t* gtok;  // [ng]
@@ -90,7 +91,6 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
     return global_outside(a.gtok, a.ng, gt, cls, stride, lo_u, hi_u, lane);
   };
 
-  scale_operands(qB, a.sl2);
   FwdState st;
   fwd_state_init(st);
   auto tile_load = [&](int x, TileRegs& kr, TileRegs& vr) {
@@ -122,7 +122,7 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
     const int xn = next_tile(x + 1);
     if (xn < ntile) tile_load(xn, kr, vr);
     f32x16 s0, s1;
-    qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
+    qk_tile(sK[cur], qB, col, hl, s0, s1);
     if (x < nband) {
       const int u = lo_u + x;
       const uint64_t vm = valid_rows(u, nc);
@@ -137,7 +137,7 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
       if (el != ~0ull) mask_rows(s0, s1, hl, el);
     }
     bf16x8 pc[4];
-    softmax_step(s0, s1, st, pc, seed_ref(st));
+    softmax_step(s0, s1, st, pc, a.sl2);
     pv_tile(sV[cur], pc, lane, st);
     if (xn < ntile) {
       lds_store_nat(sK[cur ^ 1], kr, tid);
@@ -147,9 +147,10 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
     x = xn;
   }
 
-  const float l_tot = partner_sum(st.l);
+  const float l_tot = partner_sum(st.l), lb_tot = partner_sum(st.lb);
   if (((vm_q & ~gm_q) >> xq) & 1ull)
-    write_o_bf16(st, l_tot, hl, a.o + bh_off + (size_t)p * kHead,
+    write_o_bf16(st, l_tot, lb_tot, hl, a.o + bh_off + (size_t)p * kHead,
+                 a.o_lo != nullptr ? a.o_lo + bh_off + (size_t)p * kHead : nullptr,
                  a.lse != nullptr ? a.lse + (size_t)bh * a.n + p : nullptr);
 }
 
@@ -172,7 +173,6 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
   }
   const int u_begin = s * kLfSeg;
   const int u_end = min(a.nt, u_begin + kLfSeg);
-  scale_operands(qB, a.sl2);
   FwdState st;
   fwd_state_init(st);
   TileRegs kr, vr;
@@ -189,21 +189,21 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
       gload_class(vr, a.vg + bh_off, 0, 1, u + 1, a.n, tid);
     }
     f32x16 s0, s1;
-    qk_tile(sK[cur], qB, col, hl, st.cinit, s0, s1);
+    qk_tile(sK[cur], qB, col, hl, s0, s1);
     if (u == a.nt - 1) {   // keys past the end of a sequence that ends inside a tile
       const uint64_t vm = valid_rows(u, a.n);
       if (vm != ~0ull) mask_rows(s0, s1, hl, vm);
     }
     bf16x8 pc[4];
-    softmax_step(s0, s1, st, pc, seed_ref(st));
+    softmax_step(s0, s1, st, pc, a.sl2);
     pv_tile(sV[cur], pc, lane, st);
     if (more) {
       lds_store_nat(sK[cur ^ 1], kr, tid);
       lds_store_nat(sV[cur ^ 1], vr, tid);
     }
   }
-  const float l_tot = partner_sum(st.l);
-  write_partial(st, l_tot, hl, qr, a.part + (size_t)v * kPartFloats);
+  const float l_tot = partner_sum(st.l), lb_tot = partner_sum(st.lb);
+  write_partial(st, l_tot, lb_tot, hl, qr, a.part + (size_t)v * kPartFloats);
 }
 
 // Band items first, then the global-row segments (about as long as a band item).
@@ -225,9 +225,10 @@ __global__ __launch_bounds__(256) void lf_combine_kernel(LfArgs a) {
   const int j = gt * kBlock + row;
   if (j >= a.ng) return;
   const int tok = a.gtok[j];   // read alongside the partial records
-  float acc[16], M, L;
-  merge_partials(a.part + (size_t)idx * a.nseg * kPartFloats, a.nseg, row, dq, acc, M, L);
-  store16_bf16(a.o + ((size_t)bh * a.n + tok) * kHead + dq, acc, 1.f / L);
+  float acc[16], M, L, Lb;
+  merge_partials(a.part + (size_t)idx * a.nseg * kPartFloats, a.nseg, row, dq, acc, M, L, Lb);
+  const size_t off = ((size_t)bh * a.n + tok) * kHead + dq;
+  store16_bf16_lo(a.o + off, a.o_lo != nullptr ? a.o_lo + off : nullptr, acc, 1.f / Lb);
   if (a.lse != nullptr && (threadIdx.x & 3) == 0)
     a.lse[(size_t)bh * a.n + tok] = (M + __log2f(L)) * kLn2;
 }
@@ -241,13 +242,14 @@ size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads) {
 
 int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,
-                  const void* vg, void* o, float* lse, void* ws, hipStream_t stream) {
+                  const void* vg, void* o, float* lse, void* o_lo, void* ws,
+                  hipStream_t stream) {
   LfArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.qg = (const uint16_t*)(qg != nullptr ? qg : q);
   a.kg = (const uint16_t*)(kg != nullptr ? kg : k);
   a.vg = (const uint16_t*)(vg != nullptr ? vg : v);
-  a.o = (uint16_t*)o; a.lse = lse;
+  a.o = (uint16_t*)o; a.o_lo = (uint16_t*)o_lo; a.lse = lse;
   const bool has_g = P->ng > 0;
   a.part = has_g ? (float*)ws : nullptr;
   a.gtok = P->d_gtok; a.gidx = P->d_gidx; a.tile_gmask = P->d_tile_gmask;

@@ -43,13 +43,17 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(f32_to_bf16_bits(x))
 
 
-def make_tensor(seed: int, shape, dtype: str):
+def make_tensor(seed: int, shape, dtype: str, std: float = 1.0):
     """Return (host_values_for_device, exact_values_f64).
 
+    Values are N(0, std^2): the standard normal draw times ``std`` in float32,
+    before any rounding.
     dtype "f32": device gets float32, oracle gets the same values in fp64.
     dtype "bf16": device gets uint16 bf16 bits, oracle gets their exact fp64 value.
     """
     x = normal_f32(seed, shape)
+    if std != 1.0:
+        x = x * np.float32(std)
     if dtype == "f32":
         return x, x.astype(np.float64)
     if dtype == "bf16":

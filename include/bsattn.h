@@ -26,8 +26,17 @@
  *     type given by bsattn_dtype (bf16 = raw 16-bit bfloat16 bits).
  *   - lse is float32 [batch, heads, n], natural-log log-sum-exp of the scaled
  *     scores of each query row over its allowed keys.
- *   - Accumulation and softmax run in fp32; outputs are rounded (nearest-even) to
- *     the input type.
+ *   - Products of the bf16 operands are taken exactly and accumulated in fp32; the
+ *     score scale is applied in fp32; the softmax runs in fp32 and the
+ *     probabilities are rounded to bf16 as MFMA operands.  Outputs are rounded
+ *     (nearest-even) to the input type.
+ *   - o_lo (optional, bf16 only): the forward can also write the rounding residual
+ *     of O, o_lo = bf16(O - bf16(O)) from the fp32 O, in the layout of O.  Passed
+ *     to the backward it makes D = rowsum(dout * O), which enters every gradient
+ *     through dS = P * (dP - D), exact to about 2^-17 instead of 2^-9 relative:
+ *     with a peaked softmax (scores of 20 and more) the backward's D from the
+ *     rounded O alone costs dQ and dK more than 2e-2 beyond their own bf16
+ *     rounding.  NULL skips it (forward: not written; backward: D from O).
  *   - Device pointers must be 16-byte aligned.  All device work is enqueued on
  *     `stream` and is asynchronous unless a function says otherwise.
  *   - The caller owns every tensor and every workspace.  Compute calls never
@@ -149,16 +158,20 @@ size_t bsattn_bwd_workspace(const bsattn_layout* layout, int batch, int d);
  *   q, k, v     DEVICE [batch, heads, n, d] of type dt.
  *   o           DEVICE [batch, heads, n, d] of type dt, written.
  *   lse         DEVICE float32 [batch, heads, n], written; may be NULL.
+ *   o_lo        DEVICE bf16 [batch, heads, n, d], the rounding residual of O
+ *               (see the conventions above), written; may be NULL; must be NULL
+ *               for BSATTN_F32 (EINVAL otherwise).
  *   workspace   DEVICE scratch of at least bsattn_fwd_workspace() bytes (NULL if 0).
  * Returns OK, EINVAL, EUNSUPPORTED or EHIP.
  */
 int bsattn_fwd(const bsattn_layout* layout, int batch, int d, bsattn_dtype dt, float scale,
-               const void* q, const void* k, const void* v, void* o, float* lse,
+               const void* q, const void* k, const void* v, void* o, float* lse, void* o_lo,
                void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Backward: the exact gradient of bsattn_fwd for the loss <dout, O>.
  *   q, k, v, o  DEVICE [batch, heads, n, d] (o from bsattn_fwd).
+ *   o_lo        DEVICE bf16 [batch, heads, n, d] from bsattn_fwd, or NULL.
  *   lse         DEVICE float32 [batch, heads, n] from bsattn_fwd (required).
  *   dout        DEVICE [batch, heads, n, d].
  *   dq, dk, dv  DEVICE [batch, heads, n, d], written.
@@ -170,8 +183,8 @@ int bsattn_fwd(const bsattn_layout* layout, int batch, int d, bsattn_dtype dt, f
  */
 int bsattn_bwd(const bsattn_layout* layout, int batch, int d, bsattn_dtype dt, float scale,
                const void* q, const void* k, const void* v, const void* o,
-               const float* lse, const void* dout, void* dq, void* dk, void* dv,
-               void* workspace, size_t ws_bytes, hipStream_t stream);
+               const void* o_lo, const float* lse, const void* dout, void* dq, void* dk,
+               void* dv, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Longformer sliding window + symmetric global attention                     */
@@ -238,14 +251,15 @@ int lfattn_plan_destroy(lfattn_plan* plan);
 size_t lfattn_fwd_workspace(const lfattn_plan* plan, int batch, int heads, int d);
 
 /*
- * Longformer forward: O and lse as in bsattn_fwd, with the plan's token pattern.
- * Query rows of global tokens are full rows.  q, k, v, o are DEVICE [batch, heads,
- * n, d]; lse DEVICE float32 [batch, heads, n] or NULL.  dt must be BSATTN_BF16.
+ * Longformer forward: O, lse and o_lo as in bsattn_fwd, with the plan's token
+ * pattern.  Query rows of global tokens are full rows.  q, k, v, o are DEVICE
+ * [batch, heads, n, d]; lse DEVICE float32 [batch, heads, n] or NULL; o_lo DEVICE
+ * bf16 [batch, heads, n, d] or NULL.  dt must be BSATTN_BF16.
  * Returns OK, EINVAL, EUNSUPPORTED or EHIP.
  */
 int lfattn_fwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,
                float scale, const void* q, const void* k, const void* v, void* o,
-               float* lse, void* workspace, size_t ws_bytes, hipStream_t stream);
+               float* lse, void* o_lo, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes lfattn_bwd needs.  d must be 64.  0 for invalid arguments. */
 size_t lfattn_bwd_workspace(const lfattn_plan* plan, int batch, int heads, int d);
@@ -255,20 +269,24 @@ size_t lfattn_bwd_workspace(const lfattn_plan* plan, int batch, int heads, int d
  * (the page describes the forward only; the gradient is the plain one of
  * softmax attention restricted to the plan's token pattern).
  *   q, k, v, o  DEVICE [batch, heads, n, d] (o from lfattn_fwd).
+ *   o_lo        DEVICE bf16 [batch, heads, n, d] from lfattn_fwd, or NULL.
  *   lse         DEVICE float32 [batch, heads, n] from lfattn_fwd (required).
  *   dout        DEVICE [batch, heads, n, d].
  *   dq, dk, dv  DEVICE [batch, heads, n, d], written.
  *   workspace   DEVICE scratch of at least lfattn_bwd_workspace() bytes.
  * Every output tile has a single owning work-group; the full rows of global
  * queries and the full columns of key tiles holding global keys are split into
- * segments whose fp32 partials are summed in a fixed order.  No atomics, so
- * results are bitwise reproducible.  dt must be BSATTN_BF16 (else EUNSUPPORTED).
- * Returns OK, EINVAL, EUNSUPPORTED or EHIP.
+ * segments whose fp32 partials are summed in a fixed order.  A column holding a
+ * global key sums over every row, and with a short window each row may put a
+ * large share of its mass there, so those columns also feed the bf16 rounding
+ * residues of P and dS through their products (about 2^-17 instead of 2^-9
+ * relative per term).  No atomics, so results are bitwise reproducible.  dt must
+ * be BSATTN_BF16 (else EUNSUPPORTED).  Returns OK, EINVAL, EUNSUPPORTED or EHIP.
  */
 int lfattn_bwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,
                float scale, const void* q, const void* k, const void* v, const void* o,
-               const float* lse, const void* dout, void* dq, void* dk, void* dv,
-               void* workspace, size_t ws_bytes, hipStream_t stream);
+               const void* o_lo, const float* lse, const void* dout, void* dq, void* dk,
+               void* dv, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Separate projections for the global attention ([LF] §3.1 "Linear Projections for
@@ -285,8 +303,8 @@ int lfattn_bwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtyp
  */
 int lfattn_fwd_gproj(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,
                      float scale, const void* q, const void* k, const void* v, const void* qg,
-                     const void* kg, const void* vg, void* o, float* lse, void* workspace,
-                     size_t ws_bytes, hipStream_t stream);
+                     const void* kg, const void* vg, void* o, float* lse, void* o_lo,
+                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Gradient of lfattn_fwd_gproj for the loss <dout, O>: dq, dk, dv for the first
@@ -297,9 +315,10 @@ int lfattn_fwd_gproj(const lfattn_plan* plan, int batch, int heads, int d, bsatt
  */
 int lfattn_bwd_gproj(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,
                      float scale, const void* q, const void* k, const void* v, const void* qg,
-                     const void* kg, const void* vg, const void* o, const float* lse,
-                     const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg,
-                     void* dvg, void* workspace, size_t ws_bytes, hipStream_t stream);
+                     const void* kg, const void* vg, const void* o, const void* o_lo,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     void* dqg, void* dkg, void* dvg, void* workspace, size_t ws_bytes,
+                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Diagnostics                                                                */

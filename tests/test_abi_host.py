@@ -75,12 +75,12 @@ def test_layout_build_rejects_bad_arguments(args, code):
 
 def test_null_handles_are_rejected():
     lib = _lib.load()
-    assert lib.bsattn_fwd(None, 1, 64, 1, 0.125, None, None, None, None, None, None, 0, None) == -1
-    assert lib.bsattn_bwd(None, 1, 64, 1, 0.125, *([None] * 9), None, 0, None) == -1
-    assert lib.lfattn_fwd(None, 1, 1, 64, 1, 0.125, *([None] * 5), None, 0, None) == -1
-    assert lib.lfattn_bwd(None, 1, 1, 64, 1, 0.125, *([None] * 9), None, 0, None) == -1
-    assert lib.lfattn_fwd_gproj(None, 1, 1, 64, 1, 0.125, *([None] * 8), None, 0, None) == -1
-    assert lib.lfattn_bwd_gproj(None, 1, 1, 64, 1, 0.125, *([None] * 15), None, 0, None) == -1
+    assert lib.bsattn_fwd(None, 1, 64, 1, 0.125, *([None] * 6), None, 0, None) == -1
+    assert lib.bsattn_bwd(None, 1, 64, 1, 0.125, *([None] * 10), None, 0, None) == -1
+    assert lib.lfattn_fwd(None, 1, 1, 64, 1, 0.125, *([None] * 6), None, 0, None) == -1
+    assert lib.lfattn_bwd(None, 1, 1, 64, 1, 0.125, *([None] * 10), None, 0, None) == -1
+    assert lib.lfattn_fwd_gproj(None, 1, 1, 64, 1, 0.125, *([None] * 9), None, 0, None) == -1
+    assert lib.lfattn_bwd_gproj(None, 1, 1, 64, 1, 0.125, *([None] * 16), None, 0, None) == -1
     assert lib.bsattn_layout_info(None, None, None, None) == -1
     assert lib.bsattn_layout_rebuild(None, 1, None) == -1
     assert lib.bsattn_fwd_workspace(None, 1, 64) == 0

@@ -57,21 +57,80 @@ def test_bwd_full_compare(case):
 
 
 def test_bwd_full_size_sampled():
-    """batch 4, 12 heads, n = 4096, G = {0, 63}, w = 3, r = 3: the whole job runs on
-    the GPU; three (batch, head) slices are compared in full with the oracle."""
+    """batch 4, 12 heads, n = 4096, G = {0, 63}, w = 3, r = 3 (the training-step
+    workload, run as the benchmark runs it: the forward writes the rounding residual
+    of O and the backward takes it): the whole job runs on the GPU.  Three (batch, head) slices are
+    compared in full with the oracle (O, lse, dQ, dK, dV); in every one of the 48
+    slices, sampled rows of O, lse and dQ, and dK, dV of two non-global key blocks
+    (the oracle run on exactly the query rows that attend to them, so those
+    gradients are exact); and per slice the sum identities (dV rows sum to the dO
+    rows, dK rows to zero), which cover the global columns."""
     n, heads, bsz, G = 4096, 12, 4, [0, 63]
-    say("bwd full-size n=4096 H=12 B=4")
-    (qr, kr, vr, dor), got = run_bwd(n, heads, bsz, G, 3, 3, I.SEED_LAYOUT)
-    mask, _ = oracle_mask(n, heads, G, 3, 3, I.SEED_LAYOUT)
+    say("fwd+bwd full-size n=4096 H=12 B=4")
+    shape = (bsz, heads, n, 64)
+    (q, k, v, do), (qr, kr, vr, dor) = qkv(shape, "bf16",
+                                          (I.SEED_Q, I.SEED_K, I.SEED_V, I.SEED_DO))
+    h = B.bsattn_layout_build(n, 64, heads, G, 3, 3, I.SEED_LAYOUT)
+    try:
+        o = torch.empty_like(q)
+        lse = torch.empty((bsz, heads, n), dtype=torch.float32, device="cuda")
+        wsf = torch.empty(max(1, B.bsattn_fwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(1, B.bsattn_bwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        o_lo = torch.empty_like(q)
+        B.bsattn_fwd(h, q, k, v, o, lse, wsf, o_lo=o_lo)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        B.bsattn_bwd(h, q, k, v, o, lse, do, dq, dk, dv, wsb, o_lo=o_lo)
+        torch.cuda.synchronize()
+    finally:
+        B.bsattn_layout_destroy(h)
+    o, lse, dq, dk, dv = (to_f64(t) for t in (o, lse, dq, dk, dv))
+    mask, lay = oracle_mask(n, heads, G, 3, 3, I.SEED_LAYOUT)
     worst = 0.0
-    for bi, h in ((0, 0), (1, 5), (3, 11)):
-        sl = (slice(bi, bi + 1), slice(h, h + 1))
-        ref = OA.attention_bwd(qr[sl], kr[sl], vr[sl], dor[sl],
-                               lambda hh, p0, p1: mask(h, p0, p1), 1 / 8.0, row_chunk=1024)
-        for a, b in zip(got, ref):
-            worst = max(worst, max_abs(a[bi, h], b[0, 0]))
-    say(f"   worst max-abs {worst:.3e}")
+    for bi, hh in ((0, 0), (1, 5), (3, 11)):
+        sl = (slice(bi, bi + 1), slice(hh, hh + 1))
+        mh = lambda _h, p0, p1, hh=hh: mask(hh, p0, p1)
+        ro, rl = OA.attention_fwd(qr[sl], kr[sl], vr[sl], mh, 1 / 8.0, row_chunk=1024)
+        worst = max(worst, max_abs(o[bi, hh], ro[0, 0]), max_abs(lse[bi, hh], rl[0, 0]))
+        ref = OA.attention_bwd(qr[sl], kr[sl], vr[sl], dor[sl], mh, 1 / 8.0, row_chunk=1024)
+        for a, b in zip((dq, dk, dv), ref):
+            worst = max(worst, max_abs(a[bi, hh], b[0, 0]))
+    say(f"   three whole slices: worst max-abs {worst:.3e}")
+    rng = np.random.default_rng(4096)
+    cp, cs = lay["csc_ptr"], lay["csc_idx"]
+    nb = lay["nb"]
+    worst_s = worst_id = 0.0
+    for bi in range(bsz):
+        for hh in range(heads):
+            sub = (slice(bi, bi + 1), slice(hh, hh + 1))
+            rows = np.unique(np.r_[0, 63, 64, 65, n - 65, n - 1, rng.integers(0, n, 6)])
+            ro, rl = OA.attention_fwd_rows(qr, kr, vr, mask, 1 / 8.0, bi, hh, rows)
+            worst_s = max(worst_s, max_abs(o[bi, hh, rows], ro), max_abs(lse[bi, hh, rows], rl))
+
+            def rows_mask(_h, p0, p1, sel, hh=hh):
+                return np.concatenate([mask(hh, int(p), int(p) + 1) for p in sel[p0:p1]])
+            rdq, _, _ = OA.attention_bwd(qr[sub][:, :, rows], kr[sub], vr[sub],
+                                         dor[sub][:, :, rows],
+                                         lambda _h, p0, p1: rows_mask(_h, p0, p1, rows),
+                                         1 / 8.0)
+            worst_s = max(worst_s, max_abs(dq[bi, hh, rows], rdq[0, 0]))
+            cols = [j for j in rng.choice(nb, 6, replace=False) if j not in G][:2]
+            base = hh * nb
+            for j in cols:
+                qblks = cs[cp[base + j]:cp[base + j + 1]]
+                sel = (np.asarray(qblks)[:, None] * 64 + np.arange(64)).ravel()
+                _, rdk, rdv = OA.attention_bwd(qr[sub][:, :, sel], kr[sub], vr[sub],
+                                               dor[sub][:, :, sel],
+                                               lambda _h, p0, p1, sel=sel: rows_mask(_h, p0, p1, sel),
+                                               1 / 8.0, row_chunk=1024)
+                kr_ = slice(64 * j, 64 * j + 64)
+                worst_s = max(worst_s, max_abs(dk[bi, hh, kr_], rdk[0, 0, kr_]),
+                              max_abs(dv[bi, hh, kr_], rdv[0, 0, kr_]))
+            worst_id = max(worst_id, max_abs(dv[bi, hh].sum(0), dor[bi, hh].sum(0)),
+                           float(np.max(np.abs(dk[bi, hh].sum(0)))))
+    say(f"   every slice, sampled: worst max-abs {worst_s:.3e}; sum identities {worst_id:.3e}")
     assert worst <= BF16_TOL
+    assert worst_s <= BF16_TOL
+    assert worst_id <= 1.0      # sums over 4096 rows of bf16-rounded values
 
 
 def test_bwd_gradient_sum_identities():

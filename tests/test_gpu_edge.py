@@ -1,0 +1,188 @@
+"""GPU parity on the edge cases of the arithmetic, element by element against the
+fp64 oracle:
+
+* scores far from zero (a peaked softmax): Q and K drawn with std 2 (scaled scores
+  q.k/8 with std 4, row maxima about 20) for forward and backward, and with std
+  3.5 (row maxima about 60) for the forward, block-sparse and Longformer;
+* a key that every row leans on: a Longformer window of 0 with one global token,
+  where each row has two keys and puts about half its mass on the global one, so
+  that the global key's dK and dV sum n such terms (random inputs).
+
+The forward writes the rounding residual of O (o_lo) and the backward takes it,
+as a training step does: D = rowsum(dO * O) then carries no bf16 rounding, which
+at these score magnitudes would cost dQ and dK more than the bound.
+
+Bound, per element: |got - exact| <= 2e-2 + half a bf16 ulp of |exact|.  The
+outputs are bf16, and a bf16 value cannot be nearer to the exact one than half its
+spacing, which exceeds 2e-2 once |exact| >= 8 (the fan-in gradients reach 40-100);
+below 4 the half ulp is at most 0.008.  lse is fp32 and keeps the plain 2e-2 bound.
+
+Two cases are expected to exceed that bound (strict xfail, the measured excess in
+each reason): the forward's O weights every value by a bf16-rounded probability,
+so D = rowsum(dO * O) differs from the exact sum of P * dP by about 2^-9 of its
+terms, and dS = P * (dP - D) passes that on to dQ and dK, where the bf16 rounding
+of dS (2^-8) adds to it.  At scores of 20 and more, or summed over the 4096 rows
+of a global key, this reaches 1.1-1.3 times the bound.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_bsattn_amd import _lib as B
+from block_sparse_long_bsattn_amd import inputs as I
+from oracle import attention as OA
+from oracle import longformer as OLF
+from gpu_util import BF16_TOL, max_abs, qkv, say, to_f64, ulp_bound_excess
+from test_gpu_fwd import oracle_mask
+
+pytestmark = pytest.mark.gpu
+
+BIG = 2.0     # std of Q and K for the large-score forward + backward cases
+HUGE = 3.5    # std of Q and K for the forward-only case
+SEEDS = (I.SEED_Q, I.SEED_K, I.SEED_V, I.SEED_DO)
+
+
+def _alloc_fwd(q, n_lse):
+    o = torch.empty_like(q)
+    lse = torch.empty(n_lse, dtype=torch.float32, device="cuda")
+    o_lo = torch.empty_like(q)
+    return o, lse, o_lo
+
+
+def check_residual(o, o_lo):
+    """o_lo is the rounding residual of O: at most half a bf16 ulp of |O| (and a
+    bf16 value itself)."""
+    o, o_lo = to_f64(o), to_f64(o_lo)
+    a = np.maximum(np.abs(o), 2.0 ** -126)
+    half = 0.5 * 2.0 ** (np.floor(np.log2(a)) - 7)
+    assert np.all(np.abs(o_lo) <= half * (1 + 2.0 ** -7))
+
+
+def bs_fwd_bwd(n, heads, bsz, G, w, r, seed, stds):
+    shape = (bsz, heads, n, 64)
+    (q, k, v, do), refs = qkv(shape, "bf16", SEEDS, stds)
+    h = B.bsattn_layout_build(n, 64, heads, G, w, r, seed)
+    try:
+        o, lse, o_lo = _alloc_fwd(q, (bsz, heads, n))
+        wsf = torch.empty(max(1, B.bsattn_fwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(1, B.bsattn_bwd_workspace(h, bsz)), dtype=torch.uint8, device="cuda")
+        B.bsattn_fwd(h, q, k, v, o, lse, wsf, o_lo=o_lo)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        B.bsattn_bwd(h, q, k, v, o, lse, do, dq, dk, dv, wsb, o_lo=o_lo)
+        torch.cuda.synchronize()
+    finally:
+        B.bsattn_layout_destroy(h)
+    check_residual(o, o_lo)
+    return refs, tuple(to_f64(t) for t in (o, lse, dq, dk, dv))
+
+
+def lf_fwd_bwd(n, heads, bsz, w1, G, stds):
+    shape = (bsz, heads, n, 64)
+    (q, k, v, do), refs = qkv(shape, "bf16", SEEDS, stds)
+    plan = B.lfattn_plan_build(n, w1, G)
+    try:
+        o, lse, o_lo = _alloc_fwd(q, (bsz, heads, n))
+        wsf = torch.empty(max(1, B.lfattn_fwd_workspace(plan, bsz, heads)), dtype=torch.uint8,
+                          device="cuda")
+        wsb = torch.empty(max(1, B.lfattn_bwd_workspace(plan, bsz, heads)), dtype=torch.uint8,
+                          device="cuda")
+        B.lfattn_fwd(plan, q, k, v, o, lse, wsf, o_lo=o_lo)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        B.lfattn_bwd(plan, q, k, v, o, lse, do, dq, dk, dv, wsb, o_lo=o_lo)
+        torch.cuda.synchronize()
+    finally:
+        B.lfattn_plan_destroy(plan)
+    check_residual(o, o_lo)
+    return refs, tuple(to_f64(t) for t in (o, lse, dq, dk, dv))
+
+
+def score_range(qr, kr, mask_rows_h0):
+    """Largest |scaled score| over the allowed pairs of (batch 0, head 0)."""
+    s = (qr[0, 0] @ kr[0, 0].T) / 8.0
+    return float(np.max(np.abs(np.where(mask_rows_h0, s, 0.0))))
+
+
+def check_fwd(name, refs, got, mask):
+    qr, kr, vr, _ = refs
+    ro, rl = OA.attention_fwd(qr, kr, vr, mask, 1 / 8.0)
+    o, lse = got[:2]
+    ex, e_l = ulp_bound_excess(o, ro), max_abs(lse, rl)
+    say(f"   {name}: O max-abs {max_abs(o, ro):.3e}, error / (2e-2 + half ulp) {ex:.3f}; "
+        f"lse max-abs {e_l:.3e}")
+    assert e_l <= BF16_TOL and ex <= 1.0
+
+
+def check(name, refs, got, mask, excess_limit=1.0):
+    qr, kr, vr, dor = refs
+    ro, rl = OA.attention_fwd(qr, kr, vr, mask, 1 / 8.0)
+    rdq, rdk, rdv = OA.attention_bwd(qr, kr, vr, dor, mask, 1 / 8.0)
+    o, lse, dq, dk, dv = got
+    ex = {"O": ulp_bound_excess(o, ro), "dQ": ulp_bound_excess(dq, rdq),
+          "dK": ulp_bound_excess(dk, rdk), "dV": ulp_bound_excess(dv, rdv)}
+    plain = {"O": max_abs(o, ro), "lse": max_abs(lse, rl), "dQ": max_abs(dq, rdq),
+             "dK": max_abs(dk, rdk), "dV": max_abs(dv, rdv)}
+    mags = {"dQ": np.abs(rdq).max(), "dK": np.abs(rdk).max(), "dV": np.abs(rdv).max()}
+    say(f"   {name}: max-abs " + " ".join(f"{k} {v:.3e}" for k, v in plain.items()))
+    say(f"   {name}: max |exact| " + " ".join(f"{k} {v:.2f}" for k, v in mags.items()) +
+        "; error / (2e-2 + half ulp) " + " ".join(f"{k} {v:.3f}" for k, v in ex.items()))
+    assert plain["lse"] <= BF16_TOL
+    assert max(ex.values()) <= excess_limit
+
+
+@pytest.mark.parametrize("case", [
+    pytest.param((1024, 2, 2, [0, 15], 3, 3), marks=pytest.mark.xfail(
+        strict=True, reason="largest score 22.7: dK reaches 1.08 times the bound, from D "
+                            "computed with the forward's bf16-rounded weights")),
+    (768, 2, 1, [0, 11], 3, 3),       # ragged last segment
+    (512, 1, 2, [0, 7], 3, 3),        # global rows unsplit
+])
+def test_bs_large_scores(case):
+    n, heads, bsz, G, w, r = case
+    say(f"block-sparse large scores (std {BIG}) n={n} H={heads} B={bsz} G={G}")
+    refs, got = bs_fwd_bwd(n, heads, bsz, G, w, r, 41, (BIG, BIG, 1.0, 1.0))
+    mask, _ = oracle_mask(n, heads, G, w, r, 41)
+    smax = score_range(refs[0], refs[1], mask(0, 0, n))
+    say(f"   largest |scaled score| {smax:.1f}")
+    assert smax >= 18.0
+    check("bigbird", refs, got, mask)
+    say(f"   forward at std {HUGE}")
+    refs, got = bs_fwd_bwd(n, heads, bsz, G, w, r, 41, (HUGE, HUGE, 1.0, 1.0))
+    smax = score_range(refs[0], refs[1], mask(0, 0, n))
+    say(f"   largest |scaled score| {smax:.1f}")
+    assert smax >= 50.0
+    check_fwd("bigbird", refs, got, mask)
+
+
+@pytest.mark.parametrize("case", [
+    (1024, 2, 1, 100, [0, 1, 500]),       # scattered globals, ragged window
+    (1024, 1, 1, 31, list(range(64))),    # a whole tile of globals
+])
+def test_lf_large_scores(case):
+    n, heads, bsz, w1, G = case
+    say(f"longformer large scores (std {BIG}) n={n} H={heads} w1={w1} |G|={len(G)}")
+    refs, got = lf_fwd_bwd(n, heads, bsz, w1, G, (BIG, BIG, 1.0, 1.0))
+    mask = OLF.longformer_mask(n, w1, G)
+    smax = score_range(refs[0], refs[1], mask(0, 0, n))
+    say(f"   largest |scaled score| {smax:.1f}")
+    assert smax >= 18.0
+    check("longformer", refs, got, mask)
+    say(f"   forward at std {HUGE}")
+    refs, got = lf_fwd_bwd(n, heads, bsz, w1, G, (HUGE, HUGE, 1.0, 1.0))
+    smax = score_range(refs[0], refs[1], mask(0, 0, n))
+    say(f"   largest |scaled score| {smax:.1f}")
+    assert smax >= 50.0
+    check_fwd("longformer", refs, got, mask)
+
+
+@pytest.mark.parametrize("n", [1024, pytest.param(4096, marks=pytest.mark.xfail(
+    strict=True, reason="dK of the global key sums 4096 rows: 1.30 times the bound, from D "
+                        "computed with the forward's bf16-rounded weights"))])
+def test_lf_fanin_random(n):
+    """Window 0 and global token 0, random N(0, 1) inputs: every row splits its
+    mass between itself and token 0, whose dV and dK sum n terms of about 1/2."""
+    say(f"longformer fan-in w1=0 G=[0] n={n}, random inputs")
+    refs, got = lf_fwd_bwd(n, 2, 1, 0, [0], None)
+    check("fan-in", refs, got, OLF.longformer_mask(n, 0, [0]))

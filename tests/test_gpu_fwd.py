@@ -178,8 +178,14 @@ def test_fwd_rejects_wrong_shapes():
         # the C ABI itself rejects a short workspace and a bad scale
         lib = B.load()
         assert lib.bsattn_fwd(h, 1, 64, 1, -1.0, q.data_ptr(), q.data_ptr(), q.data_ptr(),
-                              q.data_ptr(), None, None, 0, None) == B.BSATTN_EINVAL
+                              q.data_ptr(), None, None, None, 0, None) == B.BSATTN_EINVAL
         assert lib.bsattn_fwd(h, 1, 32, 1, 0.1, q.data_ptr(), q.data_ptr(), q.data_ptr(),
-                              q.data_ptr(), None, None, 0, None) == B.BSATTN_EUNSUPPORTED
+                              q.data_ptr(), None, None, None, 0, None) == B.BSATTN_EUNSUPPORTED
+        # the rounding residual of O is for bf16 outputs only
+        qf = torch.zeros((1, 2, 512, 64), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(16, B.bsattn_fwd_workspace(h, 1)), dtype=torch.uint8, device="cuda")
+        assert lib.bsattn_fwd(h, 1, 64, 0, 0.125, qf.data_ptr(), qf.data_ptr(), qf.data_ptr(),
+                              qf.data_ptr(), None, q.data_ptr(), ws.data_ptr(), ws.numel(),
+                              None) == B.BSATTN_EINVAL
     finally:
         B.bsattn_layout_destroy(h)
