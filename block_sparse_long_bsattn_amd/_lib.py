@@ -22,12 +22,14 @@ BSATTN_EHIP = -3
 BSATTN_ENOMEM = -4
 BSATTN_F32 = 0
 BSATTN_BF16 = 1
+BSATTN_BWD_NOALLOC_SCRATCH_BYTES = 64 << 20   # static scratch of bsattn_bwd_noalloc
 
 # every exported symbol declared in include/bsattn.h
 EXPORTS = (
     "bsattn_layout_build", "bsattn_layout_rebuild", "bsattn_layout_info",
     "bsattn_layout_to_host", "bsattn_layout_destroy", "bsattn_fwd_workspace",
-    "bsattn_bwd_workspace", "bsattn_fwd", "bsattn_bwd", "lfattn_plan_build",
+    "bsattn_bwd_workspace", "bsattn_fwd", "bsattn_bwd", "bsattn_bwd_noalloc",
+    "lfattn_plan_build",
     "lfattn_plan_build_dilated", "lfattn_plan_build_etc", "lfattn_plan_destroy",
     "lfattn_fwd_workspace", "lfattn_fwd", "lfattn_bwd_workspace", "lfattn_bwd",
     "lfattn_fwd_gproj", "lfattn_bwd_gproj", "bsattn_status_str",
@@ -67,6 +69,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                        + [c_size_t, c_void_p]),
         "bsattn_bwd": (c_int, [c_void_p, c_int, c_int, c_int, c_float] + [c_void_p] * 11
                        + [c_size_t, c_void_p]),
+        "bsattn_bwd_noalloc": (c_int, [c_void_p, c_int, c_int, c_int, c_float] + [c_void_p] * 10
+                               + [c_void_p]),
         "lfattn_plan_build": (c_int, [c_int, c_int, POINTER(c_int32), c_int, c_void_p,
                                       POINTER(c_void_p)]),
         "lfattn_plan_build_dilated": (c_int, [c_int, c_int, POINTER(c_int32), c_int, c_int,
@@ -264,6 +268,25 @@ def bsattn_bwd(layout, q, k, v, o, lse, dout, dq, dk, dv, workspace=None, scale=
                              _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(dout), _ptr(dq),
                              _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)),
            "bsattn_bwd")
+
+
+def bsattn_bwd_noalloc(layout, q, k, v, o, lse, dout, dq, dk, dv, scale=None, stream=None,
+                       o_lo=None) -> None:
+    """bsattn_bwd with the library's static device scratch instead of a workspace
+    (no allocation; calls that overlap on one device race)."""
+    bsz, _, _, d = q.shape
+    nb, heads, _ = bsattn_layout_info(layout)
+    shape = (bsz, heads, _layout_len(layout, nb), d)
+    if lse is None:
+        raise ValueError("bsattn_bwd_noalloc: lse is required")
+    _check_tensors("bsattn_bwd_noalloc", shape, q.dtype,
+                   (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)), lse, None, 0, o_lo)
+    scale = d ** -0.5 if scale is None else scale
+    _check(load().bsattn_bwd_noalloc(layout, bsz, d, _dtype_code(q), c_float(scale), _ptr(q),
+                                     _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse),
+                                     _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
+           "bsattn_bwd_noalloc")
 
 
 # --- Longformer -----------------------------------------------------------------

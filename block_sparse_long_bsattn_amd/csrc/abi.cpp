@@ -381,6 +381,30 @@ int bsattn_bwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float 
   return launch_bwd(L, batch, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, workspace, stream);
 }
 
+int bsattn_bwd_noalloc(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
+                       const void* q, const void* k, const void* v, const void* o,
+                       const void* o_lo, const float* lse, const void* dout, void* dq, void* dk,
+                       void* dv, hipStream_t stream) {
+  clear_error();
+  if (L == nullptr) return set_error(BSATTN_EINVAL, "bwd_noalloc: null layout");
+  if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "bwd_noalloc: only bf16 is built");
+  int st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "bwd_noalloc");
+  if (st) return st;
+  if ((st = check_o_lo(o_lo, dt, "bwd_noalloc"))) return st;
+  if ((int64_t)batch * L->heads * L->n * kHead >= ((int64_t)1 << 40))
+    return set_error(BSATTN_EUNSUPPORTED, "bwd_noalloc: tensor too large");
+  const size_t need = bwd_workspace_bytes(L, batch);
+  if (need > noalloc_scratch_bytes())
+    return set_error(BSATTN_EINVAL, "bwd_noalloc: needs " + std::to_string(need) +
+                                        " bytes of scratch, above the static " +
+                                        std::to_string(noalloc_scratch_bytes()) +
+                                        "; use bsattn_bwd with a workspace");
+  if ((st = check_device(L->device))) return st;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws))) return st;
+  return launch_bwd(L, batch, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, ws, stream);
+}
+
 }  // extern "C"
 
 namespace {

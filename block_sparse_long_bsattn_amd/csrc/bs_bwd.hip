@@ -16,9 +16,20 @@
 //                partials, summed here in segment order, so results are bitwise
 //                reproducible.  Each XCD starts its segments before other items.
 
+#include <mutex>
+#include <string>
+
 #include "bs_bwd.hpp"
 
 namespace bsattn {
+
+// Device scratch of bsattn_bwd_noalloc (D and the fp32 partials of split global
+// rows and columns), for callers that cannot allocate.  Each device holds its own
+// copy for the life of the process.  In host code this name is only a stand-in for
+// the device symbol: its device address comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = BSATTN_BWD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
 
 using namespace bwd;
@@ -355,6 +366,30 @@ __global__ __launch_bounds__(256) void bs_bwd_reduce_kernel(
 }
 
 }  // namespace
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+int noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return check_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(BSATTN_EUNSUPPORTED, "bwd_noalloc: device index above 63");
+  std::lock_guard<std::mutex> lk(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return check_hip(e, "hipGetSymbolAddress(scratch)");
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return BSATTN_OK;
+}
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
 
 size_t bwd_workspace_bytes(const bsattn_layout* L, int batch) {
   size_t bytes = (size_t)batch * L->heads * L->n * sizeof(float);   // D

@@ -126,4 +126,9 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const
                   void* dvg, void* ws, hipStream_t stream);
 size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads);
 
+// The static device scratch of bsattn_bwd_noalloc: its address on the current
+// device (looked up once per device) and its size.
+int noalloc_scratch(void** out);
+size_t noalloc_scratch_bytes();
+
 }  // namespace bsattn

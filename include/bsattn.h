@@ -186,6 +186,28 @@ int bsattn_bwd(const bsattn_layout* layout, int batch, int d, bsattn_dtype dt, f
                const void* o_lo, const float* lse, const void* dout, void* dq, void* dk,
                void* dv, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * bsattn_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving or training loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels, results and return codes as
+ * bsattn_bwd, minus workspace and ws_bytes: its scratch (D and the partials of
+ * split global rows and columns, bsattn_bwd_workspace() bytes) lives in a static
+ * device array of BSATTN_BWD_NOALLOC_SCRATCH_BYTES (64 MiB), one per device, held
+ * until the process ends.  Nothing in it needs to start at zero: every byte
+ * a call reads was written earlier in the same call.  The call allocates nothing
+ * (its first call on a device looks up the array's address once).
+ *   - EINVAL when this layout and batch need more scratch than the array holds
+ *     (e.g. B = 4, 12 heads, n = 4096 needs about 20 MB; the limit leaves room
+ *     for about three times that); use bsattn_bwd then.
+ *   - All calls on one device share the array: calls that may overlap in time on
+ *     one device (other streams, other threads) race; order them on one stream.
+ */
+#define BSATTN_BWD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int bsattn_bwd_noalloc(const bsattn_layout* layout, int batch, int d, bsattn_dtype dt,
+                       float scale, const void* q, const void* k, const void* v,
+                       const void* o, const void* o_lo, const float* lse, const void* dout,
+                       void* dq, void* dk, void* dv, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Longformer sliding window + symmetric global attention                     */
 /* ------------------------------------------------------------------------- */

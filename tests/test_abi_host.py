@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_binding_exports():
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     assert sorted(_lib.EXPORTS) == names
 
 
@@ -77,6 +77,7 @@ def test_null_handles_are_rejected():
     lib = _lib.load()
     assert lib.bsattn_fwd(None, 1, 64, 1, 0.125, *([None] * 6), None, 0, None) == -1
     assert lib.bsattn_bwd(None, 1, 64, 1, 0.125, *([None] * 10), None, 0, None) == -1
+    assert lib.bsattn_bwd_noalloc(None, 1, 64, 1, 0.125, *([None] * 10), None) == -1
     assert lib.lfattn_fwd(None, 1, 1, 64, 1, 0.125, *([None] * 6), None, 0, None) == -1
     assert lib.lfattn_bwd(None, 1, 1, 64, 1, 0.125, *([None] * 10), None, 0, None) == -1
     assert lib.lfattn_fwd_gproj(None, 1, 1, 64, 1, 0.125, *([None] * 9), None, 0, None) == -1
