@@ -122,6 +122,7 @@ int check_workspace(void* ws, size_t ws_bytes, size_t need, const char* who) {
 }
 
 void free_layout(bsattn_layout* L) {
+  if (L->built != nullptr) (void)hipEventDestroy(L->built);
   (void)hipFree(L->d_gblk);
   (void)hipFree(L->d_ngblk);
   (void)hipFree(L->d_row_ptr);
@@ -136,6 +137,7 @@ void free_layout(bsattn_layout* L) {
 }
 
 void free_plan(lfattn_plan* P) {
+  if (P->built != nullptr) (void)hipEventDestroy(P->built);
   (void)hipFree(P->d_gtok);
   (void)hipFree(P->d_gidx);
   (void)hipFree(P->d_tile_gmask);
@@ -290,6 +292,11 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
     free_layout(L);
     return st;
   }
+  if ((st = check_hip(hipEventCreateWithFlags(&L->built, hipEventDisableTiming), "layout event")) ||
+      (st = check_hip(hipEventRecord(L->built, stream), "layout event record"))) {
+    free_layout(L);
+    return st;
+  }
   *out = L;
   return BSATTN_OK;
 }
@@ -300,7 +307,8 @@ int bsattn_layout_rebuild(bsattn_layout* L, uint64_t seed, hipStream_t stream) {
   int st = check_device(L->device);
   if (st) return st;
   L->seed = seed;
-  return launch_layout_build(L, stream);
+  if ((st = launch_layout_build(L, stream))) return st;
+  return check_hip(hipEventRecord(L->built, stream), "layout event record");
 }
 
 int bsattn_layout_info(const bsattn_layout* L, int* nb, int* heads, int64_t* nnzb_total) {
@@ -318,20 +326,29 @@ int bsattn_layout_to_host(const bsattn_layout* L, int32_t* row_ptr, int32_t* col
   if (L == nullptr) return set_error(BSATTN_EINVAL, "layout_to_host: null layout");
   int st = check_device(L->device);
   if (st) return st;
-  if ((st = check_hip(hipDeviceSynchronize(), "layout_to_host sync"))) return st;
+  // wait for this layout's last build or redraw only (not for the whole device),
+  // then copy on a private stream that does not wait for other work either
+  if ((st = check_hip(hipEventSynchronize(L->built), "layout_to_host wait"))) return st;
+  hipStream_t s = nullptr;
+  if ((st = check_hip(hipStreamCreateWithFlags(&s, hipStreamNonBlocking), "layout_to_host stream")))
+    return st;
   const size_t np = ((size_t)L->heads * L->nb + 1) * 4;
   const size_t nz = (size_t)(L->nnz_per_head * L->heads) * 4;
-  if (row_ptr && (st = check_hip(hipMemcpy(row_ptr, L->d_row_ptr, np, hipMemcpyDeviceToHost), "copy row_ptr"))) return st;
-  if (col_idx && (st = check_hip(hipMemcpy(col_idx, L->d_col_idx, nz, hipMemcpyDeviceToHost), "copy col_idx"))) return st;
-  if (csc_ptr && (st = check_hip(hipMemcpy(csc_ptr, L->d_csc_ptr, np, hipMemcpyDeviceToHost), "copy csc_ptr"))) return st;
-  if (csc_idx && (st = check_hip(hipMemcpy(csc_idx, L->d_csc_idx, nz, hipMemcpyDeviceToHost), "copy csc_idx"))) return st;
-  return BSATTN_OK;
+  if (row_ptr) st = check_hip(hipMemcpyAsync(row_ptr, L->d_row_ptr, np, hipMemcpyDeviceToHost, s), "copy row_ptr");
+  if (!st && col_idx) st = check_hip(hipMemcpyAsync(col_idx, L->d_col_idx, nz, hipMemcpyDeviceToHost, s), "copy col_idx");
+  if (!st && csc_ptr) st = check_hip(hipMemcpyAsync(csc_ptr, L->d_csc_ptr, np, hipMemcpyDeviceToHost, s), "copy csc_ptr");
+  if (!st && csc_idx) st = check_hip(hipMemcpyAsync(csc_idx, L->d_csc_idx, nz, hipMemcpyDeviceToHost, s), "copy csc_idx");
+  const int st2 = check_hip(hipStreamSynchronize(s), "layout_to_host copy");
+  (void)hipStreamDestroy(s);
+  return st ? st : st2;
 }
 
 int bsattn_layout_destroy(bsattn_layout* L) {
   clear_error();
   if (L == nullptr) return BSATTN_OK;
-  int st = check_hip(hipDeviceSynchronize(), "layout_destroy sync");
+  // the handle's own build work; releasing its arrays then follows hipFree's rules
+  // for work still reading them (the caller orders its own calls before this one)
+  int st = check_hip(hipEventSynchronize(L->built), "layout_destroy wait");
   free_layout(L);
   return st;
 }
@@ -515,7 +532,9 @@ int lf_plan_build(int n, int window_one_side, const int32_t* global_tokens, int 
       (st = check_hip(hipMemcpyAsync(P->d_tile_gmask, P->tile_gmask.data(), (size_t)P->nt * 8,
                                      hipMemcpyHostToDevice, stream), "upload tile masks")) ||
       (st = check_hip(hipMemcpyAsync(P->d_ct, P->ct.data(), (size_t)P->nct * sizeof(LfTileRef),
-                                     hipMemcpyHostToDevice, stream), "upload class tiles"))) {
+                                     hipMemcpyHostToDevice, stream), "upload class tiles")) ||
+      (st = check_hip(hipEventCreateWithFlags(&P->built, hipEventDisableTiming), "plan event")) ||
+      (st = check_hip(hipEventRecord(P->built, stream), "plan event record"))) {
     free_plan(P);
     return st;
   }
@@ -571,7 +590,9 @@ int lfattn_plan_build_dilated(int n, int window_one_side, const int32_t* global_
 int lfattn_plan_destroy(lfattn_plan* P) {
   clear_error();
   if (P == nullptr) return BSATTN_OK;
-  int st = check_hip(hipDeviceSynchronize(), "lf_plan_destroy sync");
+  // the plan's uploads; releasing its arrays then follows hipFree's rules for work
+  // still reading them (the caller orders its own calls before this one)
+  int st = check_hip(hipEventSynchronize(P->built), "lf_plan_destroy wait");
   free_plan(P);
   return st;
 }

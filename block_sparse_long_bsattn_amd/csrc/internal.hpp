@@ -36,6 +36,7 @@ struct bsattn_layout {
   int32_t* d_row_info = nullptr;
   int32_t* d_col_info = nullptr;
   std::vector<int32_t> kv_order_init;
+  hipEvent_t built = nullptr;     // recorded after the last build or redraw
 };
 
 // How one call cuts the full-length (global) rows and columns into work items:
@@ -75,6 +76,7 @@ struct lfattn_plan {
   std::vector<uint64_t> tile_gmask;
   std::vector<int32_t> dil;      // dilation per head ([heads], or one value)
   std::vector<LfTileRef> ct;
+  hipEvent_t built = nullptr;    // recorded after the build-time uploads
 };
 
 namespace bsattn {

@@ -117,7 +117,8 @@ int bsattn_layout_info(const bsattn_layout* layout, int* nb, int* heads,
                        int64_t* nnzb_total);
 
 /*
- * Copy a layout to host memory (synchronous; waits for the build).
+ * Copy a layout to host memory (synchronous; waits for the layout's last build or
+ * redraw, not for other work on the device).
  *   row_ptr [heads*nb + 1]  head h, query block i: keys at col_idx[row_ptr[h*nb+i] ..
  *                           row_ptr[h*nb+i+1]), ascending.
  *   col_idx [nnzb_total]
@@ -129,7 +130,9 @@ int bsattn_layout_info(const bsattn_layout* layout, int* nb, int* heads,
 int bsattn_layout_to_host(const bsattn_layout* layout, int32_t* row_ptr, int32_t* col_idx,
                           int32_t* csc_ptr, int32_t* csc_idx);
 
-/* Free a layout (synchronises the device first).  NULL is accepted. */
+/* Free a layout.  Waits for its last build or redraw; work enqueued with it must be
+ * ordered before this call by the caller (the device arrays are released with
+ * hipFree).  NULL is accepted. */
 int bsattn_layout_destroy(bsattn_layout* layout);
 
 /* ------------------------------------------------------------------------- */
@@ -266,7 +269,9 @@ int lfattn_plan_build_dilated(int n, int window_one_side, const int32_t* global_
                               int n_global, int heads, const int32_t* dilation, int causal,
                               hipStream_t stream, lfattn_plan** out);
 
-/* Free a plan (synchronises the device first).  NULL is accepted. */
+/* Free a plan.  Waits for its build-time uploads; work enqueued with it must be
+ * ordered before this call by the caller (the device arrays are released with
+ * hipFree).  NULL is accepted. */
 int lfattn_plan_destroy(lfattn_plan* plan);
 
 /* Workspace bytes lfattn_fwd needs.  d must be 64.  0 for invalid arguments. */
