@@ -90,10 +90,15 @@ int check_device(int device) {
   return BSATTN_OK;
 }
 
+// d_max: the largest head dimension the caller's kernels are built for (64, or 128
+// for the bf16 block-sparse forward and backward, which take d = 64 or 128).
 int check_tensor_args(int batch, int d, float scale, std::initializer_list<const void*> ptrs,
-                      const char* who) {
+                      const char* who, int d_max = kHead) {
   if (batch < 1) return set_error(BSATTN_EINVAL, std::string(who) + ": batch must be >= 1");
-  if (d != kHead) return set_error(BSATTN_EUNSUPPORTED, std::string(who) + ": head dim must be 64");
+  if (d != kHead && !(d == 128 && d_max == 128))
+    return set_error(BSATTN_EUNSUPPORTED,
+                     std::string(who) + (d_max == 128 ? ": head dim must be 64 or 128"
+                                                      : ": head dim must be 64"));
   if (!(scale > 0.f) || !std::isfinite(scale))
     return set_error(BSATTN_EINVAL, std::string(who) + ": scale must be finite and > 0");
   for (const void* p : ptrs) {
@@ -354,13 +359,13 @@ int bsattn_layout_destroy(bsattn_layout* L) {
 }
 
 size_t bsattn_fwd_workspace(const bsattn_layout* L, int batch, int d) {
-  if (L == nullptr || batch < 1 || d != kHead) return 0;
-  return fwd_workspace_bytes(L, batch);
+  if (L == nullptr || batch < 1 || (d != kHead && d != 128)) return 0;
+  return fwd_workspace_bytes(L, batch, d);
 }
 
 size_t bsattn_bwd_workspace(const bsattn_layout* L, int batch, int d) {
-  if (L == nullptr || batch < 1 || d != kHead) return 0;
-  return bwd_workspace_bytes(L, batch);
+  if (L == nullptr || batch < 1 || (d != kHead && d != 128)) return 0;
+  return bwd_workspace_bytes(L, batch, d);
 }
 
 int bsattn_fwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
@@ -369,16 +374,17 @@ int bsattn_fwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float 
   clear_error();
   if (L == nullptr) return set_error(BSATTN_EINVAL, "fwd: null layout");
   if (dt != BSATTN_F32 && dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "fwd: unknown dtype");
-  int st = check_tensor_args(batch, d, scale, {q, k, v, o}, "fwd");
+  int st = check_tensor_args(batch, d, scale, {q, k, v, o}, "fwd",
+                             dt == BSATTN_BF16 ? 128 : kHead);
   if (st) return st;
   if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, "fwd: lse not 16-byte aligned");
   if ((st = check_o_lo(o_lo, dt, "fwd"))) return st;
-  if ((int64_t)batch * L->heads * L->n * kHead >= ((int64_t)1 << 40))
+  if ((int64_t)batch * L->heads * L->n * d >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, "fwd: tensor too large");
-  const size_t need = fwd_workspace_bytes_dt(L, batch, dt);
+  const size_t need = fwd_workspace_bytes_dt(L, batch, dt, d);
   if ((st = check_workspace(workspace, ws_bytes, need, "fwd"))) return st;
   if ((st = check_device(L->device))) return st;
-  return launch_fwd(L, batch, dt, scale, q, k, v, o, lse, o_lo, workspace, stream);
+  return launch_fwd(L, batch, dt, d, scale, q, k, v, o, lse, o_lo, workspace, stream);
 }
 
 int bsattn_bwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
@@ -388,14 +394,14 @@ int bsattn_bwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float 
   clear_error();
   if (L == nullptr) return set_error(BSATTN_EINVAL, "bwd: null layout");
   if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "bwd: only bf16 is built");
-  int st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "bwd");
+  int st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "bwd", 128);
   if (st) return st;
   if ((st = check_o_lo(o_lo, dt, "bwd"))) return st;
-  if ((int64_t)batch * L->heads * L->n * kHead >= ((int64_t)1 << 40))
+  if ((int64_t)batch * L->heads * L->n * d >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, "bwd: tensor too large");
-  if ((st = check_workspace(workspace, ws_bytes, bwd_workspace_bytes(L, batch), "bwd"))) return st;
+  if ((st = check_workspace(workspace, ws_bytes, bwd_workspace_bytes(L, batch, d), "bwd"))) return st;
   if ((st = check_device(L->device))) return st;
-  return launch_bwd(L, batch, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, workspace, stream);
+  return launch_bwd(L, batch, d, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, workspace, stream);
 }
 
 int bsattn_bwd_noalloc(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
@@ -405,12 +411,13 @@ int bsattn_bwd_noalloc(const bsattn_layout* L, int batch, int d, bsattn_dtype dt
   clear_error();
   if (L == nullptr) return set_error(BSATTN_EINVAL, "bwd_noalloc: null layout");
   if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, "bwd_noalloc: only bf16 is built");
-  int st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, "bwd_noalloc");
+  int st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv},
+                             "bwd_noalloc", 128);
   if (st) return st;
   if ((st = check_o_lo(o_lo, dt, "bwd_noalloc"))) return st;
-  if ((int64_t)batch * L->heads * L->n * kHead >= ((int64_t)1 << 40))
+  if ((int64_t)batch * L->heads * L->n * d >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, "bwd_noalloc: tensor too large");
-  const size_t need = bwd_workspace_bytes(L, batch);
+  const size_t need = bwd_workspace_bytes(L, batch, d);
   if (need > noalloc_scratch_bytes())
     return set_error(BSATTN_EINVAL, "bwd_noalloc: needs " + std::to_string(need) +
                                         " bytes of scratch, above the static " +
@@ -419,7 +426,7 @@ int bsattn_bwd_noalloc(const bsattn_layout* L, int batch, int d, bsattn_dtype dt
   if ((st = check_device(L->device))) return st;
   void* ws = nullptr;
   if ((st = noalloc_scratch(&ws))) return st;
-  return launch_bwd(L, batch, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, ws, stream);
+  return launch_bwd(L, batch, d, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, ws, stream);
 }
 
 }  // extern "C"

@@ -1,23 +1,28 @@
 // One step of the streaming attention forward for a 64-row query tile held by two
 // waves (wave w owns query rows 32w..32w+31, one query per lane column):
 //   S^T = K Q^T over a 64-key tile, online softmax in fp32, O^T += V^T P^T.
-// Shared by the block-sparse and the banded forward kernels.
+// Shared by the block-sparse and the banded forward kernels.  The head dimension D
+// (64, or 128 for the block-sparse instances that take it) sets the number of
+// 16-wide contraction chunks of S^T and of 32-row O^T tiles.
 #pragma once
 
 #include "common.hpp"
 
 namespace bsattn {
 
-struct FwdState {
-  f32x16 o0, o1;   // O^T accumulators: d rows 0..31 and 32..63, column = query
+template <int D>
+struct FwdStateT {
+  f32x16 o[D / 32];   // O^T accumulators: o[t] holds d rows 32t..32t+31, column = query
   float m;         // reference max (log2 units), -inf until the row saw a finite score
   float l;         // this half-lane's share of the row sum (fp32 probabilities)
   float lb;        // ... of the bf16-rounded probabilities that the PV product uses
 };
+using FwdState = FwdStateT<kHead>;
 
-__device__ __forceinline__ void fwd_state_init(FwdState& st) {
-  st.o0 = zero16();
-  st.o1 = zero16();
+template <int D>
+__device__ __forceinline__ void fwd_state_init(FwdStateT<D>& st) {
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) st.o[t] = zero16();
   st.m = -INFINITY;
   st.l = 0.f;
   st.lb = 0.f;
@@ -26,20 +31,22 @@ __device__ __forceinline__ void fwd_state_init(FwdState& st) {
 // S^T for the 64 keys of the LDS tile sK (natural layout) against this lane's query:
 // the plain products of the bf16 operands, accumulated in fp32 (the scale is applied
 // afterwards, in fp32).  s0 holds keys 0..31, s1 keys 32..63; register r <-> key
-// 8*(r/4) + 4*hl + r%4.
-__device__ __forceinline__ void qk_tile(const uint16_t* sK, const bf16x8 (&qB)[4], int col,
+// 8*(r/4) + 4*hl + r%4.  qB holds this lane's query as NQ = D/16 operands.
+template <int NQ>
+__device__ __forceinline__ void qk_tile(const uint16_t* sK, const bf16x8 (&qB)[NQ], int col,
                                         int hl, f32x16& s0, f32x16& s1) {
-  bf16x8 a[8];
+  constexpr int kS = kStrideOf<16 * NQ>;
+  bf16x8 a[2 * NQ];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    a[2 * c] = ld16(sK + col * kLdsStride + 16 * c + 8 * hl);
-    a[2 * c + 1] = ld16(sK + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+  for (int c = 0; c < NQ; ++c) {
+    a[2 * c] = ld16(sK + col * kS + 16 * c + 8 * hl);
+    a[2 * c + 1] = ld16(sK + (32 + col) * kS + 16 * c + 8 * hl);
   }
   const f32x16 z = zero16();
   s0 = mfma32(a[0], qB[0], z);
   s1 = mfma32(a[1], qB[0], z);
 #pragma unroll
-  for (int c = 1; c < 4; ++c) {
+  for (int c = 1; c < NQ; ++c) {
     s0 = mfma32(a[2 * c], qB[c], s0);
     s1 = mfma32(a[2 * c + 1], qB[c], s1);
   }
@@ -74,7 +81,8 @@ __device__ __forceinline__ void mask_keys_from(f32x16& s0, f32x16& s1, int hl, i
 // gradient of a key that every row sees) would accumulate its rounding.
 constexpr float kRescaleSlack = 8.f;
 
-__device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& st,
+template <int D>
+__device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdStateT<D>& st,
                                              bf16x8 (&pc)[4], float sl2) {
   float mx = __builtin_fmaxf(s0[0], s1[0]);
 #pragma unroll
@@ -90,10 +98,9 @@ __device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& s
       st.l *= alpha;
       st.lb *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        st.o0[r] *= alpha;
-        st.o1[r] *= alpha;
-      }
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) st.o[t][r] *= alpha;
       st.m = mx;
     }
   }
@@ -130,27 +137,33 @@ __device__ __forceinline__ void softmax_step(f32x16& s0, f32x16& s1, FwdState& s
 }
 
 // O^T += V^T P^T; V is the natural LDS tile sV, its transposed operand comes from
-// ds_read_b64_tr_b16 reads.  pv_load issues the reads (early, so that their latency
-// hides behind the softmax), pv_mma the MFMAs.
-__device__ __forceinline__ void pv_load(const uint16_t* sV, int lane, bf16x8 (&v)[8]) {
+// ds_read_b64_tr_b16 reads: v[(D/32) c + t] is key chunk c of O^T tile t.  pv_load
+// issues the reads (early, so that their latency hides behind the softmax), pv_mma
+// the MFMAs.
+template <int NV>
+__device__ __forceinline__ void pv_load(const uint16_t* sV, int lane, bf16x8 (&v)[NV]) {
+  constexpr int D = 8 * NV, kT = D / 32;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    v[2 * c] = ld_tr8(sV, 0, c, lane);
-    v[2 * c + 1] = ld_tr8(sV, 1, c, lane);
-  }
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int t = 0; t < kT; ++t) v[kT * c + t] = ld_tr8<D>(sV, t, c, lane);
 }
 
-__device__ __forceinline__ void pv_mma(const bf16x8 (&v)[8], const bf16x8 (&pc)[4], FwdState& st) {
+template <int NV, int D>
+__device__ __forceinline__ void pv_mma(const bf16x8 (&v)[NV], const bf16x8 (&pc)[4],
+                                       FwdStateT<D>& st) {
+  static_assert(NV == D / 8, "one operand per key chunk and O^T tile");
+  constexpr int kT = D / 32;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    st.o0 = mfma32(v[2 * c], pc[c], st.o0);
-    st.o1 = mfma32(v[2 * c + 1], pc[c], st.o1);
-  }
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int t = 0; t < kT; ++t) st.o[t] = mfma32(v[kT * c + t], pc[c], st.o[t]);
 }
 
+template <int D>
 __device__ __forceinline__ void pv_tile(const uint16_t* sV, const bf16x8 (&pc)[4], int lane,
-                                        FwdState& st) {
-  bf16x8 v[8];
+                                        FwdStateT<D>& st) {
+  bf16x8 v[D / 8];
   pv_load(sV, lane, v);
   pv_mma(v, pc, st);
 }
@@ -160,66 +173,68 @@ __device__ __forceinline__ void pv_tile(const uint16_t* sV, const bf16x8 (&pc)[4
 // (natural log, from l_tot).  orow / olo_row point at this lane's query row;
 // lse_out may be null.  l_tot and lb_tot are the row's full sums (both
 // half-lanes, partner_sum) of st.l and st.lb.
-__device__ __forceinline__ void write_o_bf16(const FwdState& st, float l_tot, float lb_tot,
+template <int D>
+__device__ __forceinline__ void write_o_bf16(const FwdStateT<D>& st, float l_tot, float lb_tot,
                                              int hl, uint16_t* orow, uint16_t* olo_row,
                                              float* lse_out) {
   const float inv = 1.f / lb_tot;
   uint16_t* op = orow + 4 * hl;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float x0[4], x1[4];
+    constexpr int kT = D / 32;
+    float x[kT][4];
+    u32x2 w[kT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x0[e] = st.o0[4 * j + e] * inv;
-      x1[e] = st.o1[4 * j + e] * inv;
+    for (int t = 0; t < kT; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[t][e] = st.o[t][4 * j + e] * inv;
+      w[t][0] = pack_bf16x2(x[t][0], x[t][1]);
+      w[t][1] = pack_bf16x2(x[t][2], x[t][3]);
     }
-    u32x2 w0, w1;
-    w0[0] = pack_bf16x2(x0[0], x0[1]);
-    w0[1] = pack_bf16x2(x0[2], x0[3]);
-    w1[0] = pack_bf16x2(x1[0], x1[1]);
-    w1[1] = pack_bf16x2(x1[2], x1[3]);
-    *reinterpret_cast<u32x2*>(op + 8 * j) = w0;
-    *reinterpret_cast<u32x2*>(op + 32 + 8 * j) = w1;
+#pragma unroll
+    for (int t = 0; t < kT; ++t) *reinterpret_cast<u32x2*>(op + 32 * t + 8 * j) = w[t];
     if (olo_row != nullptr) {
       uint16_t* lp = olo_row + 4 * hl;
-      u32x2 r0, r1;
-      r0[0] = pack_bf16x2(x0[0] - bf16_lo(w0[0]), x0[1] - bf16_hi(w0[0]));
-      r0[1] = pack_bf16x2(x0[2] - bf16_lo(w0[1]), x0[3] - bf16_hi(w0[1]));
-      r1[0] = pack_bf16x2(x1[0] - bf16_lo(w1[0]), x1[1] - bf16_hi(w1[0]));
-      r1[1] = pack_bf16x2(x1[2] - bf16_lo(w1[1]), x1[3] - bf16_hi(w1[1]));
-      *reinterpret_cast<u32x2*>(lp + 8 * j) = r0;
-      *reinterpret_cast<u32x2*>(lp + 32 + 8 * j) = r1;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        u32x2 r;
+        r[0] = pack_bf16x2(x[t][0] - bf16_lo(w[t][0]), x[t][1] - bf16_hi(w[t][0]));
+        r[1] = pack_bf16x2(x[t][2] - bf16_lo(w[t][1]), x[t][3] - bf16_hi(w[t][1]));
+        *reinterpret_cast<u32x2*>(lp + 32 * t + 8 * j) = r;
+      }
     }
   }
   if (lse_out != nullptr && hl == 0) *lse_out = (st.m + __log2f(l_tot)) * kLn2;
 }
 
-// Partial record of a split full row: O unnormalised [64][64] fp32, then m[64]
+// Partial record of a split full row: O unnormalised [64][D] fp32, then m[64]
 // (log2 units), l[64] and lb[64] (the two row sums), row qr of the query tile.
-constexpr int kPartFloats = kBlock * kHead + 3 * kBlock;
+template <int D>
+constexpr int kPartFloatsOf = kBlock * D + 3 * kBlock;
+constexpr int kPartFloats = kPartFloatsOf<kHead>;
 
-__device__ __forceinline__ void write_partial(const FwdState& st, float l_tot, float lb_tot,
+template <int D>
+__device__ __forceinline__ void write_partial(const FwdStateT<D>& st, float l_tot, float lb_tot,
                                               int hl, int qr, float* rec) {
-  float* orow = rec + qr * kHead + 4 * hl;
+  float* orow = rec + qr * D + 4 * hl;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    f32x4 w0, w1;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w0[e] = st.o0[4 * j + e];
-      w1[e] = st.o1[4 * j + e];
+    for (int t = 0; t < D / 32; ++t) {
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = st.o[t][4 * j + e];
+      *reinterpret_cast<f32x4*>(orow + 32 * t + 8 * j) = w;
     }
-    *reinterpret_cast<f32x4*>(orow + 8 * j) = w0;
-    *reinterpret_cast<f32x4*>(orow + 32 + 8 * j) = w1;
   }
   if (hl == 0) {
-    rec[kBlock * kHead + qr] = st.m;
-    rec[kBlock * kHead + kBlock + qr] = l_tot;
-    rec[kBlock * kHead + 2 * kBlock + qr] = lb_tot;
+    rec[kBlock * D + qr] = st.m;
+    rec[kBlock * D + kBlock + qr] = l_tot;
+    rec[kBlock * D + 2 * kBlock + qr] = lb_tot;
   }
 }
 
-// Merge nseg partial records (stride kPartFloats) for row `row`, columns dq..dq+15,
+// Merge nseg partial records (stride kPartFloatsOf<D>) for row `row`, columns dq..dq+15,
 // in segment order: M = max m_s, f_s = 2^(m_s - M), L = sum l_s f_s,
 // Lb = sum lb_s f_s, acc = sum O_s f_s (O is then acc / Lb, lse M + log2 L).
 // Up to kMergeBatch records are read with all their loads in flight together (one
@@ -227,26 +242,28 @@ __device__ __forceinline__ void write_partial(const FwdState& st, float l_tot, f
 // the arithmetic is the same, in the same order, either way.
 constexpr int kMergeBatch = 8;
 
+template <int D = kHead>
 __device__ __forceinline__ void merge_partials(const float* base, int nseg, int row, int dq,
                                                float (&acc)[16], float& M, float& L,
                                                float& Lb) {
+  constexpr int kPart = kPartFloatsOf<D>;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   L = 0.f;
   Lb = 0.f;
-  constexpr int kM = kBlock * kHead, kL = kM + kBlock, kLb = kM + 2 * kBlock;
+  constexpr int kM = kBlock * D, kL = kM + kBlock, kLb = kM + 2 * kBlock;
   if (nseg <= kMergeBatch) {
     float mv[kMergeBatch], lv[kMergeBatch], lbv[kMergeBatch];
     f32x4 x[kMergeBatch][4];
 #pragma unroll
     for (int s = 0; s < kMergeBatch; ++s) {
       if (s < nseg) {
-        const float* ps = base + (size_t)s * kPartFloats;
+        const float* ps = base + (size_t)s * kPart;
         mv[s] = ps[kM + row];
         lv[s] = ps[kL + row];
         lbv[s] = ps[kLb + row];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) x[s][q] = *reinterpret_cast<const f32x4*>(ps + row * kHead + dq + 4 * q);
+        for (int q = 0; q < 4; ++q) x[s][q] = *reinterpret_cast<const f32x4*>(ps + row * D + dq + 4 * q);
       }
     }
     M = -INFINITY;
@@ -273,17 +290,17 @@ __device__ __forceinline__ void merge_partials(const float* base, int nseg, int 
   }
   M = -INFINITY;
 #pragma unroll 8
-  for (int s = 0; s < nseg; ++s) M = fmaxf(M, base[(size_t)s * kPartFloats + kM + row]);
+  for (int s = 0; s < nseg; ++s) M = fmaxf(M, base[(size_t)s * kPart + kM + row]);
   const float Mref = M == -INFINITY ? 0.f : M;
 #pragma unroll 4
   for (int s = 0; s < nseg; ++s) {
-    const float* ps = base + (size_t)s * kPartFloats;
+    const float* ps = base + (size_t)s * kPart;
     const float f = fast_exp2(ps[kM + row] - Mref);
     L += ps[kL + row] * f;
     Lb += ps[kLb + row] * f;
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(ps + row * kHead + dq + e);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(ps + row * D + dq + e);
       acc[e] += x[0] * f;
       acc[e + 1] += x[1] * f;
       acc[e + 2] += x[2] * f;

@@ -6,6 +6,8 @@
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
+// Head dimension d = 64 or 128: one template per kernel, instantiated for both.
+//
 // No atomics: every output tile has one owner.
 //   bs_bwd_dq    one work-group per query block (row of the layout): computes
 //                D for its rows (written for the next kernel) and dQ.
@@ -36,17 +38,18 @@ using namespace bwd;
 
 constexpr int kThreads = 128;
 
-template <bool kRagged>
+template <int D, bool kRagged>
 __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
+  constexpr int kS = kStrideOf<D>, kC = D / 16, kT = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kS];
 
   const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
   if (v < 0) return;
   const Item it = decode(a, v, false);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const size_t bh_off = (size_t)it.bh * a.n * kHead;
+  const size_t bh_off = (size_t)it.bh * a.n * D;
   const int qrow = it.blk * kBlock + 32 * wave + col;
 
   const int32_t* keys = a.col_idx + it.start;
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   // Keys past the end of a sequence that ends inside its last block stage as zero
   // rows of K and V, which give them dP = 0 and no dQ contribution; query rows past
   // the end read nothing and write nothing.
-  TileRegs kr, vr;
+  TileRegsT<D> kr, vr;
   if (it.len > 0) {
     load_block<kRagged>(kr, kbase, it.first, a, tid);
     load_block<kRagged>(vr, vbase, it.first, a, tid);
@@ -63,13 +66,13 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   // block index of the next tile, read one iteration ahead of its use
   int kb_next = it.len > 1 ? it.at(keys, 1) : 0;
   const bool qvalid = !kRagged || qrow < a.n;
-  bf16x8 qB[4], doB[4];
+  bf16x8 qB[kC], doB[kC];
   float dsum = 0.f;
   {
-    const size_t off = bh_off + (size_t)qrow * kHead + 8 * hl;
+    const size_t off = bh_off + (size_t)qrow * D + 8 * hl;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kC; ++c) {
       const u32x4 qv = qvalid ? ldg16(a.q + off + 16 * c) : z;
       const u32x4 dv = qvalid ? ldg16(a.dout + off + 16 * c) : z;
       const u32x4 ov = qvalid ? ldg16(a.o + off + 16 * c) : z;
@@ -105,7 +108,9 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   lds_store_nat(sK[0], kr, tid);
   lds_store_nat(sV[0], vr, tid);
 
-  f32x16 g0 = zero16(), g1 = zero16();   // dQ^T, d rows 0..31 and 32..63
+  f32x16 g[kT];   // dQ^T: g[t] holds d rows 32t..32t+31
+#pragma unroll
+  for (int t = 0; t < kT; ++t) g[t] = zero16();
   for (int t = 0; t < it.len; ++t) {
     const int cur = t & 1;
     __syncthreads();
@@ -118,11 +123,11 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
     f32x16 s0 = seed_s, s1 = seed_s, p0 = seed_d, p1 = seed_d;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bf16x8 k0 = ld16(sK[cur] + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 k1 = ld16(sK[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 v0 = ld16(sV[cur] + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 v1 = ld16(sV[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+    for (int c = 0; c < kC; ++c) {
+      const bf16x8 k0 = ld16(sK[cur] + col * kS + 16 * c + 8 * hl);
+      const bf16x8 k1 = ld16(sK[cur] + (32 + col) * kS + 16 * c + 8 * hl);
+      const bf16x8 v0 = ld16(sV[cur] + col * kS + 16 * c + 8 * hl);
+      const bf16x8 v1 = ld16(sV[cur] + (32 + col) * kS + 16 * c + 8 * hl);
       s0 = mfma32(k0, qB[c], s0);
       s1 = mfma32(k1, qB[c], s1);
       p0 = mfma32(v0, doB[c], p0);
@@ -136,10 +141,9 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]; K^T from transpose reads
     const bf16x8 dc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      g0 = mfma32(ld_tr8(sK[cur], 0, c, lane), dc[c], g0);
-      g1 = mfma32(ld_tr8(sK[cur], 1, c, lane), dc[c], g1);
-    }
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < kT; ++t) g[t] = mfma32(ld_tr8<D>(sK[cur], t, c, lane), dc[c], g[t]);
     if (more) {
       lds_store_nat(sK[cur ^ 1], kr, tid);
       lds_store_nat(sV[cur ^ 1], vr, tid);
@@ -149,34 +153,38 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   const float sc = a.scale;
   if (it.slot < 0) {
     if (!qvalid) return;
-    uint16_t* op = a.dq + bh_off + (size_t)qrow * kHead + 4 * hl;
+    uint16_t* op = a.dq + bh_off + (size_t)qrow * D + 4 * hl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x2 w0, w1;
-      w0[0] = pack_bf16x2(g0[4 * j] * sc, g0[4 * j + 1] * sc);
-      w0[1] = pack_bf16x2(g0[4 * j + 2] * sc, g0[4 * j + 3] * sc);
-      w1[0] = pack_bf16x2(g1[4 * j] * sc, g1[4 * j + 1] * sc);
-      w1[1] = pack_bf16x2(g1[4 * j + 2] * sc, g1[4 * j + 3] * sc);
-      *reinterpret_cast<u32x2*>(op + 8 * j) = w0;
-      *reinterpret_cast<u32x2*>(op + 32 + 8 * j) = w1;
+      u32x2 w[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        w[t][0] = pack_bf16x2(g[t][4 * j] * sc, g[t][4 * j + 1] * sc);
+        w[t][1] = pack_bf16x2(g[t][4 * j + 2] * sc, g[t][4 * j + 3] * sc);
+      }
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<u32x2*>(op + 32 * t + 8 * j) = w[t];
     }
   } else {
-    float* pp = a.part_q + (size_t)it.slot * kTile + (32 * wave + col) * kHead + 4 * hl;
+    float* pp = a.part_q + (size_t)it.slot * kTileOf<D> + (32 * wave + col) * D + 4 * hl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f32x4 w0, w1;
+      f32x4 w[kT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { w0[e] = g0[4 * j + e] * sc; w1[e] = g1[4 * j + e] * sc; }
-      *reinterpret_cast<f32x4*>(pp + 8 * j) = w0;
-      *reinterpret_cast<f32x4*>(pp + 32 + 8 * j) = w1;
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[t][e] = g[t][4 * j + e] * sc;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<f32x4*>(pp + 32 * t + 8 * j) = w[t];
     }
   }
 }
 
-template <bool kRagged>
+template <int D, bool kRagged>
 __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[2][kBlock * kLdsStride];   // dO
+  constexpr int kS = kStrideOf<D>, kC = D / 16, kT = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kBlock * kS];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[2][kBlock * kS];   // dO
   __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse / scale
   __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
 
@@ -185,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   const Item it = decode(a, v, true);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const size_t bh_off = (size_t)it.bh * a.n * kHead;
+  const size_t bh_off = (size_t)it.bh * a.n * D;
   const int krow = it.blk * kBlock + 32 * wave + col;   // this lane's key token
 
   const int32_t* qblks = a.csc_idx + it.start;
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   // Query rows past the end of a sequence that ends inside its last block stage as
   // zero rows of Q and dO with lse = +inf and D = 0, so that P = 0 and dS = 0 there;
   // key rows past the end read nothing and write nothing.
-  TileRegs qr, dr;
+  TileRegsT<D> qr, dr;
   float lv = 0.f, dval = 0.f;
   auto load_rowvals = [&](int qb) {
     if (tid < kBlock) {
@@ -213,11 +221,11 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   // block index of the next tile, read one iteration ahead of its use
   int qb_next = it.len > 1 ? it.at(qblks, 1) : 0;
   const bool kvalid = !kRagged || krow < a.n;
-  bf16x8 kB[4], vB[4];
+  bf16x8 kB[kC], vB[kC];
   {
-    const size_t off = bh_off + (size_t)krow * kHead + 8 * hl;
+    const size_t off = bh_off + (size_t)krow * D + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kC; ++c) {
       kB[c] = kvalid ? ld16(a.k + off + 16 * c) : bf16x8{};
       vB[c] = kvalid ? ld16(a.v + off + 16 * c) : bf16x8{};
     }
@@ -231,7 +239,12 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   // loop's first use of vB waits on every iteration's tile prefetch as well
   wait_all_loads();
 
-  f32x16 dv0 = zero16(), dv1 = zero16(), dk0 = zero16(), dk1 = zero16();
+  f32x16 dv[kT], dk[kT];   // dV^T, dK^T: tile t holds d rows 32t..32t+31
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    dv[t] = zero16();
+    dk[t] = zero16();
+  }
   for (int t = 0; t < it.len; ++t) {
     const int cur = t & 1;
     __syncthreads();
@@ -261,11 +274,11 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bf16x8 q0 = ld16(sQ[cur] + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 q1 = ld16(sQ[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 o0 = ld16(sO[cur] + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 o1 = ld16(sO[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+    for (int c = 0; c < kC; ++c) {
+      const bf16x8 q0 = ld16(sQ[cur] + col * kS + 16 * c + 8 * hl);
+      const bf16x8 q1 = ld16(sQ[cur] + (32 + col) * kS + 16 * c + 8 * hl);
+      const bf16x8 o0 = ld16(sO[cur] + col * kS + 16 * c + 8 * hl);
+      const bf16x8 o1 = ld16(sO[cur] + (32 + col) * kS + 16 * c + 8 * hl);
       s0 = mfma32(q0, kB[c], s0);
       s1 = mfma32(q1, kB[c], s1);
       p0 = mfma32(o0, vB[c], p0);
@@ -283,10 +296,10 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
     const bf16x8 dc[4] = {pack8(p0, 0), pack8(p0, 8), pack8(p1, 0), pack8(p1, 8)};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      dv0 = mfma32(ld_tr8(sO[cur], 0, c, lane), pc[c], dv0);
-      dv1 = mfma32(ld_tr8(sO[cur], 1, c, lane), pc[c], dv1);
-      dk0 = mfma32(ld_tr8(sQ[cur], 0, c, lane), dc[c], dk0);
-      dk1 = mfma32(ld_tr8(sQ[cur], 1, c, lane), dc[c], dk1);
+#pragma unroll
+      for (int t = 0; t < kT; ++t) dv[t] = mfma32(ld_tr8<D>(sO[cur], t, c, lane), pc[c], dv[t]);
+#pragma unroll
+      for (int t = 0; t < kT; ++t) dk[t] = mfma32(ld_tr8<D>(sQ[cur], t, c, lane), dc[c], dk[t]);
     }
     if (more) {
       lds_store_nat(sQ[cur ^ 1], qr, tid);
@@ -298,46 +311,52 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dkdv_kernel(BwdArgs a) {
   const float sc = a.scale;
   if (it.slot < 0) {
     if (!kvalid) return;
-    const size_t off = bh_off + (size_t)krow * kHead + 4 * hl;
+    const size_t off = bh_off + (size_t)krow * D + 4 * hl;
     uint16_t* kp = a.dk + off;
     uint16_t* vp = a.dv + off;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x2 k0w, k1w, v0w, v1w;
-      k0w[0] = pack_bf16x2(dk0[4 * j] * sc, dk0[4 * j + 1] * sc);
-      k0w[1] = pack_bf16x2(dk0[4 * j + 2] * sc, dk0[4 * j + 3] * sc);
-      k1w[0] = pack_bf16x2(dk1[4 * j] * sc, dk1[4 * j + 1] * sc);
-      k1w[1] = pack_bf16x2(dk1[4 * j + 2] * sc, dk1[4 * j + 3] * sc);
-      v0w[0] = pack_bf16x2(dv0[4 * j], dv0[4 * j + 1]);
-      v0w[1] = pack_bf16x2(dv0[4 * j + 2], dv0[4 * j + 3]);
-      v1w[0] = pack_bf16x2(dv1[4 * j], dv1[4 * j + 1]);
-      v1w[1] = pack_bf16x2(dv1[4 * j + 2], dv1[4 * j + 3]);
-      *reinterpret_cast<u32x2*>(kp + 8 * j) = k0w;
-      *reinterpret_cast<u32x2*>(kp + 32 + 8 * j) = k1w;
-      *reinterpret_cast<u32x2*>(vp + 8 * j) = v0w;
-      *reinterpret_cast<u32x2*>(vp + 32 + 8 * j) = v1w;
+      u32x2 kw[kT], vw[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        kw[t][0] = pack_bf16x2(dk[t][4 * j] * sc, dk[t][4 * j + 1] * sc);
+        kw[t][1] = pack_bf16x2(dk[t][4 * j + 2] * sc, dk[t][4 * j + 3] * sc);
+      }
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        vw[t][0] = pack_bf16x2(dv[t][4 * j], dv[t][4 * j + 1]);
+        vw[t][1] = pack_bf16x2(dv[t][4 * j + 2], dv[t][4 * j + 3]);
+      }
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<u32x2*>(kp + 32 * t + 8 * j) = kw[t];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<u32x2*>(vp + 32 * t + 8 * j) = vw[t];
     }
   } else {
-    float* pk = a.part_kv + (size_t)it.slot * 2 * kTile + (32 * wave + col) * kHead + 4 * hl;
-    float* pv = pk + kTile;
+    float* pk = a.part_kv + (size_t)it.slot * 2 * kTileOf<D> + (32 * wave + col) * D + 4 * hl;
+    float* pv = pk + kTileOf<D>;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f32x4 k0w, k1w, v0w, v1w;
+      f32x4 kw[kT], vw[kT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k0w[e] = dk0[4 * j + e] * sc; k1w[e] = dk1[4 * j + e] * sc;
-        v0w[e] = dv0[4 * j + e]; v1w[e] = dv1[4 * j + e];
-      }
-      *reinterpret_cast<f32x4*>(pk + 8 * j) = k0w;
-      *reinterpret_cast<f32x4*>(pk + 32 + 8 * j) = k1w;
-      *reinterpret_cast<f32x4*>(pv + 8 * j) = v0w;
-      *reinterpret_cast<f32x4*>(pv + 32 + 8 * j) = v1w;
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kw[t][e] = dk[t][4 * j + e] * sc;
+          vw[t][e] = dv[t][4 * j + e];
+        }
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<f32x4*>(pk + 32 * t + 8 * j) = kw[t];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<f32x4*>(pv + 32 * t + 8 * j) = vw[t];
     }
   }
 }
 
 // Sum the fp32 partial tiles of split global rows (dQ) and columns (dK, dV) in
-// segment order.  Work-group (bh*g + gi)*3 + kind, kind 0 = dQ, 1 = dK, 2 = dV.
+// segment order.  Work-group (bh*g + gi)*3 + kind, kind 0 = dQ, 1 = dK, 2 = dV;
+// thread t sums floats 16 (t + 256 u) .. +15 of the 64 x D tile, u < D/64.
+template <int D>
 __global__ __launch_bounds__(256) void bs_bwd_reduce_kernel(
     const float* __restrict__ part_q, const float* __restrict__ part_kv,
     const int32_t* __restrict__ gblk, int n, int g, int nseg, uint16_t* __restrict__ dq,
@@ -345,23 +364,27 @@ __global__ __launch_bounds__(256) void bs_bwd_reduce_kernel(
   const int kind = blockIdx.x % 3;
   const int idx = blockIdx.x / 3;   // bh*g + gi
   const int bh = idx / g, gi = idx - bh * g;
-  const int e0 = threadIdx.x * 16;  // 16 consecutive floats of the 64x64 tile
+  constexpr int kTile = kTileOf<D>;
   const size_t slot0 = (size_t)idx * nseg;
-  float acc[16];
-  if (kind == 0) sum_partials(part_q + slot0 * kTile + e0, kTile, nseg, acc);
-  else sum_partials(part_kv + slot0 * 2 * kTile + (kind - 1) * kTile + e0, 2 * kTile, nseg, acc);
-  // rows past the end of a sequence that ends inside this block are not written
-  if (gblk[gi] * kBlock + e0 / kHead >= n) return;
-  uint16_t* dst = kind == 0 ? dq : (kind == 1 ? dk : dv);
-  dst += ((size_t)bh * n + (size_t)gblk[gi] * kBlock) * kHead + e0;
 #pragma unroll
-  for (int e = 0; e < 16; e += 8) {
-    u32x4 w;
-    w[0] = pack_bf16x2(acc[e], acc[e + 1]);
-    w[1] = pack_bf16x2(acc[e + 2], acc[e + 3]);
-    w[2] = pack_bf16x2(acc[e + 4], acc[e + 5]);
-    w[3] = pack_bf16x2(acc[e + 6], acc[e + 7]);
-    *reinterpret_cast<u32x4*>(dst + e) = w;
+  for (int u = 0; u < D / 64; ++u) {
+    const int e0 = (threadIdx.x + 256 * u) * 16;  // 16 consecutive floats of the tile
+    float acc[16];
+    if (kind == 0) sum_partials(part_q + slot0 * kTile + e0, kTile, nseg, acc);
+    else sum_partials(part_kv + slot0 * 2 * kTile + (kind - 1) * kTile + e0, 2 * kTile, nseg, acc);
+    // rows past the end of a sequence that ends inside this block are not written
+    if (gblk[gi] * kBlock + e0 / D >= n) return;
+    uint16_t* dst = kind == 0 ? dq : (kind == 1 ? dk : dv);
+    dst += ((size_t)bh * n + (size_t)gblk[gi] * kBlock) * D + e0;
+#pragma unroll
+    for (int e = 0; e < 16; e += 8) {
+      u32x4 w;
+      w[0] = pack_bf16x2(acc[e], acc[e + 1]);
+      w[1] = pack_bf16x2(acc[e + 2], acc[e + 3]);
+      w[2] = pack_bf16x2(acc[e + 4], acc[e + 5]);
+      w[3] = pack_bf16x2(acc[e + 6], acc[e + 7]);
+      *reinterpret_cast<u32x4*>(dst + e) = w;
+    }
   }
 }
 
@@ -391,17 +414,21 @@ int noalloc_scratch(void** out) {
 
 size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
 
-size_t bwd_workspace_bytes(const bsattn_layout* L, int batch) {
+size_t bwd_workspace_bytes(const bsattn_layout* L, int batch, int d) {
   size_t bytes = (size_t)batch * L->heads * L->n * sizeof(float);   // D
   bytes = (bytes + 255) & ~(size_t)255;
   const SegPlan sp = seg_plan(L, batch);
-  if (sp.split) bytes += (size_t)batch * L->heads * L->g * sp.nseg * 3 * kTile * sizeof(float);
+  if (sp.split) bytes += (size_t)batch * L->heads * L->g * sp.nseg * 3 * (kBlock * d) * sizeof(float);
   return bytes;
 }
 
-int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, const void* k,
-               const void* v, const void* o, const void* o_lo, const float* lse,
-               const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t stream) {
+namespace {
+
+template <int D>
+int launch_bwd_d(const bsattn_layout* L, int batch, float scale, const void* q, const void* k,
+                 const void* v, const void* o, const void* o_lo, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t stream) {
+  constexpr int kTile = kTileOf<D>;
   BwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.o = (const uint16_t*)o; a.o_lo = (const uint16_t*)o_lo; a.lse = lse;
@@ -427,30 +454,40 @@ int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q, co
   a.inv_scale = 1.f / scale;
   const int grid = 8 * ((a.total_items + 7) / 8);
   {
-    ProfScope prof_("bs_bwd_dq", stream);
+    ProfScope prof_(D == kHead ? "bs_bwd_dq" : "bs_bwd_dq_d128", stream);
     if (a.last_rows < kBlock)
-      hipLaunchKernelGGL(bs_bwd_dq_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bs_bwd_dq_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(bs_bwd_dq_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bs_bwd_dq_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   }
   int st = check_hip(hipGetLastError(), "bs_bwd_dq launch");
   if (st) return st;
   {
-    ProfScope prof_("bs_bwd_dkdv", stream);
+    ProfScope prof_(D == kHead ? "bs_bwd_dkdv" : "bs_bwd_dkdv_d128", stream);
     if (a.last_rows < kBlock)
-      hipLaunchKernelGGL(bs_bwd_dkdv_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bs_bwd_dkdv_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(bs_bwd_dkdv_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bs_bwd_dkdv_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   }
   st = check_hip(hipGetLastError(), "bs_bwd_dkdv launch");
   if (st || !sp.split || L->g == 0) return st;
   {
     ProfScope prof_("bs_bwd_reduce", stream);
-    hipLaunchKernelGGL(bs_bwd_reduce_kernel, dim3(batch * L->heads * L->g * 3), dim3(256), 0,
+    hipLaunchKernelGGL(bs_bwd_reduce_kernel<D>, dim3(batch * L->heads * L->g * 3), dim3(256), 0,
                        stream, (const float*)a.part_q, (const float*)a.part_kv, L->d_gblk, L->n,
                        L->g, sp.nseg, a.dq, a.dk, a.dv);
   }
   return check_hip(hipGetLastError(), "bs_bwd_reduce launch");
+}
+
+}  // namespace
+
+int launch_bwd(const bsattn_layout* L, int batch, int d, float scale, const void* q,
+               const void* k, const void* v, const void* o, const void* o_lo, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t stream) {
+  if (d == 128)
+    return launch_bwd_d<128>(L, batch, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, ws, stream);
+  return launch_bwd_d<kHead>(L, batch, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, ws, stream);
 }
 
 }  // namespace bsattn

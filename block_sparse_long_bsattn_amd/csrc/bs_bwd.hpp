@@ -7,7 +7,8 @@
 namespace bsattn {
 namespace bwd {
 
-constexpr int kTile = kBlock * kHead;   // floats in one 64x64 partial tile
+template <int D>
+constexpr int kTileOf = kBlock * D;   // floats in one 64 x D partial tile
 
 struct BwdArgs {
   const uint16_t* q;
@@ -21,8 +22,8 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* dbuf;      // D [B*H*n]
-  float* part_q;    // [B*H*g*nseg][64][64]
-  float* part_kv;   // [B*H*g*nseg][2][64][64]
+  float* part_q;    // [B*H*g*nseg][64][d]
+  float* part_kv;   // [B*H*g*nseg][2][64][d]
   const int32_t* col_idx;
   const int32_t* csc_idx;
   const int32_t* gblk;
@@ -37,10 +38,10 @@ struct BwdArgs {
 // Tile loads for a sequence that may end inside its last block (kRagged): that
 // block's missing rows are not read and stage as zeros.  The kernels below are
 // instantiated with and without those guards; the whole-block instance has none.
-template <bool kRagged>
-__device__ __forceinline__ void load_block(TileRegs& r, const uint16_t* base, int blk,
+template <bool kRagged, int D>
+__device__ __forceinline__ void load_block(TileRegsT<D>& r, const uint16_t* base, int blk,
                                            const BwdArgs& a, int tid) {
-  const uint16_t* g = base + (size_t)blk * kBlock * kHead;
+  const uint16_t* g = base + (size_t)blk * kBlock * D;
   if (kRagged && blk == a.nb - 1) gload_nat_rows(r, g, tid, a.last_rows);
   else gload_nat(r, g, tid);
 }

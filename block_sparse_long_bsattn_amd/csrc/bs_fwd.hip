@@ -5,6 +5,9 @@
 // Sequences", §2 eq. (AT) and App. D eq. (13), Fig. 6; scaled scores as in
 // "Longformer: The Long-Document Transformer", §3.1 eq. (1)).
 //
+// Head dimension d = 64 (every configuration on the pages) or 128 (bf16 only):
+// one kernel template, the d-wide loops unrolled per instance.
+//
 // Work decomposition (one 128-thread work-group = 2 waves = one 64-row query
 // block; wave w owns query rows 32w .. 32w+31):
 //   * a non-global query block is one item walking its whole key-block list;
@@ -93,28 +96,28 @@ __device__ __forceinline__ Item decode_row_item(const FwdArgs& a, int v) {
 }
 
 // kRagged: the sequence ends inside its last block (n % 64 != 0); the instance for
-// whole blocks carries none of that block's masking and guards.
-template <bool kRagged>
+// whole blocks carries none of that block's masking and guards.  D: head dimension.
+template <int D, bool kRagged>
 __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kStrideOf<D>];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBlock * kStrideOf<D>];
 
   const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
   if (v < 0) return;
   const Item it = decode_row_item(a, v);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const size_t bh_off = (size_t)it.bh * a.n * kHead;
+  const size_t bh_off = (size_t)it.bh * a.n * D;
   const int qrow = it.i * kBlock + 32 * wave + col;   // token index of this lane's query
   const int32_t* keys = a.col_idx + it.start;
   const uint16_t* kbase = a.k + bh_off;
   const uint16_t* vbase = a.v + bh_off;
   const int len = it.len;
-  auto kaddr = [&](int kb) { return kbase + (size_t)kb * kBlock * kHead; };
-  auto vaddr = [&](int kb) { return vbase + (size_t)kb * kBlock * kHead; };
+  auto kaddr = [&](int kb) { return kbase + (size_t)kb * kBlock * D; };
+  auto vaddr = [&](int kb) { return vbase + (size_t)kb * kBlock * D; };
   // a sequence that ends inside its last block: that block's missing rows are
   // neither read nor attended to, and no output is written for them
-  auto tile_load = [&](int kb, TileRegs& kr, TileRegs& vr) {
+  auto tile_load = [&](int kb, TileRegsT<D>& kr, TileRegsT<D>& vr) {
     if (kRagged && kb == a.nb - 1) {
       gload_nat_rows(kr, kaddr(kb), tid, a.last_rows);
       gload_nat_rows(vr, vaddr(kb), tid, a.last_rows);
@@ -124,22 +127,22 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  TileRegs kr, vr;
+  TileRegsT<D> kr, vr;
   int kb_cur = 0;
   if (len > 0) {
     kb_cur = it.first;
     tile_load(kb_cur, kr, vr);
   }
   int kb_next = len > 1 ? it.at(keys, 1) : 0;
-  bf16x8 qB[4];
+  bf16x8 qB[D / 16];
   {
-    const uint16_t* qp = a.q + bh_off + (size_t)qrow * kHead + 8 * hl;
+    const uint16_t* qp = a.q + bh_off + (size_t)qrow * D + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qB[c] = !kRagged || qrow < a.n ? ld16(qp + 16 * c) : bf16x8{};
+    for (int c = 0; c < D / 16; ++c) qB[c] = !kRagged || qrow < a.n ? ld16(qp + 16 * c) : bf16x8{};
   }
   lds_store_nat(sK[0], kr, tid);
   lds_store_nat(sV[0], vr, tid);
-  FwdState st;
+  FwdStateT<D> st;
   fwd_state_init(st);
   for (int t = 0; t < len; ++t) {
     const int cur = t & 1;
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
       kb_next = t + 2 < len ? it.at(keys, t + 2) : 0;
     }
     // V^T operands read now; the softmax covers their LDS latency
-    bf16x8 vA[8];
+    bf16x8 vA[D / 8];
     pv_load(sV[cur], lane, vA);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 pc[4];
@@ -170,18 +173,20 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   const float l_tot = partner_sum(st.l), lb_tot = partner_sum(st.lb);
   if (it.slot < 0) {
     if (!kRagged || qrow < a.n)
-      write_o_bf16(st, l_tot, lb_tot, hl, a.o + bh_off + (size_t)qrow * kHead,
-                   a.o_lo != nullptr ? a.o_lo + bh_off + (size_t)qrow * kHead : nullptr,
+      write_o_bf16(st, l_tot, lb_tot, hl, a.o + bh_off + (size_t)qrow * D,
+                   a.o_lo != nullptr ? a.o_lo + bh_off + (size_t)qrow * D : nullptr,
                    a.lse != nullptr ? a.lse + (size_t)it.bh * a.n + qrow : nullptr);
   } else {
     write_partial(st, l_tot, lb_tot, hl, 32 * wave + col,
-                  a.part + (size_t)it.slot * kPartFloats);
+                  a.part + (size_t)it.slot * kPartFloatsOf<D>);
   }
 }
 
 // Merge the segment partials of every split global query block, in segment
 // order: M = max_s m_s, L = sum_s l_s 2^(m_s - M) (and Lb from the lb_s),
-// O = sum_s O_s 2^(m_s - M) / Lb, lse = M + log2 L.
+// O = sum_s O_s 2^(m_s - M) / Lb, lse = M + log2 L.  Thread t: query row t / 4,
+// columns 16 (t % 4) + 64 u .. +15, u = 0 .. D/64 - 1.
+template <int D>
 __global__ __launch_bounds__(256) void bs_fwd_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ gblk, int heads, int n,
     int g, int nseg, uint16_t* __restrict__ o, uint16_t* __restrict__ o_lo,
@@ -189,12 +194,17 @@ __global__ __launch_bounds__(256) void bs_fwd_combine_kernel(
   const int idx = blockIdx.x;           // (bh, gi)
   const int bh = idx / g, gi = idx - bh * g;
   const int row = threadIdx.x >> 2, dq = (threadIdx.x & 3) * 16;
-  float acc[16], M, L, Lb;
-  merge_partials(part + (size_t)idx * nseg * kPartFloats, nseg, row, dq, acc, M, L, Lb);
   const int tok = gblk[gi] * kBlock + row;
-  if (tok >= n) return;   // past the end of a sequence that ends inside this block
-  const size_t off = ((size_t)bh * n + tok) * kHead + dq;
-  store16_bf16_lo(o + off, o_lo != nullptr ? o_lo + off : nullptr, acc, 1.f / Lb);
+  float M = 0.f, L = 0.f;
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) {
+    float acc[16], Lb;
+    merge_partials<D>(part + (size_t)idx * nseg * kPartFloatsOf<D>, nseg, row, dq + 64 * u, acc,
+                      M, L, Lb);
+    if (tok >= n) return;   // past the end of a sequence that ends inside this block
+    const size_t off = ((size_t)bh * n + tok) * D + dq + 64 * u;
+    store16_bf16_lo(o + off, o_lo != nullptr ? o_lo + off : nullptr, acc, 1.f / Lb);
+  }
   if (lse != nullptr && (threadIdx.x & 3) == 0)
     lse[(size_t)bh * n + tok] = (M + __log2f(L)) * kLn2;
   (void)heads;
@@ -476,24 +486,31 @@ F32Plan f32_plan(const bsattn_layout* L, int batch) {
 }  // namespace
 
 // Workspace of one dtype's forward: bf16 global-row segments or fp32 row segments.
-size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt) {
+size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt, int d) {
   if (dt == BSATTN_F32) {
     const F32Plan fp = f32_plan(L, batch);
     return fp.nseg > 1 ? (size_t)batch * L->heads * L->nb * fp.nseg * kPartFloats * sizeof(float) : 0;
   }
   const SegPlan sp = seg_plan(L, batch);
-  return sp.split ? (size_t)batch * L->heads * L->g * sp.nseg * kPartFloats * sizeof(float) : 0;
+  const size_t part = d == 128 ? kPartFloatsOf<128> : kPartFloats;
+  return sp.split ? (size_t)batch * L->heads * L->g * sp.nseg * part * sizeof(float) : 0;
 }
 
-// The size the public query reports: enough for either dtype.
-size_t fwd_workspace_bytes(const bsattn_layout* L, int batch) {
-  return std::max(fwd_workspace_bytes_dt(L, batch, BSATTN_BF16),
-                  fwd_workspace_bytes_dt(L, batch, BSATTN_F32));
+// The size the public query reports: enough for either dtype that the head
+// dimension is built for (fp32 has d = 64 only).
+size_t fwd_workspace_bytes(const bsattn_layout* L, int batch, int d) {
+  const size_t bf = fwd_workspace_bytes_dt(L, batch, BSATTN_BF16, d);
+  return d == kHead ? std::max(bf, fwd_workspace_bytes_dt(L, batch, BSATTN_F32, d)) : bf;
 }
 
-int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, const void* q,
-               const void* k, const void* v, void* o, float* lse, void* o_lo, void* ws,
-               hipStream_t stream) {
+template <int D>
+int launch_fwd_bf16(const bsattn_layout* L, int batch, float scale, const void* q,
+                    const void* k, const void* v, void* o, float* lse, void* o_lo, void* ws,
+                    hipStream_t stream);
+
+int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, int d, float scale,
+               const void* q, const void* k, const void* v, void* o, float* lse, void* o_lo,
+               void* ws, hipStream_t stream) {
   const int bhn = batch * L->heads;
   if (dt == BSATTN_F32) {
     FwdF32Args a;
@@ -525,6 +542,15 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
     }
     return check_hip(hipGetLastError(), "bs_fwd_f32_combine launch");
   }
+  if (d == 128) return launch_fwd_bf16<128>(L, batch, scale, q, k, v, o, lse, o_lo, ws, stream);
+  return launch_fwd_bf16<kHead>(L, batch, scale, q, k, v, o, lse, o_lo, ws, stream);
+}
+
+template <int D>
+int launch_fwd_bf16(const bsattn_layout* L, int batch, float scale, const void* q,
+                    const void* k, const void* v, void* o, float* lse, void* o_lo, void* ws,
+                    hipStream_t stream) {
+  const int bhn = batch * L->heads;
   FwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.o = (uint16_t*)o; a.o_lo = (uint16_t*)o_lo; a.lse = lse; a.part = (float*)ws;
@@ -539,17 +565,17 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale, 
   a.sl2 = scale * kLog2e;
   const int grid = 8 * ((a.total_items + 7) / 8);
   {
-    ProfScope prof_("bs_fwd_bf16", stream);
+    ProfScope prof_(D == kHead ? "bs_fwd_bf16" : "bs_fwd_bf16_d128", stream);
     if (a.last_rows < kBlock)
-      hipLaunchKernelGGL(bs_fwd_bf16_kernel<true>, dim3(grid), dim3(kFwdThreads), 0, stream, a);
+      hipLaunchKernelGGL((bs_fwd_bf16_kernel<D, true>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(bs_fwd_bf16_kernel<false>, dim3(grid), dim3(kFwdThreads), 0, stream, a);
+      hipLaunchKernelGGL((bs_fwd_bf16_kernel<D, false>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
   }
   int st = check_hip(hipGetLastError(), "bs_fwd_bf16 launch");
   if (st || !sp.split || L->g == 0) return st;
   {
     ProfScope prof_("bs_fwd_combine", stream);
-    hipLaunchKernelGGL(bs_fwd_combine_kernel, dim3(bhn * L->g), dim3(256), 0, stream,
+    hipLaunchKernelGGL(bs_fwd_combine_kernel<D>, dim3(bhn * L->g), dim3(256), 0, stream,
                        (const float*)ws, L->d_gblk, L->heads, L->n, L->g, sp.nseg,
                        (uint16_t*)o, (uint16_t*)o_lo, lse);
   }

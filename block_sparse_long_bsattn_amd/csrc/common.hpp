@@ -30,7 +30,7 @@
 namespace bsattn {
 
 constexpr int kBlock = 64;   // tokens per block (b) and per Longformer tile
-constexpr int kHead = 64;    // head dimension (d)
+constexpr int kHead = 64;    // head dimension (d) of every kernel but the d = 128 instances
 constexpr int kLfSeg = 8;    // key tiles per work item of a split Longformer global row
 constexpr int kLdsStride = 72;  // bf16 elements per LDS tile row (64 + 8 pad)
 
@@ -119,46 +119,66 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ---------------------------------------------------------------------------
-// Cooperative 64x64 bf16 tile staging through LDS (128 threads): LDS row x holds
-// global row x (64 values + pad).  Thread t moves 16-byte chunk (t % 8) of rows
-// (t / 8) + 16u, u = 0..3, so eight lanes cover one 128-byte row.
+// Cooperative 64 x D bf16 tile staging through LDS (128 threads, D = 64 or 128):
+// LDS row x holds global row x (D values + an 8-element pad, so that the
+// row-strided reads spread over the banks as described above).  Thread t moves
+// 16-byte chunk (t % (D/8)) of rows t / (D/8) + (1024/D) u, u = 0 .. D/16 - 1,
+// so D/8 consecutive lanes cover one row.
 // ---------------------------------------------------------------------------
 
-struct TileRegs { u32x4 v[4]; };
+template <int D>
+constexpr int kStrideOf = D + 8;   // bf16 elements per LDS tile row
+static_assert(kStrideOf<kHead> == kLdsStride, "LDS row stride of the d = 64 tiles");
 
-__device__ __forceinline__ void gload_nat(TileRegs& r, const uint16_t* g, int tid) {
-  const int c = tid & 7, row = tid >> 3;
+template <int D>
+struct TileRegsT { u32x4 v[D / 16]; };
+using TileRegs = TileRegsT<kHead>;
+
+template <int D>
+__device__ __forceinline__ void gload_nat(TileRegsT<D>& r, const uint16_t* g, int tid) {
+  constexpr int kCpr = D / 8, kRpp = 128 / kCpr, kShift = D == 64 ? 3 : 4;
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  const int c = tid & (kCpr - 1), row = tid >> kShift;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) r.v[u] = ldg16(g + (row + 16 * u) * kHead + 8 * c);
+  for (int u = 0; u < D / 16; ++u) r.v[u] = ldg16(g + (row + kRpp * u) * D + 8 * c);
 }
 
 // The same for the last block of a sequence that ends inside it: only its first
 // `rows` rows are tokens; the others are not read and are staged as zeros.
-__device__ __forceinline__ void gload_nat_rows(TileRegs& r, const uint16_t* g, int tid, int rows) {
-  const int c = tid & 7, row = tid >> 3;
+template <int D>
+__device__ __forceinline__ void gload_nat_rows(TileRegsT<D>& r, const uint16_t* g, int tid,
+                                               int rows) {
+  constexpr int kCpr = D / 8, kRpp = 128 / kCpr, kShift = D == 64 ? 3 : 4;
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  const int c = tid & (kCpr - 1), row = tid >> kShift;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < D / 16; ++u) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (row + 16 * u < rows) x = ldg16(g + (row + 16 * u) * kHead + 8 * c);
+    if (row + kRpp * u < rows) x = ldg16(g + (row + kRpp * u) * D + 8 * c);
     r.v[u] = x;
   }
 }
 
-__device__ __forceinline__ void lds_store_nat(uint16_t* s, const TileRegs& r, int tid) {
-  const int c = tid & 7, row = tid >> 3;
+template <int D>
+__device__ __forceinline__ void lds_store_nat(uint16_t* s, const TileRegsT<D>& r, int tid) {
+  constexpr int kCpr = D / 8, kRpp = 128 / kCpr, kShift = D == 64 ? 3 : 4;
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  const int c = tid & (kCpr - 1), row = tid >> kShift;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    *reinterpret_cast<u32x4*>(s + (row + 16 * u) * kLdsStride + 8 * c) = r.v[u];
+  for (int u = 0; u < D / 16; ++u)
+    *reinterpret_cast<u32x4*>(s + (row + kRpp * u) * kStrideOf<D> + 8 * c) = r.v[u];
 }
 
 // MFMA operand of 8 k-slots for chunk c of a contraction over the rows of the
-// natural LDS tile s, for output rows/columns 32*tile .. 32*tile + 31 (the tile's
-// columns).  See the lane mapping described at the top of this file.
+// natural LDS tile s (row stride D + 8), for output rows/columns 32*tile ..
+// 32*tile + 31 (the tile's columns).  See the lane mapping described at the top
+// of this file.
+template <int D = kHead>
 __device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* s, int tile, int c, int lane) {
   const int row = 16 * c + 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int col = 32 * tile + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const lds_v4i16* p0 = (const lds_v4i16*)(s + row * kLdsStride + col);
-  const lds_v4i16* p1 = (const lds_v4i16*)(s + (row + 8) * kLdsStride + col);
+  const lds_v4i16* p0 = (const lds_v4i16*)(s + row * kStrideOf<D> + col);
+  const lds_v4i16* p1 = (const lds_v4i16*)(s + (row + 8) * kStrideOf<D> + col);
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4i16*>(p0));
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4i16*>(p1));
   const v4i16 both[2] = {lo, hi};

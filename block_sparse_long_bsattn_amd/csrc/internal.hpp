@@ -103,11 +103,11 @@ int check_hip(hipError_t e, const char* what);
 int launch_layout_rowptr(bsattn_layout* L, hipStream_t stream);
 int launch_layout_build(bsattn_layout* L, hipStream_t stream);
 // o_lo (forward: written, backward: read) is the bf16 rounding residual of O, or
-// null.
-int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, float scale,
+// null.  d: head dimension, 64 (any dtype) or 128 (bf16).
+int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, int d, float scale,
                const void* q, const void* k, const void* v, void* o, float* lse,
                void* o_lo, void* ws, hipStream_t stream);
-int launch_bwd(const bsattn_layout* L, int batch, float scale, const void* q,
+int launch_bwd(const bsattn_layout* L, int batch, int d, float scale, const void* q,
                const void* k, const void* v, const void* o, const void* o_lo,
                const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
                hipStream_t stream);
@@ -117,9 +117,9 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const
                   const void* vg, void* o, float* lse, void* o_lo, void* ws,
                   hipStream_t stream);
 
-size_t fwd_workspace_bytes(const bsattn_layout* L, int batch);   // enough for either dtype
-size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt);
-size_t bwd_workspace_bytes(const bsattn_layout* L, int batch);
+size_t fwd_workspace_bytes(const bsattn_layout* L, int batch, int d);   // either dtype
+size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt, int d);
+size_t bwd_workspace_bytes(const bsattn_layout* L, int batch, int d);
 size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads);
 int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,

@@ -139,11 +139,12 @@ int bsattn_layout_destroy(bsattn_layout* layout);
 /* BigBird-ITC forward and backward                                           */
 /* ------------------------------------------------------------------------- */
 
-/* Workspace bytes bsattn_fwd / bsattn_bwd need for this layout and batch (may be
- * 0).  d must be 64.  Returns 0 for invalid arguments as well.  The forward's size
- * serves both dtypes: bf16 uses it for the segments of split global rows, fp32 for
- * the segments of rows split when the problem has fewer query blocks than half
- * the device's work-group slots (small, latency-bound problems). */
+/* Workspace bytes bsattn_fwd / bsattn_bwd need for this layout, batch and head
+ * dimension d (64 or 128; may be 0).  Returns 0 for invalid arguments as well.
+ * For d = 64 the forward's size serves both dtypes: bf16 uses it for the segments
+ * of split global rows, fp32 for the segments of rows split when the problem has
+ * fewer query blocks than half the device's work-group slots (small,
+ * latency-bound problems); for d = 128 (bf16 only) it is the bf16 size. */
 size_t bsattn_fwd_workspace(const bsattn_layout* layout, int batch, int d);
 size_t bsattn_bwd_workspace(const bsattn_layout* layout, int batch, int d);
 
@@ -155,7 +156,8 @@ size_t bsattn_bwd_workspace(const bsattn_layout* layout, int batch, int d);
  *
  *   layout      built layout (heads and n taken from it).
  *   batch       >= 1.
- *   d           head dimension; must be 64.
+ *   d           head dimension: 64, or 128 with BSATTN_BF16 (EUNSUPPORTED
+ *               otherwise).  Every configuration of [BB] and [LF] has d = 64.
  *   dt          BSATTN_BF16 (bf16 MFMA products, fp32 softmax) or BSATTN_F32.
  *   scale       score scale, e.g. 1/sqrt(d).
  *   q, k, v     DEVICE [batch, heads, n, d] of type dt.
@@ -173,6 +175,7 @@ int bsattn_fwd(const bsattn_layout* layout, int batch, int d, bsattn_dtype dt, f
 
 /*
  * Backward: the exact gradient of bsattn_fwd for the loss <dout, O>.
+ *   d           head dimension, 64 or 128 (EUNSUPPORTED otherwise).
  *   q, k, v, o  DEVICE [batch, heads, n, d] (o from bsattn_fwd).
  *   o_lo        DEVICE bf16 [batch, heads, n, d] from bsattn_fwd, or NULL.
  *   lse         DEVICE float32 [batch, heads, n] from bsattn_fwd (required).
