@@ -382,6 +382,101 @@ def cpu_baseline(cfg: dict, budget_s: float):
 
 
 # ---------------------------------------------------------------------------
+# Results table: every configured single-pass workload on the GPU, next to the
+# oracle on the same inputs (max-abs error) and the oracle's own time on one host
+# thread (median of three full runs where that fits in about a minute)
+# ---------------------------------------------------------------------------
+
+# (workload, part of it given to the oracle, three timed oracle runs (else one))
+TABLE_WORKLOADS = [
+    ("bigbird_fwd_fp32_b1_h1_n512", "all", True),
+    ("bigbird_fwd_b2_h12_n4096", "all", True),
+    ("bigbird_fwd_b1_h16_n16384", "all", False),
+    ("bigbird_fwd_bwd_b4_h12_n4096", "all", False),
+    ("longformer_fwd_b1_h12_n4096_w256_g64", "all", True),
+]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def oracle_mask(cfg: dict):
+    """Mask callback (h, p0, p1) of a workload's token pattern."""
+    from block_sparse_long_bsattn_amd import inputs as I
+    from oracle import layout as OL
+    from oracle import longformer as OLF
+    if cfg["kind"] == "longformer":
+        return OLF.longformer_mask(cfg["n"], cfg["w1"], cfg["G"])
+    n = cfg["n"]
+    nb = n // 64
+    lay = OL.build_layout(n, 64, cfg["heads"], cfg["G"], cfg["w"], cfg["r"], I.SEED_LAYOUT)
+
+    def mask(h, p0, p1):
+        blk = np.zeros((p1 - p0, nb), dtype=bool)
+        for p in range(p0, p1):
+            blk[p - p0, lay["rows"][h][p // 64]] = True
+        return np.repeat(blk, 64, axis=1)
+    return mask
+
+
+def results_table(steps: int, warmup: int, settle_ms: float) -> dict:
+    import torch
+    from threadpoolctl import threadpool_limits
+    from block_sparse_long_bsattn_amd import inputs as I
+    from oracle import attention as OA
+    rows = []
+    for name, part, time_full in TABLE_WORKLOADS:
+        cfg = WORKLOADS[name]
+        log(f"table: {name}")
+        job = Job(name, cfg)
+        settle(job, settle_ms)
+        ms, _ = time_steps(job, steps, warmup)
+        job.step()
+        torch.cuda.synchronize()
+        got = {"o": job.o, "lse": job.lse}
+        if cfg["bwd"]:
+            got.update(dq=job.dq, dk=job.dk, dv=job.dv)
+        got = {k: v.float().cpu().numpy().astype(np.float64) for k, v in got.items()}
+        flops = job.flops
+        job.close()
+        shape = (cfg["batch"], cfg["heads"], cfg["n"], D)
+        q, k, v, do = (I.make_tensor(sd, shape, cfg["dtype"])[1]
+                       for sd in (I.SEED_Q, I.SEED_K, I.SEED_V, I.SEED_DO))
+        mask = oracle_mask(cfg)
+        scale = 1 / math.sqrt(D)
+        sl = (slice(None), slice(None)) if part == "all" else (slice(0, 1), slice(0, 1))
+        mh = mask if part == "all" else (lambda _h, p0, p1: mask(0, p0, p1))
+        secs = []
+        with threadpool_limits(1):
+            for _ in range(3 if time_full else 1):
+                t0 = time.perf_counter()
+                ro, rl = OA.attention_fwd(q[sl], k[sl], v[sl], mh, scale)
+                ref = [ro, rl]
+                if cfg["bwd"]:
+                    ref += list(OA.attention_bwd(q[sl], k[sl], v[sl], do[sl], mh, scale))
+                secs.append(time.perf_counter() - t0)
+                log(f"  oracle run {len(secs)}: {secs[-1]:.2f} s")
+        names = ["o", "lse"] + (["dq", "dk", "dv"] if cfg["bwd"] else [])
+        err = max(float(np.max(np.abs(got[nm][sl] - r))) for nm, r in zip(names, ref))
+        peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_FP32_TFLOPS
+        tfl = flops / (ms * 1e-3) / 1e12
+        rows.append({"workload": name, "gpu_us_per_step": round(ms * 1e3, 2),
+                     "useful_tflops": round(tfl, 2), "pct_peak": round(100 * tfl / peak, 2),
+                     "max_abs_vs_oracle": err, "oracle_part": part,
+                     "oracle_s_1thread": round(float(np.median(secs)), 3),
+                     "oracle_runs": len(secs)})
+        log(f"  {ms * 1e3:.1f} us, {tfl:.1f} TFLOP/s, max-abs {err:.2e}, oracle "
+            f"{np.median(secs):.2f} s ({part}, 1 thread)")
+    return {"cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(), "rows": rows}
+
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -390,6 +485,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="untimed steps for this long before the warm-up steps (clock ramp)")
+    ap.add_argument("--table", action="store_true",
+                    help="print only the per-workload table (GPU time, error against the "
+                         "oracle, oracle time on one host thread) as one JSON line")
     ap.add_argument("--workload", default=PRIMARY, choices=sorted(WORKLOADS))
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -413,6 +511,10 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copy calibration: {args.copy_mib} MiB")
         del src, dst
+
+    if args.table:
+        print(json.dumps(results_table(args.steps, args.warmup, args.settle_ms)), flush=True)
+        return 0
 
     cfg = WORKLOADS[args.workload]
     log(f"workload {args.workload}: setting up")

@@ -7,13 +7,15 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
 #include <vector>
 
-#include "common.hpp"
 #include "internal.hpp"
+#include "shape.hpp"
 
 namespace bsattn {
 
@@ -36,7 +38,16 @@ bool g_prof_on = false;
 std::vector<ProfRecord> g_prof;
 }  // namespace
 
+int debug_level() {
+  static const int level = [] {
+    const char* s = std::getenv("BSATTN_DEBUG");
+    return s != nullptr ? std::atoi(s) : 0;
+  }();
+  return level;
+}
+
 ProfScope::ProfScope(const char* name, hipStream_t stream) : name_(name), stream_(stream) {
+  if (debug_level() >= 1) std::fprintf(stderr, "[bsattn] launch %s stream=%p\n", name, (void*)stream);
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
   if (hipEventCreate(&start_) != hipSuccess) { start_ = nullptr; return; }
@@ -60,7 +71,50 @@ ProfScope::~ProfScope() {
 
 int set_error(int status, const std::string& msg) {
   g_last_error = msg;
+  if (debug_level() >= 1) std::fprintf(stderr, "[bsattn] error %d: %s\n", status, msg.c_str());
   return status;
+}
+
+namespace {
+constexpr size_t kCanaryBytes = 64;
+constexpr unsigned char kCanary = 0xA5;
+}  // namespace
+
+DebugCall::DebugCall(const char* who, hipStream_t stream, void* ws, size_t ws_bytes,
+                     size_t need)
+    : who_(who), stream_(stream), ws_(ws), need_(need) {
+  const int level = debug_level();
+  if (level < 1) return;
+  std::fprintf(stderr, "[bsattn] call %s stream=%p workspace=%zu of %zu bytes needed\n", who,
+               (void*)stream, ws_bytes, need);
+  if (level < 2 || ws == nullptr || ws_bytes < need + kCanaryBytes) return;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+  static const std::vector<unsigned char> pattern(kCanaryBytes, kCanary);
+  canary_ = hipMemcpyAsync(static_cast<char*>(ws) + need, pattern.data(), kCanaryBytes,
+                           hipMemcpyHostToDevice, stream) == hipSuccess;
+}
+
+int DebugCall::finish(int st) {
+  if (st != BSATTN_OK || debug_level() < 2) return st;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream_, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return st;
+  const std::string w(who_);
+  hipError_t e = hipStreamSynchronize(stream_);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return set_error(BSATTN_EHIP, w + ": kernel failed: " + hipGetErrorString(e));
+  if (canary_) {
+    std::vector<unsigned char> got(kCanaryBytes, 0);
+    e = hipMemcpy(got.data(), static_cast<char*>(ws_) + need_, kCanaryBytes, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return check_hip(e, "debug canary read");
+    for (unsigned char c : got)
+      if (c != kCanary)
+        return set_error(BSATTN_EHIP, w + ": workspace written past the " +
+                                          std::to_string(need_) + " bytes the call needs");
+  }
+  if (debug_level() >= 1) std::fprintf(stderr, "[bsattn] done %s\n", who_);
+  return st;
 }
 
 void clear_error() { g_last_error.clear(); }
@@ -293,12 +347,14 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
     free_layout(L);
     return st;
   }
+  DebugCall dbg("layout_build", stream, nullptr, 0, 0);
   if ((st = launch_layout_rowptr(L, stream)) || (st = launch_layout_build(L, stream))) {
     free_layout(L);
     return st;
   }
   if ((st = check_hip(hipEventCreateWithFlags(&L->built, hipEventDisableTiming), "layout event")) ||
-      (st = check_hip(hipEventRecord(L->built, stream), "layout event record"))) {
+      (st = check_hip(hipEventRecord(L->built, stream), "layout event record")) ||
+      (st = dbg.finish(BSATTN_OK))) {
     free_layout(L);
     return st;
   }
@@ -312,8 +368,9 @@ int bsattn_layout_rebuild(bsattn_layout* L, uint64_t seed, hipStream_t stream) {
   int st = check_device(L->device);
   if (st) return st;
   L->seed = seed;
+  DebugCall dbg("layout_rebuild", stream, nullptr, 0, 0);
   if ((st = launch_layout_build(L, stream))) return st;
-  return check_hip(hipEventRecord(L->built, stream), "layout event record");
+  return dbg.finish(check_hip(hipEventRecord(L->built, stream), "layout event record"));
 }
 
 int bsattn_layout_info(const bsattn_layout* L, int* nb, int* heads, int64_t* nnzb_total) {
@@ -384,7 +441,8 @@ int bsattn_fwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float 
   const size_t need = fwd_workspace_bytes_dt(L, batch, dt, d);
   if ((st = check_workspace(workspace, ws_bytes, need, "fwd"))) return st;
   if ((st = check_device(L->device))) return st;
-  return launch_fwd(L, batch, dt, d, scale, q, k, v, o, lse, o_lo, workspace, stream);
+  DebugCall dbg("fwd", stream, workspace, ws_bytes, need);
+  return dbg.finish(launch_fwd(L, batch, dt, d, scale, q, k, v, o, lse, o_lo, workspace, stream));
 }
 
 int bsattn_bwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
@@ -399,9 +457,12 @@ int bsattn_bwd(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float 
   if ((st = check_o_lo(o_lo, dt, "bwd"))) return st;
   if ((int64_t)batch * L->heads * L->n * d >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, "bwd: tensor too large");
-  if ((st = check_workspace(workspace, ws_bytes, bwd_workspace_bytes(L, batch, d), "bwd"))) return st;
+  const size_t need = bwd_workspace_bytes(L, batch, d);
+  if ((st = check_workspace(workspace, ws_bytes, need, "bwd"))) return st;
   if ((st = check_device(L->device))) return st;
-  return launch_bwd(L, batch, d, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, workspace, stream);
+  DebugCall dbg("bwd", stream, workspace, ws_bytes, need);
+  return dbg.finish(
+      launch_bwd(L, batch, d, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, workspace, stream));
 }
 
 int bsattn_bwd_noalloc(const bsattn_layout* L, int batch, int d, bsattn_dtype dt, float scale,
@@ -426,7 +487,9 @@ int bsattn_bwd_noalloc(const bsattn_layout* L, int batch, int d, bsattn_dtype dt
   if ((st = check_device(L->device))) return st;
   void* ws = nullptr;
   if ((st = noalloc_scratch(&ws))) return st;
-  return launch_bwd(L, batch, d, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, ws, stream);
+  DebugCall dbg("bwd_noalloc", stream, ws, noalloc_scratch_bytes(), need);
+  return dbg.finish(
+      launch_bwd(L, batch, d, scale, q, k, v, o, o_lo, lse, dout, dq, dk, dv, ws, stream));
 }
 
 }  // extern "C"
@@ -631,10 +694,12 @@ int lf_fwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int
   if ((st = check_o_lo(o_lo, dt, who))) return st;
   if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, w + ": tensor too large");
-  if ((st = check_workspace(workspace, ws_bytes, lf_workspace_bytes(P, batch, heads), who))) return st;
+  const size_t need = lf_workspace_bytes(P, batch, heads);
+  if ((st = check_workspace(workspace, ws_bytes, need, who))) return st;
   if ((st = check_device(P->device))) return st;
-  return launch_lf_fwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, lse, o_lo, workspace,
-                       stream);
+  DebugCall dbg(who, stream, workspace, ws_bytes, need);
+  return dbg.finish(launch_lf_fwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, lse, o_lo,
+                                  workspace, stream));
 }
 
 }  // namespace
@@ -694,11 +759,12 @@ int lf_bwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int
   }
   if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, w + ": tensor too large");
-  if ((st = check_workspace(workspace, ws_bytes, lf_bwd_workspace_bytes(P, batch, heads), who)))
-    return st;
+  const size_t need = lf_bwd_workspace_bytes(P, batch, heads);
+  if ((st = check_workspace(workspace, ws_bytes, need, who))) return st;
   if ((st = check_device(P->device))) return st;
-  return launch_lf_bwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, o_lo, lse, dout, dq, dk,
-                       dv, dqg, dkg, dvg, workspace, stream);
+  DebugCall dbg(who, stream, workspace, ws_bytes, need);
+  return dbg.finish(launch_lf_bwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, o_lo, lse, dout,
+                                  dq, dk, dv, dqg, dkg, dvg, workspace, stream));
 }
 
 }  // namespace

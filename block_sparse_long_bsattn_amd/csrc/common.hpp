@@ -27,11 +27,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "shape.hpp"
+
 namespace bsattn {
 
-constexpr int kBlock = 64;   // tokens per block (b) and per Longformer tile
-constexpr int kHead = 64;    // head dimension (d) of every kernel but the d = 128 instances
-constexpr int kLfSeg = 8;    // key tiles per work item of a split Longformer global row
 constexpr int kLdsStride = 72;  // bf16 elements per LDS tile row (64 + 8 pad)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

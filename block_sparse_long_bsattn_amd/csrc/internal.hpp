@@ -95,6 +95,28 @@ class ProfScope {
   hipEvent_t start_ = nullptr;
 };
 
+// BSATTN_DEBUG, read once from the environment: 0 (unset) silent; 1 logs every
+// compute call, kernel launch and error to stderr; 2 also synchronises the stream
+// after each compute call (unless it is being captured into a graph) and reports a
+// failed kernel, or a write past the workspace bytes the call needs (a canary
+// placed after them when the caller's workspace has 64 spare bytes), as BSATTN_EHIP
+// at the call that caused it.
+int debug_level();
+
+// The level-1 log and level-2 checks of one compute call, around its launches.
+class DebugCall {
+ public:
+  DebugCall(const char* who, hipStream_t stream, void* ws, size_t ws_bytes, size_t need);
+  int finish(int st);   // st, or the failure the level-2 checks found
+
+ private:
+  const char* who_;
+  hipStream_t stream_;
+  void* ws_;
+  size_t need_;
+  bool canary_ = false;
+};
+
 int set_error(int status, const std::string& msg);
 void clear_error();
 int check_hip(hipError_t e, const char* what);
