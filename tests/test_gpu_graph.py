@@ -88,3 +88,28 @@ def test_longformer_step_replays_bitwise():
         assert capture_and_replay(step, [o, lse, dq, dk, dv])
     finally:
         B.lfattn_plan_destroy(plan)
+
+
+def test_blocksparse_d128_noalloc_step_replays_bitwise():
+    """Head dimension 128, the forward writing the O residual and the backward
+    without a workspace (its static scratch): the step a graph-capturing caller that
+    cannot allocate would record."""
+    n, heads, bsz, d = 768, 2, 1, 128
+    (q, k, v, do), _ = qkv((bsz, heads, n, d), "bf16", SEEDS)
+    lay = B.bsattn_layout_build(n, 64, heads, [0, 11], 3, 3, 9)
+    try:
+        o, olo = torch.empty_like(q), torch.empty_like(q)
+        lse = torch.empty((bsz, heads, n), dtype=torch.float32, device="cuda")
+        wsf = torch.empty(max(16, B.bsattn_fwd_workspace(lay, bsz, d)), dtype=torch.uint8,
+                          device="cuda")
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+        def step():
+            B.bsattn_layout_rebuild(lay, 13)
+            B.bsattn_fwd(lay, q, k, v, o, lse, wsf, o_lo=olo)
+            B.bsattn_bwd_noalloc(lay, q, k, v, o, lse, do, dq, dk, dv, o_lo=olo)
+
+        say("graph: block-sparse d=128 rebuild + fwd + no-allocation bwd")
+        assert capture_and_replay(step, [o, olo, lse, dq, dk, dv])
+    finally:
+        B.bsattn_layout_destroy(lay)
