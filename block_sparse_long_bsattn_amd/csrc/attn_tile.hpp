@@ -64,6 +64,16 @@ __device__ __forceinline__ void mask_keys_from(f32x16& s0, f32x16& s1, int hl, i
   }
 }
 
+// The same keys set to zero instead (dS of keys that are not tokens).
+__device__ __forceinline__ void zero_keys_from(f32x16& s0, f32x16& s1, int hl, int kmin) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int x = 8 * (r >> 2) + 4 * hl + (r & 3);
+    if (x >= kmin) s0[r] = 0.f;
+    if (32 + x >= kmin) s1[r] = 0.f;
+  }
+}
+
 // Online softmax over one key tile of raw scores S = Q.K (fp32; -inf marks an
 // excluded key).  Probabilities are 2^(S*sl2 - m) with sl2 = scale*log2(e) applied
 // in fp32 and m a reference maximum in log2 units.  The reference only moves when

@@ -9,8 +9,10 @@
 // Head dimension d = 64 or 128: one template per kernel, instantiated for both.
 //
 // No atomics: every output tile has one owner.
-//   bs_bwd_dq    one work-group per query block (row of the layout): computes
-//                D for its rows (written for the next kernel) and dQ.
+//   bs_bwd_dq    one work-group per query block (row of the layout): dQ, and D
+//                for the next kernel (rowsum(dO * O), corrected by the row sum of
+//                dS where the item holds the whole row: then it is sum P * dP
+//                with the probabilities this backward recomputes).
 //   bs_bwd_dkdv  one work-group per key block (column of the transposed layout):
 //                dK and dV, walking the query blocks that see that key block.
 //   bs_bwd_reduce  global rows / columns are full-length; they are split into
@@ -94,7 +96,11 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     }
   }
   const float Dq = partner_sum(dsum);   // D = rowsum(dO * O)
-  if (it.seg == 0 && hl == 0 && qvalid) a.dbuf[(size_t)it.bh * a.n + qrow] = Dq;
+  // A segment of a split row writes this D for the dK/dV kernel.  An item holding a
+  // whole row writes it after the loop, corrected by the row sum of dS: that sum is
+  // sum P dP - D sum P, with the probabilities P the backward itself recomputes, so
+  // D + sum dS is sum P dP free of the bf16 rounding of the weights behind O.
+  if (it.slot >= 0 && it.seg == 0 && hl == 0 && qvalid) a.dbuf[(size_t)it.bh * a.n + qrow] = Dq;
   // accumulators seeded so that the MFMAs return S - lse/scale (raw score units,
   // the scale applied in fp32 below: P = 2^((S - lse/scale) * scale*log2(e))) and
   // dP - D
@@ -111,6 +117,8 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
   f32x16 g[kT];   // dQ^T: g[t] holds d rows 32t..32t+31
 #pragma unroll
   for (int t = 0; t < kT; ++t) g[t] = zero16();
+  float ds_sum = 0.f;   // this half-lane's share of the row sum of dS
+  int kb_cur = it.len > 0 ? it.first : 0;
   for (int t = 0; t < it.len; ++t) {
     const int cur = t & 1;
     __syncthreads();
@@ -118,8 +126,9 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
     if (more) {
       load_block<kRagged>(kr, kbase, kb_next, a, tid);
       load_block<kRagged>(vr, vbase, kb_next, a, tid);
-      kb_next = t + 2 < it.len ? it.at(keys, t + 2) : 0;
     }
+    const int kb_after = kb_next;   // block of tile t + 1
+    if (more) kb_next = t + 2 < it.len ? it.at(keys, t + 2) : 0;
     // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
     f32x16 s0 = seed_s, s1 = seed_s, p0 = seed_d, p1 = seed_d;
 #pragma unroll
@@ -138,6 +147,18 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
       s0[r] = fast_exp2(s0[r] * a.sl2) * p0[r];      // dS = P * (dP - D)
       s1[r] = fast_exp2(s1[r] * a.sl2) * p1[r];
     }
+    // keys past the end of a sequence that ends inside this block are zero rows of
+    // K and V: their dS multiplies a zero K row in dQ, but is not part of the row sum
+    if (kRagged && kb_cur == a.nb - 1) zero_keys_from(s0, s1, hl, a.last_rows);
+    {
+      float r0 = s0[0], r1 = s1[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        r0 += s0[r];
+        r1 += s1[r];
+      }
+      ds_sum += r0 + r1;
+    }
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]; K^T from transpose reads
     const bf16x8 dc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
 #pragma unroll
@@ -148,11 +169,14 @@ __global__ __launch_bounds__(kThreads) void bs_bwd_dq_kernel(BwdArgs a) {
       lds_store_nat(sK[cur ^ 1], kr, tid);
       lds_store_nat(sV[cur ^ 1], vr, tid);
     }
+    kb_cur = kb_after;
   }
 
   const float sc = a.scale;
   if (it.slot < 0) {
+    const float dfix = Dq + partner_sum(ds_sum);
     if (!qvalid) return;
+    if (hl == 0) a.dbuf[(size_t)it.bh * a.n + qrow] = dfix;
     uint16_t* op = a.dq + bh_off + (size_t)qrow * D + 4 * hl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

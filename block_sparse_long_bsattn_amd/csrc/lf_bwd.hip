@@ -15,8 +15,9 @@
 //   lf_bwd_dq    row-owned, two kinds of item:
 //                * a 64-row query class tile (not made only of global tokens): its
 //                  window's key tiles, then the tiles of global keys outside them
-//                  (rows gathered by index), as in the forward; writes D for its
-//                  rows and dQ for its non-global rows;
+//                  (rows gathered by index), as in the forward; writes dQ and D
+//                  for its non-global rows (rowsum(dO * O) corrected by the row
+//                  sum of dS: sum P * dP with the recomputed probabilities);
 //                * a segment of kLfSeg key tiles for a tile of global query rows
 //                  (full rows): writes D (first segment) and an fp32 partial dQ.
 //   lf_bwd_dkdv  column-owned, two kinds of item:
@@ -178,7 +179,12 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     }
   }
   const float Dq = partner_sum(dsum);   // D = rowsum(dO * O)
-  if (seg == 0 && hl == 0 && ((vm_q >> xq) & 1ull)) a.dbuf[(size_t)bh * a.n + p] = Dq;
+  // The first segment of a global query tile writes this D for the dK/dV kernels.  A
+  // band item holds every key of its (non-global) rows and writes D after the loop,
+  // corrected by the row sum of dS: that sum is sum P dP - D sum P, with the
+  // probabilities P the backward itself recomputes, so D + sum dS is sum P dP free
+  // of the bf16 rounding of the weights behind O.
+  if (!band && seg == 0 && hl == 0) a.dbuf[(size_t)bh * a.n + p] = Dq;
   const float lse2 = a.lse[(size_t)bh * a.n + p] * kLog2e;
   if (x < ntile) {
     lds_store_nat(sK[0], kr, tid);
@@ -187,6 +193,7 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
   wait_all_loads();
 
   f32x16 g0 = zero16(), g1 = zero16();   // dQ^T, d rows 0..31 and 32..63
+  float ds_sum = 0.f;   // this half-lane's share of the row sum of dS (masked keys: 0)
   int cur = 0;
   while (x < ntile) {
     __syncthreads();
@@ -230,6 +237,15 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
       s0[r] = fast_exp2(__builtin_fmaf(s0[r], a.sl2, -lse2)) * (p0[r] - Dq);
       s1[r] = fast_exp2(__builtin_fmaf(s1[r], a.sl2, -lse2)) * (p1[r] - Dq);
     }
+    if constexpr (kBand) {
+      float r0 = s0[0], r1 = s1[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        r0 += s0[r];
+        r1 += s1[r];
+      }
+      ds_sum += r0 + r1;
+    }
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]; K^T from transpose reads
     const bf16x8 dc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
 #pragma unroll
@@ -247,7 +263,9 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
 
   const float sc = a.scale;
   if constexpr (kBand) {
+    const float dfix = Dq + partner_sum(ds_sum);
     if (((vm_q & ~gm_q) >> xq) & 1ull) {   // rows of global tokens: global items
+      if (hl == 0) a.dbuf[(size_t)bh * a.n + p] = dfix;
       uint16_t* op = a.dq + bh_off + (size_t)p * kHead + 4 * hl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
