@@ -46,6 +46,13 @@
  *   - Errors are returned as negative bsattn_status codes; nothing is thrown
  *     across the ABI.  Arguments are checked on the host before any launch;
  *     bsattn_last_error() returns a message for the calling thread's last error.
+ *   - The environment variable BSATTN_DEBUG, read once per process: 1 logs every
+ *     compute call, kernel launch and error to stderr; 2 also synchronises the
+ *     stream after each compute call (not while the stream is being captured into
+ *     a graph) and returns BSATTN_EHIP from the call whose kernels failed, or whose
+ *     kernels wrote into the 64 bytes after the workspace bytes the call needs
+ *     (checked when the workspace passed has that much spare).  Unset or 0: no
+ *     logging and no extra synchronisation.
  */
 #ifndef BSATTN_H
 #define BSATTN_H
