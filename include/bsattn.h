@@ -119,7 +119,10 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
 int bsattn_layout_rebuild(bsattn_layout* layout, uint64_t seed, hipStream_t stream);
 
 /* Sizes of a layout: blocks per head, heads, and total stored block pairs over all
- * heads (the length of col_idx and of csc_idx).  Any output pointer may be NULL. */
+ * heads (the length of col_idx and of csc_idx).  Any output pointer may be NULL.
+ * Every head stores the same number of pairs, nnzb_total / heads: a row's length
+ * depends on its block index, the global set, w and r, never on the random draws
+ * ("Big Bird", App. D: r random blocks per row beside the window and the globals). */
 int bsattn_layout_info(const bsattn_layout* layout, int* nb, int* heads,
                        int64_t* nnzb_total);
 

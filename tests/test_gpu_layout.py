@@ -22,9 +22,14 @@ def compare(n, heads, G, w, r, seed):
     h = B.bsattn_layout_build(n, 64, heads, G, w, r, seed)
     try:
         rp, ci, cp, cs = B.bsattn_layout_to_host(h)
+        nb, hh, nnz = B.bsattn_layout_info(h)
     finally:
         B.bsattn_layout_destroy(h)
     ref = OL.build_layout(n, 64, heads, G, w, r, seed)
+    assert (nb, hh, nnz) == ((n + 63) // 64, heads, len(ref["col_idx"]))
+    # every head stores nnz / heads pairs
+    assert all(ref["row_ptr"][(x + 1) * nb] - ref["row_ptr"][x * nb] == nnz // heads
+               for x in range(heads))
     np.testing.assert_array_equal(rp, ref["row_ptr"])
     np.testing.assert_array_equal(ci, ref["col_idx"])
     np.testing.assert_array_equal(cp, ref["csc_ptr"])

@@ -107,6 +107,9 @@ def test_layout_invariants(case):
             c0, c1 = lay["csc_ptr"][h * nb + j], lay["csc_ptr"][h * nb + j + 1]
             assert list(lay["csc_idx"][c0:c1]) == list(np.nonzero(dense[:, j])[0])
     assert lay["csc_ptr"][-1] == lay["row_ptr"][-1] == len(lay["col_idx"])
+    # row lengths do not depend on the draws, so every head stores the same count
+    per_head = [lay["row_ptr"][(h + 1) * nb] - lay["row_ptr"][h * nb] for h in range(heads)]
+    assert len(set(per_head)) == 1
 
 
 def test_heads_draw_independently():
