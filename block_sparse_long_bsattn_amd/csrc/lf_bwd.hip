@@ -131,11 +131,48 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     ntile = hi_u - lo_u + 1;
   }
   const int nband = hi_u - lo_u + 1;
-  auto next_tile = [&](int x) -> int {
-    while (x < ntile && x >= nband &&
-           global_outside(a.gtok, a.ng, x - nband, cls, stride, lo_u, hi_u, lane) == 0ull)
-      ++x;
+  // The next tile at or after x, skipping global tiles with no eligible key; for a
+  // global tile, el receives its eligible keys.
+  auto next_tile = [&](int x, uint64_t& el) -> int {
+    for (; x < ntile; ++x) {
+      if (x < nband) return x;
+      el = global_outside(a.gtok, a.ng, x - nband, cls, stride, lo_u, hi_u, lane);
+      if (el != 0ull) return x;
+    }
     return x;
+  };
+  // Keys of tile x this lane's row may attend to, in two steps (see lf_band_item of
+  // the forward): mask_issue reads the tile's global-row word before the iteration's
+  // prefetch, mask_done (every lane) applies it.
+  struct TileMask {
+    bool need;      // uniform
+    bool cut;       // a band tile the window cuts or the class ends in
+    uint64_t bits;  // cut band tile: window and class-end bits; global tile: el
+    ClassGBits g;
+  };
+  auto mask_issue = [&](int x, uint64_t el) -> TileMask {
+    TileMask m{false, false, el, ClassGBits{0ull, -1}};
+    if constexpr (kBand) {
+      if (x >= nband) {
+        m.need = el != ~0ull;
+        return m;
+      }
+      const int u = lo_u + x;
+      const uint64_t vm = valid_rows(u, nc);
+      if (!tiles_in_window(a.win, t, u) || vm != ~0ull) {
+        const int j0 = u * kBlock;
+        m.need = m.cut = true;
+        m.bits = bit_range(klo - j0, khi - j0) & vm;
+        m.g = class_gbits_issue(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane);
+      }
+    } else if (lo_u + x == a.nt - 1) {   // keys past the end of the sequence
+      m.bits = valid_rows(a.nt - 1, a.n);
+      m.need = m.bits != ~0ull;
+    }
+    return m;
+  };
+  auto mask_done = [&](const TileMask& m) -> uint64_t {
+    return m.cut ? m.bits | class_gbits_done(m.g, a.ng, stride) : m.bits;
   };
   const uint16_t* kbase = (band ? a.k : a.kg) + bh_off;
   const uint16_t* vbase = (band ? a.v : a.vg) + bh_off;
@@ -149,7 +186,8 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     }
   };
 
-  int x = next_tile(0);
+  uint64_t el = ~0ull;   // eligible keys of tile x when it is a global tile
+  int x = next_tile(0, el);
   TileRegs kr, vr;
   if (x < ntile) tile_load(x, kr, vr);
   bf16x8 qB[4], doB[4];
@@ -197,7 +235,9 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
   int cur = 0;
   while (x < ntile) {
     __syncthreads();
-    const int xn = next_tile(x + 1);
+    uint64_t el_next = ~0ull;
+    const int xn = next_tile(x + 1, el_next);
+    const TileMask mk = mask_issue(x, el);
     if (xn < ntile) tile_load(xn, kr, vr);
     // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
@@ -212,24 +252,7 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
       p0 = mfma32(v0, doB[c], p0);
       p1 = mfma32(v1, doB[c], p1);
     }
-    if constexpr (kBand) {
-      if (x < nband) {
-        const int u = lo_u + x;
-        const uint64_t vm = valid_rows(u, nc);
-        if (!tiles_in_window(a.win, t, u) || vm != ~0ull) {
-          const int j0 = u * kBlock;
-          const uint64_t ok = (bit_range(klo - j0, khi - j0) & vm) |
-                              class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane);
-          mask_rows(s0, s1, hl, ok);
-        }
-      } else {
-        const uint64_t el = global_outside(a.gtok, a.ng, x - nband, cls, stride, lo_u, hi_u, lane);
-        if (el != ~0ull) mask_rows(s0, s1, hl, el);
-      }
-    } else if (lo_u + x == a.nt - 1) {   // keys past the end of the sequence
-      const uint64_t vm = valid_rows(a.nt - 1, a.n);
-      if (vm != ~0ull) mask_rows(s0, s1, hl, vm);
-    }
+    if (mk.need) mask_rows(s0, s1, hl, mask_done(mk));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       // P = 2^(S*scale*log2(e) - lse*log2(e)), the scale applied in fp32;
@@ -259,6 +282,7 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     }
     cur ^= 1;
     x = xn;
+    el = el_next;
   }
 
   const float sc = a.scale;
@@ -384,11 +408,28 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
     ntile = hi - lo + 1;
   }
   const int nband = hi - lo + 1;
-  auto next_tile = [&](int x) -> int {
-    while (x < ntile && x >= nband &&
-           global_outside(a.gtok, a.ng, x - nband, cls, stride, lo, hi, lane) == 0ull)
-      ++x;
+  // The next tile at or after x, skipping global tiles with no eligible row; for a
+  // global tile, el receives its eligible rows.
+  auto next_tile = [&](int x, uint64_t& el) -> int {
+    for (; x < ntile; ++x) {
+      if (x < nband) return x;
+      el = global_outside(a.gtok, a.ng, x - nband, cls, stride, lo, hi, lane);
+      if (el != 0ull) return x;
+    }
     return x;
+  };
+  // The global rows of a plain item's band tile, read before the iteration's
+  // prefetch (see lf_band_item of the forward); a zero word when not needed.
+  auto plain_gbits_issue = [&](int x) -> ClassGBits {
+    ClassGBits g{0ull, -1};
+    if constexpr (kPlain) {
+      if (x < nband) {
+        const int tq = lo + x;
+        if (!tiles_in_window(a.win, tq, u) || valid_rows(tq, nc) != ~0ull || a.gproj)
+          g = class_gbits_issue(a.gidx, a.tile_gmask, a.ng, cls, stride, tq, nc, lane);
+      }
+    }
+    return g;
   };
   // Segment items test the dilated window in token coordinates: query rows whose
   // distance to the key is a multiple of the stride (bits 0, s, 2s, ... shifted).
@@ -399,25 +440,26 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   const uint16_t* dobase = a.dout + bh_off;
   const float* lbase = a.lse + (size_t)bh * a.n;
   const float* dbase = a.dbuf + (size_t)bh * a.n;
-  // tile loads plus the lse and D of row tid (tid < 64)
+  // the lse and D of row tid (tid < 64), then the tile loads (issued last, so that a
+  // wait for the small loads never has to wait for the tiles)
   auto tile_load = [&](int x, TileRegs& qr, TileRegs& dr, float& lv, float& dval) {
-    int tok_row;
-    if (x < nband) {
-      gload_class(qr, qbase, qc, qs, lo + x, qnc, tid);
-      gload_class(dr, dobase, qc, qs, lo + x, qnc, tid);
-      tok_row = class_token(qc, qs, lo + x, qnc, tid & 63);
-    } else {
-      gload_gather(qr, qbase, a.gtok, a.ng, x - nband, tid);
-      gload_gather(dr, dobase, a.gtok, a.ng, x - nband, tid);
-      tok_row = global_token(a.gtok, a.ng, x - nband, tid & 63);
-    }
+    const int tok_row = x < nband ? class_token(qc, qs, lo + x, qnc, tid & 63)
+                                  : global_token(a.gtok, a.ng, x - nband, tid & 63);
     if (tid < kBlock) {
       lv = lbase[tok_row];
       dval = dbase[tok_row];
     }
+    if (x < nband) {
+      gload_class(qr, qbase, qc, qs, lo + x, qnc, tid);
+      gload_class(dr, dobase, qc, qs, lo + x, qnc, tid);
+    } else {
+      gload_gather(qr, qbase, a.gtok, a.ng, x - nband, tid);
+      gload_gather(dr, dobase, a.gtok, a.ng, x - nband, tid);
+    }
   };
 
-  int x = next_tile(0);
+  uint64_t el = ~0ull;   // eligible rows of tile x when it is a global tile
+  int x = next_tile(0, el);
   TileRegs qr, dr;
   float lv = 0.f, dval = 0.f;
   if (x < ntile) tile_load(x, qr, dr, lv, dval);
@@ -443,7 +485,9 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   int cur = 0;
   while (x < ntile) {
     __syncthreads();
-    const int xn = next_tile(x + 1);
+    uint64_t el_next = ~0ull;
+    const int xn = next_tile(x + 1, el_next);
+    const ClassGBits gw = plain_gbits_issue(x);
     if (xn < ntile) tile_load(xn, qr, dr, lv, dval);
     // S[q][key] = Q K^T, dP[q][key] = dO V^T; rows = queries (2 tiles), column = key.
     // Row q of register r is 32*qt + 8*(r/4) + 4*hl + r%4.
@@ -482,7 +526,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
         const uint64_t vq = valid_rows(tq, nc);
         if (!tiles_in_window(a.win, tq, u) || vq != ~0ull || a.gproj) {
           const uint64_t win = bit_range(rlo - i0, rhi - i0) & vq;
-          const uint64_t gq = class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, tq, nc, lane);
+          const uint64_t gq = class_gbits_done(gw, a.ng, stride);
           const uint64_t ok = a.gproj ? win & ~gq : win | gq;
           if (ok != ~0ull) mask_rows(s0, s1, hl, ok);
         }
@@ -491,7 +535,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
         // cls + s*rlo .. cls + s*rhi at a multiple of s from it) or that are global;
         // every row for a global key; only rows before the end of the sequence
         const uint64_t vq = valid_rows(tq, a.n);
-        const uint64_t gq = a.tile_gmask[tq];
+        const uint64_t gq = load_uniform_u64(a.tile_gmask, tq);
         if (key_global) {
           const uint64_t ok = a.gproj ? vq & ~gq : vq;
           if (ok != ~0ull) mask_rows(s0, s1, hl, ok);
@@ -504,9 +548,8 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
           mask_rows(s0, s1, hl, ok);
         }
       }
-    } else {
-      const uint64_t el = global_outside(a.gtok, a.ng, x - nband, cls, stride, lo, hi, lane);
-      if (el != ~0ull) mask_rows(s0, s1, hl, el);
+    } else if (el != ~0ull) {
+      mask_rows(s0, s1, hl, el);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -553,6 +596,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
     }
     cur ^= 1;
     x = xn;
+    el = el_next;
   }
 
   const float sc = a.scale;

@@ -103,39 +103,69 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
     }
   };
 
-  // skip global tiles with no eligible key
-  auto next_tile = [&](int x) -> int {
-    while (x < ntile && x >= nband && global_elig(x - nband) == 0ull) ++x;
+  // The next tile at or after x, skipping global tiles with no eligible key; for a
+  // global tile, el receives its eligible keys.
+  auto next_tile = [&](int x, uint64_t& el) -> int {
+    for (; x < ntile; ++x) {
+      if (x < nband) return x;
+      el = global_elig(x - nband);
+      if (el != 0ull) return x;
+    }
     return x;
   };
+  // Keys of tile x this lane's row may attend to.  A band tile needs a mask where
+  // the window cuts it or the class ends inside it (keys that are global are
+  // allowed anywhere); a global tile has the eligible keys el of next_tile.
+  // mask_issue reads the tile's global-row word, mask_done (every lane) applies it.
+  struct TileMask {
+    bool need;           // uniform: the tile needs a mask
+    bool band;
+    uint64_t bits;       // band: window and class-end bits; global tile: el
+    ClassGBits g;        // band: the global rows of the tile
+  };
+  auto mask_issue = [&](int x, uint64_t el) -> TileMask {
+    TileMask m{false, x < nband, el, ClassGBits{0ull, -1}};
+    if (!m.band) {
+      m.need = el != ~0ull;
+      return m;
+    }
+    const int u = lo_u + x;
+    const uint64_t vm = valid_rows(u, nc);
+    m.need = !tiles_in_window(a.win, t, u) || vm != ~0ull;
+    if (m.need) {
+      const int j0 = u * kBlock;
+      m.bits = bit_range(klo - j0, khi - j0) & vm;
+      m.g = class_gbits_issue(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane);
+    }
+    return m;
+  };
+  auto mask_done = [&](const TileMask& m) -> uint64_t {
+    return m.band ? m.bits | class_gbits_done(m.g, a.ng, stride) : m.bits;
+  };
 
-  int x = next_tile(0);
+  uint64_t el = ~0ull;   // eligible keys of tile x when it is a global tile
+  int x = next_tile(0, el);
   TileRegs kr, vr;
   if (x < ntile) {
     tile_load(x, kr, vr);
     lds_store_nat(sK[0], kr, tid);
     lds_store_nat(sV[0], vr, tid);
   }
+  // Drain the prologue's loads (Q): a wait for them left inside the loop would, with
+  // the in-order load counter, also wait for each iteration's prefetch.  For the
+  // same reason an iteration reads its tile's mask word before it issues the
+  // prefetch, so that the wait for the word leaves the prefetch in flight.
+  wait_all_loads();
   int cur = 0;
   while (x < ntile) {
     __syncthreads();
-    const int xn = next_tile(x + 1);
+    uint64_t el_next = ~0ull;
+    const int xn = next_tile(x + 1, el_next);
+    const TileMask mk = mask_issue(x, el);
     if (xn < ntile) tile_load(xn, kr, vr);
     f32x16 s0, s1;
     qk_tile(sK[cur], qB, col, hl, s0, s1);
-    if (x < nband) {
-      const int u = lo_u + x;
-      const uint64_t vm = valid_rows(u, nc);
-      if (!tiles_in_window(a.win, t, u) || vm != ~0ull) {
-        const int j0 = u * kBlock;
-        const uint64_t ok = (bit_range(klo - j0, khi - j0) & vm) |
-                            class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, u, nc, lane);
-        mask_rows(s0, s1, hl, ok);
-      }
-    } else {
-      const uint64_t el = global_elig(x - nband);
-      if (el != ~0ull) mask_rows(s0, s1, hl, el);
-    }
+    if (mk.need) mask_rows(s0, s1, hl, mask_done(mk));
     bf16x8 pc[4];
     softmax_step(s0, s1, st, pc, a.sl2);
     pv_tile(sV[cur], pc, lane, st);
@@ -145,6 +175,7 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
     }
     cur ^= 1;
     x = xn;
+    el = el_next;
   }
 
   const float l_tot = partner_sum(st.l), lb_tot = partner_sum(st.lb);
@@ -180,6 +211,7 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
   gload_class(vr, a.vg + bh_off, 0, 1, u_begin, a.n, tid);
   lds_store_nat(sK[0], kr, tid);
   lds_store_nat(sV[0], vr, tid);
+  wait_all_loads();   // Q: see lf_band_item
   for (int u = u_begin; u < u_end; ++u) {
     const int cur = (u - u_begin) & 1;
     __syncthreads();

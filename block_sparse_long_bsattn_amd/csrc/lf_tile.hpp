@@ -63,14 +63,50 @@ __device__ __forceinline__ uint64_t valid_rows(int t, int nc) {
   return m >= kBlock ? ~0ull : (1ull << m) - 1;
 }
 
+// Word t of a read-only table, t the same in every lane, read as a scalar load
+// (constant address space): it counts against the scalar/LDS counter, so waiting
+// for it never waits for the vector loads in flight.
+__device__ __forceinline__ uint64_t load_uniform_u64(const uint64_t* table, int t) {
+  typedef const __attribute__((address_space(4))) uint64_t* ConstPtr;
+  return ((ConstPtr)table)[t];
+}
+
 // Rows of class tile t that are global tokens.  Every lane of the wave must call
 // it (a ballot, except for stride 1 where the natural tile mask is read).
 __device__ __forceinline__ uint64_t class_gbits(const int32_t* gidx, const uint64_t* tile_gmask,
                                                 int ng, int c, int s, int t, int nc, int lane) {
   if (ng == 0) return 0ull;
-  if (s == 1) return tile_gmask[t];
+  if (s == 1) return load_uniform_u64(tile_gmask, t);
   const int i = t * kBlock + lane;
   return __ballot(i < nc && gidx[c + s * i] >= 0);
+}
+
+// class_gbits in two steps, for a loop that loads the word one iteration before it
+// uses it: issue reads the per-lane data, done (called by every lane of the wave)
+// turns it into the row bits.
+struct ClassGBits {
+  uint64_t w;   // stride 1: the tile's bit word
+  int g;        // larger strides: this lane's row's index among the global tokens, or -1
+};
+
+__device__ __forceinline__ ClassGBits class_gbits_issue(const int32_t* gidx,
+                                                        const uint64_t* tile_gmask, int ng,
+                                                        int c, int s, int t, int nc, int lane) {
+  ClassGBits r{0ull, -1};
+  if (ng == 0) return r;
+  if (s == 1) {
+    r.w = load_uniform_u64(tile_gmask, t);
+  } else {
+    const int i = t * kBlock + lane;
+    if (i < nc) r.g = gidx[c + s * i];
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint64_t class_gbits_done(const ClassGBits& r, int ng, int s) {
+  if (ng == 0) return 0ull;
+  if (s == 1) return r.w;
+  return __ballot(r.g >= 0);
 }
 
 // Which rows of global tile gt are global tokens that no tile of [lo, hi] in class
