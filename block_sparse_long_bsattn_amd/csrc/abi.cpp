@@ -668,9 +668,9 @@ int lfattn_plan_destroy(lfattn_plan* P) {
 }
 
 size_t lfattn_fwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
-  if (P == nullptr || batch < 1 || heads < 1 || d != kHead) return 0;
+  if (P == nullptr || batch < 1 || heads < 1 || (d != kHead && d != 128)) return 0;
   if (P->heads > 0 && heads != P->heads) return 0;
-  return lf_workspace_bytes(P, batch, heads);
+  return lf_workspace_bytes(P, batch, heads, d);
 }
 
 }  // extern "C"
@@ -688,17 +688,17 @@ int lf_fwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int
   int st = check_plan_heads(P, heads, who);
   if (st) return st;
   if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, w + ": only bf16 is built");
-  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o}, who))) return st;
-  if (qg != nullptr && (st = check_tensor_args(batch, d, scale, {qg, kg, vg}, who))) return st;
+  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o}, who, 128))) return st;
+  if (qg != nullptr && (st = check_tensor_args(batch, d, scale, {qg, kg, vg}, who, 128))) return st;
   if (lse != nullptr && !aligned16(lse)) return set_error(BSATTN_EINVAL, w + ": lse not 16-byte aligned");
   if ((st = check_o_lo(o_lo, dt, who))) return st;
-  if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
+  if ((int64_t)batch * heads * P->n * d >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, w + ": tensor too large");
-  const size_t need = lf_workspace_bytes(P, batch, heads);
+  const size_t need = lf_workspace_bytes(P, batch, heads, d);
   if ((st = check_workspace(workspace, ws_bytes, need, who))) return st;
   if ((st = check_device(P->device))) return st;
   DebugCall dbg(who, stream, workspace, ws_bytes, need);
-  return dbg.finish(launch_lf_fwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, lse, o_lo,
+  return dbg.finish(launch_lf_fwd(P, batch, heads, d, scale, q, k, v, qg, kg, vg, o, lse, o_lo,
                                   workspace, stream));
 }
 

@@ -134,7 +134,7 @@ int launch_bwd(const bsattn_layout* L, int batch, int d, float scale, const void
                const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
                hipStream_t stream);
 // qg, kg, vg (and dqg, dkg, dvg) may be null: one projection set for every row.
-int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
+int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, int d, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,
                   const void* vg, void* o, float* lse, void* o_lo, void* ws,
                   hipStream_t stream);
@@ -142,7 +142,7 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const
 size_t fwd_workspace_bytes(const bsattn_layout* L, int batch, int d);   // either dtype
 size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt, int d);
 size_t bwd_workspace_bytes(const bsattn_layout* L, int batch, int d);
-size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads);
+size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads, int d);
 int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,
                   const void* vg, const void* o, const void* o_lo, const float* lse,

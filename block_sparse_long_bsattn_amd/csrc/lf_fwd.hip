@@ -1,4 +1,6 @@
 // Longformer sliding-window + symmetric global attention forward on gfx950.
+// Head dimension d = 64 (every configuration on the pages) or 128: one template,
+// the d-wide loops unrolled per instance.
 //
 // Pattern ("Longformer: The Long-Document Transformer", §3.1 "Sliding Window",
 // "Dilated Sliding Window" and "Global Attention"; the autoregressive mode of
@@ -55,9 +57,12 @@ struct LfArgs {
   float sl2;
 };
 
-typedef uint16_t LdsTile[kBlock * kLdsStride];
+template <int D>
+using LdsTileT = uint16_t[kBlock * kStrideOf<D>];
 
-__device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK, LdsTile* sV) {
+template <int D>
+__device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTileT<D>* sK,
+                                             LdsTileT<D>* sV) {
   const int per = v / a.nct;
   const LfTileRef e = a.ct[v - per * a.nct];
   const int bh = per * a.ph + e.h;
@@ -67,16 +72,16 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
   const uint64_t vm_q = valid_rows(t, nc);
   const uint64_t gm_q = class_gbits(a.gidx, a.tile_gmask, a.ng, cls, stride, t, nc, lane);
   if (gm_q == vm_q) return;   // every row global: the global items own them
-  const size_t bh_off = (size_t)bh * a.n * kHead;
+  const size_t bh_off = (size_t)bh * a.n * D;
   const int xq = 32 * wave + col;
   const int i = min(t * kBlock + xq, nc - 1);   // this lane's class index
   const int p = cls + stride * i;               // ... and its token
 
-  bf16x8 qB[4];
+  bf16x8 qB[D / 16];
   {
-    const uint16_t* qp = a.q + bh_off + (size_t)p * kHead + 8 * hl;
+    const uint16_t* qp = a.q + bh_off + (size_t)p * D + 8 * hl;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) qB[k] = ld16(qp + 16 * k);
+    for (int k = 0; k < D / 16; ++k) qB[k] = ld16(qp + 16 * k);
   }
   const int ntc = (nc + kBlock - 1) / kBlock;
   int lo_u, hi_u;
@@ -91,9 +96,9 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
     return global_outside(a.gtok, a.ng, gt, cls, stride, lo_u, hi_u, lane);
   };
 
-  FwdState st;
+  FwdStateT<D> st;
   fwd_state_init(st);
-  auto tile_load = [&](int x, TileRegs& kr, TileRegs& vr) {
+  auto tile_load = [&](int x, TileRegsT<D>& kr, TileRegsT<D>& vr) {
     if (x < nband) {
       gload_class(kr, a.k + bh_off, cls, stride, lo_u + x, nc, tid);
       gload_class(vr, a.v + bh_off, cls, stride, lo_u + x, nc, tid);
@@ -145,7 +150,7 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
 
   uint64_t el = ~0ull;   // eligible keys of tile x when it is a global tile
   int x = next_tile(0, el);
-  TileRegs kr, vr;
+  TileRegsT<D> kr, vr;
   if (x < ntile) {
     tile_load(x, kr, vr);
     lds_store_nat(sK[0], kr, tid);
@@ -180,33 +185,35 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTile* sK
 
   const float l_tot = partner_sum(st.l), lb_tot = partner_sum(st.lb);
   if (((vm_q & ~gm_q) >> xq) & 1ull)
-    write_o_bf16(st, l_tot, lb_tot, hl, a.o + bh_off + (size_t)p * kHead,
-                 a.o_lo != nullptr ? a.o_lo + bh_off + (size_t)p * kHead : nullptr,
+    write_o_bf16(st, l_tot, lb_tot, hl, a.o + bh_off + (size_t)p * D,
+                 a.o_lo != nullptr ? a.o_lo + bh_off + (size_t)p * D : nullptr,
                  a.lse != nullptr ? a.lse + (size_t)bh * a.n + p : nullptr);
 }
 
 // Item v of the global rows: (bh, global tile gt, segment s of kLfSeg key tiles).
-__device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* sK, LdsTile* sV) {
+template <int D>
+__device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTileT<D>* sK,
+                                               LdsTileT<D>* sV) {
   const int per_bh = a.ngt * a.nseg;
   const int bh = v / per_bh;
   const int rem = v - bh * per_bh;
   const int gt = rem / a.nseg, s = rem - gt * a.nseg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const size_t bh_off = (size_t)bh * a.n * kHead;
+  const size_t bh_off = (size_t)bh * a.n * D;
   const int qr = 32 * wave + col;
 
-  bf16x8 qB[4];
+  bf16x8 qB[D / 16];
   {
-    const uint16_t* qp = a.qg + bh_off + (size_t)global_token(a.gtok, a.ng, gt, qr) * kHead + 8 * hl;
+    const uint16_t* qp = a.qg + bh_off + (size_t)global_token(a.gtok, a.ng, gt, qr) * D + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qB[c] = ld16(qp + 16 * c);
+    for (int c = 0; c < D / 16; ++c) qB[c] = ld16(qp + 16 * c);
   }
   const int u_begin = s * kLfSeg;
   const int u_end = min(a.nt, u_begin + kLfSeg);
-  FwdState st;
+  FwdStateT<D> st;
   fwd_state_init(st);
-  TileRegs kr, vr;
+  TileRegsT<D> kr, vr;
   gload_class(kr, a.kg + bh_off, 0, 1, u_begin, a.n, tid);
   gload_class(vr, a.vg + bh_off, 0, 1, u_begin, a.n, tid);
   lds_store_nat(sK[0], kr, tid);
@@ -235,21 +242,25 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTile* 
     }
   }
   const float l_tot = partner_sum(st.l), lb_tot = partner_sum(st.lb);
-  write_partial(st, l_tot, lb_tot, hl, qr, a.part + (size_t)v * kPartFloats);
+  write_partial(st, l_tot, lb_tot, hl, qr, a.part + (size_t)v * kPartFloatsOf<D>);
 }
 
 // Band items first, then the global-row segments (about as long as a band item).
-__global__ __launch_bounds__(kThreads, 2) void lf_attn_kernel(LfArgs a) {
-  __shared__ __attribute__((aligned(16))) LdsTile sK[2];
-  __shared__ __attribute__((aligned(16))) LdsTile sV[2];
+// D = 128 takes more than half the registers: one wave per SIMD.
+template <int D>
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void lf_attn_kernel(LfArgs a) {
+  __shared__ __attribute__((aligned(16))) LdsTileT<D> sK[2];
+  __shared__ __attribute__((aligned(16))) LdsTileT<D> sV[2];
   const int v = xcd_remap(blockIdx.x, a.total_items);
   if (v >= a.total_items) return;
   if (v < a.band_items)
-    lf_band_item(a, v, sK, sV);
+    lf_band_item<D>(a, v, sK, sV);
   else
-    lf_global_item(a, v - a.band_items, sK, sV);
+    lf_global_item<D>(a, v - a.band_items, sK, sV);
 }
 
+// Thread t: global row t / 4 of the tile, columns 16 (t % 4) + 64 u .. +15.
+template <int D>
 __global__ __launch_bounds__(256) void lf_combine_kernel(LfArgs a) {
   const int idx = blockIdx.x;   // bh * ngt + gt
   const int bh = idx / a.ngt, gt = idx - bh * a.ngt;
@@ -257,22 +268,28 @@ __global__ __launch_bounds__(256) void lf_combine_kernel(LfArgs a) {
   const int j = gt * kBlock + row;
   if (j >= a.ng) return;
   const int tok = a.gtok[j];   // read alongside the partial records
-  float acc[16], M, L, Lb;
-  merge_partials(a.part + (size_t)idx * a.nseg * kPartFloats, a.nseg, row, dq, acc, M, L, Lb);
-  const size_t off = ((size_t)bh * a.n + tok) * kHead + dq;
-  store16_bf16_lo(a.o + off, a.o_lo != nullptr ? a.o_lo + off : nullptr, acc, 1.f / Lb);
+  float M = 0.f, L = 0.f;
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) {
+    float acc[16], Lb;
+    merge_partials<D>(a.part + (size_t)idx * a.nseg * kPartFloatsOf<D>, a.nseg, row, dq + 64 * u,
+                      acc, M, L, Lb);
+    const size_t off = ((size_t)bh * a.n + tok) * D + dq + 64 * u;
+    store16_bf16_lo(a.o + off, a.o_lo != nullptr ? a.o_lo + off : nullptr, acc, 1.f / Lb);
+  }
   if (a.lse != nullptr && (threadIdx.x & 3) == 0)
     a.lse[(size_t)bh * a.n + tok] = (M + __log2f(L)) * kLn2;
 }
 
 }  // namespace
 
-size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads) {
+size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads, int d) {
   if (P->ng == 0) return 0;
-  return (size_t)batch * heads * P->ngt * P->nseg * kPartFloats * sizeof(float);
+  const size_t rec = d == 128 ? kPartFloatsOf<128> : kPartFloatsOf<kHead>;
+  return (size_t)batch * heads * P->ngt * P->nseg * rec * sizeof(float);
 }
 
-int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
+int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, int d, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,
                   const void* vg, void* o, float* lse, void* o_lo, void* ws,
                   hipStream_t stream) {
@@ -297,15 +314,21 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, float scale, const
   a.total_items = a.band_items + (has_g ? bhn * P->ngt * P->nseg : 0);
   int st;
   {
-    ProfScope prof_("lf_attn", stream);
-    hipLaunchKernelGGL(lf_attn_kernel, dim3(8 * ((a.total_items + 7) / 8)), dim3(kThreads), 0,
-                       stream, a);
+    ProfScope prof_(d == 128 ? "lf_attn_d128" : "lf_attn", stream);
+    const dim3 grid(8 * ((a.total_items + 7) / 8));
+    if (d == 128)
+      hipLaunchKernelGGL(lf_attn_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(lf_attn_kernel<kHead>, grid, dim3(kThreads), 0, stream, a);
   }
   if ((st = check_hip(hipGetLastError(), "lf_attn launch"))) return st;
   if (!has_g) return 0;
   {
     ProfScope prof_("lf_combine", stream);
-    hipLaunchKernelGGL(lf_combine_kernel, dim3(bhn * P->ngt), dim3(256), 0, stream, a);
+    if (d == 128)
+      hipLaunchKernelGGL(lf_combine_kernel<128>, dim3(bhn * P->ngt), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(lf_combine_kernel<kHead>, dim3(bhn * P->ngt), dim3(256), 0, stream, a);
   }
   return check_hip(hipGetLastError(), "lf_combine launch");
 }

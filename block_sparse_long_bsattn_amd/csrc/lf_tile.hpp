@@ -11,8 +11,8 @@
 // Sequences need not fill their last 64-token tile: rows past the end are clamped
 // on load and masked or skipped.
 //
-// Tiles whose rows are global tokens are gathered by index from the [n][64]
-// tensors.
+// Tiles whose rows are global tokens are gathered by index from the [n][d]
+// tensors (d = 64, or 128 for the instances that take it).
 #pragma once
 
 #include "common.hpp"
@@ -26,13 +26,15 @@ __device__ __forceinline__ int global_token(const int32_t* gtok, int ng, int gt,
   return gtok[min(gt * kBlock + x, ng - 1)];
 }
 
-// gload_nat for a tile of global tokens, rows gathered from `base` ([n][64]).
-__device__ __forceinline__ void gload_gather(TileRegs& r, const uint16_t* base,
+// gload_nat for a tile of global tokens, rows gathered from `base` ([n][D]).
+template <int D>
+__device__ __forceinline__ void gload_gather(TileRegsT<D>& r, const uint16_t* base,
                                              const int32_t* gtok, int ng, int gt, int tid) {
-  const int c = tid & 7, row = tid >> 3;
+  constexpr int kCpr = D / 8, kRpp = 128 / kCpr, kShift = D == 64 ? 3 : 4;
+  const int c = tid & (kCpr - 1), row = tid >> kShift;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    r.v[u] = ldg16(base + (size_t)global_token(gtok, ng, gt, row + 16 * u) * kHead + 8 * c);
+  for (int u = 0; u < D / 16; ++u)
+    r.v[u] = ldg16(base + (size_t)global_token(gtok, ng, gt, row + kRpp * u) * D + 8 * c);
 }
 
 // Token of row x of class tile t; rows past the class repeat its last token.
@@ -40,13 +42,15 @@ __device__ __forceinline__ int class_token(int c, int s, int t, int nc, int x) {
   return c + s * min(t * kBlock + x, nc - 1);
 }
 
-// gload_nat for class tile t: row x from token c + s*(64t + x) of `base` ([n][64]).
-__device__ __forceinline__ void gload_class(TileRegs& r, const uint16_t* base, int c, int s,
+// gload_nat for class tile t: row x from token c + s*(64t + x) of `base` ([n][D]).
+template <int D>
+__device__ __forceinline__ void gload_class(TileRegsT<D>& r, const uint16_t* base, int c, int s,
                                             int t, int nc, int tid) {
-  const int k = tid & 7, row = tid >> 3;
+  constexpr int kCpr = D / 8, kRpp = 128 / kCpr, kShift = D == 64 ? 3 : 4;
+  const int k = tid & (kCpr - 1), row = tid >> kShift;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    r.v[u] = ldg16(base + (size_t)class_token(c, s, t, nc, row + 16 * u) * kHead + 8 * k);
+  for (int u = 0; u < D / 16; ++u)
+    r.v[u] = ldg16(base + (size_t)class_token(c, s, t, nc, row + kRpp * u) * D + 8 * k);
 }
 
 // Bits [lo, hi] of a 64-bit word, clipped to [0, 63]; empty when hi < lo.

@@ -287,14 +287,15 @@ int lfattn_plan_build_dilated(int n, int window_one_side, const int32_t* global_
  * hipFree).  NULL is accepted. */
 int lfattn_plan_destroy(lfattn_plan* plan);
 
-/* Workspace bytes lfattn_fwd needs.  d must be 64.  0 for invalid arguments. */
+/* Workspace bytes lfattn_fwd needs (d = 64 or 128).  0 for invalid arguments. */
 size_t lfattn_fwd_workspace(const lfattn_plan* plan, int batch, int heads, int d);
 
 /*
  * Longformer forward: O, lse and o_lo as in bsattn_fwd, with the plan's token
  * pattern.  Query rows of global tokens are full rows.  q, k, v, o are DEVICE
  * [batch, heads, n, d]; lse DEVICE float32 [batch, heads, n] or NULL; o_lo DEVICE
- * bf16 [batch, heads, n, d] or NULL.  dt must be BSATTN_BF16.
+ * bf16 [batch, heads, n, d] or NULL.  dt must be BSATTN_BF16.  d = 64 (every
+ * configuration of [LF] and of the BigBird-ETC tables in [BB] App. E) or 128.
  * Returns OK, EINVAL, EUNSUPPORTED or EHIP.
  */
 int lfattn_fwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,

@@ -117,7 +117,7 @@ int launch_layout_build(bsattn_layout*, hipStream_t) { return BSATTN_OK; }
 size_t fwd_workspace_bytes(const bsattn_layout*, int, int) { return kFakeFwd; }
 size_t fwd_workspace_bytes_dt(const bsattn_layout*, int, bsattn_dtype, int) { return kFakeFwd; }
 size_t bwd_workspace_bytes(const bsattn_layout*, int, int) { return kFakeBwd; }
-size_t lf_workspace_bytes(const lfattn_plan*, int, int) { return kFakeFwd; }
+size_t lf_workspace_bytes(const lfattn_plan*, int, int, int) { return kFakeFwd; }
 size_t lf_bwd_workspace_bytes(const lfattn_plan*, int, int) { return kFakeBwd; }
 
 int launch_fwd(const bsattn_layout*, int, bsattn_dtype, int, float, const void*, const void*,
@@ -134,7 +134,7 @@ int launch_bwd(const bsattn_layout*, int, int, float, const void*, const void*, 
   return BSATTN_OK;
 }
 
-int launch_lf_fwd(const lfattn_plan*, int, int, float, const void*, const void*, const void*,
+int launch_lf_fwd(const lfattn_plan*, int, int, int, float, const void*, const void*, const void*,
                   const void*, const void*, const void*, void*, float*, void*, void*,
                   hipStream_t) {
   return BSATTN_OK;
