@@ -726,9 +726,9 @@ int lfattn_fwd_gproj(const lfattn_plan* P, int batch, int heads, int d, bsattn_d
 }
 
 size_t lfattn_bwd_workspace(const lfattn_plan* P, int batch, int heads, int d) {
-  if (P == nullptr || batch < 1 || heads < 1 || d != kHead) return 0;
+  if (P == nullptr || batch < 1 || heads < 1 || (d != kHead && d != 128)) return 0;
   if (P->heads > 0 && heads != P->heads) return 0;
-  return lf_bwd_workspace_bytes(P, batch, heads);
+  return lf_bwd_workspace_bytes(P, batch, heads, d);
 }
 
 }  // extern "C"
@@ -747,24 +747,25 @@ int lf_bwd_impl(const char* who, const lfattn_plan* P, int batch, int heads, int
   int st = check_plan_heads(P, heads, who);
   if (st) return st;
   if (dt != BSATTN_BF16) return set_error(BSATTN_EUNSUPPORTED, w + ": only bf16 is built");
-  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, who)))
+  if ((st = check_tensor_args(batch, d, scale, {q, k, v, o, lse, dout, dq, dk, dv}, who, 128)))
     return st;
   if ((st = check_o_lo(o_lo, dt, who))) return st;
   if (qg != nullptr) {
-    if ((st = check_tensor_args(batch, d, scale, {qg, kg, vg, dqg, dkg, dvg}, who))) return st;
+    if ((st = check_tensor_args(batch, d, scale, {qg, kg, vg, dqg, dkg, dvg}, who, 128)))
+      return st;
     const void* outs[6] = {dq, dk, dv, dqg, dkg, dvg};
     for (int x = 0; x < 6; ++x)
       for (int y = x + 1; y < 6; ++y)
         if (outs[x] == outs[y]) return set_error(BSATTN_EINVAL, w + ": output gradients alias");
   }
-  if ((int64_t)batch * heads * P->n * kHead >= ((int64_t)1 << 40))
+  if ((int64_t)batch * heads * P->n * d >= ((int64_t)1 << 40))
     return set_error(BSATTN_EUNSUPPORTED, w + ": tensor too large");
-  const size_t need = lf_bwd_workspace_bytes(P, batch, heads);
+  const size_t need = lf_bwd_workspace_bytes(P, batch, heads, d);
   if ((st = check_workspace(workspace, ws_bytes, need, who))) return st;
   if ((st = check_device(P->device))) return st;
   DebugCall dbg(who, stream, workspace, ws_bytes, need);
-  return dbg.finish(launch_lf_bwd(P, batch, heads, scale, q, k, v, qg, kg, vg, o, o_lo, lse, dout,
-                                  dq, dk, dv, dqg, dkg, dvg, workspace, stream));
+  return dbg.finish(launch_lf_bwd(P, batch, heads, d, scale, q, k, v, qg, kg, vg, o, o_lo, lse,
+                                  dout, dq, dk, dv, dqg, dkg, dvg, workspace, stream));
 }
 
 }  // namespace

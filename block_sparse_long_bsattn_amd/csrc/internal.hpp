@@ -143,12 +143,12 @@ size_t fwd_workspace_bytes(const bsattn_layout* L, int batch, int d);   // eithe
 size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt, int d);
 size_t bwd_workspace_bytes(const bsattn_layout* L, int batch, int d);
 size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads, int d);
-int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
+int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, int d, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,
                   const void* vg, const void* o, const void* o_lo, const float* lse,
                   const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg,
                   void* dvg, void* ws, hipStream_t stream);
-size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads);
+size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads, int d);
 
 // The static device scratch of bsattn_bwd_noalloc: its address on the current
 // device (looked up once per device) and its size.

@@ -38,7 +38,8 @@ namespace bsattn {
 namespace {
 
 constexpr int kThreads = 128;
-constexpr int kTile = kBlock * kHead;
+template <int D>
+constexpr int kTileOf = kBlock * D;   // floats of one fp32 partial tile
 
 struct LfBwdArgs {
   const uint16_t* q;
@@ -61,8 +62,8 @@ struct LfBwdArgs {
   uint16_t* dvg;
   int gproj;
   float* dbuf;       // D [B*H*n]
-  float* part_q;     // [B*H*ngt*nseg][64][64] dQ of the global query rows
-  float* part_kv;    // [periods*nct_g*nseg][2][64][64] dK, dV of key class tiles
+  float* part_q;     // [B*H*ngt*nseg][64][d] dQ of the global query rows
+  float* part_kv;    // [periods*nct_g*nseg][2][64][d] dK, dV of key class tiles
                      // holding global keys
   const int32_t* gtok;         // [ng]
   const int32_t* gidx;         // [n]
@@ -82,13 +83,15 @@ struct LfBwdArgs {
 // dQ (and D)
 // ---------------------------------------------------------------------------
 
-typedef uint16_t LdsTile[kBlock * kLdsStride];
+template <int D>
+using LdsTileT = uint16_t[kBlock * kStrideOf<D>];
 
 // One dQ item; kBand: a 64-row query class tile (v indexes periods*nct), else a
-// segment of a global query tile (v indexes B*H*ngt*nseg).
-template <bool kBand>
-__device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTile* sK,
-                                               LdsTile* sV) {
+// segment of a global query tile (v indexes B*H*ngt*nseg).  D: head dimension.
+template <int D, bool kBand>
+__device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTileT<D>* sK,
+                                               LdsTileT<D>* sV) {
+  constexpr int kS = kStrideOf<D>, kC = D / 16, kT = D / 32;
   constexpr bool band = kBand;
   int bh, gt = 0, seg = 0;
   int cls = 0, stride = 1, t = 0, nc = a.n;   // class tile of a band item
@@ -110,7 +113,7 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     seg = rem - gt * a.nseg;
   }
   const int hl = lane >> 5, col = lane & 31;
-  const size_t bh_off = (size_t)bh * a.n * kHead;
+  const size_t bh_off = (size_t)bh * a.n * D;
   const int xq = 32 * wave + col;
   // this lane's class index (band items) and query token
   const int i = band ? min(t * kBlock + xq, nc - 1) : 0;
@@ -176,7 +179,7 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
   };
   const uint16_t* kbase = (band ? a.k : a.kg) + bh_off;
   const uint16_t* vbase = (band ? a.v : a.vg) + bh_off;
-  auto tile_load = [&](int x, TileRegs& kr, TileRegs& vr) {
+  auto tile_load = [&](int x, TileRegsT<D>& kr, TileRegsT<D>& vr) {
     if (x < nband) {
       gload_class(kr, kbase, cls, stride, lo_u + x, nc, tid);
       gload_class(vr, vbase, cls, stride, lo_u + x, nc, tid);
@@ -188,14 +191,14 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
 
   uint64_t el = ~0ull;   // eligible keys of tile x when it is a global tile
   int x = next_tile(0, el);
-  TileRegs kr, vr;
+  TileRegsT<D> kr, vr;
   if (x < ntile) tile_load(x, kr, vr);
-  bf16x8 qB[4], doB[4];
+  bf16x8 qB[kC], doB[kC];
   float dsum = 0.f;
   {
-    const size_t off = bh_off + (size_t)p * kHead + 8 * hl;
+    const size_t off = bh_off + (size_t)p * D + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kC; ++c) {
       const u32x4 qv = ldg16((band ? a.q : a.qg) + off + 16 * c);
       const u32x4 dv = ldg16(a.dout + off + 16 * c);
       const u32x4 ov = ldg16(a.o + off + 16 * c);
@@ -230,7 +233,9 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
   }
   wait_all_loads();
 
-  f32x16 g0 = zero16(), g1 = zero16();   // dQ^T, d rows 0..31 and 32..63
+  f32x16 g[kT];   // dQ^T: g[t] holds d rows 32t..32t+31
+#pragma unroll
+  for (int t = 0; t < kT; ++t) g[t] = zero16();
   float ds_sum = 0.f;   // this half-lane's share of the row sum of dS (masked keys: 0)
   int cur = 0;
   while (x < ntile) {
@@ -242,11 +247,11 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     // S^T = K Q^T and dP^T = V dO^T  (rows = keys, columns = this lane's query)
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bf16x8 k0 = ld16(sK[cur] + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 k1 = ld16(sK[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 v0 = ld16(sV[cur] + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 v1 = ld16(sV[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+    for (int c = 0; c < kC; ++c) {
+      const bf16x8 k0 = ld16(sK[cur] + col * kS + 16 * c + 8 * hl);
+      const bf16x8 k1 = ld16(sK[cur] + (32 + col) * kS + 16 * c + 8 * hl);
+      const bf16x8 v0 = ld16(sV[cur] + col * kS + 16 * c + 8 * hl);
+      const bf16x8 v1 = ld16(sV[cur] + (32 + col) * kS + 16 * c + 8 * hl);
       s0 = mfma32(k0, qB[c], s0);
       s1 = mfma32(k1, qB[c], s1);
       p0 = mfma32(v0, doB[c], p0);
@@ -272,10 +277,9 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]; K^T from transpose reads
     const bf16x8 dc[4] = {pack8(s0, 0), pack8(s0, 8), pack8(s1, 0), pack8(s1, 8)};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      g0 = mfma32(ld_tr8(sK[cur], 0, c, lane), dc[c], g0);
-      g1 = mfma32(ld_tr8(sK[cur], 1, c, lane), dc[c], g1);
-    }
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < kT; ++t) g[t] = mfma32(ld_tr8<D>(sK[cur], t, c, lane), dc[c], g[t]);
     if (xn < ntile) {
       lds_store_nat(sK[cur ^ 1], kr, tid);
       lds_store_nat(sV[cur ^ 1], vr, tid);
@@ -290,50 +294,54 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     const float dfix = Dq + partner_sum(ds_sum);
     if (((vm_q & ~gm_q) >> xq) & 1ull) {   // rows of global tokens: global items
       if (hl == 0) a.dbuf[(size_t)bh * a.n + p] = dfix;
-      uint16_t* op = a.dq + bh_off + (size_t)p * kHead + 4 * hl;
+      uint16_t* op = a.dq + bh_off + (size_t)p * D + 4 * hl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u32x2 w0, w1;
-        w0[0] = pack_bf16x2(g0[4 * j] * sc, g0[4 * j + 1] * sc);
-        w0[1] = pack_bf16x2(g0[4 * j + 2] * sc, g0[4 * j + 3] * sc);
-        w1[0] = pack_bf16x2(g1[4 * j] * sc, g1[4 * j + 1] * sc);
-        w1[1] = pack_bf16x2(g1[4 * j + 2] * sc, g1[4 * j + 3] * sc);
-        *reinterpret_cast<u32x2*>(op + 8 * j) = w0;
-        *reinterpret_cast<u32x2*>(op + 32 + 8 * j) = w1;
+        u32x2 w[kT];
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+          w[t][0] = pack_bf16x2(g[t][4 * j] * sc, g[t][4 * j + 1] * sc);
+          w[t][1] = pack_bf16x2(g[t][4 * j + 2] * sc, g[t][4 * j + 3] * sc);
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t) *reinterpret_cast<u32x2*>(op + 32 * t + 8 * j) = w[t];
       }
       if (a.gproj) {   // the global projections get nothing from this row
-        uint16_t* zp = a.dqg + bh_off + (size_t)p * kHead + 4 * hl;
+        uint16_t* zp = a.dqg + bh_off + (size_t)p * D + 4 * hl;
         const u32x2 z = {0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          *reinterpret_cast<u32x2*>(zp + 8 * j) = z;
-          *reinterpret_cast<u32x2*>(zp + 32 + 8 * j) = z;
-        }
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int t = 0; t < kT; ++t) *reinterpret_cast<u32x2*>(zp + 32 * t + 8 * j) = z;
       }
     }
   } else {
     const size_t slot = ((size_t)bh * a.ngt + gt) * a.nseg + seg;
-    float* pp = a.part_q + slot * kTile + xq * kHead + 4 * hl;
+    float* pp = a.part_q + slot * kTileOf<D> + xq * D + 4 * hl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f32x4 w0, w1;
+      f32x4 w[kT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { w0[e] = g0[4 * j + e] * sc; w1[e] = g1[4 * j + e] * sc; }
-      *reinterpret_cast<f32x4*>(pp + 8 * j) = w0;
-      *reinterpret_cast<f32x4*>(pp + 32 + 8 * j) = w1;
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int t = 0; t < kT; ++t) w[t][e] = g[t][4 * j + e] * sc;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<f32x4*>(pp + 32 * t + 8 * j) = w[t];
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void lf_bwd_dq_kernel(LfBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) LdsTile sK[2];
-  __shared__ __attribute__((aligned(16))) LdsTile sV[2];
+// D = 128 takes more than half the registers: one wave per SIMD.
+template <int D>
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void lf_bwd_dq_kernel(LfBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) LdsTileT<D> sK[2];
+  __shared__ __attribute__((aligned(16))) LdsTileT<D> sV[2];
   const int v = xcd_remap(blockIdx.x, a.dq_items);
   if (v >= a.dq_items) return;
   if (v < a.dq_band_items)
-    lf_bwd_dq_item<true>(a, v, sK, sV);
+    lf_bwd_dq_item<D, true>(a, v, sK, sV);
   else
-    lf_bwd_dq_item<false>(a, v - a.dq_band_items, sK, sV);
+    lf_bwd_dq_item<D, false>(a, v - a.dq_band_items, sK, sV);
 }
 
 // ---------------------------------------------------------------------------
@@ -348,10 +356,11 @@ enum LfKvKind {
                   // global query rows only, giving dK_g, dV_g (v indexes B*H*nt)
 };
 
-template <int kKind>
-__device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsTile* sQ,
-                                                 LdsTile* sO, float (*sL)[kBlock],
+template <int D, int kKind>
+__device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsTileT<D>* sQ,
+                                                 LdsTileT<D>* sO, float (*sL)[kBlock],
                                                  float (*sD)[kBlock]) {
+  constexpr int kS = kStrideOf<D>, kC = D / 16, kT = D / 32;
   constexpr bool kPlain = kKind == kKvPlain;
   constexpr bool kGRows = kKind == kKvGRows;
   int per = 0, gki = 0, seg = 0, bh, cls = 0, stride = 1, u, nc = a.n;
@@ -376,7 +385,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const size_t bh_off = (size_t)bh * a.n * kHead;
+  const size_t bh_off = (size_t)bh * a.n * D;
   const int kx = 32 * wave + col;                 // this lane's key within the tile
   const int jc = min(u * kBlock + kx, nc - 1);    // ... its class index
   const int q_tok = cls + stride * jc;            // ... and its token
@@ -442,7 +451,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   const float* dbase = a.dbuf + (size_t)bh * a.n;
   // the lse and D of row tid (tid < 64), then the tile loads (issued last, so that a
   // wait for the small loads never has to wait for the tiles)
-  auto tile_load = [&](int x, TileRegs& qr, TileRegs& dr, float& lv, float& dval) {
+  auto tile_load = [&](int x, TileRegsT<D>& qr, TileRegsT<D>& dr, float& lv, float& dval) {
     const int tok_row = x < nband ? class_token(qc, qs, lo + x, qnc, tid & 63)
                                   : global_token(a.gtok, a.ng, x - nband, tid & 63);
     if (tid < kBlock) {
@@ -460,14 +469,14 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
 
   uint64_t el = ~0ull;   // eligible rows of tile x when it is a global tile
   int x = next_tile(0, el);
-  TileRegs qr, dr;
+  TileRegsT<D> qr, dr;
   float lv = 0.f, dval = 0.f;
   if (x < ntile) tile_load(x, qr, dr, lv, dval);
-  bf16x8 kB[4], vB[4];
+  bf16x8 kB[kC], vB[kC];
   {
-    const size_t off = bh_off + (size_t)q_tok * kHead + 8 * hl;
+    const size_t off = bh_off + (size_t)q_tok * D + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kC; ++c) {
       kB[c] = ld16((kGRows ? a.kg : a.k) + off + 16 * c);
       vB[c] = ld16((kGRows ? a.vg : a.v) + off + 16 * c);
     }
@@ -481,7 +490,12 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   }
   wait_all_loads();
 
-  f32x16 dv0 = zero16(), dv1 = zero16(), dk0 = zero16(), dk1 = zero16();
+  f32x16 dv[kT], dk[kT];   // dV^T, dK^T: tile t holds d rows 32t..32t+31
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    dv[t] = zero16();
+    dk[t] = zero16();
+  }
   int cur = 0;
   while (x < ntile) {
     __syncthreads();
@@ -507,11 +521,11 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
       }
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bf16x8 q0 = ld16(sQ[cur] + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 q1 = ld16(sQ[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 o0 = ld16(sO[cur] + col * kLdsStride + 16 * c + 8 * hl);
-      const bf16x8 o1 = ld16(sO[cur] + (32 + col) * kLdsStride + 16 * c + 8 * hl);
+    for (int c = 0; c < kC; ++c) {
+      const bf16x8 q0 = ld16(sQ[cur] + col * kS + 16 * c + 8 * hl);
+      const bf16x8 q1 = ld16(sQ[cur] + (32 + col) * kS + 16 * c + 8 * hl);
+      const bf16x8 o0 = ld16(sO[cur] + col * kS + 16 * c + 8 * hl);
+      const bf16x8 o1 = ld16(sO[cur] + (32 + col) * kS + 16 * c + 8 * hl);
       s0 = mfma32(q0, kB[c], s0);
       s1 = mfma32(q1, kB[c], s1);
       p0 = mfma32(o0, vB[c], p0);
@@ -563,10 +577,10 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
     const bf16x8 dc[4] = {pack8(p0, 0), pack8(p0, 8), pack8(p1, 0), pack8(p1, 8)};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      dv0 = mfma32(ld_tr8(sO[cur], 0, c, lane), pc[c], dv0);
-      dv1 = mfma32(ld_tr8(sO[cur], 1, c, lane), pc[c], dv1);
-      dk0 = mfma32(ld_tr8(sQ[cur], 0, c, lane), dc[c], dk0);
-      dk1 = mfma32(ld_tr8(sQ[cur], 1, c, lane), dc[c], dk1);
+#pragma unroll
+      for (int t = 0; t < kT; ++t) dv[t] = mfma32(ld_tr8<D>(sO[cur], t, c, lane), pc[c], dv[t]);
+#pragma unroll
+      for (int t = 0; t < kT; ++t) dk[t] = mfma32(ld_tr8<D>(sQ[cur], t, c, lane), dc[c], dk[t]);
     }
     if constexpr (kKind == kKvSeg) {
       // A column holding global keys sums over every row of the sequence, and with a
@@ -583,10 +597,10 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
       const bf16x8 dl[4] = {pack8(p0, 0), pack8(p0, 8), pack8(p1, 0), pack8(p1, 8)};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        dv0 = mfma32(ld_tr8(sO[cur], 0, c, lane), pl[c], dv0);
-        dv1 = mfma32(ld_tr8(sO[cur], 1, c, lane), pl[c], dv1);
-        dk0 = mfma32(ld_tr8(sQ[cur], 0, c, lane), dl[c], dk0);
-        dk1 = mfma32(ld_tr8(sQ[cur], 1, c, lane), dl[c], dk1);
+#pragma unroll
+        for (int t = 0; t < kT; ++t) dv[t] = mfma32(ld_tr8<D>(sO[cur], t, c, lane), pl[c], dv[t]);
+#pragma unroll
+        for (int t = 0; t < kT; ++t) dk[t] = mfma32(ld_tr8<D>(sQ[cur], t, c, lane), dl[c], dk[t]);
       }
     }
     if (xn < ntile) {
@@ -602,41 +616,45 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
   const float sc = a.scale;
   if constexpr (kKind != kKvSeg) {
     if (!key_valid) return;
-    const size_t off = bh_off + (size_t)q_tok * kHead + 4 * hl;
+    const size_t off = bh_off + (size_t)q_tok * D + 4 * hl;
     uint16_t* kp = (kGRows ? a.dkg : a.dk) + off;
     uint16_t* vp = (kGRows ? a.dvg : a.dv) + off;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x2 k0w, k1w, v0w, v1w;
-      k0w[0] = pack_bf16x2(dk0[4 * j] * sc, dk0[4 * j + 1] * sc);
-      k0w[1] = pack_bf16x2(dk0[4 * j + 2] * sc, dk0[4 * j + 3] * sc);
-      k1w[0] = pack_bf16x2(dk1[4 * j] * sc, dk1[4 * j + 1] * sc);
-      k1w[1] = pack_bf16x2(dk1[4 * j + 2] * sc, dk1[4 * j + 3] * sc);
-      v0w[0] = pack_bf16x2(dv0[4 * j], dv0[4 * j + 1]);
-      v0w[1] = pack_bf16x2(dv0[4 * j + 2], dv0[4 * j + 3]);
-      v1w[0] = pack_bf16x2(dv1[4 * j], dv1[4 * j + 1]);
-      v1w[1] = pack_bf16x2(dv1[4 * j + 2], dv1[4 * j + 3]);
-      *reinterpret_cast<u32x2*>(kp + 8 * j) = k0w;
-      *reinterpret_cast<u32x2*>(kp + 32 + 8 * j) = k1w;
-      *reinterpret_cast<u32x2*>(vp + 8 * j) = v0w;
-      *reinterpret_cast<u32x2*>(vp + 32 + 8 * j) = v1w;
+      u32x2 kw[kT], vw[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        kw[t][0] = pack_bf16x2(dk[t][4 * j] * sc, dk[t][4 * j + 1] * sc);
+        kw[t][1] = pack_bf16x2(dk[t][4 * j + 2] * sc, dk[t][4 * j + 3] * sc);
+      }
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        vw[t][0] = pack_bf16x2(dv[t][4 * j], dv[t][4 * j + 1]);
+        vw[t][1] = pack_bf16x2(dv[t][4 * j + 2], dv[t][4 * j + 3]);
+      }
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<u32x2*>(kp + 32 * t + 8 * j) = kw[t];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<u32x2*>(vp + 32 * t + 8 * j) = vw[t];
     }
   } else {
     const size_t slot = ((size_t)per * a.nct_g + gki) * a.nseg + seg;
-    float* pk = a.part_kv + slot * 2 * kTile + kx * kHead + 4 * hl;
-    float* pv = pk + kTile;
+    float* pk = a.part_kv + slot * 2 * kTileOf<D> + kx * D + 4 * hl;
+    float* pv = pk + kTileOf<D>;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f32x4 k0w, k1w, v0w, v1w;
+      f32x4 kw[kT], vw[kT];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        k0w[e] = dk0[4 * j + e] * sc; k1w[e] = dk1[4 * j + e] * sc;
-        v0w[e] = dv0[4 * j + e]; v1w[e] = dv1[4 * j + e];
+#pragma unroll
+        for (int t = 0; t < kT; ++t) kw[t][e] = dk[t][4 * j + e] * sc;
+#pragma unroll
+        for (int t = 0; t < kT; ++t) vw[t][e] = dv[t][4 * j + e];
       }
-      *reinterpret_cast<f32x4*>(pk + 8 * j) = k0w;
-      *reinterpret_cast<f32x4*>(pk + 32 + 8 * j) = k1w;
-      *reinterpret_cast<f32x4*>(pv + 8 * j) = v0w;
-      *reinterpret_cast<f32x4*>(pv + 32 + 8 * j) = v1w;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<f32x4*>(pk + 32 * t + 8 * j) = kw[t];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) *reinterpret_cast<f32x4*>(pv + 32 * t + 8 * j) = vw[t];
     }
   }
 }
@@ -645,104 +663,148 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
 // two waves per SIMD, about 25 % faster than one.  (Asking for two waves
 // explicitly makes the compiler spill two registers instead; the resource report
 // of the build shows which one it got.)
+template <int D>
 __global__ __launch_bounds__(kThreads) void lf_bwd_dkdv_kernel(LfBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) LdsTile sQ[2];
-  __shared__ __attribute__((aligned(16))) LdsTile sO[2];   // dO
+  __shared__ __attribute__((aligned(16))) LdsTileT<D> sQ[2];
+  __shared__ __attribute__((aligned(16))) LdsTileT<D> sO[2];   // dO
   __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse / scale
   __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
   const int v = xcd_remap(blockIdx.x, a.kv_items);
   if (v >= a.kv_items) return;
   if (v < a.kv_plain_items)
-    lf_bwd_dkdv_item<kKvPlain>(a, v, sQ, sO, sL, sD);
+    lf_bwd_dkdv_item<D, kKvPlain>(a, v, sQ, sO, sL, sD);
   else
-    lf_bwd_dkdv_item<kKvGRows>(a, v - a.kv_plain_items, sQ, sO, sL, sD);
+    lf_bwd_dkdv_item<D, kKvGRows>(a, v - a.kv_plain_items, sQ, sO, sL, sD);
 }
 
 // The segments of key class tiles holding global keys, a launch of their own: their
 // residue products need more registers than the window items may use at two
 // waves per SIMD.  Launched before lf_bwd_dkdv_kernel: they are few and as long as
 // its items.
+template <int D>
 __global__ __launch_bounds__(kThreads) void lf_bwd_dkdv_seg_kernel(LfBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) LdsTile sQ[2];
-  __shared__ __attribute__((aligned(16))) LdsTile sO[2];   // dO
+  __shared__ __attribute__((aligned(16))) LdsTileT<D> sQ[2];
+  __shared__ __attribute__((aligned(16))) LdsTileT<D> sO[2];   // dO
   __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse / scale
   __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
   const int v = xcd_remap(blockIdx.x, a.kv_seg_items);
   if (v >= a.kv_seg_items) return;
-  lf_bwd_dkdv_item<kKvSeg>(a, v, sQ, sO, sL, sD);
+  lf_bwd_dkdv_item<D, kKvSeg>(a, v, sQ, sO, sL, sD);
 }
 
 // Segment sums in segment order.  Work-groups [0, B*H*ngt): dQ of global tile gt,
 // rows scattered to their tokens; then periods*nct_g*2: dK (kind 0) or dV (kind 1)
 // of the key class tiles holding global keys, rows scattered to their tokens.
+// Thread t sums 16 consecutive floats of the 64 x D tile at 16 t + 4096 u,
+// u = 0 .. D/64 - 1.
+template <int D>
 __global__ __launch_bounds__(256) void lf_bwd_reduce_kernel(LfBwdArgs a, int nq_groups) {
-  const int e0 = threadIdx.x * 16;   // 16 consecutive floats of the 64x64 tile
-  const int row = e0 / kHead;
-  const float* src;
-  size_t stride;
-  uint16_t* dst;
-  if ((int)blockIdx.x < nq_groups) {
-    const int idx = blockIdx.x;   // bh * ngt + gt
-    const int bh = idx / a.ngt, gt = idx - bh * a.ngt;
-    const int j = gt * kBlock + row;
-    if (j >= a.ng) return;
-    src = a.part_q + (size_t)idx * a.nseg * kTile + e0;
-    stride = kTile;
-    const size_t row_off = ((size_t)bh * a.n + a.gtok[j]) * kHead + (e0 % kHead);
-    dst = a.dqg + row_off;
-    if (a.gproj) {   // the window projections get nothing from a global row
-      float z[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) z[e] = 0.f;
-      store16_bf16(a.dq + row_off, z, 1.f);
+  for (int u = 0; u < D / 64; ++u) {
+    const int e0 = threadIdx.x * 16 + 4096 * u;
+    const int row = e0 / D;
+    const float* src;
+    size_t stride;
+    uint16_t* dst;
+    if ((int)blockIdx.x < nq_groups) {
+      const int idx = blockIdx.x;   // bh * ngt + gt
+      const int bh = idx / a.ngt, gt = idx - bh * a.ngt;
+      const int j = gt * kBlock + row;
+      if (j >= a.ng) continue;
+      src = a.part_q + (size_t)idx * a.nseg * kTileOf<D> + e0;
+      stride = kTileOf<D>;
+      const size_t row_off = ((size_t)bh * a.n + a.gtok[j]) * D + (e0 % D);
+      dst = a.dqg + row_off;
+      if (a.gproj) {   // the window projections get nothing from a global row
+        float z[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = 0.f;
+        store16_bf16(a.dq + row_off, z, 1.f);
+      }
+    } else {
+      const int w = blockIdx.x - nq_groups;
+      const int kind = w & 1, idx = w >> 1;   // idx = period * nct_g + gki
+      const int per = idx / a.nct_g, gki = idx - per * a.nct_g;
+      const LfTileRef e = a.ct[a.nct_plain + gki];
+      const int ci = e.t * kBlock + row;      // class index of this row
+      if (ci >= e.nc) continue;
+      const int bh = per * a.ph + e.h;
+      src = a.part_kv + (size_t)idx * a.nseg * 2 * kTileOf<D> + kind * kTileOf<D> + e0;
+      stride = 2 * kTileOf<D>;
+      dst = (kind == 0 ? a.dk : a.dv) + ((size_t)bh * a.n + e.c + (size_t)e.s * ci) * D +
+            (e0 % D);
     }
-  } else {
-    const int w = blockIdx.x - nq_groups;
-    const int kind = w & 1, idx = w >> 1;   // idx = period * nct_g + gki
-    const int per = idx / a.nct_g, gki = idx - per * a.nct_g;
-    const LfTileRef e = a.ct[a.nct_plain + gki];
-    const int ci = e.t * kBlock + row;      // class index of this row
-    if (ci >= e.nc) return;
-    const int bh = per * a.ph + e.h;
-    src = a.part_kv + (size_t)idx * a.nseg * 2 * kTile + kind * kTile + e0;
-    stride = 2 * kTile;
-    dst = (kind == 0 ? a.dk : a.dv) + ((size_t)bh * a.n + e.c + (size_t)e.s * ci) * kHead +
-          (e0 % kHead);
+    float acc[16];
+    sum_partials(src, stride, a.nseg, acc);
+    store16_bf16(dst, acc, 1.f);
   }
-  float acc[16];
-  sum_partials(src, stride, a.nseg, acc);
-  store16_bf16(dst, acc, 1.f);
 }
 
 struct LfBwdWs {
   size_t dbuf, part_q, part_kv, total;
 };
 
-LfBwdWs lf_bwd_ws_layout(const lfattn_plan* P, int batch, int heads) {
+LfBwdWs lf_bwd_ws_layout(const lfattn_plan* P, int batch, int heads, int d) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t bh = (size_t)batch * heads;
   const size_t periods = bh / (P->heads > 0 ? P->heads : 1);
+  const size_t tile = (size_t)kBlock * d;   // floats of one partial tile
   LfBwdWs w;
   w.dbuf = 0;
   w.part_q = up(bh * P->n * sizeof(float));
-  w.part_kv = up(w.part_q + bh * P->ngt * P->nseg * kTile * sizeof(float));
-  w.total = up(w.part_kv + periods * (P->nct - P->nct_plain) * P->nseg * 2 * kTile *
+  w.part_kv = up(w.part_q + bh * P->ngt * P->nseg * tile * sizeof(float));
+  w.total = up(w.part_kv + periods * (P->nct - P->nct_plain) * P->nseg * 2 * tile *
                                sizeof(float));
   return w;
 }
 
+template <int D>
+int launch_lf_bwd_d(const LfBwdArgs& a, const lfattn_plan* P, int bhn, int periods,
+                    hipStream_t stream) {
+  int st;
+  {
+    ProfScope prof_(D == 128 ? "lf_bwd_dq_d128" : "lf_bwd_dq", stream);
+    hipLaunchKernelGGL(lf_bwd_dq_kernel<D>, dim3(8 * ((a.dq_items + 7) / 8)), dim3(kThreads), 0,
+                       stream, a);
+  }
+  if ((st = check_hip(hipGetLastError(), "lf_bwd_dq launch"))) return st;
+  if (a.kv_seg_items > 0) {
+    {
+      ProfScope prof_(D == 128 ? "lf_bwd_dkdv_seg_d128" : "lf_bwd_dkdv_seg", stream);
+      hipLaunchKernelGGL(lf_bwd_dkdv_seg_kernel<D>, dim3(8 * ((a.kv_seg_items + 7) / 8)),
+                         dim3(kThreads), 0, stream, a);
+    }
+    if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv_seg launch"))) return st;
+  }
+  if (a.kv_items > 0) {
+    {
+      ProfScope prof_(D == 128 ? "lf_bwd_dkdv_d128" : "lf_bwd_dkdv", stream);
+      hipLaunchKernelGGL(lf_bwd_dkdv_kernel<D>, dim3(8 * ((a.kv_items + 7) / 8)), dim3(kThreads),
+                         0, stream, a);
+    }
+    if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv launch"))) return st;
+  }
+  const int nq_groups = bhn * P->ngt;
+  const int groups = nq_groups + periods * a.nct_g * 2;
+  if (groups == 0) return 0;
+  {
+    ProfScope prof_(D == 128 ? "lf_bwd_reduce_d128" : "lf_bwd_reduce", stream);
+    hipLaunchKernelGGL(lf_bwd_reduce_kernel<D>, dim3(groups), dim3(256), 0, stream, a, nq_groups);
+  }
+  return check_hip(hipGetLastError(), "lf_bwd_reduce launch");
+}
 }  // namespace
 
-size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads) {
-  return lf_bwd_ws_layout(P, batch, heads).total;
+size_t lf_bwd_workspace_bytes(const lfattn_plan* P, int batch, int heads, int d) {
+  return lf_bwd_ws_layout(P, batch, heads, d).total;
 }
 
-int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const void* q,
+int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, int d, float scale, const void* q,
                   const void* k, const void* v, const void* qg, const void* kg,
                   const void* vg, const void* o, const void* o_lo, const float* lse,
                   const void* dout, void* dq, void* dk, void* dv, void* dqg, void* dkg,
                   void* dvg, void* ws, hipStream_t stream) {
-  const LfBwdWs w = lf_bwd_ws_layout(P, batch, heads);
+  const LfBwdWs w = lf_bwd_ws_layout(P, batch, heads, d);
   char* base = (char*)ws;
   LfBwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
@@ -776,37 +838,8 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, float scale, const
   a.kv_plain_items = periods * a.nct_plain;
   a.kv_items = a.kv_plain_items + (a.gproj ? bhn * P->nt : 0);
   a.kv_seg_items = periods * a.nct_g * P->nseg;
-  int st;
-  {
-    ProfScope prof_("lf_bwd_dq", stream);
-    hipLaunchKernelGGL(lf_bwd_dq_kernel, dim3(8 * ((a.dq_items + 7) / 8)), dim3(kThreads), 0,
-                       stream, a);
-  }
-  if ((st = check_hip(hipGetLastError(), "lf_bwd_dq launch"))) return st;
-  if (a.kv_seg_items > 0) {
-    {
-      ProfScope prof_("lf_bwd_dkdv_seg", stream);
-      hipLaunchKernelGGL(lf_bwd_dkdv_seg_kernel, dim3(8 * ((a.kv_seg_items + 7) / 8)),
-                         dim3(kThreads), 0, stream, a);
-    }
-    if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv_seg launch"))) return st;
-  }
-  if (a.kv_items > 0) {
-    {
-      ProfScope prof_("lf_bwd_dkdv", stream);
-      hipLaunchKernelGGL(lf_bwd_dkdv_kernel, dim3(8 * ((a.kv_items + 7) / 8)), dim3(kThreads),
-                         0, stream, a);
-    }
-    if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv launch"))) return st;
-  }
-  const int nq_groups = bhn * P->ngt;
-  const int groups = nq_groups + periods * a.nct_g * 2;
-  if (groups == 0) return 0;
-  {
-    ProfScope prof_("lf_bwd_reduce", stream);
-    hipLaunchKernelGGL(lf_bwd_reduce_kernel, dim3(groups), dim3(256), 0, stream, a, nq_groups);
-  }
-  return check_hip(hipGetLastError(), "lf_bwd_reduce launch");
+  return d == 128 ? launch_lf_bwd_d<128>(a, P, bhn, periods, stream)
+                  : launch_lf_bwd_d<kHead>(a, P, bhn, periods, stream);
 }
 
 }  // namespace bsattn

@@ -302,7 +302,7 @@ int lfattn_fwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtyp
                float scale, const void* q, const void* k, const void* v, void* o,
                float* lse, void* o_lo, void* workspace, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes lfattn_bwd needs.  d must be 64.  0 for invalid arguments. */
+/* Workspace bytes lfattn_bwd needs (d = 64 or 128).  0 for invalid arguments. */
 size_t lfattn_bwd_workspace(const lfattn_plan* plan, int batch, int heads, int d);
 
 /*
@@ -322,7 +322,8 @@ size_t lfattn_bwd_workspace(const lfattn_plan* plan, int batch, int heads, int d
  * large share of its mass there, so those columns also feed the bf16 rounding
  * residues of P and dS through their products (about 2^-17 instead of 2^-9
  * relative per term).  No atomics, so results are bitwise reproducible.  dt must
- * be BSATTN_BF16 (else EUNSUPPORTED).  Returns OK, EINVAL, EUNSUPPORTED or EHIP.
+ * be BSATTN_BF16 and d 64 or 128 (else EUNSUPPORTED).  Returns OK, EINVAL,
+ * EUNSUPPORTED or EHIP.
  */
 int lfattn_bwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtype dt,
                float scale, const void* q, const void* k, const void* v, const void* o,

@@ -118,7 +118,7 @@ size_t fwd_workspace_bytes(const bsattn_layout*, int, int) { return kFakeFwd; }
 size_t fwd_workspace_bytes_dt(const bsattn_layout*, int, bsattn_dtype, int) { return kFakeFwd; }
 size_t bwd_workspace_bytes(const bsattn_layout*, int, int) { return kFakeBwd; }
 size_t lf_workspace_bytes(const lfattn_plan*, int, int, int) { return kFakeFwd; }
-size_t lf_bwd_workspace_bytes(const lfattn_plan*, int, int) { return kFakeBwd; }
+size_t lf_bwd_workspace_bytes(const lfattn_plan*, int, int, int) { return kFakeBwd; }
 
 int launch_fwd(const bsattn_layout*, int, bsattn_dtype, int, float, const void*, const void*,
                const void*, void*, float*, void*, void* ws, hipStream_t stream) {
@@ -140,7 +140,7 @@ int launch_lf_fwd(const lfattn_plan*, int, int, int, float, const void*, const v
   return BSATTN_OK;
 }
 
-int launch_lf_bwd(const lfattn_plan*, int, int, float, const void*, const void*, const void*,
+int launch_lf_bwd(const lfattn_plan*, int, int, int, float, const void*, const void*, const void*,
                   const void*, const void*, const void*, const void*, const void*, const float*,
                   const void*, void*, void*, void*, void*, void*, void*, void*, hipStream_t) {
   return BSATTN_OK;

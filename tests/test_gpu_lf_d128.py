@@ -128,3 +128,73 @@ def test_lf_d128_full_size_forward():
     say(f"lf d128 fwd full size n={n} H={heads} w1={w1}")
     refs, got = run(B.lfattn_plan_build(n, w1, G), n, heads, 1, bwd=False)
     assert compare(refs, got, OLF.longformer_mask(n, w1, G), heads=(3, 5)) <= BF16_TOL
+
+
+@pytest.mark.parametrize("case", LF_CASES[:4])
+def test_lf_d128_forward_backward(case):
+    n, heads, bsz, w1, G = case
+    say(f"lf d128 fwd+bwd n={n} H={heads} B={bsz} w1={w1} |G|={len(G)}")
+    refs, got = run(B.lfattn_plan_build(n, w1, G), n, heads, bsz)
+    assert compare(refs, got, OLF.longformer_mask(n, w1, G)) <= BF16_TOL
+
+
+def test_lf_d128_dilated_causal_backward():
+    n, w1, dil = 900, 50, [0, 2]
+    say(f"lf d128 fwd+bwd dilated causal n={n} w1={w1} dilation={dil}")
+    plan = B.lfattn_plan_build_dilated(n, w1, [], 2, dil, True)
+    refs, got = run(plan, n, 2, 1)
+    assert compare(refs, got, OLF.longformer_mask(n, w1, [], dil, True)) <= BF16_TOL
+
+
+def test_lf_d128_dilated_with_globals_backward():
+    n, w1, dil, G = 700, 40, [1, 3], [0, 2, 650]
+    say(f"lf d128 fwd+bwd dilated n={n} w1={w1} dilation={dil} G={G}")
+    plan = B.lfattn_plan_build_dilated(n, w1, G, 2, dil, False)
+    refs, got = run(plan, n, 2, 1)
+    assert compare(refs, got, OLF.longformer_mask(n, w1, G, dil, False)) <= BF16_TOL
+
+
+@pytest.mark.parametrize("case", [(64, 300, 84, 5), (16, 200, 23, 3)])
+def test_etc_d128_backward(case):
+    g, n, b, w = case
+    say(f"etc d128 fwd+bwd g={g} n={n} b={b} w={w}")
+    refs, got = run(B.lfattn_plan_build_etc(g, n, b, w), g + n, 2, 1)
+    assert compare(refs, got, OE.etc_mask(g, n, b, w)) <= BF16_TOL
+
+
+def test_lf_d128_gproj_backward():
+    n, w1, G = 1024, 64, [5, 300, 301, 777]
+    say(f"lf d128 gproj fwd+bwd n={n} w1={w1} G={G}")
+    dev, refs = qkv((1, 2, n, D), "bf16", (101, 102, 103, 104, 105, 106, 107))
+    q, k, v, qg, kg, vg, do = dev
+    plan = B.lfattn_plan_build(n, w1, G)
+    try:
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((1, 2, n), float("nan"), dtype=torch.float32, device="cuda")
+        wsf = torch.empty(max(1, B.lfattn_fwd_workspace(plan, 1, 2, D)), dtype=torch.uint8,
+                          device="cuda")
+        wsb = torch.empty(max(1, B.lfattn_bwd_workspace(plan, 1, 2, D)), dtype=torch.uint8,
+                          device="cuda")
+        B.lfattn_fwd_gproj(plan, q, k, v, qg, kg, vg, o, lse, wsf, scale=SCALE)
+        grads = [torch.full_like(q, float("nan")) for _ in range(6)]
+        B.lfattn_bwd_gproj(plan, q, k, v, qg, kg, vg, o, lse, do, *grads, wsb, scale=SCALE)
+        torch.cuda.synchronize()
+    finally:
+        B.lfattn_plan_destroy(plan)
+    qr, kr, vr, qgr, kgr, vgr, dor = refs
+    ro, rl = OLF.longformer_gproj_fwd(qr, kr, vr, qgr, kgr, vgr, n, w1, G, SCALE)
+    rg = OLF.longformer_gproj_bwd(qr, kr, vr, qgr, kgr, vgr, dor, n, w1, G, SCALE)
+    names = ("O", "lse", "dQ", "dK", "dV", "dQg", "dKg", "dVg")
+    got = [to_f64(t) for t in [o, lse] + grads]
+    errs = {nm: max_abs(a, b) for nm, a, b in zip(names, got, (ro, rl) + tuple(rg))}
+    say("   max-abs " + "  ".join(f"{a} {b:.2e}" for a, b in errs.items()))
+    assert max(errs.values()) <= BF16_TOL
+
+
+def test_lf_d128_full_size_backward():
+    """The Longformer workload's shape at d = 128, forward and backward; two heads
+    compared in full."""
+    n, heads, w1, G = 4096, 12, 256, list(range(64))
+    say(f"lf d128 fwd+bwd full size n={n} H={heads} w1={w1}")
+    refs, got = run(B.lfattn_plan_build(n, w1, G), n, heads, 1)
+    assert compare(refs, got, OLF.longformer_mask(n, w1, G), heads=(7, 9)) <= BF16_TOL
