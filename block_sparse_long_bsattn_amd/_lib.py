@@ -55,6 +55,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is missing: build it with `python -m block_sparse_long_bsattn_amd.build` "
             "(the attention path runs only in the HIP library; there is no fallback)")
+    # PyTorch ships its own HIP runtime and the tensors handed to the library live
+    # in it; importing torch first makes the library bind to that runtime instead
+    # of loading the system one beside it (two runtimes in one process do not share
+    # devices, memory or streams)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     sig = {
         "bsattn_layout_build": (c_int, [c_int, c_int, c_int, POINTER(c_int32), c_int, c_int, c_int,

@@ -408,11 +408,13 @@ __device__ __forceinline__ bool bit_of(const uint64_t (&b)[W], int x) {
   return (v >> (x & 63)) & 1ull;
 }
 
+// every word is updated (with a zero mask where x is not), so the array stays in
+// registers: a store under a data-dependent condition sends it to per-lane memory
 template <int W>
 __device__ __forceinline__ void set_bit(uint64_t (&b)[W], int x) {
+  const uint64_t m = 1ull << (x & 63);
 #pragma unroll
-  for (int k = 0; k < W; ++k)
-    if ((x >> 6) == k) b[k] |= 1ull << (x & 63);
+  for (int k = 0; k < W; ++k) b[k] |= (x >> 6) == k ? m : 0ull;
 }
 
 // position of the x-th (0-based) set bit; x < popcount(f)
@@ -495,11 +497,14 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
   // dynamic LDS: random picks per key block (nb x wpc words, bit i = query block
   // i), the global list G[g], every column's offset within the head, every
   // column's length, columns by length, first rank per length, every column's
-  // first query block
+  // first query block, columns per length, list offsets of the global rows
   extern __shared__ __attribute__((aligned(16))) int32_t dyn[];
   __shared__ uint32_t sGb[2 * W];
   __shared__ int part[kBuildThreads / 64];
   const int h = blockIdx.x, tid = threadIdx.x;
+  // the first row's list offset is loaded before anything else, so that its
+  // latency overlaps that of the global list
+  const int rp0 = tid < nb ? row_ptr[(int64_t)h * nb + tid] : 0;
   const int wpc = (nb + 31) / 32;
   uint32_t* colmap = reinterpret_cast<uint32_t*>(dyn);
   int32_t* sG = dyn + nb * wpc;
@@ -508,8 +513,11 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
   uint32_t* sBk = reinterpret_cast<uint32_t*>(sColLen + nb);   // [nb + 1][wpc] columns by length
   int32_t* sBase = reinterpret_cast<int32_t*>(sBk + (nb + 1) * wpc);   // [nb + 1] first rank
   int32_t* sColFirst = sBase + nb + 1;                 // [nb] first query block
+  int32_t* sLenCnt = sColFirst + nb;                   // [nb + 1] columns per length
+  int32_t* sGrp = sLenCnt + nb + 1;                    // [g] global rows' list offsets
   for (int x = tid; x < nb * wpc; x += kBuildThreads) colmap[x] = 0u;
   for (int x = tid; x < (nb + 1) * wpc; x += kBuildThreads) sBk[x] = 0u;
+  for (int x = tid; x <= nb; x += kBuildThreads) sLenCnt[x] = 0;
   for (int x = tid; x < g; x += kBuildThreads) sG[x] = Gglob[x];
   if (tid < 2 * W) sGb[tid] = 0u;
   __syncthreads();
@@ -525,7 +533,11 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
 
   // rows (global rows are written by the whole group at the end)
   for (int i = tid; i < nb; i += kBuildThreads) {
-    if (bit_of(gb, i)) continue;
+    const int rp = i == tid ? rp0 : row_ptr[(int64_t)h * nb + i];
+    if (bit_of(gb, i)) {
+      sGrp[bits_below(gb, i)] = rp;
+      continue;
+    }
     uint64_t row[W], freeb[W];
     int m = 0;
 #pragma unroll
@@ -543,21 +555,21 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
       if (t < take) {
         const uint64_t u = splitmix64_draw(seed, k0 + t);
         const int s = t + (int)mod_small(u, (uint32_t)(m - t));
-        int vt = -1, vs = -1;
+        // the log holds candidate positions, not blocks: only the pick itself is
+        // turned into a block (one bit select per draw)
+        int pt = t, ps = s;
 #pragma unroll kUnroll
         for (int q = 0; q < t; ++q) {
-          if (key[q] == t) vt = val[q];
-          if (key[q] == s) vs = val[q];
+          if (key[q] == t) pt = val[q];
+          if (key[q] == s) ps = val[q];
         }
-        if (vt < 0) vt = select_bit(freeb, t);
-        if (vs < 0) vs = select_bit(freeb, s);
         key[t] = s != t ? s : -1;
-        val[t] = vt;
+        val[t] = pt;
+        const int vs = select_bit(freeb, ps);
         set_bit(row, vs);
         atomicOr(&colmap[vs * wpc + (i >> 5)], 1u << (i & 31));
       }
     }
-    const int rp = row_ptr[(int64_t)h * nb + i];
     const int len = write_bits(row, col_idx + rp);
     // the row's work-item record, at its rank among the non-global rows
     int32_t* rec = row_info + 4 * ((int64_t)h * (nb - g) + i - bits_below(gb, i));
@@ -596,8 +608,11 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     sColPos[j] = pos;
     sColLen[j] = len;
     sColFirst[j] = first_bit(c);
-    if (!bit_of(gb, j)) atomicOr(&sBk[len * wpc + (j >> 5)], 1u << (j & 31));
-    if (!bit_of(gb, j)) write_bits(c, csc_idx + p);
+    if (!bit_of(gb, j)) {
+      atomicOr(&sBk[len * wpc + (j >> 5)], 1u << (j & 31));
+      atomicAdd(&sLenCnt[len], 1);
+      write_bits(c, csc_idx + p);
+    }
     pos += len;
   }
   if (h == gridDim.x - 1 && tid == kBuildThreads - 1)
@@ -609,17 +624,16 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
   // column j is the count of longer columns plus the columns of its length before
   // it.
   {
-    // the nb + 1 lengths are counted by the first wave alone (a wave scan, no
-    // work-group barrier)
-    const int bper = (nb + 1 + 63) / 64;
+    // the first rank of each length is an exclusive scan of the column counts
+    // over descending lengths (up to 63 blocks all lengths sit in the first wave)
+    const int bper = (nb + 1 + kBuildThreads - 1) / kBuildThreads;
     const int d0 = min(nb + 1, tid * bper), d1 = min(nb + 1, d0 + bper);   // L = nb - d
     int cnt = 0;
-    for (int d = d0; d < d1; ++d)
-      for (int x = 0; x < wpc; ++x) cnt += __popc(sBk[(nb - d) * wpc + x]);
-    int base = wave_exclusive_scan(cnt);
+    for (int d = d0; d < d1; ++d) cnt += sLenCnt[nb - d];
+    int base = nb < 64 ? wave_exclusive_scan(cnt) : block_exclusive_scan(cnt, part);
     for (int d = d0; d < d1; ++d) {
       sBase[nb - d] = base;
-      for (int x = 0; x < wpc; ++x) base += __popc(sBk[(nb - d) * wpc + x]);
+      base += sLenCnt[nb - d];
     }
   }
   __syncthreads();
@@ -638,9 +652,8 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
   // global rows and columns hold every block
   for (int e = tid; e < g * nb; e += kBuildThreads) {
     const int a = e / nb, j = e - a * nb;
-    const int x = sG[a];
-    col_idx[row_ptr[(int64_t)h * nb + x] + j] = j;
-    csc_idx[(int64_t)h * nnz_per_head + sColPos[x] + j] = j;
+    col_idx[sGrp[a] + j] = j;
+    csc_idx[(int64_t)h * nnz_per_head + sColPos[sG[a]] + j] = j;
   }
 }
 
@@ -719,11 +732,12 @@ __global__ __launch_bounds__(64) void layout_info_kernel(
 }
 
 namespace {
-// Dynamic LDS of layout_head_kernel: random picks, global list, column offsets and
-// lengths, columns by length, first rank per length.
+// Dynamic LDS of layout_head_kernel: random picks, global list, column offsets,
+// lengths and first query blocks, columns by length, first rank per length,
+// columns per length, global rows' list offsets.
 size_t head_lds_bytes(const bsattn_layout* L) {
   const int wpc = (L->nb + 31) / 32;
-  return ((size_t)L->nb * wpc + L->g + 3 * L->nb + (size_t)(L->nb + 1) * (wpc + 1)) *
+  return ((size_t)L->nb * wpc + L->g + 3 * L->nb + (size_t)(L->nb + 1) * (wpc + 2) + L->g) *
          sizeof(int32_t);
 }
 
