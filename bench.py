@@ -14,7 +14,8 @@ bf16 inputs with fp32 accumulation.  Prints ONE JSON line on stdout:
              host cores, in the same unit
   secondary  the other workloads (forward only at n = 4096 and 16384, fp32 at
              n = 512, Longformer window 256 + 64 global tokens forward, and its
-             forward + backward, BigBird-etc base (256 added global tokens,
+             forward + backward, the same with separate projections for the
+             global tokens, BigBird-etc base (256 added global tokens,
              blocks of 84) forward + backward, and the causal character-LM shape
              with dilation on two heads, forward + backward), each timed alone
 
@@ -64,6 +65,10 @@ WORKLOADS = {
     "longformer_fwd_bwd_b1_h12_n4096_w256_g64": dict(kind="longformer", n=4096, heads=12,
                                                       batch=1, w1=256, G=list(range(64)),
                                                       dtype="bf16", bwd=True),
+    # the same with separate projections for the global tokens' attention (Q_g, K_g, V_g)
+    "longformer_gproj_fwd_bwd_b1_h12_n4096_w256_g64": dict(kind="longformer", n=4096, heads=12,
+                                                            batch=1, w1=256, G=list(range(64)),
+                                                            dtype="bf16", bwd=True, gproj=True),
     # BigBird-etc base: 256 added global tokens, blocks of 84, window of 3 blocks
     "etc_fwd_bwd_b4_h12_g256_n4096_b84": dict(kind="etc", g=256, n=4096, b=84, w=3, heads=12,
                                               batch=4, dtype="bf16", bwd=True),
@@ -195,25 +200,46 @@ class Job:
                                        for h in range(heads))
             ws = B.lfattn_fwd_workspace(self.handle, bsz, heads)
             self.wsf = torch.empty(max(16, ws), dtype=torch.uint8, device="cuda")
-            B.lfattn_fwd(self.handle, self.q, self.k, self.v, self.o, self.lse, self.wsf,
-                         o_lo=self.olo)
             h = ctypes.c_void_p(self.handle)
-            self.calls.append((lib.lfattn_fwd, (h, bsz, heads, D, dt, scale, P(self.q), P(self.k),
-                                                P(self.v), P(self.o), P(self.lse), P(self.olo),
-                                                P(self.wsf), self.wsf.numel(), stream)))
+            gproj = cfg.get("gproj", False)
+            if gproj:   # the global tokens' projections, seeded after the others
+                self.qg, self.kg, self.vg = (dev(I.SEED_DO + x) for x in (1, 2, 3))
+                B.lfattn_fwd_gproj(self.handle, self.q, self.k, self.v, self.qg, self.kg, self.vg,
+                                   self.o, self.lse, self.wsf, o_lo=self.olo)
+                self.calls.append((lib.lfattn_fwd_gproj, (
+                    h, bsz, heads, D, dt, scale, P(self.q), P(self.k), P(self.v), P(self.qg),
+                    P(self.kg), P(self.vg), P(self.o), P(self.lse), P(self.olo), P(self.wsf),
+                    self.wsf.numel(), stream)))
+            else:
+                B.lfattn_fwd(self.handle, self.q, self.k, self.v, self.o, self.lse, self.wsf,
+                             o_lo=self.olo)
+                self.calls.append((lib.lfattn_fwd, (
+                    h, bsz, heads, D, dt, scale, P(self.q), P(self.k), P(self.v), P(self.o),
+                    P(self.lse), P(self.olo), P(self.wsf), self.wsf.numel(), stream)))
             self.flops = 4 * D * self.pairs
             if cfg["bwd"]:
                 self.do = dev(I.SEED_DO)
                 self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
                 wsb = B.lfattn_bwd_workspace(self.handle, bsz, heads)
                 self.wsb = torch.empty(max(16, wsb), dtype=torch.uint8, device="cuda")
-                B.lfattn_bwd(self.handle, self.q, self.k, self.v, self.o, self.lse, self.do,
-                             self.dq, self.dk, self.dv, self.wsb, o_lo=self.olo)
-                self.calls.append((lib.lfattn_bwd, (h, bsz, heads, D, dt, scale, P(self.q),
-                                                    P(self.k), P(self.v), P(self.o),
-                                                    P(self.olo), P(self.lse), P(self.do),
-                                                    P(self.dq), P(self.dk), P(self.dv),
-                                                    P(self.wsb), self.wsb.numel(), stream)))
+                if gproj:
+                    self.dqg, self.dkg, self.dvg = (torch.empty_like(self.q) for _ in range(3))
+                    B.lfattn_bwd_gproj(self.handle, self.q, self.k, self.v, self.qg, self.kg,
+                                       self.vg, self.o, self.lse, self.do, self.dq, self.dk,
+                                       self.dv, self.dqg, self.dkg, self.dvg, self.wsb,
+                                       o_lo=self.olo)
+                    self.calls.append((lib.lfattn_bwd_gproj, (
+                        h, bsz, heads, D, dt, scale, P(self.q), P(self.k), P(self.v), P(self.qg),
+                        P(self.kg), P(self.vg), P(self.o), P(self.olo), P(self.lse), P(self.do),
+                        P(self.dq), P(self.dk), P(self.dv), P(self.dqg), P(self.dkg),
+                        P(self.dvg), P(self.wsb), self.wsb.numel(), stream)))
+                else:
+                    B.lfattn_bwd(self.handle, self.q, self.k, self.v, self.o, self.lse, self.do,
+                                 self.dq, self.dk, self.dv, self.wsb, o_lo=self.olo)
+                    self.calls.append((lib.lfattn_bwd, (
+                        h, bsz, heads, D, dt, scale, P(self.q), P(self.k), P(self.v), P(self.o),
+                        P(self.olo), P(self.lse), P(self.do), P(self.dq), P(self.dk), P(self.dv),
+                        P(self.wsb), self.wsb.numel(), stream)))
                 self.flops += 8 * D * self.pairs
         torch.cuda.synchronize()
 
@@ -588,6 +614,7 @@ def main() -> int:
                        "passes": "fwd+bwd" if cfg["bwd"] else "fwd"} if cfg["kind"] == "etc" else
                       {"window_one_side": cfg["w1"], "global_tokens": len(cfg["G"]),
                        "dilation": cfg.get("dil", 0), "causal": cfg.get("causal", False),
+                       "global_projections": cfg.get("gproj", False),
                        "passes": "fwd+bwd" if cfg["bwd"] else "fwd"})},
         "pct_peak": round(100 * value / peak, 3),
         "useful_pairs": job.pairs,

@@ -669,8 +669,8 @@ __global__ __launch_bounds__(kThreads) void lf_bwd_dkdv_kernel(LfBwdArgs a) {
   __shared__ __attribute__((aligned(16))) LdsTileT<D> sO[2];   // dO
   __shared__ __attribute__((aligned(16))) float sL[2][kBlock];   // -lse / scale
   __shared__ __attribute__((aligned(16))) float sD[2][kBlock];   // -D
-  const int v = xcd_remap(blockIdx.x, a.kv_items);
-  if (v >= a.kv_items) return;
+  const int v = xcd_remap_two(blockIdx.x, a.kv_plain_items, a.kv_items - a.kv_plain_items);
+  if (v < 0) return;
   if (v < a.kv_plain_items)
     lf_bwd_dkdv_item<D, kKvPlain>(a, v, sQ, sO, sL, sD);
   else
@@ -779,8 +779,9 @@ int launch_lf_bwd_d(const LfBwdArgs& a, const lfattn_plan* P, int bhn, int perio
   if (a.kv_items > 0) {
     {
       ProfScope prof_(D == 128 ? "lf_bwd_dkdv_d128" : "lf_bwd_dkdv", stream);
-      hipLaunchKernelGGL(lf_bwd_dkdv_kernel<D>, dim3(8 * ((a.kv_items + 7) / 8)), dim3(kThreads),
-                         0, stream, a);
+      const int kg = a.kv_items - a.kv_plain_items;
+      hipLaunchKernelGGL(lf_bwd_dkdv_kernel<D>, dim3(8 * ((a.kv_plain_items + 7) / 8 + (kg + 7) / 8)),
+                         dim3(kThreads), 0, stream, a);
     }
     if ((st = check_hip(hipGetLastError(), "lf_bwd_dkdv launch"))) return st;
   }
