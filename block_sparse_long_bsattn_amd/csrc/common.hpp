@@ -205,22 +205,6 @@ __device__ __forceinline__ int xcd_remap(int g, int total) {
   return (g & 7) * per + (g >> 3);
 }
 
-// Two lists, n1 items and then n2: each XCD runs its eighth of the first list and
-// then its eighth of the second, so that both kinds of item spread over all eight
-// (eighths of the joined list would give the first XCDs only the first kind).
-// Returns the item (the second list numbered from n1 on), or -1 for a work-group
-// past the end of its XCD's share.  Grid: 8 * (ceil(n1/8) + ceil(n2/8)).
-__device__ __forceinline__ int xcd_remap_two(int g, int n1, int n2) {
-  const int p1 = (n1 + 7) / 8, p2 = (n2 + 7) / 8;
-  const int x = g & 7, k = g >> 3;
-  if (k < p1) {
-    const int v = x * p1 + k;
-    return v < n1 ? v : -1;
-  }
-  const int v = x * p2 + (k - p1);
-  return v < n2 ? n1 + v : -1;
-}
-
 // The same eighths, for a list made of consecutive groups of ipb items whose
 // first ng are short and the rest long: each XCD runs the long items of its eighth
 // before the short ones, so the longest work starts first.  Returns the item of

@@ -20,6 +20,22 @@
 
 namespace bsattn {
 
+// Two lists, n1 items and then n2: each XCD runs its eighth of the first list and
+// then its eighth of the second, so that both kinds of item spread over all eight
+// (eighths of the joined list would give the first XCDs only the first kind).
+// Returns the item (the second list numbered from n1 on), or -1 for a work-group
+// past the end of its XCD's share.  Grid: 8 * (ceil(n1/8) + ceil(n2/8)).
+__device__ __forceinline__ int xcd_remap_two(int g, int n1, int n2) {
+  const int p1 = (n1 + 7) / 8, p2 = (n2 + 7) / 8;
+  const int x = g & 7, k = g >> 3;
+  if (k < p1) {
+    const int v = x * p1 + k;
+    return v < n1 ? v : -1;
+  }
+  const int v = x * p2 + (k - p1);
+  return v < n2 ? n1 + v : -1;
+}
+
 // Token behind row x of global tile gt: the (gt*64 + x)-th global token; rows past
 // the last one repeat it (their keys or queries are masked out or not written).
 __device__ __forceinline__ int global_token(const int32_t* gtok, int ng, int gt, int x) {
