@@ -336,8 +336,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void lf_bwd_dq_kernel(LfBwdArgs a) {
   __shared__ __attribute__((aligned(16))) LdsTileT<D> sK[2];
   __shared__ __attribute__((aligned(16))) LdsTileT<D> sV[2];
-  const int v = xcd_remap(blockIdx.x, a.dq_items);
-  if (v >= a.dq_items) return;
+  const int v = xcd_remap_two(blockIdx.x, a.dq_band_items, a.dq_items - a.dq_band_items);
+  if (v < 0) return;
   if (v < a.dq_band_items)
     lf_bwd_dq_item<D, true>(a, v, sK, sV);
   else
@@ -764,8 +764,9 @@ int launch_lf_bwd_d(const LfBwdArgs& a, const lfattn_plan* P, int bhn, int perio
   int st;
   {
     ProfScope prof_(D == 128 ? "lf_bwd_dq_d128" : "lf_bwd_dq", stream);
-    hipLaunchKernelGGL(lf_bwd_dq_kernel<D>, dim3(8 * ((a.dq_items + 7) / 8)), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL(lf_bwd_dq_kernel<D>,
+                       dim3(8 * ((a.dq_band_items + 7) / 8 + (a.dq_items - a.dq_band_items + 7) / 8)),
+                       dim3(kThreads), 0, stream, a);
   }
   if ((st = check_hip(hipGetLastError(), "lf_bwd_dq launch"))) return st;
   if (a.kv_seg_items > 0) {

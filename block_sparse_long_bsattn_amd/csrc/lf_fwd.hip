@@ -245,14 +245,15 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTileT<
   write_partial(st, l_tot, lb_tot, hl, qr, a.part + (size_t)v * kPartFloatsOf<D>);
 }
 
-// Band items first, then the global-row segments (about as long as a band item).
-// D = 128 takes more than half the registers: one wave per SIMD.
+// Band items first, then the global-row segments (about as long as a band item), each
+// kind spread over all XCDs.  D = 128 takes more than half the registers: one wave
+// per SIMD.
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void lf_attn_kernel(LfArgs a) {
   __shared__ __attribute__((aligned(16))) LdsTileT<D> sK[2];
   __shared__ __attribute__((aligned(16))) LdsTileT<D> sV[2];
-  const int v = xcd_remap(blockIdx.x, a.total_items);
-  if (v >= a.total_items) return;
+  const int v = xcd_remap_two(blockIdx.x, a.band_items, a.total_items - a.band_items);
+  if (v < 0) return;
   if (v < a.band_items)
     lf_band_item<D>(a, v, sK, sV);
   else
@@ -315,7 +316,7 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   int st;
   {
     ProfScope prof_(d == 128 ? "lf_attn_d128" : "lf_attn", stream);
-    const dim3 grid(8 * ((a.total_items + 7) / 8));
+    const dim3 grid(8 * ((a.band_items + 7) / 8 + (a.total_items - a.band_items + 7) / 8));
     if (d == 128)
       hipLaunchKernelGGL(lf_attn_kernel<128>, grid, dim3(kThreads), 0, stream, a);
     else
