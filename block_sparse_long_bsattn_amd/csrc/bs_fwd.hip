@@ -97,6 +97,18 @@ __device__ __forceinline__ Item decode_row_item(const FwdArgs& a, int v) {
 
 // kRagged: the sequence ends inside its last block (n % 64 != 0); the instance for
 // whole blocks carries none of that block's masking and guards.  D: head dimension.
+// gload_nat for a tile whose rows at or past `rows` are not tokens: those rows read
+// row rows - 1 instead.  The values are finite and the caller masks those keys out
+// (P = 0) or drops those query rows, so no per-row predicate or branch is needed.
+template <int D>
+__device__ __forceinline__ void gload_nat_clamp(TileRegsT<D>& r, const uint16_t* g, int tid,
+                                                int rows) {
+  constexpr int kCpr = D / 8, kRpp = 128 / kCpr, kShift = D == 64 ? 3 : 4;
+  const int c = tid & (kCpr - 1), row = tid >> kShift;
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) r.v[u] = ldg16(g + min(row + kRpp * u, rows - 1) * D + 8 * c);
+}
+
 template <int D, bool kRagged>
 __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlock * kStrideOf<D>];
@@ -115,12 +127,14 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   const int len = it.len;
   auto kaddr = [&](int kb) { return kbase + (size_t)kb * kBlock * D; };
   auto vaddr = [&](int kb) { return vbase + (size_t)kb * kBlock * D; };
-  // a sequence that ends inside its last block: that block's missing rows are
-  // neither read nor attended to, and no output is written for them
+  // a sequence that ends inside its last block: that block's missing rows are not
+  // read (their positions repeat the last token's row, one code path for every
+  // tile), they are masked out as keys, and no output is written for them
   auto tile_load = [&](int kb, TileRegsT<D>& kr, TileRegsT<D>& vr) {
-    if (kRagged && kb == a.nb - 1) {
-      gload_nat_rows(kr, kaddr(kb), tid, a.last_rows);
-      gload_nat_rows(vr, vaddr(kb), tid, a.last_rows);
+    if (kRagged) {
+      const int rows = kb == a.nb - 1 ? a.last_rows : kBlock;
+      gload_nat_clamp(kr, kaddr(kb), tid, rows);
+      gload_nat_clamp(vr, vaddr(kb), tid, rows);
     } else {
       gload_nat(kr, kaddr(kb), tid);
       gload_nat(vr, vaddr(kb), tid);
@@ -136,9 +150,10 @@ __global__ __launch_bounds__(kFwdThreads) void bs_fwd_bf16_kernel(FwdArgs a) {
   int kb_next = len > 1 ? it.at(keys, 1) : 0;
   bf16x8 qB[D / 16];
   {
-    const uint16_t* qp = a.q + bh_off + (size_t)qrow * D + 8 * hl;
+    // query rows past the end read the last token's row; their outputs are dropped
+    const uint16_t* qp = a.q + bh_off + (size_t)(kRagged ? min(qrow, a.n - 1) : qrow) * D + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) qB[c] = !kRagged || qrow < a.n ? ld16(qp + 16 * c) : bf16x8{};
+    for (int c = 0; c < D / 16; ++c) qB[c] = ld16(qp + 16 * c);
   }
   lds_store_nat(sK[0], kr, tid);
   lds_store_nat(sV[0], vr, tid);
