@@ -243,10 +243,14 @@ struct FwdF32Args {
   float* lse;
   const int32_t* row_ptr;
   const int32_t* col_idx;
-  float* part;       // partial records [rows][nseg][kPartFloats] when split
-  int heads, n, nb, total_items;
+  const int32_t* row_info;   // [heads][nb - g][4] non-global row records
+  const int32_t* gblk;
+  float* part;       // partial records [rows][nseg][kPartFloats] of the split rows
+  int heads, n, nb, g, total_items;
   int last_rows;   // tokens in the last block: n - 64 (nb - 1), 1..64
   int fseg, nseg;  // split rows: segments of fseg key blocks, at most nseg per row
+  int gsplit;      // only the global rows are split: items_per_bh items per (batch,
+  int items_per_bh;   // head), the non-global rows whole, then the global segments
   float scale;
 };
 
@@ -294,10 +298,43 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
   __shared__ __attribute__((aligned(16))) float sQ[kBlock * kF32Stride];
   __shared__ __attribute__((aligned(16))) float sK[kBlock * kF32Stride];   // K, then P
   __shared__ __attribute__((aligned(16))) float sV[kBlock * kF32Stride];
-  const int v = xcd_remap(blockIdx.x, a.total_items);
-  if (v >= a.total_items) return;
-  const int row = v / a.nseg, seg = v - row * a.nseg;
-  const int bh = row / a.nb, i = row - bh * a.nb, h = bh % a.heads;
+  // this item's query block i, its key list [rp0, rp1) and, for a segment of a split
+  // row, the index of its partial record (-1: the item holds its whole row)
+  int bh, i, rp0, rp1, slot = -1;
+  if (a.gsplit) {   // non-global rows whole, global rows in segments, long items first
+    const int v = xcd_item_long_first(blockIdx.x, a.total_items, a.items_per_bh, a.nb - a.g);
+    if (v < 0) return;
+    bh = v / a.items_per_bh;
+    const int r = v - bh * a.items_per_bh, h = bh % a.heads, ng = a.nb - a.g;
+    if (r < ng) {
+      const int32_t* rec = a.row_info + 4 * ((int64_t)h * ng + r);
+      i = rec[0];
+      rp0 = rec[1];
+      rp1 = rp0 + rec[2];
+    } else {
+      const int gi = (r - ng) / a.nseg, s = (r - ng) - gi * a.nseg;
+      i = a.gblk[gi];
+      const int base = a.row_ptr[(int64_t)h * a.nb + i];   // a global row lists 0 .. nb-1
+      rp0 = base + s * a.fseg;
+      rp1 = base + min(a.nb, (s + 1) * a.fseg);
+      slot = (bh * a.g + gi) * a.nseg + s;
+    }
+  } else {   // every row split into nseg segments (or whole when nseg = 1)
+    const int v = xcd_remap(blockIdx.x, a.total_items);
+    if (v >= a.total_items) return;
+    const int row = v / a.nseg, seg = v - row * a.nseg;
+    bh = row / a.nb;
+    i = row - bh * a.nb;
+    const int h = bh % a.heads;
+    rp0 = a.row_ptr[(int64_t)h * a.nb + i];
+    rp1 = a.row_ptr[(int64_t)h * a.nb + i + 1];
+    if (a.nseg > 1) {   // this item's segment of the row
+      rp0 += seg * a.fseg;
+      if (rp0 >= rp1) return;
+      rp1 = min(rp1, rp0 + a.fseg);
+      slot = v;
+    }
+  }
   const int tid = threadIdx.x, tq = tid >> 4, tk = tid & 15;
   const size_t bh_off = (size_t)bh * a.n * kHead;
   auto rows_of = [&](int blk) { return blk == a.nb - 1 ? a.last_rows : kBlock; };
@@ -314,12 +351,6 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
     l[r] = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-  }
-  int rp0 = a.row_ptr[(int64_t)h * a.nb + i], rp1 = a.row_ptr[(int64_t)h * a.nb + i + 1];
-  if (a.nseg > 1) {   // this item's segment of the row
-    rp0 += seg * a.fseg;
-    if (rp0 >= rp1) return;
-    rp1 = min(rp1, rp0 + a.fseg);
   }
   // K and V of the next key block are loaded into registers one block ahead
   TileF32 kt, vt;
@@ -411,8 +442,8 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
           for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(pv[r][x], vv[x][c], acc[r][c]);
     }
   }
-  if (a.nseg > 1) {   // partial record: O unnormalised, then m, then l (natural log units)
-    float* rec = a.part + (size_t)v * kPartFloats;
+  if (slot >= 0) {   // partial record: O unnormalised, then m, then l (natural log units)
+    float* rec = a.part + (size_t)slot * kPartFloats;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const f32x4 w = {acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
@@ -437,12 +468,17 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_kernel(FwdF32Args a) {
 
 // Merge the segment records of every split fp32 row, in segment order:
 // M = max_s m_s, L = sum_s l_s e^(m_s - M), O = sum_s O_s e^(m_s - M) / L, lse = M + ln L.
-// One work-group per row (query block); thread t: query row t / 4, 16 columns.
+// One work-group per split row: work-group (bh, i) when every row is split, (bh, gi)
+// for global block gblk[gi] when only the global rows are (gblk not null); thread t:
+// query row t / 4, 16 columns.
 __global__ __launch_bounds__(256) void bs_fwd_f32_combine_kernel(
-    const float* __restrict__ part, const int32_t* __restrict__ row_ptr, int heads, int n,
-    int nb, int fseg, int nseg, float* __restrict__ o, float* __restrict__ lse) {
-  const int row = blockIdx.x;   // (bh, i)
-  const int bh = row / nb, i = row - bh * nb, h = bh % heads;
+    const float* __restrict__ part, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ gblk, int heads, int n, int nb, int g, int fseg, int nseg,
+    float* __restrict__ o, float* __restrict__ lse) {
+  const int row = blockIdx.x;   // (bh, i) or (bh, gi)
+  const int per = gblk != nullptr ? g : nb;
+  const int bh = row / per, h = bh % heads;
+  const int i = gblk != nullptr ? gblk[row - bh * per] : row - bh * per;
   const int qr = threadIdx.x >> 2, dq = (threadIdx.x & 3) * 16;
   const int tok = i * kBlock + qr;
   if (tok >= n) return;   // past the end of a sequence that ends inside this block
@@ -477,16 +513,22 @@ __global__ __launch_bounds__(256) void bs_fwd_f32_combine_kernel(
   if (lse != nullptr && (threadIdx.x & 3) == 0) lse[(size_t)bh * n + tok] = M + logf(L);
 }
 
-// fp32 row split: rows of fseg key blocks when the rows alone would leave most
-// work-group slots (four per compute unit) idle; at most kF32MaxItems items.
-struct F32Plan { int fseg, nseg; };
+// fp32 row split.  When the rows alone would leave most work-group slots (four per
+// compute unit) idle, every row is cut into segments of fseg key blocks (at most
+// kF32MaxItems items).  Otherwise the global rows, which list every block, are cut
+// into the segments of the bf16 path (seg_plan) and the other rows run whole.
+struct F32Plan { int fseg, nseg, gsplit; };
 constexpr int kF32MaxItems = 2048;
 
 F32Plan f32_plan(const bsattn_layout* L, int batch) {
   const int64_t rows = (int64_t)batch * L->heads * L->nb;
   const int64_t slots = 4 * (int64_t)(L->cus > 0 ? L->cus : 1);
-  F32Plan p{L->nb, 1};
-  if (2 * rows >= slots) return p;
+  F32Plan p{L->nb, 1, 0};
+  if (2 * rows >= slots) {
+    const SegPlan sp = seg_plan(L, batch);
+    if (L->g > 0 && sp.split) p = F32Plan{sp.seg, sp.nseg, 1};
+    return p;
+  }
   const int64_t pairs = (int64_t)batch * L->heads * L->nnz_per_head;
   int fseg = (int)std::max<int64_t>(1, (pairs + slots - 1) / slots);
   int nseg = (L->nb + fseg - 1) / fseg;
@@ -494,7 +536,7 @@ F32Plan f32_plan(const bsattn_layout* L, int batch) {
     fseg *= 2;
     nseg = (L->nb + fseg - 1) / fseg;
   }
-  if (nseg > 1) p = F32Plan{fseg, nseg};
+  if (nseg > 1) p = F32Plan{fseg, nseg, 0};
   return p;
 }
 
@@ -504,7 +546,8 @@ F32Plan f32_plan(const bsattn_layout* L, int batch) {
 size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt, int d) {
   if (dt == BSATTN_F32) {
     const F32Plan fp = f32_plan(L, batch);
-    return fp.nseg > 1 ? (size_t)batch * L->heads * L->nb * fp.nseg * kPartFloats * sizeof(float) : 0;
+    const size_t rows = (size_t)batch * L->heads * (fp.gsplit ? L->g : L->nb);
+    return fp.nseg > 1 ? rows * fp.nseg * kPartFloats * sizeof(float) : 0;
   }
   const SegPlan sp = seg_plan(L, batch);
   const size_t part = d == 128 ? kPartFloatsOf<128> : kPartFloats;
@@ -532,11 +575,13 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, int d, float 
     a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;
     a.o = (float*)o; a.lse = lse;
     a.row_ptr = L->d_row_ptr; a.col_idx = L->d_col_idx;
-    a.heads = L->heads; a.n = L->n; a.nb = L->nb;
+    a.row_info = L->d_row_info; a.gblk = L->d_gblk;
+    a.heads = L->heads; a.n = L->n; a.nb = L->nb; a.g = L->g;
     const F32Plan fp = f32_plan(L, batch);
-    a.fseg = fp.fseg; a.nseg = fp.nseg;
+    a.fseg = fp.fseg; a.nseg = fp.nseg; a.gsplit = fp.gsplit;
     a.part = (float*)ws;
-    a.total_items = bhn * L->nb * fp.nseg;
+    a.items_per_bh = fp.gsplit ? (L->nb - L->g) + L->g * fp.nseg : L->nb * fp.nseg;
+    a.total_items = bhn * a.items_per_bh;
     a.last_rows = L->n - kBlock * (L->nb - 1);
     a.scale = scale;
     const int grid = 8 * ((a.total_items + 7) / 8);
@@ -551,9 +596,10 @@ int launch_fwd(const bsattn_layout* L, int batch, bsattn_dtype dt, int d, float 
     if (st || fp.nseg == 1) return st;
     {
       ProfScope prof_("bs_fwd_f32_combine", stream);
-      hipLaunchKernelGGL(bs_fwd_f32_combine_kernel, dim3(bhn * L->nb), dim3(256), 0, stream,
-                         (const float*)ws, L->d_row_ptr, L->heads, L->n, L->nb, fp.fseg, fp.nseg,
-                         (float*)o, lse);
+      hipLaunchKernelGGL(bs_fwd_f32_combine_kernel, dim3(bhn * (fp.gsplit ? L->g : L->nb)),
+                         dim3(256), 0, stream, (const float*)ws, L->d_row_ptr,
+                         fp.gsplit ? (const int32_t*)L->d_gblk : nullptr, L->heads, L->n, L->nb,
+                         L->g, fp.fseg, fp.nseg, (float*)o, lse);
     }
     return check_hip(hipGetLastError(), "bs_fwd_f32_combine launch");
   }

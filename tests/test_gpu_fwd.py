@@ -98,8 +98,9 @@ def test_fwd_fp32_other_shapes():
 
 
 def test_fwd_fp32_unsplit_rows():
-    """Enough query blocks (batch 1, 8 heads, n = 4096: 512 rows) that fp32 rows run
-    whole, one work-group per row."""
+    """Enough query blocks (batch 1, 8 heads, n = 4096: 512 rows) that the ordinary
+    fp32 rows run whole, one work-group per row, while the global rows (every block)
+    are cut into segments merged in order."""
     check_full(4096, 8, 1, [0, 63], 3, 3, 6, dtype="f32")
 
 

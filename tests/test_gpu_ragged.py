@@ -91,6 +91,19 @@ def test_ragged_fwd_fp32():
     assert e_o <= F32_TOL and e_l <= F32_TOL
 
 
+def test_ragged_fwd_fp32_global_segments():
+    """fp32 path with enough rows (9 heads, n = 4000: 567 rows) that only the global
+    rows are cut into segments; the last block (32 tokens) is one of them."""
+    n, heads, bsz, G = 4000, 9, 1, [0, 62]
+    say("ragged fwd fp32 n=4000 H=9, global segments")
+    (qr, kr, vr, _), o, lse, _ = run(n, heads, bsz, G, 3, 3, 8, dtype="f32", bwd=False)
+    ro, rl = OA.attention_fwd(qr, kr, vr, ragged_mask(n, heads, G, 3, 3, 8), 1 / 8.0)
+    e_o, e_l = max_abs(o, ro), max_abs(lse, rl)
+    say(f"   max-abs O {e_o:.3e} lse {e_l:.3e}")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    assert e_o <= F32_TOL and e_l <= F32_TOL
+
+
 def test_ragged_layout_is_the_padded_one():
     """The device layout of n = 1000 equals the oracle's, which is that of 1024."""
     h = B.bsattn_layout_build(1000, 64, 2, [0, 15], 3, 3, 9)
