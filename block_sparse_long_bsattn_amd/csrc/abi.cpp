@@ -588,6 +588,8 @@ int lf_plan_build(int n, int window_one_side, const int32_t* global_tokens, int 
   build_class_tiles(P);
   hipError_t e = hipGetDevice(&P->device);
   if (e != hipSuccess) { delete P; return check_hip(e, "hipGetDevice"); }
+  e = hipDeviceGetAttribute(&P->cus, hipDeviceAttributeMultiprocessorCount, P->device);
+  if (e != hipSuccess) { delete P; return check_hip(e, "hipDeviceGetAttribute"); }
   int st;
   if ((st = dev_alloc(&P->d_gtok, (size_t)n_global)) || (st = dev_alloc(&P->d_gidx, (size_t)n)) ||
       (st = dev_alloc(&P->d_tile_gmask, (size_t)P->nt)) ||

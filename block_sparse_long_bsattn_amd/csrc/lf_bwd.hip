@@ -63,13 +63,15 @@ struct LfBwdArgs {
   int gproj;
   float* dbuf;       // D [B*H*n]
   float* part_q;     // [B*H*ngt*nseg][64][d] dQ of the global query rows
-  float* part_kv;    // [periods*nct_g*nseg][2][64][d] dK, dV of key class tiles
+  float* part_kv;    // [periods*nct_g*cnseg][2][64][d] dK, dV of key class tiles
                      // holding global keys
   const int32_t* gtok;         // [ng]
   const int32_t* gidx;         // [n]
   const uint64_t* tile_gmask;  // [nt]
   const LfTileRef* ct;         // [nct]: class tiles without global keys, then those with
-  int heads, n, nt, ng, ngt, nseg;
+  int heads, n, nt, ng, ngt;
+  int nseg, rseg;   // global query rows: nseg segments of rseg key tiles
+  int cnseg;        // columns holding global keys: cnseg segments of kLfSeg query tiles
   int nct, nct_plain, nct_g, ph;   // class tiles (all / without / with global keys), heads
                                    // per head period
   LfWindow win;                    // key range of each row, in class indices
@@ -120,8 +122,8 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
   const int p = band ? cls + stride * i : global_token(a.gtok, a.ng, gt, xq);
 
   // key tiles: band items walk the window's class tiles [lo_u, hi_u], then the
-  // global tiles with an eligible key; global items walk the kLfSeg natural tiles
-  // of their segment
+  // global tiles with an eligible key; global items walk the rseg natural tiles of
+  // their segment
   int lo_u = 0, hi_u = -1, ntile;
   int klo = 0, khi = -1;   // this row's window, in class indices (band items)
   if constexpr (kBand) {
@@ -129,8 +131,8 @@ __device__ __forceinline__ void lf_bwd_dq_item(const LfBwdArgs& a, int v, LdsTil
     a.win.keys(i, klo, khi);
     ntile = hi_u - lo_u + 1 + a.ngt;
   } else {
-    lo_u = seg * kLfSeg;
-    hi_u = min(a.nt, lo_u + kLfSeg) - 1;
+    lo_u = seg * a.rseg;
+    hi_u = min(a.nt, lo_u + a.rseg) - 1;
     ntile = hi_u - lo_u + 1;
   }
   const int nband = hi_u - lo_u + 1;
@@ -336,12 +338,13 @@ template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void lf_bwd_dq_kernel(LfBwdArgs a) {
   __shared__ __attribute__((aligned(16))) LdsTileT<D> sK[2];
   __shared__ __attribute__((aligned(16))) LdsTileT<D> sV[2];
-  const int v = xcd_remap_two(blockIdx.x, a.dq_band_items, a.dq_items - a.dq_band_items);
+  const int gitems = a.dq_items - a.dq_band_items;   // global-row segments first
+  const int v = xcd_remap_two(blockIdx.x, gitems, a.dq_band_items);
   if (v < 0) return;
-  if (v < a.dq_band_items)
-    lf_bwd_dq_item<D, true>(a, v, sK, sV);
+  if (v < gitems)
+    lf_bwd_dq_item<D, false>(a, v, sK, sV);
   else
-    lf_bwd_dq_item<D, false>(a, v - a.dq_band_items, sK, sV);
+    lf_bwd_dq_item<D, true>(a, v - gitems, sK, sV);
 }
 
 // ---------------------------------------------------------------------------
@@ -373,11 +376,11 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
       per = v / a.nct_plain;
       ref = a.ct[v - per * a.nct_plain];
     } else {
-      const int per_p = a.nct_g * a.nseg;
+      const int per_p = a.nct_g * a.cnseg;
       per = v / per_p;
       const int rem = v - per * per_p;
-      gki = rem / a.nseg;
-      seg = rem - gki * a.nseg;
+      gki = rem / a.cnseg;
+      seg = rem - gki * a.cnseg;
       ref = a.ct[a.nct_plain + gki];
     }
     bh = per * a.ph + ref.h;
@@ -638,7 +641,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
       for (int t = 0; t < kT; ++t) *reinterpret_cast<u32x2*>(vp + 32 * t + 8 * j) = vw[t];
     }
   } else {
-    const size_t slot = ((size_t)per * a.nct_g + gki) * a.nseg + seg;
+    const size_t slot = ((size_t)per * a.nct_g + gki) * a.cnseg + seg;
     float* pk = a.part_kv + slot * 2 * kTileOf<D> + kx * D + 4 * hl;
     float* pv = pk + kTileOf<D>;
 #pragma unroll
@@ -729,13 +732,13 @@ __global__ __launch_bounds__(256) void lf_bwd_reduce_kernel(LfBwdArgs a, int nq_
       const int ci = e.t * kBlock + row;      // class index of this row
       if (ci >= e.nc) continue;
       const int bh = per * a.ph + e.h;
-      src = a.part_kv + (size_t)idx * a.nseg * 2 * kTileOf<D> + kind * kTileOf<D> + e0;
+      src = a.part_kv + (size_t)idx * a.cnseg * 2 * kTileOf<D> + kind * kTileOf<D> + e0;
       stride = 2 * kTileOf<D>;
       dst = (kind == 0 ? a.dk : a.dv) + ((size_t)bh * a.n + e.c + (size_t)e.s * ci) * D +
             (e0 % D);
     }
     float acc[16];
-    sum_partials(src, stride, a.nseg, acc);
+    sum_partials(src, stride, (int)blockIdx.x < nq_groups ? a.nseg : a.cnseg, acc);
     store16_bf16(dst, acc, 1.f);
   }
 }
@@ -752,7 +755,7 @@ LfBwdWs lf_bwd_ws_layout(const lfattn_plan* P, int batch, int heads, int d) {
   LfBwdWs w;
   w.dbuf = 0;
   w.part_q = up(bh * P->n * sizeof(float));
-  w.part_kv = up(w.part_q + bh * P->ngt * P->nseg * tile * sizeof(float));
+  w.part_kv = up(w.part_q + bh * P->ngt * lf_row_seg(P, batch, heads).nseg * tile * sizeof(float));
   w.total = up(w.part_kv + periods * (P->nct - P->nct_plain) * P->nseg * 2 * tile *
                                sizeof(float));
   return w;
@@ -826,7 +829,8 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   a.gtok = P->d_gtok; a.gidx = P->d_gidx; a.tile_gmask = P->d_tile_gmask;
   a.ct = P->d_ct;
   a.heads = heads; a.n = P->n; a.nt = P->nt; a.ng = P->ng; a.ngt = P->ngt;
-  a.nseg = P->nseg;
+  const LfRowSeg rs = lf_row_seg(P, batch, heads);
+  a.nseg = rs.nseg; a.rseg = rs.seg; a.cnseg = P->nseg;
   a.nct = P->nct; a.nct_plain = P->nct_plain; a.nct_g = P->nct - P->nct_plain;
   a.ph = P->heads > 0 ? P->heads : 1;
   a.win = lf_window(P);
@@ -836,7 +840,7 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   const int bhn = batch * heads;
   const int periods = bhn / a.ph;
   a.dq_band_items = periods * a.nct;
-  a.dq_items = a.dq_band_items + bhn * P->ngt * P->nseg;
+  a.dq_items = a.dq_band_items + bhn * P->ngt * a.nseg;
   a.kv_plain_items = periods * a.nct_plain;
   a.kv_items = a.kv_plain_items + (a.gproj ? bhn * P->nt : 0);
   a.kv_seg_items = periods * a.nct_g * P->nseg;

@@ -50,7 +50,7 @@ struct LfArgs {
   const int32_t* gidx;  // [n]
   const uint64_t* tile_gmask;  // [nt] bit x set iff token 64u+x is global
   const LfTileRef* ct;  // [nct] class tiles of one head period
-  int heads, n, nt, ng, ngt, nseg;
+  int heads, n, nt, ng, ngt, nseg, rseg;   // global rows: nseg segments of rseg tiles
   int nct, ph;          // class tiles and heads per head period
   LfWindow win;         // key range of each row, in class indices
   int band_items, total_items;
@@ -209,8 +209,8 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTileT<
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) qB[c] = ld16(qp + 16 * c);
   }
-  const int u_begin = s * kLfSeg;
-  const int u_end = min(a.nt, u_begin + kLfSeg);
+  const int u_begin = s * a.rseg;
+  const int u_end = min(a.nt, u_begin + a.rseg);
   FwdStateT<D> st;
   fwd_state_init(st);
   TileRegsT<D> kr, vr;
@@ -245,19 +245,20 @@ __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTileT<
   write_partial(st, l_tot, lb_tot, hl, qr, a.part + (size_t)v * kPartFloatsOf<D>);
 }
 
-// Band items first, then the global-row segments (about as long as a band item), each
-// kind spread over all XCDs.  D = 128 takes more than half the registers: one wave
-// per SIMD.
+// The global-row segments first (up to the average work of a work-group slot), then
+// the band items, each kind spread over all XCDs.  D = 128 takes more than half the
+// registers: one wave per SIMD.
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void lf_attn_kernel(LfArgs a) {
   __shared__ __attribute__((aligned(16))) LdsTileT<D> sK[2];
   __shared__ __attribute__((aligned(16))) LdsTileT<D> sV[2];
-  const int v = xcd_remap_two(blockIdx.x, a.band_items, a.total_items - a.band_items);
+  const int gitems = a.total_items - a.band_items;
+  const int v = xcd_remap_two(blockIdx.x, gitems, a.band_items);
   if (v < 0) return;
-  if (v < a.band_items)
-    lf_band_item<D>(a, v, sK, sV);
+  if (v < gitems)
+    lf_global_item<D>(a, v, sK, sV);
   else
-    lf_global_item<D>(a, v - a.band_items, sK, sV);
+    lf_band_item<D>(a, v - gitems, sK, sV);
 }
 
 // Thread t: global row t / 4 of the tile, columns 16 (t % 4) + 64 u .. +15.
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256) void lf_combine_kernel(LfArgs a) {
 size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads, int d) {
   if (P->ng == 0) return 0;
   const size_t rec = d == 128 ? kPartFloatsOf<128> : kPartFloatsOf<kHead>;
-  return (size_t)batch * heads * P->ngt * P->nseg * rec * sizeof(float);
+  return (size_t)batch * heads * P->ngt * lf_row_seg(P, batch, heads).nseg * rec * sizeof(float);
 }
 
 int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, int d, float scale, const void* q,
@@ -305,14 +306,15 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   a.gtok = P->d_gtok; a.gidx = P->d_gidx; a.tile_gmask = P->d_tile_gmask;
   a.ct = P->d_ct;
   a.heads = heads; a.n = P->n; a.nt = P->nt; a.ng = P->ng; a.ngt = P->ngt;
-  a.nseg = P->nseg;
+  const LfRowSeg rs = lf_row_seg(P, batch, heads);
+  a.nseg = rs.nseg; a.rseg = rs.seg;
   a.nct = P->nct;
   a.ph = P->heads > 0 ? P->heads : 1;
   a.win = lf_window(P);
   a.sl2 = scale * kLog2e;
   const int bhn = batch * heads;
   a.band_items = bhn / a.ph * P->nct;
-  a.total_items = a.band_items + (has_g ? bhn * P->ngt * P->nseg : 0);
+  a.total_items = a.band_items + (has_g ? bhn * P->ngt * a.nseg : 0);
   int st;
   {
     ProfScope prof_(d == 128 ? "lf_attn_d128" : "lf_attn", stream);

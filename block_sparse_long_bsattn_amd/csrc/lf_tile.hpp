@@ -15,10 +15,35 @@
 // tensors (d = 64, or 128 for the instances that take it).
 #pragma once
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace bsattn {
+
+// Segments of the global query rows (a global token attends to every token), per
+// call: seg key tiles each, the largest power of two in kLfSeg..64 within the average
+// work of one work-group slot (four per compute unit).  The segments run first on each
+// XCD and so end within the run, while longer segments write and merge fewer fp32
+// partials.  The work counted: every band item's window tiles and global tiles, and
+// the global rows' tiles.
+struct LfRowSeg {
+  int seg, nseg;
+};
+
+inline LfRowSeg lf_row_seg(const lfattn_plan* P, int batch, int heads) {
+  const int64_t bhn = (int64_t)batch * heads;
+  const int64_t band_items = bhn / (P->heads > 0 ? P->heads : 1) * P->nct;
+  const int64_t span = P->wb > 0 ? (int64_t)(2 * P->whalf + 1) * P->wb
+                                 : (P->causal ? P->w1 + 1 : 2 * (int64_t)P->w1 + 1);
+  const int64_t band_tiles = std::min<int64_t>(P->nt, (span + kBlock - 1) / kBlock + 1);
+  const int64_t work = band_items * (band_tiles + P->ngt) + bhn * P->ngt * P->nt;
+  const int64_t avg = work / (4 * (int64_t)(P->cus > 0 ? P->cus : 1));
+  int seg = kLfSeg;
+  while (seg < 64 && 2 * seg <= avg) seg *= 2;
+  return LfRowSeg{seg, (P->nt + seg - 1) / seg};
+}
 
 // Two lists, n1 items and then n2: each XCD runs its eighth of the first list and
 // then its eighth of the second, so that both kinds of item spread over all eight
