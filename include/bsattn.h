@@ -287,7 +287,9 @@ int lfattn_plan_build_dilated(int n, int window_one_side, const int32_t* global_
  * hipFree).  NULL is accepted. */
 int lfattn_plan_destroy(lfattn_plan* plan);
 
-/* Workspace bytes lfattn_fwd needs (d = 64 or 128).  0 for invalid arguments. */
+/* Workspace bytes lfattn_fwd needs (d = 64 or 128).  0 for invalid arguments.  The
+ * size depends on batch and heads (the global rows are cut into segments sized from
+ * the whole call's work), so query it with the values the call will use. */
 size_t lfattn_fwd_workspace(const lfattn_plan* plan, int batch, int heads, int d);
 
 /*
@@ -302,7 +304,8 @@ int lfattn_fwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtyp
                float scale, const void* q, const void* k, const void* v, void* o,
                float* lse, void* o_lo, void* workspace, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes lfattn_bwd needs (d = 64 or 128).  0 for invalid arguments. */
+/* Workspace bytes lfattn_bwd needs (d = 64 or 128).  0 for invalid arguments.  Like
+ * lfattn_fwd_workspace, it depends on batch and heads. */
 size_t lfattn_bwd_workspace(const lfattn_plan* plan, int batch, int heads, int d);
 
 /*
