@@ -83,6 +83,50 @@ def test_lf_bwd_full_size_sampled():
     assert worst <= BF16_TOL and same
 
 
+def test_lf_long_row_segments():
+    """Batch 4, 12 heads, n = 4096, 256 per side, global tokens 0..63: enough work per
+    work-group slot that the global rows run in segments of 32 key tiles (two per row,
+    read off the forward's workspace size) instead of 8.  Forward and backward of two
+    (batch, head) slices compared in full with the oracle."""
+    n, heads, bsz, w1, G = 4096, 12, 4, 256, list(range(64))
+    plan = B.lfattn_plan_build(n, w1, G)
+    try:
+        rec = 64 * 64 + 3 * 64    # floats of one partial record of a 64-row global tile
+        nseg = B.lfattn_fwd_workspace(plan, bsz, heads) // (bsz * heads * 1 * rec * 4)
+    finally:
+        B.lfattn_plan_destroy(plan)
+    say(f"lf long row segments n={n} H={heads} B={bsz}: {nseg} segments per global row")
+    assert nseg == 2
+    (q, k, v, do), refs = qkv((bsz, heads, n, 64), "bf16",
+                             (I.SEED_Q, I.SEED_K, I.SEED_V, I.SEED_DO))
+    plan = B.lfattn_plan_build(n, w1, G)
+    try:
+        o = torch.empty_like(q)
+        lse = torch.empty((bsz, heads, n), dtype=torch.float32, device="cuda")
+        wsf = torch.empty(B.lfattn_fwd_workspace(plan, bsz, heads), dtype=torch.uint8,
+                          device="cuda")
+        wsb = torch.empty(B.lfattn_bwd_workspace(plan, bsz, heads), dtype=torch.uint8,
+                          device="cuda")
+        B.lfattn_fwd(plan, q, k, v, o, lse, wsf)
+        grads = [torch.empty_like(q) for _ in range(3)]
+        B.lfattn_bwd(plan, q, k, v, o, lse, do, *grads, wsb)
+        torch.cuda.synchronize()
+    finally:
+        B.lfattn_plan_destroy(plan)
+    got = [to_f64(t) for t in [o, lse] + grads]
+    qr, kr, vr, dor = refs
+    mask = OLF.longformer_mask(n, w1, G)
+    worst = 0.0
+    for b, h in ((0, 5), (3, 11)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ro, rl = OA.attention_fwd(qr[sl], kr[sl], vr[sl], mask, 1 / 8.0)
+        rg = OA.attention_bwd(qr[sl], kr[sl], vr[sl], dor[sl], mask, 1 / 8.0, row_chunk=1024)
+        for a, r in zip(got, (ro, rl) + tuple(rg)):
+            worst = max(worst, max_abs(a[sl], r))
+    say(f"   worst max-abs {worst:.3e}")
+    assert worst <= BF16_TOL
+
+
 def test_lf_bwd_sum_identities():
     """Rows of P sum to one and rows of dS to zero, so per (batch, head) the dV rows
     sum to the dO rows and the dK rows sum to zero (bf16 outputs: loose bound)."""
