@@ -615,7 +615,7 @@ __global__ __launch_bounds__(kBuildThreads) void layout_head_kernel(
     }
     pos += len;
   }
-  if (h == gridDim.x - 1 && tid == kBuildThreads - 1)
+  if (h == (int)gridDim.x - 1 && tid == kBuildThreads - 1)
     csc_ptr[(int64_t)gridDim.x * nb] = (int32_t)((int64_t)gridDim.x * nnz_per_head);
   __syncthreads();
 
@@ -694,7 +694,7 @@ __global__ __launch_bounds__(kBuildThreads) void layout_cols_kernel(
     write_col(G, nb, w, j, hb + (int64_t)j * wpc, wpc, csc_idx + pos);
     pos += len;
   }
-  if (h == gridDim.x - 1 && tid == kBuildThreads - 1)
+  if (h == (int)gridDim.x - 1 && tid == kBuildThreads - 1)
     csc_ptr[(int64_t)gridDim.x * nb] = (int32_t)((int64_t)gridDim.x * nnz_per_head);
 }
 
