@@ -18,8 +18,9 @@
 //                  (rows gathered by index), as in the forward; writes dQ and D
 //                  for its non-global rows (rowsum(dO * O) corrected by the row
 //                  sum of dS: sum P * dP with the recomputed probabilities);
-//                * a segment of kLfSeg key tiles for a tile of global query rows
-//                  (full rows): writes D (first segment) and an fp32 partial dQ.
+//                * a segment of rseg key tiles (as in the forward) for a tile of
+//                  global query rows (full rows): writes D (first segment) and an
+//                  fp32 partial dQ.
 //   lf_bwd_dkdv  column-owned, two kinds of item:
 //                * a 64-key class tile holding no global key: the query tiles of
 //                  its class within the window, then the global query rows

@@ -18,7 +18,8 @@
 //                 Only tiles the window cuts need an element mask; keys that are
 //                 global are allowed in every tile.  Rows of global tokens and
 //                 rows past the class's end are not written.
-//               * a segment of kLfSeg key tiles for a tile of global query rows
+//               * a segment of key tiles (8 to 64, sized per call from the work
+//                 per work-group slot) for a tile of global query rows
 //                 (a global token attends to every token), query rows gathered by
 //                 index, writing a partial record.  With separate global
 //                 projections (§3.1 "Linear Projections for Global Attention") these
@@ -190,7 +191,7 @@ __device__ __forceinline__ void lf_band_item(const LfArgs& a, int v, LdsTileT<D>
                  a.lse != nullptr ? a.lse + (size_t)bh * a.n + p : nullptr);
 }
 
-// Item v of the global rows: (bh, global tile gt, segment s of kLfSeg key tiles).
+// Item v of the global rows: (bh, global tile gt, segment s of rseg key tiles).
 template <int D>
 __device__ __forceinline__ void lf_global_item(const LfArgs& a, int v, LdsTileT<D>* sK,
                                                LdsTileT<D>* sV) {
