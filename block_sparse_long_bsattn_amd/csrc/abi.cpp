@@ -569,7 +569,6 @@ int lf_plan_build(int n, int window_one_side, const int32_t* global_tokens, int 
   P->ng = n_global;
   P->nt = (n + kBlock - 1) / kBlock;
   P->ngt = (n_global + kBlock - 1) / kBlock;
-  P->nseg = (P->nt + kLfSeg - 1) / kLfSeg;
   P->heads = heads;
   P->causal = causal;
   P->wb = bw.wb;

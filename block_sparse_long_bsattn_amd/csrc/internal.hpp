@@ -64,7 +64,6 @@ struct lfattn_plan {
   int wb = 0, woff = 0, whalf = 0;   // blocked window: block size (0: sliding window),
                                      // first ordinary token, (w - 1) / 2
   int device = 0;
-  int nseg = 1;                  // kLfSeg-tile segments of a full column holding global keys
   int cus = 256;                 // compute units of the device (sizes the row segments)
   int nct = 0;                   // class tiles per head period (all heads, or one)
   int nct_plain = 0;             // ... of them holding no global key (listed first)

@@ -25,9 +25,9 @@
 //                * a 64-key class tile holding no global key: the query tiles of
 //                  its class within the window, then the global query rows
 //                  outside them (gathered);
-//                * a segment of kLfSeg natural query tiles for a key class tile
-//                  holding global keys (their columns are full): fp32 partial
-//                  dK, dV.
+//                * a segment of cseg natural query tiles (sized per call) for a key
+//                  class tile holding global keys (their columns are full): fp32
+//                  partial dK, dV.
 //   lf_bwd_reduce  sums the partials in segment order and writes dQ of the
 //                global rows and dK, dV of the key class tiles holding global keys.
 
@@ -72,7 +72,7 @@ struct LfBwdArgs {
   const LfTileRef* ct;         // [nct]: class tiles without global keys, then those with
   int heads, n, nt, ng, ngt;
   int nseg, rseg;   // global query rows: nseg segments of rseg key tiles
-  int cnseg;        // columns holding global keys: cnseg segments of kLfSeg query tiles
+  int cnseg, cseg;  // columns holding global keys: cnseg segments of cseg query tiles
   int nct, nct_plain, nct_g, ph;   // class tiles (all / without / with global keys), heads
                                    // per head period
   LfWindow win;                    // key range of each row, in class indices
@@ -402,7 +402,7 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
 
   // query tiles: plain items walk the window's class tiles [lo, hi] of the key's
   // class, then the global tiles with an eligible row (none with separate global
-  // projections: those rows are the global-row items'); segment items walk kLfSeg
+  // projections: those rows are the global-row items'); segment items walk cseg
   // natural tiles (the column of a global key is full); global-row items walk the
   // global tiles only
   int lo, hi, ntile;
@@ -416,8 +416,8 @@ __device__ __forceinline__ void lf_bwd_dkdv_item(const LfBwdArgs& a, int v, LdsT
     ntile = a.ngt;
   } else {
     qc = 0; qs = 1; qnc = a.n;
-    lo = seg * kLfSeg;
-    hi = min(a.nt, lo + kLfSeg) - 1;
+    lo = seg * a.cseg;
+    hi = min(a.nt, lo + a.cseg) - 1;
     ntile = hi - lo + 1;
   }
   const int nband = hi - lo + 1;
@@ -756,9 +756,10 @@ LfBwdWs lf_bwd_ws_layout(const lfattn_plan* P, int batch, int heads, int d) {
   LfBwdWs w;
   w.dbuf = 0;
   w.part_q = up(bh * P->n * sizeof(float));
-  w.part_kv = up(w.part_q + bh * P->ngt * lf_row_seg(P, batch, heads).nseg * tile * sizeof(float));
-  w.total = up(w.part_kv + periods * (P->nct - P->nct_plain) * P->nseg * 2 * tile *
-                               sizeof(float));
+  const size_t rows = bh * P->ngt * lf_row_seg(P, batch, heads).nseg;
+  const size_t cols = periods * (P->nct - P->nct_plain) * lf_col_seg(P, batch, heads).nseg;
+  w.part_kv = up(w.part_q + rows * tile * sizeof(float));
+  w.total = up(w.part_kv + cols * 2 * tile * sizeof(float));
   return w;
 }
 
@@ -831,7 +832,8 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   a.ct = P->d_ct;
   a.heads = heads; a.n = P->n; a.nt = P->nt; a.ng = P->ng; a.ngt = P->ngt;
   const LfRowSeg rs = lf_row_seg(P, batch, heads);
-  a.nseg = rs.nseg; a.rseg = rs.seg; a.cnseg = P->nseg;
+  const LfRowSeg cs = lf_col_seg(P, batch, heads);
+  a.nseg = rs.nseg; a.rseg = rs.seg; a.cnseg = cs.nseg; a.cseg = cs.seg;
   a.nct = P->nct; a.nct_plain = P->nct_plain; a.nct_g = P->nct - P->nct_plain;
   a.ph = P->heads > 0 ? P->heads : 1;
   a.win = lf_window(P);
@@ -844,7 +846,7 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   a.dq_items = a.dq_band_items + bhn * P->ngt * a.nseg;
   a.kv_plain_items = periods * a.nct_plain;
   a.kv_items = a.kv_plain_items + (a.gproj ? bhn * P->nt : 0);
-  a.kv_seg_items = periods * a.nct_g * P->nseg;
+  a.kv_seg_items = periods * a.nct_g * a.cnseg;
   return d == 128 ? launch_lf_bwd_d<128>(a, P, bhn, periods, stream)
                   : launch_lf_bwd_d<kHead>(a, P, bhn, periods, stream);
 }

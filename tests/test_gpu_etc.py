@@ -87,6 +87,31 @@ def test_etc_full_size(cfg):
     assert worst <= BF16_TOL and same
 
 
+def test_etc_base_batch4_long_segments():
+    """BigBird-etc base at batch 4 (the benchmark shape): enough work per work-group
+    slot that the global rows run in segments of 32 key tiles and the columns of the
+    global keys in segments of 16 query tiles (read off the backward's workspace
+    size); two (batch, head) slices compared in full with the oracle."""
+    g, n, b, w, heads, bsz = 256, 4096, 84, 3, 12, 4
+    N, nt, tile = g + n, (g + n + 63) // 64, 64 * 64 * 4
+    plan = B.lfattn_plan_build_etc(g, n, b, w)
+    try:
+        ws = B.lfattn_bwd_workspace(plan, bsz, heads)
+    finally:
+        B.lfattn_plan_destroy(plan)
+    up = lambda x: (x + 255) // 256 * 256
+    rows, cols = bsz * heads * 4 * -(-nt // 32), bsz * heads * 4 * -(-nt // 16)
+    assert ws == up(up(up(bsz * heads * N * 4) + rows * tile) + cols * 2 * tile)
+    say(f"etc base batch 4: row segments of 32 tiles, column segments of 16 (workspace {ws})")
+    refs, got, same = run(B.lfattn_plan_build_etc(g, n, b, w), N, heads, bsz)
+    worst = 0.0
+    for bi, h in ((0, 0), (3, 11)):
+        sl = (slice(bi, bi + 1), slice(None))
+        worst = max(worst, compare([x[sl] for x in refs], [x[sl] for x in got],
+                                   OE.etc_mask(g, n, b, w), heads=(h, h + 1)))
+    assert worst <= BF16_TOL and same
+
+
 @pytest.mark.parametrize("case", [
     (1000, 70, [3, 999], [0], False),      # sliding window, ends 40 tokens into a tile
     (700, 33, [], [0, 2], True),           # causal, dilated, ragged
