@@ -831,8 +831,8 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   a.gtok = P->d_gtok; a.gidx = P->d_gidx; a.tile_gmask = P->d_tile_gmask;
   a.ct = P->d_ct;
   a.heads = heads; a.n = P->n; a.nt = P->nt; a.ng = P->ng; a.ngt = P->ngt;
-  const LfRowSeg rs = lf_row_seg(P, batch, heads);
-  const LfRowSeg cs = lf_col_seg(P, batch, heads);
+  const LfSeg rs = lf_row_seg(P, batch, heads);
+  const LfSeg cs = lf_col_seg(P, batch, heads);
   a.nseg = rs.nseg; a.rseg = rs.seg; a.cnseg = cs.nseg; a.cseg = cs.seg;
   a.nct = P->nct; a.nct_plain = P->nct_plain; a.nct_g = P->nct - P->nct_plain;
   a.ph = P->heads > 0 ? P->heads : 1;

@@ -28,11 +28,11 @@ namespace bsattn {
 // XCD and so end within the run, while longer segments write and merge fewer fp32
 // partials.  The work counted: every band item's window tiles and global tiles, and
 // the global rows' tiles.
-struct LfRowSeg {
+struct LfSeg {
   int seg, nseg;
 };
 
-inline LfRowSeg lf_row_seg(const lfattn_plan* P, int batch, int heads) {
+inline LfSeg lf_row_seg(const lfattn_plan* P, int batch, int heads) {
   const int64_t bhn = (int64_t)batch * heads;
   const int64_t band_items = bhn / (P->heads > 0 ? P->heads : 1) * P->nct;
   const int64_t span = P->wb > 0 ? (int64_t)(2 * P->whalf + 1) * P->wb
@@ -42,21 +42,21 @@ inline LfRowSeg lf_row_seg(const lfattn_plan* P, int batch, int heads) {
   const int64_t avg = work / (4 * (int64_t)(P->cus > 0 ? P->cus : 1));
   int seg = kLfSeg;
   while (seg < 64 && 2 * seg <= avg) seg *= 2;
-  return LfRowSeg{seg, (P->nt + seg - 1) / seg};
+  return LfSeg{seg, (P->nt + seg - 1) / seg};
 }
 
 // Segments of the columns of the key tiles holding global keys (every query tile
 // sees a global key), per call: seg query tiles each, the smallest power of two in
 // kLfSeg..64 above the average of those columns' tiles per work-group slot, and at
-// most half a column.  They run in a kernel of their own, so longer segments only
-// cost when that kernel has fewer items than slots; they halve the fp32 partials.
-inline LfRowSeg lf_col_seg(const lfattn_plan* P, int batch, int heads) {
+// most half a column.  They run in a kernel of their own; longer segments write and
+// sum fewer fp32 partials.
+inline LfSeg lf_col_seg(const lfattn_plan* P, int batch, int heads) {
   const int64_t periods = (int64_t)batch * heads / (P->heads > 0 ? P->heads : 1);
   const int64_t work = periods * (P->nct - P->nct_plain) * P->nt;
   const int64_t avg = work / (4 * (int64_t)(P->cus > 0 ? P->cus : 1));
   int seg = kLfSeg;
   while (seg < 64 && seg <= avg && 2 * seg < P->nt) seg *= 2;
-  return LfRowSeg{seg, (P->nt + seg - 1) / seg};
+  return LfSeg{seg, (P->nt + seg - 1) / seg};
 }
 
 // Two lists, n1 items and then n2: each XCD runs its eighth of the first list and
