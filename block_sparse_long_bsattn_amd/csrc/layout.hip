@@ -226,10 +226,7 @@ __device__ void draw_any(const RowCtx<GS>& c, int m, int take, uint64_t seed, ui
 template <typename GS>
 __device__ void build_row(const GS& G, int nb, int w, int r, uint64_t seed, int h, int i,
                           int32_t* out, uint32_t* hb, int wpc) {
-  if (G.contains(i)) {
-    for (int j = 0; j < nb; ++j) out[j] = j;
-    return;
-  }
+  if (G.contains(i)) return;   // a global row lists every block: written by layout_cols
   const RowCtx<GS> c = row_ctx(G, nb, w, i);
   const int m = nb - c.excl_size();
   const int take = r < m ? r : m;
@@ -280,12 +277,12 @@ __device__ int col_length(const GS& G, int nb, int w, int j, const uint32_t* bit
   return n;
 }
 
+// A non-global column (global columns list every block and are written by the whole
+// work-group).
 template <typename GS>
 __device__ void write_col(const GS& G, int nb, int w, int j, uint32_t* bits, int wpc,
                           int32_t* out) {
-  if (G.contains(j)) {
-    for (int i = 0; i < nb; ++i) out[i] = i;
-  } else {
+  {
     const RowCtx<GS> c = row_ctx(G, nb, w, j);
     // random rows below x, from the bitmap
     auto rnd_below = [&](int x) -> int {
@@ -327,7 +324,7 @@ __device__ __forceinline__ int wave_exclusive_scan(int v) {
   return x - v;
 }
 
-// exclusive scan of v over the work-group (kBuildThreads threads); `part` holds
+// exclusive scan of v over the work-group (any multiple of 64 threads); `part` holds
 // one int per wave.  Returns the exclusive prefix.
 __device__ int block_exclusive_scan(int v, int* part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -672,30 +669,47 @@ __global__ __launch_bounds__(64) void layout_rows_kernel(
   build_row(G, nb, w, r, seed, h, i, col_idx + row_ptr[idx], rbits + (int64_t)h * nb * wpc, wpc);
 }
 
-// Larger layouts, phase 2: one work-group per head; clears the bitmap.
+// Larger layouts, phase 2: one work-group of kColThreads per head (a column per
+// thread up to 1024 blocks); clears the bitmap.  The lists of the global rows and
+// columns (every block) are written last by the whole work-group.
+constexpr int kColThreads = 1024;
+
 template <typename GS>
-__global__ __launch_bounds__(kBuildThreads) void layout_cols_kernel(
+__global__ __launch_bounds__(kColThreads) void layout_cols_kernel(
     const int32_t* __restrict__ Gglob, int g, int nb, int w, int64_t nnz_per_head,
-    uint32_t* __restrict__ rbits, int wpc, int32_t* __restrict__ csc_ptr,
+    uint32_t* __restrict__ rbits, int wpc, const int32_t* __restrict__ row_ptr,
+    int32_t* __restrict__ col_idx, int32_t* __restrict__ csc_ptr,
     int32_t* __restrict__ csc_idx) {
-  extern __shared__ int32_t sG[];
-  __shared__ int part[kBuildThreads / 64];
+  extern __shared__ int32_t sG[];   // [g] global blocks (GLds), then [g] their column offsets
+  int32_t* sGpos = sG + g;
+  __shared__ int part[kColThreads / 64];
   const int h = blockIdx.x, tid = threadIdx.x;
   const GS G = load_gset<GS>(Gglob, g, sG);
   uint32_t* hb = rbits + (int64_t)h * nb * wpc;
-  const int per = (nb + kBuildThreads - 1) / kBuildThreads;
+  const int per = (nb + kColThreads - 1) / kColThreads;
   const int j0 = min(nb, tid * per), j1 = min(nb, j0 + per);
   int local = 0;
   for (int j = j0; j < j1; ++j) local += col_length(G, nb, w, j, hb + (int64_t)j * wpc, wpc);
-  int64_t pos = (int64_t)h * nnz_per_head + block_exclusive_scan(local, part);
+  int pos = block_exclusive_scan(local, part);   // offset within the head
+  const int64_t head0 = (int64_t)h * nnz_per_head;
   for (int j = j0; j < j1; ++j) {
-    csc_ptr[(int64_t)h * nb + j] = (int32_t)pos;
+    csc_ptr[(int64_t)h * nb + j] = (int32_t)(head0 + pos);
     const int len = col_length(G, nb, w, j, hb + (int64_t)j * wpc, wpc);
-    write_col(G, nb, w, j, hb + (int64_t)j * wpc, wpc, csc_idx + pos);
+    if (G.contains(j))
+      sGpos[G.count_le(j) - 1] = pos;
+    else
+      write_col(G, nb, w, j, hb + (int64_t)j * wpc, wpc, csc_idx + head0 + pos);
     pos += len;
   }
-  if (h == (int)gridDim.x - 1 && tid == kBuildThreads - 1)
+  if (h == (int)gridDim.x - 1 && tid == kColThreads - 1)
     csc_ptr[(int64_t)gridDim.x * nb] = (int32_t)((int64_t)gridDim.x * nnz_per_head);
+  __syncthreads();
+  for (int e = tid; e < g * nb; e += kColThreads) {
+    const int a = e / nb, j = e - a * nb;
+    const int x = Gglob[a];
+    col_idx[row_ptr[(int64_t)h * nb + x] + j] = j;
+    csc_idx[head0 + sGpos[a] + j] = j;
+  }
 }
 
 }  // namespace
@@ -776,9 +790,9 @@ int launch_rows_cols(bsattn_layout* L, hipStream_t stream) {
   if (st) return st;
   {
     ProfScope prof_("layout_cols", stream);
-    hipLaunchKernelGGL(layout_cols_kernel<GS>, dim3(L->heads), dim3(kBuildThreads), g_lds,
+    hipLaunchKernelGGL(layout_cols_kernel<GS>, dim3(L->heads), dim3(kColThreads), 2 * g_lds,
                        stream, L->d_gblk, L->g, L->nb, L->w, L->nnz_per_head, L->d_rbits, wpc,
-                       L->d_csc_ptr, L->d_csc_idx);
+                       L->d_row_ptr, L->d_col_idx, L->d_csc_ptr, L->d_csc_idx);
   }
   st = check_hip(hipGetLastError(), "layout_cols launch");
   const int ng = L->nb - L->g;
