@@ -317,14 +317,14 @@ int bsattn_layout_build(int n, int b, int heads, const int32_t* global_blocks, i
       (st = dev_alloc(&L->d_col_idx, (size_t)(nnz * heads))) ||
       (st = dev_alloc(&L->d_csc_ptr, (size_t)heads * nb + 1)) ||
       (st = dev_alloc(&L->d_csc_idx, (size_t)(nnz * heads))) ||
-      (st = dev_alloc(&L->d_rbits, (size_t)heads * nb * ((nb + 31) / 32))) ||
+      (st = dev_alloc(&L->d_rbits, (size_t)heads * nb * ((nb + 31) / 32 + 1))) ||
       (st = dev_alloc(&L->d_kv_order, (size_t)heads * ng.size())) ||
       (st = dev_alloc(&L->d_row_info, (size_t)heads * ng.size() * 4)) ||
       (st = dev_alloc(&L->d_col_info, (size_t)heads * ng.size() * 4))) {
     free_layout(L);
     return st;
   }
-  if ((st = check_hip(hipMemsetAsync(L->d_rbits, 0, (size_t)heads * nb * ((nb + 31) / 32) * 4, stream),
+  if ((st = check_hip(hipMemsetAsync(L->d_rbits, 0, (size_t)heads * nb * ((nb + 31) / 32 + 1) * 4, stream),
                       "clear random-pick bitmap"))) {
     free_layout(L);
     return st;

@@ -26,7 +26,8 @@ struct bsattn_layout {
   int32_t* d_col_idx = nullptr;  // [heads*nnz_per_head]
   int32_t* d_csc_ptr = nullptr;  // [heads*nb + 1]
   int32_t* d_csc_idx = nullptr;  // [heads*nnz_per_head]
-  uint32_t* d_rbits = nullptr;   // [heads][nb][ceil(nb/32)] random picks, zero between builds
+  uint32_t* d_rbits = nullptr;   // [heads][nb][ceil(nb/32)] random picks, then [heads][nb]
+                                 // picks per column; zero between builds
   int32_t* d_kv_order = nullptr; // [heads][nb - g] non-global key blocks, longest column
                                  // first (the dK/dV work order; ascending until a build
                                  // kernel that sorts has run)

@@ -15,11 +15,13 @@
 //                 bitmaps in registers (row i = G | window | R_i; column j = G |
 //                 window | rows that drew j), the lists are their set bits in
 //                 ascending order, the column offsets a block scan.
-//   layout_rows + layout_cols (larger n/b): one thread per row, then one
-//                 work-group per head for the columns, with the random picks in a
-//                 global bitmap (cleared after use).  Row and column lists are
-//                 written by rank: the position of a block in the sorted union is
-//                 the number of union members below it.
+//   layout_rows + layout_cols + layout_info (larger n/b): one thread per row
+//                 (its list written by rank: the position of a block in the sorted
+//                 union is the number of union members below it), the random picks
+//                 in a global bitmap with a count per column; then a work-group per
+//                 64 columns (each column's list read off its bitmap words in one
+//                 pass); then the work records.  Bitmap and counts are cleared after
+//                 use; global rows and columns are written by whole work-groups.
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -225,7 +227,7 @@ __device__ void draw_any(const RowCtx<GS>& c, int m, int take, uint64_t seed, ui
 // column; atomics on LDS or global memory).
 template <typename GS>
 __device__ void build_row(const GS& G, int nb, int w, int r, uint64_t seed, int h, int i,
-                          int32_t* out, uint32_t* hb, int wpc) {
+                          int32_t* out, uint32_t* hb, int wpc, int32_t* hcnt) {
   if (G.contains(i)) return;   // a global row lists every block: written by layout_cols
   const RowCtx<GS> c = row_ctx(G, nb, w, i);
   const int m = nb - c.excl_size();
@@ -249,7 +251,10 @@ __device__ void build_row(const GS& G, int nb, int w, int r, uint64_t seed, int 
     write_row(c, take, cnt, at, out);
 #pragma unroll
     for (int t = 0; t < kFastR; ++t)
-      if (t < take) atomicOr(&hb[(int64_t)rnd[t] * wpc + (i >> 5)], 1u << (i & 31));
+      if (t < take) {
+        atomicOr(&hb[(int64_t)rnd[t] * wpc + (i >> 5)], 1u << (i & 31));
+        atomicAdd(&hcnt[rnd[t]], 1);
+      }
   } else {
     int rnd[kMaxR];
     draw_any(c, m, take, seed, k0, rnd);
@@ -260,55 +265,33 @@ __device__ void build_row(const GS& G, int nb, int w, int r, uint64_t seed, int 
     };
     auto at = [&](int t) { return rnd[t]; };
     write_row(c, take, cnt, at, out);
-    for (int t = 0; t < take; ++t) atomicOr(&hb[(int64_t)rnd[t] * wpc + (i >> 5)], 1u << (i & 31));
+    for (int t = 0; t < take; ++t) {
+      atomicOr(&hb[(int64_t)rnd[t] * wpc + (i >> 5)], 1u << (i & 31));
+      atomicAdd(&hcnt[rnd[t]], 1);
+    }
   }
 }
 
-// Column j.  The query blocks seeing key block j are all blocks when j is global,
-// otherwise the global blocks, the non-global blocks within the window of j, and
-// the blocks whose random draw picked j (bitmap bits); the three sets are
-// disjoint, so the list is written by rank like the rows.
-template <typename GS>
-__device__ int col_length(const GS& G, int nb, int w, int j, const uint32_t* bits, int wpc) {
-  if (G.contains(j)) return nb;
-  const RowCtx<GS> c = row_ctx(G, nb, w, j);
-  int n = G.g + c.win_below(c.hi + 1);
-  for (int x = 0; x < wpc; ++x) n += __popc(bits[x]);
-  return n;
-}
-
-// A non-global column (global columns list every block and are written by the whole
-// work-group).
-template <typename GS>
-__device__ void write_col(const GS& G, int nb, int w, int j, uint32_t* bits, int wpc,
-                          int32_t* out) {
-  {
-    const RowCtx<GS> c = row_ctx(G, nb, w, j);
-    // random rows below x, from the bitmap
-    auto rnd_below = [&](int x) -> int {
-      int n = 0;
-      const int wx = x >> 5;
-      for (int y = 0; y < wx && y < wpc; ++y) n += __popc(bits[y]);
-      if (wx < wpc && (x & 31)) n += __popc(bits[wx] & ((1u << (x & 31)) - 1u));
-      return n;
-    };
-    G.for_each([&](int a, int x) { out[a + c.win_below(x) + rnd_below(x)] = x; });
-    for (int x = c.lo; x <= c.hi; ++x) {
-      if (G.contains(x)) continue;
-      out[G.count_le(x - 1) + c.win_below(x) + rnd_below(x)] = x;
-    }
-    int t = 0;
-    for (int y = 0; y < wpc; ++y) {
-      uint32_t word = bits[y];
-      while (word) {
-        const int x = 32 * y + __builtin_ctz(word);
-        word &= word - 1u;
-        out[G.count_le(x - 1) + c.win_below(x) + t] = x;
-        ++t;
-      }
+// The list of a non-global column j (global columns list every block and are
+// written by the whole work-group): the set bits, in ascending order, of the union
+// of the global blocks (gbits), the window of j and the rows that drew j (bits),
+// three disjoint sets.  One pass over the column's words, which it also clears for
+// the next draw.
+__device__ __forceinline__ void write_col(const uint32_t* gbits, int nb, int w, int j,
+                                          uint32_t* bits, int wpc, int32_t* out) {
+  const int half = (w - 1) / 2;
+  const int lo = max(0, j - half), hi = min(nb - 1, j + half);
+  int q = 0;
+  for (int y = 0; y < wpc; ++y) {
+    const int a = max(lo - 32 * y, 0), b = min(hi - 32 * y, 31);
+    const uint32_t win = a > b ? 0u : (b == 31 ? ~0u : (2u << b) - 1u) & ~((1u << a) - 1u);
+    uint32_t word = bits[y] | gbits[y] | win;
+    bits[y] = 0u;
+    while (word) {
+      out[q++] = 32 * y + __builtin_ctz(word);
+      word &= word - 1u;
     }
   }
-  for (int y = 0; y < wpc; ++y) bits[y] = 0u;          // ready for the next draw
 }
 
 // exclusive scan of v within each wave (no work-group barrier): for values that
@@ -340,6 +323,18 @@ __device__ int block_exclusive_scan(int v, int* part) {
   for (int q = 0; q < wave; ++q) base += part[q];
   __syncthreads();
   return base + x - v;
+}
+
+// sum of v over the work-group (any multiple of 64 threads); `part` one int per wave
+__device__ int block_sum(int v, int* part) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+  for (int q = 0; q < (int)(blockDim.x >> 6); ++q) t += part[q];
+  __syncthreads();
+  return t;
 }
 
 template <typename GS>
@@ -660,56 +655,71 @@ template <typename GS>
 __global__ __launch_bounds__(64) void layout_rows_kernel(
     const int32_t* __restrict__ Gglob, int g, int nb, int w, int r, int heads, uint64_t seed,
     const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
-    uint32_t* __restrict__ rbits, int wpc) {
+    uint32_t* __restrict__ rbits, int32_t* __restrict__ counts, int wpc) {
   extern __shared__ int32_t sG[];
   const GS G = load_gset<GS>(Gglob, g, sG);
   const int idx = blockIdx.x * 64 + threadIdx.x;
   if (idx >= heads * nb) return;
   const int h = idx / nb, i = idx - h * nb;
-  build_row(G, nb, w, r, seed, h, i, col_idx + row_ptr[idx], rbits + (int64_t)h * nb * wpc, wpc);
+  build_row(G, nb, w, r, seed, h, i, col_idx + row_ptr[idx], rbits + (int64_t)h * nb * wpc, wpc,
+            counts + (int64_t)h * nb);
 }
 
-// Larger layouts, phase 2: one work-group of kColThreads per head (a column per
-// thread up to 1024 blocks); clears the bitmap.  The lists of the global rows and
-// columns (every block) are written last by the whole work-group.
-constexpr int kColThreads = 1024;
+// Larger layouts, phase 2: a work-group per kColThreads columns of a head (a column
+// per thread).  A column's length is g (or every block for a global column), its
+// non-global window rows and the rows that drew it (counted by phase 1), so each
+// work-group finds its offset by summing the lengths of the head's earlier columns.
+// Writes the column lists (clearing the pick bitmap), then with all threads the
+// global columns it owns and its slice of every global row.
+constexpr int kColThreads = 64;
 
 template <typename GS>
 __global__ __launch_bounds__(kColThreads) void layout_cols_kernel(
     const int32_t* __restrict__ Gglob, int g, int nb, int w, int64_t nnz_per_head,
-    uint32_t* __restrict__ rbits, int wpc, const int32_t* __restrict__ row_ptr,
-    int32_t* __restrict__ col_idx, int32_t* __restrict__ csc_ptr,
-    int32_t* __restrict__ csc_idx) {
-  extern __shared__ int32_t sG[];   // [g] global blocks (GLds), then [g] their column offsets
-  int32_t* sGpos = sG + g;
+    uint32_t* __restrict__ rbits, const int32_t* __restrict__ counts, int wpc,
+    const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
+    int32_t* __restrict__ csc_ptr, int32_t* __restrict__ csc_idx) {
+  // dynamic LDS: [g] global blocks (GLds), then [wpc] the global blocks as a bitmap
+  extern __shared__ int32_t sG[];
+  uint32_t* sGbits = reinterpret_cast<uint32_t*>(sG + g);
   __shared__ int part[kColThreads / 64];
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const GS G = load_gset<GS>(Gglob, g, sG);
-  uint32_t* hb = rbits + (int64_t)h * nb * wpc;
-  const int per = (nb + kColThreads - 1) / kColThreads;
-  const int j0 = min(nb, tid * per), j1 = min(nb, j0 + per);
-  int local = 0;
-  for (int j = j0; j < j1; ++j) local += col_length(G, nb, w, j, hb + (int64_t)j * wpc, wpc);
-  int pos = block_exclusive_scan(local, part);   // offset within the head
-  const int64_t head0 = (int64_t)h * nnz_per_head;
-  for (int j = j0; j < j1; ++j) {
-    csc_ptr[(int64_t)h * nb + j] = (int32_t)(head0 + pos);
-    const int len = col_length(G, nb, w, j, hb + (int64_t)j * wpc, wpc);
-    if (G.contains(j))
-      sGpos[G.count_le(j) - 1] = pos;
-    else
-      write_col(G, nb, w, j, hb + (int64_t)j * wpc, wpc, csc_idx + head0 + pos);
-    pos += len;
-  }
-  if (h == (int)gridDim.x - 1 && tid == kColThreads - 1)
-    csc_ptr[(int64_t)gridDim.x * nb] = (int32_t)((int64_t)gridDim.x * nnz_per_head);
+  __shared__ int sPos[kColThreads];
+  const int chunks = (nb + kColThreads - 1) / kColThreads;
+  const int h = blockIdx.x / chunks, c = blockIdx.x - h * chunks, tid = threadIdx.x;
+  for (int y = tid; y < wpc; y += kColThreads) sGbits[y] = 0u;
+  const GS G = load_gset<GS>(Gglob, g, sG);   // (GLds: ends with a barrier)
   __syncthreads();
-  for (int e = tid; e < g * nb; e += kColThreads) {
-    const int a = e / nb, j = e - a * nb;
-    const int x = Gglob[a];
-    col_idx[row_ptr[(int64_t)h * nb + x] + j] = j;
-    csc_idx[head0 + sGpos[a] + j] = j;
+  for (int a = tid; a < g; a += kColThreads) atomicOr(&sGbits[Gglob[a] >> 5], 1u << (Gglob[a] & 31));
+  __syncthreads();
+  const int32_t* hcnt = counts + (int64_t)h * nb;
+  auto is_global = [&](int j) { return (sGbits[j >> 5] >> (j & 31)) & 1u; };
+  auto len_of = [&](int j) {
+    if (is_global(j)) return nb;
+    const RowCtx<GS> rc = row_ctx(G, nb, w, j);
+    return G.g + rc.win_below(rc.hi + 1) + hcnt[j];
+  };
+  int before = 0;
+  for (int j = tid; j < c * kColThreads; j += kColThreads) before += len_of(j);
+  const int base = block_sum(before, part);
+  const int j = c * kColThreads + tid;
+  const int len = j < nb ? len_of(j) : 0;
+  const int pos = base + block_exclusive_scan(len, part);   // offset within the head
+  const int64_t head0 = (int64_t)h * nnz_per_head;
+  sPos[tid] = pos;
+  if (j < nb) {
+    csc_ptr[(int64_t)h * nb + j] = (int32_t)(head0 + pos);
+    if (!is_global(j))
+      write_col(sGbits, nb, w, j, rbits + ((int64_t)h * nb + j) * wpc, wpc, csc_idx + head0 + pos);
   }
+  if (h == (int)gridDim.x / chunks - 1 && c == chunks - 1 && tid == 0)
+    csc_ptr[(int64_t)(h + 1) * nb] = (int32_t)((int64_t)(h + 1) * nnz_per_head);
+  __syncthreads();
+  // the global columns of this chunk, then this chunk's slice of every global row
+  for (int x = 0; x < kColThreads && c * kColThreads + x < nb; ++x)
+    if (is_global(c * kColThreads + x))
+      for (int e = tid; e < nb; e += kColThreads) csc_idx[head0 + sPos[x] + e] = e;
+  if (j < nb)
+    for (int a = 0; a < g; ++a) col_idx[row_ptr[(int64_t)h * nb + Gglob[a]] + j] = j;
 }
 
 }  // namespace
@@ -725,14 +735,17 @@ int launch_layout_rowptr(bsattn_layout* L, hipStream_t stream) {
 }
 
 // Larger layouts, phase 3: the work-item records of the non-global rows (in block
-// order) and columns (in dK/dV order), one thread per (head, rank).
+// order) and columns (in dK/dV order), one thread per (head, rank); clears the
+// per-column pick counts for the next draw (one thread per (head, block)).
 __global__ __launch_bounds__(64) void layout_info_kernel(
     const int32_t* __restrict__ ngblk, const int32_t* __restrict__ kv_order, int nb, int g,
     int heads, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ csc_ptr, const int32_t* __restrict__ csc_idx,
-    int32_t* __restrict__ row_info, int32_t* __restrict__ col_info) {
+    int32_t* __restrict__ row_info, int32_t* __restrict__ col_info,
+    int32_t* __restrict__ counts) {
   const int ng = nb - g;
   const int idx = blockIdx.x * 64 + threadIdx.x;
+  if (idx < heads * nb) counts[idx] = 0;
   if (idx >= heads * ng) return;
   const int h = idx / ng, r = idx - h * ng;
   const int i = ngblk[r];
@@ -780,28 +793,33 @@ template <typename GS>
 int launch_rows_cols(bsattn_layout* L, hipStream_t stream) {
   const int wpc = (L->nb + 31) / 32;
   const size_t g_lds = (size_t)L->g * sizeof(int32_t);
+  // per-column pick counts after the pick bitmap (zero between builds, like it)
+  int32_t* counts = reinterpret_cast<int32_t*>(L->d_rbits + (size_t)L->heads * L->nb * wpc);
+  const int chunks = (L->nb + kColThreads - 1) / kColThreads;
   {
     ProfScope prof_("layout_rows", stream);
     hipLaunchKernelGGL(layout_rows_kernel<GS>, dim3((L->heads * L->nb + 63) / 64), dim3(64),
                        g_lds, stream, L->d_gblk, L->g, L->nb, L->w, L->r, L->heads, L->seed,
-                       L->d_row_ptr, L->d_col_idx, L->d_rbits, wpc);
+                       L->d_row_ptr, L->d_col_idx, L->d_rbits, counts, wpc);
   }
   int st = check_hip(hipGetLastError(), "layout_rows launch");
   if (st) return st;
   {
     ProfScope prof_("layout_cols", stream);
-    hipLaunchKernelGGL(layout_cols_kernel<GS>, dim3(L->heads), dim3(kColThreads), 2 * g_lds,
-                       stream, L->d_gblk, L->g, L->nb, L->w, L->nnz_per_head, L->d_rbits, wpc,
-                       L->d_row_ptr, L->d_col_idx, L->d_csc_ptr, L->d_csc_idx);
+    hipLaunchKernelGGL(layout_cols_kernel<GS>, dim3(L->heads * chunks), dim3(kColThreads),
+                       g_lds + (size_t)wpc * sizeof(uint32_t), stream, L->d_gblk, L->g, L->nb,
+                       L->w, L->nnz_per_head, L->d_rbits, counts, wpc, L->d_row_ptr,
+                       L->d_col_idx, L->d_csc_ptr, L->d_csc_idx);
   }
   st = check_hip(hipGetLastError(), "layout_cols launch");
   const int ng = L->nb - L->g;
   if (st || ng == 0) return st;
   {
     ProfScope prof_("layout_info", stream);
-    hipLaunchKernelGGL(layout_info_kernel, dim3((L->heads * ng + 63) / 64), dim3(64), 0, stream,
-                       L->d_ngblk, L->d_kv_order, L->nb, L->g, L->heads, L->d_row_ptr,
-                       L->d_col_idx, L->d_csc_ptr, L->d_csc_idx, L->d_row_info, L->d_col_info);
+    hipLaunchKernelGGL(layout_info_kernel, dim3((L->heads * L->nb + 63) / 64), dim3(64), 0,
+                       stream, L->d_ngblk, L->d_kv_order, L->nb, L->g, L->heads, L->d_row_ptr,
+                       L->d_col_idx, L->d_csc_ptr, L->d_csc_idx, L->d_row_info, L->d_col_info,
+                       counts);
   }
   return check_hip(hipGetLastError(), "layout_info launch");
 }
