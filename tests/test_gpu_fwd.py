@@ -132,6 +132,22 @@ def test_fwd_bf16_full_size_sampled(cfg):
     assert worst <= BF16_TOL
 
 
+def test_fwd_max_blocks_sampled():
+    """The largest layout (4096 blocks, n = 262,144), 1 head: the two global rows
+    (4096 blocks each, cut into segments), the sequence ends and random rows against
+    the oracle."""
+    n, G = 64 * 4096, [0, 4095]
+    say(f"fwd max blocks n={n}")
+    (qr, kr, vr), o, lse = run_fwd(n, 1, 1, G, 3, 3, 91, "bf16")
+    mask, _ = oracle_mask(n, 1, G, 3, 3, 91)
+    rows = np.unique(np.r_[0, 63, 64, 127, n - 65, n - 64, n - 1,
+                           np.random.default_rng(7).integers(0, n, 6)])
+    ro, rl = OA.attention_fwd_rows(qr, kr, vr, mask, 1 / 8.0, 0, 0, rows)
+    worst = max(max_abs(o[0, 0, rows], ro), max_abs(lse[0, 0, rows], rl))
+    say(f"   {len(rows)} rows, worst max-abs {worst:.3e}")
+    assert worst <= BF16_TOL
+
+
 def test_fwd_zero_queries_closed_form():
     """Q = 0: every score is exactly 0 and every probability exactly 1/|keys|, so O is
     the plain mean of the allowed value rows (fp32 sums) and lse = ln(64 |N(i)|);

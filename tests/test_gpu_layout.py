@@ -70,6 +70,11 @@ def test_layout_edge_cases_bit_exact():
     compare(64 * 512, 1, [0, 511], 3, 3, 94)         # 512 blocks: largest one-kernel layout
 
 
+def test_layout_max_blocks_bit_exact():
+    """The largest layout the library builds: n/b = 4096 blocks (n = 262,144)."""
+    compare(64 * 4096, 1, [0, 4095], 3, 3, 93)
+
+
 def test_layout_rebuild_matches_new_seed():
     n, heads, G, w, r = 4096, 3, [0, 63], 3, 3
     h = B.bsattn_layout_build(n, 64, heads, G, w, r, 11)
