@@ -133,6 +133,54 @@ def test_bwd_full_size_sampled():
     assert worst_id <= 1.0      # sums over 4096 rows of bf16-rounded values
 
 
+def test_fwd_bwd_max_blocks_sampled():
+    """The largest layout (4096 blocks, n = 262,144), 1 head, forward and backward:
+    sampled rows of O, lse and dQ (the two global rows among them), and dK, dV of two
+    non-global key blocks (the oracle run on exactly the query rows that see them)."""
+    n, G, seed = 64 * 4096, [0, 4095], 92
+    say(f"fwd+bwd max blocks n={n}")
+    shape = (1, 1, n, 64)
+    (q, k, v, do), (qr, kr, vr, dor) = qkv(shape, "bf16",
+                                          (I.SEED_Q, I.SEED_K, I.SEED_V, I.SEED_DO))
+    h = B.bsattn_layout_build(n, 64, 1, G, 3, 3, seed)
+    try:
+        o = torch.empty_like(q)
+        lse = torch.empty((1, 1, n), dtype=torch.float32, device="cuda")
+        wsf = torch.empty(max(1, B.bsattn_fwd_workspace(h, 1)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(1, B.bsattn_bwd_workspace(h, 1)), dtype=torch.uint8, device="cuda")
+        o_lo = torch.empty_like(q)
+        B.bsattn_fwd(h, q, k, v, o, lse, wsf, o_lo=o_lo)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        B.bsattn_bwd(h, q, k, v, o, lse, do, dq, dk, dv, wsb, o_lo=o_lo)
+        torch.cuda.synchronize()
+    finally:
+        B.bsattn_layout_destroy(h)
+    o, lse, dq, dk, dv = (to_f64(t) for t in (o, lse, dq, dk, dv))
+    mask, lay = oracle_mask(n, 1, G, 3, 3, seed)
+    rng = np.random.default_rng(262144)
+    rows = np.unique(np.r_[0, 63, 64, n - 65, n - 64, n - 1, rng.integers(0, n, 6)])
+    ro, rl = OA.attention_fwd_rows(qr, kr, vr, mask, 1 / 8.0, 0, 0, rows)
+    worst = max(max_abs(o[0, 0, rows], ro), max_abs(lse[0, 0, rows], rl))
+
+    def rows_mask(p0, p1, sel):
+        return np.concatenate([mask(0, int(p), int(p) + 1) for p in sel[p0:p1]])
+    rdq, _, _ = OA.attention_bwd(qr[:, :, rows], kr, vr, dor[:, :, rows],
+                                 lambda _h, p0, p1: rows_mask(p0, p1, rows), 1 / 8.0)
+    worst = max(worst, max_abs(dq[0, 0, rows], rdq[0, 0]))
+    cp, cs = lay["csc_ptr"], lay["csc_idx"]
+    for j in (1234, 3000):
+        sel = (np.asarray(cs[cp[j]:cp[j + 1]])[:, None] * 64 + np.arange(64)).ravel()
+        _, rdk, rdv = OA.attention_bwd(qr[:, :, sel], kr, vr, dor[:, :, sel],
+                                       lambda _h, p0, p1, sel=sel: rows_mask(p0, p1, sel),
+                                       1 / 8.0, row_chunk=128)
+        kr_ = slice(64 * j, 64 * j + 64)
+        worst = max(worst, max_abs(dk[0, 0, kr_], rdk[0, 0, kr_]),
+                    max_abs(dv[0, 0, kr_], rdv[0, 0, kr_]))
+    say(f"   sampled rows and two key blocks: worst max-abs {worst:.3e}")
+    assert worst <= BF16_TOL
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+
+
 def test_bwd_gradient_sum_identities():
     """Rows of P sum to 1 and rows of dS to 0, so per (batch, head) the dV rows sum
     to the dO rows and the dK rows sum to zero."""
