@@ -88,15 +88,15 @@ CSRC = os.path.join(ROOT, "block_sparse_long_bsattn_amd", "csrc")
 # reported while none of them has changed since the counters were taken
 KERNEL_SOURCES = {
     "bs_bwd_dkdv": ["bs_bwd.hip", "bs_bwd.hpp", "attn_tile.hpp", "common.hpp", "shape.hpp",
-                    "internal.hpp", "abi.cpp"],
+                    "internal.hpp", "abi.cpp", "fold.hpp"],
     "bs_bwd_dq": ["bs_bwd.hip", "bs_bwd.hpp", "attn_tile.hpp", "common.hpp", "shape.hpp",
-                  "internal.hpp", "abi.cpp"],
+                  "internal.hpp", "abi.cpp", "fold.hpp"],
     "bs_fwd_bf16": ["bs_fwd.hip", "attn_tile.hpp", "common.hpp", "shape.hpp", "internal.hpp",
-                    "abi.cpp"],
+                    "abi.cpp", "fold.hpp"],
     "lf_attn": ["lf_fwd.hip", "lf_tile.hpp", "attn_tile.hpp", "common.hpp", "shape.hpp",
-                "internal.hpp", "abi.cpp"],
+                "internal.hpp", "abi.cpp", "fold.hpp"],
     "lf_bwd_dkdv": ["lf_bwd.hip", "lf_tile.hpp", "attn_tile.hpp", "common.hpp", "shape.hpp",
-                    "internal.hpp", "abi.cpp"],
+                    "internal.hpp", "abi.cpp", "fold.hpp"],
 }
 
 

@@ -24,6 +24,7 @@
 #include <string>
 
 #include "bs_bwd.hpp"
+#include "fold.hpp"
 
 namespace bsattn {
 
@@ -442,7 +443,10 @@ size_t bwd_workspace_bytes(const bsattn_layout* L, int batch, int d) {
   size_t bytes = (size_t)batch * L->heads * L->n * sizeof(float);   // D
   bytes = (bytes + 255) & ~(size_t)255;
   const SegPlan sp = seg_plan(L, batch);
-  if (sp.split) bytes += (size_t)batch * L->heads * L->g * sp.nseg * 3 * (kBlock * d) * sizeof(float);
+  const Fold f = fold_plan(sp.nseg);
+  if (sp.split)   // dQ, dK, dV partials, then their folds
+    bytes += (size_t)batch * L->heads * L->g * (sp.nseg + (f.chunk ? f.nfold : 0)) * 3 *
+             (kBlock * d) * sizeof(float);
   return bytes;
 }
 
@@ -495,11 +499,28 @@ int launch_bwd_d(const bsattn_layout* L, int batch, float scale, const void* q, 
   }
   st = check_hip(hipGetLastError(), "bs_bwd_dkdv launch");
   if (st || !sp.split || L->g == 0) return st;
+  const Fold f = fold_plan(sp.nseg);
+  const float* red_q = a.part_q;    // what the reduce sums: the partials or their folds
+  const float* red_kv = a.part_kv;
+  if (f.chunk) {
+    const int groups = batch * L->heads * L->g;
+    float* fq = a.part_kv + nslots * 2 * kTile;
+    float* fkv = fq + (size_t)groups * f.nfold * kTile;
+    const FoldSumJob jq = fold_sum_job(a.part_q, fq, groups, sp.nseg, f, kTile);
+    const FoldSumJob jkv = fold_sum_job(a.part_kv, fkv, groups, sp.nseg, f, 2 * kTile);
+    {
+      ProfScope prof_("bs_bwd_fold", stream);
+      hipLaunchKernelGGL(fold_sum_kernel, dim3(jq.blocks + jkv.blocks), dim3(256), 0, stream, jq,
+                         jkv);
+    }
+    if ((st = check_hip(hipGetLastError(), "bs_bwd_fold launch"))) return st;
+    red_q = fq;
+    red_kv = fkv;
+  }
   {
     ProfScope prof_("bs_bwd_reduce", stream);
     hipLaunchKernelGGL(bs_bwd_reduce_kernel<D>, dim3(batch * L->heads * L->g * 3), dim3(256), 0,
-                       stream, (const float*)a.part_q, (const float*)a.part_kv, L->d_gblk, L->n,
-                       L->g, sp.nseg, a.dq, a.dk, a.dv);
+                       stream, red_q, red_kv, L->d_gblk, L->n, L->g, f.nfold, a.dq, a.dk, a.dv);
   }
   return check_hip(hipGetLastError(), "bs_bwd_reduce launch");
 }

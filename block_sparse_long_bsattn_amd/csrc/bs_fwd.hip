@@ -25,6 +25,7 @@
 #include <algorithm>
 
 #include "attn_tile.hpp"
+#include "fold.hpp"
 #include "internal.hpp"
 
 namespace bsattn {
@@ -551,7 +552,10 @@ size_t fwd_workspace_bytes_dt(const bsattn_layout* L, int batch, bsattn_dtype dt
   }
   const SegPlan sp = seg_plan(L, batch);
   const size_t part = d == 128 ? kPartFloatsOf<128> : kPartFloats;
-  return sp.split ? (size_t)batch * L->heads * L->g * sp.nseg * part * sizeof(float) : 0;
+  const Fold f = fold_plan(sp.nseg);
+  return sp.split ? (size_t)batch * L->heads * L->g * (sp.nseg + (f.chunk ? f.nfold : 0)) * part *
+                        sizeof(float)
+                  : 0;
 }
 
 // The size the public query reports: enough for either dtype that the head
@@ -634,11 +638,23 @@ int launch_fwd_bf16(const bsattn_layout* L, int batch, float scale, const void* 
   }
   int st = check_hip(hipGetLastError(), "bs_fwd_bf16 launch");
   if (st || !sp.split || L->g == 0) return st;
+  const Fold f = fold_plan(sp.nseg);
+  const float* merged = (const float*)ws;   // what the combine merges: the partials or folds
+  if (f.chunk) {
+    float* dst = (float*)ws + (size_t)bhn * L->g * sp.nseg * kPartFloatsOf<D>;
+    {
+      ProfScope prof_("bs_fwd_fold", stream);
+      hipLaunchKernelGGL(fold_softmax_kernel<D>, dim3(bhn * L->g * f.nfold * (D / 16)), dim3(256),
+                         0, stream, (const float*)ws, dst, sp.nseg, f.chunk, f.nfold);
+    }
+    if ((st = check_hip(hipGetLastError(), "bs_fwd_fold launch"))) return st;
+    merged = dst;
+  }
   {
     ProfScope prof_("bs_fwd_combine", stream);
-    hipLaunchKernelGGL(bs_fwd_combine_kernel<D>, dim3(bhn * L->g), dim3(256), 0, stream,
-                       (const float*)ws, L->d_gblk, L->heads, L->n, L->g, sp.nseg,
-                       (uint16_t*)o, (uint16_t*)o_lo, lse);
+    hipLaunchKernelGGL(bs_fwd_combine_kernel<D>, dim3(bhn * L->g), dim3(256), 0, stream, merged,
+                       L->d_gblk, L->heads, L->n, L->g, f.nfold, (uint16_t*)o, (uint16_t*)o_lo,
+                       lse);
   }
   return check_hip(hipGetLastError(), "bs_fwd_combine launch");
 }

@@ -28,10 +28,13 @@
 //                * a segment of cseg natural query tiles (sized per call) for a key
 //                  class tile holding global keys (their columns are full): fp32
 //                  partial dK, dV.
+//   lf_bwd_fold    (past 16 segments only) folds runs of consecutive partials into one
+//                  each, over many work-groups, so that the sums below stay short.
 //   lf_bwd_reduce  sums the partials in segment order and writes dQ of the
 //                global rows and dK, dV of the key class tiles holding global keys.
 
 #include "attn_tile.hpp"
+#include "fold.hpp"
 #include "internal.hpp"
 #include "lf_tile.hpp"
 
@@ -65,6 +68,9 @@ struct LfBwdArgs {
   float* dbuf;       // D [B*H*n]
   float* part_q;     // [B*H*ngt*nseg][64][d] dQ of the global query rows
   float* part_kv;    // [periods*nct_g*cnseg][2][64][d] dK, dV of key class tiles
+  const float* red_q;   // what lf_bwd_reduce sums: part_q, or its folds (rq_n per tile)
+  const float* red_kv;  // part_kv, or its folds (rkv_n per tile)
+  int rq_n, rkv_n;
                      // holding global keys
   const int32_t* gtok;         // [ng]
   const int32_t* gidx;         // [n]
@@ -715,7 +721,7 @@ __global__ __launch_bounds__(256) void lf_bwd_reduce_kernel(LfBwdArgs a, int nq_
       const int bh = idx / a.ngt, gt = idx - bh * a.ngt;
       const int j = gt * kBlock + row;
       if (j >= a.ng) continue;
-      src = a.part_q + (size_t)idx * a.nseg * kTileOf<D> + e0;
+      src = a.red_q + (size_t)idx * a.rq_n * kTileOf<D> + e0;
       stride = kTileOf<D>;
       const size_t row_off = ((size_t)bh * a.n + a.gtok[j]) * D + (e0 % D);
       dst = a.dqg + row_off;
@@ -733,19 +739,19 @@ __global__ __launch_bounds__(256) void lf_bwd_reduce_kernel(LfBwdArgs a, int nq_
       const int ci = e.t * kBlock + row;      // class index of this row
       if (ci >= e.nc) continue;
       const int bh = per * a.ph + e.h;
-      src = a.part_kv + (size_t)idx * a.cnseg * 2 * kTileOf<D> + kind * kTileOf<D> + e0;
+      src = a.red_kv + (size_t)idx * a.rkv_n * 2 * kTileOf<D> + kind * kTileOf<D> + e0;
       stride = 2 * kTileOf<D>;
       dst = (kind == 0 ? a.dk : a.dv) + ((size_t)bh * a.n + e.c + (size_t)e.s * ci) * D +
             (e0 % D);
     }
     float acc[16];
-    sum_partials(src, stride, (int)blockIdx.x < nq_groups ? a.nseg : a.cnseg, acc);
+    sum_partials(src, stride, (int)blockIdx.x < nq_groups ? a.rq_n : a.rkv_n, acc);
     store16_bf16(dst, acc, 1.f);
   }
 }
 
 struct LfBwdWs {
-  size_t dbuf, part_q, part_kv, total;
+  size_t dbuf, part_q, part_kv, fold_q, fold_kv, total;
 };
 
 LfBwdWs lf_bwd_ws_layout(const lfattn_plan* P, int batch, int heads, int d) {
@@ -756,10 +762,15 @@ LfBwdWs lf_bwd_ws_layout(const lfattn_plan* P, int batch, int heads, int d) {
   LfBwdWs w;
   w.dbuf = 0;
   w.part_q = up(bh * P->n * sizeof(float));
-  const size_t rows = bh * P->ngt * lf_row_seg(P, batch, heads).nseg;
-  const size_t cols = periods * (P->nct - P->nct_plain) * lf_col_seg(P, batch, heads).nseg;
+  const size_t tiles_q = bh * P->ngt, tiles_kv = periods * (P->nct - P->nct_plain);
+  const Fold fq = fold_plan(lf_row_seg(P, batch, heads).nseg);
+  const Fold fkv = fold_plan(lf_col_seg(P, batch, heads).nseg);
+  const size_t rows = tiles_q * lf_row_seg(P, batch, heads).nseg;
+  const size_t cols = tiles_kv * lf_col_seg(P, batch, heads).nseg;
   w.part_kv = up(w.part_q + rows * tile * sizeof(float));
-  w.total = up(w.part_kv + cols * 2 * tile * sizeof(float));
+  w.fold_q = up(w.part_kv + cols * 2 * tile * sizeof(float));
+  w.fold_kv = up(w.fold_q + (fq.chunk ? tiles_q * fq.nfold * tile * sizeof(float) : 0));
+  w.total = up(w.fold_kv + (fkv.chunk ? tiles_kv * fkv.nfold * 2 * tile * sizeof(float) : 0));
   return w;
 }
 
@@ -794,6 +805,19 @@ int launch_lf_bwd_d(const LfBwdArgs& a, const lfattn_plan* P, int bhn, int perio
   const int nq_groups = bhn * P->ngt;
   const int groups = nq_groups + periods * a.nct_g * 2;
   if (groups == 0) return 0;
+  const Fold fq = fold_plan(a.nseg), fkv = fold_plan(a.cnseg);
+  const FoldSumJob jq = fold_sum_job(a.part_q, const_cast<float*>(a.red_q), nq_groups, a.nseg,
+                                     fq, kTileOf<D>);
+  const FoldSumJob jkv = fold_sum_job(a.part_kv, const_cast<float*>(a.red_kv),
+                                      periods * a.nct_g, a.cnseg, fkv, 2 * kTileOf<D>);
+  if (jq.blocks + jkv.blocks > 0) {
+    {
+      ProfScope prof_("lf_bwd_fold", stream);
+      hipLaunchKernelGGL(fold_sum_kernel, dim3(jq.blocks + jkv.blocks), dim3(256), 0, stream, jq,
+                         jkv);
+    }
+    if ((st = check_hip(hipGetLastError(), "lf_bwd_fold launch"))) return st;
+  }
   {
     ProfScope prof_(D == 128 ? "lf_bwd_reduce_d128" : "lf_bwd_reduce", stream);
     hipLaunchKernelGGL(lf_bwd_reduce_kernel<D>, dim3(groups), dim3(256), 0, stream, a, nq_groups);
@@ -834,6 +858,10 @@ int launch_lf_bwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   const LfSeg rs = lf_row_seg(P, batch, heads);
   const LfSeg cs = lf_col_seg(P, batch, heads);
   a.nseg = rs.nseg; a.rseg = rs.seg; a.cnseg = cs.nseg; a.cseg = cs.seg;
+  const Fold fq = fold_plan(a.nseg), fkv = fold_plan(a.cnseg);
+  a.red_q = fq.chunk ? (const float*)(base + w.fold_q) : a.part_q;
+  a.red_kv = fkv.chunk ? (const float*)(base + w.fold_kv) : a.part_kv;
+  a.rq_n = fq.nfold; a.rkv_n = fkv.nfold;
   a.nct = P->nct; a.nct_plain = P->nct_plain; a.nct_g = P->nct - P->nct_plain;
   a.ph = P->heads > 0 ? P->heads : 1;
   a.win = lf_window(P);

@@ -24,10 +24,13 @@
 //                 index, writing a partial record.  With separate global
 //                 projections (§3.1 "Linear Projections for Global Attention") these
 //                 rows read Q_g, K_g, V_g instead of Q, K, V.
+//   lf_fold     (past 16 segments only) folds runs of consecutive partial records into
+//               one each, over many work-groups, so that the merge below stays short.
 //   lf_combine  merges those partials in a fixed order and scatters O and lse back
 //               to the global tokens' positions.
 
 #include "attn_tile.hpp"
+#include "fold.hpp"
 #include "internal.hpp"
 #include "lf_tile.hpp"
 
@@ -47,6 +50,8 @@ struct LfArgs {
   uint16_t* o_lo;       // bf16 rounding residual of O, or null
   float* lse;
   float* part;          // [B*H*ngt*nseg] partial records of the global query rows
+  const float* mpart;   // [B*H*ngt*mcount] records lf_combine merges: part, or its folds
+  int mcount;
   const int32_t* gtok;  // [ng]
   const int32_t* gidx;  // [n]
   const uint64_t* tile_gmask;  // [nt] bit x set iff token 64u+x is global
@@ -275,8 +280,8 @@ __global__ __launch_bounds__(256) void lf_combine_kernel(LfArgs a) {
 #pragma unroll
   for (int u = 0; u < D / 64; ++u) {
     float acc[16], Lb;
-    merge_partials<D>(a.part + (size_t)idx * a.nseg * kPartFloatsOf<D>, a.nseg, row, dq + 64 * u,
-                      acc, M, L, Lb);
+    merge_partials<D>(a.mpart + (size_t)idx * a.mcount * kPartFloatsOf<D>, a.mcount, row,
+                      dq + 64 * u, acc, M, L, Lb);
     const size_t off = ((size_t)bh * a.n + tok) * D + dq + 64 * u;
     store16_bf16_lo(a.o + off, a.o_lo != nullptr ? a.o_lo + off : nullptr, acc, 1.f / Lb);
   }
@@ -289,7 +294,9 @@ __global__ __launch_bounds__(256) void lf_combine_kernel(LfArgs a) {
 size_t lf_workspace_bytes(const lfattn_plan* P, int batch, int heads, int d) {
   if (P->ng == 0) return 0;
   const size_t rec = d == 128 ? kPartFloatsOf<128> : kPartFloatsOf<kHead>;
-  return (size_t)batch * heads * P->ngt * lf_row_seg(P, batch, heads).nseg * rec * sizeof(float);
+  const int nseg = lf_row_seg(P, batch, heads).nseg;
+  const Fold f = fold_plan(nseg);
+  return (size_t)batch * heads * P->ngt * (nseg + (f.chunk ? f.nfold : 0)) * rec * sizeof(float);
 }
 
 int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, int d, float scale, const void* q,
@@ -314,6 +321,10 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   a.win = lf_window(P);
   a.sl2 = scale * kLog2e;
   const int bhn = batch * heads;
+  const Fold fold = fold_plan(a.nseg);
+  const size_t rec = d == 128 ? kPartFloatsOf<128> : kPartFloatsOf<kHead>;
+  a.mpart = fold.chunk && has_g ? a.part + (size_t)bhn * P->ngt * a.nseg * rec : a.part;
+  a.mcount = fold.nfold;
   a.band_items = bhn / a.ph * P->nct;
   a.total_items = a.band_items + (has_g ? bhn * P->ngt * a.nseg : 0);
   int st;
@@ -327,6 +338,18 @@ int launch_lf_fwd(const lfattn_plan* P, int batch, int heads, int d, float scale
   }
   if ((st = check_hip(hipGetLastError(), "lf_attn launch"))) return st;
   if (!has_g) return 0;
+  if (fold.chunk) {
+    ProfScope prof_("lf_fold", stream);
+    float* dst = const_cast<float*>(a.mpart);
+    const int groups = bhn * P->ngt * fold.nfold;
+    if (d == 128)
+      hipLaunchKernelGGL(fold_softmax_kernel<128>, dim3(groups * 8), dim3(256), 0, stream, a.part,
+                         dst, a.nseg, fold.chunk, fold.nfold);
+    else
+      hipLaunchKernelGGL(fold_softmax_kernel<kHead>, dim3(groups * 4), dim3(256), 0, stream,
+                         a.part, dst, a.nseg, fold.chunk, fold.nfold);
+    if ((st = check_hip(hipGetLastError(), "lf_fold launch"))) return st;
+  }
   {
     ProfScope prof_("lf_combine", stream);
     if (d == 128)

@@ -154,7 +154,9 @@ int bsattn_layout_destroy(bsattn_layout* layout);
  * For d = 64 the forward's size serves both dtypes: bf16 uses it for the segments
  * of split global rows, fp32 for the segments of rows split when the problem has
  * fewer query blocks than half the device's work-group slots (small,
- * latency-bound problems); for d = 128 (bf16 only) it is the bf16 size. */
+ * latency-bound problems); for d = 128 (bf16 only) it is the bf16 size.  Past 16
+ * segments per global row (long sequences) both sizes include an area for the
+ * first level of a two-level merge of the segments' fp32 partials. */
 size_t bsattn_fwd_workspace(const bsattn_layout* layout, int batch, int d);
 size_t bsattn_bwd_workspace(const bsattn_layout* layout, int batch, int d);
 
@@ -305,7 +307,9 @@ int lfattn_fwd(const lfattn_plan* plan, int batch, int heads, int d, bsattn_dtyp
                float* lse, void* o_lo, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes lfattn_bwd needs (d = 64 or 128).  0 for invalid arguments.  Like
- * lfattn_fwd_workspace, it depends on batch and heads. */
+ * lfattn_fwd_workspace, it depends on batch and heads.  Past 16 segments per global
+ * row or column (long sequences) both sizes include an area for the first level of a
+ * two-level merge of the segments' fp32 partials. */
 size_t lfattn_bwd_workspace(const lfattn_plan* plan, int batch, int heads, int d);
 
 /*
