@@ -282,14 +282,24 @@ __device__ __forceinline__ void write_col(const uint32_t* gbits, int nb, int w, 
   const int half = (w - 1) / 2;
   const int lo = max(0, j - half), hi = min(nb - 1, j + half);
   int q = 0;
-  for (int y = 0; y < wpc; ++y) {
-    const int a = max(lo - 32 * y, 0), b = min(hi - 32 * y, 31);
-    const uint32_t win = a > b ? 0u : (b == 31 ? ~0u : (2u << b) - 1u) & ~((1u << a) - 1u);
-    uint32_t word = bits[y] | gbits[y] | win;
-    bits[y] = 0u;
-    while (word) {
-      out[q++] = 32 * y + __builtin_ctz(word);
-      word &= word - 1u;
+  // the words are read eight at a time (clamped reads, all in flight together); a
+  // column holds a few picks, so only the words that had one are cleared
+  for (int y0 = 0; y0 < wpc; y0 += 8) {
+    uint32_t pw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pw[u] = bits[min(y0 + u, wpc - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int y = y0 + u;
+      if (y >= wpc) break;
+      if (pw[u]) bits[y] = 0u;
+      const int a = max(lo - 32 * y, 0), b = min(hi - 32 * y, 31);
+      const uint32_t win = a > b ? 0u : (b == 31 ? ~0u : (2u << b) - 1u) & ~((1u << a) - 1u);
+      uint32_t word = pw[u] | gbits[y] | win;
+      while (word) {
+        out[q++] = 32 * y + __builtin_ctz(word);
+        word &= word - 1u;
+      }
     }
   }
 }
@@ -693,16 +703,26 @@ __global__ __launch_bounds__(kColThreads) void layout_cols_kernel(
   __syncthreads();
   const int32_t* hcnt = counts + (int64_t)h * nb;
   auto is_global = [&](int j) { return (sGbits[j >> 5] >> (j & 31)) & 1u; };
-  auto len_of = [&](int j) {
+  auto len_of = [&](int j, int picks) {
     if (is_global(j)) return nb;
     const RowCtx<GS> rc = row_ctx(G, nb, w, j);
-    return G.g + rc.win_below(rc.hi + 1) + hcnt[j];
+    return G.g + rc.win_below(rc.hi + 1) + picks;
   };
+  // lengths of the columns of the earlier chunks: their pick counts are read 16
+  // chunks at a time (clamped reads, all in flight together), not one round trip
+  // per chunk
   int before = 0;
-  for (int j = tid; j < c * kColThreads; j += kColThreads) before += len_of(j);
+  for (int k0 = 0; k0 < c; k0 += 16) {
+    int pk[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) pk[u] = hcnt[min(k0 + u, c - 1) * kColThreads + tid];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (k0 + u < c) before += len_of((k0 + u) * kColThreads + tid, pk[u]);
+  }
   const int base = block_sum(before, part);
   const int j = c * kColThreads + tid;
-  const int len = j < nb ? len_of(j) : 0;
+  const int len = j < nb ? len_of(j, hcnt[j]) : 0;
   const int pos = base + block_exclusive_scan(len, part);   // offset within the head
   const int64_t head0 = (int64_t)h * nnz_per_head;
   sPos[tid] = pos;
